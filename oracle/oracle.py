@@ -1,0 +1,240 @@
+"""ctypes front-end for the C oracle (bfp8moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test-suite, the smoke check and the
+CPU-baseline leg of the benchmark, never by the library.  Arrays are numpy
+(BF16 travels as uint16 bit patterns, E4M3 as uint8 codes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "bfp8moe_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+SCALE_FP32 = 0
+SCALE_UE8M0 = 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc: -O2, no FP contraction, no fast-math."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+                               "-std=gnu11", "-Wall", "-shared", "-fPIC", SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        sig = {
+            "oracle_bf16_to_f64": (ctypes.c_double, [ctypes.c_uint16]),
+            "oracle_f32_to_bf16": (ctypes.c_uint16, [f32]),
+            "oracle_f64_to_bf16": (ctypes.c_uint16, [ctypes.c_double]),
+            "oracle_e4m3_decode": (ctypes.c_double, [ctypes.c_uint8]),
+            "oracle_e4m3_encode": (ctypes.c_uint8, [f32]),
+            "oracle_group_scale": (f32, [f32, i32]),
+            "oracle_quant_fp8": (None, [P, i64, i32, i32, P, P]),
+            "oracle_exp_rn": (f32, [f32]),
+            "oracle_swiglu_one": (ctypes.c_uint16, [ctypes.c_uint16, ctypes.c_uint16, f32]),
+            "oracle_silu_and_mul": (None, [P, i64, i32, f32, P]),
+            "oracle_silu_and_mul_quant_fp8": (None, [P, i64, i32, P, P, i32, f32, i32, P, P]),
+            "oracle_max_blocks": (i64, [i64, i32, i32]),
+            "oracle_route_prepare": (i64, [P, i64, i32, i32, i32, P, P, P, P, i64, P]),
+            "oracle_grouped_gemm": (None, [P, P, i32, P, P, i32, i32, P, i64, i32, i32, P]),
+            "oracle_moe_reduce": (None, [P, P, P, i32, i32, i64, i32, i32, P]),
+            "oracle_fused_moe": (None, [P, i64, i32, P, P, i32, P, P, P, P, i32, i32, i32, i32, f32,
+                                        P, i64, P, P, P, P, P]),
+            "oracle_num_threads": (i32, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def as_np(t, dtype=None):
+    """torch tensor (CPU or GPU) or numpy array -> contiguous numpy array.
+    BF16 tensors come out as uint16 bit patterns, float8 as uint8 codes."""
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            t = t.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                t = t.view(torch.int16)
+                return t.numpy().view(np.uint16)
+            if t.dtype == torch.float8_e4m3fn:
+                t = t.view(torch.uint8)
+            t = t.numpy()
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(t)
+    if dtype is not None:
+        assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+# ---------------------------------------------------------------- scalars
+
+def e4m3_decode(c: int) -> float:
+    return lib().oracle_e4m3_decode(c)
+
+
+def e4m3_encode(x: float) -> int:
+    return lib().oracle_e4m3_encode(x)
+
+
+def f32_to_bf16(x: float) -> int:
+    return lib().oracle_f32_to_bf16(x)
+
+
+def f64_to_bf16(x: float) -> int:
+    return lib().oracle_f64_to_bf16(x)
+
+
+def bf16_to_f64(h: int) -> float:
+    return lib().oracle_bf16_to_f64(h)
+
+
+def exp_rn(x: float) -> float:
+    return lib().oracle_exp_rn(x)
+
+
+def group_scale(amax: float, fmt: int) -> float:
+    return lib().oracle_group_scale(amax, fmt)
+
+
+def swiglu_one(gate: int, up: int, clamp: float = float("inf")) -> int:
+    return lib().oracle_swiglu_one(gate, up, clamp)
+
+
+# ---------------------------------------------------------------- arrays
+
+def quant_fp8(x_bf16: np.ndarray, fmt: int = SCALE_FP32):
+    x = as_np(x_bf16, np.uint16)
+    rows, K = x.shape
+    q = np.zeros((rows, K), np.uint8)
+    s = np.zeros((rows, K // 128), np.float32)
+    lib().oracle_quant_fp8(_p(x), rows, K, fmt, _p(q), _p(s))
+    return q, s
+
+
+def silu_and_mul(gate_up_bf16, clamp: float = float("inf")):
+    x = as_np(gate_up_bf16, np.uint16)
+    rows, I2 = x.shape
+    out = np.zeros((rows, I2 // 2), np.uint16)
+    lib().oracle_silu_and_mul(_p(x), rows, I2 // 2, clamp, _p(out))
+    return out
+
+
+def silu_and_mul_quant_fp8(gate_up_bf16, row_expert_ids=None, expert_map=None, E: int = 0,
+                           clamp: float = float("inf"), fmt: int = SCALE_FP32,
+                           q_init=None, s_init=None):
+    x = as_np(gate_up_bf16, np.uint16)
+    rows, I2 = x.shape
+    I = I2 // 2
+    q = np.zeros((rows, I), np.uint8) if q_init is None else np.array(q_init, np.uint8, copy=True)
+    s = np.zeros((rows, I // 128), np.float32) if s_init is None else np.array(s_init, np.float32, copy=True)
+    ids = None if row_expert_ids is None else as_np(row_expert_ids, np.int32)
+    emap = None if expert_map is None else as_np(expert_map, np.int32)
+    lib().oracle_silu_and_mul_quant_fp8(_p(x), rows, I, _p(ids), _p(emap), E, clamp, fmt, _p(q), _p(s))
+    return q, s
+
+
+def max_blocks(R: int, L: int, block_m: int) -> int:
+    return lib().oracle_max_blocks(R, L, block_m)
+
+
+def route_prepare(topk_ids, expert_offset: int, L: int, block_m: int, with_blocks: bool = True):
+    ids = as_np(topk_ids, np.int32).reshape(-1)
+    R = ids.size
+    mb = max_blocks(R, L, block_m)
+    sorted_routes = np.zeros(R, np.int32)
+    offsets = np.zeros(L + 1, np.int32)
+    be = np.zeros(mb, np.int32) if with_blocks else None
+    bs = np.zeros(mb, np.int32) if with_blocks else None
+    nb = np.zeros(1, np.int32)
+    lib().oracle_route_prepare(_p(ids), R, expert_offset, L, block_m, _p(sorted_routes), _p(offsets),
+                               _p(be), _p(bs), mb, _p(nb))
+    return dict(sorted_routes=sorted_routes, expert_offsets=offsets, block_expert=be, block_start=bs,
+                num_blocks=int(nb[0]), max_blocks=mb)
+
+
+def grouped_gemm(A, A_s, a_row_div: int, B, B_s, topk_ids, expert_offset: int, L: int, C_init=None):
+    A = as_np(A, np.uint8); A_s = as_np(A_s, np.float32)
+    B = as_np(B, np.uint8); B_s = as_np(B_s, np.float32)
+    ids = as_np(topk_ids, np.int32).reshape(-1)
+    N, K = B.shape[1], B.shape[2]
+    R = ids.size
+    C = np.zeros((R, N), np.uint16) if C_init is None else np.array(C_init, np.uint16, copy=True)
+    lib().oracle_grouped_gemm(_p(A), _p(A_s), a_row_div, _p(B), _p(B_s), N, K, _p(ids), R,
+                              expert_offset, L, _p(C))
+    return C
+
+
+def moe_reduce(y_bf16, topk_w, topk_ids=None, expert_offset: int = 0, L: int = 1 << 30):
+    y = as_np(y_bf16, np.uint16)
+    w = as_np(topk_w, np.float32)
+    M, k = w.shape
+    H = y.shape[1]
+    ids = None if topk_ids is None else as_np(topk_ids, np.int32)
+    out = np.zeros((M, H), np.uint16)
+    lib().oracle_moe_reduce(_p(y), _p(w), _p(ids), expert_offset, L, M, k, H, _p(out))
+    return out
+
+
+def fused_moe(hidden, topk_ids, topk_w, w13, w13_s, w2, w2_s, expert_offset: int = 0, L: int = None,
+              scale_fmt: int = SCALE_FP32, clamp: float = float("inf"), tokens=None,
+              want_intermediates: bool = False):
+    """Whole layer for all tokens, or for the listed token subset.  Returns the
+    [M, H] BF16 output (rows of unlisted tokens are zero) and, optionally, the
+    intermediates keyed by route id."""
+    h = as_np(hidden, np.uint16)
+    ids = as_np(topk_ids, np.int32)
+    w = as_np(topk_w, np.float32)
+    w13 = as_np(w13, np.uint8); w13_s = as_np(w13_s, np.float32)
+    w2 = as_np(w2, np.uint8); w2_s = as_np(w2_s, np.float32)
+    M, H = h.shape
+    k = ids.shape[1]
+    Lw = w13.shape[0]
+    if L is None:
+        L = Lw
+    I = w2.shape[2]
+    out = np.zeros((M, H), np.uint16)
+    tok = None if tokens is None else np.ascontiguousarray(np.asarray(tokens, np.int64))
+    nt = M if tok is None else tok.size
+    inter = None
+    if want_intermediates:
+        inter = dict(h13=np.zeros((M * k, 2 * I), np.uint16), q=np.zeros((M * k, I), np.uint8),
+                     s=np.zeros((M * k, I // 128), np.float32), y=np.zeros((M * k, H), np.uint16))
+    lib().oracle_fused_moe(_p(h), M, H, _p(ids), _p(w), k, _p(w13), _p(w13_s), _p(w2), _p(w2_s),
+                           expert_offset, L, I, scale_fmt, clamp, _p(tok), nt, _p(out),
+                           _p(inter["h13"]) if inter else None, _p(inter["q"]) if inter else None,
+                           _p(inter["s"]) if inter else None, _p(inter["y"]) if inter else None)
+    return (out, inter) if want_intermediates else out
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
