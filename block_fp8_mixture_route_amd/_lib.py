@@ -1,0 +1,225 @@
+"""ctypes binding of libbfp8moe.so (the C ABI in include/bfp8moe.h).
+
+Argument marshalling only: torch tensors are turned into raw device pointers,
+the current HIP stream is passed through, and a non-zero status raises.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback of any kind.  The library must have been built first
+(``python -m block_fp8_mixture_route_amd.build``); importing this module
+without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libbfp8moe.so")
+
+SCALE_FP32 = 0
+SCALE_UE8M0 = 1
+
+FLAG_ROUTE_SINGLE_WG = 1 << 0
+FLAG_ROUTE_MULTI_WG = 1 << 1
+FLAG_LAYER_GENERAL = 1 << 2
+FLAG_LAYER_DECODE = 1 << 3
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip"}
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [
+        ("block_m", ctypes.c_int32),
+        ("scale_fmt", ctypes.c_int32),
+        ("clamp_limit", ctypes.c_float),
+        ("expert_offset", ctypes.c_int32),
+        ("local_num_experts", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class BFP8MoEError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_i32, _i64, _u32, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
+
+SIGNATURES = {
+    "bfp8moe_opts_init": (None, [ctypes.POINTER(Opts)]),
+    "bfp8moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "bfp8moe_last_error": (ctypes.c_char_p, []),
+    "bfp8moe_max_blocks": (_i64, [_i64, _i32, _i32]),
+    "moe_route_prepare_workspace_size": (_sz, [_i64, _i32, _u32]),
+    "moe_route_prepare": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _P, _P, _P, _P, _i64, _P, _P, _sz, _u32, _P]),
+    "quant_fp8": (ctypes.c_int, [_P, _i64, _i32, _i32, _P, _P, _P]),
+    "silu_and_mul": (ctypes.c_int, [_P, _i64, _i32, _f32, _P, _P]),
+    "silu_and_mul_quant_fp8": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _f32, _i32, _P, _P, _P]),
+    "moe_fp8_grouped_gemm": (ctypes.c_int, [_P, _P, _i32, _P, _P, _i32, _i32, _i32, _P, _P, _P, _P, _P, _i64, _i32,
+                                            _i64, _P, _P]),
+    "moe_reduce": (ctypes.c_int, [_P, _P, _P, _i32, _i32, _i64, _i32, _i32, _P, _P]),
+    "fused_moe_block_fp8_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(Opts)]),
+    "fused_moe_block_fp8": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32,
+                                           ctypes.POINTER(Opts), _P, _P, _sz, _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_fp8_mixture_route_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(status: int):
+    if status != 0:
+        raise BFP8MoEError(status, lib().bfp8moe_last_error().decode())
+
+
+def ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def stream_of(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_device(*ts):
+    for t in ts:
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("library entry points take device tensors")
+
+
+def _u16(t):
+    return t.view(torch.uint16) if t.dtype == torch.bfloat16 else t
+
+
+def opts(block_m=0, scale_fmt=SCALE_FP32, clamp_limit=math.inf, expert_offset=0, local_num_experts=0, flags=0):
+    o = Opts()
+    lib().bfp8moe_opts_init(ctypes.byref(o))
+    o.block_m, o.scale_fmt, o.clamp_limit = block_m, scale_fmt, clamp_limit
+    o.expert_offset, o.local_num_experts, o.flags = expert_offset, local_num_experts, flags
+    return o
+
+
+# ------------------------------------------------------------------ entry points
+
+def max_blocks(R: int, L: int, block_m: int) -> int:
+    return lib().bfp8moe_max_blocks(R, L, block_m)
+
+
+def moe_route_prepare(topk_ids: torch.Tensor, expert_offset: int, L: int, block_m: int, with_blocks=True, flags=0):
+    _require_device(topk_ids)
+    ids = topk_ids.reshape(-1)
+    R = ids.numel()
+    dev = ids.device
+    mb = max_blocks(R, L, block_m)
+    out = dict(
+        sorted_routes=torch.empty(max(R, 1), dtype=torch.int32, device=dev)[:R],
+        expert_offsets=torch.empty(L + 1, dtype=torch.int32, device=dev),
+        block_expert=torch.empty(max(mb, 1), dtype=torch.int32, device=dev) if with_blocks else None,
+        block_start=torch.empty(max(mb, 1), dtype=torch.int32, device=dev) if with_blocks else None,
+        num_blocks=torch.empty(1, dtype=torch.int32, device=dev),
+        max_blocks=mb,
+    )
+    wsb = lib().moe_route_prepare_workspace_size(R, L, flags)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    check(lib().moe_route_prepare(ptr(ids), R, expert_offset, L, block_m, ptr(out["sorted_routes"]),
+                                  ptr(out["expert_offsets"]), ptr(out["block_expert"]), ptr(out["block_start"]),
+                                  mb, ptr(out["num_blocks"]), ptr(ws), wsb, flags, stream_of(dev)))
+    out["_ws"] = ws  # keep alive until the stream has consumed it
+    return out
+
+
+def quant_fp8(x: torch.Tensor, scale_fmt=SCALE_FP32, q=None, scales=None):
+    _require_device(x)
+    rows, K = x.shape
+    q = torch.empty(rows, K, dtype=torch.uint8, device=x.device) if q is None else q
+    scales = torch.empty(rows, K // 128, dtype=torch.float32, device=x.device) if scales is None else scales
+    check(lib().quant_fp8(ptr(_u16(x)), rows, K, scale_fmt, ptr(q), ptr(scales), stream_of(x.device)))
+    return q, scales
+
+
+def silu_and_mul(gate_up: torch.Tensor, clamp_limit=math.inf, out=None):
+    _require_device(gate_up)
+    rows, I2 = gate_up.shape
+    out = torch.empty(rows, I2 // 2, dtype=torch.bfloat16, device=gate_up.device) if out is None else out
+    check(lib().silu_and_mul(ptr(_u16(gate_up)), rows, I2 // 2, clamp_limit, ptr(_u16(out)),
+                             stream_of(gate_up.device)))
+    return out
+
+
+def silu_and_mul_quant_fp8(gate_up: torch.Tensor, row_expert_ids=None, expert_map=None, E=0,
+                           clamp_limit=math.inf, scale_fmt=SCALE_FP32, q=None, scales=None):
+    _require_device(gate_up, row_expert_ids, expert_map)
+    rows, I2 = gate_up.shape
+    I = I2 // 2
+    q = torch.empty(rows, I, dtype=torch.uint8, device=gate_up.device) if q is None else q
+    scales = torch.empty(rows, I // 128, dtype=torch.float32, device=gate_up.device) if scales is None else scales
+    check(lib().silu_and_mul_quant_fp8(ptr(_u16(gate_up)), rows, I, ptr(row_expert_ids), ptr(expert_map), E,
+                                       clamp_limit, scale_fmt, ptr(q), ptr(scales), stream_of(gate_up.device)))
+    return q, scales
+
+
+def moe_fp8_grouped_gemm(A, A_scale, a_row_div, B, B_scale, route, block_m, R, C=None):
+    """route: the dict returned by moe_route_prepare (with blocks)."""
+    _require_device(A, A_scale, B, B_scale)
+    L, N, K = B.shape
+    C = torch.empty(R, N, dtype=torch.bfloat16, device=A.device) if C is None else C
+    check(lib().moe_fp8_grouped_gemm(ptr(A), ptr(A_scale), a_row_div, ptr(B), ptr(B_scale), L, N, K,
+                                     ptr(route["sorted_routes"]), ptr(route["expert_offsets"]),
+                                     ptr(route["block_expert"]), ptr(route["block_start"]),
+                                     ptr(route["num_blocks"]), route["max_blocks"], block_m, R, ptr(_u16(C)),
+                                     stream_of(A.device)))
+    return C
+
+
+def moe_reduce(y, topk_w, topk_ids=None, expert_offset=0, L=0, out=None):
+    _require_device(y, topk_w, topk_ids)
+    M, k = topk_w.shape
+    H = y.shape[1]
+    out = torch.empty(M, H, dtype=torch.bfloat16, device=y.device) if out is None else out
+    check(lib().moe_reduce(ptr(_u16(y)), ptr(topk_w), ptr(topk_ids), expert_offset, L, M, k, H, ptr(_u16(out)),
+                           stream_of(y.device)))
+    return out
+
+
+def fused_moe_workspace_size(M, H, k, E, I, o: Opts) -> int:
+    return lib().fused_moe_block_fp8_workspace_size(M, H, k, E, I, ctypes.byref(o))
+
+
+def fused_moe_block_fp8(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, E=None, o: Opts = None,
+                        out=None, ws=None):
+    _require_device(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale)
+    M, H = hidden.shape
+    k = topk_ids.shape[1]
+    I = w2.shape[2]
+    E = w13.shape[0] if E is None else E
+    o = opts() if o is None else o
+    need = fused_moe_workspace_size(M, H, k, E, I, o)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    out = torch.empty(M, H, dtype=torch.bfloat16, device=hidden.device) if out is None else out
+    check(lib().fused_moe_block_fp8(ptr(_u16(hidden)), M, H, ptr(topk_ids), ptr(topk_w), k, ptr(w13),
+                                    ptr(w13_scale), ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o),
+                                    ptr(_u16(out)), ptr(ws), ws.numel(), stream_of(hidden.device)))
+    return out

@@ -1,0 +1,336 @@
+// api.hip -- the C ABI declared in include/bfp8moe.h.  Host code: validates
+// arguments before anything is enqueued, lays out workspaces, picks kernels
+// by shape and launches them on the caller's stream.  Never allocates device
+// memory, never synchronises, never reads device data.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/bfp8moe.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bfp8moe_status_t fail(bfp8moe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bfp8moe_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BFP8MOE_OK;
+  return fail(BFP8MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define REQUIRE(cond, ...)                                        \
+  do {                                                            \
+    if (!(cond)) return fail(BFP8MOE_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace carving for the fused layer.
+struct LayerPlan {
+  int64_t M, R;
+  int32_t H, I, k, E, L, offset, block_m, fmt;
+  float clamp;
+  int64_t max_blocks;
+  bool route_single;
+  size_t off_aq, off_as, off_sorted, off_eoff, off_bexp, off_bstart, off_nb, off_rws, off_h13, off_q, off_s,
+      off_y, total;
+};
+
+int auto_block_m(int64_t R, int32_t L) {
+  const int64_t per_expert = R / (L > 0 ? L : 1);
+  if (per_expert <= 16) return 16;
+  if (per_expert <= 48) return 32;
+  return 64;
+}
+
+void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_t I, const bfp8moe_opts_t& o) {
+  p.M = M;
+  p.H = H;
+  p.I = I;
+  p.k = k;
+  p.E = E;
+  p.R = M * k;
+  p.L = o.local_num_experts > 0 ? o.local_num_experts : E;
+  p.offset = o.expert_offset;
+  p.fmt = o.scale_fmt;
+  p.clamp = o.clamp_limit;
+  p.block_m = o.block_m > 0 ? o.block_m : auto_block_m(p.R, p.L);
+  p.max_blocks = bfp8moe_max_blocks(p.R, p.L, p.block_m);
+  if (o.flags & BFP8MOE_FLAG_ROUTE_SINGLE_WG)
+    p.route_single = true;
+  else if (o.flags & BFP8MOE_FLAG_ROUTE_MULTI_WG)
+    p.route_single = false;
+  else
+    p.route_single = bfp8::route_prep_single_fits(p.R, p.L);
+  size_t o_ = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o_;
+    o_ = align_up(o_ + bytes);
+    return at;
+  };
+  p.off_aq = take((size_t)M * H);
+  p.off_as = take(sizeof(float) * (size_t)M * (H / 128));
+  p.off_sorted = take(sizeof(int32_t) * (size_t)p.R);
+  p.off_eoff = take(sizeof(int32_t) * ((size_t)p.L + 1));
+  p.off_bexp = take(sizeof(int32_t) * (size_t)p.max_blocks);
+  p.off_bstart = take(sizeof(int32_t) * (size_t)p.max_blocks);
+  p.off_nb = take(sizeof(int32_t));
+  p.off_rws = take(p.route_single ? 0 : bfp8::route_prep_ws_bytes(p.R, p.L));
+  p.off_h13 = take(sizeof(uint16_t) * (size_t)p.R * 2 * I);
+  p.off_q = take((size_t)p.R * I);
+  p.off_s = take(sizeof(float) * (size_t)p.R * (I / 128));
+  p.off_y = take(sizeof(uint16_t) * (size_t)p.R * H);
+  p.total = o_;
+}
+
+bool valid_fmt(int32_t f) { return f == BFP8MOE_SCALE_FP32 || f == BFP8MOE_SCALE_UE8M0; }
+
+}  // namespace
+
+extern "C" {
+
+void bfp8moe_opts_init(bfp8moe_opts_t* opts) {
+  if (!opts) return;
+  opts->block_m = 0;
+  opts->scale_fmt = BFP8MOE_SCALE_FP32;
+  opts->clamp_limit = INFINITY;
+  opts->expert_offset = 0;
+  opts->local_num_experts = 0;
+  opts->flags = 0;
+}
+
+const char* bfp8moe_status_string(int status) {
+  switch (status) {
+    case BFP8MOE_OK: return "ok";
+    case BFP8MOE_ERR_INVALID_ARG: return "invalid argument";
+    case BFP8MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case BFP8MOE_ERR_WORKSPACE: return "workspace too small";
+    case BFP8MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* bfp8moe_last_error(void) { return g_last_error.c_str(); }
+
+int64_t bfp8moe_max_blocks(int64_t R, int32_t L, int32_t block_m) {
+  if (R <= 0 || L <= 0 || block_m <= 0) return 0;
+  const int64_t d = R < L ? R : L;
+  return (R + d * (block_m - 1)) / block_m;
+}
+
+size_t moe_route_prepare_workspace_size(int64_t R, int32_t L, uint32_t flags) {
+  if (R < 0 || L <= 0) return 0;
+  bool single = (flags & BFP8MOE_FLAG_ROUTE_SINGLE_WG)  ? true
+                : (flags & BFP8MOE_FLAG_ROUTE_MULTI_WG) ? false
+                                                         : bfp8::route_prep_single_fits(R, L);
+  return single ? 0 : bfp8::route_prep_ws_bytes(R, L);
+}
+
+bfp8moe_status_t moe_route_prepare(const int32_t* topk_ids, int64_t R, int32_t expert_offset, int32_t L,
+                                   int32_t block_m, int32_t* sorted_routes, int32_t* expert_offsets,
+                                   int32_t* block_expert, int32_t* block_start, int64_t max_blocks,
+                                   int32_t* num_blocks, void* ws, size_t ws_bytes, uint32_t flags,
+                                   void* stream) {
+  REQUIRE(R >= 0 && R <= 0x7FFFFFFF, "R=%lld out of range [0, 2^31)", (long long)R);
+  REQUIRE(L >= 1, "local_num_experts=%d must be >= 1", L);
+  REQUIRE(expert_offset >= 0, "expert_offset=%d must be >= 0", expert_offset);
+  REQUIRE(block_m >= 1, "block_m=%d must be >= 1", block_m);
+  REQUIRE(R == 0 || (topk_ids && sorted_routes), "topk_ids and sorted_routes must be non-null");
+  REQUIRE(expert_offsets && num_blocks, "expert_offsets and num_blocks must be non-null");
+  REQUIRE((block_expert == nullptr) == (block_start == nullptr),
+          "block_expert and block_start must both be given or both be null");
+  const int64_t need_blocks = bfp8moe_max_blocks(R, L, block_m);
+  REQUIRE(block_expert == nullptr || max_blocks >= need_blocks, "max_blocks=%lld < required %lld",
+          (long long)max_blocks, (long long)need_blocks);
+  if (L > 2048) return fail(BFP8MOE_ERR_UNSUPPORTED, "local_num_experts=%d above 2048", L);
+  const bool single = (flags & BFP8MOE_FLAG_ROUTE_SINGLE_WG)  ? true
+                      : (flags & BFP8MOE_FLAG_ROUTE_MULTI_WG) ? false
+                                                               : bfp8::route_prep_single_fits(R, L);
+  const size_t need = single ? 0 : bfp8::route_prep_ws_bytes(R, L);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(BFP8MOE_ERR_WORKSPACE, "route workspace %zu bytes < required %zu", ws_bytes, need);
+  return hip_status(bfp8::launch_route_prepare(topk_ids, R, expert_offset, L, block_m, sorted_routes,
+                                               expert_offsets, block_expert, block_start,
+                                               block_expert ? max_blocks : 0, num_blocks, single, ws,
+                                               (hipStream_t)stream),
+                    "moe_route_prepare");
+}
+
+bfp8moe_status_t quant_fp8(const uint16_t* x, int64_t rows, int32_t K, int32_t scale_fmt, uint8_t* q,
+                           float* scales, void* stream) {
+  REQUIRE(rows >= 0, "rows=%lld must be >= 0", (long long)rows);
+  REQUIRE(K > 0 && K % 128 == 0, "K=%d must be a positive multiple of 128", K);
+  REQUIRE(valid_fmt(scale_fmt), "scale_fmt=%d is not 0 (fp32) or 1 (ue8m0)", scale_fmt);
+  REQUIRE(rows == 0 || (x && q && scales), "x, q and scales must be non-null");
+  REQUIRE(aligned16(x) && aligned16(q), "x and q must be 16-byte aligned");
+  return hip_status(bfp8::launch_quant_fp8(x, rows, K, scale_fmt, q, scales, (hipStream_t)stream), "quant_fp8");
+}
+
+bfp8moe_status_t silu_and_mul(const uint16_t* gate_up, int64_t rows, int32_t I, float clamp_limit, uint16_t* out,
+                              void* stream) {
+  REQUIRE(rows >= 0, "rows=%lld must be >= 0", (long long)rows);
+  REQUIRE(I > 0 && I % 128 == 0, "I=%d must be a positive multiple of 128", I);
+  REQUIRE(!isnan(clamp_limit) && clamp_limit > 0, "clamp_limit must be positive (+inf = unclamped)");
+  REQUIRE(rows == 0 || (gate_up && out), "gate_up and out must be non-null");
+  REQUIRE(aligned16(gate_up) && aligned16(out), "gate_up and out must be 16-byte aligned");
+  return hip_status(bfp8::launch_silu_and_mul(gate_up, rows, I, clamp_limit, out, (hipStream_t)stream),
+                    "silu_and_mul");
+}
+
+bfp8moe_status_t silu_and_mul_quant_fp8(const uint16_t* gate_up, int64_t rows, int32_t I,
+                                        const int32_t* row_expert_ids, const int32_t* expert_map, int32_t E,
+                                        float clamp_limit, int32_t scale_fmt, uint8_t* q, float* scales,
+                                        void* stream) {
+  REQUIRE(rows >= 0, "rows=%lld must be >= 0", (long long)rows);
+  REQUIRE(I > 0 && I % 128 == 0, "I=%d must be a positive multiple of 128", I);
+  REQUIRE(valid_fmt(scale_fmt), "scale_fmt=%d is not 0 (fp32) or 1 (ue8m0)", scale_fmt);
+  REQUIRE(!isnan(clamp_limit) && clamp_limit > 0, "clamp_limit must be positive (+inf = unclamped)");
+  REQUIRE(rows == 0 || (gate_up && q && scales), "gate_up, q and scales must be non-null");
+  REQUIRE(expert_map == nullptr || row_expert_ids != nullptr, "expert_map requires row_expert_ids");
+  REQUIRE(row_expert_ids == nullptr || E >= 1, "E=%d must be >= 1 when row_expert_ids is given", E);
+  REQUIRE(aligned16(gate_up) && aligned16(q), "gate_up and q must be 16-byte aligned");
+  bfp8::RowFilter f;
+  f.ids = row_expert_ids;
+  f.map = expert_map;
+  f.E = E;
+  f.mode = row_expert_ids == nullptr ? bfp8::kRowsAll : (expert_map ? bfp8::kRowsIdsMap : bfp8::kRowsIds);
+  return hip_status(bfp8::launch_silu_and_mul_quant(gate_up, rows, I, f, clamp_limit, scale_fmt, q, scales,
+                                                    (hipStream_t)stream),
+                    "silu_and_mul_quant_fp8");
+}
+
+bfp8moe_status_t moe_fp8_grouped_gemm(const uint8_t* A, const float* A_scale, int32_t a_row_div,
+                                      const uint8_t* B, const float* B_scale, int32_t L, int32_t N, int32_t K,
+                                      const int32_t* sorted_routes, const int32_t* expert_offsets,
+                                      const int32_t* block_expert, const int32_t* block_start,
+                                      const int32_t* num_blocks, int64_t max_blocks, int32_t block_m,
+                                      int64_t R, uint16_t* C, void* stream) {
+  REQUIRE(N > 0 && N % 128 == 0, "N=%d must be a positive multiple of 128", N);
+  REQUIRE(K > 0 && K % 128 == 0, "K=%d must be a positive multiple of 128", K);
+  REQUIRE(L >= 1, "L=%d must be >= 1", L);
+  REQUIRE(a_row_div >= 1, "a_row_div=%d must be >= 1", a_row_div);
+  REQUIRE(block_m == 16 || block_m == 32 || block_m == 64, "block_m=%d must be 16, 32 or 64", block_m);
+  REQUIRE(R >= 0 && R <= 0x7FFFFFFF, "R=%lld out of range", (long long)R);
+  REQUIRE(max_blocks >= 0, "max_blocks must be >= 0");
+  REQUIRE(max_blocks == 0 || (A && A_scale && B && B_scale && sorted_routes && expert_offsets && block_expert &&
+                              block_start && num_blocks && C),
+          "all pointers must be non-null");
+  REQUIRE(aligned16(A) && aligned16(B) && aligned16(C), "A, B and C must be 16-byte aligned");
+  return hip_status(bfp8::launch_grouped_gemm(A, A_scale, a_row_div, B, B_scale, N, K, sorted_routes,
+                                              expert_offsets, block_expert, block_start, num_blocks, max_blocks,
+                                              block_m, C, (hipStream_t)stream),
+                    "moe_fp8_grouped_gemm");
+}
+
+bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_t* topk_ids, int32_t expert_offset,
+                            int32_t L, int64_t M, int32_t k, int32_t H, uint16_t* out, void* stream) {
+  REQUIRE(M >= 0 && k >= 1, "M=%lld k=%d invalid", (long long)M, k);
+  REQUIRE(H > 0 && H % 8 == 0, "H=%d must be a positive multiple of 8", H);
+  REQUIRE(topk_ids == nullptr || (L >= 1 && expert_offset >= 0), "invalid expert slice");
+  REQUIRE(M == 0 || (y && topk_w && out), "y, topk_w and out must be non-null");
+  REQUIRE(aligned16(y) && aligned16(out), "y and out must be 16-byte aligned");
+  return hip_status(bfp8::launch_moe_reduce(y, topk_w, topk_ids, expert_offset, L, M, k, H, out,
+                                            (hipStream_t)stream),
+                    "moe_reduce");
+}
+
+size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32_t E, int32_t I,
+                                          const bfp8moe_opts_t* opts) {
+  if (M < 0 || H <= 0 || k <= 0 || E <= 0 || I <= 0) return 0;
+  bfp8moe_opts_t o;
+  bfp8moe_opts_init(&o);
+  if (opts) o = *opts;
+  LayerPlan p;
+  plan_layer(p, M, H, k, E, I, o);
+  return p.total;
+}
+
+bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
+                                     const float* topk_w, int32_t k, const uint8_t* w13, const float* w13_scale,
+                                     const uint8_t* w2, const float* w2_scale, int32_t E, int32_t I,
+                                     const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  bfp8moe_opts_t o;
+  bfp8moe_opts_init(&o);
+  if (opts) o = *opts;
+  REQUIRE(M >= 0 && M * (int64_t)(k > 0 ? k : 1) <= 0x7FFFFFFF, "M=%lld out of range", (long long)M);
+  REQUIRE(k >= 1, "k=%d must be >= 1", k);
+  REQUIRE(E >= 1, "E=%d must be >= 1", E);
+  REQUIRE(H > 0 && H % 128 == 0, "H=%d must be a positive multiple of 128", H);
+  REQUIRE(I > 0 && I % 128 == 0, "I=%d must be a positive multiple of 128", I);
+  REQUIRE(valid_fmt(o.scale_fmt), "scale_fmt=%d is not 0 (fp32) or 1 (ue8m0)", o.scale_fmt);
+  REQUIRE(!isnan(o.clamp_limit) && o.clamp_limit > 0, "clamp_limit must be positive (+inf = unclamped)");
+  const int32_t L = o.local_num_experts > 0 ? o.local_num_experts : E;
+  REQUIRE(o.local_num_experts >= 0 && o.expert_offset >= 0 && (int64_t)o.expert_offset + L <= E,
+          "expert slice [%d, %d + %d) is not inside [0, %d)", o.expert_offset, o.expert_offset, L, E);
+  REQUIRE(o.block_m == 0 || o.block_m == 16 || o.block_m == 32 || o.block_m == 64,
+          "block_m=%d must be 0, 16, 32 or 64", o.block_m);
+  REQUIRE((o.flags & (BFP8MOE_FLAG_ROUTE_SINGLE_WG | BFP8MOE_FLAG_ROUTE_MULTI_WG)) !=
+              (BFP8MOE_FLAG_ROUTE_SINGLE_WG | BFP8MOE_FLAG_ROUTE_MULTI_WG),
+          "route flags are exclusive");
+  REQUIRE(M == 0 || (hidden && topk_ids && topk_w && w13 && w13_scale && w2 && w2_scale && out),
+          "all pointers must be non-null");
+  REQUIRE(aligned16(hidden) && aligned16(w13) && aligned16(w2) && aligned16(out),
+          "hidden, w13, w2 and out must be 16-byte aligned");
+  if (L > 2048) return fail(BFP8MOE_ERR_UNSUPPORTED, "local_num_experts=%d above 2048", L);
+  if (M == 0) return BFP8MOE_OK;
+  LayerPlan p;
+  plan_layer(p, M, H, k, E, I, o);
+  if (ws == nullptr || ws_bytes < p.total)
+    return fail(BFP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
+  REQUIRE((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) == 0, "workspace must be 256-byte aligned");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* base = static_cast<char*>(ws);
+  uint8_t* aq = reinterpret_cast<uint8_t*>(base + p.off_aq);
+  float* as = reinterpret_cast<float*>(base + p.off_as);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + p.off_sorted);
+  int32_t* eoff = reinterpret_cast<int32_t*>(base + p.off_eoff);
+  int32_t* bexp = reinterpret_cast<int32_t*>(base + p.off_bexp);
+  int32_t* bstart = reinterpret_cast<int32_t*>(base + p.off_bstart);
+  int32_t* nb = reinterpret_cast<int32_t*>(base + p.off_nb);
+  void* rws = base + p.off_rws;
+  uint16_t* h13 = reinterpret_cast<uint16_t*>(base + p.off_h13);
+  uint8_t* q = reinterpret_cast<uint8_t*>(base + p.off_q);
+  float* s = reinterpret_cast<float*>(base + p.off_s);
+  uint16_t* y = reinterpret_cast<uint16_t*>(base + p.off_y);
+
+  hipError_t e;
+  e = bfp8::launch_route_prepare(topk_ids, p.R, p.offset, p.L, p.block_m, sorted, eoff, bexp, bstart, p.max_blocks,
+                                 nb, p.route_single, rws, st);
+  if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: route prep");
+  e = bfp8::launch_quant_fp8(hidden, M, H, p.fmt, aq, as, st);
+  if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: input quant");
+  e = bfp8::launch_grouped_gemm(aq, as, k, w13, w13_scale, 2 * I, H, sorted, eoff, bexp, bstart, nb, p.max_blocks,
+                                p.block_m, h13, st);
+  if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: gate/up GEMM");
+  bfp8::RowFilter f;
+  f.ids = topk_ids;
+  f.offset = p.offset;
+  f.L = p.L;
+  f.mode = bfp8::kRowsLocalSlice;
+  e = bfp8::launch_silu_and_mul_quant(h13, p.R, I, f, p.clamp, p.fmt, q, s, st);
+  if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: act+quant");
+  e = bfp8::launch_grouped_gemm(q, s, 1, w2, w2_scale, H, I, sorted, eoff, bexp, bstart, nb, p.max_blocks,
+                                p.block_m, y, st);
+  if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: down GEMM");
+  e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, p.offset, p.L, M, k, H, out, st);
+  return hip_status(e, "fused_moe_block_fp8: moe_reduce");
+}
+
+}  // extern "C"

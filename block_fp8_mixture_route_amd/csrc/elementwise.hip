@@ -1,0 +1,212 @@
+// elementwise.hip -- group-128 activation quantisation, SwiGLU, fused
+// SwiGLU + quantisation and moe_reduce for gfx950.
+//
+// Work mapping shared by the quant kernels: one group of 128 values is owned
+// by 16 consecutive lanes, each lane holding 8 values (one 16-byte load of
+// BF16).  A wave therefore covers 4 groups; the group amax is a 16-lane
+// butterfly.  Loads and stores are 16/8-byte vectors, contiguous across lanes.
+//
+// [P1 Modification, Fused SwiGLU and FP8 quantization] the fused kernel keeps
+// the BF16 SwiGLU value in registers and writes only codes and scales.
+// [P3 Purpose] clamp, UE8M0 scales and row filtering.
+// [P4 Pull request overview] moe_reduce applies the router weights.
+#include "device.h"
+#include "internal.h"
+
+namespace bfp8 {
+
+namespace {
+
+constexpr int kThreads = 256;                 // 4 waves, 16 groups per workgroup
+constexpr int kGroupsPerBlock = kThreads / 16;
+
+struct Bf16x8 { uint4 v; };
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// Quantise 8 values owned by this lane, given the 16-lane group scale.
+__device__ __forceinline__ uint2 encode8(const float (&f)[8], float s) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) c[i] = e4m3_encode(f[i] / s);
+  uint2 out;
+  out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  return out;
+}
+
+__device__ __forceinline__ float lane_amax8(const float (&f)[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(f[i]));
+  return m;
+}
+
+__global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __restrict__ x, int64_t n_groups,
+                                                             int gpr, int fmt, uint8_t* __restrict__ q,
+                                                             float* __restrict__ s) {
+  const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
+  if (gid >= n_groups) return;  // whole 16-lane group leaves together
+  const size_t base = (size_t)gid * kGroup + (size_t)l16 * 8;  // rows are contiguous groups
+  uint4 v = *reinterpret_cast<const uint4*>(x + base);
+  float f[8];
+  unpack8(v, f);
+  float amax = max_over_16(lane_amax8(f));
+  float sc = group_scale(amax, fmt);
+  *reinterpret_cast<uint2*>(q + base) = encode8(f, sc);
+  if (l16 == 0) s[gid] = sc;
+  (void)gpr;
+}
+
+__device__ __forceinline__ bool row_live(const RowFilter& f, int64_t r) {
+  if (f.mode == kRowsAll) return true;
+  int32_t id = f.ids[r];
+  if (f.mode == kRowsLocalSlice) {
+    int64_t e = (int64_t)id - f.offset;
+    return e >= 0 && e < f.L;
+  }
+  if (id < 0 || id >= f.E) return false;
+  if (f.mode == kRowsIdsMap && f.map[id] < 0) return false;
+  return true;
+}
+
+// SwiGLU of this lane's 8 outputs of group g in row r (gate at column
+// g*128 + 8*l16, up I columns later); returns them as BF16-valued floats.
+__device__ __forceinline__ void swiglu8(const uint16_t* __restrict__ gu, int64_t r, int I, int g, int l16,
+                                        float limit, bool clamp, float (&a)[8]) {
+  const uint16_t* row = gu + (size_t)r * 2 * I + (size_t)g * kGroup + (size_t)l16 * 8;
+  uint4 gv = *reinterpret_cast<const uint4*>(row);
+  uint4 uv = *reinterpret_cast<const uint4*>(row + I);
+  float gf[8], uf[8];
+  unpack8(gv, gf);
+  unpack8(uv, uf);
+#pragma unroll
+  for (int i = 0; i < 8; i++) a[i] = swiglu_bf16(gf[i], uf[i], limit, clamp);
+}
+
+__global__ __launch_bounds__(kThreads) void silu_and_mul_kernel(const uint16_t* __restrict__ gu, int64_t n_groups,
+                                                                int I, float limit, int clamp,
+                                                                uint16_t* __restrict__ out) {
+  const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
+  if (gid >= n_groups) return;
+  const int gpr = I / kGroup;
+  const int64_t r = gid / gpr;
+  const int g = (int)(gid - r * gpr);
+  float a[8];
+  swiglu8(gu, r, I, g, l16, limit, clamp != 0, a);
+  uint4 o;
+  o.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
+  o.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
+  o.z = f32_to_bf16(a[4]) | (f32_to_bf16(a[5]) << 16);
+  o.w = f32_to_bf16(a[6]) | (f32_to_bf16(a[7]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)r * I + (size_t)g * kGroup + (size_t)l16 * 8) = o;
+}
+
+__global__ __launch_bounds__(kThreads) void silu_and_mul_quant_kernel(const uint16_t* __restrict__ gu,
+                                                                      int64_t n_groups, int I, RowFilter filt,
+                                                                      float limit, int clamp, int fmt,
+                                                                      uint8_t* __restrict__ q,
+                                                                      float* __restrict__ s) {
+  const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
+  if (gid >= n_groups) return;
+  const int gpr = I / kGroup;
+  const int64_t r = gid / gpr;
+  const int g = (int)(gid - r * gpr);
+  if (!row_live(filt, r)) return;  // masked rows are left untouched
+  float a[8];
+  swiglu8(gu, r, I, g, l16, limit, clamp != 0, a);
+  float amax = max_over_16(lane_amax8(a));
+  float sc = group_scale(amax, fmt);
+  *reinterpret_cast<uint2*>(q + (size_t)r * I + (size_t)g * kGroup + (size_t)l16 * 8) = encode8(a, sc);
+  if (l16 == 0) s[(size_t)r * gpr + g] = sc;
+}
+
+// One thread per (token, 8 consecutive columns): acc over the k routes in
+// order with fmaf, one rounding to BF16.
+__global__ __launch_bounds__(kThreads) void moe_reduce_kernel(const uint16_t* __restrict__ y,
+                                                              const float* __restrict__ w,
+                                                              const int32_t* __restrict__ ids, int32_t offset,
+                                                              int32_t L, int64_t M, int k, int H,
+                                                              uint16_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int h8 = H / 8;
+  if (idx >= M * h8) return;
+  const int64_t t = idx / h8;
+  const int c = (int)(idx - t * h8) * 8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) acc[i] = 0.0f;
+  for (int j = 0; j < k; j++) {
+    const int64_t r = t * k + j;
+    if (ids) {
+      int64_t e = (int64_t)ids[r] - offset;
+      if (e < 0 || e >= L) continue;
+    }
+    const float wt = w[r];
+    uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)r * H + c);
+    float f[8];
+    unpack8(v, f);
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = __builtin_fmaf(wt, f[i], acc[i]);
+  }
+  uint4 o;
+  o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+  o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+  o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+  o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * H + c) = o;
+}
+
+inline unsigned blocks_for(int64_t n, int64_t per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t rows, int K, int fmt, uint8_t* q, float* s,
+                            hipStream_t stream) {
+  const int64_t ng = rows * (K / kGroup);
+  if (ng == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_fp8_kernel, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0, stream, x, ng,
+                     K / kGroup, fmt, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_and_mul(const uint16_t* gu, int64_t rows, int I, float limit, uint16_t* out,
+                               hipStream_t stream) {
+  const int64_t ng = rows * (I / kGroup);
+  if (ng == 0) return hipSuccess;
+  const int clamp = __builtin_isfinite(limit) ? 1 : 0;
+  hipLaunchKernelGGL(silu_and_mul_kernel, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0, stream, gu,
+                     ng, I, limit, clamp, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_and_mul_quant(const uint16_t* gu, int64_t rows, int I, const RowFilter& f, float limit,
+                                     int fmt, uint8_t* q, float* s, hipStream_t stream) {
+  const int64_t ng = rows * (I / kGroup);
+  if (ng == 0) return hipSuccess;
+  const int clamp = __builtin_isfinite(limit) ? 1 : 0;
+  hipLaunchKernelGGL(silu_and_mul_quant_kernel, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0, stream,
+                     gu, ng, I, f, limit, clamp, fmt, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_reduce(const uint16_t* y, const float* w, const int32_t* ids, int32_t offset, int32_t L,
+                             int64_t M, int k, int H, uint16_t* out, hipStream_t stream) {
+  const int64_t n = M * (H / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_reduce_kernel, dim3(blocks_for(n, kThreads)), dim3(kThreads), 0, stream, y, w, ids, offset,
+                     L, M, k, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace bfp8

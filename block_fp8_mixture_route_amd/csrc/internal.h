@@ -1,0 +1,56 @@
+// internal.h -- launchers shared by the C-ABI layer (api.hip) and the kernel
+// files.  Every launcher enqueues on `stream` and returns the launch status;
+// argument checking is done by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bfp8 {
+
+// Which rows of an act+quant call are processed.
+enum RowFilterMode : int {
+  kRowsAll = 0,       // every row
+  kRowsIds = 1,       // ids[r] in [0, E)
+  kRowsIdsMap = 2,    // ids[r] in [0, E) and map[ids[r]] >= 0
+  kRowsLocalSlice = 3 // ids[r] - offset in [0, L)
+};
+
+struct RowFilter {
+  const int32_t* ids = nullptr;
+  const int32_t* map = nullptr;
+  int32_t E = 0;
+  int32_t offset = 0;
+  int32_t L = 0;
+  int mode = kRowsAll;
+};
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t rows, int K, int fmt, uint8_t* q, float* s,
+                            hipStream_t stream);
+hipError_t launch_silu_and_mul(const uint16_t* gu, int64_t rows, int I, float limit, uint16_t* out,
+                               hipStream_t stream);
+hipError_t launch_silu_and_mul_quant(const uint16_t* gu, int64_t rows, int I, const RowFilter& f, float limit,
+                                     int fmt, uint8_t* q, float* s, hipStream_t stream);
+hipError_t launch_moe_reduce(const uint16_t* y, const float* w, const int32_t* ids, int32_t offset, int32_t L,
+                             int64_t M, int k, int H, uint16_t* out, hipStream_t stream);
+
+// Route preparation.  Picks the single-workgroup kernel when `single` is true,
+// otherwise count -> scan+scatter over `route_prep_num_segments(R)` workgroups
+// with a workspace of route_prep_ws_bytes(R, L) bytes.
+bool route_prep_single_fits(int64_t R, int32_t L);
+int route_prep_num_segments(int64_t R);
+size_t route_prep_ws_bytes(int64_t R, int32_t L);
+hipError_t launch_route_prepare(const int32_t* ids, int64_t R, int32_t offset, int32_t L, int32_t block_m,
+                                int32_t* sorted_routes, int32_t* expert_offsets, int32_t* block_expert,
+                                int32_t* block_start, int64_t max_blocks, int32_t* num_blocks, bool single,
+                                void* ws, hipStream_t stream);
+
+// Grouped block-FP8 GEMM over compact blocks (general path).
+hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div, const uint8_t* B,
+                               const float* Bs, int N, int K, const int32_t* sorted_routes,
+                               const int32_t* expert_offsets, const int32_t* block_expert,
+                               const int32_t* block_start, const int32_t* num_blocks, int64_t max_blocks,
+                               int block_m, uint16_t* C, hipStream_t stream);
+
+}  // namespace bfp8

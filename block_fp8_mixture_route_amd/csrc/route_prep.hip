@@ -1,0 +1,263 @@
+// route_prep.hip -- route preparation for gfx950: top-k routes sorted by local
+// expert (stable) plus compact per-expert blocks of block_m routes, emitted
+// only for experts that receive routes.
+//
+// [P2 Changes] one workgroup handles small problems end to end; larger ones
+// run a count pass over many workgroups, then a scan + scatter pass.
+// [P2 Suppressed comments] the slice [expert_offset, expert_offset + L) is
+// validated on the host before anything runs.
+// [P1 Modification, Active-expert block scheduling] blocks exist only for
+// experts with routes.
+//
+// Determinism and stability without atomics on positions: every segment of
+// routes is split into 16 contiguous wave sub-segments; each wave counts its
+// sub-segment into its own LDS histogram; an exclusive scan over
+// (expert, segment, wave) gives every wave a private cursor per expert; each
+// wave then walks its sub-segment 64 routes at a time in route order, ranks
+// equal experts inside the chunk with ballots, and advances its cursors.  The
+// result equals a stable counting sort.
+#include <mutex>
+
+#include "device.h"
+#include "internal.h"
+
+namespace bfp8 {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxL = 2048;
+constexpr int64_t kSingleMaxRoutes = 4096;
+
+__device__ __forceinline__ int local_expert(const int32_t* ids, int64_t r, int32_t offset, int32_t L) {
+  int64_t e = (int64_t)ids[r] - offset;
+  return (e >= 0 && e < L) ? (int)e : -1;
+}
+
+// Exclusive scan of v[0..n) in LDS by the whole 1024-thread workgroup.
+// Returns the total.  tmp: 32 ints of LDS.  Ends with a barrier.
+__device__ int block_exclusive_scan(int* v, int n, int* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (n + kThreads - 1) / kThreads;  // consecutive items per thread
+  const int b = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; i++)
+    if (b + i < n) local += v[b + i];
+  // inclusive scan of `local` across the wave
+  int x = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int s = lane < kWaves ? tmp[lane] : 0;
+    int t = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int y = __shfl_up(t, d);
+      if (lane >= d) t += y;
+    }
+    if (lane < kWaves) tmp[lane] = t - s;  // exclusive wave offsets
+    if (lane == kWaves - 1) tmp[kWaves] = t;
+  }
+  __syncthreads();
+  int run = tmp[wave] + x - local;  // exclusive prefix of this thread
+  for (int i = 0; i < per; i++) {
+    if (b + i < n) {
+      int c = v[b + i];
+      v[b + i] = run;
+      run += c;
+    }
+  }
+  int total = tmp[kWaves];
+  __syncthreads();
+  return total;
+}
+
+// Count pass of the multi-workgroup path: hist[seg][e] for each segment.
+__global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __restrict__ ids, int64_t R,
+                                                               int32_t offset, int32_t L, int64_t seg_len,
+                                                               int32_t* __restrict__ hist) {
+  extern __shared__ int lds[];
+  int* h = lds;
+  for (int e = threadIdx.x; e < L; e += kThreads) h[e] = 0;
+  __syncthreads();
+  const int64_t s0 = (int64_t)blockIdx.x * seg_len;
+  const int64_t s1 = s0 + seg_len < R ? s0 + seg_len : R;
+  for (int64_t r = s0 + threadIdx.x; r < s1; r += kThreads) {
+    int e = local_expert(ids, r, offset, L);
+    if (e >= 0) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < L; e += kThreads) hist[(size_t)blockIdx.x * L + e] = h[e];
+}
+
+// Scan + scatter.  With n_seg == 1 and hist == nullptr this is the whole
+// single-workgroup route preparation.  Workgroup 0 also writes the offsets,
+// the blocks and the -1 fills.
+__global__ __launch_bounds__(kThreads) void route_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int32_t offset, int32_t L, int32_t block_m, int64_t seg_len,
+    const int32_t* __restrict__ hist, int n_seg, int32_t* __restrict__ sorted_routes,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ block_expert, int32_t* __restrict__ block_start,
+    int64_t max_blocks, int32_t* __restrict__ num_blocks) {
+  extern __shared__ int lds[];
+  int* wh = lds;                       // [kWaves][L] wave histograms -> cursors
+  int* offs = wh + kWaves * L;         // [L] expert totals -> exclusive offsets
+  int* base = offs + L;                // [L] routes of this expert in earlier segments
+  int* cnt = base + L;                 // [L] expert totals (kept)
+  int* tmp = cnt + L;                  // [64] scan scratch
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = blockIdx.x;
+
+  for (int i = tid; i < kWaves * L; i += kThreads) wh[i] = 0;
+  __syncthreads();
+
+  const int64_t s0 = (int64_t)seg * seg_len;
+  const int64_t s1 = s0 + seg_len < R ? s0 + seg_len : R;
+  const int64_t n = s1 > s0 ? s1 - s0 : 0;
+  const int64_t sub = ((n + kWaves - 1) / kWaves + 63) / 64 * 64;  // wave sub-segment, whole chunks
+  const int64_t w0 = s0 + wave * sub;
+  const int64_t w1 = w0 + sub < s1 ? w0 + sub : s1;
+
+  // 1. wave histograms
+  for (int64_t r = w0 + lane; r < w1; r += 64) {
+    int e = local_expert(ids, r, offset, L);
+    if (e >= 0) atomicAdd(&wh[wave * L + e], 1);
+  }
+  __syncthreads();
+
+  // 2. per expert: exclusive over waves; totals over all segments
+  for (int e = tid; e < L; e += kThreads) {
+    int run = 0;
+    for (int w = 0; w < kWaves; w++) {
+      int c = wh[w * L + e];
+      wh[w * L + e] = run;
+      run += c;
+    }
+    int before = 0, total = run;
+    if (hist) {
+      total = 0;
+      for (int b = 0; b < n_seg; b++) {
+        int c = hist[(size_t)b * L + e];
+        if (b < seg) before += c;
+        total += c;
+      }
+    }
+    base[e] = before;
+    cnt[e] = total;
+    offs[e] = total;
+  }
+  __syncthreads();
+  const int n_kept = block_exclusive_scan(offs, L, tmp);
+
+  for (int i = tid; i < kWaves * L; i += kThreads) {
+    int e = i % L;
+    wh[i] += offs[e] + base[e];
+  }
+  __syncthreads();
+
+  // 3. in-order scatter, 64 routes per step per wave
+  int nbits = 0;
+  while ((1 << nbits) < L) nbits++;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t c0 = w0; c0 < w1; c0 += 64) {
+    const int64_t r = c0 + lane;
+    int e = r < w1 ? local_expert(ids, r, offset, L) : -1;
+    uint64_t same = __ballot(e >= 0);
+    for (int bit = 0; bit < nbits; bit++) {
+      uint64_t m = __ballot(e >= 0 && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? m : ~m;
+    }
+    if (e >= 0) {
+      int rank = __popcll(same & below);
+      int p = wh[wave * L + e];
+      sorted_routes[p + rank] = (int32_t)r;
+      if (rank == 0) wh[wave * L + e] = p + __popcll(same);
+    }
+  }
+
+  if (seg != 0) return;
+
+  // 4. offsets, blocks and fills (workgroup 0 only)
+  for (int e = tid; e < L; e += kThreads) expert_offsets[e] = offs[e];
+  if (tid == 0) expert_offsets[L] = n_kept;
+  for (int64_t i = n_kept + tid; i < R; i += kThreads) sorted_routes[i] = -1;
+  __syncthreads();
+  for (int e = tid; e < L; e += kThreads) base[e] = (cnt[e] + block_m - 1) / block_m;
+  __syncthreads();
+  const int nb = block_exclusive_scan(base, L, tmp);
+  if (block_expert) {
+    for (int e = tid; e < L; e += kThreads) {
+      const int nbe = (cnt[e] + block_m - 1) / block_m;
+      for (int i = 0; i < nbe; i++) {
+        block_expert[base[e] + i] = e;
+        block_start[base[e] + i] = offs[e] + i * block_m;
+      }
+    }
+    for (int64_t i = nb + tid; i < max_blocks; i += kThreads) {
+      block_expert[i] = -1;
+      block_start[i] = -1;
+    }
+  }
+  if (tid == 0) *num_blocks = nb;
+}
+
+size_t scatter_lds_bytes(int32_t L) { return sizeof(int) * ((size_t)(kWaves + 3) * L + 64); }
+
+}  // namespace
+
+bool route_prep_single_fits(int64_t R, int32_t L) { return R <= kSingleMaxRoutes && L <= kMaxL; }
+
+int route_prep_num_segments(int64_t R) {
+  int64_t seg = 1024;
+  while ((R + seg - 1) / seg > 64) seg *= 2;
+  int64_t n = (R + seg - 1) / seg;
+  return n < 1 ? 1 : (int)n;
+}
+
+static int64_t segment_length(int64_t R) {
+  int n = route_prep_num_segments(R);
+  return R == 0 ? 1 : (R + n - 1) / n;
+}
+
+size_t route_prep_ws_bytes(int64_t R, int32_t L) {
+  return sizeof(int32_t) * (size_t)route_prep_num_segments(R) * (size_t)L;
+}
+
+hipError_t launch_route_prepare(const int32_t* ids, int64_t R, int32_t offset, int32_t L, int32_t block_m,
+                                int32_t* sorted_routes, int32_t* expert_offsets, int32_t* block_expert,
+                                int32_t* block_start, int64_t max_blocks, int32_t* num_blocks, bool single,
+                                void* ws, hipStream_t stream) {
+  // Large expert counts need more than 64 KB of LDS in one workgroup
+  // (gfx950 allows up to 160 KB); raise the function's limit once.
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute((const void*)route_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)scatter_lds_bytes(kMaxL));
+    (void)hipGetLastError();
+  });
+  const size_t lds = scatter_lds_bytes(L);
+  if (single) {
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(1), dim3(kThreads), lds, stream, ids, R, offset, L, block_m,
+                       R > 0 ? R : (int64_t)1, (const int32_t*)nullptr, 1, sorted_routes, expert_offsets,
+                       block_expert, block_start, max_blocks, num_blocks);
+    return hipGetLastError();
+  }
+  const int n_seg = route_prep_num_segments(R);
+  const int64_t seg_len = segment_length(R);
+  int32_t* hist = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(route_count_kernel, dim3(n_seg), dim3(kThreads), sizeof(int) * (size_t)L, stream, ids, R,
+                     offset, L, seg_len, hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(n_seg), dim3(kThreads), lds, stream, ids, R, offset, L, block_m,
+                     seg_len, (const int32_t*)hist, n_seg, sorted_routes, expert_offsets, block_expert,
+                     block_start, max_blocks, num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace bfp8

@@ -1,0 +1,248 @@
+/*
+ * bfp8moe.h -- C ABI of the block-FP8 fused MoE library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library computes one mixture-of-experts FFN layer whose expert weights
+ * are OCP E4M3FN bytes with one fp32 scale per 128x128 block, and whose
+ * activations are quantised on the fly to E4M3FN with one scale per 1x128
+ * group.  The layer is a pipeline of five steps, each also exported alone:
+ *
+ *   moe_route_prepare       top-k routes sorted by expert into compact blocks
+ *   quant_fp8               group-128 dynamic activation quantisation
+ *   moe_fp8_grouped_gemm    block-FP8 grouped GEMM over active experts only
+ *   silu_and_mul_quant_fp8  SwiGLU (optionally clamped) fused with quant_fp8
+ *   moe_reduce              top-k weighted sum back to token order
+ *
+ * and fused_moe_block_fp8 runs the whole layer in one call.
+ *
+ * Sources, cited by page title and section:
+ *   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
+ *   [P2] lmdeploy PR "perf(pytorch): optimize compact blocked FP8 MoE and route
+ *        preparation"
+ *   [P3] vLLM PR "[Kernel][Perf] Fuse clamped MoE activation and UE8M0 FP8 block
+ *        quantization"
+ *   [P4] lmdeploy PR "Moe Reduce kernel"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer argument is a DEVICE pointer unless it is marked
+ *   "host".  The caller owns all memory (inputs, outputs, workspace); the
+ *   library never allocates, frees, synchronises the host or reads device data
+ *   on the host, so every call is legal inside HIP stream capture.
+ * Layout.  Row-major and contiguous.  BF16 is passed as uint16_t bit patterns,
+ *   E4M3FN as uint8_t codes.  Device pointers must be 16-byte aligned.
+ * Streams.  `stream` is a hipStream_t passed as void*; NULL is the default
+ *   stream.  Work is enqueued asynchronously on it.
+ * Errors.  Arguments are validated on the host before anything is enqueued; a
+ *   non-zero status means nothing was launched (except BFP8MOE_ERR_HIP, which
+ *   reports a failed launch).  bfp8moe_last_error() returns a message for the
+ *   most recent failure on the calling thread.
+ * Masked routes.  A route whose expert id, minus expert_offset, falls outside
+ *   [0, local_num_experts) -- for example -1 -- is not an error: it is skipped
+ *   by every step, and rows that belong to it are left untouched
+ *   [P3 Purpose: optional filtering of invalid or non-local expert rows].
+ * Determinism.  Repeated calls with the same inputs give bit-identical outputs.
+ */
+#ifndef BFP8MOE_H
+#define BFP8MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BFP8MOE_OK = 0,
+    BFP8MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, slice outside [0, E), ... */
+    BFP8MOE_ERR_UNSUPPORTED = 2,   /* a shape the kernels do not handle (no silent fallback) */
+    BFP8MOE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    BFP8MOE_ERR_HIP = 4            /* a HIP launch failed */
+} bfp8moe_status_t;
+
+/* Format of the per-group activation scales.  Both are stored as fp32.
+ * FP32:  scale = max(amax, 1e-10) / 448, one IEEE fp32 division.
+ * UE8M0: that value rounded up to a power of two (its fp32 exponent field,
+ *        plus one when the mantissa is non-zero)
+ *        [P4 Pull request overview: scale_fmt 'ue8m0'; P3 Purpose: UE8M0 scales]. */
+typedef enum { BFP8MOE_SCALE_FP32 = 0, BFP8MOE_SCALE_UE8M0 = 1 } bfp8moe_scale_fmt_t;
+
+/* Test-only switches that force one implementation where several exist. */
+enum {
+    BFP8MOE_FLAG_ROUTE_SINGLE_WG = 1u << 0,  /* route prep: one workgroup */
+    BFP8MOE_FLAG_ROUTE_MULTI_WG = 1u << 1,   /* route prep: count -> scan+scatter over many workgroups */
+    BFP8MOE_FLAG_LAYER_GENERAL = 1u << 2,    /* fused layer: staged general path */
+    BFP8MOE_FLAG_LAYER_DECODE = 1u << 3      /* fused layer: small-batch two-kernel path */
+};
+
+/* Options of the fused layer.  Initialise with bfp8moe_opts_init(). */
+typedef struct {
+    int32_t block_m;            /* routes per compact block for the general path; 0 = auto (16, 32 or 64) */
+    int32_t scale_fmt;          /* bfp8moe_scale_fmt_t for both activation quantisations */
+    float clamp_limit;          /* SwiGLU clamp; +INFINITY = unclamped [P3 Purpose: finite SwiGLU clamping] */
+    int32_t expert_offset;      /* first global expert held locally [P2 Suppressed comments] */
+    int32_t local_num_experts;  /* experts held locally (weights' leading dimension); 0 = all E */
+    uint32_t flags;             /* BFP8MOE_FLAG_* (tests only); 0 = choose by shape */
+} bfp8moe_opts_t;
+
+/* Fill *opts with the defaults: block_m 0, FP32 scales, no clamp, the full
+ * expert range, no flags.  opts: host pointer. */
+void bfp8moe_opts_init(bfp8moe_opts_t* opts);
+
+const char* bfp8moe_status_string(int status);
+/* Message of the last failure on this thread ("" if none).  Host string owned
+ * by the library, valid until the next call on the same thread. */
+const char* bfp8moe_last_error(void);
+
+/* ------------------------------------------------------------------------- */
+/* Route preparation                                                         */
+/* [P2 Changes: shared route preparation, one workgroup for small problems,   */
+/*  a scalable parallel path for large ones, sorted-indices and compact-block */
+/*  contracts; P1 Modification, Active-expert block scheduling: blocks only   */
+/*  for experts that receive tokens]                                          */
+/* ------------------------------------------------------------------------- */
+
+/* Upper bound on the number of compact blocks for R routes over L local
+ * experts: floor((R + min(L, R) * (block_m - 1)) / block_m).  Host function. */
+int64_t bfp8moe_max_blocks(int64_t R, int32_t L, int32_t block_m);
+
+/* Device workspace (bytes) moe_route_prepare needs for R routes and L experts
+ * (0 when the single-workgroup path will be used). */
+size_t moe_route_prepare_workspace_size(int64_t R, int32_t L, uint32_t flags);
+
+/* topk_ids [R] int32: the flattened [M, k] router choice, route r = t*k + j.
+ * A route is kept when topk_ids[r] - expert_offset lies in [0, L).
+ * Outputs:
+ *   sorted_routes  [R]   kept routes ordered by local expert, ties by route
+ *                        index (stable); entries past the kept routes are -1.
+ *   expert_offsets [L+1] start of each local expert's segment in sorted_routes;
+ *                        expert_offsets[L] = number of kept routes.
+ *   block_expert, block_start [max_blocks] (both NULL = sorted-indices contract
+ *                        only): for each expert with c > 0 routes, in expert
+ *                        order, ceil(c / block_m) blocks naming the local
+ *                        expert and the block's first position in
+ *                        sorted_routes; a block holds min(block_m, segment end
+ *                        - start) routes.  Unused slots hold -1.
+ *   num_blocks     [1]   number of blocks (device int32).
+ * max_blocks must be >= bfp8moe_max_blocks(R, L, block_m).  Requires
+ * 0 <= expert_offset, 1 <= L, block_m >= 1, R <= 2^31 - 1.  ws may be NULL when
+ * the size function returns 0. */
+bfp8moe_status_t moe_route_prepare(const int32_t* topk_ids, int64_t R, int32_t expert_offset, int32_t L,
+                                   int32_t block_m, int32_t* sorted_routes, int32_t* expert_offsets,
+                                   int32_t* block_expert, int32_t* block_start, int64_t max_blocks,
+                                   int32_t* num_blocks, void* ws, size_t ws_bytes, uint32_t flags,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Group-128 activation quantisation                                         */
+/* [P1 Motivation: quant_fp8 feeding the FP8 projection; P4 Pull request      */
+/*  overview: scale_fmt; P3 Purpose: dynamic E4M3 block quantisation]         */
+/* ------------------------------------------------------------------------- */
+
+/* x [rows, K] BF16 -> q [rows, K] E4M3FN and scales [rows, K/128] fp32.
+ * Per group of 128 columns: s from the group's amax (see bfp8moe_scale_fmt_t),
+ * q_i = E4M3FN(x_i / s) by IEEE fp32 division and round-to-nearest-even,
+ * saturating at +-448.  K must be a positive multiple of 128. */
+bfp8moe_status_t quant_fp8(const uint16_t* x, int64_t rows, int32_t K, int32_t scale_fmt, uint8_t* q,
+                           float* scales, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* SwiGLU and fused SwiGLU + quantisation                                    */
+/* [P1 Modification, Fused SwiGLU and FP8 quantization; P3 Purpose]           */
+/* ------------------------------------------------------------------------- */
+
+/* gate_up [rows, 2I] BF16, gate in columns [0, I), up in [I, 2I).
+ * out [rows, I] BF16 = bf16(silu(g) * u) with g = min(gate, clamp_limit),
+ * u = clamp(up, -clamp_limit, clamp_limit) when clamp_limit is finite, and
+ * silu(g) = g / (1 + exp(-g)) evaluated in fp32 (exp correctly rounded), one
+ * rounding to BF16.  I must be a positive multiple of 128.  This is the
+ * unfused half of the two-kernel path. */
+bfp8moe_status_t silu_and_mul(const uint16_t* gate_up, int64_t rows, int32_t I, float clamp_limit,
+                              uint16_t* out, void* stream);
+
+/* Fused SwiGLU + group-128 quantisation: for every live row, q and scales are
+ * bit-identical to quant_fp8(silu_and_mul(gate_up)); the BF16 SwiGLU value
+ * never leaves registers.  A row r is live unless row_expert_ids is given and
+ * row_expert_ids[r] is outside [0, E), or expert_map [E] is given and
+ * expert_map[row_expert_ids[r]] < 0.  Rows that are not live are not written.
+ * q [rows, I] E4M3FN, scales [rows, I/128] fp32.  expert_map requires
+ * row_expert_ids. */
+bfp8moe_status_t silu_and_mul_quant_fp8(const uint16_t* gate_up, int64_t rows, int32_t I,
+                                        const int32_t* row_expert_ids, const int32_t* expert_map, int32_t E,
+                                        float clamp_limit, int32_t scale_fmt, uint8_t* q, float* scales,
+                                        void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Block-FP8 grouped GEMM over compact blocks                                */
+/* [P3 Purpose: FP8 W8A8 block shape [128, 128]; P1 Modification:            */
+/*  GEMM programs only for blocks that receive tokens; P2 Changes: transposed */
+/*  MMA for small-M gate/up tiles]                                           */
+/* ------------------------------------------------------------------------- */
+
+/* For every block b < *num_blocks (device value) with local expert
+ * e = block_expert[b] and routes r = sorted_routes[p] for p in
+ * [block_start[b], min(block_start[b] + block_m, expert_offsets[e+1])):
+ *   C[r, n] = bf16( sum_g (A_scale[r/a_row_div, g] * B_scale[e, n/128, g])
+ *                        * sum_{i in group g} A[r/a_row_div, i] * B[e, n, i] ),  n < N,
+ * accumulated in fp32.  A [R/a_row_div rows, K] E4M3FN with A_scale [.., K/128];
+ * B [L, N, K] E4M3FN with B_scale [L, N/128, K/128]; C [R, N] BF16 indexed by
+ * route id (rows of routes not in any block are untouched).  a_row_div is the
+ * top-k for the gate/up projection (token rows feed k routes) and 1 for the
+ * down projection.  N and K must be positive multiples of 128; block_m one of
+ * 16, 32, 64; max_blocks the size of the block arrays; R the number of routes
+ * (rows of C). */
+bfp8moe_status_t moe_fp8_grouped_gemm(const uint8_t* A, const float* A_scale, int32_t a_row_div,
+                                      const uint8_t* B, const float* B_scale, int32_t L, int32_t N, int32_t K,
+                                      const int32_t* sorted_routes, const int32_t* expert_offsets,
+                                      const int32_t* block_expert, const int32_t* block_start,
+                                      const int32_t* num_blocks, int64_t max_blocks, int32_t block_m,
+                                      int64_t R, uint16_t* C, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* moe_reduce                                                                */
+/* [P4 Pull request overview: a dedicated reduction applies the router        */
+/*  weights, which the expert GEMMs no longer apply]                          */
+/* ------------------------------------------------------------------------- */
+
+/* out[t, n] = bf16(acc) where acc starts at +0 and, for j = 0..k-1 in order,
+ * acc = fmaf(topk_w[t, j], y[t*k + j, n], acc) over live routes (all routes
+ * when topk_ids is NULL; otherwise topk_ids[t, j] - expert_offset in [0, L)).
+ * y [M*k, H] BF16, topk_w [M, k] fp32, out [M, H] BF16.  H must be a positive
+ * multiple of 8. */
+bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_t* topk_ids,
+                            int32_t expert_offset, int32_t L, int64_t M, int32_t k, int32_t H, uint16_t* out,
+                            void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* The whole layer                                                           */
+/* [P1 Modification: gate/up GEMM -> fused SwiGLU + FP8 quant -> down GEMM;   */
+/*  P4: moe_reduce; P2 Changes: route preparation]                            */
+/* ------------------------------------------------------------------------- */
+
+/* Workspace (bytes) fused_moe_block_fp8 needs for these sizes and options. */
+size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32_t E, int32_t I,
+                                          const bfp8moe_opts_t* opts);
+
+/* hidden [M, H] BF16; topk_ids [M, k] int32 global expert ids (masked as
+ * described above); topk_w [M, k] fp32 router weights;
+ * w13 [L, 2I, H] E4M3FN (rows [0, I) gate, [I, 2I) up) with
+ * w13_scale [L, 2I/128, H/128]; w2 [L, H, I] E4M3FN with w2_scale
+ * [L, H/128, I/128]; L = opts->local_num_experts (or E).
+ * out [M, H] BF16 = moe_reduce over routes of
+ *   down( silu_and_mul_quant( gate_up( quant_fp8(hidden) ) ) ).
+ * The hidden states and the SwiGLU output are both quantised with
+ * opts->scale_fmt.  H and I must be positive multiples of 128.  ws: device
+ * workspace of at least fused_moe_block_fp8_workspace_size() bytes.
+ * opts: host pointer (NULL = defaults). */
+bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
+                                     const float* topk_w, int32_t k, const uint8_t* w13, const float* w13_scale,
+                                     const uint8_t* w2, const float* w2_scale, int32_t E, int32_t I,
+                                     const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BFP8MOE_H */

@@ -1,0 +1,94 @@
+"""The C-ABI library loads and exports every function include/bfp8moe.h
+declares, and its host-side argument checks reject bad calls before anything
+reaches the GPU (no device needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import block_fp8_mixture_route_amd as bfp8
+from block_fp8_mixture_route_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bfp8moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "sizeof")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_route_prepare", "quant_fp8", "moe_fp8_grouped_gemm", "silu_and_mul_quant_fp8", "moe_reduce",
+              "fused_moe_block_fp8", "silu_and_mul", "fused_moe_block_fp8_workspace_size", "bfp8moe_max_blocks"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bfp8.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    # and the binding's signature table covers them all
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_opts_layout_and_defaults():
+    assert ctypes.sizeof(_lib.Opts) == 24
+    o = bfp8.opts()
+    assert o.block_m == 0 and o.scale_fmt == 0 and math.isinf(o.clamp_limit) and o.flags == 0
+
+
+def test_max_blocks_formula():
+    assert bfp8.max_blocks(8, 256, 16) == 8
+    assert bfp8.max_blocks(16384, 512, 64) == (16384 + 512 * 63) // 64
+    assert bfp8.max_blocks(0, 8, 16) == 0
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, bfp8.lib().bfp8moe_last_error().decode()
+
+
+def test_host_validation_rejects_bad_calls():
+    L = bfp8.lib()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: validation fails first
+    st, msg = _status(L.quant_fp8, fake, 4, 100, 0, fake, fake, None)
+    assert st == 1 and "multiple of 128" in msg
+    st, msg = _status(L.quant_fp8, fake, 4, 128, 7, fake, fake, None)
+    assert st == 1 and "scale_fmt" in msg
+    st, msg = _status(L.silu_and_mul_quant_fp8, fake, 4, 128, None, fake, 0, math.inf, 0, fake, fake, None)
+    assert st == 1 and "expert_map requires" in msg
+    st, msg = _status(L.moe_fp8_grouped_gemm, fake, fake, 8, fake, fake, 4, 256, 256, fake, fake, fake, fake, fake,
+                      8, 24, 8, fake, None)
+    assert st == 1 and "block_m" in msg
+    st, msg = _status(L.moe_route_prepare, fake, 10, 0, 8, 16, fake, fake, fake, fake, 1, fake, None, 0, 0, None)
+    assert st == 1 and "max_blocks" in msg
+    st, msg = _status(L.moe_route_prepare, fake, 10, -1, 8, 16, fake, fake, None, None, 0, fake, None, 0, 0, None)
+    assert st == 1 and "expert_offset" in msg
+    st, msg = _status(L.moe_route_prepare, fake, 10, 0, 4096, 16, fake, fake, None, None, 0, fake, None, 0, 0, None)
+    assert st == 2  # unsupported: more than 2048 local experts
+    st, msg = _status(L.moe_route_prepare, fake, 100000, 0, 64, 16, fake, fake, None, None, 0, fake, None, 0, 0,
+                      None)
+    assert st == 3  # the multi-workgroup path needs a workspace
+    o = bfp8.opts(expert_offset=200, local_num_experts=100)
+    st, msg = _status(L.fused_moe_block_fp8, fake, 1, 7168, fake, fake, 8, fake, fake, fake, fake, 256, 256,
+                      ctypes.byref(o), fake, fake, 1 << 30, None)
+    assert st == 1 and "slice" in msg
+    o = bfp8.opts()
+    st, msg = _status(L.fused_moe_block_fp8, fake, 1, 7168, fake, fake, 8, fake, fake, fake, fake, 256, 256,
+                      ctypes.byref(o), fake, fake, 16, None)
+    assert st == 3 and "workspace" in msg
+    st, msg = _status(L.moe_reduce, fake, fake, None, 0, 0, 2, 8, 100, fake, None)
+    assert st == 1 and "multiple of 8" in msg
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        bfp8.quant_fp8(torch.zeros(1, 128, dtype=torch.bfloat16))

@@ -1,0 +1,119 @@
+"""GPU parity (through the C ABI) for the whole layer, fused_moe_block_fp8,
+on every layer workload: the GPU output must be within the normwise 2e-2
+bound of the oracle (all tokens where the oracle is quick, a seeded sample of
+tokens at the large sizes), bit-identical across repeated calls, and each
+forced implementation must agree with the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_fp8_mixture_route_amd as bfp8
+from block_fp8_mixture_route_amd import synth
+from oracle import oracle as O
+from tests.gpu_util import LAYER_TOL, bf16_np, dev, normwise_err, print_case
+
+pytestmark = pytest.mark.gpu
+
+# tokens the oracle evaluates per workload (None = all)
+SAMPLE = {"tiny": None, "decode_m1": None, "decode_m4": None, "decode_m16": None, "decode_m32": 16,
+          "small_m128": 12, "small_m512": 12, "large_m2048": 12}
+
+
+def _inputs(case, instance=0):
+    c = synth.LAYER_CASES[case]
+    hidden, ids, w, W = synth.layer_inputs(c, instance, device=dev())
+    return c, hidden, ids, w, W
+
+
+def _oracle_on_tokens(c, hidden, ids, w, W, tokens, fmt, clamp):
+    """Oracle output for the listed tokens, given device inputs: only the
+    experts those tokens use are copied to the host."""
+    ids_t = ids[tokens].cpu()
+    used = torch.unique(ids_t[ids_t >= 0])
+    remap = torch.full((c.E,), -1, dtype=torch.int32)
+    remap[used.long()] = torch.arange(used.numel(), dtype=torch.int32)
+    ids_local = torch.where(ids_t >= 0, remap[ids_t.clamp(min=0).long()], ids_t).to(torch.int32)
+    sel = used.to(dev()).long()
+    out = O.fused_moe(hidden[tokens].cpu(), ids_local, w[tokens].cpu(), W.w13[sel].cpu(), W.w13_s[sel].cpu(),
+                      W.w2[sel].cpu(), W.w2_s[sel].cpu(), scale_fmt=fmt, clamp=clamp)
+    return out
+
+
+def _run(c, hidden, ids, w, W, **kw):
+    o = bfp8.opts(**kw)
+    out = bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E, o=o)
+    torch.cuda.synchronize()
+    return out
+
+
+def _tokens(case, M):
+    n = SAMPLE[case]
+    if n is None or n >= M:
+        return list(range(M))
+    g = torch.Generator().manual_seed(M)
+    return sorted(torch.randperm(M, generator=g)[:n].tolist())
+
+
+@pytest.mark.parametrize("case", list(SAMPLE))
+def test_layer_matches_oracle(case):
+    print_case("layer", case)
+    c, hidden, ids, w, W = _inputs(case)
+    toks = _tokens(case, c.M)
+    ref = _oracle_on_tokens(c, hidden, ids, w, W, toks, c.scale_fmt, c.clamp)
+    out = _run(c, hidden, ids, w, W, scale_fmt=c.scale_fmt, clamp_limit=c.clamp)
+    got = bf16_np(out)[toks]
+    err = normwise_err(got, ref)
+    print("normwise err", err)
+    assert err <= LAYER_TOL
+    # determinism: a second call gives the same bits
+    out2 = _run(c, hidden, ids, w, W, scale_fmt=c.scale_fmt, clamp_limit=c.clamp)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("path", [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE])
+@pytest.mark.parametrize("case", ["tiny", "decode_m1", "decode_m4"])
+@pytest.mark.parametrize("fmt,clamp", [(bfp8.SCALE_FP32, math.inf), (bfp8.SCALE_UE8M0, 7.0)])
+def test_layer_paths_fmt_clamp(case, path, fmt, clamp):
+    print_case("layer path", case, path, fmt, clamp)
+    c, hidden, ids, w, W = _inputs(case, 1)
+    toks = list(range(c.M))
+    ref = _oracle_on_tokens(c, hidden, ids, w, W, toks, fmt, clamp)
+    out = _run(c, hidden, ids, w, W, scale_fmt=fmt, clamp_limit=clamp, flags=path)
+    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("path", [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE])
+def test_layer_masked_routes_and_local_slice(path):
+    # ids outside the local slice [offset, offset + L) are skipped; a token
+    # whose routes are all non-local gives zeros
+    print_case("layer slice", path)
+    c = synth.LAYER_CASES["tiny"]
+    hidden, ids, w, W = synth.layer_inputs(c, 3, device=dev())
+    ids = ids.clone()
+    ids[0, 0] = -1
+    ids[1, :] = 9  # beyond E: masked
+    off, L = 2, 4
+    Wl = synth.MoEWeights(W.w13[off:off + L].contiguous(), W.w13_s[off:off + L].contiguous(),
+                          W.w2[off:off + L].contiguous(), W.w2_s[off:off + L].contiguous())
+    out = bfp8.fused_moe_block_fp8(hidden, ids, w, Wl.w13, Wl.w13_s, Wl.w2, Wl.w2_s, E=c.E,
+                                   o=bfp8.opts(expert_offset=off, local_num_experts=L, flags=path))
+    torch.cuda.synchronize()
+    ref = O.fused_moe(hidden.cpu(), ids.cpu(), w.cpu(), Wl.w13.cpu(), Wl.w13_s.cpu(), Wl.w2.cpu(), Wl.w2_s.cpu(),
+                      expert_offset=off, L=L)
+    got = bf16_np(out)
+    assert (got[1] == 0).all()
+    assert normwise_err(got, ref) <= LAYER_TOL
+
+
+def test_layer_rejects_bad_arguments():
+    print_case("layer bad args")
+    c, hidden, ids, w, W = _inputs("tiny")
+    with pytest.raises(bfp8.BFP8MoEError):
+        _run(c, hidden, ids, w, W, expert_offset=6, local_num_experts=4)  # slice beyond E
+    with pytest.raises(bfp8.BFP8MoEError):
+        _run(c, hidden, ids, w, W, block_m=24)
+    small = torch.empty(16, dtype=torch.uint8, device=dev())
+    with pytest.raises(bfp8.BFP8MoEError):
+        bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E, ws=small)
