@@ -1,0 +1,347 @@
+"""Benchmark of the block-FP8 fused MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config decode_m1] [--instances N]
+
+A step is one fused_moe_block_fp8 call (route preparation, gate/up GEMM,
+SwiGLU + quantisation, down GEMM, moe_reduce) on one batch.  The workload is
+the M=1, E=256, top-k=8 decode layer (H=7168, I=256) by default.  Inputs are
+seeded synthetic tensors already resident in HBM.  Steps rotate over
+independent layer instances (own weights, routing and hidden states) whose
+combined weight bytes exceed the 256 MB Infinity Cache several times, so the
+weights stream from HBM as in a real multi-layer decode.  The K steps are
+replayed from a HIP graph that holds one rotation, and timed with HIP events
+between a device synchronisation on both sides.
+
+Printed: one JSON line with the metric (achieved HBM GB/s of the whole layer
+from its compulsory bytes), microseconds per layer, the roofline of the
+dominant kernel (its algorithmic bytes over its average duration, measured
+with HIP events the library records between its launches, in eager calls
+queued back to back behind a GPU spin), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused block-FP8 MoE layer µs + achieved HBM GB/s at M=1, E=256, top-k=8"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ HIP runtime via ctypes
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs: a stream, graph capture
+    and replay, and events."""
+
+    def __init__(self):
+        # bind to the HIP runtime already mapped into the process (torch's),
+        # never a second copy
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        self.h = ctypes.CDLL(path or "libamdhip64.so.7")
+        P, PP = ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)
+        sig = {
+            "hipStreamCreateWithFlags": [PP, ctypes.c_uint],
+            "hipStreamSynchronize": [P],
+            "hipStreamDestroy": [P],
+            "hipStreamBeginCapture": [P, ctypes.c_int],
+            "hipStreamEndCapture": [P, PP],
+            "hipGraphInstantiate": [PP, P, P, P, ctypes.c_size_t],
+            "hipGraphLaunch": [P, P],
+            "hipGraphExecDestroy": [P],
+            "hipGraphDestroy": [P],
+            "hipEventCreate": [PP],
+            "hipEventDestroy": [P],
+            "hipEventRecord": [P, P],
+            "hipEventSynchronize": [P],
+            "hipEventElapsedTime": [ctypes.POINTER(ctypes.c_float), P, P],
+            "hipDeviceSynchronize": [],
+            "hipGetErrorString": [ctypes.c_int],
+        }
+        for n, a in sig.items():
+            f = getattr(self.h, n)
+            f.argtypes = a
+            f.restype = ctypes.c_char_p if n == "hipGetErrorString" else ctypes.c_int
+
+    def ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {self.h.hipGetErrorString(rc).decode()}")
+
+    def stream(self):
+        s = ctypes.c_void_p()
+        self.ok(self.h.hipStreamCreateWithFlags(ctypes.byref(s), 1), "hipStreamCreateWithFlags")
+        return s
+
+    def event(self):
+        e = ctypes.c_void_p()
+        self.ok(self.h.hipEventCreate(ctypes.byref(e)), "hipEventCreate")
+        return e
+
+    def capture(self, stream, body):
+        self.ok(self.h.hipStreamBeginCapture(stream, 0), "hipStreamBeginCapture")  # global mode
+        try:
+            body()
+        finally:
+            g = ctypes.c_void_p()
+            rc = self.h.hipStreamEndCapture(stream, ctypes.byref(g))
+        self.ok(rc, "hipStreamEndCapture")
+        ex = ctypes.c_void_p()
+        self.ok(self.h.hipGraphInstantiate(ctypes.byref(ex), g, None, None, 0), "hipGraphInstantiate")
+        return g, ex
+
+    def launch(self, ex, stream):
+        self.ok(self.h.hipGraphLaunch(ex, stream), "hipGraphLaunch")
+
+    def sync(self, stream=None):
+        if stream is None:
+            self.ok(self.h.hipDeviceSynchronize(), "hipDeviceSynchronize")
+        else:
+            self.ok(self.h.hipStreamSynchronize(stream), "hipStreamSynchronize")
+
+    def record(self, ev, stream):
+        self.ok(self.h.hipEventRecord(ev, stream), "hipEventRecord")
+
+    def elapsed_ms(self, a, b):
+        self.ok(self.h.hipEventSynchronize(b), "hipEventSynchronize")
+        ms = ctypes.c_float()
+        self.ok(self.h.hipEventElapsedTime(ctypes.byref(ms), a, b), "hipEventElapsedTime")
+        return float(ms.value)
+
+
+# ------------------------------------------------------------------ bytes
+
+def layer_bytes(case, ids):
+    """Compulsory HBM bytes of one layer: every distinct active expert's W13 and
+    W2 with their block scales, hidden states in, output out, routing in."""
+    import torch
+    d = int(torch.unique(ids[ids >= 0]).numel())
+    H, I = case.H, case.I
+    per_expert = 2 * I * H + H * I + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128))
+    io = case.M * H * 2 * 2 + case.M * case.k * 8
+    return d * per_expert + io, d
+
+
+def stage_bytes(case, ids, stage):
+    """Algorithmic bytes of the dominant stage.
+    decode_token (the whole layer in one kernel): the layer's compulsory bytes
+    plus the BF16 act rows it writes and reads back through global memory.
+    decode_gate_up_swiglu / gate_up_gemm: W13 + its scales of every active
+    expert, the hidden states (BF16 in, or E4M3 codes + scales for the general
+    GEMM), routing in, the stage's output rows out."""
+    import torch
+    d = int(torch.unique(ids[ids >= 0]).numel())
+    H, I, R = case.H, case.I, case.M * case.k
+    if stage == "decode_token":
+        return layer_bytes(case, ids)[0] + 2 * R * I * 2
+    w = d * (2 * I * H + 4 * (2 * I // 128) * (H // 128))
+    if stage == "decode_gate_up_swiglu":
+        return w + case.M * H * 2 + R * 4 + R * I * 2
+    return w + case.M * H + case.M * (H // 128) * 4 + R * 4 + R * 2 * I * 2
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--config", default="decode_m1")
+    ap.add_argument("--instances", type=int, default=0, help="layer instances to rotate over (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_fp8_mixture_route_amd as bfp8
+    from block_fp8_mixture_route_amd import synth
+
+    case = synth.LAYER_CASES[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # one instance first, to size the rotation
+    t0 = time.time()
+    first = synth.layer_inputs(case, 0, device=dev)
+    b0, d0 = layer_bytes(case, first[1])
+    n_inst = args.instances or max(1, min(64, math.ceil(4 * MALL_BYTES / b0)))
+    insts = [first] + [synth.layer_inputs(case, i, device=dev) for i in range(1, n_inst)]
+    torch.cuda.synchronize()
+    log(f"{args.config}: {n_inst} instances generated in {time.time() - t0:.1f}s, "
+        f"{b0 / 1e6:.2f} MB compulsory per layer (instance 0, {d0} active experts)")
+
+    o = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp)
+    stages = bfp8.fused_moe_stages(case.M, case.H, case.k, case.E, case.I, o)
+    ws_bytes = bfp8.fused_moe_workspace_size(case.M, case.H, case.k, case.E, case.I, o)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # barrier counter starts at 0
+    outs = [torch.empty(case.M, case.H, dtype=torch.bfloat16, device=dev) for _ in range(n_inst)]
+    bytes_per = [layer_bytes(case, x[1])[0] for x in insts]
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    stream = hip.stream()
+    L = bfp8.lib()
+    P = ctypes.c_void_p
+
+    def call(i, opts_obj):
+        hidden, ids, w, W = insts[i]
+        bfp8._lib.check(L.fused_moe_block_fp8(P(hidden.data_ptr()), case.M, case.H, P(ids.data_ptr()),
+                                              P(w.data_ptr()), case.k, P(W.w13.data_ptr()), P(W.w13_s.data_ptr()),
+                                              P(W.w2.data_ptr()), P(W.w2_s.data_ptr()), case.E, case.I,
+                                              ctypes.byref(opts_obj), P(outs[i].data_ptr()), P(ws.data_ptr()),
+                                              ws_bytes, stream))
+
+    # warm-up: W eager steps
+    for s in range(args.warmup):
+        call(s % n_inst, o)
+    hip.sync(stream)
+    log(f"warm-up {args.warmup} steps done; stages: {stages}")
+
+    # graph of one rotation (+ a partial rotation so that exactly K steps run)
+    full, rem = divmod(args.steps, n_inst)
+    _, g_rot = hip.capture(stream, lambda: [call(i, o) for i in range(n_inst)])
+    g_rem = hip.capture(stream, lambda: [call(i, o) for i in range(rem)])[1] if rem else None
+    hip.launch(g_rot, stream)  # one untimed replay to settle the graph
+    hip.sync(stream)
+
+    ev0, ev1 = hip.event(), hip.event()
+    hip.sync()
+    hip.record(ev0, stream)
+    for _ in range(full):
+        hip.launch(g_rot, stream)
+    if g_rem is not None:
+        hip.launch(g_rem, stream)
+    hip.record(ev1, stream)
+    hip.sync()
+    total_ms = hip.elapsed_ms(ev0, ev1)
+    steps = full * n_inst + rem
+    ms_per_step = total_ms / steps
+    total_bytes = full * sum(bytes_per) + sum(bytes_per[:rem])
+    gbs = total_bytes / (total_ms * 1e-3) / 1e9
+    log(f"timed {steps} steps: {ms_per_step * 1e3:.2f} us/layer, {gbs:.0f} GB/s")
+
+    # per-stage durations: eager calls whose stage boundaries the library marks
+    # with events; a GPU spin queued first lets the whole rotation be enqueued
+    # before the GPU reaches it, so the kernels run back to back as in the graph
+    n_st = len(stages)
+    evs = [[hip.event() for _ in range(n_st + 1)] for _ in range(n_inst)]
+    arrays = [(ctypes.c_void_p * (n_st + 1))(*[e.value for e in row]) for row in evs]
+    o_ev = []
+    for i in range(n_inst):
+        oi = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp)
+        oi.stage_events = ctypes.cast(arrays[i], ctypes.POINTER(ctypes.c_void_p))
+        o_ev.append(oi)
+    ext = torch.cuda.ExternalStream(stream.value, device=dev)
+    reps = 10
+    stage_ms = [0.0] * n_st
+    for _ in range(reps):
+        with torch.cuda.stream(ext):
+            torch.cuda._sleep(20_000_000)  # ~8 ms of GPU spin at 2.4 GHz
+        for i in range(n_inst):
+            call(i, o_ev[i])
+        hip.sync(stream)
+        for i in range(n_inst):
+            for s_ in range(n_st):
+                stage_ms[s_] += hip.elapsed_ms(evs[i][s_], evs[i][s_ + 1])
+    stage_us = {stages[s_]: stage_ms[s_] * 1e3 / (reps * n_inst) for s_ in range(n_st)}
+    log("stage us: " + ", ".join(f"{k}={v:.2f}" for k, v in stage_us.items()))
+
+    dom = next(s_ for s_ in ("decode_token", "decode_gate_up_swiglu", "gate_up_gemm") if s_ in stage_us)
+    dom_bytes = sum(stage_bytes(case, x[1], dom) for x in insts) / n_inst
+    achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes": int(dom_bytes), "avg_us": round(stage_us[dom], 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, insts[0], args.cpu_seconds)
+
+    hidden0, ids0 = insts[0][0], insts[0][1]
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_layer": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{case.name}: M={case.M} E={case.E} top-k={case.k} H={case.H} I={case.I} "
+                        f"{case.routing} routing, {'UE8M0' if case.scale_fmt else 'fp32'} activation scales",
+            "M": case.M, "E": case.E, "top_k": case.k, "hidden": case.H, "intermediate": case.I,
+            "instances": n_inst, "bytes_per_layer": int(sum(bytes_per) / n_inst),
+            "hbm_roofline_us": round(sum(bytes_per) / n_inst / (HBM_PEAK_GBS * 1e3), 3),
+        },
+        "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(case, inst, seconds):
+    """The CPU oracle on the same layer (instance 0), repeated for about
+    `seconds`; throughput in the metric's unit (GB/s of compulsory bytes)."""
+    import torch
+    from oracle import oracle as O
+
+    hidden, ids, w, W = inst
+    used = torch.unique(ids[ids >= 0]).cpu()
+    remap = torch.full((case.E,), -1, dtype=torch.int32)
+    remap[used.long()] = torch.arange(used.numel(), dtype=torch.int32)
+    ids_c = ids.cpu()
+    ids_l = torch.where(ids_c >= 0, remap[ids_c.clamp(min=0).long()], ids_c).to(torch.int32)
+    sel = used.to(W.w13.device).long()
+    args = (hidden.cpu(), ids_l, w.cpu(), W.w13[sel].cpu(), W.w13_s[sel].cpu(), W.w2[sel].cpu(), W.w2_s[sel].cpu())
+    np_args = [O.as_np(a) for a in args]
+    nbytes, _ = layer_bytes(case, ids)
+    O.fused_moe(*np_args, scale_fmt=case.scale_fmt, clamp=case.clamp)  # warm
+    t0 = time.time()
+    n = 0
+    while True:
+        O.fused_moe(*np_args, scale_fmt=case.scale_fmt, clamp=case.clamp)
+        n += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = (time.time() - t0) / n
+    threads = min(O.num_threads(), case.M)  # the oracle parallelises over tokens
+    log(f"cpu oracle: {dt * 1e3:.1f} ms/layer over {n} runs, {threads} thread(s)")
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{case.name} instance 0, whole layer, {n} runs ({dt * 1e3:.1f} ms each)",
+            "us_per_layer": round(dt * 1e6, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -8,12 +8,14 @@ from ._lib import (  # noqa: F401
     BFP8MoEError,
     FLAG_LAYER_DECODE,
     FLAG_LAYER_GENERAL,
+    FLAG_LAYER_TOKEN,
     FLAG_ROUTE_MULTI_WG,
     FLAG_ROUTE_SINGLE_WG,
     SCALE_FP32,
     SCALE_UE8M0,
     Opts,
     fused_moe_block_fp8,
+    fused_moe_stages,
     fused_moe_workspace_size,
     lib,
     max_blocks,

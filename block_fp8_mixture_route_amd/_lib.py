@@ -25,6 +25,7 @@ FLAG_ROUTE_SINGLE_WG = 1 << 0
 FLAG_ROUTE_MULTI_WG = 1 << 1
 FLAG_LAYER_GENERAL = 1 << 2
 FLAG_LAYER_DECODE = 1 << 3
+FLAG_LAYER_TOKEN = 1 << 4
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip"}
 
@@ -37,6 +38,7 @@ class Opts(ctypes.Structure):
         ("expert_offset", ctypes.c_int32),
         ("local_num_experts", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
     ]
 
 
@@ -63,6 +65,8 @@ SIGNATURES = {
                                             _i64, _P, _P]),
     "moe_reduce": (ctypes.c_int, [_P, _P, _P, _i32, _i32, _i64, _i32, _i32, _P, _P]),
     "fused_moe_block_fp8_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(Opts)]),
+    "fused_moe_block_fp8_stages": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(Opts),
+                                          ctypes.POINTER(ctypes.c_char_p), _i32]),
     "fused_moe_block_fp8": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32,
                                            ctypes.POINTER(Opts), _P, _P, _sz, _P]),
 }
@@ -207,6 +211,16 @@ def fused_moe_workspace_size(M, H, k, E, I, o: Opts) -> int:
     return lib().fused_moe_block_fp8_workspace_size(M, H, k, E, I, ctypes.byref(o))
 
 
+def fused_moe_stages(M, H, k, E, I, o: Opts):
+    """Names of the kernel stages a fused_moe_block_fp8 call with these sizes
+    and options launches, in order."""
+    names = (ctypes.c_char_p * 16)()
+    n = lib().fused_moe_block_fp8_stages(M, H, k, E, I, ctypes.byref(o), names, 16)
+    if n < 0:
+        raise BFP8MoEError(1, lib().bfp8moe_last_error().decode())
+    return [names[i].decode() for i in range(n)]
+
+
 def fused_moe_block_fp8(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, E=None, o: Opts = None,
                         out=None, ws=None):
     _require_device(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale)
@@ -217,7 +231,8 @@ def fused_moe_block_fp8(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, 
     o = opts() if o is None else o
     need = fused_moe_workspace_size(M, H, k, E, I, o)
     if ws is None:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+        # zero-filled: the first 8 KB hold grid-barrier state that must start at 0
+        ws = torch.zeros(max(need, 8192), dtype=torch.uint8, device=hidden.device)
     out = torch.empty(M, H, dtype=torch.bfloat16, device=hidden.device) if out is None else out
     check(lib().fused_moe_block_fp8(ptr(_u16(hidden)), M, H, ptr(topk_ids), ptr(topk_w), k, ptr(w13),
                                     ptr(w13_scale), ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o),

@@ -47,9 +47,27 @@ struct LayerPlan {
   float clamp;
   int64_t max_blocks;
   bool route_single;
+  int mode;  // kModeGeneral, kModeDecode, kModeToken
   size_t off_aq, off_as, off_sorted, off_eoff, off_bexp, off_bstart, off_nb, off_rws, off_h13, off_q, off_s,
-      off_y, total;
+      off_y, off_act, total;
 };
+
+const char* const kGeneralStages[] = {"route_prepare", "quant_fp8", "gate_up_gemm",
+                                      "silu_and_mul_quant", "down_gemm", "moe_reduce"};
+const char* const kDecodeStages[] = {"decode_gate_up_swiglu", "decode_down_reduce"};
+const char* const kTokenStages[] = {"decode_token"};
+enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
+constexpr size_t kBarrierBytes = 8192;  // grid-barrier state, reserved at the start of every workspace
+
+// CU count used for planning: the current device's, or MI355X's 256 when no
+// device is visible (host-only planning, e.g. sizing a workspace).
+int planning_cus() {
+  const int n = bfp8::device_cu_count();
+  return n > 0 ? n : 256;
+}
+
+// The small-batch path is the default up to this many tokens.
+constexpr int64_t kDecodeAutoMaxM = 4;
 
 int auto_block_m(int64_t R, int32_t L) {
   const int64_t per_expert = R / (L > 0 ? L : 1);
@@ -71,18 +89,36 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.clamp = o.clamp_limit;
   p.block_m = o.block_m > 0 ? o.block_m : auto_block_m(p.R, p.L);
   p.max_blocks = bfp8moe_max_blocks(p.R, p.L, p.block_m);
+  const bool fits = bfp8::decode_path_fits(M, H, k, I);
+  const bool token_fits = bfp8::token_path_fits(M, H, k, p.L, I, planning_cus());
+  if (o.flags & BFP8MOE_FLAG_LAYER_GENERAL)
+    p.mode = kModeGeneral;
+  else if (o.flags & BFP8MOE_FLAG_LAYER_DECODE)
+    p.mode = fits ? kModeDecode : kModeGeneral;
+  else if (o.flags & BFP8MOE_FLAG_LAYER_TOKEN)
+    p.mode = token_fits ? kModeToken : kModeGeneral;
+  else if (token_fits)
+    p.mode = kModeToken;
+  else
+    p.mode = (fits && M <= kDecodeAutoMaxM) ? kModeDecode : kModeGeneral;
   if (o.flags & BFP8MOE_FLAG_ROUTE_SINGLE_WG)
     p.route_single = true;
   else if (o.flags & BFP8MOE_FLAG_ROUTE_MULTI_WG)
     p.route_single = false;
   else
     p.route_single = bfp8::route_prep_single_fits(p.R, p.L);
-  size_t o_ = 0;
+  size_t o_ = kBarrierBytes;
   auto take = [&](size_t bytes) {
     size_t at = o_;
     o_ = align_up(o_ + bytes);
     return at;
   };
+  if (p.mode != kModeGeneral) {
+    p.off_act = take(sizeof(uint16_t) * (size_t)p.R * I);
+    p.total = o_;
+    return;
+  }
+  p.off_act = 0;
   p.off_aq = take((size_t)M * H);
   p.off_as = take(sizeof(float) * (size_t)M * (H / 128));
   p.off_sorted = take(sizeof(int32_t) * (size_t)p.R);
@@ -112,6 +148,7 @@ void bfp8moe_opts_init(bfp8moe_opts_t* opts) {
   opts->expert_offset = 0;
   opts->local_num_experts = 0;
   opts->flags = 0;
+  opts->stage_events = nullptr;
 }
 
 const char* bfp8moe_status_string(int status) {
@@ -249,25 +286,11 @@ bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_
                     "moe_reduce");
 }
 
-size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32_t E, int32_t I,
-                                          const bfp8moe_opts_t* opts) {
-  if (M < 0 || H <= 0 || k <= 0 || E <= 0 || I <= 0) return 0;
-  bfp8moe_opts_t o;
-  bfp8moe_opts_init(&o);
-  if (opts) o = *opts;
-  LayerPlan p;
-  plan_layer(p, M, H, k, E, I, o);
-  return p.total;
-}
+}  // extern "C"
 
-bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
-                                     const float* topk_w, int32_t k, const uint8_t* w13, const float* w13_scale,
-                                     const uint8_t* w2, const float* w2_scale, int32_t E, int32_t I,
-                                     const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
-                                     void* stream) {
-  bfp8moe_opts_t o;
-  bfp8moe_opts_init(&o);
-  if (opts) o = *opts;
+namespace {
+
+bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, int32_t I, const bfp8moe_opts_t& o) {
   REQUIRE(M >= 0 && M * (int64_t)(k > 0 ? k : 1) <= 0x7FFFFFFF, "M=%lld out of range", (long long)M);
   REQUIRE(k >= 1, "k=%d must be >= 1", k);
   REQUIRE(E >= 1, "E=%d must be >= 1", E);
@@ -283,11 +306,69 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   REQUIRE((o.flags & (BFP8MOE_FLAG_ROUTE_SINGLE_WG | BFP8MOE_FLAG_ROUTE_MULTI_WG)) !=
               (BFP8MOE_FLAG_ROUTE_SINGLE_WG | BFP8MOE_FLAG_ROUTE_MULTI_WG),
           "route flags are exclusive");
+  if (L > 2048) return fail(BFP8MOE_ERR_UNSUPPORTED, "local_num_experts=%d above 2048", L);
+  if ((o.flags & BFP8MOE_FLAG_LAYER_DECODE) && M > 0 && !bfp8::decode_path_fits(M, H, k, I))
+    return fail(BFP8MOE_ERR_UNSUPPORTED,
+                "small-batch path forced but M=%lld k=%d H=%d I=%d exceed its limits (M<=8, k<=8, H<=8192, "
+                "I<=512)",
+                (long long)M, k, H, I);
+  if ((o.flags & BFP8MOE_FLAG_LAYER_TOKEN) && M > 0 && !bfp8::token_path_fits(M, H, k, L, I, planning_cus()))
+    return fail(BFP8MOE_ERR_UNSUPPORTED,
+                "one-token path forced but M=%lld k=%d H=%d I=%d do not fit it (M=1, k<=8, H<=8192, I<=512, "
+                "grid of %d workgroups <= %d compute units)",
+                (long long)M, k, H, I, bfp8::token_kernel_grid(H, k, L, I), planning_cus());
+  {
+    const uint32_t paths = o.flags & (BFP8MOE_FLAG_LAYER_GENERAL | BFP8MOE_FLAG_LAYER_DECODE | BFP8MOE_FLAG_LAYER_TOKEN);
+    REQUIRE((paths & (paths - 1)) == 0, "layer path flags are exclusive");
+  }
+  return BFP8MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fused_moe_block_fp8_stages(int64_t M, int32_t H, int32_t k, int32_t E, int32_t I,
+                                   const bfp8moe_opts_t* opts, const char** names, int32_t cap) {
+  bfp8moe_opts_t o;
+  bfp8moe_opts_init(&o);
+  if (opts) o = *opts;
+  if (check_layer_shape(M, H, k, E, I, o) != BFP8MOE_OK) return -1;
+  LayerPlan p;
+  plan_layer(p, M, H, k, E, I, o);
+  const char* const* list = p.mode == kModeToken ? kTokenStages : p.mode == kModeDecode ? kDecodeStages : kGeneralStages;
+  const int32_t n = p.mode == kModeToken ? 1 : p.mode == kModeDecode ? 2 : 6;
+  for (int32_t i = 0; names && i < n && i < cap; i++) names[i] = list[i];
+  return n;
+}
+
+size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32_t E, int32_t I,
+                                          const bfp8moe_opts_t* opts) {
+  bfp8moe_opts_t o;
+  bfp8moe_opts_init(&o);
+  if (opts) o = *opts;
+  if (check_layer_shape(M, H, k, E, I, o) != BFP8MOE_OK) return 0;
+  LayerPlan p;
+  plan_layer(p, M, H, k, E, I, o);
+  return p.total;
+}
+
+bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
+                                     const float* topk_w, int32_t k, const uint8_t* w13, const float* w13_scale,
+                                     const uint8_t* w2, const float* w2_scale, int32_t E, int32_t I,
+                                     const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  bfp8moe_opts_t o;
+  bfp8moe_opts_init(&o);
+  if (opts) o = *opts;
+  {
+    const bfp8moe_status_t st = check_layer_shape(M, H, k, E, I, o);
+    if (st != BFP8MOE_OK) return st;
+  }
   REQUIRE(M == 0 || (hidden && topk_ids && topk_w && w13 && w13_scale && w2 && w2_scale && out),
           "all pointers must be non-null");
   REQUIRE(aligned16(hidden) && aligned16(w13) && aligned16(w2) && aligned16(out),
           "hidden, w13, w2 and out must be 16-byte aligned");
-  if (L > 2048) return fail(BFP8MOE_ERR_UNSUPPORTED, "local_num_experts=%d above 2048", L);
   if (M == 0) return BFP8MOE_OK;
   LayerPlan p;
   plan_layer(p, M, H, k, E, I, o);
@@ -297,6 +378,21 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
 
   hipStream_t st = (hipStream_t)stream;
   char* base = static_cast<char*>(ws);
+  bfp8::LaunchHook hook;
+  hook.events = o.stage_events;
+  hook.n = o.stage_events ? (p.mode == kModeToken ? 2 : p.mode == kModeDecode ? 3 : 7) : 0;
+  if (p.mode == kModeToken) {
+    uint16_t* act = reinterpret_cast<uint16_t*>(base + p.off_act);
+    return hip_status(bfp8::launch_token_layer(hidden, H, topk_ids, topk_w, k, p.offset, p.L, w13, w13_scale, w2,
+                                               w2_scale, I, p.fmt, p.clamp, act, base, out, st, &hook),
+                      "fused_moe_block_fp8 (one token)");
+  }
+  if (p.mode == kModeDecode) {
+    uint16_t* act = reinterpret_cast<uint16_t*>(base + p.off_act);
+    return hip_status(bfp8::launch_decode_layer(hidden, M, H, topk_ids, topk_w, k, p.offset, p.L, w13, w13_scale, w2,
+                                                w2_scale, I, p.fmt, p.clamp, act, out, st, &hook),
+                      "fused_moe_block_fp8 (small batch)");
+  }
   uint8_t* aq = reinterpret_cast<uint8_t*>(base + p.off_aq);
   float* as = reinterpret_cast<float*>(base + p.off_as);
   int32_t* sorted = reinterpret_cast<int32_t*>(base + p.off_sorted);
@@ -311,11 +407,14 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   uint16_t* y = reinterpret_cast<uint16_t*>(base + p.off_y);
 
   hipError_t e;
+  hook.before(0, st);
   e = bfp8::launch_route_prepare(topk_ids, p.R, p.offset, p.L, p.block_m, sorted, eoff, bexp, bstart, p.max_blocks,
                                  nb, p.route_single, rws, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: route prep");
+  hook.before(1, st);
   e = bfp8::launch_quant_fp8(hidden, M, H, p.fmt, aq, as, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: input quant");
+  hook.before(2, st);
   e = bfp8::launch_grouped_gemm(aq, as, k, w13, w13_scale, 2 * I, H, sorted, eoff, bexp, bstart, nb, p.max_blocks,
                                 p.block_m, h13, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: gate/up GEMM");
@@ -324,12 +423,16 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   f.offset = p.offset;
   f.L = p.L;
   f.mode = bfp8::kRowsLocalSlice;
+  hook.before(3, st);
   e = bfp8::launch_silu_and_mul_quant(h13, p.R, I, f, p.clamp, p.fmt, q, s, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: act+quant");
+  hook.before(4, st);
   e = bfp8::launch_grouped_gemm(q, s, 1, w2, w2_scale, H, I, sorted, eoff, bexp, bstart, nb, p.max_blocks,
                                 p.block_m, y, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: down GEMM");
+  hook.before(5, st);
   e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, p.offset, p.L, M, k, H, out, st);
+  hook.before(6, st);
   return hip_status(e, "fused_moe_block_fp8: moe_reduce");
 }
 

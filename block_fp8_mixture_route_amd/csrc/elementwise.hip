@@ -20,8 +20,6 @@ namespace {
 constexpr int kThreads = 256;                 // 4 waves, 16 groups per workgroup
 constexpr int kGroupsPerBlock = kThreads / 16;
 
-struct Bf16x8 { uint4 v; };
-
 __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -29,17 +27,6 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
     f[2 * i] = __uint_as_float(w[i] << 16);
     f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
-}
-
-// Quantise 8 values owned by this lane, given the 16-lane group scale.
-__device__ __forceinline__ uint2 encode8(const float (&f)[8], float s) {
-  uint32_t c[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) c[i] = e4m3_encode(f[i] / s);
-  uint2 out;
-  out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-  return out;
 }
 
 __device__ __forceinline__ float lane_amax8(const float (&f)[8]) {
@@ -61,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __r
   unpack8(v, f);
   float amax = max_over_16(lane_amax8(f));
   float sc = group_scale(amax, fmt);
-  *reinterpret_cast<uint2*>(q + base) = encode8(f, sc);
+  *reinterpret_cast<uint2*>(q + base) = encode8_scaled(f, sc);
   if (l16 == 0) s[gid] = sc;
   (void)gpr;
 }
@@ -127,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void silu_and_mul_quant_kernel(const uint
   swiglu8(gu, r, I, g, l16, limit, clamp != 0, a);
   float amax = max_over_16(lane_amax8(a));
   float sc = group_scale(amax, fmt);
-  *reinterpret_cast<uint2*>(q + (size_t)r * I + (size_t)g * kGroup + (size_t)l16 * 8) = encode8(a, sc);
+  *reinterpret_cast<uint2*>(q + (size_t)r * I + (size_t)g * kGroup + (size_t)l16 * 8) = encode8_scaled(a, sc);
   if (l16 == 0) s[(size_t)r * gpr + g] = sc;
 }
 

@@ -17,6 +17,16 @@ enum RowFilterMode : int {
   kRowsLocalSlice = 3 // ids[r] - offset in [0, L)
 };
 
+// Optional profiling hook: records caller-owned HIP events on the stream
+// before stage i (and, with i == number of stages, after the last one).
+struct LaunchHook {
+  void* const* events = nullptr;
+  int n = 0;  // number of events in the array
+  void before(int i, hipStream_t stream) const {
+    if (events && i < n && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
+  }
+};
+
 struct RowFilter {
   const int32_t* ids = nullptr;
   const int32_t* map = nullptr;
@@ -52,5 +62,24 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
                                const int32_t* expert_offsets, const int32_t* block_expert,
                                const int32_t* block_start, const int32_t* num_blocks, int64_t max_blocks,
                                int block_m, uint16_t* C, hipStream_t stream);
+
+// Small-batch path of the fused layer: gate/up + SwiGLU kernel, then down +
+// moe_reduce kernel.  act: [M*k, I] BF16 scratch.
+bool decode_path_fits(int64_t M, int H, int k, int I);
+// One-token path: a single persistent kernel (one workgroup per CU, grid
+// barrier between gate/up and down).  Needs the whole grid resident.
+bool token_path_fits(int64_t M, int H, int k, int32_t L, int I, int num_cus);
+int token_kernel_grid(int H, int k, int32_t L, int I);
+int device_cu_count();  // of the current device; 0 when there is none
+// barrier: 256 bytes of device memory, zero before the first launch; the
+// kernel leaves its count at zero.
+hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids, const float* topk_w, int k,
+                              int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s, const uint8_t* w2,
+                              const float* w2_s, int I, int fmt, float limit, uint16_t* act, void* barrier,
+                              uint16_t* out, hipStream_t stream, const LaunchHook* hook);
+hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
+                               int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
+                               const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
+                               uint16_t* out, hipStream_t stream, const LaunchHook* hook);
 
 }  // namespace bfp8

@@ -73,7 +73,8 @@ enum {
     BFP8MOE_FLAG_ROUTE_SINGLE_WG = 1u << 0,  /* route prep: one workgroup */
     BFP8MOE_FLAG_ROUTE_MULTI_WG = 1u << 1,   /* route prep: count -> scan+scatter over many workgroups */
     BFP8MOE_FLAG_LAYER_GENERAL = 1u << 2,    /* fused layer: staged general path */
-    BFP8MOE_FLAG_LAYER_DECODE = 1u << 3      /* fused layer: small-batch two-kernel path */
+    BFP8MOE_FLAG_LAYER_DECODE = 1u << 3,     /* fused layer: small-batch two-kernel path */
+    BFP8MOE_FLAG_LAYER_TOKEN = 1u << 4       /* fused layer: one-token single-kernel path */
 };
 
 /* Options of the fused layer.  Initialise with bfp8moe_opts_init(). */
@@ -84,10 +85,14 @@ typedef struct {
     int32_t expert_offset;      /* first global expert held locally [P2 Suppressed comments] */
     int32_t local_num_experts;  /* experts held locally (weights' leading dimension); 0 = all E */
     uint32_t flags;             /* BFP8MOE_FLAG_* (tests only); 0 = choose by shape */
+    void* const* stage_events;  /* profiling, NULL = off: host array of n+1 hipEvent_t (as void*) for a call
+                                   of n stages (fused_moe_block_fp8_stages); event i is recorded on the
+                                   stream before stage i, event n after the last.  Events are caller-owned.
+                                   For eager calls; not for use under stream capture. */
 } bfp8moe_opts_t;
 
 /* Fill *opts with the defaults: block_m 0, FP32 scales, no clamp, the full
- * expert range, no flags.  opts: host pointer. */
+ * expert range, no flags, no stage events.  opts: host pointer. */
 void bfp8moe_opts_init(bfp8moe_opts_t* opts);
 
 const char* bfp8moe_status_string(int status);
@@ -220,6 +225,17 @@ bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_
 /*  P4: moe_reduce; P2 Changes: route preparation]                            */
 /* ------------------------------------------------------------------------- */
 
+/* Number of stages (kernel launches, route preparation counted as one) a
+ * fused_moe_block_fp8 call with these sizes and options makes on the current
+ * device, and, when names is non-NULL, up to cap stage names (static strings)
+ * in order.  The one-token path has one stage ("decode_token"); the
+ * small-batch path two ("decode_gate_up_swiglu", "decode_down_reduce"); the
+ * general path six ("route_prepare", "quant_fp8", "gate_up_gemm",
+ * "silu_and_mul_quant", "down_gemm", "moe_reduce").  Returns -1 for arguments
+ * fused_moe_block_fp8 would reject. */
+int32_t fused_moe_block_fp8_stages(int64_t M, int32_t H, int32_t k, int32_t E, int32_t I,
+                                   const bfp8moe_opts_t* opts, const char** names, int32_t cap);
+
 /* Workspace (bytes) fused_moe_block_fp8 needs for these sizes and options. */
 size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32_t E, int32_t I,
                                           const bfp8moe_opts_t* opts);
@@ -233,8 +249,26 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
  *   down( silu_and_mul_quant( gate_up( quant_fp8(hidden) ) ) ).
  * The hidden states and the SwiGLU output are both quantised with
  * opts->scale_fmt.  H and I must be positive multiples of 128.  ws: device
- * workspace of at least fused_moe_block_fp8_workspace_size() bytes.
- * opts: host pointer (NULL = defaults). */
+ * workspace of at least fused_moe_block_fp8_workspace_size() bytes, 256-byte
+ * aligned.  Its first 8192 bytes hold grid-barrier state that must be ZERO
+ * before the first call with that workspace (allocate it zero-filled once);
+ * calls keep it valid, and no other use of the workspace touches those bytes,
+ * so one workspace serves any mix of calls.  Calls that share a
+ * workspace must not run concurrently.  opts: host pointer (NULL = defaults).
+ * Three implementations, chosen by shape unless a test flag forces one:
+ *   one token (M = 1, k <= 8, H <= 8192, I <= 512, and a grid of
+ *     max(min(k, L) * I/8, H/32) workgroups that fits one per compute unit):
+ *     a single persistent kernel -- route grouping, input quantisation,
+ *     gate/up GEMM, SwiGLU, then (after a grid barrier) the SwiGLU output's
+ *     quantisation, the down GEMM and moe_reduce, with the down weights
+ *     requested before the barrier;
+ *   small batch (M <= 8, k <= 8, H <= 8192, I <= 512): two kernels -- gate/up
+ *     GEMM with route grouping, input quantisation and SwiGLU fused; then the
+ *     SwiGLU output's quantisation, down GEMM and moe_reduce fused;
+ *   general: route prep -> quant_fp8 -> grouped GEMM -> silu_and_mul_quant_fp8
+ *     -> grouped GEMM -> moe_reduce.
+ * Forcing a path on a shape outside its limits returns
+ * BFP8MOE_ERR_UNSUPPORTED. */
 bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
                                      const float* topk_w, int32_t k, const uint8_t* w13, const float* w13_scale,
                                      const uint8_t* w2, const float* w2_scale, int32_t E, int32_t I,

@@ -38,9 +38,24 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_opts_layout_and_defaults():
-    assert ctypes.sizeof(_lib.Opts) == 24
+    assert ctypes.sizeof(_lib.Opts) == 32
     o = bfp8.opts()
     assert o.block_m == 0 and o.scale_fmt == 0 and math.isinf(o.clamp_limit) and o.flags == 0
+
+
+def test_stage_lists():
+    o = bfp8.opts()
+    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == ["decode_token"]
+    assert bfp8.fused_moe_stages(4, 7168, 8, 256, 256, o) == ["decode_gate_up_swiglu", "decode_down_reduce"]
+    assert bfp8.fused_moe_stages(512, 4096, 8, 256, 768, o)[2] == "gate_up_gemm"
+    assert len(bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_GENERAL))) == 6
+    with pytest.raises(bfp8.BFP8MoEError):
+        bfp8.fused_moe_stages(64, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_DECODE))
+    with pytest.raises(bfp8.BFP8MoEError):
+        bfp8.fused_moe_stages(2, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_TOKEN))
+    with pytest.raises(bfp8.BFP8MoEError):  # exclusive path flags
+        bfp8.fused_moe_stages(1, 7168, 8, 256, 256,
+                              bfp8.opts(flags=bfp8.FLAG_LAYER_TOKEN | bfp8.FLAG_LAYER_GENERAL))
 
 
 def test_max_blocks_formula():

@@ -31,10 +31,11 @@ def _oracle_on_tokens(c, hidden, ids, w, W, tokens, fmt, clamp):
     """Oracle output for the listed tokens, given device inputs: only the
     experts those tokens use are copied to the host."""
     ids_t = ids[tokens].cpu()
-    used = torch.unique(ids_t[ids_t >= 0])
+    live = (ids_t >= 0) & (ids_t < c.E)
+    used = torch.unique(ids_t[live])
     remap = torch.full((c.E,), -1, dtype=torch.int32)
     remap[used.long()] = torch.arange(used.numel(), dtype=torch.int32)
-    ids_local = torch.where(ids_t >= 0, remap[ids_t.clamp(min=0).long()], ids_t).to(torch.int32)
+    ids_local = torch.where(live, remap[ids_t.clamp(0, c.E - 1).long()], torch.full_like(ids_t, -1)).to(torch.int32)
     sel = used.to(dev()).long()
     out = O.fused_moe(hidden[tokens].cpu(), ids_local, w[tokens].cpu(), W.w13[sel].cpu(), W.w13_s[sel].cpu(),
                       W.w2[sel].cpu(), W.w2_s[sel].cpu(), scale_fmt=fmt, clamp=clamp)
@@ -72,16 +73,71 @@ def test_layer_matches_oracle(case):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
-@pytest.mark.parametrize("path", [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE])
+PATHS = [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE, bfp8.FLAG_LAYER_TOKEN]
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("case", ["tiny", "decode_m1", "decode_m4"])
 @pytest.mark.parametrize("fmt,clamp", [(bfp8.SCALE_FP32, math.inf), (bfp8.SCALE_UE8M0, 7.0)])
 def test_layer_paths_fmt_clamp(case, path, fmt, clamp):
     print_case("layer path", case, path, fmt, clamp)
     c, hidden, ids, w, W = _inputs(case, 1)
+    if path == bfp8.FLAG_LAYER_TOKEN and c.M != 1:
+        with pytest.raises(bfp8.BFP8MoEError) as ei:
+            _run(c, hidden, ids, w, W, flags=path)
+        assert ei.value.status == 2  # unsupported: the one-token path needs M = 1
+        return
     toks = list(range(c.M))
     ref = _oracle_on_tokens(c, hidden, ids, w, W, toks, fmt, clamp)
     out = _run(c, hidden, ids, w, W, scale_fmt=fmt, clamp_limit=clamp, flags=path)
     assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_one_token_masked_and_duplicate_experts(path):
+    # one token whose routes include masked ids (-1, out of range) and an
+    # expert chosen twice: every path must agree with the oracle
+    print_case("one token masked/duplicate", path)
+    c = synth.LAYER_CASES["decode_m1"]
+    hidden, ids, w, W = synth.layer_inputs(c, 5, device=dev())
+    ids = ids.clone()
+    ids[0, 2] = -1
+    ids[0, 5] = 999
+    ids[0, 6] = ids[0, 1]
+    used = sorted(set(ids[ids >= 0].tolist()) & set(range(c.E)))
+    for e in used:
+        if e not in W.real:
+            cw, sw = synth.block_fp8_weight(2 * c.I, c.H, "dup", e, device=dev())
+            W.w13[e].copy_(cw); W.w13_s[e].copy_(sw)
+            cw, sw = synth.block_fp8_weight(c.H, c.I, "dup2", e, device=dev())
+            W.w2[e].copy_(cw); W.w2_s[e].copy_(sw)
+    ref = _oracle_on_tokens(c, hidden, ids, w, W, [0], c.scale_fmt, c.clamp)
+    out = _run(c, hidden, ids, w, W, flags=path)
+    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+
+
+def test_workspace_shared_across_paths():
+    # one zero-filled workspace used by the one-token, small-batch and general
+    # paths in turn, twice: the barrier state survives every mix
+    print_case("workspace shared")
+    c = synth.LAYER_CASES["decode_m1"]
+    hidden, ids, w, W = synth.layer_inputs(c, 6, device=dev())
+    ref = _oracle_on_tokens(c, hidden, ids, w, W, [0], c.scale_fmt, c.clamp)
+    sizes = [bfp8.fused_moe_workspace_size(1, c.H, c.k, c.E, c.I, bfp8.opts(flags=f)) for f in PATHS]
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device=dev())
+    for _ in range(2):
+        for f in [bfp8.FLAG_LAYER_TOKEN, bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE, bfp8.FLAG_LAYER_TOKEN]:
+            out = bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E,
+                                           o=bfp8.opts(flags=f), ws=ws)
+            torch.cuda.synchronize()
+            assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+    # the barrier's expiry flag is clear and every workgroup flag matches the
+    # published generation
+    head = ws[:8192].view(torch.int32).cpu()
+    gen = int(head[0])
+    assert int(head[1]) == 0 and gen > 0
+    grid = int((head[32:] != 0).sum())
+    assert grid > 0 and (head[32:32 + grid] == gen).all()
 
 
 @pytest.mark.parametrize("path", [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE])
