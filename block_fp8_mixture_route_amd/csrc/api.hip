@@ -57,7 +57,6 @@ const char* const kGeneralStages[] = {"route_prepare", "quant_fp8", "gate_up_gem
 const char* const kDecodeStages[] = {"decode_gate_up_swiglu", "decode_down_reduce"};
 const char* const kTokenStages[] = {"decode_token"};
 enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
-constexpr size_t kBarrierBytes = 8192;  // grid-barrier state, reserved at the start of every workspace
 
 // CU count used for planning: the current device's, or MI355X's 256 when no
 // device is visible (host-only planning, e.g. sizing a workspace).
@@ -107,13 +106,18 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
     p.route_single = false;
   else
     p.route_single = bfp8::route_prep_single_fits(p.R, p.L);
-  size_t o_ = kBarrierBytes;
+  size_t o_ = bfp8::kTokenStateBytes;  // launch state of the one-token kernel comes first
   auto take = [&](size_t bytes) {
     size_t at = o_;
     o_ = align_up(o_ + bytes);
     return at;
   };
-  if (p.mode != kModeGeneral) {
+  if (p.mode == kModeToken) {
+    p.off_act = 0;
+    p.total = o_;
+    return;
+  }
+  if (p.mode == kModeDecode) {
     p.off_act = take(sizeof(uint16_t) * (size_t)p.R * I);
     p.total = o_;
     return;
@@ -382,9 +386,8 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   hook.events = o.stage_events;
   hook.n = o.stage_events ? (p.mode == kModeToken ? 2 : p.mode == kModeDecode ? 3 : 7) : 0;
   if (p.mode == kModeToken) {
-    uint16_t* act = reinterpret_cast<uint16_t*>(base + p.off_act);
     return hip_status(bfp8::launch_token_layer(hidden, H, topk_ids, topk_w, k, p.offset, p.L, w13, w13_scale, w2,
-                                               w2_scale, I, p.fmt, p.clamp, act, base, out, st, &hook),
+                                               w2_scale, I, p.fmt, p.clamp, base, out, st, &hook),
                       "fused_moe_block_fp8 (one token)");
   }
   if (p.mode == kModeDecode) {

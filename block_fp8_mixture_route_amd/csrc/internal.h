@@ -66,17 +66,19 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
 // Small-batch path of the fused layer: gate/up + SwiGLU kernel, then down +
 // moe_reduce kernel.  act: [M*k, I] BF16 scratch.
 bool decode_path_fits(int64_t M, int H, int k, int I);
-// One-token path: a single persistent kernel (one workgroup per CU, grid
-// barrier between gate/up and down).  Needs the whole grid resident.
+// One-token path: a single persistent kernel (one workgroup per CU; the
+// gate/up and down halves exchange the SwiGLU output through tagged words).
+// Needs the whole grid resident.
 bool token_path_fits(int64_t M, int H, int k, int32_t L, int I, int num_cus);
 int token_kernel_grid(int H, int k, int32_t L, int I);
 int device_cu_count();  // of the current device; 0 when there is none
-// barrier: 256 bytes of device memory, zero before the first launch; the
-// kernel leaves its count at zero.
+// Bytes of launch state the one-token kernel keeps at the start of every
+// workspace (zero before the first launch; launches keep it valid).
+constexpr size_t kTokenStateBytes = 172032;  // 168 KB
 hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids, const float* topk_w, int k,
                               int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s, const uint8_t* w2,
-                              const float* w2_s, int I, int fmt, float limit, uint16_t* act, void* barrier,
-                              uint16_t* out, hipStream_t stream, const LaunchHook* hook);
+                              const float* w2_s, int I, int fmt, float limit, void* state, uint16_t* out,
+                              hipStream_t stream, const LaunchHook* hook);
 hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
                                int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
                                const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,

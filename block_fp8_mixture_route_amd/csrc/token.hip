@@ -15,26 +15,28 @@
 // [P4 Pull request overview] the down projection ends with the top-k weighted
 // reduction, routes in order.
 //
-// Grid: one 1024-thread workgroup per compute unit, all resident.  Small
-// straight-line code per wave matters: a dispatch starts with a cold
-// instruction cache, so each wave handles one weight row (and up to four 1 KB
-// pieces of W2) instead of many unrolled rows.  Workgroup w serves
+// Grid: one 1024-thread workgroup per compute unit, all resident.  Workgroup w
+// serves
 //   gate/up unit w: active-expert slot w / (I/8) (experts in ascending order),
-//     gate rows n0 = 8 (w % (I/8)) .. n0+7 and up rows I+n0 .. I+n0+7;
-//   down unit w: output rows DR w .. DR w + DR - 1 for all k routes.
-// Timeline per workgroup:
-//   ids -> slot's expert -> W13 loads (one row per wave) -> hidden row
-//   quantised into LDS -> W2 loads (k x DL units of 1 KB, four per wave over
-//   waves 1..15) -> gate/up dot products (need W13 only) -> SwiGLU, act rows
-//   to global memory (wave 0, which holds no W2 loads and so waits only for
-//   its own stores) -> grid barrier -> act rows of the k routes quantised into
-//   LDS (waves 0..7) -> down dot products as the W2 data lands (waves 1..15)
-//   -> weighted reduction -> out.
-// The barrier and the act exchange overlap the tail of the W2 stream.  Every
-// load is issued unconditionally (clamped addresses, counts fixed at compile
-// time) and the W2 loads share one straight-line branch with the gate/up work
-// of their waves, so that the compiler's waits for W13 data never include the
-// W2 loads issued after it.
+//     gate rows n0 = 8 (w % (I/8)) .. n0+7 and up rows I+n0 .. I+n0+7, one row
+//     per wave;
+//   down unit w: output rows DR w .. DR w + DR - 1 for all k routes, as k x DL
+//     pieces of 1 KB spread four per wave.
+// Every wave runs the same straight-line load sequence -- block-scale tables,
+// its W13 row, its four W2 pieces -- so that the waits the compiler places
+// for the W13 data never include the W2 loads issued after them (the memory
+// counter is in order), and the W2 stream overlaps the gate/up work.
+//
+// No grid barrier: the SwiGLU outputs are written as 8-byte words holding two
+// BF16 values and a 32-bit launch tag, into state kept at the start of the
+// workspace.  A consumer polls the words it needs until every tag equals the
+// current launch's tag, so data and completion travel in one store.  The tag
+// of a launch is gen + 1, where gen is read by every workgroup at its start;
+// each workgroup then records that it has read gen, and workgroup 0 advances
+// gen once every workgroup has done so.  Zero-filled state is valid, tags
+// never repeat within 2^32 launches, and no other use of the workspace
+// touches this state.  Bounded waits: a wait that runs out sets an expiry
+// word and lets the kernel finish.
 #include "device.h"
 #include "internal.h"
 
@@ -42,30 +44,40 @@ namespace bfp8 {
 
 namespace {
 
-constexpr int kThreads = 1024;  // 16 waves: one W13 row each; waves 8..15 also one route's W2 rows
+constexpr int kThreads = 1024;  // 16 waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxK = 8;
 constexpr int kMaxH = 8192;
 constexpr int kMaxRowLoads = kMaxH / 1024;  // 1 KB loads per W13 row
 constexpr int kMaxI = 512;
 constexpr int kMaxDownLoads = 8;            // 1 KB W2 loads per route per workgroup
-constexpr int kDownUnitsPerWave = 4;        // (route, 1 KB chunk) W2 units per wave 1..15
-constexpr int kMaxGrid = 1024;
+constexpr int kW2Units = 8;                 // (route, 1 KB piece) W2 units per down wave
+constexpr int kMaxGrid = 512;               // 64 flags per down wave
+constexpr int kReplicas = 4;                // copies of the polled state, read by workgroup b from copy b % 4
+constexpr int kTabSlots = 2 * (kMaxH / 128) + kMaxK * 2 * (kMaxI / 128) + 1;
 
-typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-// Grid barrier state, at the start of the workspace.  Generation-numbered
-// flags: each workgroup publishes gen+1 in its own slot, workgroup 0 waits
-// for all of them and then publishes gen+1 itself; everything stays
-// consistent across launches without a reset.  Zero-filled memory is a valid
-// initial state.
-struct TokenBarrier {
-  uint32_t gen;
-  uint32_t expired;
-  uint32_t pad[30];
-  uint32_t flag[kMaxGrid];
+// Launch state at the start of the workspace.  Words that many workgroups
+// poll at once are kept in kReplicas copies so that no single memory line
+// serves the whole grid.  The SwiGLU output depends only on the expert and
+// the column (one token), so it is kept per active-expert slot: row s holds
+// slot s's I columns as 64-bit words.  Workgroup (slot s, slice q) writes its
+// 8 columns as one 64-byte piece from one wave.  Every write here is a whole
+// 64-byte piece: small writes that many workgroups aim at one memory line
+// are serialised by the memory system and stall the weight stream.  A
+// producer's tagged piece also shows that it has read gen; only workgroups
+// without a slot write a separate flag.
+struct TokenState {
+  uint32_t gen[kReplicas][32];               // tag of the last completed launch, one copy per 128-byte line
+  uint32_t expired;                          // set when a bounded wait ran out
+  uint32_t pad[31];
+  uint32_t pad2[(8192 - kReplicas * 128 - 128) / 4];
+  uint32_t flag[kMaxGrid][16];               // workgroups without a slot: 64 bytes of tag once they have read gen
+  uint64_t act[kReplicas][kMaxK * kMaxI];    // [slot][column]: BF16 value (low 16 bits) + tag (high half)
 };
-static_assert(sizeof(TokenBarrier) <= 8192, "barrier header");
+static_assert(sizeof(TokenState) <= kTokenStateBytes, "token state");
+static_assert(offsetof(TokenState, flag) == 8192 && offsetof(TokenState, act) == 8192 + 64 * kMaxGrid, "layout");
 
 constexpr unsigned kSpinLimit = 1u << 22;
 
@@ -77,50 +89,6 @@ constexpr unsigned kSpinLimit = 1u << 22;
 __device__ __forceinline__ void wg_sync() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): vmcnt and expcnt left at their maximum
   __builtin_amdgcn_s_barrier();
-}
-
-// Grid barrier.  Before it, every act store of this workgroup must have been
-// acknowledged: the act writer (wave 0) waits for its vector memory counter,
-// the other waves hold only loads and do not wait.
-__device__ void grid_barrier(TokenBarrier* b, unsigned nwg, int wave) {
-  __shared__ uint32_t s_gen;
-  if (wave == 0) __builtin_amdgcn_s_waitcnt(0);
-  wg_sync();
-  if (threadIdx.x == 0) {
-    const uint32_t g = ATOMIC_LD(&b->gen);
-    __builtin_amdgcn_s_waitcnt(0);
-    ATOMIC_ST(&b->flag[blockIdx.x], g + 1);
-    s_gen = g;
-  }
-  wg_sync();
-  const uint32_t g = s_gen;
-  if (blockIdx.x == 0) {
-    for (unsigned i = threadIdx.x; i < nwg; i += kThreads) {
-      unsigned spins = 0;
-      while (ATOMIC_LD(&b->flag[i]) != g + 1) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins == kSpinLimit) {
-          ATOMIC_ST(&b->expired, 1u);
-          break;
-        }
-      }
-    }
-    wg_sync();
-    if (threadIdx.x == 0) {
-      __builtin_amdgcn_s_waitcnt(0);
-      ATOMIC_ST(&b->gen, g + 1);
-    }
-  } else if (threadIdx.x == 0) {
-    unsigned spins = 0;
-    while (ATOMIC_LD(&b->gen) == g) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins == kSpinLimit) {
-        ATOMIC_ST(&b->expired, 1u);
-        break;
-      }
-    }
-  }
-  wg_sync();
 }
 
 __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
@@ -139,263 +107,365 @@ __device__ __forceinline__ float amax8(const float (&f)[8]) {
   return m;
 }
 
-// Quantise 8 BF16-valued floats of one group (scale sc) and return the
-// decoded E4M3 values, i.e. dec(E4M3(x / sc)), as fp32.
-__device__ __forceinline__ void quant_dequant8(const float (&f)[8], float sc, float (&d)[8]) {
+// Quantise 8 BF16-valued floats of one group (scale sc) and store the E4M3
+// values dec(E4M3(x / sc)) as four FP16 pairs (every E4M3 value is exact in
+// FP16, subnormals included) at dst (LDS, 16-byte aligned).
+__device__ __forceinline__ void quant_store8(const float (&f)[8], float sc, h2* dst) {
   const uint2 q = encode8_scaled(f, sc);
-  const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
-  const v2f c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false), e = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
-  d[0] = a.x; d[1] = a.y; d[2] = b.x; d[3] = b.y; d[4] = c.x; d[5] = c.y; d[6] = e.x; d[7] = e.y;
+  const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)q.x, 1.0f, false);
+  const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)q.x, 1.0f, true);
+  const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)q.y, 1.0f, false);
+  const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)q.y, 1.0f, true);
+  dst[0] = a; dst[1] = b; dst[2] = c; dst[3] = d;
 }
 
-// sum_i dec(w_i) * a_i over 16 E4M3 weights (one 16-byte load) and 16 fp32
-// activations at p (LDS, 16-byte aligned); two interleaved fp32 chains.
-__device__ __forceinline__ float dot16(const uint4& w, const float* p) {
-  const float4 a0 = *reinterpret_cast<const float4*>(p);
-  const float4 a1 = *reinterpret_cast<const float4*>(p + 4);
-  const float4 a2 = *reinterpret_cast<const float4*>(p + 8);
-  const float4 a3 = *reinterpret_cast<const float4*>(p + 12);
-  const v2f w0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false), w1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-  const v2f w2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false), w3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-  const v2f w4 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.z, false), w5 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.z, true);
-  const v2f w6 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.w, false), w7 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.w, true);
-  float s0 = w0.x * a0.x, s1 = w0.y * a0.y;
-  s0 = __builtin_fmaf(w1.x, a0.z, s0); s1 = __builtin_fmaf(w1.y, a0.w, s1);
-  s0 = __builtin_fmaf(w2.x, a1.x, s0); s1 = __builtin_fmaf(w2.y, a1.y, s1);
-  s0 = __builtin_fmaf(w3.x, a1.z, s0); s1 = __builtin_fmaf(w3.y, a1.w, s1);
-  s0 = __builtin_fmaf(w4.x, a2.x, s0); s1 = __builtin_fmaf(w4.y, a2.y, s1);
-  s0 = __builtin_fmaf(w5.x, a2.z, s0); s1 = __builtin_fmaf(w5.y, a2.w, s1);
-  s0 = __builtin_fmaf(w6.x, a3.x, s0); s1 = __builtin_fmaf(w6.y, a3.y, s1);
-  s0 = __builtin_fmaf(w7.x, a3.z, s0); s1 = __builtin_fmaf(w7.y, a3.w, s1);
+// sum_i dec(w_i) * a_i over 16 E4M3 weights (one 16-byte load) and 16 E4M3
+// activations held as FP16 pairs at p (LDS, 16-byte aligned).  Weight bytes
+// are widened to FP16 pairs (exact), and each v_dot2 product of two E4M3
+// values is exact in FP32; only the FP32 additions round.  Two chains.
+__device__ __forceinline__ float dot16(const uint4& w, const h2* p) {
+  const h2* q = p;
+  const h2 a0 = q[0], a1 = q[1], a2 = q[2], a3 = q[3], a4 = q[4], a5 = q[5], a6 = q[6], a7 = q[7];
+  float s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.x, 1.0f, false), a0, 0.0f, false);
+  float s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.x, 1.0f, true), a1, 0.0f, false);
+  s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.y, 1.0f, false), a2, s0, false);
+  s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.y, 1.0f, true), a3, s1, false);
+  s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.z, 1.0f, false), a4, s0, false);
+  s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.z, 1.0f, true), a5, s1, false);
+  s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.w, 1.0f, false), a6, s0, false);
+  s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.w, 1.0f, true), a7, s1, false);
   return s0 + s1;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+// Sum (or max) over aligned groups of N lanes (N = 8, 16, 32 or 64), the
+// result in every lane of the group.  Within a 16-lane row the exchanges are
+// DPP moves (quad swaps, then the half-row and row mirrors); wider groups add
+// cross-row shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm 1,0,3,2
+  v += dpp<0x4E>(v);   // quad_perm 2,3,0,1
+  v += dpp<0x141>(v);  // row_half_mirror: the other quad of the half row
+  if (N >= 16) v += dpp<0x140>(v);  // row_mirror: the other half row
+  if (N >= 32) v += __shfl_xor(v, 16);
+  if (N >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  if (N >= 16) v = fmaxf(v, dpp<0x140>(v));
+  if (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
   return v;
 }
 
-// Gate/up dot product of one wave's row from its RL loads (lane-partial).
-template <int RL>
-__device__ __forceinline__ float gate_up_row(const uint4 (&wa)[RL], const float* s_af, const float* s_as,
-                                             const float* wsc, int H, int lane) {
-  float acc = 0.0f;
-#pragma unroll
-  for (int c = 0; c < RL; c++) {
-    const int kof = 1024 * c + 16 * lane;
-    const int kc = min(kof, H - 16);
-    const float sc = kof < H ? s_as[kc / 128] * wsc[kc / 128] : 0.0f;
-    acc = __builtin_fmaf(dot16(wa[c], s_af + kc), sc, acc);
-  }
-  return acc;
+// Two BF16-valued floats of one group quantised with scale sc, returned as
+// the FP16 pair of their E4M3 values (same rounding as quant_store8).
+__device__ __forceinline__ h2 quant2(float a, float b, float sc) {
+  const double rs = 1.0 / (double)sc;
+  const int q = __builtin_amdgcn_cvt_pk_fp8_f32((float)((double)a * rs), (float)((double)b * rs), 0, false);
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, 1.0f, false);
 }
 
-template <int RL, int DL>
+// Down wave d (0..7): wait until every SwiGLU word of its groups gi = d,
+// d + 8, ... (route j = gi / (I/128), group g, read from the row of route
+// j's slot) carries tag T -- and, in
+// workgroup 0, until flags 64 d .. 64 d + 63 do -- then quantise the groups
+// into LDS.  Lane l takes columns 2l and 2l + 1 of a group.  All loads of a
+// round go out together; the first round also waits for the wave's W2 data,
+// which the memory counter returns first.
+template <int I>
+__device__ __forceinline__ void take_groups(TokenState* st, int rep, int d, int k, const int* s_e, const int* s_slot,
+                                           int n_slots, uint32_t T, int fmt, h2 (*s_qh)[I / 2],
+                                           float (*s_qs)[I / 128], int lane) {
+  constexpr int GI = I / 128;
+  constexpr int NG = GI;  // groups per down wave at k = 8
+  bool live[NG];
+  const uint64_t* src[NG];
+#pragma unroll
+  for (int m = 0; m < NG; m++) {
+    const int gi = d + 8 * m;
+    const int j = min(gi / GI, k - 1), g = gi - (gi / GI) * GI;
+    live[m] = gi < k * GI && s_e[j] >= 0;
+    src[m] = &st->act[rep][s_slot[j] * kMaxI + g * 128 + 2 * lane];
+  }
+  const bool chk_flags = blockIdx.x == 0 && 64 * d < (int)gridDim.x;
+  const int fi = min(64 * d + lane, (int)gridDim.x - 1);
+  const bool fi_has_slot = fi / (I / 8) < n_slots;  // such a workgroup's SwiGLU piece is checked instead
+  uint64_t w[NG][2];
+  unsigned spins = 0;
+#pragma nounroll
+  for (;;) {
+#pragma unroll
+    for (int m = 0; m < NG; m++) {
+      w[m][0] = ATOMIC_LD(src[m]);
+      w[m][1] = ATOMIC_LD(src[m] + 1);
+    }
+    const uint32_t f = ATOMIC_LD(&st->flag[fi][0]);
+    bool ok = !chk_flags || fi_has_slot || f == T;
+#pragma unroll
+    for (int m = 0; m < NG; m++)
+      ok = ok && (!live[m] || ((uint32_t)(w[m][0] >> 32) == T && (uint32_t)(w[m][1] >> 32) == T));
+    if (__all(ok)) break;
+    if (++spins == kSpinLimit) {
+      ATOMIC_ST(&st->expired, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (int m = 0; m < NG; m++) {
+    if (!live[m]) continue;
+    const int gi = d + 8 * m, j = gi / GI, g = gi - j * GI;
+    const float a0 = bf16_to_f32((uint32_t)w[m][0] & 0xFFFFu), a1 = bf16_to_f32((uint32_t)w[m][1] & 0xFFFFu);
+    const float sc = group_scale(group_max<64>(fmaxf(fabsf(a0), fabsf(a1))), fmt);
+    s_qh[j][g * 64 + lane] = quant2(a0, a1, sc);
+    if (lane == 0) s_qs[j][g] = sc;
+  }
+}
+
+template <int RL, int I>
 __global__ __launch_bounds__(kThreads) void token_layer_kernel(
     const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
     int k, int32_t offset, int32_t L, const uint8_t* __restrict__ w13, const float* __restrict__ w13_s,
-    const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int I, int fmt, float limit, int clamp,
-    int down_rows, uint16_t* __restrict__ act, TokenBarrier* bar, uint16_t* __restrict__ out) {
-  __shared__ int s_e[kMaxK];
+    const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int fmt, float limit, int clamp,
+    int down_rows, int DL, uint32_t dl_magic, uint32_t tab_magic, TokenState* st, uint16_t* __restrict__ out) {
+  constexpr int GI = I / 128;
+  constexpr int kSlices = I / 8;     // gate/up units per expert
+  constexpr int kRpl = 1024 / I;     // W2 rows per 1 KB load
+  constexpr int kLpr = I / 16;       // lanes per W2 row
+  __shared__ __align__(16) int s_e[kMaxK];
+  __shared__ int s_slot[kMaxK];                    // active-expert slot of each route
   __shared__ float s_w[kMaxK];
-  __shared__ int s_expert;
-  __shared__ uint32_t s_route_mask;
-  __shared__ __align__(16) float s_af[kMaxH];       // dequantised hidden row
-  __shared__ float s_as[kMaxH / 128];               // its group scales
-  __shared__ float s_rows[16];                      // gate/up row totals
-  __shared__ __align__(16) float s_qf[kMaxK][kMaxI];  // dequantised act rows
-  __shared__ float s_qs[kMaxK][kMaxI / 128];
+  __shared__ uint32_t s_tag;
+  __shared__ uint32_t s_pub[8];                    // this workgroup's 8 SwiGLU columns (BF16)
+  __shared__ int s_pub_count;
+  __shared__ int s_expert, s_nslots;
+  __shared__ __align__(16) h2 s_ah[kMaxH / 2];     // quantised hidden row (E4M3 values as FP16)
+  __shared__ float s_as[kMaxH / 128];              // its group scales
+  __shared__ __align__(16) h2 s_qh[kMaxK][I / 2];  // quantised SwiGLU rows (E4M3 values as FP16)
+  __shared__ float s_qs[kMaxK][GI];
   __shared__ float s_y[kMaxK][64];
-  __shared__ float s_tab[2 * (kMaxH / 128) + kMaxK * 2 * (kMaxI / 128)];  // block-scale tables
+  __shared__ float s_tab[kTabSlots];               // block-scale tables (+ a spare slot)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = H / 128, GI = I / 128;
-  const int slices = I / 8;
-  const int slot = blockIdx.x / slices;
-  const int n0 = (blockIdx.x - slot * slices) * 8;
-  const int rpl = 1024 / I;                       // W2 rows per 1 KB load
-  const int lpr = I / 16;                         // lanes per W2 row
-  const int d0 = blockIdx.x * down_rows;
+  const int G = H / 128;
+  const int slot = blockIdx.x / kSlices;
+  const int n0 = (blockIdx.x - slot * kSlices) * 8;
+  const int d0 = blockIdx.x * down_rows;  // >= H: no down unit
   const int d_end = min(H, d0 + down_rows);
   const int l16 = tid & 15;
+  const int rep = blockIdx.x % kReplicas;
 
-  // 0. routing and the hidden row (group tid/16, 8 values per lane): issued first
-  int e_mine = -1;
-  if (tid < k) {
-    const int64_t e = (int64_t)ids[tid] - offset;
-    e_mine = (e >= 0 && e < L) ? (int)e : -1;
-    s_w[tid] = topk_w[tid];
-    s_e[tid] = e_mine;
-  }
+  // 0. the hidden row (group tid/16, 8 values per lane), the routing through
+  //    scalar loads (one request per wave, not one per lane) and, in wave 0,
+  //    gen.  The hidden load is unconditional (clamped index): a vector load
+  //    in a branch makes the compiler wait for it where the branch joins.
   const int hg = min(tid >> 4, G - 1);
   const uint4 hv = *reinterpret_cast<const uint4*>(hidden + (size_t)hg * 128 + l16 * 8);
+  int32_t id_raw[kMaxK];
+  float w_raw[kMaxK];
+#pragma unroll
+  for (int r = 0; r < kMaxK; r++) {
+    id_raw[r] = r < k ? ids[r] : -1;
+    w_raw[r] = r < k ? topk_w[r] : 0.0f;
+  }
+  uint32_t gen = 0;
+  if (wave == 0) gen = ATOMIC_LD(&st->gen[rep][0]);
 
-  // 1. this workgroup's active-expert slot (distinct live experts, ascending)
-  if (tid == 0) { s_expert = -1; s_route_mask = 0; }
+  // 1. quantise the hidden row into LDS while the routing settles
+  if ((tid >> 4) < G) {
+    float f[8];
+    unpack8(hv, f);
+    const float sc = group_scale(max_over_16(amax8(f)), fmt);
+    quant_store8(f, sc, s_ah + (hg * 128 + l16 * 8) / 2);
+    if (l16 == 0) s_as[hg] = sc;
+  }
+  if (tid < kMaxK) {
+    int32_t id = id_raw[0];
+    float wt = w_raw[0];
+#pragma unroll
+    for (int r = 1; r < kMaxK; r++)
+      if (tid == r) {
+        id = id_raw[r];
+        wt = w_raw[r];
+      }
+    const int64_t e = (int64_t)id - offset;
+    s_e[tid] = (tid < k && e >= 0 && e < L) ? (int)e : -1;
+    s_w[tid] = wt;
+  }
+  if (tid == 0) {
+    s_tag = gen + 1;
+    s_pub_count = 0;
+    s_expert = -1;
+  }
   wg_sync();
-  if (tid < k && e_mine >= 0) {
-    bool first = true;
+
+  // 2. this workgroup's active-expert slot: the distinct live experts in
+  //    ascending order.  Lane r < k of wave 0 works out route r's rank
+  //    (vector code: the scalar unit is shared by all waves of the CU).
+  if (wave == 0) {
+    const int r = min(lane, kMaxK - 1);
+    const int er = s_e[r];
+    bool first = lane < kMaxK && er >= 0;
     int rank = 0;
-    for (int r = 0; r < k; r++) {
-      const int o = s_e[r];
-      if (r < tid && o == e_mine) first = false;
-      bool o_first = o >= 0;
-      for (int q = 0; q < r; q++) o_first = o_first && (s_e[q] != o);
-      rank += (o_first && o < e_mine) ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < kMaxK; q++) {
+      const int eq = s_e[q];
+      first = first && !(q < r && eq == er);
+      bool q_first = eq >= 0;
+#pragma unroll
+      for (int p = 0; p < q; p++) q_first = q_first && s_e[p] != eq;
+      rank += (q_first && eq < er) ? 1 : 0;
     }
-    if (first && rank == slot) s_expert = e_mine;
+    const uint64_t firsts = __ballot(first);
+    if (lane < kMaxK) s_slot[lane] = rank;  // a route's expert has this rank among the distinct live experts
+    if (first && rank == slot) s_expert = er;
+    if (lane == 0) s_nslots = __popcll(firsts);
   }
   wg_sync();
   const int e = __builtin_amdgcn_readfirstlane(s_expert);  // -1: no gate/up unit
-  if (tid < k && e >= 0 && e_mine == e) atomicOr(&s_route_mask, 1u << tid);
+  const int n_slots = __builtin_amdgcn_readfirstlane(s_nslots);
+  const uint32_t T = s_tag;
 
-  // 2. scale tables: W13 block scales of the gate and up row blocks (threads
-  //    0..2G-1), W2 block scales of this unit's (at most two) row blocks for
-  //    every route (threads 512..).  One unconditional load per thread.
+  // 3. block-scale tables, one load per thread: W13 scales of
+  //    the gate and up row blocks (entries 0 .. 2G-1), then the W2 scales of
+  //    this unit's (at most two) row blocks for every route.  A barrier puts
+  //    them ahead of every weight load of the workgroup.
   const int e_ld = e >= 0 ? e : 0;  // a workgroup without a slot loads expert 0 and discards it
   const int blk_gate = n0 / 128, blk_up = (I + n0) / 128;
   const int rb0 = min(d0, H - 1) / 128, rb1 = min(max(d_end - 1, d0), H - 1) / 128;
+  const int n_tab = 2 * G + k * 2 * GI;
   float tab;
-  int tab_slot;
   {
-    const bool is13 = tid < 512;
-    const int t13 = min(tid, 2 * G - 1);
-    const int b13 = t13 < G ? blk_gate : blk_up, g13 = t13 < G ? t13 : t13 - G;
-    const int q = min(max(tid - 512, 0), 2 * kMaxK * GI - 1);
-    const int j2 = min(q / (2 * GI), k - 1), which = (q / GI) & 1, g2 = q % GI;
-    const int e2 = s_e[j2] >= 0 ? s_e[j2] : 0;
-    const float* src = is13 ? w13_s + ((size_t)e_ld * (2 * I / 128) + b13) * G + g13
-                            : w2_s + ((size_t)e2 * G + (which ? rb1 : rb0)) * GI + g2;
+    const int t = tid - n_tab * (int)(((uint32_t)tid * tab_magic) >> 20);  // tid mod n_tab: threads past the tables repeat entries
+    const float* src;
+    if (t < 2 * G) {
+      src = w13_s + ((size_t)e_ld * (2 * I / 128) + (t < G ? blk_gate : blk_up)) * G + (t < G ? t : t - G);
+    } else {
+      const int q = t - 2 * G;
+      const int j = q / (2 * GI), which = (q / GI) & 1, g2 = q % GI;
+      const int ej = s_e[j] >= 0 ? s_e[j] : 0;
+      src = w2_s + ((size_t)ej * G + (which ? rb1 : rb0)) * GI + g2;
+    }
     tab = *src;
-    tab_slot = is13 ? (tid < 2 * G ? tid : -1) : (q == tid - 512 ? 2 * G + q : -1);
-  }
-
-  // 3. W13: this wave's row (gate row n0 + w for w < 8, up row I + n0 + w - 8)
-  uint4 wa[RL];
-  {
-    const int row = wave < 8 ? n0 + wave : I + n0 + (wave - 8);
-    const uint8_t* src = w13 + ((size_t)e_ld * 2 * I + row) * H;
-#pragma unroll
-    for (int c = 0; c < RL; c++) wa[c] = *reinterpret_cast<const uint4*>(src + min(1024 * c + 16 * lane, H - 16));
   }
   __builtin_amdgcn_sched_barrier(0);
-
-  // 4. quantise the hidden row, dequantised into LDS; the tables land in LDS
-  if ((tid >> 4) < G) {
-    float f[8], d[8];
-    unpack8(hv, f);
-    const float sc = group_scale(max_over_16(amax8(f)), fmt);
-    quant_dequant8(f, sc, d);
-    float* dst = s_af + hg * 128 + l16 * 8;
-    *reinterpret_cast<float4*>(dst) = make_float4(d[0], d[1], d[2], d[3]);
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(d[4], d[5], d[6], d[7]);
-    if (l16 == 0) s_as[hg] = sc;
-  }
-  if (tab_slot >= 0) s_tab[tab_slot] = tab;
-  wg_sync();
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 5. gate/up dot products; waves 1..15 first issue their W2 units, in the
-  //    same straight-line branch.  Unit u = (wave - 1) + 15 i (i < 4) is route
-  //    u / DL, 1 KB chunk u % DL of the down rows; every wave issues exactly
-  //    four loads (units past k * DL, masked routes and missing routes load a
-  //    valid row and are discarded).
-  float part;
-  uint4 wb[kDownUnitsPerWave];
-  const float* wsc = s_tab + (wave < 8 ? 0 : G);
-  if (wave >= 1) {
-#pragma unroll
-    for (int i = 0; i < kDownUnitsPerWave; i++) {
-      const int u = min((wave - 1) + 15 * i, k * DL - 1);
-      const int j = u / DL, c = u - j * DL;
-      const int ee = s_e[j] >= 0 ? s_e[j] : 0;
-      const int row = min(d0 + c * rpl + lane / lpr, H - 1);
-      wb[i] = *reinterpret_cast<const uint4*>(w2 + ((size_t)ee * H + row) * I + 16 * (lane % lpr));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    part = gate_up_row<RL>(wa, s_af, s_as, wsc, H, lane);
-  } else {
-    part = gate_up_row<RL>(wa, s_af, s_as, wsc, H, lane);
-  }
-  {
-    const float t = wave_sum(part);
-    if (lane == 0) s_rows[wave] = t;
-  }
   wg_sync();
 
-  // 6. SwiGLU on the BF16 gate/up values; act rows stored by wave 0
-  if (e >= 0 && wave == 0 && lane < 2 * kMaxK) {
-    const uint32_t mask = s_route_mask;
-    const int r_idx = lane >> 1, half = lane & 1;  // lane pairs: route, 4 of the 8 columns
-    int r = -1, cnt = 0;
-    for (int q = 0; q < k; q++)
-      if ((mask >> q) & 1) {
-        if (cnt == r_idx) r = q;
-        cnt++;
-      }
-    if (r >= 0) {
-      uint32_t h[4];
+  if (wave >= 8) {
+    s_tab[kTabSlots - 1] = tab;  // the spare slot: keeps this wave's table load out of any branch
+    wg_sync();
+    if (d0 >= H) return;
+    // 4. down wave w: W2 units u = (w - 8) + 8 i, route u / DL, 1 KB piece
+    //    u % DL of the down rows, requested after every W13 load
+    uint4 wb[kW2Units];
+    const int kof = 16 * (lane % kLpr);
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int i = 4 * half + v;
-        const float g = bf16_to_f32(f32_to_bf16(s_rows[i]));
-        const float u = bf16_to_f32(f32_to_bf16(s_rows[8 + i]));
-        h[v] = f32_to_bf16(swiglu_bf16(g, u, limit, clamp != 0));
-      }
-      const uint64_t o = (uint64_t)(h[0] | (h[1] << 16)) | ((uint64_t)(h[2] | (h[3] << 16)) << 32);
-      ATOMIC_ST(reinterpret_cast<uint64_t*>(act + (size_t)r * I + n0 + 4 * half), o);
+    for (int i = 0; i < kW2Units; i++) {
+      const int u = min((wave - 8) + 8 * i, k * DL - 1);
+      const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
+      const int ej = s_e[j] >= 0 ? s_e[j] : 0;
+      const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
+      if ((wave - 8) + 8 * i < k * DL) wb[i] = *reinterpret_cast<const uint4*>(w2 + ((size_t)ej * H + row) * I + kof);
     }
-  }
 
-  // 7. every act row is complete past this point
-  grid_barrier(bar, gridDim.x, wave);
-  if (d0 >= H) return;
+    // 6. SwiGLU rows into LDS, quantised
+    take_groups<I>(st, rep, wave - 8, k, s_e, s_slot, n_slots, T, fmt, s_qh, s_qs, lane);
+    wg_sync();
 
-  // 8. the k act rows, quantised per group of 128 and dequantised into LDS,
-  //    by waves 0..7 (one group per 16 lanes; waves 8..15 wait for W2 data)
-  if (wave < 8) {
-    const int gid = tid >> 4;
-    if (gid < k * GI) {
-      const int j = gid / GI, g = gid - j * GI;
-      if (s_e[j] >= 0) {
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(act + (size_t)j * I + g * 128 + l16 * 8);
-        const uint64_t a0 = ATOMIC_LD(src), a1 = ATOMIC_LD(src + 1);
-        const uint4 v = make_uint4((uint32_t)a0, (uint32_t)(a0 >> 32), (uint32_t)a1, (uint32_t)(a1 >> 32));
-        float f[8], d[8];
-        unpack8(v, f);
-        const float sc = group_scale(max_over_16(amax8(f)), fmt);
-        quant_dequant8(f, sc, d);
-        float* dst = &s_qf[j][g * 128 + l16 * 8];
-        *reinterpret_cast<float4*>(dst) = make_float4(d[0], d[1], d[2], d[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(d[4], d[5], d[6], d[7]);
-        if (l16 == 0) s_qs[j][g] = sc;
-      }
-    }
-  }
-  wg_sync();
-
-  // 9. down projection: each of waves 1..15 finishes its W2 units
-  if (wave >= 1) {
+    // 7. down projection of this wave's units (lanes kLpr r .. kLpr r +
+    //    kLpr - 1 hold row r of a piece), reduced together; live units kept
+    float v[kW2Units];
 #pragma unroll
-    for (int i = 0; i < kDownUnitsPerWave; i++) {
-      const int u = (wave - 1) + 15 * i;
-      if (u >= k * DL) break;
-      const int j = u / DL, c = u - j * DL;
-      if (s_e[j] < 0) continue;
-      const int kof = 16 * (lane % lpr);
-      const int row = min(d0 + c * rpl + lane / lpr, H - 1);
+    for (int i = 0; i < kW2Units; i++) {
+      const int u = min((wave - 8) + 8 * i, k * DL - 1);
+      const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
+      const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
       const float w2sc = s_tab[2 * G + (j * 2 + (row / 128 == rb0 ? 0 : 1)) * GI + kof / 128];
-      float v = dot16(wb[i], &s_qf[j][kof]) * (s_qs[j][kof / 128] * w2sc);
-      for (int m = lpr / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-      const int rl = c * rpl + lane / lpr;
-      if (lane % lpr == 0 && d0 + rl < d_end) s_y[j][rl] = bf16_to_f32(f32_to_bf16(v));
+      v[i] = dot16(wb[i], &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * w2sc);
     }
-  }
-  wg_sync();
+#pragma unroll
+    for (int i = 0; i < kW2Units; i++) v[i] = group_sum<kLpr>(v[i]);
+#pragma unroll
+    for (int i = 0; i < kW2Units; i++) {
+      const int u = (wave - 8) + 8 * i;
+      const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
+      const int rl = c * kRpl + lane / kLpr;
+      if (u < k * DL && lane % kLpr == 0 && d0 + rl < d_end && s_e[j] >= 0) s_y[j][rl] = bf16_to_f32(f32_to_bf16(v[i]));
+    }
+    wg_sync();
+    } else {
+    // 4. gate/up wave w: column n = n0 + w, i.e. gate row n and up row I + n
+    //    of expert e, requested first
+    uint4 wg[RL], wu[RL];
+    {
+      // every chunk but the last lies inside the row; the last is clamped
+      const uint8_t* gsrc = w13 + ((size_t)e_ld * 2 * I + n0 + wave) * H;
+      const uint8_t* usrc = gsrc + (size_t)I * H;
+      const int last = min(1024 * (RL - 1) + 16 * lane, H - 16);
+#pragma unroll
+      for (int c = 0; c < RL; c++) {
+        const int off = c < RL - 1 ? 1024 * c + 16 * lane : last;
+        wg[c] = *reinterpret_cast<const uint4*>(gsrc + off);
+        wu[c] = *reinterpret_cast<const uint4*>(usrc + off);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every W13 load goes out before the table wait
+    s_tab[min(tid, kTabSlots - 1)] = tab;  // threads past the tables write the spare slot
+    wg_sync();
 
-  // 10. weighted reduction over the routes, j ascending
+    // 5. gate and up dot products as the data lands, then SwiGLU on their
+    //    BF16 values; lane r_idx publishes the column of its route (the
+    //    r_idx-th route whose expert is e) to every copy
+    float ag = 0.0f, au = 0.0f;
+#pragma unroll
+    for (int c = 0; c < RL; c++) {
+      const int kof = 1024 * c + 16 * lane;  // past H only in the last chunk: its terms are dropped
+      const float as = s_as[kof / 128];
+      float pg = dot16(wg[c], s_ah + kof / 2) * (as * s_tab[kof / 128]);
+      float pu = dot16(wu[c], s_ah + kof / 2) * (as * s_tab[G + kof / 128]);
+      if (c == RL - 1 && kof >= H) pg = pu = 0.0f;
+      ag += pg;
+      au += pu;
+    }
+    ag = group_sum<64>(ag);
+    au = group_sum<64>(au);
+    if (e >= 0) {
+      // the last of the 8 gate/up waves to finish writes the workgroup's
+      // 8 columns, tagged, to every copy
+      const float g = bf16_to_f32(f32_to_bf16(ag)), u = bf16_to_f32(f32_to_bf16(au));
+      const uint32_t h = f32_to_bf16(swiglu_bf16(g, u, limit, clamp != 0));
+      int done = 0;
+      if (lane == 0) {
+        s_pub[wave] = h;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        done = atomicAdd(&s_pub_count, 1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      }
+      done = __builtin_amdgcn_readfirstlane(done);
+      if (done == kWaves / 2 - 1 && lane < 8) {
+        const uint64_t word = (uint64_t)s_pub[lane] | ((uint64_t)T << 32);
+#pragma unroll
+        for (int x = 0; x < kReplicas; x++) ATOMIC_ST(&st->act[x][slot * kMaxI + n0 + lane], word);
+      }
+    }
+    if (e < 0 && wave == 0 && lane < 16) ATOMIC_ST(&st->flag[blockIdx.x][lane], T);
+    if (d0 >= H) return;  // the whole workgroup leaves: no down unit
+    wg_sync();  // the down waves have the SwiGLU rows in LDS
+    wg_sync();  // ... and the down rows in s_y
+  }
+  if (blockIdx.x == 0 && tid < kReplicas) ATOMIC_ST(&st->gen[tid][0], T);  // every workgroup has read gen
+
+  // 8. weighted reduction over the routes, j ascending
   if (tid < d_end - d0) {
     float a = 0.0f;
     for (int j = 0; j < k; j++)
@@ -430,39 +500,53 @@ bool token_path_fits(int64_t M, int H, int k, int32_t L, int I, int num_cus) {
   const int up = slots * (I / 8);
   const int dr = token_down_rows(H, I, up);
   if (dr > 64 || dr * I / 1024 > kMaxDownLoads) return false;
-  if (dr * I / 1024 != (H + 1023) / 1024) return false;  // kernels are instantiated for equal load counts
-  if (k * (dr * I / 1024) > 15 * kDownUnitsPerWave) return false;  // W2 units of waves 1..15
+  if (k * (dr * I / 1024) > 8 * kW2Units) return false;  // W2 units of the 8 down waves
   const int grid = token_kernel_grid(H, k, L, I);
   return grid <= num_cus && grid <= kMaxGrid;
 }
 
 hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids, const float* topk_w, int k,
                               int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s, const uint8_t* w2,
-                              const float* w2_s, int I, int fmt, float limit, uint16_t* act, void* barrier,
-                              uint16_t* out, hipStream_t stream, const LaunchHook* hook) {
+                              const float* w2_s, int I, int fmt, float limit, void* state, uint16_t* out,
+                              hipStream_t stream, const LaunchHook* hook) {
   const int clamp = __builtin_isfinite(limit) ? 1 : 0;
   const int slots = k < L ? k : L;
   const int dr = token_down_rows(H, I, slots * (I / 8));
   const int grid = token_kernel_grid(H, k, L, I);
   const int rl = (H + 1023) / 1024, dl = dr * I / 1024;
-  if (rl != dl || rl < 1 || rl > kMaxRowLoads) return hipErrorInvalidValue;  // token_path_fits rules this out
+  if (!(I == 128 || I == 256 || I == 512) || rl < 1 || rl > kMaxRowLoads || dl < 1 || dl > kMaxDownLoads || k * dl > 8 * kW2Units)
+    return hipErrorInvalidValue;  // token_path_fits rules these out
+  // exact quotients by multiply and shift: u / dl for u < 64 and t / n_tab for
+  // t < 1024 (the rounding error of the multiplier stays below one step)
+  const uint32_t dl_magic = (65536u + dl - 1) / dl;
+  const uint32_t n_tab = 2 * (H / 128) + k * 2 * (I / 128);
+  const uint32_t tab_magic = ((1u << 20) + n_tab - 1) / n_tab;
   if (hook) hook->before(0, stream);
-#define BFP8_TOKEN_CASE(N)                                                                                   \
+#define BFP8_TOKEN_CASE(N, II)                                                                               \
   case N:                                                                                                    \
-    hipLaunchKernelGGL((token_layer_kernel<N, N>), dim3(grid), dim3(kThreads), 0, stream, hidden, H, ids,    \
-                       topk_w, k, offset, L, w13, w13_s, w2, w2_s, I, fmt, limit, clamp, dr, act,           \
-                       static_cast<TokenBarrier*>(barrier), out);                                            \
+    hipLaunchKernelGGL((token_layer_kernel<N, II>), dim3(grid), dim3(kThreads), 0, stream, hidden, H, ids,   \
+                       topk_w, k, offset, L, w13, w13_s, w2, w2_s, fmt, limit, clamp, dr, dl, dl_magic,     \
+                       tab_magic, static_cast<TokenState*>(state), out);                                     \
     break;
-  switch (rl) {
-    BFP8_TOKEN_CASE(1)
-    BFP8_TOKEN_CASE(2)
-    BFP8_TOKEN_CASE(3)
-    BFP8_TOKEN_CASE(4)
-    BFP8_TOKEN_CASE(5)
-    BFP8_TOKEN_CASE(6)
-    BFP8_TOKEN_CASE(7)
-    BFP8_TOKEN_CASE(8)
+#define BFP8_TOKEN_RL(II)                                                                                    \
+  switch (rl) {                                                                                              \
+    BFP8_TOKEN_CASE(1, II)                                                                                   \
+    BFP8_TOKEN_CASE(2, II)                                                                                   \
+    BFP8_TOKEN_CASE(3, II)                                                                                   \
+    BFP8_TOKEN_CASE(4, II)                                                                                   \
+    BFP8_TOKEN_CASE(5, II)                                                                                   \
+    BFP8_TOKEN_CASE(6, II)                                                                                   \
+    BFP8_TOKEN_CASE(7, II)                                                                                   \
+    BFP8_TOKEN_CASE(8, II)                                                                                   \
   }
+  if (I == 128) {
+    BFP8_TOKEN_RL(128)
+  } else if (I == 256) {
+    BFP8_TOKEN_RL(256)
+  } else {
+    BFP8_TOKEN_RL(512)
+  }
+#undef BFP8_TOKEN_RL
 #undef BFP8_TOKEN_CASE
   hipError_t e = hipGetLastError();
   if (hook) hook->before(1, stream);

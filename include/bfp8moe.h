@@ -250,18 +250,20 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
  * The hidden states and the SwiGLU output are both quantised with
  * opts->scale_fmt.  H and I must be positive multiples of 128.  ws: device
  * workspace of at least fused_moe_block_fp8_workspace_size() bytes, 256-byte
- * aligned.  Its first 8192 bytes hold grid-barrier state that must be ZERO
- * before the first call with that workspace (allocate it zero-filled once);
- * calls keep it valid, and no other use of the workspace touches those bytes,
- * so one workspace serves any mix of calls.  Calls that share a
- * workspace must not run concurrently.  opts: host pointer (NULL = defaults).
+ * aligned.  Its first 172032 bytes hold launch state of the one-token kernel
+ * that must be ZERO before the first call with that workspace (allocate it
+ * zero-filled once); calls keep it valid, and no other use of the workspace
+ * touches those bytes, so one workspace serves any mix of calls.  Calls that
+ * share a workspace must not run concurrently.  opts: host pointer (NULL =
+ * defaults).
  * Three implementations, chosen by shape unless a test flag forces one:
  *   one token (M = 1, k <= 8, H <= 8192, I <= 512, and a grid of
  *     max(min(k, L) * I/8, H/32) workgroups that fits one per compute unit):
  *     a single persistent kernel -- route grouping, input quantisation,
- *     gate/up GEMM, SwiGLU, then (after a grid barrier) the SwiGLU output's
- *     quantisation, the down GEMM and moe_reduce, with the down weights
- *     requested before the barrier;
+ *     gate/up GEMM and SwiGLU, whose output words carry a launch tag; each
+ *     workgroup then waits for the tagged words it needs, quantises them and
+ *     runs its share of the down GEMM and moe_reduce, with its down weights
+ *     requested before the gate/up work;
  *   small batch (M <= 8, k <= 8, H <= 8192, I <= 512): two kernels -- gate/up
  *     GEMM with route grouping, input quantisation and SwiGLU fused; then the
  *     SwiGLU output's quantisation, down GEMM and moe_reduce fused;

@@ -118,7 +118,7 @@ def test_one_token_masked_and_duplicate_experts(path):
 
 def test_workspace_shared_across_paths():
     # one zero-filled workspace used by the one-token, small-batch and general
-    # paths in turn, twice: the barrier state survives every mix
+    # paths in turn, twice: the one-token launch state survives every mix
     print_case("workspace shared")
     c = synth.LAYER_CASES["decode_m1"]
     hidden, ids, w, W = synth.layer_inputs(c, 6, device=dev())
@@ -131,13 +131,20 @@ def test_workspace_shared_across_paths():
                                            o=bfp8.opts(flags=f), ws=ws)
             torch.cuda.synchronize()
             assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
-    # the barrier's expiry flag is clear and every workgroup flag matches the
-    # published generation
-    head = ws[:8192].view(torch.int32).cpu()
-    gen = int(head[0])
-    assert int(head[1]) == 0 and gen > 0
-    grid = int((head[32:] != 0).sum())
-    assert grid > 0 and (head[32:32 + grid] == gen).all()
+    # the expiry word is clear, every copy of gen holds the last launch's tag
+    # and no flag is ahead of it
+    st = _token_state(ws)
+    gen = int(st["gen"][0])
+    assert st["expired"] == 0 and gen > 0 and (st["gen"] == gen).all()
+    assert (st["flag"] <= gen).all()
+
+
+def _token_state(ws):
+    """The one-token kernel's launch state at the start of a workspace: gen
+    (4 copies, one per 128-byte line), the expiry word, and from byte 8192
+    one 64-byte flag piece per workgroup."""
+    head = ws[:8192 + 64 * 512].view(torch.int32).cpu()
+    return {"gen": head[0:128:32], "expired": int(head[128]), "flag": head[2048::16]}
 
 
 @pytest.mark.parametrize("path", [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE])
@@ -173,3 +180,47 @@ def test_layer_rejects_bad_arguments():
     small = torch.empty(16, dtype=torch.uint8, device=dev())
     with pytest.raises(bfp8.BFP8MoEError):
         bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E, ws=small)
+
+
+# one-token shapes other than the decode workload: every load count of the
+# kernel's W13 rows and W2 pieces, grids from 32 to 256 workgroups
+TOKEN_SHAPES = [
+    synth.LayerCase("tok_h256_i128_k2", M=1, E=8, k=2, H=256, I=128, routing="uniform"),
+    synth.LayerCase("tok_h2048_i128_k4", M=1, E=16, k=4, H=2048, I=128, routing="uniform"),
+    synth.LayerCase("tok_h4096_i128_k8", M=1, E=64, k=8, H=4096, I=128, routing="uniform"),
+    synth.LayerCase("tok_h3072_i512_k3", M=1, E=32, k=3, H=3072, I=512, routing="uniform"),
+    synth.LayerCase("tok_h8192_i256_k8", M=1, E=32, k=8, H=8192, I=256, routing="uniform"),
+]
+
+
+@pytest.mark.parametrize("c", TOKEN_SHAPES, ids=lambda c: c.name)
+def test_one_token_shapes(c):
+    print_case("one-token shape", c.name)
+    if bfp8.fused_moe_stages(1, c.H, c.k, c.E, c.I, bfp8.opts()) != ["decode_token"]:
+        pytest.skip("shape outside the one-token kernel on this device")
+    hidden, ids, w, W = synth.layer_inputs(c, 0, device=dev())
+    ref = _oracle_on_tokens(c, hidden, ids, w, W, [0], bfp8.SCALE_UE8M0, 7.0)
+    out = _run(c, hidden, ids, w, W, scale_fmt=bfp8.SCALE_UE8M0, clamp_limit=7.0, flags=bfp8.FLAG_LAYER_TOKEN)
+    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+
+
+def test_one_token_grid_changes_on_one_workspace():
+    # launches with different grids share one workspace: the tags and the
+    # per-workgroup flags stay consistent however the grid changes
+    print_case("one-token grid changes")
+    cases = [TOKEN_SHAPES[0], synth.LAYER_CASES["decode_m1"], TOKEN_SHAPES[1], TOKEN_SHAPES[0]]
+    data = []
+    for c in dict((c.name, c) for c in cases).values():
+        hidden, ids, w, W = synth.layer_inputs(c, 2, device=dev())
+        data.append((c.name, (c, hidden, ids, w, W, _oracle_on_tokens(c, hidden, ids, w, W, [0], c.scale_fmt, c.clamp))))
+    data = dict(data)
+    need = max(bfp8.fused_moe_workspace_size(1, c.H, c.k, c.E, c.I, bfp8.opts()) for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    for _ in range(2):
+        for c in cases:
+            c, hidden, ids, w, W, ref = data[c.name]
+            out = bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E,
+                                           o=bfp8.opts(flags=bfp8.FLAG_LAYER_TOKEN), ws=ws)
+            torch.cuda.synchronize()
+            assert normwise_err(bf16_np(out), ref) <= LAYER_TOL, c.name
+    assert _token_state(ws)["expired"] == 0  # no wait ran out
