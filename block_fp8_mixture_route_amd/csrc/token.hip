@@ -51,9 +51,9 @@ constexpr int kMaxH = 8192;
 constexpr int kMaxRowLoads = kMaxH / 1024;  // 1 KB loads per W13 row
 constexpr int kMaxI = 512;
 constexpr int kMaxDownLoads = 8;            // 1 KB W2 loads per route per workgroup
-constexpr int kW2Units = 8;                 // (route, 1 KB piece) W2 units per down wave
+constexpr int kW2PerWave = 8;               // (route, 1 KB piece) W2 units per down wave
 constexpr int kMaxGrid = 512;               // 64 flags per down wave
-constexpr int kReplicas = 4;                // copies of the polled state, read by workgroup b from copy b % 4
+constexpr int kReplicas = 8;                // copies of the polled state, read by workgroup b from copy b % 8
 constexpr int kTabSlots = 2 * (kMaxH / 128) + kMaxK * 2 * (kMaxI / 128) + 1;
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -62,19 +62,19 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 // poll at once are kept in kReplicas copies so that no single memory line
 // serves the whole grid.  The SwiGLU output depends only on the expert and
 // the column (one token), so it is kept per active-expert slot: row s holds
-// slot s's I columns as 64-bit words.  Workgroup (slot s, slice q) writes its
-// 8 columns as one 64-byte piece from one wave.  Every write here is a whole
-// 64-byte piece: small writes that many workgroups aim at one memory line
-// are serialised by the memory system and stall the weight stream.  A
-// producer's tagged piece also shows that it has read gen; only workgroups
-// without a slot write a separate flag.
+// slot s's I columns as 64-bit words of two columns each.  Workgroup (slot s,
+// slice q) writes its 8 columns as one 32-byte piece from one wave.  Writes
+// here are whole pieces from one wave: small writes that many workgroups aim
+// at one memory line are serialised by the memory system and stall the
+// weight stream.  A producer's tagged piece also shows that it has read gen;
+// only workgroups without a slot write a separate flag.
 struct TokenState {
   uint32_t gen[kReplicas][32];               // tag of the last completed launch, one copy per 128-byte line
   uint32_t expired;                          // set when a bounded wait ran out
   uint32_t pad[31];
   uint32_t pad2[(8192 - kReplicas * 128 - 128) / 4];
   uint32_t flag[kMaxGrid][16];               // workgroups without a slot: 64 bytes of tag once they have read gen
-  uint64_t act[kReplicas][kMaxK * kMaxI];    // [slot][column]: BF16 value (low 16 bits) + tag (high half)
+  uint64_t act[kReplicas][kMaxK * kMaxI / 2];  // [slot][column pair]: 2 BF16 (low half) + tag (high half)
 };
 static_assert(sizeof(TokenState) <= kTokenStateBytes, "token state");
 static_assert(offsetof(TokenState, flag) == 8192 && offsetof(TokenState, act) == 8192 + 64 * kMaxGrid, "layout");
@@ -174,19 +174,18 @@ __device__ __forceinline__ h2 quant2(float a, float b, float sc) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, 1.0f, false);
 }
 
-// Down wave d (0..7): wait until every SwiGLU word of its groups gi = d,
-// d + 8, ... (route j = gi / (I/128), group g, read from the row of route
-// j's slot) carries tag T -- and, in
-// workgroup 0, until flags 64 d .. 64 d + 63 do -- then quantise the groups
-// into LDS.  Lane l takes columns 2l and 2l + 1 of a group.  All loads of a
-// round go out together; the first round also waits for the wave's W2 data,
-// which the memory counter returns first.
+// Gate/up wave d (0..7), once it has published: wait until every SwiGLU
+// word of its groups gi = d, d + 8, ... (route j = gi / (I/128), group g,
+// read from the row of route j's slot) carries tag T -- and, in workgroup 0,
+// until the flags of workgroups 64 d .. 64 d + 63 without a slot do -- then
+// quantise the groups into LDS.  Lane l takes the word of columns 2l and
+// 2l + 1 of a group.  All loads of a round go out together.
 template <int I>
 __device__ __forceinline__ void take_groups(TokenState* st, int rep, int d, int k, const int* s_e, const int* s_slot,
                                            int n_slots, uint32_t T, int fmt, h2 (*s_qh)[I / 2],
                                            float (*s_qs)[I / 128], int lane) {
   constexpr int GI = I / 128;
-  constexpr int NG = GI;  // groups per down wave at k = 8
+  constexpr int NG = GI;  // groups per wave at k = 8
   bool live[NG];
   const uint64_t* src[NG];
 #pragma unroll
@@ -194,25 +193,21 @@ __device__ __forceinline__ void take_groups(TokenState* st, int rep, int d, int 
     const int gi = d + 8 * m;
     const int j = min(gi / GI, k - 1), g = gi - (gi / GI) * GI;
     live[m] = gi < k * GI && s_e[j] >= 0;
-    src[m] = &st->act[rep][s_slot[j] * kMaxI + g * 128 + 2 * lane];
+    src[m] = &st->act[rep][s_slot[j] * (kMaxI / 2) + g * 64 + lane];
   }
   const bool chk_flags = blockIdx.x == 0 && 64 * d < (int)gridDim.x;
   const int fi = min(64 * d + lane, (int)gridDim.x - 1);
   const bool fi_has_slot = fi / (I / 8) < n_slots;  // such a workgroup's SwiGLU piece is checked instead
-  uint64_t w[NG][2];
+  uint64_t w[NG];
   unsigned spins = 0;
 #pragma nounroll
   for (;;) {
 #pragma unroll
-    for (int m = 0; m < NG; m++) {
-      w[m][0] = ATOMIC_LD(src[m]);
-      w[m][1] = ATOMIC_LD(src[m] + 1);
-    }
+    for (int m = 0; m < NG; m++) w[m] = ATOMIC_LD(src[m]);
     const uint32_t f = ATOMIC_LD(&st->flag[fi][0]);
     bool ok = !chk_flags || fi_has_slot || f == T;
 #pragma unroll
-    for (int m = 0; m < NG; m++)
-      ok = ok && (!live[m] || ((uint32_t)(w[m][0] >> 32) == T && (uint32_t)(w[m][1] >> 32) == T));
+    for (int m = 0; m < NG; m++) ok = ok && (!live[m] || (uint32_t)(w[m] >> 32) == T);
     if (__all(ok)) break;
     if (++spins == kSpinLimit) {
       ATOMIC_ST(&st->expired, 1u);
@@ -224,10 +219,70 @@ __device__ __forceinline__ void take_groups(TokenState* st, int rep, int d, int 
   for (int m = 0; m < NG; m++) {
     if (!live[m]) continue;
     const int gi = d + 8 * m, j = gi / GI, g = gi - j * GI;
-    const float a0 = bf16_to_f32((uint32_t)w[m][0] & 0xFFFFu), a1 = bf16_to_f32((uint32_t)w[m][1] & 0xFFFFu);
+    const float a0 = bf16_to_f32((uint32_t)w[m] & 0xFFFFu), a1 = bf16_to_f32(((uint32_t)w[m] >> 16) & 0xFFFFu);
     const float sc = group_scale(group_max<64>(fmaxf(fabsf(a0), fabsf(a1))), fmt);
     s_qh[j][g * 64 + lane] = quant2(a0, a1, sc);
     if (lane == 0) s_qs[j][g] = sc;
+  }
+}
+
+typedef __attribute__((address_space(1))) const void* global_ptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// W2 units u = d + 8 i (down wave d = wave - 8) of the workgroup's down
+// rows, copied by direct-to-LDS loads into s_w2[u] (1 KB each): route u / DL,
+// 1 KB piece u % DL, i.e. kRpl rows of I bytes; lane l's 16 bytes land at
+// byte 16 l of the unit.  Units past the last repeat it (a cache hit);
+// masked routes read expert 0.  Completion is counted by the wave's memory
+// counter.
+template <int I>
+__device__ __forceinline__ void issue_w2(uint8_t* s_w2, int wave, int k, int DL, uint32_t dl_magic, const int* s_e,
+                                         const uint8_t* __restrict__ w2, int H, int d0, int lane) {
+  constexpr int kRpl = 1024 / I, kLpr = I / 16;
+  const uint8_t* src[kW2PerWave];
+#pragma unroll
+  for (int i = 0; i < kW2PerWave; i++) {
+    const int u = min((wave - 8) + 8 * i, k * DL - 1);
+    const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
+    const int ej = max(s_e[j], 0);
+    const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
+    src[i] = w2 + ((size_t)ej * H + row) * I + 16 * (lane % kLpr);
+  }
+#pragma unroll
+  for (int i = 0; i < kW2PerWave; i++)
+    __builtin_amdgcn_global_load_lds((global_ptr)src[i], (lds_ptr)(s_w2 + ((wave - 8) + 8 * i) * 1024), 16, 0, 0);
+}
+
+// Down projection of wave w's W2 units u = w + 16 i (read from LDS): each
+// row's dot product with the quantised SwiGLU row of its route, both block
+// scales applied per group, reduced over the row's lanes; live rows go to
+// s_y as BF16-valued floats.
+template <int I>
+__device__ __forceinline__ void down_units(const uint8_t* s_w2, int wave, int k, int DL, uint32_t dl_magic,
+                                           const int* s_e, const float* s_tab, const h2 (*s_qh)[I / 2],
+                                           const float (*s_qs)[I / 128], float (*s_y)[64], int G, int H, int d0,
+                                           int d_end, int rb0, int lane) {
+  constexpr int GI = I / 128, kRpl = 1024 / I, kLpr = I / 16;
+  constexpr int kUnits = 8 * kW2PerWave / kWaves;
+  const int kof = 16 * (lane % kLpr);
+  float v[kUnits];
+#pragma unroll
+  for (int i = 0; i < kUnits; i++) {
+    const int u = min(wave + kWaves * i, k * DL - 1);
+    const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
+    const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
+    const float w2sc = s_tab[2 * G + (j * 2 + (row / 128 == rb0 ? 0 : 1)) * GI + kof / 128];
+    const uint4 wv = *reinterpret_cast<const uint4*>(s_w2 + u * 1024 + 16 * lane);
+    v[i] = dot16(wv, &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * w2sc);
+  }
+#pragma unroll
+  for (int i = 0; i < kUnits; i++) v[i] = group_sum<kLpr>(v[i]);
+#pragma unroll
+  for (int i = 0; i < kUnits; i++) {
+    const int u = wave + kWaves * i;
+    const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
+    const int rl = c * kRpl + lane / kLpr;
+    if (u < k * DL && lane % kLpr == 0 && d0 + rl < d_end && s_e[j] >= 0) s_y[j][rl] = bf16_to_f32(f32_to_bf16(v[i]));
   }
 }
 
@@ -239,8 +294,6 @@ __global__ __launch_bounds__(kThreads) void token_layer_kernel(
     int down_rows, int DL, uint32_t dl_magic, uint32_t tab_magic, TokenState* st, uint16_t* __restrict__ out) {
   constexpr int GI = I / 128;
   constexpr int kSlices = I / 8;     // gate/up units per expert
-  constexpr int kRpl = 1024 / I;     // W2 rows per 1 KB load
-  constexpr int kLpr = I / 16;       // lanes per W2 row
   __shared__ __align__(16) int s_e[kMaxK];
   __shared__ int s_slot[kMaxK];                    // active-expert slot of each route
   __shared__ float s_w[kMaxK];
@@ -254,6 +307,7 @@ __global__ __launch_bounds__(kThreads) void token_layer_kernel(
   __shared__ float s_qs[kMaxK][GI];
   __shared__ float s_y[kMaxK][64];
   __shared__ float s_tab[kTabSlots];               // block-scale tables (+ a spare slot)
+  __shared__ __align__(16) uint8_t s_w2[8 * kW2PerWave * 1024];  // the workgroup's W2 units
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -313,18 +367,24 @@ __global__ __launch_bounds__(kThreads) void token_layer_kernel(
   //    ascending order.  Lane r < k of wave 0 works out route r's rank
   //    (vector code: the scalar unit is shared by all waves of the CU).
   if (wave == 0) {
+    int ev[kMaxK];
+    {
+      const int4 a = *reinterpret_cast<const int4*>(s_e), b = *reinterpret_cast<const int4*>(s_e + 4);
+      ev[0] = a.x; ev[1] = a.y; ev[2] = a.z; ev[3] = a.w; ev[4] = b.x; ev[5] = b.y; ev[6] = b.z; ev[7] = b.w;
+    }
     const int r = min(lane, kMaxK - 1);
-    const int er = s_e[r];
+    int er = ev[0];
+#pragma unroll
+    for (int q = 1; q < kMaxK; q++) er = r == q ? ev[q] : er;
     bool first = lane < kMaxK && er >= 0;
     int rank = 0;
 #pragma unroll
     for (int q = 0; q < kMaxK; q++) {
-      const int eq = s_e[q];
-      first = first && !(q < r && eq == er);
-      bool q_first = eq >= 0;
+      bool q_first = ev[q] >= 0;
 #pragma unroll
-      for (int p = 0; p < q; p++) q_first = q_first && s_e[p] != eq;
-      rank += (q_first && eq < er) ? 1 : 0;
+      for (int p2 = 0; p2 < q; p2++) q_first = q_first && ev[p2] != ev[q];
+      first = first && !(q < r && ev[q] == er);
+      rank += (q_first && ev[q] < er) ? 1 : 0;
     }
     const uint64_t firsts = __ballot(first);
     if (lane < kMaxK) s_slot[lane] = rank;  // a route's expert has this rank among the distinct live experts
@@ -336,76 +396,38 @@ __global__ __launch_bounds__(kThreads) void token_layer_kernel(
   const int n_slots = __builtin_amdgcn_readfirstlane(s_nslots);
   const uint32_t T = s_tag;
 
-  // 3. block-scale tables, one load per thread: W13 scales of
-  //    the gate and up row blocks (entries 0 .. 2G-1), then the W2 scales of
-  //    this unit's (at most two) row blocks for every route.  A barrier puts
-  //    them ahead of every weight load of the workgroup.
   const int e_ld = e >= 0 ? e : 0;  // a workgroup without a slot loads expert 0 and discards it
-  const int blk_gate = n0 / 128, blk_up = (I + n0) / 128;
   const int rb0 = min(d0, H - 1) / 128, rb1 = min(max(d_end - 1, d0), H - 1) / 128;
-  const int n_tab = 2 * G + k * 2 * GI;
-  float tab;
-  {
-    const int t = tid - n_tab * (int)(((uint32_t)tid * tab_magic) >> 20);  // tid mod n_tab: threads past the tables repeat entries
-    const float* src;
-    if (t < 2 * G) {
-      src = w13_s + ((size_t)e_ld * (2 * I / 128) + (t < G ? blk_gate : blk_up)) * G + (t < G ? t : t - G);
-    } else {
-      const int q = t - 2 * G;
-      const int j = q / (2 * GI), which = (q / GI) & 1, g2 = q % GI;
-      const int ej = s_e[j] >= 0 ? s_e[j] : 0;
-      src = w2_s + ((size_t)ej * G + (which ? rb1 : rb0)) * GI + g2;
-    }
-    tab = *src;
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  wg_sync();
 
   if (wave >= 8) {
-    s_tab[kTabSlots - 1] = tab;  // the spare slot: keeps this wave's table load out of any branch
+    // 3. down waves: block-scale tables into LDS, one load per thread: W13
+    //    scales of the gate and up row blocks (entries 0 .. 2G-1), then the
+    //    W2 scales of this unit's (at most two) row blocks for every route
+    {
+      const int n_tab = 2 * G + k * 2 * GI;
+      const int blk_gate = n0 / 128, blk_up = (I + n0) / 128;
+      const int t0 = tid - 512;
+      const int t = t0 - n_tab * (int)(((uint32_t)t0 * tab_magic) >> 20);  // t0 mod n_tab
+      const float* src;
+      if (t < 2 * G) {
+        src = w13_s + ((size_t)e_ld * (2 * I / 128) + (t < G ? blk_gate : blk_up)) * G + (t < G ? t : t - G);
+      } else {
+        const int q = t - 2 * G;
+        const int j = q / (2 * GI), which = (q / GI) & 1, g2 = q % GI;
+        const int ej = s_e[j] >= 0 ? s_e[j] : 0;
+        src = w2_s + ((size_t)ej * G + (which ? rb1 : rb0)) * GI + g2;
+      }
+      s_tab[t0 < n_tab ? t0 : kTabSlots - 1] = *src;  // past the tables: the spare slot
+    }
     wg_sync();
     if (d0 >= H) return;
-    // 4. down wave w: W2 units u = (w - 8) + 8 i, route u / DL, 1 KB piece
-    //    u % DL of the down rows, requested after every W13 load
-    uint4 wb[kW2Units];
-    const int kof = 16 * (lane % kLpr);
-#pragma unroll
-    for (int i = 0; i < kW2Units; i++) {
-      const int u = min((wave - 8) + 8 * i, k * DL - 1);
-      const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
-      const int ej = s_e[j] >= 0 ? s_e[j] : 0;
-      const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
-      if ((wave - 8) + 8 * i < k * DL) wb[i] = *reinterpret_cast<const uint4*>(w2 + ((size_t)ej * H + row) * I + kof);
-    }
-
-    // 6. SwiGLU rows into LDS, quantised
-    take_groups<I>(st, rep, wave - 8, k, s_e, s_slot, n_slots, T, fmt, s_qh, s_qs, lane);
-    wg_sync();
-
-    // 7. down projection of this wave's units (lanes kLpr r .. kLpr r +
-    //    kLpr - 1 hold row r of a piece), reduced together; live units kept
-    float v[kW2Units];
-#pragma unroll
-    for (int i = 0; i < kW2Units; i++) {
-      const int u = min((wave - 8) + 8 * i, k * DL - 1);
-      const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
-      const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
-      const float w2sc = s_tab[2 * G + (j * 2 + (row / 128 == rb0 ? 0 : 1)) * GI + kof / 128];
-      v[i] = dot16(wb[i], &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * w2sc);
-    }
-#pragma unroll
-    for (int i = 0; i < kW2Units; i++) v[i] = group_sum<kLpr>(v[i]);
-#pragma unroll
-    for (int i = 0; i < kW2Units; i++) {
-      const int u = (wave - 8) + 8 * i;
-      const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
-      const int rl = c * kRpl + lane / kLpr;
-      if (u < k * DL && lane % kLpr == 0 && d0 + rl < d_end && s_e[j] >= 0) s_y[j][rl] = bf16_to_f32(f32_to_bf16(v[i]));
-    }
-    wg_sync();
-    } else {
+    // 4. their W2 units into LDS, queued behind the W13 loads of the
+    //    gate/up waves
+    issue_w2<I>(s_w2, wave, k, DL, dl_magic, s_e, w2, H, d0, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // the W2 units are in LDS
+  } else {
     // 4. gate/up wave w: column n = n0 + w, i.e. gate row n and up row I + n
-    //    of expert e, requested first
+    //    of expert e, requested as soon as the slot is known
     uint4 wg[RL], wu[RL];
     {
       // every chunk but the last lies inside the row; the last is clamped
@@ -419,13 +441,10 @@ __global__ __launch_bounds__(kThreads) void token_layer_kernel(
         wu[c] = *reinterpret_cast<const uint4*>(usrc + off);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);  // every W13 load goes out before the table wait
-    s_tab[min(tid, kTabSlots - 1)] = tab;  // threads past the tables write the spare slot
-    wg_sync();
+    wg_sync();  // the tables are in LDS
 
     // 5. gate and up dot products as the data lands, then SwiGLU on their
-    //    BF16 values; lane r_idx publishes the column of its route (the
-    //    r_idx-th route whose expert is e) to every copy
+    //    BF16 values
     float ag = 0.0f, au = 0.0f;
 #pragma unroll
     for (int c = 0; c < RL; c++) {
@@ -452,17 +471,22 @@ __global__ __launch_bounds__(kThreads) void token_layer_kernel(
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       }
       done = __builtin_amdgcn_readfirstlane(done);
-      if (done == kWaves / 2 - 1 && lane < 8) {
-        const uint64_t word = (uint64_t)s_pub[lane] | ((uint64_t)T << 32);
+      if (done == kWaves / 2 - 1 && lane < 4) {
+        const uint64_t word = (uint64_t)(s_pub[2 * lane] | (s_pub[2 * lane + 1] << 16)) | ((uint64_t)T << 32);
 #pragma unroll
-        for (int x = 0; x < kReplicas; x++) ATOMIC_ST(&st->act[x][slot * kMaxI + n0 + lane], word);
+        for (int x = 0; x < kReplicas; x++) ATOMIC_ST(&st->act[x][slot * (kMaxI / 2) + n0 / 2 + lane], word);
       }
     }
     if (e < 0 && wave == 0 && lane < 16) ATOMIC_ST(&st->flag[blockIdx.x][lane], T);
     if (d0 >= H) return;  // the whole workgroup leaves: no down unit
-    wg_sync();  // the down waves have the SwiGLU rows in LDS
-    wg_sync();  // ... and the down rows in s_y
+    // 6. SwiGLU rows into LDS, quantised
+    take_groups<I>(st, rep, wave, k, s_e, s_slot, n_slots, T, fmt, s_qh, s_qs, lane);
   }
+  wg_sync();  // the quantised SwiGLU rows are in LDS
+
+  // 7. down projection, shared by all 16 waves, then the route rows in s_y
+  down_units<I>(s_w2, wave, k, DL, dl_magic, s_e, s_tab, s_qh, s_qs, s_y, G, H, d0, d_end, rb0, lane);
+  wg_sync();
   if (blockIdx.x == 0 && tid < kReplicas) ATOMIC_ST(&st->gen[tid][0], T);  // every workgroup has read gen
 
   // 8. weighted reduction over the routes, j ascending
@@ -500,7 +524,7 @@ bool token_path_fits(int64_t M, int H, int k, int32_t L, int I, int num_cus) {
   const int up = slots * (I / 8);
   const int dr = token_down_rows(H, I, up);
   if (dr > 64 || dr * I / 1024 > kMaxDownLoads) return false;
-  if (k * (dr * I / 1024) > 8 * kW2Units) return false;  // W2 units of the 8 down waves
+  if (k * (dr * I / 1024) > 8 * kW2PerWave) return false;  // W2 units of the 8 down waves
   const int grid = token_kernel_grid(H, k, L, I);
   return grid <= num_cus && grid <= kMaxGrid;
 }
@@ -514,7 +538,7 @@ hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids,
   const int dr = token_down_rows(H, I, slots * (I / 8));
   const int grid = token_kernel_grid(H, k, L, I);
   const int rl = (H + 1023) / 1024, dl = dr * I / 1024;
-  if (!(I == 128 || I == 256 || I == 512) || rl < 1 || rl > kMaxRowLoads || dl < 1 || dl > kMaxDownLoads || k * dl > 8 * kW2Units)
+  if (!(I == 128 || I == 256 || I == 512) || rl < 1 || rl > kMaxRowLoads || dl < 1 || dl > kMaxDownLoads || k * dl > 8 * kW2PerWave)
     return hipErrorInvalidValue;  // token_path_fits rules these out
   // exact quotients by multiply and shift: u / dl for u < 64 and t / n_tab for
   // t < 1024 (the rounding error of the multiplier stays below one step)

@@ -141,10 +141,10 @@ def test_workspace_shared_across_paths():
 
 def _token_state(ws):
     """The one-token kernel's launch state at the start of a workspace: gen
-    (4 copies, one per 128-byte line), the expiry word, and from byte 8192
+    (8 copies, one per 128-byte line), the expiry word, and from byte 8192
     one 64-byte flag piece per workgroup."""
     head = ws[:8192 + 64 * 512].view(torch.int32).cpu()
-    return {"gen": head[0:128:32], "expired": int(head[128]), "flag": head[2048::16]}
+    return {"gen": head[0:256:32], "expired": int(head[256]), "flag": head[2048::16]}
 
 
 @pytest.mark.parametrize("path", [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE])
