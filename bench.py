@@ -14,10 +14,12 @@ between a device synchronisation on both sides.
 
 Printed: one JSON line with the metric (achieved HBM GB/s of the whole layer
 from its compulsory bytes), microseconds per layer, the roofline of the
-dominant kernel (its algorithmic bytes over its average duration, measured
-with HIP events the library records between its launches, in eager calls
-queued back to back behind a GPU spin), and the CPU oracle timed on a bounded
-sample of the same workload.
+dominant kernel (its algorithmic bytes over its average duration: the
+graph-timed step when the layer is that one kernel, otherwise HIP events the
+library records between its launches, in eager calls queued back to back
+behind a GPU spin), the kernel's HBM traffic from the hardware-counter
+summary in profiles/ while the kernel's sources match it, and the CPU oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -169,6 +171,9 @@ def main():
     ap.add_argument("--instances", type=int, default=0, help="layer instances to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run 4 plain device copies of this many MiB (a known-size reference for "
+                         "hardware traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -185,6 +190,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: 4 copies of {args.calibrate_copy_mib} MiB")
+
     # one instance first, to size the rotation
     t0 = time.time()
     first = synth.layer_inputs(case, 0, device=dev)
@@ -198,7 +213,7 @@ def main():
     o = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp)
     stages = bfp8.fused_moe_stages(case.M, case.H, case.k, case.E, case.I, o)
     ws_bytes = bfp8.fused_moe_workspace_size(case.M, case.H, case.k, case.E, case.I, o)
-    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)  # barrier counter starts at 0
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # launch state starts at zero
     outs = [torch.empty(case.M, case.H, dtype=torch.bfloat16, device=dev) for _ in range(n_inst)]
     bytes_per = [layer_bytes(case, x[1])[0] for x in insts]
     torch.cuda.synchronize()
@@ -273,10 +288,15 @@ def main():
 
     dom = next(s_ for s_ in ("decode_token", "decode_gate_up_swiglu", "gate_up_gemm") if s_ in stage_us)
     dom_bytes = sum(stage_bytes(case, x[1], dom) for x in insts) / n_inst
-    achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
+    # a one-kernel layer: the kernel's average launch-to-launch duration is the
+    # graph-timed step (events around the timed region, kernels back to back);
+    # events between eager launches would add each launch's dispatch overhead
+    dom_us = ms_per_step * 1e3 if n_st == 1 else stage_us[dom]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = measured_traffic(dom, args.config)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes": int(dom_bytes), "avg_us": round(stage_us[dom], 3)}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": int(dom_bytes), "avg_us": round(dom_us, 3)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -309,6 +329,48 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+KERNEL_SOURCES = {
+    "decode_token": ["block_fp8_mixture_route_amd/csrc/token.hip", "block_fp8_mixture_route_amd/csrc/device.h"],
+}
+
+
+def kernel_source_hash(kernel):
+    """SHA-256 of the kernel's sources with comments and blank lines removed,
+    so that a comment edit does not count as a kernel change."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, config):
+    """HBM bytes per launch of `kernel` from the hardware-counter summary in
+    profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by the counters' reading for a
+    plain copy of known size), or None when there is none or the kernel's
+    sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.md")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                vals[k.strip("`")] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_hash(kernel):
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(case, inst, seconds):

@@ -31,6 +31,14 @@
 //      silu_and_mul_quant_fp8);
 //   4. MFMA per route, scales, BF16 y values in LDS;
 //   5. out[t, n] = bf16(fmaf chain over j ascending) over live routes.
+//
+// Pages cited in brackets, by key and section:
+//   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
+//   [P2] lmdeploy PR "perf(pytorch): optimize compact blocked FP8 MoE and route
+//        preparation"
+//   [P3] vLLM PR "[Kernel][Perf] Fuse clamped MoE activation and UE8M0 FP8 block
+//        quantization"
+//   [P4] lmdeploy PR "Moe Reduce kernel"
 #include <mutex>
 
 #include "device.h"

@@ -10,6 +10,14 @@
 // the BF16 SwiGLU value in registers and writes only codes and scales.
 // [P3 Purpose] clamp, UE8M0 scales and row filtering.
 // [P4 Pull request overview] moe_reduce applies the router weights.
+//
+// Pages cited in brackets, by key and section:
+//   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
+//   [P2] lmdeploy PR "perf(pytorch): optimize compact blocked FP8 MoE and route
+//        preparation"
+//   [P3] vLLM PR "[Kernel][Perf] Fuse clamped MoE activation and UE8M0 FP8 block
+//        quantization"
+//   [P4] lmdeploy PR "Moe Reduce kernel"
 #include "device.h"
 #include "internal.h"
 

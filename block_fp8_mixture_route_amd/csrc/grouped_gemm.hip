@@ -13,6 +13,14 @@
 // accumulator.  Operands come straight from global memory into registers (see
 // mfma.h for the K slot order that keeps each load 64-byte contiguous per row);
 // the activation fragments are shared by the 4 waves through L1.
+//
+// Pages cited in brackets, by key and section:
+//   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
+//   [P2] lmdeploy PR "perf(pytorch): optimize compact blocked FP8 MoE and route
+//        preparation"
+//   [P3] vLLM PR "[Kernel][Perf] Fuse clamped MoE activation and UE8M0 FP8 block
+//        quantization"
+//   [P4] lmdeploy PR "Moe Reduce kernel"
 #include "device.h"
 #include "internal.h"
 #include "mfma.h"

@@ -16,6 +16,14 @@
 // wave then walks its sub-segment 64 routes at a time in route order, ranks
 // equal experts inside the chunk with ballots, and advances its cursors.  The
 // result equals a stable counting sort.
+//
+// Pages cited in brackets, by key and section:
+//   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
+//   [P2] lmdeploy PR "perf(pytorch): optimize compact blocked FP8 MoE and route
+//        preparation"
+//   [P3] vLLM PR "[Kernel][Perf] Fuse clamped MoE activation and UE8M0 FP8 block
+//        quantization"
+//   [P4] lmdeploy PR "Moe Reduce kernel"
 #include <mutex>
 
 #include "device.h"

@@ -37,6 +37,14 @@
 // never repeat within 2^32 launches, and no other use of the workspace
 // touches this state.  Bounded waits: a wait that runs out sets an expiry
 // word and lets the kernel finish.
+//
+// Pages cited in brackets, by key and section:
+//   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
+//   [P2] lmdeploy PR "perf(pytorch): optimize compact blocked FP8 MoE and route
+//        preparation"
+//   [P3] vLLM PR "[Kernel][Perf] Fuse clamped MoE activation and UE8M0 FP8 block
+//        quantization"
+//   [P4] lmdeploy PR "Moe Reduce kernel"
 #include "device.h"
 #include "internal.h"
 
