@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     FLAG_LAYER_DECODE,
     FLAG_LAYER_GENERAL,
     FLAG_LAYER_TOKEN,
+    FLAG_ONLY_STAGE,
     FLAG_ROUTE_MULTI_WG,
     FLAG_ROUTE_SINGLE_WG,
     SCALE_FP32,

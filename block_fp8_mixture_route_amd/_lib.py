@@ -27,6 +27,11 @@ FLAG_LAYER_GENERAL = 1 << 2
 FLAG_LAYER_DECODE = 1 << 3
 FLAG_LAYER_TOKEN = 1 << 4
 
+
+def FLAG_ONLY_STAGE(s):
+    """Launch only stage s of the fused layer (tests and profiling)."""
+    return (s + 1) << 8
+
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip"}
 
 
@@ -231,8 +236,7 @@ def fused_moe_block_fp8(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, 
     o = opts() if o is None else o
     need = fused_moe_workspace_size(M, H, k, E, I, o)
     if ws is None:
-        # zero-filled: the first 168 KB hold launch state that must start at 0
-        ws = torch.zeros(need, dtype=torch.uint8, device=hidden.device)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
     out = torch.empty(M, H, dtype=torch.bfloat16, device=hidden.device) if out is None else out
     check(lib().fused_moe_block_fp8(ptr(_u16(hidden)), M, H, ptr(topk_ids), ptr(topk_w), k, ptr(w13),
                                     ptr(w13_scale), ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o),

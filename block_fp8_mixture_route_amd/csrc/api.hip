@@ -55,15 +55,8 @@ struct LayerPlan {
 const char* const kGeneralStages[] = {"route_prepare", "quant_fp8", "gate_up_gemm",
                                       "silu_and_mul_quant", "down_gemm", "moe_reduce"};
 const char* const kDecodeStages[] = {"decode_gate_up_swiglu", "decode_down_reduce"};
-const char* const kTokenStages[] = {"decode_token"};
+const char* const kTokenStages[] = {"token_gate_up_swiglu", "token_down_reduce"};
 enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
-
-// CU count used for planning: the current device's, or MI355X's 256 when no
-// device is visible (host-only planning, e.g. sizing a workspace).
-int planning_cus() {
-  const int n = bfp8::device_cu_count();
-  return n > 0 ? n : 256;
-}
 
 // The small-batch path is the default up to this many tokens.
 constexpr int64_t kDecodeAutoMaxM = 4;
@@ -89,7 +82,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.block_m = o.block_m > 0 ? o.block_m : auto_block_m(p.R, p.L);
   p.max_blocks = bfp8moe_max_blocks(p.R, p.L, p.block_m);
   const bool fits = bfp8::decode_path_fits(M, H, k, I);
-  const bool token_fits = bfp8::token_path_fits(M, H, k, p.L, I, planning_cus());
+  const bool token_fits = bfp8::token_path_fits(M, H, k, I);
   if (o.flags & BFP8MOE_FLAG_LAYER_GENERAL)
     p.mode = kModeGeneral;
   else if (o.flags & BFP8MOE_FLAG_LAYER_DECODE)
@@ -106,18 +99,13 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
     p.route_single = false;
   else
     p.route_single = bfp8::route_prep_single_fits(p.R, p.L);
-  size_t o_ = bfp8::kTokenStateBytes;  // launch state of the one-token kernel comes first
+  size_t o_ = 0;
   auto take = [&](size_t bytes) {
     size_t at = o_;
     o_ = align_up(o_ + bytes);
     return at;
   };
-  if (p.mode == kModeToken) {
-    p.off_act = 0;
-    p.total = o_;
-    return;
-  }
-  if (p.mode == kModeDecode) {
+  if (p.mode == kModeToken || p.mode == kModeDecode) {
     p.off_act = take(sizeof(uint16_t) * (size_t)p.R * I);
     p.total = o_;
     return;
@@ -316,11 +304,11 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
                 "small-batch path forced but M=%lld k=%d H=%d I=%d exceed its limits (M<=8, k<=8, H<=8192, "
                 "I<=512)",
                 (long long)M, k, H, I);
-  if ((o.flags & BFP8MOE_FLAG_LAYER_TOKEN) && M > 0 && !bfp8::token_path_fits(M, H, k, L, I, planning_cus()))
+  if ((o.flags & BFP8MOE_FLAG_LAYER_TOKEN) && M > 0 && !bfp8::token_path_fits(M, H, k, I))
     return fail(BFP8MOE_ERR_UNSUPPORTED,
-                "one-token path forced but M=%lld k=%d H=%d I=%d do not fit it (M=1, k<=8, H<=8192, I<=512, "
-                "grid of %d workgroups <= %d compute units)",
-                (long long)M, k, H, I, bfp8::token_kernel_grid(H, k, L, I), planning_cus());
+                "one-token path forced but M=%lld k=%d H=%d I=%d do not fit it (M=1, k<=8, H<=8192, "
+                "I in {128, 256, 512})",
+                (long long)M, k, H, I);
   {
     const uint32_t paths = o.flags & (BFP8MOE_FLAG_LAYER_GENERAL | BFP8MOE_FLAG_LAYER_DECODE | BFP8MOE_FLAG_LAYER_TOKEN);
     REQUIRE((paths & (paths - 1)) == 0, "layer path flags are exclusive");
@@ -341,7 +329,7 @@ int32_t fused_moe_block_fp8_stages(int64_t M, int32_t H, int32_t k, int32_t E, i
   LayerPlan p;
   plan_layer(p, M, H, k, E, I, o);
   const char* const* list = p.mode == kModeToken ? kTokenStages : p.mode == kModeDecode ? kDecodeStages : kGeneralStages;
-  const int32_t n = p.mode == kModeToken ? 1 : p.mode == kModeDecode ? 2 : 6;
+  const int32_t n = p.mode == kModeGeneral ? 6 : 2;
   for (int32_t i = 0; names && i < n && i < cap; i++) names[i] = list[i];
   return n;
 }
@@ -376,6 +364,9 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   if (M == 0) return BFP8MOE_OK;
   LayerPlan p;
   plan_layer(p, M, H, k, E, I, o);
+  const int only = (int)((o.flags >> BFP8MOE_FLAG_STAGE_SHIFT) & 15u) - 1;
+  const int n_stages = p.mode == kModeGeneral ? 6 : 2;
+  if (only >= n_stages) return fail(BFP8MOE_ERR_INVALID_ARG, "stage %d selected, the path has %d", only, n_stages);
   if (ws == nullptr || ws_bytes < p.total)
     return fail(BFP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
   REQUIRE((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) == 0, "workspace must be 256-byte aligned");
@@ -384,10 +375,12 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   char* base = static_cast<char*>(ws);
   bfp8::LaunchHook hook;
   hook.events = o.stage_events;
-  hook.n = o.stage_events ? (p.mode == kModeToken ? 2 : p.mode == kModeDecode ? 3 : 7) : 0;
+  hook.n = o.stage_events ? (p.mode == kModeGeneral ? 7 : 3) : 0;
+  hook.only = only;
   if (p.mode == kModeToken) {
+    uint16_t* act = reinterpret_cast<uint16_t*>(base + p.off_act);
     return hip_status(bfp8::launch_token_layer(hidden, H, topk_ids, topk_w, k, p.offset, p.L, w13, w13_scale, w2,
-                                               w2_scale, I, p.fmt, p.clamp, base, out, st, &hook),
+                                               w2_scale, I, p.fmt, p.clamp, act, out, st, &hook),
                       "fused_moe_block_fp8 (one token)");
   }
   if (p.mode == kModeDecode) {
@@ -409,17 +402,19 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   float* s = reinterpret_cast<float*>(base + p.off_s);
   uint16_t* y = reinterpret_cast<uint16_t*>(base + p.off_y);
 
-  hipError_t e;
+  hipError_t e = hipSuccess;
   hook.before(0, st);
-  e = bfp8::launch_route_prepare(topk_ids, p.R, p.offset, p.L, p.block_m, sorted, eoff, bexp, bstart, p.max_blocks,
-                                 nb, p.route_single, rws, st);
+  if (hook.run(0))
+    e = bfp8::launch_route_prepare(topk_ids, p.R, p.offset, p.L, p.block_m, sorted, eoff, bexp, bstart, p.max_blocks,
+                                   nb, p.route_single, rws, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: route prep");
   hook.before(1, st);
-  e = bfp8::launch_quant_fp8(hidden, M, H, p.fmt, aq, as, st);
+  if (hook.run(1)) e = bfp8::launch_quant_fp8(hidden, M, H, p.fmt, aq, as, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: input quant");
   hook.before(2, st);
-  e = bfp8::launch_grouped_gemm(aq, as, k, w13, w13_scale, 2 * I, H, sorted, eoff, bexp, bstart, nb, p.max_blocks,
-                                p.block_m, h13, st);
+  if (hook.run(2))
+    e = bfp8::launch_grouped_gemm(aq, as, k, w13, w13_scale, 2 * I, H, sorted, eoff, bexp, bstart, nb, p.max_blocks,
+                                  p.block_m, h13, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: gate/up GEMM");
   bfp8::RowFilter f;
   f.ids = topk_ids;
@@ -427,14 +422,15 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   f.L = p.L;
   f.mode = bfp8::kRowsLocalSlice;
   hook.before(3, st);
-  e = bfp8::launch_silu_and_mul_quant(h13, p.R, I, f, p.clamp, p.fmt, q, s, st);
+  if (hook.run(3)) e = bfp8::launch_silu_and_mul_quant(h13, p.R, I, f, p.clamp, p.fmt, q, s, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: act+quant");
   hook.before(4, st);
-  e = bfp8::launch_grouped_gemm(q, s, 1, w2, w2_scale, H, I, sorted, eoff, bexp, bstart, nb, p.max_blocks,
-                                p.block_m, y, st);
+  if (hook.run(4))
+    e = bfp8::launch_grouped_gemm(q, s, 1, w2, w2_scale, H, I, sorted, eoff, bexp, bstart, nb, p.max_blocks,
+                                  p.block_m, y, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: down GEMM");
   hook.before(5, st);
-  e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, p.offset, p.L, M, k, H, out, st);
+  if (hook.run(5)) e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, p.offset, p.L, M, k, H, out, st);
   hook.before(6, st);
   return hip_status(e, "fused_moe_block_fp8: moe_reduce");
 }

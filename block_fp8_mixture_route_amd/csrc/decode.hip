@@ -433,13 +433,15 @@ hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const i
     (void)hipGetLastError();
   });
   if (hook) hook->before(0, stream);
-  hipLaunchKernelGGL(decode_gate_up_kernel, dim3(I / 8, slots), dim3(kThreads), lds, stream, hidden, (int)M, H,
-                     ids, k, offset, L, w13, w13_s, I, fmt, limit, clamp, tile_cap, act);
+  if (!hook || hook->run(0))
+    hipLaunchKernelGGL(decode_gate_up_kernel, dim3(I / 8, slots), dim3(kThreads), lds, stream, hidden, (int)M, H,
+                       ids, k, offset, L, w13, w13_s, I, fmt, limit, clamp, tile_cap, act);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hook) hook->before(1, stream);
-  hipLaunchKernelGGL(decode_down_reduce_kernel, dim3(H / kDownRows, (unsigned)M), dim3(kThreads), 0, stream, act,
-                     ids, topk_w, k, offset, L, w2, w2_s, H, I, fmt, out);
+  if (!hook || hook->run(1))
+    hipLaunchKernelGGL(decode_down_reduce_kernel, dim3(H / kDownRows, (unsigned)M), dim3(kThreads), 0, stream,
+                       act, ids, topk_w, k, offset, L, w2, w2_s, H, I, fmt, out);
   e = hipGetLastError();
   if (hook) hook->before(2, stream);
   return e;

@@ -18,13 +18,16 @@ enum RowFilterMode : int {
 };
 
 // Optional profiling hook: records caller-owned HIP events on the stream
-// before stage i (and, with i == number of stages, after the last one).
+// before stage i (and, with i == number of stages, after the last one), and
+// can restrict a call to one stage.
 struct LaunchHook {
   void* const* events = nullptr;
-  int n = 0;  // number of events in the array
+  int n = 0;      // number of events in the array
+  int only = -1;  // >= 0: launch stage `only` alone
   void before(int i, hipStream_t stream) const {
     if (events && i < n && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
   }
+  bool run(int i) const { return only < 0 || only == i; }
 };
 
 struct RowFilter {
@@ -66,18 +69,13 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
 // Small-batch path of the fused layer: gate/up + SwiGLU kernel, then down +
 // moe_reduce kernel.  act: [M*k, I] BF16 scratch.
 bool decode_path_fits(int64_t M, int H, int k, int I);
-// One-token path: a single persistent kernel (one workgroup per CU; the
-// gate/up and down halves exchange the SwiGLU output through tagged words).
-// Needs the whole grid resident.
-bool token_path_fits(int64_t M, int H, int k, int32_t L, int I, int num_cus);
-int token_kernel_grid(int H, int k, int32_t L, int I);
+// One-token path: gate/up + SwiGLU kernel, then down + moe_reduce kernel, both
+// matrix-vector streaming kernels.  act: [k, I] BF16 scratch.
+bool token_path_fits(int64_t M, int H, int k, int I);
 int device_cu_count();  // of the current device; 0 when there is none
-// Bytes of launch state the one-token kernel keeps at the start of every
-// workspace (zero before the first launch; launches keep it valid).
-constexpr size_t kTokenStateBytes = 172032;  // 168 KB
 hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids, const float* topk_w, int k,
                               int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s, const uint8_t* w2,
-                              const float* w2_s, int I, int fmt, float limit, void* state, uint16_t* out,
+                              const float* w2_s, int I, int fmt, float limit, uint16_t* act, uint16_t* out,
                               hipStream_t stream, const LaunchHook* hook);
 hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
                                int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,

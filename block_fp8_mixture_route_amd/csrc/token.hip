@@ -1,5 +1,5 @@
-// token.hip -- the whole block-FP8 MoE layer for one token (M = 1) in one
-// persistent kernel on gfx950.
+// token.hip -- the block-FP8 MoE layer for one token (M = 1) on gfx950 as two
+// weight-streaming kernels.
 //
 // [P1 Motivation] at M = 1, top-k 8, E = 256 at most eight experts are active
 // and the layer is pure weight streaming: 44 MB of W13 + W2 at the 7168 x 256
@@ -7,36 +7,29 @@
 // products, so they run on the vector ALUs from row-contiguous loads (every
 // wave load instruction reads 1 KB of one weight row), not on MFMA tiles whose
 // operand layout scatters each load over 16 rows.
-// [P1 Modification, Active-expert block scheduling] only the active experts'
-// rows are read; workgroups are laid out per active-expert slot.
+// [P1 Modification, Active-expert block scheduling] only the active routes'
+// rows are read: gate/up workgroups exist per route, and a route whose expert
+// lies outside the local slice exits at once.
 // [P1 Modification, Fused SwiGLU and FP8 quantization] SwiGLU is applied in the
 // gate/up epilogue; its BF16 output is group-quantised where the down
 // projection consumes it.
 // [P4 Pull request overview] the down projection ends with the top-k weighted
 // reduction, routes in order.
 //
-// Grid: one 1024-thread workgroup per compute unit, all resident.  Workgroup w
-// serves
-//   gate/up unit w: active-expert slot w / (I/8) (experts in ascending order),
-//     gate rows n0 = 8 (w % (I/8)) .. n0+7 and up rows I+n0 .. I+n0+7, one row
-//     per wave;
-//   down unit w: output rows DR w .. DR w + DR - 1 for all k routes, as k x DL
-//     pieces of 1 KB spread four per wave.
-// Every wave runs the same straight-line load sequence -- block-scale tables,
-// its W13 row, its four W2 pieces -- so that the waits the compiler places
-// for the W13 data never include the W2 loads issued after them (the memory
-// counter is in order), and the W2 stream overlaps the gate/up work.
+// gate/up kernel: workgroup (route j, slice q) computes columns n = 8 q .. 8 q
+//   + 7 of route j's SwiGLU row, one column (gate row n and up row I + n) per
+//   wave, each written as one BF16 value into act[j].
+// down kernel: workgroup b computes output rows DR b .. DR b + DR - 1 for all
+//   k routes from its W2 pieces (1 KB units: route, kRpl rows of I bytes),
+//   quantises the k SwiGLU rows itself, and ends with the weighted reduction.
 //
-// No grid barrier: the SwiGLU outputs are written as 8-byte words holding two
-// BF16 values and a 32-bit launch tag, into state kept at the start of the
-// workspace.  A consumer polls the words it needs until every tag equals the
-// current launch's tag, so data and completion travel in one store.  The tag
-// of a launch is gen + 1, where gen is read by every workgroup at its start;
-// each workgroup then records that it has read gen, and workgroup 0 advances
-// gen once every workgroup has done so.  Zero-filled state is valid, tags
-// never repeat within 2^32 launches, and no other use of the workspace
-// touches this state.  Bounded waits: a wait that runs out sets an expiry
-// word and lets the kernel finish.
+// The kernel boundary is the only exchange.  Within one kernel a compute unit
+// serves its memory requests roughly in order, so any store or poll that hands
+// the SwiGLU row from gate/up workgroups to down workgroups waits behind the
+// weight loads its compute unit issued earlier; the next launch in the stream
+// costs less than that wait.  Every load a kernel needs is issued as soon as
+// its address is known, before any of its data is used, so that the memory
+// counter waits (in order) for the small operands never include weight loads.
 //
 // Pages cited in brackets, by key and section:
 //   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
@@ -52,51 +45,26 @@ namespace bfp8 {
 
 namespace {
 
-constexpr int kThreads = 1024;  // 16 waves
-constexpr int kWaves = kThreads / 64;
+constexpr int kUpThreads = 512;     // gate/up kernel: 8 waves, one column each
+constexpr int kDownThreads = 1024;  // down kernel: 16 waves
+constexpr int kDownWaves = kDownThreads / 64;
 constexpr int kMaxK = 8;
 constexpr int kMaxH = 8192;
-constexpr int kMaxRowLoads = kMaxH / 1024;  // 1 KB loads per W13 row
-constexpr int kMaxI = 512;
-constexpr int kMaxDownLoads = 8;            // 1 KB W2 loads per route per workgroup
-constexpr int kW2PerWave = 8;               // (route, 1 KB piece) W2 units per down wave
-constexpr int kMaxGrid = 512;               // 64 flags per down wave
-constexpr int kReplicas = 8;                // copies of the polled state, read by workgroup b from copy b % 8
-constexpr int kTabSlots = 2 * (kMaxH / 128) + kMaxK * 2 * (kMaxI / 128) + 1;
+constexpr int kUnitsPerWave = 4;                            // 1 KB W2 units per down wave
+constexpr int kMaxUnits = kDownWaves * kUnitsPerWave;       // per down workgroup
+constexpr int kMaxDownRows = 64;
+constexpr int kDownTarget = 256;  // down workgroups aimed at (one per compute unit of MI355X)
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-// Launch state at the start of the workspace.  Words that many workgroups
-// poll at once are kept in kReplicas copies so that no single memory line
-// serves the whole grid.  The SwiGLU output depends only on the expert and
-// the column (one token), so it is kept per active-expert slot: row s holds
-// slot s's I columns as 64-bit words of two columns each.  Workgroup (slot s,
-// slice q) writes its 8 columns as one 32-byte piece from one wave.  Writes
-// here are whole pieces from one wave: small writes that many workgroups aim
-// at one memory line are serialised by the memory system and stall the
-// weight stream.  A producer's tagged piece also shows that it has read gen;
-// only workgroups without a slot write a separate flag.
-struct TokenState {
-  uint32_t gen[kReplicas][32];               // tag of the last completed launch, one copy per 128-byte line
-  uint32_t expired;                          // set when a bounded wait ran out
-  uint32_t pad[31];
-  uint32_t pad2[(8192 - kReplicas * 128 - 128) / 4];
-  uint32_t flag[kMaxGrid][16];               // workgroups without a slot: 64 bytes of tag once they have read gen
-  uint64_t act[kReplicas][kMaxK * kMaxI / 2];  // [slot][column pair]: 2 BF16 (low half) + tag (high half)
-};
-static_assert(sizeof(TokenState) <= kTokenStateBytes, "token state");
-static_assert(offsetof(TokenState, flag) == 8192 && offsetof(TokenState, act) == 8192 + 64 * kMaxGrid, "layout");
-
-constexpr unsigned kSpinLimit = 1u << 22;
-
-#define ATOMIC_LD(p) __hip_atomic_load((p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-#define ATOMIC_ST(p, v) __hip_atomic_store((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-
-// Workgroup-wide barrier that waits for LDS traffic only (no vector-memory
-// wait), so that waves with weight loads in flight are not held up.
+// Workgroup barrier that waits for LDS traffic only (no vector-memory wait),
+// so that waves with weight loads in flight are not held up.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void wg_sync() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): vmcnt and expcnt left at their maximum
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
@@ -182,396 +150,288 @@ __device__ __forceinline__ h2 quant2(float a, float b, float sc) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, 1.0f, false);
 }
 
-// Gate/up wave d (0..7), once it has published: wait until every SwiGLU
-// word of its groups gi = d, d + 8, ... (route j = gi / (I/128), group g,
-// read from the row of route j's slot) carries tag T -- and, in workgroup 0,
-// until the flags of workgroups 64 d .. 64 d + 63 without a slot do -- then
-// quantise the groups into LDS.  Lane l takes the word of columns 2l and
-// 2l + 1 of a group.  All loads of a round go out together.
-template <int I>
-__device__ __forceinline__ void take_groups(TokenState* st, int rep, int d, int k, const int* s_e, const int* s_slot,
-                                           int n_slots, uint32_t T, int fmt, h2 (*s_qh)[I / 2],
-                                           float (*s_qs)[I / 128], int lane) {
-  constexpr int GI = I / 128;
-  constexpr int NG = GI;  // groups per wave at k = 8
-  bool live[NG];
-  const uint64_t* src[NG];
-#pragma unroll
-  for (int m = 0; m < NG; m++) {
-    const int gi = d + 8 * m;
-    const int j = min(gi / GI, k - 1), g = gi - (gi / GI) * GI;
-    live[m] = gi < k * GI && s_e[j] >= 0;
-    src[m] = &st->act[rep][s_slot[j] * (kMaxI / 2) + g * 64 + lane];
-  }
-  const bool chk_flags = blockIdx.x == 0 && 64 * d < (int)gridDim.x;
-  const int fi = min(64 * d + lane, (int)gridDim.x - 1);
-  const bool fi_has_slot = fi / (I / 8) < n_slots;  // such a workgroup's SwiGLU piece is checked instead
-  uint64_t w[NG];
-  unsigned spins = 0;
-#pragma nounroll
-  for (;;) {
-#pragma unroll
-    for (int m = 0; m < NG; m++) w[m] = ATOMIC_LD(src[m]);
-    const uint32_t f = ATOMIC_LD(&st->flag[fi][0]);
-    bool ok = !chk_flags || fi_has_slot || f == T;
-#pragma unroll
-    for (int m = 0; m < NG; m++) ok = ok && (!live[m] || (uint32_t)(w[m] >> 32) == T);
-    if (__all(ok)) break;
-    if (++spins == kSpinLimit) {
-      ATOMIC_ST(&st->expired, 1u);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-#pragma unroll
-  for (int m = 0; m < NG; m++) {
-    if (!live[m]) continue;
-    const int gi = d + 8 * m, j = gi / GI, g = gi - j * GI;
-    const float a0 = bf16_to_f32((uint32_t)w[m] & 0xFFFFu), a1 = bf16_to_f32(((uint32_t)w[m] >> 16) & 0xFFFFu);
-    const float sc = group_scale(group_max<64>(fmaxf(fabsf(a0), fabsf(a1))), fmt);
-    s_qh[j][g * 64 + lane] = quant2(a0, a1, sc);
-    if (lane == 0) s_qs[j][g] = sc;
-  }
+// Route r's expert within the local slice [offset, offset + L), or -1.
+__device__ __forceinline__ int local_expert(int32_t id, int32_t offset, int32_t L) {
+  const int64_t e = (int64_t)id - offset;
+  return (e >= 0 && e < L) ? (int)e : -1;
 }
 
-typedef __attribute__((address_space(1))) const void* global_ptr;
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// W2 units u = d + 8 i (down wave d = wave - 8) of the workgroup's down
-// rows, copied by direct-to-LDS loads into s_w2[u] (1 KB each): route u / DL,
-// 1 KB piece u % DL, i.e. kRpl rows of I bytes; lane l's 16 bytes land at
-// byte 16 l of the unit.  Units past the last repeat it (a cache hit);
-// masked routes read expert 0.  Completion is counted by the wave's memory
-// counter.
-template <int I>
-__device__ __forceinline__ void issue_w2(uint8_t* s_w2, int wave, int k, int DL, uint32_t dl_magic, const int* s_e,
-                                         const uint8_t* __restrict__ w2, int H, int d0, int lane) {
-  constexpr int kRpl = 1024 / I, kLpr = I / 16;
-  const uint8_t* src[kW2PerWave];
-#pragma unroll
-  for (int i = 0; i < kW2PerWave; i++) {
-    const int u = min((wave - 8) + 8 * i, k * DL - 1);
-    const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
-    const int ej = max(s_e[j], 0);
-    const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
-    src[i] = w2 + ((size_t)ej * H + row) * I + 16 * (lane % kLpr);
-  }
-#pragma unroll
-  for (int i = 0; i < kW2PerWave; i++)
-    __builtin_amdgcn_global_load_lds((global_ptr)src[i], (lds_ptr)(s_w2 + ((wave - 8) + 8 * i) * 1024), 16, 0, 0);
-}
-
-// Down projection of wave w's W2 units u = w + 16 i (read from LDS): each
-// row's dot product with the quantised SwiGLU row of its route, both block
-// scales applied per group, reduced over the row's lanes; live rows go to
-// s_y as BF16-valued floats.
-template <int I>
-__device__ __forceinline__ void down_units(const uint8_t* s_w2, int wave, int k, int DL, uint32_t dl_magic,
-                                           const int* s_e, const float* s_tab, const h2 (*s_qh)[I / 2],
-                                           const float (*s_qs)[I / 128], float (*s_y)[64], int G, int H, int d0,
-                                           int d_end, int rb0, int lane) {
-  constexpr int GI = I / 128, kRpl = 1024 / I, kLpr = I / 16;
-  constexpr int kUnits = 8 * kW2PerWave / kWaves;
-  const int kof = 16 * (lane % kLpr);
-  float v[kUnits];
-#pragma unroll
-  for (int i = 0; i < kUnits; i++) {
-    const int u = min(wave + kWaves * i, k * DL - 1);
-    const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
-    const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
-    const float w2sc = s_tab[2 * G + (j * 2 + (row / 128 == rb0 ? 0 : 1)) * GI + kof / 128];
-    const uint4 wv = *reinterpret_cast<const uint4*>(s_w2 + u * 1024 + 16 * lane);
-    v[i] = dot16(wv, &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * w2sc);
-  }
-#pragma unroll
-  for (int i = 0; i < kUnits; i++) v[i] = group_sum<kLpr>(v[i]);
-#pragma unroll
-  for (int i = 0; i < kUnits; i++) {
-    const int u = wave + kWaves * i;
-    const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
-    const int rl = c * kRpl + lane / kLpr;
-    if (u < k * DL && lane % kLpr == 0 && d0 + rl < d_end && s_e[j] >= 0) s_y[j][rl] = bf16_to_f32(f32_to_bf16(v[i]));
-  }
-}
-
+// ------------------------------------------------------------------ gate/up
+//
+// Workgroup (route j, slice q), wave w: column n = 8 q + w of route j, i.e. the
+// dot products of the quantised hidden row with gate row n and up row I + n of
+// route j's expert, both block scales applied per group of 128, then SwiGLU on
+// their BF16 values, stored as act[j][n].  All loads go out before any data is used: the hidden
+// row, one block-scale entry per thread, then the wave's 2 x RL 1 KB row
+// loads.
 template <int RL, int I>
-__global__ __launch_bounds__(kThreads) void token_layer_kernel(
-    const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
-    int k, int32_t offset, int32_t L, const uint8_t* __restrict__ w13, const float* __restrict__ w13_s,
-    const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int fmt, float limit, int clamp,
-    int down_rows, int DL, uint32_t dl_magic, uint32_t tab_magic, TokenState* st, uint16_t* __restrict__ out) {
-  constexpr int GI = I / 128;
-  constexpr int kSlices = I / 8;     // gate/up units per expert
-  __shared__ __align__(16) int s_e[kMaxK];
-  __shared__ int s_slot[kMaxK];                    // active-expert slot of each route
-  __shared__ float s_w[kMaxK];
-  __shared__ uint32_t s_tag;
-  __shared__ uint32_t s_pub[8];                    // this workgroup's 8 SwiGLU columns (BF16)
-  __shared__ int s_pub_count;
-  __shared__ int s_expert, s_nslots;
-  __shared__ __align__(16) h2 s_ah[kMaxH / 2];     // quantised hidden row (E4M3 values as FP16)
-  __shared__ float s_as[kMaxH / 128];              // its group scales
-  __shared__ __align__(16) h2 s_qh[kMaxK][I / 2];  // quantised SwiGLU rows (E4M3 values as FP16)
-  __shared__ float s_qs[kMaxK][GI];
-  __shared__ float s_y[kMaxK][64];
-  __shared__ float s_tab[kTabSlots];               // block-scale tables (+ a spare slot)
-  __shared__ __align__(16) uint8_t s_w2[8 * kW2PerWave * 1024];  // the workgroup's W2 units
+__global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
+    const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, int32_t offset, int32_t L,
+    const uint8_t* __restrict__ w13, const float* __restrict__ w13_s, int fmt, float limit, int clamp,
+    uint16_t* __restrict__ act) {
+  constexpr int kSlices = I / 8;
+  __shared__ __align__(16) h2 s_ah[kMaxH / 2];  // quantised hidden row (E4M3 values as FP16)
+  __shared__ float s_as[kMaxH / 128];           // its group scales
+  __shared__ float s_tab[2 * (kMaxH / 128)];    // W13 block scales: gate row block, then up row block
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H / 128;
-  const int slot = blockIdx.x / kSlices;
-  const int n0 = (blockIdx.x - slot * kSlices) * 8;
-  const int d0 = blockIdx.x * down_rows;  // >= H: no down unit
-  const int d_end = min(H, d0 + down_rows);
+  const int j = blockIdx.x / kSlices;
+  const int n0 = (blockIdx.x - j * kSlices) * 8;
+  const int e = local_expert(ids[j], offset, L);
+  if (e < 0) return;  // route outside the local slice: it contributes nothing
+
+  // 1. loads.  Hidden groups tid/16 and tid/16 + 32, 8 values per lane; the
+  //    indices are clamped so that every load is unconditional (a load in a
+  //    branch makes the compiler wait for it where the branch joins).
   const int l16 = tid & 15;
-  const int rep = blockIdx.x % kReplicas;
-
-  // 0. the hidden row (group tid/16, 8 values per lane), the routing through
-  //    scalar loads (one request per wave, not one per lane) and, in wave 0,
-  //    gen.  The hidden load is unconditional (clamped index): a vector load
-  //    in a branch makes the compiler wait for it where the branch joins.
-  const int hg = min(tid >> 4, G - 1);
-  const uint4 hv = *reinterpret_cast<const uint4*>(hidden + (size_t)hg * 128 + l16 * 8);
-  int32_t id_raw[kMaxK];
-  float w_raw[kMaxK];
+  uint4 hv[2];
 #pragma unroll
-  for (int r = 0; r < kMaxK; r++) {
-    id_raw[r] = r < k ? ids[r] : -1;
-    w_raw[r] = r < k ? topk_w[r] : 0.0f;
+  for (int p = 0; p < 2; p++) {
+    const int hg = min((tid >> 4) + 32 * p, G - 1);
+    hv[p] = *reinterpret_cast<const uint4*>(hidden + (size_t)hg * 128 + l16 * 8);
   }
-  uint32_t gen = 0;
-  if (wave == 0) gen = ATOMIC_LD(&st->gen[rep][0]);
+  __builtin_amdgcn_sched_barrier(0);
+  const int t = min(tid, 2 * G - 1);
+  const float tab = w13_s[((size_t)e * (2 * I / 128) + (t < G ? n0 / 128 : (I + n0) / 128)) * G + (t < G ? t : t - G)];
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 wg[RL], wu[RL];
+  {
+    // every chunk but the last lies inside the row; the last is clamped
+    const uint8_t* gsrc = w13 + ((size_t)e * 2 * I + n0 + wave) * H;
+    const uint8_t* usrc = gsrc + (size_t)I * H;
+    const int last = min(1024 * (RL - 1) + 16 * lane, H - 16);
+#pragma unroll
+    for (int c = 0; c < RL; c++) {
+      const int off = c < RL - 1 ? 1024 * c + 16 * lane : last;
+      wg[c] = *reinterpret_cast<const uint4*>(gsrc + off);
+      wu[c] = *reinterpret_cast<const uint4*>(usrc + off);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
-  // 1. quantise the hidden row into LDS while the routing settles
-  if ((tid >> 4) < G) {
+  // 2. the hidden row group-quantised into LDS (same arithmetic as
+  //    quant_fp8) while the weight rows are in flight; the scale table too.
+  //    Clamped lanes repeat the last group's values and stores, so nothing
+  //    here is conditional (a branch would let the compiler move a load into
+  //    it, behind the weight loads).
+#pragma unroll
+  for (int p = 0; p < 2; p++) {
+    const int hg = min((tid >> 4) + 32 * p, G - 1);
     float f[8];
-    unpack8(hv, f);
+    unpack8(hv[p], f);
     const float sc = group_scale(max_over_16(amax8(f)), fmt);
     quant_store8(f, sc, s_ah + (hg * 128 + l16 * 8) / 2);
     if (l16 == 0) s_as[hg] = sc;
   }
-  if (tid < kMaxK) {
-    int32_t id = id_raw[0];
-    float wt = w_raw[0];
+  s_tab[t] = tab;
+  wg_sync();
+
+  // 3. gate and up dot products as the data lands
+  float ag = 0.0f, au = 0.0f;
 #pragma unroll
-    for (int r = 1; r < kMaxK; r++)
-      if (tid == r) {
-        id = id_raw[r];
-        wt = w_raw[r];
-      }
-    const int64_t e = (int64_t)id - offset;
-    s_e[tid] = (tid < k && e >= 0 && e < L) ? (int)e : -1;
-    s_w[tid] = wt;
+  for (int c = 0; c < RL; c++) {
+    const int kof = 1024 * c + 16 * lane;  // past H only in the last chunk: its terms are dropped
+    const float as = s_as[kof / 128];
+    float pg = dot16(wg[c], s_ah + kof / 2) * (as * s_tab[kof / 128]);
+    float pu = dot16(wu[c], s_ah + kof / 2) * (as * s_tab[G + kof / 128]);
+    if (c == RL - 1 && kof >= H) pg = pu = 0.0f;
+    ag += pg;
+    au += pu;
   }
-  if (tid == 0) {
-    s_tag = gen + 1;
-    s_pub_count = 0;
-    s_expert = -1;
+  ag = group_sum<64>(ag);
+  au = group_sum<64>(au);
+
+  // 4. SwiGLU of the BF16 gate/up outputs; each wave stores its column (no
+  //    barrier: a wave leaves as soon as its own data has landed)
+  const float g = bf16_to_f32(f32_to_bf16(ag)), u = bf16_to_f32(f32_to_bf16(au));
+  if (lane == 0) act[(size_t)j * I + n0 + wave] = (uint16_t)f32_to_bf16(swiglu_bf16(g, u, limit, clamp != 0));
+}
+
+// ------------------------------------------------------------------ down + reduce
+//
+// Workgroup b: output rows d0 = DR b .. d0 + DR - 1 (DR a multiple of kRpl =
+// 1024 / I, at most 64).  Its W2 data is k x DL units of 1 KB (route j, piece
+// c: rows d0 + kRpl c .. + kRpl - 1); unit u = wave + 16 i is held by that
+// wave, lane l reading row kRpl c + l / kLpr, bytes 16 (l % kLpr) .. + 15.
+// Loads leave in the order their data is needed: the SwiGLU rows (they do not
+// depend on the routing), the W2 units, the W2 block scale of each lane's
+// row and group.  Route ids are read with uniform (scalar) loads by each wave
+// that needs them: no barrier stands between the start and the W2 loads.
+template <int I>
+__global__ __launch_bounds__(kDownThreads) void token_down_kernel(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int k,
+    int32_t offset, int32_t L, const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int H, int fmt,
+    int DR, int DL, uint32_t dl_magic, uint16_t* __restrict__ out) {
+  constexpr int GI = I / 128, kRpl = 1024 / I, kLpr = I / 16;
+  constexpr int kActLoads = (kMaxK * GI + kDownWaves - 1) / kDownWaves;  // SwiGLU groups per wave
+  __shared__ __align__(16) h2 s_qh[kMaxK][I / 2];  // quantised SwiGLU rows (E4M3 values as FP16)
+  __shared__ float s_qs[kMaxK][GI];                // their group scales
+  __shared__ float s_y[kMaxK][kMaxDownRows];       // down outputs per route (BF16 values)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = H / 128;
+  const int d0 = blockIdx.x * DR, d_end = min(H, d0 + DR);
+  const int n_units = k * DL;
+  const int kof = 16 * (lane % kLpr);
+
+  // 1. the route ids (lane r: route min(r, k - 1)), then the SwiGLU groups
+  //    gi = wave + 16 m (route gi / GI, group gi % GI; lane l takes columns
+  //    2 l and 2 l + 1), which do not depend on the routing
+  const int id_lane = ids[min(lane, k - 1)];
+  const float w_lane = topk_w[min(lane, k - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t av[kActLoads];
+#pragma unroll
+  for (int m = 0; m < kActLoads; m++) {
+    const int gi = min(wave + kDownWaves * m, k * GI - 1);
+    av[m] = *reinterpret_cast<const uint32_t*>(act + (size_t)(gi / GI) * I + (gi % GI) * 128 + 2 * lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int e_lane = local_expert(id_lane, offset, L);
+
+  // 2. the wave's W2 units (past the last: repeats of it, cache hits).  A
+  //    unit of a masked route reads a line of the SwiGLU buffer instead (in
+  //    cache) and its result is dropped.
+  int eu[kUnitsPerWave];
+#pragma unroll
+  for (int i = 0; i < kUnitsPerWave; i++) {
+    const int u = min(wave + kDownWaves * i, n_units - 1);
+    eu[i] = __builtin_amdgcn_readlane(e_lane, (int)(((uint32_t)u * dl_magic) >> 16));
+  }
+  uint4 wb[kUnitsPerWave];
+  const uint8_t* spare = reinterpret_cast<const uint8_t*>(act) + min(16 * lane, k * I * 2 - 16);
+#pragma unroll
+  for (int i = 0; i < kUnitsPerWave; i++) {
+    const int u = min(wave + kDownWaves * i, n_units - 1);
+    const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
+    const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
+    const uint8_t* src = eu[i] >= 0 ? w2 + ((size_t)eu[i] * H + row) * I + kof : spare;
+    wb[i] = *reinterpret_cast<const uint4*>(src);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float wsc[kUnitsPerWave];
+#pragma unroll
+  for (int i = 0; i < kUnitsPerWave; i++) {
+    const int u = min(wave + kDownWaves * i, n_units - 1);
+    const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
+    const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
+    wsc[i] = w2_s[((size_t)max(eu[i], 0) * G + row / 128) * GI + kof / 128];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. the live routes' SwiGLU groups quantised into LDS (same arithmetic as
+  //    silu_and_mul_quant_fp8) while W2 is in flight
+#pragma unroll
+  for (int m = 0; m < kActLoads; m++) {
+    const int gi = wave + kDownWaves * m, jq = min(gi / GI, k - 1), g = gi % GI;
+    if (gi < k * GI && __builtin_amdgcn_readlane(e_lane, jq) >= 0) {
+      const float a0 = bf16_to_f32(av[m] & 0xFFFFu), a1 = bf16_to_f32(av[m] >> 16);
+      const float sc = group_scale(group_max<64>(fmaxf(fabsf(a0), fabsf(a1))), fmt);
+      s_qh[jq][g * 64 + lane] = quant2(a0, a1, sc);
+      if (lane == 0) s_qs[jq][g] = sc;
+    }
   }
   wg_sync();
 
-  // 2. this workgroup's active-expert slot: the distinct live experts in
-  //    ascending order.  Lane r < k of wave 0 works out route r's rank
-  //    (vector code: the scalar unit is shared by all waves of the CU).
-  if (wave == 0) {
-    int ev[kMaxK];
-    {
-      const int4 a = *reinterpret_cast<const int4*>(s_e), b = *reinterpret_cast<const int4*>(s_e + 4);
-      ev[0] = a.x; ev[1] = a.y; ev[2] = a.z; ev[3] = a.w; ev[4] = b.x; ev[5] = b.y; ev[6] = b.z; ev[7] = b.w;
-    }
-    const int r = min(lane, kMaxK - 1);
-    int er = ev[0];
+  // 4. down projection: each row's dot product with its route's quantised
+  //    SwiGLU row, both block scales applied per group, reduced over the row's
+  //    lanes; live rows go to s_y as BF16 values
+  float v[kUnitsPerWave];
 #pragma unroll
-    for (int q = 1; q < kMaxK; q++) er = r == q ? ev[q] : er;
-    bool first = lane < kMaxK && er >= 0;
-    int rank = 0;
+  for (int i = 0; i < kUnitsPerWave; i++) {
+    const int u = min(wave + kDownWaves * i, n_units - 1);
+    const int j = (int)(((uint32_t)u * dl_magic) >> 16);
+    v[i] = dot16(wb[i], &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * wsc[i]);
+  }
 #pragma unroll
-    for (int q = 0; q < kMaxK; q++) {
-      bool q_first = ev[q] >= 0;
+  for (int i = 0; i < kUnitsPerWave; i++) v[i] = group_sum<kLpr>(v[i]);
 #pragma unroll
-      for (int p2 = 0; p2 < q; p2++) q_first = q_first && ev[p2] != ev[q];
-      first = first && !(q < r && ev[q] == er);
-      rank += (q_first && ev[q] < er) ? 1 : 0;
-    }
-    const uint64_t firsts = __ballot(first);
-    if (lane < kMaxK) s_slot[lane] = rank;  // a route's expert has this rank among the distinct live experts
-    if (first && rank == slot) s_expert = er;
-    if (lane == 0) s_nslots = __popcll(firsts);
+  for (int i = 0; i < kUnitsPerWave; i++) {
+    const int u = wave + kDownWaves * i;
+    const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
+    const int rl = c * kRpl + lane / kLpr;
+    if (u < n_units && eu[i] >= 0 && lane % kLpr == 0 && d0 + rl < d_end) s_y[j][rl] = bf16_to_f32(f32_to_bf16(v[i]));
   }
   wg_sync();
-  const int e = __builtin_amdgcn_readfirstlane(s_expert);  // -1: no gate/up unit
-  const int n_slots = __builtin_amdgcn_readfirstlane(s_nslots);
-  const uint32_t T = s_tag;
 
-  const int e_ld = e >= 0 ? e : 0;  // a workgroup without a slot loads expert 0 and discards it
-  const int rb0 = min(d0, H - 1) / 128, rb1 = min(max(d_end - 1, d0), H - 1) / 128;
-
-  if (wave >= 8) {
-    // 3. down waves: block-scale tables into LDS, one load per thread: W13
-    //    scales of the gate and up row blocks (entries 0 .. 2G-1), then the
-    //    W2 scales of this unit's (at most two) row blocks for every route
-    {
-      const int n_tab = 2 * G + k * 2 * GI;
-      const int blk_gate = n0 / 128, blk_up = (I + n0) / 128;
-      const int t0 = tid - 512;
-      const int t = t0 - n_tab * (int)(((uint32_t)t0 * tab_magic) >> 20);  // t0 mod n_tab
-      const float* src;
-      if (t < 2 * G) {
-        src = w13_s + ((size_t)e_ld * (2 * I / 128) + (t < G ? blk_gate : blk_up)) * G + (t < G ? t : t - G);
-      } else {
-        const int q = t - 2 * G;
-        const int j = q / (2 * GI), which = (q / GI) & 1, g2 = q % GI;
-        const int ej = s_e[j] >= 0 ? s_e[j] : 0;
-        src = w2_s + ((size_t)ej * G + (which ? rb1 : rb0)) * GI + g2;
-      }
-      s_tab[t0 < n_tab ? t0 : kTabSlots - 1] = *src;  // past the tables: the spare slot
-    }
-    wg_sync();
-    if (d0 >= H) return;
-    // 4. their W2 units into LDS, queued behind the W13 loads of the
-    //    gate/up waves
-    issue_w2<I>(s_w2, wave, k, DL, dl_magic, s_e, w2, H, d0, lane);
-    __builtin_amdgcn_s_waitcnt(0);  // the W2 units are in LDS
-  } else {
-    // 4. gate/up wave w: column n = n0 + w, i.e. gate row n and up row I + n
-    //    of expert e, requested as soon as the slot is known
-    uint4 wg[RL], wu[RL];
-    {
-      // every chunk but the last lies inside the row; the last is clamped
-      const uint8_t* gsrc = w13 + ((size_t)e_ld * 2 * I + n0 + wave) * H;
-      const uint8_t* usrc = gsrc + (size_t)I * H;
-      const int last = min(1024 * (RL - 1) + 16 * lane, H - 16);
+  // 5. weighted reduction over the live routes, j ascending, by wave 0 (rows
+  //    tid < DR <= 64).  The routing comes from the wave's own lanes, read
+  //    while every lane is active; every s_y read is issued before the first
+  //    is used.
+  float wr[kMaxK];
+  bool lr[kMaxK];
 #pragma unroll
-      for (int c = 0; c < RL; c++) {
-        const int off = c < RL - 1 ? 1024 * c + 16 * lane : last;
-        wg[c] = *reinterpret_cast<const uint4*>(gsrc + off);
-        wu[c] = *reinterpret_cast<const uint4*>(usrc + off);
-      }
-    }
-    wg_sync();  // the tables are in LDS
-
-    // 5. gate and up dot products as the data lands, then SwiGLU on their
-    //    BF16 values
-    float ag = 0.0f, au = 0.0f;
-#pragma unroll
-    for (int c = 0; c < RL; c++) {
-      const int kof = 1024 * c + 16 * lane;  // past H only in the last chunk: its terms are dropped
-      const float as = s_as[kof / 128];
-      float pg = dot16(wg[c], s_ah + kof / 2) * (as * s_tab[kof / 128]);
-      float pu = dot16(wu[c], s_ah + kof / 2) * (as * s_tab[G + kof / 128]);
-      if (c == RL - 1 && kof >= H) pg = pu = 0.0f;
-      ag += pg;
-      au += pu;
-    }
-    ag = group_sum<64>(ag);
-    au = group_sum<64>(au);
-    if (e >= 0) {
-      // the last of the 8 gate/up waves to finish writes the workgroup's
-      // 8 columns, tagged, to every copy
-      const float g = bf16_to_f32(f32_to_bf16(ag)), u = bf16_to_f32(f32_to_bf16(au));
-      const uint32_t h = f32_to_bf16(swiglu_bf16(g, u, limit, clamp != 0));
-      int done = 0;
-      if (lane == 0) {
-        s_pub[wave] = h;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        done = atomicAdd(&s_pub_count, 1);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      }
-      done = __builtin_amdgcn_readfirstlane(done);
-      if (done == kWaves / 2 - 1 && lane < 4) {
-        const uint64_t word = (uint64_t)(s_pub[2 * lane] | (s_pub[2 * lane + 1] << 16)) | ((uint64_t)T << 32);
-#pragma unroll
-        for (int x = 0; x < kReplicas; x++) ATOMIC_ST(&st->act[x][slot * (kMaxI / 2) + n0 / 2 + lane], word);
-      }
-    }
-    if (e < 0 && wave == 0 && lane < 16) ATOMIC_ST(&st->flag[blockIdx.x][lane], T);
-    if (d0 >= H) return;  // the whole workgroup leaves: no down unit
-    // 6. SwiGLU rows into LDS, quantised
-    take_groups<I>(st, rep, wave, k, s_e, s_slot, n_slots, T, fmt, s_qh, s_qs, lane);
+  for (int r = 0; r < kMaxK; r++) {
+    lr[r] = r < k && __builtin_amdgcn_readlane(e_lane, r) >= 0;
+    wr[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), r));
   }
-  wg_sync();  // the quantised SwiGLU rows are in LDS
-
-  // 7. down projection, shared by all 16 waves, then the route rows in s_y
-  down_units<I>(s_w2, wave, k, DL, dl_magic, s_e, s_tab, s_qh, s_qs, s_y, G, H, d0, d_end, rb0, lane);
-  wg_sync();
-  if (blockIdx.x == 0 && tid < kReplicas) ATOMIC_ST(&st->gen[tid][0], T);  // every workgroup has read gen
-
-  // 8. weighted reduction over the routes, j ascending
   if (tid < d_end - d0) {
+    float y[kMaxK];
+#pragma unroll
+    for (int r = 0; r < kMaxK; r++) y[r] = s_y[r][tid];
     float a = 0.0f;
-    for (int j = 0; j < k; j++)
-      if (s_e[j] >= 0) a = __builtin_fmaf(s_w[j], s_y[j][tid], a);
+#pragma unroll
+    for (int r = 0; r < kMaxK; r++)
+      if (lr[r]) a = __builtin_fmaf(wr[r], y[r], a);
     out[d0 + tid] = (uint16_t)f32_to_bf16(a);
   }
 }
 
-// rows of the down unit: the smallest multiple of the rows per 1 KB load that
-// covers H with at most `units` workgroups
-int token_down_rows(int H, int I, int units) {
-  const int rpl = 1024 / I;
-  int dr = (H + units - 1) / units;
-  dr = (dr + rpl - 1) / rpl * rpl;
-  return dr;
-}
-
 }  // namespace
 
-int token_kernel_grid(int H, int k, int32_t L, int I) {
-  const int slots = k < L ? k : L;
-  const int up = slots * (I / 8);
-  const int dr = token_down_rows(H, I, up);
-  const int down = (H + dr - 1) / dr;
-  return up > down ? up : down;
+// Rows per down workgroup: a multiple of the rows of one 1 KB load (1024 / I)
+// giving about 256 workgroups, with at most 64 units and 64 rows per
+// workgroup.
+int token_down_rows(int H, int I, int k) {
+  const int rpl = 1024 / I;
+  int dl = ((H + kDownTarget - 1) / kDownTarget + rpl - 1) / rpl;
+  dl = dl < kMaxUnits / k ? dl : kMaxUnits / k;
+  dl = dl < kMaxDownRows / rpl ? dl : kMaxDownRows / rpl;
+  return (dl > 1 ? dl : 1) * rpl;
 }
 
-bool token_path_fits(int64_t M, int H, int k, int32_t L, int I, int num_cus) {
-  if (M != 1 || k < 1 || k > kMaxK || H > kMaxH || H % 128 != 0) return false;
-  if (!(I == 128 || I == 256 || I == 512)) return false;
-  const int slots = k < L ? k : L;
-  const int up = slots * (I / 8);
-  const int dr = token_down_rows(H, I, up);
-  if (dr > 64 || dr * I / 1024 > kMaxDownLoads) return false;
-  if (k * (dr * I / 1024) > 8 * kW2PerWave) return false;  // W2 units of the 8 down waves
-  const int grid = token_kernel_grid(H, k, L, I);
-  return grid <= num_cus && grid <= kMaxGrid;
+bool token_path_fits(int64_t M, int H, int k, int I) {
+  if (M != 1 || k < 1 || k > kMaxK || H < 128 || H > kMaxH || H % 128 != 0) return false;
+  return I == 128 || I == 256 || I == 512;
 }
 
 hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids, const float* topk_w, int k,
                               int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s, const uint8_t* w2,
-                              const float* w2_s, int I, int fmt, float limit, void* state, uint16_t* out,
+                              const float* w2_s, int I, int fmt, float limit, uint16_t* act, uint16_t* out,
                               hipStream_t stream, const LaunchHook* hook) {
+  if (!token_path_fits(1, H, k, I)) return hipErrorInvalidValue;  // the caller checks token_path_fits
   const int clamp = __builtin_isfinite(limit) ? 1 : 0;
-  const int slots = k < L ? k : L;
-  const int dr = token_down_rows(H, I, slots * (I / 8));
-  const int grid = token_kernel_grid(H, k, L, I);
-  const int rl = (H + 1023) / 1024, dl = dr * I / 1024;
-  if (!(I == 128 || I == 256 || I == 512) || rl < 1 || rl > kMaxRowLoads || dl < 1 || dl > kMaxDownLoads || k * dl > 8 * kW2PerWave)
-    return hipErrorInvalidValue;  // token_path_fits rules these out
-  // exact quotients by multiply and shift: u / dl for u < 64 and t / n_tab for
-  // t < 1024 (the rounding error of the multiplier stays below one step)
+  const int rl = (H + 1023) / 1024;
+  const int dr = token_down_rows(H, I, k);
+  const int dl = dr * I / 1024;
+  // u / dl for u < 64 by multiply and shift (exact: the multiplier's rounding
+  // error stays below one step for such u)
   const uint32_t dl_magic = (65536u + dl - 1) / dl;
-  const uint32_t n_tab = 2 * (H / 128) + k * 2 * (I / 128);
-  const uint32_t tab_magic = ((1u << 20) + n_tab - 1) / n_tab;
+  const int up_grid = k * (I / 8);
+  const int down_grid = (H + dr - 1) / dr;
   if (hook) hook->before(0, stream);
-#define BFP8_TOKEN_CASE(N, II)                                                                               \
-  case N:                                                                                                    \
-    hipLaunchKernelGGL((token_layer_kernel<N, II>), dim3(grid), dim3(kThreads), 0, stream, hidden, H, ids,   \
-                       topk_w, k, offset, L, w13, w13_s, w2, w2_s, fmt, limit, clamp, dr, dl, dl_magic,     \
-                       tab_magic, static_cast<TokenState*>(state), out);                                     \
+  const bool run0 = !hook || hook->run(0), run1 = !hook || hook->run(1);
+#define BFP8_TOKEN_CASE(N, II)                                                                                  \
+  case N:                                                                                                       \
+    hipLaunchKernelGGL((token_gate_up_kernel<N, II>), dim3(up_grid), dim3(kUpThreads), 0, stream, hidden, H,    \
+                       ids, offset, L, w13, w13_s, fmt, limit, clamp, act);                                     \
     break;
-#define BFP8_TOKEN_RL(II)                                                                                    \
-  switch (rl) {                                                                                              \
-    BFP8_TOKEN_CASE(1, II)                                                                                   \
-    BFP8_TOKEN_CASE(2, II)                                                                                   \
-    BFP8_TOKEN_CASE(3, II)                                                                                   \
-    BFP8_TOKEN_CASE(4, II)                                                                                   \
-    BFP8_TOKEN_CASE(5, II)                                                                                   \
-    BFP8_TOKEN_CASE(6, II)                                                                                   \
-    BFP8_TOKEN_CASE(7, II)                                                                                   \
-    BFP8_TOKEN_CASE(8, II)                                                                                   \
+#define BFP8_TOKEN_RL(II)   \
+  switch (rl) {             \
+    BFP8_TOKEN_CASE(1, II)  \
+    BFP8_TOKEN_CASE(2, II)  \
+    BFP8_TOKEN_CASE(3, II)  \
+    BFP8_TOKEN_CASE(4, II)  \
+    BFP8_TOKEN_CASE(5, II)  \
+    BFP8_TOKEN_CASE(6, II)  \
+    BFP8_TOKEN_CASE(7, II)  \
+    BFP8_TOKEN_CASE(8, II)  \
   }
-  if (I == 128) {
+  if (!run0) {
+  } else if (I == 128) {
     BFP8_TOKEN_RL(128)
   } else if (I == 256) {
     BFP8_TOKEN_RL(256)
@@ -581,7 +441,21 @@ hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids,
 #undef BFP8_TOKEN_RL
 #undef BFP8_TOKEN_CASE
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (hook) hook->before(1, stream);
+#define BFP8_TOKEN_DOWN(II)                                                                                    \
+  hipLaunchKernelGGL((token_down_kernel<II>), dim3(down_grid), dim3(kDownThreads), 0, stream, act, ids, topk_w, \
+                     k, offset, L, w2, w2_s, H, fmt, dr, dl, dl_magic, out)
+  if (!run1) {
+  } else if (I == 128)
+    BFP8_TOKEN_DOWN(128);
+  else if (I == 256)
+    BFP8_TOKEN_DOWN(256);
+  else
+    BFP8_TOKEN_DOWN(512);
+#undef BFP8_TOKEN_DOWN
+  e = hipGetLastError();
+  if (hook) hook->before(2, stream);
   return e;
 }
 

@@ -74,8 +74,16 @@ enum {
     BFP8MOE_FLAG_ROUTE_MULTI_WG = 1u << 1,   /* route prep: count -> scan+scatter over many workgroups */
     BFP8MOE_FLAG_LAYER_GENERAL = 1u << 2,    /* fused layer: staged general path */
     BFP8MOE_FLAG_LAYER_DECODE = 1u << 3,     /* fused layer: small-batch two-kernel path */
-    BFP8MOE_FLAG_LAYER_TOKEN = 1u << 4       /* fused layer: one-token single-kernel path */
+    BFP8MOE_FLAG_LAYER_TOKEN = 1u << 4,      /* fused layer: one-token two-kernel path */
+    BFP8MOE_FLAG_STAGE_SHIFT = 8             /* flags bits 8..11, see BFP8MOE_FLAG_ONLY_STAGE */
 };
+/* Test and profiling switch of the fused layer: launch only stage s (0-based,
+ * in the order fused_moe_block_fp8_stages lists them) of the path the call
+ * takes, reading and writing the workspace exactly as a whole call does.  A
+ * stage past the first reads what the earlier stages of a whole call with
+ * the same arguments and workspace left there; stage 0 needs nothing.  Lets
+ * a profiler time one kernel on its own.  s past the last stage is rejected. */
+#define BFP8MOE_FLAG_ONLY_STAGE(s) ((uint32_t)((s) + 1) << BFP8MOE_FLAG_STAGE_SHIFT)
 
 /* Options of the fused layer.  Initialise with bfp8moe_opts_init(). */
 typedef struct {
@@ -228,8 +236,8 @@ bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_
 /* Number of stages (kernel launches, route preparation counted as one) a
  * fused_moe_block_fp8 call with these sizes and options makes on the current
  * device, and, when names is non-NULL, up to cap stage names (static strings)
- * in order.  The one-token path has one stage ("decode_token"); the
- * small-batch path two ("decode_gate_up_swiglu", "decode_down_reduce"); the
+ * in order.  The one-token path has two stages ("token_gate_up_swiglu",
+ * "token_down_reduce"); the small-batch path two ("decode_gate_up_swiglu", "decode_down_reduce"); the
  * general path six ("route_prepare", "quant_fp8", "gate_up_gemm",
  * "silu_and_mul_quant", "down_gemm", "moe_reduce").  Returns -1 for arguments
  * fused_moe_block_fp8 would reject. */
@@ -250,20 +258,16 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
  * The hidden states and the SwiGLU output are both quantised with
  * opts->scale_fmt.  H and I must be positive multiples of 128.  ws: device
  * workspace of at least fused_moe_block_fp8_workspace_size() bytes, 256-byte
- * aligned.  Its first 172032 bytes hold launch state of the one-token kernel
- * that must be ZERO before the first call with that workspace (allocate it
- * zero-filled once); calls keep it valid, and no other use of the workspace
- * touches those bytes, so one workspace serves any mix of calls.  Calls that
- * share a workspace must not run concurrently.  opts: host pointer (NULL =
- * defaults).
+ * aligned; its contents need no initialisation and are not kept between
+ * calls.  Calls that share a workspace must not run concurrently.  opts: host
+ * pointer (NULL = defaults).
  * Three implementations, chosen by shape unless a test flag forces one:
- *   one token (M = 1, k <= 8, H <= 8192, I <= 512, and a grid of
- *     max(min(k, L) * I/8, H/32) workgroups that fits one per compute unit):
- *     a single persistent kernel -- route grouping, input quantisation,
- *     gate/up GEMM and SwiGLU, whose output words carry a launch tag; each
- *     workgroup then waits for the tagged words it needs, quantises them and
- *     runs its share of the down GEMM and moe_reduce, with its down weights
- *     requested before the gate/up work;
+ *   one token (M = 1, k <= 8, H <= 8192, I in {128, 256, 512}): two
+ *     matrix-vector kernels -- input quantisation, gate/up GEMM and SwiGLU
+ *     per route (k x I/8 workgroups, one column per wave); then the SwiGLU
+ *     output's quantisation, down GEMM and moe_reduce per block of output
+ *     rows (about 256 workgroups), each issuing its down weight loads as soon
+ *     as it has read the routing;
  *   small batch (M <= 8, k <= 8, H <= 8192, I <= 512): two kernels -- gate/up
  *     GEMM with route grouping, input quantisation and SwiGLU fused; then the
  *     SwiGLU output's quantisation, down GEMM and moe_reduce fused;

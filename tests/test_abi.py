@@ -45,7 +45,9 @@ def test_opts_layout_and_defaults():
 
 def test_stage_lists():
     o = bfp8.opts()
-    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == ["decode_token"]
+    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
+    # the one-token path needs I in {128, 256, 512}; other shapes fall back
+    assert bfp8.fused_moe_stages(1, 4096, 8, 256, 384, o) == ["decode_gate_up_swiglu", "decode_down_reduce"]
     assert bfp8.fused_moe_stages(4, 7168, 8, 256, 256, o) == ["decode_gate_up_swiglu", "decode_down_reduce"]
     assert bfp8.fused_moe_stages(512, 4096, 8, 256, 768, o)[2] == "gate_up_gemm"
     assert len(bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_GENERAL))) == 6
@@ -99,6 +101,10 @@ def test_host_validation_rejects_bad_calls():
     st, msg = _status(L.fused_moe_block_fp8, fake, 1, 7168, fake, fake, 8, fake, fake, fake, fake, 256, 256,
                       ctypes.byref(o), fake, fake, 16, None)
     assert st == 3 and "workspace" in msg
+    o = bfp8.opts(flags=bfp8.FLAG_ONLY_STAGE(2))  # the one-token path has two stages
+    st, msg = _status(L.fused_moe_block_fp8, fake, 1, 7168, fake, fake, 8, fake, fake, fake, fake, 256, 256,
+                      ctypes.byref(o), fake, fake, 1 << 30, None)
+    assert st == 1 and "stage 2" in msg
     st, msg = _status(L.moe_reduce, fake, fake, None, 0, 0, 2, 8, 100, fake, None)
     assert st == 1 and "multiple of 8" in msg
 

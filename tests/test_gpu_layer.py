@@ -117,34 +117,79 @@ def test_one_token_masked_and_duplicate_experts(path):
 
 
 def test_workspace_shared_across_paths():
-    # one zero-filled workspace used by the one-token, small-batch and general
-    # paths in turn, twice: the one-token launch state survives every mix
+    # one workspace, filled with NaN bytes first (its contents need no
+    # initialisation), used by the one-token, small-batch and general paths in
+    # turn, twice
     print_case("workspace shared")
     c = synth.LAYER_CASES["decode_m1"]
     hidden, ids, w, W = synth.layer_inputs(c, 6, device=dev())
     ref = _oracle_on_tokens(c, hidden, ids, w, W, [0], c.scale_fmt, c.clamp)
     sizes = [bfp8.fused_moe_workspace_size(1, c.H, c.k, c.E, c.I, bfp8.opts(flags=f)) for f in PATHS]
-    ws = torch.zeros(max(sizes), dtype=torch.uint8, device=dev())
+    ws = torch.full((max(sizes),), 0xFF, dtype=torch.uint8, device=dev())
     for _ in range(2):
         for f in [bfp8.FLAG_LAYER_TOKEN, bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE, bfp8.FLAG_LAYER_TOKEN]:
             out = bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E,
                                            o=bfp8.opts(flags=f), ws=ws)
             torch.cuda.synchronize()
             assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
-    # the expiry word is clear, every copy of gen holds the last launch's tag
-    # and no flag is ahead of it
-    st = _token_state(ws)
-    gen = int(st["gen"][0])
-    assert st["expired"] == 0 and gen > 0 and (st["gen"] == gen).all()
-    assert (st["flag"] <= gen).all()
 
 
-def _token_state(ws):
-    """The one-token kernel's launch state at the start of a workspace: gen
-    (8 copies, one per 128-byte line), the expiry word, and from byte 8192
-    one 64-byte flag piece per workgroup."""
-    head = ws[:8192 + 64 * 512].view(torch.int32).cpu()
-    return {"gen": head[0:256:32], "expired": int(head[256]), "flag": head[2048::16]}
+@pytest.mark.parametrize("path", PATHS)
+def test_stages_run_one_at_a_time(path):
+    # BFP8MOE_FLAG_ONLY_STAGE: the stages of a path launched one by one on one
+    # workspace give the whole call's output bit for bit, and a later stage
+    # alone reads what a whole call left in the workspace
+    print_case("stages one at a time", path)
+    c = synth.LAYER_CASES["decode_m1"]
+    hidden, ids, w, W = synth.layer_inputs(c, 7, device=dev())
+    o = bfp8.opts(flags=path)
+    n = len(bfp8.fused_moe_stages(1, c.H, c.k, c.E, c.I, o))
+    ws = torch.empty(bfp8.fused_moe_workspace_size(1, c.H, c.k, c.E, c.I, o), dtype=torch.uint8, device=dev())
+    whole = bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E, o=o, ws=ws)
+    out = torch.zeros_like(whole)
+    for s_ in range(n):
+        bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E,
+                                 o=bfp8.opts(flags=path | bfp8.FLAG_ONLY_STAGE(s_)), ws=ws, out=out)
+    last = torch.zeros_like(whole)
+    bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E,
+                             o=bfp8.opts(flags=path | bfp8.FLAG_ONLY_STAGE(n - 1)), ws=ws, out=last)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), whole.view(torch.int16))
+    assert torch.equal(last.view(torch.int16), whole.view(torch.int16))
+
+
+def test_one_token_local_slice():
+    # one token under expert parallelism: only the routes whose expert lies in
+    # [offset, offset + L) count (the others are skipped by both kernels, on a
+    # NaN-filled workspace), and a token with no local route gives zeros
+    print_case("one token local slice")
+    c = synth.LayerCase("tok_slice", M=1, E=64, k=8, H=2048, I=256, routing="uniform")
+    hidden, ids, w, W = synth.layer_inputs(c, 4, device=dev())
+    off, L = 16, 24
+    ids = ids.clone()
+    ids[0] = torch.tensor([3, 17, 40, 63, 20, -1, 39, 16], dtype=ids.dtype)
+    Wl = synth.MoEWeights(W.w13[off:off + L].contiguous(), W.w13_s[off:off + L].contiguous(),
+                          W.w2[off:off + L].contiguous(), W.w2_s[off:off + L].contiguous())
+    for e in (17, 20, 39, 16):
+        if W.real is not None and e not in W.real:
+            cw, sw = synth.block_fp8_weight(2 * c.I, c.H, "slice", e, device=dev())
+            Wl.w13[e - off].copy_(cw); Wl.w13_s[e - off].copy_(sw)
+            cw, sw = synth.block_fp8_weight(c.H, c.I, "slice2", e, device=dev())
+            Wl.w2[e - off].copy_(cw); Wl.w2_s[e - off].copy_(sw)
+    o = bfp8.opts(expert_offset=off, local_num_experts=L, flags=bfp8.FLAG_LAYER_TOKEN)
+    need = bfp8.fused_moe_workspace_size(1, c.H, c.k, c.E, c.I, o)
+    for case_ids in (ids, torch.full_like(ids, 5)):
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev())
+        out = bfp8.fused_moe_block_fp8(hidden, case_ids, w, Wl.w13, Wl.w13_s, Wl.w2, Wl.w2_s, E=c.E, o=o, ws=ws)
+        torch.cuda.synchronize()
+        ref = O.fused_moe(hidden.cpu(), case_ids.cpu(), w.cpu(), Wl.w13.cpu(), Wl.w13_s.cpu(), Wl.w2.cpu(),
+                          Wl.w2_s.cpu(), expert_offset=off, L=L)
+        got = bf16_np(out)
+        if (case_ids == 5).all():
+            assert (got == 0).all()
+        else:
+            assert np.abs(ref).max() > 0
+            assert normwise_err(got, ref) <= LAYER_TOL
 
 
 @pytest.mark.parametrize("path", [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE])
@@ -182,8 +227,9 @@ def test_layer_rejects_bad_arguments():
         bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=c.E, ws=small)
 
 
-# one-token shapes other than the decode workload: every load count of the
-# kernel's W13 rows and W2 pieces, grids from 32 to 256 workgroups
+# one-token shapes other than the decode workload: W13 rows of 1 to 8 loads,
+# I = 128, 256 and 512 (1 KB W2 units of 8, 4 and 2 rows), down workgroups of
+# 8 to 32 rows
 TOKEN_SHAPES = [
     synth.LayerCase("tok_h256_i128_k2", M=1, E=8, k=2, H=256, I=128, routing="uniform"),
     synth.LayerCase("tok_h2048_i128_k4", M=1, E=16, k=4, H=2048, I=128, routing="uniform"),
@@ -196,8 +242,8 @@ TOKEN_SHAPES = [
 @pytest.mark.parametrize("c", TOKEN_SHAPES, ids=lambda c: c.name)
 def test_one_token_shapes(c):
     print_case("one-token shape", c.name)
-    if bfp8.fused_moe_stages(1, c.H, c.k, c.E, c.I, bfp8.opts()) != ["decode_token"]:
-        pytest.skip("shape outside the one-token kernel on this device")
+    assert bfp8.fused_moe_stages(1, c.H, c.k, c.E, c.I, bfp8.opts()) == ["token_gate_up_swiglu",
+                                                                        "token_down_reduce"]
     hidden, ids, w, W = synth.layer_inputs(c, 0, device=dev())
     ref = _oracle_on_tokens(c, hidden, ids, w, W, [0], bfp8.SCALE_UE8M0, 7.0)
     out = _run(c, hidden, ids, w, W, scale_fmt=bfp8.SCALE_UE8M0, clamp_limit=7.0, flags=bfp8.FLAG_LAYER_TOKEN)
@@ -205,8 +251,7 @@ def test_one_token_shapes(c):
 
 
 def test_one_token_grid_changes_on_one_workspace():
-    # launches with different grids share one workspace: the tags and the
-    # per-workgroup flags stay consistent however the grid changes
+    # launches with different grids share one workspace
     print_case("one-token grid changes")
     cases = [TOKEN_SHAPES[0], synth.LAYER_CASES["decode_m1"], TOKEN_SHAPES[1], TOKEN_SHAPES[0]]
     data = []
@@ -223,4 +268,3 @@ def test_one_token_grid_changes_on_one_workspace():
                                            o=bfp8.opts(flags=bfp8.FLAG_LAYER_TOKEN), ws=ws)
             torch.cuda.synchronize()
             assert normwise_err(bf16_np(out), ref) <= LAYER_TOL, c.name
-    assert _token_state(ws)["expired"] == 0  # no wait ran out
