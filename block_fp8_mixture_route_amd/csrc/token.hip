@@ -18,7 +18,8 @@
 //
 // gate/up kernel: workgroup (route j, slice q) computes columns n = 8 q .. 8 q
 //   + 7 of route j's SwiGLU row, one column (gate row n and up row I + n) per
-//   wave, each written as one BF16 value into act[j].
+//   column wave, each written as one BF16 value into act[j]; the other 8
+//   waves prepare the quantised hidden row in LDS.
 // down kernel: workgroup b computes output rows DR b .. DR b + DR - 1 for all
 //   k routes from its W2 pieces (1 KB units: route, kRpl rows of I bytes),
 //   quantises the k SwiGLU rows itself, and ends with the weighted reduction.
@@ -45,7 +46,9 @@ namespace bfp8 {
 
 namespace {
 
-constexpr int kUpThreads = 512;     // gate/up kernel: 8 waves, one column each
+constexpr int kUpThreads = 1024;    // gate/up kernel: 8 column waves + 8 hidden-row waves
+constexpr int kUpWaves = kUpThreads / 64;
+constexpr int kColumnWaves = 8;
 constexpr int kDownThreads = 1024;  // down kernel: 16 waves
 constexpr int kDownWaves = kDownThreads / 64;
 constexpr int kMaxK = 8;
@@ -54,6 +57,7 @@ constexpr int kUnitsPerWave = 4;                            // 1 KB W2 units per
 constexpr int kMaxUnits = kDownWaves * kUnitsPerWave;       // per down workgroup
 constexpr int kMaxDownRows = 64;
 constexpr int kDownTarget = 256;  // down workgroups aimed at (one per compute unit of MI355X)
+constexpr unsigned kSpinLimit = 1u << 20;  // bound of the LDS waits (about 0.03 s)
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
@@ -158,12 +162,16 @@ __device__ __forceinline__ int local_expert(int32_t id, int32_t offset, int32_t 
 
 // ------------------------------------------------------------------ gate/up
 //
-// Workgroup (route j, slice q), wave w: column n = 8 q + w of route j, i.e. the
-// dot products of the quantised hidden row with gate row n and up row I + n of
-// route j's expert, both block scales applied per group of 128, then SwiGLU on
-// their BF16 values, stored as act[j][n].  All loads go out before any data is used: the hidden
-// row, one block-scale entry per thread, then the wave's 2 x RL 1 KB row
-// loads.
+// Workgroup (route j, slice q) computes columns 8 q .. 8 q + 7 of route j's
+// SwiGLU row.  Waves 0-7 own one column n = 8 q + w each: the dot products of
+// the quantised hidden row with gate row n and up row I + n of route j's
+// expert, both block scales applied per group of 128, then SwiGLU on their
+// BF16 values, stored as act[j][n].  Waves 8-15 quantise the hidden row and
+// load the block-scale table into LDS and count themselves done in an LDS
+// word.  The column waves wait for that word, not for a workgroup barrier: a
+// barrier would also wait for every column wave to have issued its loads,
+// which the compute unit's memory queue holds back for microseconds, and no
+// wave could start its dot products before then.
 template <int RL, int I>
 __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
     const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, int32_t offset, int32_t L,
@@ -173,32 +181,68 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   __shared__ __align__(16) h2 s_ah[kMaxH / 2];  // quantised hidden row (E4M3 values as FP16)
   __shared__ float s_as[kMaxH / 128];           // its group scales
   __shared__ float s_tab[2 * (kMaxH / 128)];    // W13 block scales: gate row block, then up row block
+  __shared__ int s_ready;                       // hidden-row waves done
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H / 128;
   const int j = blockIdx.x / kSlices;
   const int n0 = (blockIdx.x - j * kSlices) * 8;
+  if (tid == 0) s_ready = 0;
   const int e = local_expert(ids[j], offset, L);
   if (e < 0) return;  // route outside the local slice: it contributes nothing
 
-  // 1. loads.  Hidden groups tid/16 and tid/16 + 32, 8 values per lane; the
-  //    indices are clamped so that every load is unconditional (a load in a
-  //    branch makes the compiler wait for it where the branch joins).
-  const int l16 = tid & 15;
+  // the small operands, loaded by every wave (the column waves' copies go
+  // unused) so that the loads are unconditional: hidden groups t/16 and
+  // t/16 + 32 (t = tid % 512), 8 values per lane, and one W13 block-scale
+  // entry per thread.  Clamped lanes repeat the last group.
+  // The pointers pass through empty asm statements: loads through a
+  // restrict pointer count as invariant, and the compiler would otherwise
+  // sink them past the barrier into the only branch that uses them.
+  const int t = tid & 511, l16 = t & 15;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const u32x4* g_u32x4;
+  typedef __attribute__((address_space(1))) const float* g_float;
+  g_u32x4 hid = (g_u32x4)hidden;  // global address space kept: generic loads would count as LDS traffic too
+  g_float ws13 = (g_float)w13_s;
+  asm volatile("" : "+s"(hid), "+s"(ws13));
   uint4 hv[2];
 #pragma unroll
   for (int p = 0; p < 2; p++) {
-    const int hg = min((tid >> 4) + 32 * p, G - 1);
-    hv[p] = *reinterpret_cast<const uint4*>(hidden + (size_t)hg * 128 + l16 * 8);
+    const int hg = min((t >> 4) + 32 * p, G - 1);
+    const u32x4 x = hid[(size_t)hg * 16 + l16];
+    hv[p] = make_uint4(x.x, x.y, x.z, x.w);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  const int t = min(tid, 2 * G - 1);
-  const float tab = w13_s[((size_t)e * (2 * I / 128) + (t < G ? n0 / 128 : (I + n0) / 128)) * G + (t < G ? t : t - G)];
-  __builtin_amdgcn_sched_barrier(0);
+  const int te = min(t, 2 * G - 1);
+  const float tab =
+      ws13[((size_t)e * (2 * I / 128) + (te < G ? n0 / 128 : (I + n0) / 128)) * G + (te < G ? te : te - G)];
+  // every wave's small loads have left before any W13 load: the compute
+  // unit returns data roughly in issue order, so they land first
+  wg_sync();
+
+  if (wave >= kColumnWaves) {
+    // hidden-row waves: quantise into LDS (same arithmetic as quant_fp8),
+    // store the table, and count themselves done
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      const int hg = min((t >> 4) + 32 * p, G - 1);
+      float f[8];
+      unpack8(hv[p], f);
+      const float sc = group_scale(max_over_16(amax8(f)), fmt);
+      quant_store8(f, sc, s_ah + (hg * 128 + l16 * 8) / 2);
+      if (l16 == 0) s_as[hg] = sc;
+    }
+    s_tab[te] = tab;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS stores are done
+    if (lane == 0) __hip_atomic_fetch_add(&s_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return;
+  }
+
+  // column waves: the gate and up rows of column n0 + wave, 2 x RL 1 KB
+  // loads, all issued before any data is used (every chunk but the last lies
+  // inside the row; the last is clamped)
   uint4 wg[RL], wu[RL];
   {
-    // every chunk but the last lies inside the row; the last is clamped
     const uint8_t* gsrc = w13 + ((size_t)e * 2 * I + n0 + wave) * H;
     const uint8_t* usrc = gsrc + (size_t)I * H;
     const int last = min(1024 * (RL - 1) + 16 * lane, H - 16);
@@ -210,25 +254,15 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  // the hidden row and the table are in LDS (bounded wait; a run-out leaves
+  // the column's value unspecified but ends the kernel)
+  for (unsigned spins = 0;
+       __hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kUpWaves - kColumnWaves &&
+       spins < kSpinLimit;
+       spins++)
+    __builtin_amdgcn_s_sleep(1);
 
-  // 2. the hidden row group-quantised into LDS (same arithmetic as
-  //    quant_fp8) while the weight rows are in flight; the scale table too.
-  //    Clamped lanes repeat the last group's values and stores, so nothing
-  //    here is conditional (a branch would let the compiler move a load into
-  //    it, behind the weight loads).
-#pragma unroll
-  for (int p = 0; p < 2; p++) {
-    const int hg = min((tid >> 4) + 32 * p, G - 1);
-    float f[8];
-    unpack8(hv[p], f);
-    const float sc = group_scale(max_over_16(amax8(f)), fmt);
-    quant_store8(f, sc, s_ah + (hg * 128 + l16 * 8) / 2);
-    if (l16 == 0) s_as[hg] = sc;
-  }
-  s_tab[t] = tab;
-  wg_sync();
-
-  // 3. gate and up dot products as the data lands
+  // gate and up dot products as the data lands
   float ag = 0.0f, au = 0.0f;
 #pragma unroll
   for (int c = 0; c < RL; c++) {
@@ -243,8 +277,7 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   ag = group_sum<64>(ag);
   au = group_sum<64>(au);
 
-  // 4. SwiGLU of the BF16 gate/up outputs; each wave stores its column (no
-  //    barrier: a wave leaves as soon as its own data has landed)
+  // SwiGLU of the BF16 gate/up outputs; each wave stores its column
   const float g = bf16_to_f32(f32_to_bf16(ag)), u = bf16_to_f32(f32_to_bf16(au));
   if (lane == 0) act[(size_t)j * I + n0 + wave] = (uint16_t)f32_to_bf16(swiglu_bf16(g, u, limit, clamp != 0));
 }
