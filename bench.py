@@ -1,6 +1,7 @@
 """Benchmark of the block-FP8 fused MoE layer on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config decode_m1] [--instances N]
+    python bench.py --suite out.json   # every config + act/quant + route prep + copy
 
 A step is one fused_moe_block_fp8 call (route preparation, gate/up GEMM,
 SwiGLU + quantisation, down GEMM, moe_reduce) on one batch.  The workload is
@@ -14,10 +15,9 @@ between a device synchronisation on both sides.
 
 Printed: one JSON line with the metric (achieved HBM GB/s of the whole layer
 from its compulsory bytes), microseconds per layer, the roofline of the
-dominant kernel (its algorithmic bytes over its average duration: the
-graph-timed step when the layer is that one kernel, otherwise HIP events the
-library records between its launches, in eager calls queued back to back
-behind a GPU spin), the kernel's HBM traffic from the hardware-counter
+dominant kernel (its algorithmic bytes over its average duration, that
+kernel launched alone back to back from a HIP graph, timed with HIP events on
+its stream), the kernel's HBM traffic from the hardware-counter
 summary in profiles/ while the kernel's sources match it, and the CPU oracle
 timed on a bounded sample of the same workload.
 """
@@ -156,54 +156,49 @@ def stage_bytes(case, ids, stage):
     return w + case.M * H + case.M * (H // 128) * 4 + R * 4 + R * 2 * I * 2
 
 
-# ------------------------------------------------------------------ main
+# ------------------------------------------------------------------ one layer config
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=480)
-    ap.add_argument("--warmup", type=int, default=48)
-    ap.add_argument("--config", default="decode_m1")
-    ap.add_argument("--instances", type=int, default=0, help="layer instances to rotate over (0 = auto)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="first run 4 plain device copies of this many MiB (a known-size reference for "
-                         "hardware traffic counters)")
-    args = ap.parse_args()
+FP8_PEAK_TFLOPS = 5000.0  # dense FP8 MFMA
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
-              file=sys.stderr)
-        sys.exit(2)
 
+def layer_flops(case):
+    """Multiply-add flops of the two projections over all routes."""
+    return 2 * case.M * case.k * (2 * case.I * case.H + case.H * case.I)
+
+
+def time_graph(hip, stream, body, reps):
+    """Capture body() into a HIP graph, replay it once untimed, then time
+    `reps` replays with HIP events on `stream`; milliseconds per replay."""
+    _, g = hip.capture(stream, body)
+    hip.launch(g, stream)
+    hip.sync(stream)
+    ev0, ev1 = hip.event(), hip.event()
+    hip.sync()
+    hip.record(ev0, stream)
+    for _ in range(reps):
+        hip.launch(g, stream)
+    hip.record(ev1, stream)
+    hip.sync()
+    return hip.elapsed_ms(ev0, ev1) / reps
+
+
+def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=True):
+    """Graph-timed fused_moe_block_fp8 on `case`, rotating over independent
+    instances; optionally each stage alone.  Returns a dict of figures and the
+    instances (for the CPU leg)."""
     import torch
 
     import block_fp8_mixture_route_amd as bfp8
     from block_fp8_mixture_route_amd import synth
 
-    case = synth.LAYER_CASES[args.config]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"copy calibration: 4 copies of {args.calibrate_copy_mib} MiB")
-
     # one instance first, to size the rotation
     t0 = time.time()
     first = synth.layer_inputs(case, 0, device=dev)
     b0, d0 = layer_bytes(case, first[1])
-    n_inst = args.instances or max(1, min(64, math.ceil(4 * MALL_BYTES / b0)))
+    n_inst = instances or max(1, min(64, math.ceil(4 * MALL_BYTES / b0)))
     insts = [first] + [synth.layer_inputs(case, i, device=dev) for i in range(1, n_inst)]
     torch.cuda.synchronize()
-    log(f"{args.config}: {n_inst} instances generated in {time.time() - t0:.1f}s, "
+    log(f"{case.name}: {n_inst} instances generated in {time.time() - t0:.1f}s, "
         f"{b0 / 1e6:.2f} MB compulsory per layer (instance 0, {d0} active experts)")
 
     o = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp)
@@ -213,9 +208,6 @@ def main():
     outs = [torch.empty(case.M, case.H, dtype=torch.bfloat16, device=dev) for _ in range(n_inst)]
     bytes_per = [layer_bytes(case, x[1])[0] for x in insts]
     torch.cuda.synchronize()
-
-    hip = Hip()
-    stream = hip.stream()
     L = bfp8.lib()
     P = ctypes.c_void_p
 
@@ -228,18 +220,17 @@ def main():
                                               ws_bytes, stream))
 
     # warm-up: W eager steps
-    for s in range(args.warmup):
-        call(s % n_inst, o)
+    for s_ in range(warmup):
+        call(s_ % n_inst, o)
     hip.sync(stream)
-    log(f"warm-up {args.warmup} steps done; stages: {stages}")
+    log(f"warm-up {warmup} steps done; stages: {stages}")
 
     # graph of one rotation (+ a partial rotation so that exactly K steps run)
-    full, rem = divmod(args.steps, n_inst)
+    full, rem = divmod(steps, n_inst)
     _, g_rot = hip.capture(stream, lambda: [call(i, o) for i in range(n_inst)])
     g_rem = hip.capture(stream, lambda: [call(i, o) for i in range(rem)])[1] if rem else None
     hip.launch(g_rot, stream)  # one untimed replay to settle the graph
     hip.sync(stream)
-
     ev0, ev1 = hip.event(), hip.event()
     hip.sync()
     hip.record(ev0, stream)
@@ -263,20 +254,188 @@ def main():
     # reads what the whole calls above left in the workspace (same code path
     # and traffic; the values are not checked here).
     stage_us = {}
-    reps = max(1, math.ceil(args.steps / n_inst))
-    for s_, name in enumerate(stages):
-        os_ = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=bfp8.FLAG_ONLY_STAGE(s_))
-        _, g_s = hip.capture(stream, lambda: [call(i, os_) for i in range(n_inst)])
-        hip.launch(g_s, stream)  # untimed replay
-        hip.sync(stream)
-        hip.record(ev0, stream)
-        for _ in range(reps):
-            hip.launch(g_s, stream)
-        hip.record(ev1, stream)
-        hip.sync()
-        stage_us[name] = hip.elapsed_ms(ev0, ev1) * 1e3 / (reps * n_inst)
-    log("stage us (each stage alone, graph-timed): " + ", ".join(f"{k}={v:.2f}" for k, v in stage_us.items()))
+    if per_stage:
+        reps = max(1, math.ceil(steps / n_inst))
+        for s_, name in enumerate(stages):
+            os_ = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=bfp8.FLAG_ONLY_STAGE(s_))
+            stage_us[name] = time_graph(hip, stream, lambda: [call(i, os_) for i in range(n_inst)], reps) * 1e3 / n_inst
+        log("stage us (each stage alone, graph-timed): " + ", ".join(f"{k}={v:.2f}" for k, v in stage_us.items()))
+    mean_bytes = sum(bytes_per) / n_inst
+    roof_us = max(mean_bytes / (HBM_PEAK_GBS * 1e3), layer_flops(case) / (FP8_PEAK_TFLOPS * 1e6))
+    return {"us_per_layer": ms_per_step * 1e3, "ms_per_step": ms_per_step, "gbs": gbs, "steps": steps,
+            "n_inst": n_inst, "bytes_per_layer": mean_bytes, "flops_per_layer": layer_flops(case),
+            "roofline_us": roof_us, "roofline_frac": roof_us / (ms_per_step * 1e3), "stages": stages,
+            "stage_us": stage_us, "insts": insts, "active_experts_inst0": d0}
 
+
+# ------------------------------------------------------------------ suite
+
+SUITE_STEPS = {"tiny": 200, "decode_m1": 480, "decode_m4": 200, "decode_m16": 100, "decode_m32": 100,
+               "small_m128": 20, "small_m512": 20, "large_m2048": 10}
+
+
+def suite(hip, stream, dev):
+    """Every layer config, the activation+quant workload (fused against two
+    kernels), route preparation (one workgroup against many) and a plain copy
+    as the practical bandwidth ceiling.  Prints markdown tables; returns the
+    figures."""
+    import torch
+
+    import block_fp8_mixture_route_amd as bfp8
+    from block_fp8_mixture_route_amd import synth
+
+    L_ = bfp8.lib()
+    P = ctypes.c_void_p
+    ext = torch.cuda.ExternalStream(stream.value, device=dev)
+    res = {"layers": {}, "act_quant": {}, "route_prep": {}, "copy": {}}
+
+    print("| config | M | E | k | H | I | path | µs / layer | GB/s | roofline µs | fraction | stages µs (each alone) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for name, case in synth.LAYER_CASES.items():
+        r = measure_layer(case, SUITE_STEPS.get(name, 50), 4, 0, hip, stream, dev)
+        r.pop("insts")
+        res["layers"][name] = r
+        st = ", ".join(f"{k} {v:.2f}" for k, v in r["stage_us"].items())
+        path = "one token" if r["stages"][0].startswith("token") else (
+            "small batch" if r["stages"][0].startswith("decode") else "general")
+        print(f"| {name} | {case.M} | {case.E} | {case.k} | {case.H} | {case.I} | {path} | {r['us_per_layer']:.2f} | "
+              f"{r['gbs']:.0f} | {r['roofline_us']:.2f} | {r['roofline_frac']:.3f} | {st} |", flush=True)
+        torch.cuda.empty_cache()
+
+    # activation + quant (warm, like the pages): fused kernel against SwiGLU
+    # then quant_fp8 as two launches
+    print()
+    print("| tokens | rows | fused µs | two kernels µs | speedup | fused GB/s (unmasked rows) |")
+    print("|---|---|---|---|---|---|")
+    I = synth.ACT_I
+    for tok in synth.ACT_TOKENS:
+        rows = tok * 8
+        gu, rid = synth.act_rows(rows, I, synth.ACT_E, "bench", tok, device=dev)
+        q = torch.empty(rows, I, dtype=torch.uint8, device=dev)
+        sc = torch.empty(rows, I // 128, dtype=torch.float32, device=dev)
+        h = torch.empty(rows, I, dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+        def fused():
+            bfp8._lib.check(L_.silu_and_mul_quant_fp8(P(gu.data_ptr()), rows, I, P(rid.data_ptr()), None,
+                                                      synth.ACT_E, synth.ACT_CLAMP, bfp8.SCALE_UE8M0,
+                                                      P(q.data_ptr()), P(sc.data_ptr()), stream))
+
+        def two():
+            bfp8._lib.check(L_.silu_and_mul(P(gu.data_ptr()), rows, I, synth.ACT_CLAMP, P(h.data_ptr()), stream))
+            bfp8._lib.check(L_.quant_fp8(P(h.data_ptr()), rows, I, bfp8.SCALE_UE8M0, P(q.data_ptr()),
+                                         P(sc.data_ptr()), stream))
+
+        tf = time_graph(hip, stream, lambda: [fused() for _ in range(20)], 20) * 1e3 / 20
+        t2 = time_graph(hip, stream, lambda: [two() for _ in range(20)], 20) * 1e3 / 20
+        live = int(((rid >= 0) & (rid < synth.ACT_E)).sum().item())
+        nbytes = live * (4 * I + I + 4 * (I // 128))
+        res["act_quant"][tok] = {"rows": rows, "fused_us": tf, "two_kernel_us": t2}
+        print(f"| {tok} | {rows} | {tf:.2f} | {t2:.2f} | {t2 / tf:.2f} | {nbytes / (tf * 1e3):.0f} |", flush=True)
+
+    # route preparation: single workgroup against count + scan/scatter
+    print()
+    print("| routes R | local experts L | block_m | one workgroup µs | many workgroups µs |")
+    print("|---|---|---|---|---|")
+    for (R, L, bm, routing) in [(8, 256, 16, "uniform"), (1024, 256, 16, "mixed"), (4096, 256, 32, "mixed"),
+                                (16384, 512, 64, "zipf")]:
+        M = R // 8
+        c = synth.LayerCase("rp", M=M, E=L, k=8, H=128, I=128, routing=routing, zipf_s=1.0 if routing == "zipf" else 1.2)
+        ids, _ = synth.routing_for(c, "bench_rp", device=dev)
+        ids = ids.reshape(-1).contiguous()
+        mb = bfp8.max_blocks(R, L, bm)
+        outs = [torch.empty(max(n, 1), dtype=torch.int32, device=dev) for n in (R, L + 1, mb, mb, 1)]
+        row = []
+        for flags in (bfp8.FLAG_ROUTE_SINGLE_WG, bfp8.FLAG_ROUTE_MULTI_WG):
+            wsb = L_.moe_route_prepare_workspace_size(R, L, flags)
+            wsr = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
+
+            def rp(flags=flags, wsr=wsr, wsb=wsb):
+                bfp8._lib.check(L_.moe_route_prepare(P(ids.data_ptr()), R, 0, L, bm, *[P(t.data_ptr()) for t in outs[:4]],
+                                                     mb, P(outs[4].data_ptr()), P(wsr.data_ptr()), wsb, flags, stream))
+
+            try:
+                row.append(time_graph(hip, stream, lambda: [rp() for _ in range(20)], 20) * 1e3 / 20)
+            except bfp8.BFP8MoEError:
+                row.append(float("nan"))  # outside that variant's limits
+        res["route_prep"][R] = {"L": L, "block_m": bm, "single_us": row[0], "multi_us": row[1]}
+        print(f"| {R} | {L} | {bm} | {row[0]:.2f} | {row[1]:.2f} |", flush=True)
+
+    # a plain device copy of the decode layer's size, rotating over buffers
+    # that together exceed the Infinity Cache: the practical HBM ceiling
+    nbytes = 44 << 20
+    nbuf = 12
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2 * nbuf)]
+    for b_ in bufs:
+        b_.fill_(1)
+    torch.cuda.synchronize()
+
+    def copies():
+        with torch.cuda.stream(ext):
+            for i in range(nbuf):
+                bufs[2 * i + 1].copy_(bufs[2 * i])
+
+    tc = time_graph(hip, stream, copies, 10) / nbuf
+    res["copy"] = {"bytes": nbytes, "us": tc * 1e3, "gbs_read_plus_write": 2 * nbytes / (tc * 1e-3) / 1e9}
+    print()
+    print(f"plain copy of {nbytes >> 20} MiB: {tc * 1e3:.2f} µs, {2 * nbytes / (tc * 1e-3) / 1e9:.0f} GB/s "
+          f"(read + write)", flush=True)
+    return res
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--config", default="decode_m1")
+    ap.add_argument("--instances", type=int, default=0, help="layer instances to rotate over (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run 4 plain device copies of this many MiB (a known-size reference for "
+                         "hardware traffic counters)")
+    ap.add_argument("--suite", metavar="JSON", default=None,
+                    help="instead of the metric line: every layer config, activation+quant, route preparation "
+                         "and a plain copy, as markdown tables on stdout and figures in JSON")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_fp8_mixture_route_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = Hip()
+    stream = hip.stream()
+
+    if args.suite:
+        res = suite(hip, stream, dev)
+        with open(args.suite, "w") as f:
+            json.dump(res, f, indent=1, default=str)
+        return
+
+    case = synth.LAYER_CASES[args.config]
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: 4 copies of {args.calibrate_copy_mib} MiB")
+
+    r = measure_layer(case, args.steps, args.warmup, args.instances, hip, stream, dev)
+    insts, stage_us, n_inst = r["insts"], r["stage_us"], r["n_inst"]
     dom = next(s_ for s_ in ("token_gate_up_swiglu", "decode_gate_up_swiglu", "gate_up_gemm") if s_ in stage_us)
     dom_bytes = sum(stage_bytes(case, x[1], dom) for x in insts) / n_inst
     dom_us = stage_us[dom]
@@ -290,16 +449,15 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, insts[0], args.cpu_seconds)
 
-    hidden0, ids0 = insts[0][0], insts[0][1]
     line = {
         "metric": METRIC,
-        "value": round(gbs, 1),
+        "value": round(r["gbs"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": r["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
-        "us_per_layer": round(ms_per_step * 1e3, 3),
+        "ms_per_step": round(r["ms_per_step"], 6),
+        "us_per_layer": round(r["us_per_layer"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -309,8 +467,8 @@ def main():
             "workload": f"{case.name}: M={case.M} E={case.E} top-k={case.k} H={case.H} I={case.I} "
                         f"{case.routing} routing, {'UE8M0' if case.scale_fmt else 'fp32'} activation scales",
             "M": case.M, "E": case.E, "top_k": case.k, "hidden": case.H, "intermediate": case.I,
-            "instances": n_inst, "bytes_per_layer": int(sum(bytes_per) / n_inst),
-            "hbm_roofline_us": round(sum(bytes_per) / n_inst / (HBM_PEAK_GBS * 1e3), 3),
+            "instances": n_inst, "bytes_per_layer": int(r["bytes_per_layer"]),
+            "hbm_roofline_us": round(r["bytes_per_layer"] / (HBM_PEAK_GBS * 1e3), 3),
         },
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": roofline,
