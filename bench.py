@@ -182,7 +182,10 @@ def time_graph(hip, stream, body, reps):
     return hip.elapsed_ms(ev0, ev1) / reps
 
 
-def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=True):
+PATH_FLAGS = {"auto": 0, "token": 1 << 4, "decode": 1 << 3, "general": 1 << 2}
+
+
+def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=True, flags=0):
     """Graph-timed fused_moe_block_fp8 on `case`, rotating over independent
     instances; optionally each stage alone.  Returns a dict of figures and the
     instances (for the CPU leg)."""
@@ -201,7 +204,7 @@ def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=Tr
     log(f"{case.name}: {n_inst} instances generated in {time.time() - t0:.1f}s, "
         f"{b0 / 1e6:.2f} MB compulsory per layer (instance 0, {d0} active experts)")
 
-    o = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp)
+    o = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=flags)
     stages = bfp8.fused_moe_stages(case.M, case.H, case.k, case.E, case.I, o)
     ws_bytes = bfp8.fused_moe_workspace_size(case.M, case.H, case.k, case.E, case.I, o)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -257,7 +260,7 @@ def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=Tr
     if per_stage:
         reps = max(1, math.ceil(steps / n_inst))
         for s_, name in enumerate(stages):
-            os_ = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=bfp8.FLAG_ONLY_STAGE(s_))
+            os_ = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=flags | bfp8.FLAG_ONLY_STAGE(s_))
             stage_us[name] = time_graph(hip, stream, lambda: [call(i, os_) for i in range(n_inst)], reps) * 1e3 / n_inst
         log("stage us (each stage alone, graph-timed): " + ", ".join(f"{k}={v:.2f}" for k, v in stage_us.items()))
     mean_bytes = sum(bytes_per) / n_inst
@@ -291,12 +294,17 @@ def suite(hip, stream, dev):
 
     print("| config | M | E | k | H | I | path | µs / layer | GB/s | roofline µs | fraction | stages µs (each alone) |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|")
-    for name, case in synth.LAYER_CASES.items():
-        r = measure_layer(case, SUITE_STEPS.get(name, 50), 4, 0, hip, stream, dev)
+    runs = [(name, case, 0) for name, case in synth.LAYER_CASES.items()]
+    # the other paths where they apply, forced (the default picks one by M)
+    runs += [(f"{n} (forced)", synth.LAYER_CASES[n], f) for n, f in
+             [("decode_m4", PATH_FLAGS["decode"]), ("decode_m4", PATH_FLAGS["general"]),
+              ("decode_m16", PATH_FLAGS["general"]), ("decode_m32", PATH_FLAGS["general"])]]
+    for name, case, flags in runs:
+        r = measure_layer(case, SUITE_STEPS.get(name.split()[0], 50), 4, 0, hip, stream, dev, flags=flags)
         r.pop("insts")
-        res["layers"][name] = r
+        res["layers"][name + (f" flags {flags}" if flags else "")] = r
         st = ", ".join(f"{k} {v:.2f}" for k, v in r["stage_us"].items())
-        path = "one token" if r["stages"][0].startswith("token") else (
+        path = "few tokens" if r["stages"][0].startswith("token") else (
             "small batch" if r["stages"][0].startswith("decode") else "general")
         print(f"| {name} | {case.M} | {case.E} | {case.k} | {case.H} | {case.I} | {path} | {r['us_per_layer']:.2f} | "
               f"{r['gbs']:.0f} | {r['roofline_us']:.2f} | {r['roofline_frac']:.3f} | {st} |", flush=True)
@@ -398,6 +406,8 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run 4 plain device copies of this many MiB (a known-size reference for "
                          "hardware traffic counters)")
+    ap.add_argument("--path", choices=sorted(PATH_FLAGS), default="auto",
+                    help="force one implementation of the layer (default: the library's choice by shape)")
     ap.add_argument("--suite", metavar="JSON", default=None,
                     help="instead of the metric line: every layer config, activation+quant, route preparation "
                          "and a plain copy, as markdown tables on stdout and figures in JSON")
@@ -434,7 +444,7 @@ def main():
         del src, dst
         log(f"copy calibration: 4 copies of {args.calibrate_copy_mib} MiB")
 
-    r = measure_layer(case, args.steps, args.warmup, args.instances, hip, stream, dev)
+    r = measure_layer(case, args.steps, args.warmup, args.instances, hip, stream, dev, flags=PATH_FLAGS[args.path])
     insts, stage_us, n_inst = r["insts"], r["stage_us"], r["n_inst"]
     dom = next(s_ for s_ in ("token_gate_up_swiglu", "decode_gate_up_swiglu", "gate_up_gemm") if s_ in stage_us)
     dom_bytes = sum(stage_bytes(case, x[1], dom) for x in insts) / n_inst

@@ -69,14 +69,15 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
 // Small-batch path of the fused layer: gate/up + SwiGLU kernel, then down +
 // moe_reduce kernel.  act: [M*k, I] BF16 scratch.
 bool decode_path_fits(int64_t M, int H, int k, int I);
-// One-token path: gate/up + SwiGLU kernel, then down + moe_reduce kernel, both
-// matrix-vector streaming kernels.  act: [k, I] BF16 scratch.
+// Few-token path: gate/up + SwiGLU kernel per route, then down + moe_reduce
+// kernel per token, both matrix-vector streaming kernels (each route reads its
+// expert's rows).  act: [M*k, I] BF16 scratch.
 bool token_path_fits(int64_t M, int H, int k, int I);
 int device_cu_count();  // of the current device; 0 when there is none
-hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids, const float* topk_w, int k,
-                              int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s, const uint8_t* w2,
-                              const float* w2_s, int I, int fmt, float limit, uint16_t* act, uint16_t* out,
-                              hipStream_t stream, const LaunchHook* hook);
+hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
+                              int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
+                              const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
+                              uint16_t* out, hipStream_t stream, const LaunchHook* hook);
 hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
                                int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
                                const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,

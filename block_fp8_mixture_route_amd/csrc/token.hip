@@ -1,5 +1,5 @@
-// token.hip -- the block-FP8 MoE layer for one token (M = 1) on gfx950 as two
-// weight-streaming kernels.
+// token.hip -- the block-FP8 MoE layer for a few tokens (M <= 32, the decode
+// regime) on gfx950 as two weight-streaming kernels.
 //
 // [P1 Motivation] at M = 1, top-k 8, E = 256 at most eight experts are active
 // and the layer is pure weight streaming: 44 MB of W13 + W2 at the 7168 x 256
@@ -17,12 +17,16 @@
 // reduction, routes in order.
 //
 // gate/up kernel: workgroup (route j, slice q) computes columns n = 8 q .. 8 q
-//   + 7 of route j's SwiGLU row, one column (gate row n and up row I + n) per
-//   column wave, each written as one BF16 value into act[j]; the other 8
-//   waves prepare the quantised hidden row in LDS.
-// down kernel: workgroup b computes output rows DR b .. DR b + DR - 1 for all
-//   k routes from its W2 pieces (1 KB units: route, kRpl rows of I bytes),
-//   quantises the k SwiGLU rows itself, and ends with the weighted reduction.
+//   + 7 of route j's SwiGLU row (route j = t k + r belongs to token t), one
+//   column (gate row n and up row I + n) per column wave, each written as one
+//   BF16 value into act[j]; the other 8 waves prepare the token's quantised
+//   hidden row in LDS.  Each route reads its expert's rows: with top-k routing
+//   the routes of one token have distinct experts, and at a few tokens the
+//   rows that two tokens share are a small part of the stream.
+// down kernel: workgroup (b, t) computes output rows DR b .. DR b + DR - 1 of
+//   token t for its k routes from their W2 pieces (1 KB units: route, kRpl
+//   rows of I bytes), quantises the k SwiGLU rows itself, and ends with the
+//   weighted reduction.
 //
 // The kernel boundary is the only exchange.  Within one kernel a compute unit
 // serves its memory requests roughly in order, so any store or poll that hands
@@ -52,6 +56,7 @@ constexpr int kColumnWaves = 8;
 constexpr int kDownThreads = 1024;  // down kernel: 16 waves
 constexpr int kDownWaves = kDownThreads / 64;
 constexpr int kMaxK = 8;
+constexpr int kMaxTokens = 32;  // tokens per call on this path
 constexpr int kMaxH = 8192;
 constexpr int kUnitsPerWave = 4;                            // 1 KB W2 units per down wave
 constexpr int kMaxUnits = kDownWaves * kUnitsPerWave;       // per down workgroup
@@ -174,7 +179,7 @@ __device__ __forceinline__ int local_expert(int32_t id, int32_t offset, int32_t 
 // wave could start its dot products before then.
 template <int RL, int I>
 __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
-    const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, int32_t offset, int32_t L,
+    const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, int k, int32_t offset, int32_t L,
     const uint8_t* __restrict__ w13, const float* __restrict__ w13_s, int fmt, float limit, int clamp,
     uint16_t* __restrict__ act) {
   constexpr int kSlices = I / 8;
@@ -203,7 +208,9 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(1))) const u32x4* g_u32x4;
   typedef __attribute__((address_space(1))) const float* g_float;
-  g_u32x4 hid = (g_u32x4)hidden;  // global address space kept: generic loads would count as LDS traffic too
+  // global address space kept: generic loads would count as LDS traffic too;
+  // route j belongs to token j / k
+  g_u32x4 hid = (g_u32x4)(hidden + (size_t)(j / k) * H);
   g_float ws13 = (g_float)w13_s;
   asm volatile("" : "+s"(hid), "+s"(ws13));
   uint4 hv[2];
@@ -309,6 +316,11 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
   const int d0 = blockIdx.x * DR, d_end = min(H, d0 + DR);
   const int n_units = k * DL;
   const int kof = 16 * (lane % kLpr);
+  // token blockIdx.y: its k routes, their SwiGLU rows, its output row
+  ids += (size_t)blockIdx.y * k;
+  topk_w += (size_t)blockIdx.y * k;
+  act += (size_t)blockIdx.y * k * I;
+  out += (size_t)blockIdx.y * H;
 
   // 1. the route ids (lane r: route min(r, k - 1)), then the SwiGLU groups
   //    gi = wave + 16 m (route gi / GI, group gi % GI; lane l takes columns
@@ -427,15 +439,15 @@ int token_down_rows(int H, int I, int k) {
 }
 
 bool token_path_fits(int64_t M, int H, int k, int I) {
-  if (M != 1 || k < 1 || k > kMaxK || H < 128 || H > kMaxH || H % 128 != 0) return false;
+  if (M < 1 || M > kMaxTokens || k < 1 || k > kMaxK || H < 128 || H > kMaxH || H % 128 != 0) return false;
   return I == 128 || I == 256 || I == 512;
 }
 
-hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids, const float* topk_w, int k,
-                              int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s, const uint8_t* w2,
-                              const float* w2_s, int I, int fmt, float limit, uint16_t* act, uint16_t* out,
-                              hipStream_t stream, const LaunchHook* hook) {
-  if (!token_path_fits(1, H, k, I)) return hipErrorInvalidValue;  // the caller checks token_path_fits
+hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
+                              int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
+                              const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
+                              uint16_t* out, hipStream_t stream, const LaunchHook* hook) {
+  if (!token_path_fits(M, H, k, I)) return hipErrorInvalidValue;  // the caller checks token_path_fits
   const int clamp = __builtin_isfinite(limit) ? 1 : 0;
   const int rl = (H + 1023) / 1024;
   const int dr = token_down_rows(H, I, k);
@@ -443,14 +455,14 @@ hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids,
   // u / dl for u < 64 by multiply and shift (exact: the multiplier's rounding
   // error stays below one step for such u)
   const uint32_t dl_magic = (65536u + dl - 1) / dl;
-  const int up_grid = k * (I / 8);
+  const int up_grid = (int)M * k * (I / 8);
   const int down_grid = (H + dr - 1) / dr;
   if (hook) hook->before(0, stream);
   const bool run0 = !hook || hook->run(0), run1 = !hook || hook->run(1);
 #define BFP8_TOKEN_CASE(N, II)                                                                                  \
   case N:                                                                                                       \
     hipLaunchKernelGGL((token_gate_up_kernel<N, II>), dim3(up_grid), dim3(kUpThreads), 0, stream, hidden, H,    \
-                       ids, offset, L, w13, w13_s, fmt, limit, clamp, act);                                     \
+                       ids, k, offset, L, w13, w13_s, fmt, limit, clamp, act);                                  \
     break;
 #define BFP8_TOKEN_RL(II)   \
   switch (rl) {             \
@@ -477,7 +489,8 @@ hipError_t launch_token_layer(const uint16_t* hidden, int H, const int32_t* ids,
   if (e != hipSuccess) return e;
   if (hook) hook->before(1, stream);
 #define BFP8_TOKEN_DOWN(II)                                                                                    \
-  hipLaunchKernelGGL((token_down_kernel<II>), dim3(down_grid), dim3(kDownThreads), 0, stream, act, ids, topk_w, \
+  hipLaunchKernelGGL((token_down_kernel<II>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0, stream, act,  \
+                     ids, topk_w,                                                                              \
                      k, offset, L, w2, w2_s, H, fmt, dr, dl, dl_magic, out)
   if (!run1) {
   } else if (I == 128)

@@ -74,7 +74,7 @@ enum {
     BFP8MOE_FLAG_ROUTE_MULTI_WG = 1u << 1,   /* route prep: count -> scan+scatter over many workgroups */
     BFP8MOE_FLAG_LAYER_GENERAL = 1u << 2,    /* fused layer: staged general path */
     BFP8MOE_FLAG_LAYER_DECODE = 1u << 3,     /* fused layer: small-batch two-kernel path */
-    BFP8MOE_FLAG_LAYER_TOKEN = 1u << 4,      /* fused layer: one-token two-kernel path */
+    BFP8MOE_FLAG_LAYER_TOKEN = 1u << 4,      /* fused layer: few-token two-kernel path */
     BFP8MOE_FLAG_STAGE_SHIFT = 8             /* flags bits 8..11, see BFP8MOE_FLAG_ONLY_STAGE */
 };
 /* Test and profiling switch of the fused layer: launch only stage s (0-based,
@@ -236,7 +236,7 @@ bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_
 /* Number of stages (kernel launches, route preparation counted as one) a
  * fused_moe_block_fp8 call with these sizes and options makes on the current
  * device, and, when names is non-NULL, up to cap stage names (static strings)
- * in order.  The one-token path has two stages ("token_gate_up_swiglu",
+ * in order.  The few-token path has two stages ("token_gate_up_swiglu",
  * "token_down_reduce"); the small-batch path two ("decode_gate_up_swiglu", "decode_down_reduce"); the
  * general path six ("route_prepare", "quant_fp8", "gate_up_gemm",
  * "silu_and_mul_quant", "down_gemm", "moe_reduce").  Returns -1 for arguments
@@ -262,12 +262,13 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
  * calls.  Calls that share a workspace must not run concurrently.  opts: host
  * pointer (NULL = defaults).
  * Three implementations, chosen by shape unless a test flag forces one:
- *   one token (M = 1, k <= 8, H <= 8192, I in {128, 256, 512}): two
- *     matrix-vector kernels -- input quantisation, gate/up GEMM and SwiGLU
- *     per route (k x I/8 workgroups, one column per wave); then the SwiGLU
- *     output's quantisation, down GEMM and moe_reduce per block of output
- *     rows (about 256 workgroups), each issuing its down weight loads as soon
- *     as it has read the routing;
+ *   few tokens (M <= 32, k <= 8, H <= 8192, I in {128, 256, 512}; the
+ *     default up to 32 tokens): two matrix-vector kernels -- input
+ *     quantisation, gate/up GEMM and SwiGLU per route (M x k x I/8
+ *     workgroups; each route reads its expert's rows), then the SwiGLU
+ *     output's quantisation, down GEMM and moe_reduce per token and block of
+ *     output rows (about 256 workgroups per token), each issuing its down
+ *     weight loads as soon as it has read the routing;
  *   small batch (M <= 8, k <= 8, H <= 8192, I <= 512): two kernels -- gate/up
  *     GEMM with route grouping, input quantisation and SwiGLU fused; then the
  *     SwiGLU output's quantisation, down GEMM and moe_reduce fused;

@@ -82,10 +82,10 @@ PATHS = [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE, bfp8.FLAG_LAYER_TOKEN]
 def test_layer_paths_fmt_clamp(case, path, fmt, clamp):
     print_case("layer path", case, path, fmt, clamp)
     c, hidden, ids, w, W = _inputs(case, 1)
-    if path == bfp8.FLAG_LAYER_TOKEN and c.M != 1:
+    if path == bfp8.FLAG_LAYER_TOKEN and c.M > 32:
         with pytest.raises(bfp8.BFP8MoEError) as ei:
             _run(c, hidden, ids, w, W, flags=path)
-        assert ei.value.status == 2  # unsupported: the one-token path needs M = 1
+        assert ei.value.status == 2  # unsupported: the few-token path takes at most 32 tokens
         return
     toks = list(range(c.M))
     ref = _oracle_on_tokens(c, hidden, ids, w, W, toks, fmt, clamp)
@@ -158,6 +158,18 @@ def test_stages_run_one_at_a_time(path):
     assert torch.equal(last.view(torch.int16), whole.view(torch.int16))
 
 
+@pytest.mark.parametrize("case", ["decode_m16", "decode_m32"])
+def test_few_token_path_at_its_limits(case):
+    # the few-token path forced at 16 and 32 tokens (each route reads its
+    # expert's rows; tokens share experts), sampled tokens against the oracle
+    print_case("few-token path", case)
+    c, hidden, ids, w, W = _inputs(case, 2)
+    toks = _tokens(case, c.M)
+    ref = _oracle_on_tokens(c, hidden, ids, w, W, toks, c.scale_fmt, c.clamp)
+    out = _run(c, hidden, ids, w, W, scale_fmt=c.scale_fmt, clamp_limit=c.clamp, flags=bfp8.FLAG_LAYER_TOKEN)
+    assert normwise_err(bf16_np(out)[toks], ref) <= LAYER_TOL
+
+
 def test_one_token_local_slice():
     # one token under expert parallelism: only the routes whose expert lies in
     # [offset, offset + L) count (the others are skipped by both kernels, on a
@@ -192,7 +204,7 @@ def test_one_token_local_slice():
             assert normwise_err(got, ref) <= LAYER_TOL
 
 
-@pytest.mark.parametrize("path", [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE])
+@pytest.mark.parametrize("path", [bfp8.FLAG_LAYER_GENERAL, bfp8.FLAG_LAYER_DECODE, bfp8.FLAG_LAYER_TOKEN])
 def test_layer_masked_routes_and_local_slice(path):
     # ids outside the local slice [offset, offset + L) are skipped; a token
     # whose routes are all non-local gives zeros
