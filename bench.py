@@ -185,7 +185,7 @@ def time_graph(hip, stream, body, reps):
 PATH_FLAGS = {"auto": 0, "token": 1 << 4, "decode": 1 << 3, "general": 1 << 2}
 
 
-def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=True, flags=0):
+def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=True, flags=0, block_m=0):
     """Graph-timed fused_moe_block_fp8 on `case`, rotating over independent
     instances; optionally each stage alone.  Returns a dict of figures and the
     instances (for the CPU leg)."""
@@ -204,7 +204,7 @@ def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=Tr
     log(f"{case.name}: {n_inst} instances generated in {time.time() - t0:.1f}s, "
         f"{b0 / 1e6:.2f} MB compulsory per layer (instance 0, {d0} active experts)")
 
-    o = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=flags)
+    o = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=flags, block_m=block_m)
     stages = bfp8.fused_moe_stages(case.M, case.H, case.k, case.E, case.I, o)
     ws_bytes = bfp8.fused_moe_workspace_size(case.M, case.H, case.k, case.E, case.I, o)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -260,7 +260,8 @@ def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=Tr
     if per_stage:
         reps = max(1, math.ceil(steps / n_inst))
         for s_, name in enumerate(stages):
-            os_ = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=flags | bfp8.FLAG_ONLY_STAGE(s_))
+            os_ = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=flags | bfp8.FLAG_ONLY_STAGE(s_),
+                            block_m=block_m)
             stage_us[name] = time_graph(hip, stream, lambda: [call(i, os_) for i in range(n_inst)], reps) * 1e3 / n_inst
         log("stage us (each stage alone, graph-timed): " + ", ".join(f"{k}={v:.2f}" for k, v in stage_us.items()))
     mean_bytes = sum(bytes_per) / n_inst
@@ -408,6 +409,7 @@ def main():
                          "hardware traffic counters)")
     ap.add_argument("--path", choices=sorted(PATH_FLAGS), default="auto",
                     help="force one implementation of the layer (default: the library's choice by shape)")
+    ap.add_argument("--block-m", type=int, default=0, help="routes per compact block of the general path (0 = auto)")
     ap.add_argument("--suite", metavar="JSON", default=None,
                     help="instead of the metric line: every layer config, activation+quant, route preparation "
                          "and a plain copy, as markdown tables on stdout and figures in JSON")
@@ -444,7 +446,8 @@ def main():
         del src, dst
         log(f"copy calibration: 4 copies of {args.calibrate_copy_mib} MiB")
 
-    r = measure_layer(case, args.steps, args.warmup, args.instances, hip, stream, dev, flags=PATH_FLAGS[args.path])
+    r = measure_layer(case, args.steps, args.warmup, args.instances, hip, stream, dev, flags=PATH_FLAGS[args.path],
+                      block_m=args.block_m)
     insts, stage_us, n_inst = r["insts"], r["stage_us"], r["n_inst"]
     dom = next(s_ for s_ in ("token_gate_up_swiglu", "decode_gate_up_swiglu", "gate_up_gemm") if s_ in stage_us)
     dom_bytes = sum(stage_bytes(case, x[1], dom) for x in insts) / n_inst

@@ -65,11 +65,13 @@ enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
 constexpr int64_t kTokenAutoMaxM = 32;
 constexpr int64_t kDecodeAutoMaxM = 4;
 
+// Routes per compact block of the general path: 32, or 64 above 48 routes per
+// local expert on average.  Measured on the small (128 and 512 tokens) and
+// large (2048 tokens) configs, 32 beat 16 everywhere (smaller blocks read each
+// expert's weight tile more often for little saved work) and tied 64 at 2048.
 int auto_block_m(int64_t R, int32_t L) {
   const int64_t per_expert = R / (L > 0 ? L : 1);
-  if (per_expert <= 16) return 16;
-  if (per_expert <= 48) return 32;
-  return 64;
+  return per_expert <= 48 ? 32 : 64;
 }
 
 void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_t I, const bfp8moe_opts_t& o) {
