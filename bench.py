@@ -300,9 +300,13 @@ def suite(hip, stream, dev):
     runs += [(f"{n} (forced)", synth.LAYER_CASES[n], f) for n, f in
              [("decode_m4", PATH_FLAGS["decode"]), ("decode_m4", PATH_FLAGS["general"]),
               ("decode_m16", PATH_FLAGS["general"]), ("decode_m32", PATH_FLAGS["general"])]]
+    oracle_insts = {}
     for name, case, flags in runs:
         r = measure_layer(case, SUITE_STEPS.get(name.split()[0], 50), 4, 0, hip, stream, dev, flags=flags)
-        r.pop("insts")
+        insts = r.pop("insts")
+        if not flags:
+            oracle_insts[name] = (case, insts[0], r["us_per_layer"])
+        del insts
         res["layers"][name + (f" flags {flags}" if flags else "")] = r
         st = ", ".join(f"{k} {v:.2f}" for k, v in r["stage_us"].items())
         path = "few tokens" if r["stages"][0].startswith("token") else (
@@ -310,6 +314,28 @@ def suite(hip, stream, dev):
         print(f"| {name} | {case.M} | {case.E} | {case.k} | {case.H} | {case.I} | {path} | {r['us_per_layer']:.2f} | "
               f"{r['gbs']:.0f} | {r['roofline_us']:.2f} | {r['roofline_frac']:.3f} | {st} |", flush=True)
         torch.cuda.empty_cache()
+
+    # the CPU oracle on instance 0 of every config: one thread and every host
+    # core for the small ones (mean of at least 5 runs and 2 s), every core only for the
+    # configs that take minutes on one (one run)
+    from oracle import oracle as O
+
+    cores = O.num_threads()
+    print()
+    print(f"CPU oracle (host threads available: {cores}), whole layer, instance 0:")
+    print()
+    print("| config | 1 thread s / layer | all threads s / layer (threads) | GPU µs / layer | GPU speedup over all threads |")
+    print("|---|---|---|---|---|")
+    res["oracle"] = {"cores": cores}
+    for name, (case, inst, gpu_us) in oracle_insts.items():
+        big = case.M >= 512
+        t1 = None if big else oracle_layer_seconds(case, inst, 2.0, threads=1, min_runs=1)[0]
+        tn, n, thr = oracle_layer_seconds(case, inst, 0.0 if big else 2.0, threads=cores, min_runs=1 if big else 5)
+        res["oracle"][name] = {"one_thread_s": t1, "all_threads_s": tn, "threads": thr}
+        t1s = "—" if t1 is None else f"{t1:.3f}"
+        print(f"| {name} | {t1s} | {tn:.3f} ({thr}) | {gpu_us:.2f} | {tn * 1e6 / gpu_us:.0f} |", flush=True)
+    oracle_insts.clear()
+    torch.cuda.empty_cache()
 
     # activation + quant (warm, like the pages): fused kernel against SwiGLU
     # then quant_fp8 as two launches
@@ -533,9 +559,9 @@ def measured_traffic(kernel, config):
         return None
 
 
-def cpu_baseline(case, inst, seconds):
-    """The CPU oracle on the same layer (instance 0), repeated for about
-    `seconds`; throughput in the metric's unit (GB/s of compulsory bytes)."""
+def oracle_layer_seconds(case, inst, seconds, threads=None, min_runs=1):
+    """The CPU oracle on one layer instance, repeated for about `seconds` (at
+    least min_runs times); seconds per layer, runs, threads used."""
     import torch
     from oracle import oracle as O
 
@@ -548,17 +574,33 @@ def cpu_baseline(case, inst, seconds):
     sel = used.to(W.w13.device).long()
     args = (hidden.cpu(), ids_l, w.cpu(), W.w13[sel].cpu(), W.w13_s[sel].cpu(), W.w2[sel].cpu(), W.w2_s[sel].cpu())
     np_args = [O.as_np(a) for a in args]
+    full = O.num_threads()
+    if threads is not None:
+        O.set_threads(threads)
+    try:
+        used_threads = min(O.num_threads(), case.M)  # the oracle parallelises over tokens
+        t0 = time.time()
+        n = 0
+        while True:
+            O.fused_moe(*np_args, scale_fmt=case.scale_fmt, clamp=case.clamp)
+            n += 1
+            if n >= min_runs and time.time() - t0 >= seconds:
+                break
+        return (time.time() - t0) / n, n, used_threads
+    finally:
+        O.set_threads(full)
+
+
+def cpu_baseline(case, inst, seconds):
+    """The CPU oracle on the same layer (instance 0), repeated for about
+    `seconds`; throughput in the metric's unit (GB/s of compulsory bytes)."""
+    from oracle import oracle as O
+
+    hidden, ids, w, W = inst
+    O.fused_moe  # the library is built and loaded before timing
     nbytes, _ = layer_bytes(case, ids)
-    O.fused_moe(*np_args, scale_fmt=case.scale_fmt, clamp=case.clamp)  # warm
-    t0 = time.time()
-    n = 0
-    while True:
-        O.fused_moe(*np_args, scale_fmt=case.scale_fmt, clamp=case.clamp)
-        n += 1
-        if time.time() - t0 >= seconds:
-            break
-    dt = (time.time() - t0) / n
-    threads = min(O.num_threads(), case.M)  # the oracle parallelises over tokens
+    oracle_layer_seconds(case, inst, 0.0)  # warm
+    dt, n, threads = oracle_layer_seconds(case, inst, seconds)
     log(f"cpu oracle: {dt * 1e3:.1f} ms/layer over {n} runs, {threads} thread(s)")
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{case.name} instance 0, whole layer, {n} runs ({dt * 1e3:.1f} ms each)",

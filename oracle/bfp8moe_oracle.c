@@ -450,10 +450,13 @@ void oracle_fused_moe(const uint16_t* hidden, int64_t M, int H,
     }
 }
 
-/* Threads OpenMP would use (for reporting the CPU baseline's core count). */
+/* Threads OpenMP would use (for reporting the CPU baseline's core count),
+ * and a way to change it for timing runs. */
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_num_threads(void) { return 1; }
+void oracle_set_threads(int n) { (void)n; }
 #endif

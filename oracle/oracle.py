@@ -59,6 +59,7 @@ def lib():
             "oracle_fused_moe": (None, [P, i64, i32, P, P, i32, P, P, P, P, i32, i32, i32, i32, f32,
                                         P, i64, P, P, P, P, P]),
             "oracle_num_threads": (i32, []),
+            "oracle_set_threads": (None, [i32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -238,3 +239,8 @@ def fused_moe(hidden, topk_ids, topk_w, w13, w13_s, w2, w2_s, expert_offset: int
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops from now on (timing runs)."""
+    lib().oracle_set_threads(n)
