@@ -10,9 +10,10 @@
 // Tile: 128 weight rows x BM routes, 4 waves of 32 rows each.  The K loop walks
 // 128-wide chunks, exactly one scale group: each chunk's MFMA result is
 // multiplied by a_scale(route, g) * w_scale(row block, g) and added to the fp32
-// accumulator.  Operands come straight from global memory into registers (see
-// mfma.h for the K slot order that keeps each load 64-byte contiguous per row);
-// the activation fragments are shared by the 4 waves through L1.
+// accumulator.  Weight chunks are loaded as whole 128-byte lines and turned
+// into MFMA fragments through a per-wave LDS slice; activation fragments come
+// straight from global memory into registers (see mfma.h for the K slot
+// order) and are shared by the 4 waves through L1.
 //
 // Pages cited in brackets, by key and section:
 //   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
@@ -77,9 +78,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
   }
   // weight rows of this lane
   const int n0 = nt * kBN + wave * kWN;
-  const uint8_t* wrow[kRT];
-#pragma unroll
-  for (int t = 0; t < kRT; t++) wrow[t] = B + ((size_t)e * N + n0 + t * 16 + col) * K;
+  const uint8_t* wrow0 = B + ((size_t)e * N + n0) * K;  // the wave's first weight row
   const float* ws = Bs + ((size_t)e * n_tiles + nt) * G;
 
   v4f acc[kRT][CT];
@@ -88,39 +87,64 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
 #pragma unroll
     for (int t = 0; t < CT; t++) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  v8i wa[kRT], xb[CT];
-#pragma unroll
-  for (int i = 0; i < kRT; i++) wa[i] = load_frag(wrow[i], kq);
-#pragma unroll
-  for (int t = 0; t < CT; t++) xb[t] = route[t] >= 0 ? load_frag(arow[t], kq) : zero_frag();
+  // Weight chunks travel as full 128-byte lines: load i of a lane reads row
+  // 8 i + lane / 8 of the wave's 32 rows, bytes 16 (lane % 8) .. + 15 of the
+  // chunk (each load instruction covers 8 whole lines; the MFMA fragment
+  // pattern would cover 16 half lines and stream about a quarter slower).  The
+  // wave writes the chunk to its own LDS slice -- 16-byte piece p of row r at
+  // piece p ^ (r & 7), against bank conflicts -- and reads its fragments
+  // back.  Only the wave itself touches its slice, and LDS accesses of one
+  // wave are carried out in order, so no barrier is needed.
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) u32x4 s_w[kThreads / 64][kWN * 8];
+  u32x4* sw = s_w[wave];
+  const uint8_t* wl = wrow0 + (size_t)(lane >> 3) * K + 16 * (lane & 7);  // load i adds 8 i rows
 
-  for (int g = 0; g < G; g++) {
-    // prefetch the next chunk while this one is multiplied
-    v8i wn[kRT], xn[CT];
-    const int gn = g + 1 < G ? g + 1 : g;
+  // One K step: request chunk gn into (wn, xn), then multiply chunk g held
+  // in (wc, xc).  Two register sets alternate, so nothing is copied.
+  auto step = [&](int g, int gn, u32x4 (&wc)[4], v8i (&xc)[CT], u32x4 (&wn)[4], v8i (&xn)[CT])
+                  __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kRT; i++) wn[i] = load_frag(wrow[i] + (size_t)gn * kGroup, kq);
+    for (int i = 0; i < 4; i++) wn[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * K + (size_t)gn * kGroup);
 #pragma unroll
     for (int t = 0; t < CT; t++) xn[t] = route[t] >= 0 ? load_frag(arow[t] + (size_t)gn * kGroup, kq) : zero_frag();
-
-    const float wsc = ws[g];
-    float asc[CT];
+    // this chunk through the wave's LDS slice into MFMA fragments (K slots
+    // as in load_frag: pieces kq and 4 + kq of the fragment's row)
 #pragma unroll
-    for (int t = 0; t < CT; t++) asc[t] = route[t] >= 0 ? asrow[t][g] * wsc : 0.0f;
-
+    for (int i = 0; i < 4; i++) {
+      const int r = 8 * i + (lane >> 3);
+      sw[r * 8 + ((lane & 7) ^ (r & 7))] = wc[i];
+    }
+    v8i wa[kRT];
 #pragma unroll
     for (int i = 0; i < kRT; i++) {
+      const int r = 16 * i + col;
+      const u32x4 lo = sw[r * 8 + (kq ^ (r & 7))];
+      const u32x4 hi = sw[r * 8 + ((4 + kq) ^ (r & 7))];
+      wa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    const float wsc = ws[g];
 #pragma unroll
-      for (int t = 0; t < CT; t++) {
-        v4f p = mfma_f8_16x16x128(wa[i], xb[t], v4f{0.f, 0.f, 0.f, 0.f});
+    for (int t = 0; t < CT; t++) {
+      const float asc = route[t] >= 0 ? asrow[t][g] * wsc : 0.0f;
 #pragma unroll
-        for (int v = 0; v < 4; v++) acc[i][t][v] = __builtin_fmaf(p[v], asc[t], acc[i][t][v]);
+      for (int i = 0; i < kRT; i++) {
+        const v4f p = mfma_f8_16x16x128(wa[i], xc[t], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int v = 0; v < 4; v++) acc[i][t][v] = __builtin_fmaf(p[v], asc, acc[i][t][v]);
       }
     }
+  };
+
+  u32x4 w0[4], w1[4];
+  v8i x0[CT], x1[CT];
 #pragma unroll
-    for (int i = 0; i < kRT; i++) wa[i] = wn[i];
+  for (int i = 0; i < 4; i++) w0[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * K);
 #pragma unroll
-    for (int t = 0; t < CT; t++) xb[t] = xn[t];
+  for (int t = 0; t < CT; t++) x0[t] = route[t] >= 0 ? load_frag(arow[t], kq) : zero_frag();
+  for (int g = 0; g < G; g += 2) {
+    step(g, min(g + 1, G - 1), w0, x0, w1, x1);
+    if (g + 1 < G) step(g + 1, min(g + 2, G - 1), w1, x1, w0, x0);
   }
 
   // epilogue: lane holds rows n0 + 16*i + 4*kq + v (v = 0..3) of route[t]
