@@ -299,7 +299,7 @@ def suite(hip, stream, dev):
     # the other paths where they apply, forced (the default picks one by M)
     runs += [(f"{n} (forced)", synth.LAYER_CASES[n], f) for n, f in
              [("decode_m4", PATH_FLAGS["decode"]), ("decode_m4", PATH_FLAGS["general"]),
-              ("decode_m16", PATH_FLAGS["general"]), ("decode_m32", PATH_FLAGS["general"])]]
+              ("decode_m16", PATH_FLAGS["token"]), ("decode_m32", PATH_FLAGS["token"])]]
     oracle_insts = {}
     for name, case, flags in runs:
         r = measure_layer(case, SUITE_STEPS.get(name.split()[0], 50), 4, 0, hip, stream, dev, flags=flags)

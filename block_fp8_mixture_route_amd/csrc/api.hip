@@ -58,20 +58,23 @@ const char* const kDecodeStages[] = {"decode_gate_up_swiglu", "decode_down_reduc
 const char* const kTokenStages[] = {"token_gate_up_swiglu", "token_down_reduce"};
 enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
 
-// The few-token path is the default up to this many tokens (measured faster
-// than the small-batch and general paths at 1, 4, 16 and 32 tokens of the
-// decode shape); the small-batch path is then the default up to
-// kDecodeAutoMaxM tokens where the few-token path does not fit.
-constexpr int64_t kTokenAutoMaxM = 32;
+// The few-token path is the default up to this many tokens: it reads one
+// expert's weights once per route, the general path once per expert, and at
+// the decode shape (256 experts, top-8, H 7168, I 256) the general path
+// overtakes it at about 14 tokens (measured at 4 to 24).  The small-batch
+// path is the default up to kDecodeAutoMaxM tokens where the few-token path
+// does not fit.
+constexpr int64_t kTokenAutoMaxM = 12;
 constexpr int64_t kDecodeAutoMaxM = 4;
 
-// Routes per compact block of the general path: 32, or 64 above 48 routes per
-// local expert on average.  Measured on the small (128 and 512 tokens) and
-// large (2048 tokens) configs, 32 beat 16 everywhere (smaller blocks read each
-// expert's weight tile more often for little saved work) and tied 64 at 2048.
+// Routes per compact block of the general path, from the routes per local
+// expert on average: 16 below 8, 32 up to 48, 64 above.  Measured: 16 beat
+// 32 at 0.5, 1 and 4 routes per expert (16 and 32 decode-shape tokens, 128
+// small-shape tokens), 32 beat 16 at 16 and 32 (512 small-shape tokens, 2048
+// large-shape tokens), and 64 lost to 32 in all of them.
 int auto_block_m(int64_t R, int32_t L) {
   const int64_t per_expert = R / (L > 0 ? L : 1);
-  return per_expert <= 48 ? 32 : 64;
+  return per_expert < 8 ? 16 : per_expert <= 48 ? 32 : 64;
 }
 
 void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_t I, const bfp8moe_opts_t& o) {

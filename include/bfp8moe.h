@@ -88,7 +88,8 @@ enum {
 /* Options of the fused layer.  Initialise with bfp8moe_opts_init(). */
 typedef struct {
     int32_t block_m;            /* routes per compact block for the general path (16, 32 or 64);
-                                   0 = auto: 32, or 64 above 48 routes per local expert */
+                                   0 = auto: 16 below 8 routes per local expert, 32 up
+                                   to 48, 64 above */
     int32_t scale_fmt;          /* bfp8moe_scale_fmt_t for both activation quantisations */
     float clamp_limit;          /* SwiGLU clamp; +INFINITY = unclamped [P3 Purpose: finite SwiGLU clamping] */
     int32_t expert_offset;      /* first global expert held locally [P2 Suppressed comments] */
@@ -264,7 +265,7 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
  * pointer (NULL = defaults).
  * Three implementations, chosen by shape unless a test flag forces one:
  *   few tokens (M <= 32, k <= 8, H <= 8192, I in {128, 256, 512}; the
- *     default up to 32 tokens): two matrix-vector kernels -- input
+ *     default up to 12 tokens): two matrix-vector kernels -- input
  *     quantisation, gate/up GEMM and SwiGLU per route (M x k x I/8
  *     workgroups; each route reads its expert's rows), then the SwiGLU
  *     output's quantisation, down GEMM and moe_reduce per token and block of

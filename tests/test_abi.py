@@ -48,10 +48,11 @@ def test_stage_lists():
     assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
     # the one-token path needs I in {128, 256, 512}; other shapes fall back
     assert bfp8.fused_moe_stages(1, 4096, 8, 256, 384, o) == ["decode_gate_up_swiglu", "decode_down_reduce"]
-    # the few-token path up to 32 tokens; the others when forced
+    # the few-token path up to 12 tokens; the others when forced
     assert bfp8.fused_moe_stages(4, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
-    assert bfp8.fused_moe_stages(32, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
-    assert bfp8.fused_moe_stages(33, 7168, 8, 256, 256, o)[0] == "route_prepare"
+    assert bfp8.fused_moe_stages(12, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
+    assert bfp8.fused_moe_stages(13, 7168, 8, 256, 256, o)[0] == "route_prepare"
+    assert bfp8.fused_moe_stages(32, 7168, 8, 256, 256, o)[0] == "route_prepare"
     assert bfp8.fused_moe_stages(4, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_DECODE)) == [
         "decode_gate_up_swiglu", "decode_down_reduce"]
     assert bfp8.fused_moe_stages(32, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_TOKEN)) == [

@@ -129,3 +129,27 @@ def test_grouped_gemm_hot_expert():
     torch.cuda.synchronize()
     ref = O.grouped_gemm(A, As, k, Bw, Bs, ids, 0, E)
     assert_gemm_close(bf16_np(C), ref, "hot expert")
+
+
+@pytest.mark.parametrize("B", [16, 32])
+def test_grouped_gemm_many_blocks(B):
+    # 601 experts of one route each: 601 blocks, all in use, the most the
+    # routing allows; from 512 blocks up the tiles go to the XCDs in pairs of
+    # blocks, and 601 leaves a last pair of one block
+    print_case("gemm many blocks", B)
+    E, N, K, k, Mt = 601, 256, 256, 1, 601
+    g = torch.Generator().manual_seed(601)
+    ids = torch.randperm(E, generator=g).to(torch.int32).reshape(Mt, k)
+    A, As = O.quant_fp8(synth.hidden_states(Mt, K, "many", 0))
+    Bw = torch.empty(E, N, K, dtype=torch.uint8)
+    Bs = torch.empty(E, N // 128, K // 128)
+    for e in range(E):
+        Bw[e], Bs[e] = synth.block_fp8_weight(N, K, "many_b", e)
+    route = bfp8.moe_route_prepare(ids.to(dev()), 0, E, B)
+    torch.cuda.synchronize()
+    assert int(route["num_blocks"].item()) == E == bfp8.max_blocks(Mt * k, E, B)
+    C = bfp8.moe_fp8_grouped_gemm(torch.from_numpy(A).to(dev()), torch.from_numpy(As).to(dev()), k, Bw.to(dev()),
+                                  Bs.to(dev()), route, B, Mt * k)
+    torch.cuda.synchronize()
+    ref = O.grouped_gemm(A, As, k, Bw, Bs, ids, 0, E)
+    assert_gemm_close(bf16_np(C), ref, f"many blocks B={B}")
