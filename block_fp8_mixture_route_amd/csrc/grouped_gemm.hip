@@ -11,9 +11,10 @@
 // 128-wide chunks, exactly one scale group: each chunk's MFMA result is
 // multiplied by a_scale(route, g) * w_scale(row block, g) and added to the fp32
 // accumulator.  Weight chunks are loaded as whole 128-byte lines and turned
-// into MFMA fragments through a per-wave LDS slice; activation fragments come
-// straight from global memory into registers (see mfma.h for the K slot
-// order) and are shared by the 4 waves through L1.
+// into MFMA fragments through a per-wave LDS slice; for blocks of 32 or 64
+// routes the workgroup loads each chunk of the block's activation rows once,
+// as whole lines, into a shared LDS buffer that all 4 waves read their
+// fragments from (see mfma.h for the K slot order).
 //
 // Pages cited in brackets, by key and section:
 //   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
@@ -49,8 +50,20 @@ inline int64_t gemm_slots_per_xcd(int64_t max_blocks, int n_tiles, int gb) {
   return (groups + kXcd - 1) / kXcd * gb * n_tiles;
 }
 
+// Activation registers of one K step: 16-byte line pieces (shared path) or
+// MFMA fragments (direct path).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <bool kShared, int XL, int CT>
+struct XRegs {
+  typedef u32x4_t type[XL];
+};
+template <int XL, int CT>
+struct XRegs<false, XL, CT> {
+  typedef v8i type[CT];
+};
+
 template <int BM>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 64 ? 3 : 1))) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, int a_row_div, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, int N, int K, const int32_t* __restrict__ sorted_routes,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ block_expert,
@@ -85,7 +98,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
   const int col = lane & 15, kq = lane >> 4;
   const int G = K / kGroup;
 
-  // activation rows of this lane's routes
+  // The activation chunks of blocks of 32 or 64 routes go through a buffer
+  // shared by the workgroup; with 16 routes each wave loads its fragments
+  // itself, which costs less than the barrier (measured).
+  constexpr bool kSharedX = BM >= 32;
+  // the routes of this lane's MFMA columns (route tile t, column col): their
+  // activation rows and activation-scale rows
   const uint8_t* arow[CT];
   const float* asrow[CT];
   int route[CT];
@@ -96,6 +114,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
     const int64_t ar = route[t] >= 0 ? route[t] / a_row_div : 0;
     arow[t] = A + (size_t)ar * K;
     asrow[t] = As + (size_t)ar * G;
+  }
+  // shared path: the activation rows this thread loads, row tid / 8 + 32 x
+  // of the block, bytes 16 (tid % 8) .. + 15 of each chunk (full 128-byte
+  // lines; a row without a route reads activation row 0, and its columns are
+  // never stored)
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int XL = kSharedX ? BM * 8 / kThreads : 1;  // 16-byte activation loads per thread
+  const int tid = threadIdx.x;
+  const uint8_t* xrow[XL];
+#pragma unroll
+  for (int x = 0; x < XL; x++) {
+    const int r = kSharedX ? (tid >> 3) + 32 * x : 0;
+    const int rt = r < len ? sorted_routes[start + r] : -1;
+    xrow[x] = A + (size_t)(rt >= 0 ? rt / a_row_div : 0) * K + 16 * (tid & 7);
   }
   // weight rows of this lane
   const int n0 = nt * kBN + wave * kWN;
@@ -108,37 +140,54 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
 #pragma unroll
     for (int t = 0; t < CT; t++) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Weight chunks travel as full 128-byte lines: load i of a lane reads row
-  // 8 i + lane / 8 of the wave's 32 rows, bytes 16 (lane % 8) .. + 15 of the
-  // chunk (each load instruction covers 8 whole lines; the MFMA fragment
-  // pattern would cover 16 half lines and stream about a quarter slower).  The
-  // wave writes the chunk to its own LDS slice -- 16-byte piece p of row r at
-  // piece p ^ (r & 7), against bank conflicts -- and reads its fragments
-  // back.  Only the wave itself touches its slice, and LDS accesses of one
-  // wave are carried out in order, so no barrier is needed.
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  // Chunks travel as full 128-byte lines and are turned into MFMA fragments
+  // in LDS, 16-byte piece p of row r stored at piece p ^ (r & 7) against bank
+  // conflicts (fragment reads take pieces kq and 4 + kq of the fragment's
+  // rows, the K slot order of load_frag).
+  //  - Weights: load i of a lane reads row 8 i + lane / 8 of the wave's 32
+  //    rows (each load instruction covers 8 whole lines; the MFMA fragment
+  //    pattern would cover 16 half lines and stream about a quarter slower).
+  //    The wave writes the chunk to its own LDS slice and reads its fragments
+  //    back; LDS accesses of one wave are carried out in order, so no barrier
+  //    is needed.
+  //  - Activations (shared path): the workgroup loads the block's rows once
+  //    (not once per wave) into one of two shared buffers, alternating by
+  //    step; one barrier per step makes the buffer whole before any wave
+  //    reads it, and the barrier of the step before has seen every read of
+  //    the buffer's previous contents.  Direct path: each wave loads its
+  //    fragments (mfma.h K slot order), shared by the 4 waves through L1.
   __shared__ __align__(16) u32x4 s_w[kThreads / 64][kWN * 8];
+  __shared__ __align__(16) u32x4 s_x[2][kSharedX ? BM * 8 : 1];
   u32x4* sw = s_w[wave];
   const uint8_t* wl = wrow0 + (size_t)(lane >> 3) * K + 16 * (lane & 7);  // load i adds 8 i rows
 
   // One K step: request chunk gn into (wn, xn, sn, wsn), then multiply the
-  // chunk held in (wc, xc, sc, wsc).  Two register sets alternate, so nothing is
-  // copied.  Every load is unconditional -- a lane without a route reads
-  // activation row 0 and its columns are never stored -- and the next
-  // chunk's loads are all issued before the current chunk is used, so the
-  // wait before the multiply covers the current chunk only.
-  auto step = [&](int gn, u32x4 (&wc)[4], v8i (&xc)[CT], float (&sc)[CT], float wsc, u32x4 (&wn)[4],
-                  v8i (&xn)[CT], float (&sn)[CT], float& wsn) __attribute__((always_inline)) {
+  // chunk held in (wc, xc, sc, wsc) through shared buffer xb.  Two register
+  // sets alternate, so nothing is copied.  Every load is unconditional and
+  // the next chunk's loads are all issued before the current chunk is used,
+  // so the wait before the multiply covers the current chunk only.
+  auto step = [&](int gn, u32x4 (&wc)[4], auto& xc, float (&sc)[CT], float wsc, u32x4 (&wn)[4], auto& xn,
+                  float (&sn)[CT], float& wsn, u32x4* xb) __attribute__((always_inline)) {
     wsn = ws[gn];
 #pragma unroll
     for (int t = 0; t < CT; t++) sn[t] = asrow[t][gn];
 #pragma unroll
     for (int i = 0; i < 4; i++) wn[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * K + (size_t)gn * kGroup);
+    if constexpr (kSharedX) {
 #pragma unroll
-    for (int t = 0; t < CT; t++) xn[t] = load_frag(arow[t] + (size_t)gn * kGroup, kq);
+      for (int x = 0; x < XL; x++) xn[x] = *reinterpret_cast<const u32x4*>(xrow[x] + (size_t)gn * kGroup);
+    } else {
+#pragma unroll
+      for (int t = 0; t < CT; t++) xn[t] = load_frag(arow[t] + (size_t)gn * kGroup, kq);
+    }
     __builtin_amdgcn_sched_barrier(0);  // the loads leave before anything waits
-    // this chunk through the wave's LDS slice into MFMA fragments (K slots
-    // as in load_frag: pieces kq and 4 + kq of the fragment's row)
+    if constexpr (kSharedX) {
+#pragma unroll
+      for (int x = 0; x < XL; x++) {
+        const int r = (tid >> 3) + 32 * x;
+        xb[r * 8 + ((tid & 7) ^ (r & 7))] = xc[x];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int r = 8 * i + (lane >> 3);
@@ -152,38 +201,61 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
       const u32x4 hi = sw[r * 8 + ((4 + kq) ^ (r & 7))];
       wa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
+    if constexpr (kSharedX) {
+      // the shared activation buffer is whole (LDS traffic only: the next
+      // chunk's loads stay in flight)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
 #pragma unroll
     for (int t = 0; t < CT; t++) {
+      v8i xf;
+      if constexpr (kSharedX) {
+        const int r = 16 * t + col;
+        const u32x4 lo = xb[r * 8 + (kq ^ (r & 7))];
+        const u32x4 hi = xb[r * 8 + ((4 + kq) ^ (r & 7))];
+        xf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      } else {
+        xf = xc[t];
+      }
       const float asc = route[t] >= 0 ? sc[t] * wsc : 0.0f;
 #pragma unroll
       for (int i = 0; i < kRT; i++) {
-        const v4f p = mfma_f8_16x16x128(wa[i], xc[t], v4f{0.f, 0.f, 0.f, 0.f});
+        const v4f p = mfma_f8_16x16x128(wa[i], xf, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int v = 0; v < 4; v++) acc[i][t][v] = __builtin_fmaf(p[v], asc, acc[i][t][v]);
       }
     }
   };
 
+  typedef typename XRegs<kSharedX, XL, CT>::type XR;
   u32x4 w0[4], w1[4];
-  v8i x0[CT], x1[CT];
+  XR x0, x1;
   float s0[CT], s1[CT];
   float ws0 = ws[0], ws1 = 0.0f;
 #pragma unroll
   for (int t = 0; t < CT; t++) s0[t] = asrow[t][0];
 #pragma unroll
   for (int i = 0; i < 4; i++) w0[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * K);
+  if constexpr (kSharedX) {
 #pragma unroll
-  for (int t = 0; t < CT; t++) x0[t] = load_frag(arow[t], kq);
+    for (int x = 0; x < XL; x++) x0[x] = *reinterpret_cast<const u32x4*>(xrow[x]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < CT; t++) x0[t] = load_frag(arow[t], kq);
+  }
   // both steps of an iteration run unconditionally (a step in a branch would
   // have its loads moved into that branch, after the other step's wait); an
   // odd chunk count ends with one more step.  The last step's request
   // repeats the last chunk (cache hits, unused).
   int g = 0;
   for (; g + 1 < G; g += 2) {
-    step(g + 1, w0, x0, s0, ws0, w1, x1, s1, ws1);
-    step(min(g + 2, G - 1), w1, x1, s1, ws1, w0, x0, s0, ws0);
+    step(g + 1, w0, x0, s0, ws0, w1, x1, s1, ws1, s_x[0]);
+    step(min(g + 2, G - 1), w1, x1, s1, ws1, w0, x0, s0, ws0, s_x[1]);
   }
-  if (g < G) step(g, w0, x0, s0, ws0, w1, x1, s1, ws1);
+  if (g < G) step(g, w0, x0, s0, ws0, w1, x1, s1, ws1, s_x[0]);
 
   // epilogue: lane holds rows n0 + 16*i + 4*kq + v (v = 0..3) of route[t]
 #pragma unroll
