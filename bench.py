@@ -272,6 +272,29 @@ def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=Tr
             "stage_us": stage_us, "insts": insts, "active_experts_inst0": d0}
 
 
+# ------------------------------------------------------------------ launch floor
+
+def launch_floor(hip, stream, dev):
+    """Launch-to-launch time of a kernel that does (almost) nothing, replayed
+    back to back from a HIP graph: the fixed cost every kernel of a layer pays
+    on top of its own work.  Uses torch's fill kernel on one element, 64
+    launches per graph."""
+    import torch
+
+    ext = torch.cuda.ExternalStream(stream.value, device=dev)
+    x = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def body():
+        with torch.cuda.stream(ext):
+            for i in range(64):
+                x.fill_(i)
+
+    us = time_graph(hip, stream, body, 20) * 1e3 / 64
+    print(f"graph launch floor: {us:.2f} µs per kernel (one-element fill, 64 launches per graph)", flush=True)
+    return us
+
+
 # ------------------------------------------------------------------ suite
 
 SUITE_STEPS = {"tiny": 200, "decode_m1": 480, "decode_m4": 200, "decode_m16": 100, "decode_m32": 100,
@@ -411,6 +434,7 @@ def suite(hip, stream, dev):
             for i in range(nbuf):
                 bufs[2 * i + 1].copy_(bufs[2 * i])
 
+    res["launch_floor_us"] = launch_floor(hip, stream, dev)
     tc = time_graph(hip, stream, copies, 10) / nbuf
     res["copy"] = {"bytes": nbytes, "us": tc * 1e3, "gbs_read_plus_write": 2 * nbytes / (tc * 1e-3) / 1e9}
     print()
@@ -436,6 +460,7 @@ def main():
     ap.add_argument("--path", choices=sorted(PATH_FLAGS), default="auto",
                     help="force one implementation of the layer (default: the library's choice by shape)")
     ap.add_argument("--block-m", type=int, default=0, help="routes per compact block of the general path (0 = auto)")
+    ap.add_argument("--floor", action="store_true", help="only the graph launch floor of one kernel")
     ap.add_argument("--suite", metavar="JSON", default=None,
                     help="instead of the metric line: every layer config, activation+quant, route preparation "
                          "and a plain copy, as markdown tables on stdout and figures in JSON")
@@ -455,6 +480,9 @@ def main():
     hip = Hip()
     stream = hip.stream()
 
+    if args.floor:
+        launch_floor(hip, stream, dev)
+        return
     if args.suite:
         res = suite(hip, stream, dev)
         with open(args.suite, "w") as f:
