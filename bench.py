@@ -250,19 +250,23 @@ def measure_layer(case, steps, warmup, instances, hip, stream, dev, per_stage=Tr
     gbs = total_bytes / (total_ms * 1e-3) / 1e9
     log(f"timed {steps} steps: {ms_per_step * 1e3:.2f} us/layer, {gbs:.0f} GB/s")
 
-    # per-stage durations: each stage alone (BFP8MOE_FLAG_ONLY_STAGE), one
-    # rotation captured in a graph and replayed, HIP events on the stream the
-    # kernels run on around the replays: launch-to-launch time of the stage's
-    # kernel, back to back as in the layer graph.  A stage past the first
-    # reads what the whole calls above left in the workspace (same code path
-    # and traffic; the values are not checked here).
+    # per-stage durations: each stage alone (BFP8MOE_FLAG_ONLY_STAGE), at
+    # least 32 calls (whole rotations) captured in a graph and replayed, HIP
+    # events on the stream the kernels run on around the replays:
+    # launch-to-launch time of the stage's kernel, back to back as in the
+    # layer graph (a graph of one short kernel would time the host's graph
+    # launches instead).  A stage past the first reads what the whole calls
+    # above left in the workspace (same code path and traffic; the values are
+    # not checked here).
     stage_us = {}
     if per_stage:
-        reps = max(1, math.ceil(steps / n_inst))
+        per_graph = n_inst * max(1, math.ceil(32 / n_inst))
+        reps = max(1, math.ceil(steps / per_graph))
         for s_, name in enumerate(stages):
             os_ = bfp8.opts(scale_fmt=case.scale_fmt, clamp_limit=case.clamp, flags=flags | bfp8.FLAG_ONLY_STAGE(s_),
                             block_m=block_m)
-            stage_us[name] = time_graph(hip, stream, lambda: [call(i, os_) for i in range(n_inst)], reps) * 1e3 / n_inst
+            stage_us[name] = time_graph(hip, stream, lambda: [call(i % n_inst, os_) for i in range(per_graph)],
+                                        reps) * 1e3 / per_graph
         log("stage us (each stage alone, graph-timed): " + ", ".join(f"{k}={v:.2f}" for k, v in stage_us.items()))
     mean_bytes = sum(bytes_per) / n_inst
     roof_us = max(mean_bytes / (HBM_PEAK_GBS * 1e3), layer_flops(case) / (FP8_PEAK_TFLOPS * 1e6))
