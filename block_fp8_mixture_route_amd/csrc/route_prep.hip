@@ -138,21 +138,32 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
   }
   __syncthreads();
 
-  // 2. per expert: exclusive over waves; totals over all segments
+  // 2. per expert: exclusive over waves; totals over all segments (the
+  //    segment counts are read 8 at a time, every load of a batch issued
+  //    before the first is used)
   for (int e = tid; e < L; e += kThreads) {
+    int cw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) cw[w] = wh[w * L + e];
     int run = 0;
+#pragma unroll
     for (int w = 0; w < kWaves; w++) {
-      int c = wh[w * L + e];
       wh[w * L + e] = run;
-      run += c;
+      run += cw[w];
     }
     int before = 0, total = run;
     if (hist) {
       total = 0;
-      for (int b = 0; b < n_seg; b++) {
-        int c = hist[(size_t)b * L + e];
-        if (b < seg) before += c;
-        total += c;
+      for (int b0 = 0; b0 < n_seg; b0 += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) c[u] = hist[(size_t)min(b0 + u, n_seg - 1) * L + e];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const int cu = b0 + u < n_seg ? c[u] : 0;
+          if (b0 + u < seg) before += cu;
+          total += cu;
+        }
       }
     }
     base[e] = before;
