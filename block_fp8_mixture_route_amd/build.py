@@ -37,6 +37,9 @@ def sources():
 
 
 def build(verbose: bool = False) -> str:
+    from . import gen_exp_table
+
+    gen_exp_table.write()  # csrc/exp_neg_table.h, included by device.h
     srcs = sources()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]

@@ -51,9 +51,11 @@ def test_quant_fp8_every_bf16_pattern(fmt):
     assert (s.cpu().numpy().view(np.uint32) == rs.view(np.uint32)).all()
 
 
-@pytest.mark.parametrize("clamp", [math.inf, 7.0])
+@pytest.mark.parametrize("clamp", [math.inf, 7.0, 7.1])
 def test_silu_and_mul_exhaustive_gate(clamp):
-    # every BF16 gate value (finite or not) against up = 1 and against random ups
+    # every BF16 gate value (finite or not) against up = 1 and against random ups;
+    # a clamp limit that is not a BF16 value (7.1) gives gates that are not
+    # either
     print_case("silu_and_mul exhaustive", clamp)
     I = 128
     gates = ALL_BF16.reshape(512, I)
