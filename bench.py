@@ -395,6 +395,40 @@ def suite(hip, stream, dev):
         res["act_quant"][tok] = {"rows": rows, "fused_us": tf, "two_kernel_us": t2}
         print(f"| {tok} | {rows} | {tf:.2f} | {t2:.2f} | {t2 / tf:.2f} | {nbytes / (tf * 1e3):.0f} |", flush=True)
 
+    # activation + quant under 8-way expert parallelism (top-k 6, width 2048,
+    # 32 of 256 experts local): the fused kernel skips the non-local rows
+    # through the expert map; the two-kernel arm has no row filter
+    print()
+    print("| tokens | rows | local rows | fused µs (expert-map filter) | two kernels µs (all rows) | "
+          "fused GB/s (local rows) |")
+    print("|---|---|---|---|---|---|")
+    res["act_quant_ep8"] = {}
+    I = synth.EP_I
+    for tok in synth.EP_TOKENS:
+        gu, rid, emap = (t.to(dev) for t in synth.ep_act_inputs(tok, "bench"))
+        rows = gu.shape[0]
+        q = torch.empty(rows, I, dtype=torch.uint8, device=dev)
+        sc = torch.empty(rows, I // 128, dtype=torch.float32, device=dev)
+        h = torch.empty(rows, I, dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+        def fused():
+            bfp8._lib.check(L_.silu_and_mul_quant_fp8(P(gu.data_ptr()), rows, I, P(rid.data_ptr()),
+                                                      P(emap.data_ptr()), synth.EP_E, synth.ACT_CLAMP,
+                                                      bfp8.SCALE_UE8M0, P(q.data_ptr()), P(sc.data_ptr()), stream))
+
+        def two():
+            bfp8._lib.check(L_.silu_and_mul(P(gu.data_ptr()), rows, I, synth.ACT_CLAMP, P(h.data_ptr()), stream))
+            bfp8._lib.check(L_.quant_fp8(P(h.data_ptr()), rows, I, bfp8.SCALE_UE8M0, P(q.data_ptr()),
+                                         P(sc.data_ptr()), stream))
+
+        tf = time_graph(hip, stream, lambda: [fused() for _ in range(20)], 20) * 1e3 / 20
+        t2 = time_graph(hip, stream, lambda: [two() for _ in range(20)], 20) * 1e3 / 20
+        live = int((emap[rid.long()] >= 0).sum().item())
+        nbytes = live * (4 * I + I + 4 * (I // 128))
+        res["act_quant_ep8"][tok] = {"rows": rows, "local_rows": live, "fused_us": tf, "two_kernel_us": t2}
+        print(f"| {tok} | {rows} | {live} | {tf:.2f} | {t2:.2f} | {nbytes / (tf * 1e3):.0f} |", flush=True)
+
     # route preparation: single workgroup against count + scan/scatter
     print()
     print("| routes R | local experts L | block_m | one workgroup µs | many workgroups µs |")

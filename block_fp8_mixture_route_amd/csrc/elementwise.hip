@@ -27,6 +27,11 @@ namespace {
 
 constexpr int kThreads = 256;                 // 4 waves, 16 groups per workgroup
 constexpr int kGroupsPerBlock = kThreads / 16;
+// SwiGLU exp by table from this many groups of 128 up: below it the kernels
+// are bound by latency, and the table's dependent load costs more than the
+// fp64 exp it saves (measured: 8 to 2,048 rows of width 512, 128 rows of 256;
+// the table wins at 4,096 rows of 768 and 16,384 of 1,024)
+constexpr int64_t kTableMinGroups = 16384;
 
 __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -75,6 +80,7 @@ __device__ __forceinline__ bool row_live(const RowFilter& f, int64_t r) {
 
 // SwiGLU of this lane's 8 outputs of group g in row r (gate at column
 // g*128 + 8*l16, up I columns later); returns them as BF16-valued floats.
+template <bool kTable>
 __device__ __forceinline__ void swiglu8(const uint16_t* __restrict__ gu, int64_t r, int I, int g, int l16,
                                         float limit, bool clamp, float (&a)[8]) {
   const uint16_t* row = gu + (size_t)r * 2 * I + (size_t)g * kGroup + (size_t)l16 * 8;
@@ -84,9 +90,10 @@ __device__ __forceinline__ void swiglu8(const uint16_t* __restrict__ gu, int64_t
   unpack8(gv, gf);
   unpack8(uv, uf);
 #pragma unroll
-  for (int i = 0; i < 8; i++) a[i] = swiglu_bf16(gf[i], uf[i], limit, clamp);
+  for (int i = 0; i < 8; i++) a[i] = swiglu_bf16<kTable>(gf[i], uf[i], limit, clamp);
 }
 
+template <bool kTable>
 __global__ __launch_bounds__(kThreads) void silu_and_mul_kernel(const uint16_t* __restrict__ gu, int64_t n_groups,
                                                                 int I, float limit, int clamp,
                                                                 uint16_t* __restrict__ out) {
@@ -97,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void silu_and_mul_kernel(const uint16_t* 
   const int64_t r = gid / gpr;
   const int g = (int)(gid - r * gpr);
   float a[8];
-  swiglu8(gu, r, I, g, l16, limit, clamp != 0, a);
+  swiglu8<kTable>(gu, r, I, g, l16, limit, clamp != 0, a);
   uint4 o;
   o.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
   o.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
@@ -106,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void silu_and_mul_kernel(const uint16_t* 
   *reinterpret_cast<uint4*>(out + (size_t)r * I + (size_t)g * kGroup + (size_t)l16 * 8) = o;
 }
 
+template <bool kTable>
 __global__ __launch_bounds__(kThreads) void silu_and_mul_quant_kernel(const uint16_t* __restrict__ gu,
                                                                       int64_t n_groups, int I, RowFilter filt,
                                                                       float limit, int clamp, int fmt,
@@ -119,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void silu_and_mul_quant_kernel(const uint
   const int g = (int)(gid - r * gpr);
   if (!row_live(filt, r)) return;  // masked rows are left untouched
   float a[8];
-  swiglu8(gu, r, I, g, l16, limit, clamp != 0, a);
+  swiglu8<kTable>(gu, r, I, g, l16, limit, clamp != 0, a);
   float amax = max_over_16(lane_amax8(a));
   float sc = group_scale(amax, fmt);
   *reinterpret_cast<uint2*>(q + (size_t)r * I + (size_t)g * kGroup + (size_t)l16 * 8) = encode8_scaled(a, sc);
@@ -180,8 +188,12 @@ hipError_t launch_silu_and_mul(const uint16_t* gu, int64_t rows, int I, float li
   const int64_t ng = rows * (I / kGroup);
   if (ng == 0) return hipSuccess;
   const int clamp = __builtin_isfinite(limit) ? 1 : 0;
-  hipLaunchKernelGGL(silu_and_mul_kernel, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0, stream, gu,
-                     ng, I, limit, clamp, out);
+  if (ng >= kTableMinGroups)
+    hipLaunchKernelGGL(silu_and_mul_kernel<true>, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0, stream,
+                       gu, ng, I, limit, clamp, out);
+  else
+    hipLaunchKernelGGL(silu_and_mul_kernel<false>, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0, stream,
+                       gu, ng, I, limit, clamp, out);
   return hipGetLastError();
 }
 
@@ -190,8 +202,12 @@ hipError_t launch_silu_and_mul_quant(const uint16_t* gu, int64_t rows, int I, co
   const int64_t ng = rows * (I / kGroup);
   if (ng == 0) return hipSuccess;
   const int clamp = __builtin_isfinite(limit) ? 1 : 0;
-  hipLaunchKernelGGL(silu_and_mul_quant_kernel, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0, stream,
-                     gu, ng, I, f, limit, clamp, fmt, q, s);
+  if (ng >= kTableMinGroups)
+    hipLaunchKernelGGL(silu_and_mul_quant_kernel<true>, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0,
+                       stream, gu, ng, I, f, limit, clamp, fmt, q, s);
+  else
+    hipLaunchKernelGGL(silu_and_mul_quant_kernel<false>, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0,
+                       stream, gu, ng, I, f, limit, clamp, fmt, q, s);
   return hipGetLastError();
 }
 

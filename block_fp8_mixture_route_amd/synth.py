@@ -198,6 +198,27 @@ ACT_E = 288
 ACT_I = 512
 ACT_CLAMP = 7.0
 
+# activation + quant under 8-way expert parallelism: routed rows = tokens x 6
+# (top-k 6), width I = 2048, 256 experts of which this rank holds 32
+EP_TOKENS = (1, 8, 64, 512, 1024)
+EP_TOPK = 6
+EP_E = 256
+EP_LOCAL = 32
+EP_I = 2048
+
+
+def ep_act_inputs(tokens: int, *key, device="cpu"):
+    """Gate/up rows [tokens * 6, 2 I] BF16 (N(0, 2)), each row's expert id
+    (top-k 6 distinct experts per token, uniform over 256) and the rank's
+    expert map (experts [0, 32) local, the rest -1)."""
+    g = gen(device, *key, "ep_act", tokens)
+    rows = tokens * EP_TOPK
+    x = (torch.randn(rows, 2 * EP_I, generator=g, device=device, dtype=torch.float32) * 2.0).to(torch.bfloat16)
+    ids = torch.stack([torch.randperm(EP_E, generator=g, device=device)[:EP_TOPK] for _ in range(tokens)])
+    emap = torch.where(torch.arange(EP_E, device=device) < EP_LOCAL, torch.arange(EP_E, device=device),
+                       torch.full((EP_E,), -1, device=device))
+    return x.contiguous(), ids.reshape(-1).to(torch.int32).contiguous(), emap.to(torch.int32).contiguous()
+
 
 def routing_for(case: LayerCase, *key, device="cpu"):
     if case.routing == "uniform":

@@ -51,14 +51,15 @@ def test_quant_fp8_every_bf16_pattern(fmt):
     assert (s.cpu().numpy().view(np.uint32) == rs.view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("I", [128, 4096])
 @pytest.mark.parametrize("clamp", [math.inf, 7.0, 7.1])
-def test_silu_and_mul_exhaustive_gate(clamp):
+def test_silu_and_mul_exhaustive_gate(clamp, I):
     # every BF16 gate value (finite or not) against up = 1 and against random ups;
     # a clamp limit that is not a BF16 value (7.1) gives gates that are not
-    # either
-    print_case("silu_and_mul exhaustive", clamp)
-    I = 128
-    gates = ALL_BF16.reshape(512, I)
+    # either.  512 rows of width 128 take the fp64 exp; width 4096 (every gate
+    # value 32 times, 16384 groups) takes the table
+    print_case("silu_and_mul exhaustive", clamp, I)
+    gates = ALL_BF16.reshape(512, 128).repeat(1, I // 128)
     for up_kind in ("one", "random"):
         if up_kind == "one":
             ups = torch.ones(512, I, dtype=torch.bfloat16)
@@ -97,6 +98,28 @@ def test_act_quant_regression_grid(I, rows, mode, fmt):
                                       7.0, fmt, q_init=qs.numpy(), s_init=ss.numpy())
     assert (q.cpu().numpy() == rq).all()
     assert (s.cpu().numpy().view(np.uint32) == rs.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("tokens", [1, 64, 1024])
+def test_act_quant_expert_parallel_workload(tokens):
+    # 8-way expert parallelism: top-k 6 rows, width 2048, 32 of 256 experts
+    # local through the expert map; the 7/8 non-local rows keep their
+    # sentinel bytes, the local ones are bit-exact
+    print_case("act_quant ep8", tokens)
+    x, ids, emap = synth.ep_act_inputs(tokens, "ep8")
+    rows, I = x.shape[0], synth.EP_I
+    qs = torch.full((rows, I), 0x3C, dtype=torch.uint8)
+    ss = torch.full((rows, I // 128), -5.0)
+    q, s = bfp8.silu_and_mul_quant_fp8(x.to(dev()), q=qs.to(dev()), scales=ss.to(dev()), row_expert_ids=ids.to(dev()),
+                                       expert_map=emap.to(dev()), E=synth.EP_E, clamp_limit=7.0,
+                                       scale_fmt=bfp8.SCALE_UE8M0)
+    torch.cuda.synchronize()
+    rq, rs = O.silu_and_mul_quant_fp8(x, ids, emap, synth.EP_E, 7.0, bfp8.SCALE_UE8M0, q_init=qs.numpy(),
+                                      s_init=ss.numpy())
+    assert (q.cpu().numpy() == rq).all()
+    assert (s.cpu().numpy().view(np.uint32) == rs.view(np.uint32)).all()
+    live = (emap[ids.long()] >= 0).numpy()
+    assert 0 < live.sum() < rows or rows == 6
 
 
 @pytest.mark.parametrize("tokens", list(synth.ACT_TOKENS))
