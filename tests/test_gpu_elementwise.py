@@ -164,3 +164,19 @@ def test_moe_reduce_bitexact(M, k, H):
     out2 = bfp8.moe_reduce(y.to(dev()), w.to(dev()))
     torch.cuda.synchronize()
     assert (bf16_np(out2) == O.moe_reduce(y, w)).all()
+
+
+def test_zero_rows():
+    # empty inputs: every elementwise entry point accepts zero rows and writes nothing
+    print_case("zero rows")
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device=dev())
+    q, s = bfp8.quant_fp8(x)
+    assert tuple(q.shape) == (0, 256) and tuple(s.shape) == (0, 2)
+    gu = torch.empty(0, 512, dtype=torch.bfloat16, device=dev())
+    assert tuple(bfp8.silu_and_mul(gu).shape) == (0, 256)
+    q, s = bfp8.silu_and_mul_quant_fp8(gu, clamp_limit=7.0)
+    assert tuple(q.shape) == (0, 256)
+    y = torch.empty(0, 256, dtype=torch.bfloat16, device=dev())
+    out = bfp8.moe_reduce(y, torch.empty(0, 2, device=dev()))
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 256)

@@ -280,3 +280,15 @@ def test_one_token_grid_changes_on_one_workspace():
                                            o=bfp8.opts(flags=bfp8.FLAG_LAYER_TOKEN), ws=ws)
             torch.cuda.synchronize()
             assert normwise_err(bf16_np(out), ref) <= LAYER_TOL, c.name
+
+
+@pytest.mark.parametrize("path", [0] + PATHS)
+def test_layer_zero_tokens(path):
+    # M = 0: nothing to do, every path returns an empty output without error
+    print_case("layer zero tokens", path)
+    c = synth.LAYER_CASES["tiny"]
+    hidden, ids, w, W = synth.layer_inputs(c, 0, device=dev())
+    out = bfp8.fused_moe_block_fp8(hidden[:0], ids[:0], w[:0], W.w13, W.w13_s, W.w2, W.w2_s, E=c.E,
+                                   o=bfp8.opts(flags=path))
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, c.H)
