@@ -47,6 +47,7 @@ struct LayerPlan {
   float clamp;
   int64_t max_blocks;
   bool route_single;
+  bool rq_fused;  // general path: route preparation carries the input quantisation
   int mode;  // kModeGeneral, kModeDecode, kModeToken
   size_t off_aq, off_as, off_sorted, off_eoff, off_bexp, off_bstart, off_nb, off_rws, off_h13, off_q, off_s,
       off_y, off_act, total;
@@ -54,6 +55,10 @@ struct LayerPlan {
 
 const char* const kGeneralStages[] = {"route_prepare", "quant_fp8", "gate_up_gemm",
                                       "silu_and_mul_quant", "down_gemm", "moe_reduce"};
+// General path whose route preparation also quantises the input (one launch
+// fewer): stage 0 covers both.
+const char* const kGeneralFusedStages[] = {"route_prepare_quant", "gate_up_gemm", "silu_and_mul_quant", "down_gemm",
+                                           "moe_reduce"};
 const char* const kDecodeStages[] = {"decode_gate_up_swiglu", "decode_down_reduce"};
 const char* const kTokenStages[] = {"token_gate_up_swiglu", "token_down_reduce"};
 enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
@@ -108,6 +113,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
     p.route_single = false;
   else
     p.route_single = bfp8::route_prep_single_fits(p.R, p.L);
+  p.rq_fused = bfp8::route_prep_can_quant(p.route_single, p.L);
   size_t o_ = 0;
   auto take = [&](size_t bytes) {
     size_t at = o_;
@@ -134,6 +140,8 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.off_y = take(sizeof(uint16_t) * (size_t)p.R * H);
   p.total = o_;
 }
+
+int plan_stages(const LayerPlan& p) { return p.mode == kModeGeneral ? (p.rq_fused ? 5 : 6) : 2; }
 
 bool valid_fmt(int32_t f) { return f == BFP8MOE_SCALE_FP32 || f == BFP8MOE_SCALE_UE8M0; }
 
@@ -337,8 +345,11 @@ int32_t fused_moe_block_fp8_stages(int64_t M, int32_t H, int32_t k, int32_t E, i
   if (check_layer_shape(M, H, k, E, I, o) != BFP8MOE_OK) return -1;
   LayerPlan p;
   plan_layer(p, M, H, k, E, I, o);
-  const char* const* list = p.mode == kModeToken ? kTokenStages : p.mode == kModeDecode ? kDecodeStages : kGeneralStages;
-  const int32_t n = p.mode == kModeGeneral ? 6 : 2;
+  const char* const* list = p.mode == kModeToken    ? kTokenStages
+                            : p.mode == kModeDecode ? kDecodeStages
+                            : p.rq_fused            ? kGeneralFusedStages
+                                                    : kGeneralStages;
+  const int32_t n = plan_stages(p);
   for (int32_t i = 0; names && i < n && i < cap; i++) names[i] = list[i];
   return n;
 }
@@ -374,7 +385,7 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   LayerPlan p;
   plan_layer(p, M, H, k, E, I, o);
   const int only = (int)((o.flags >> BFP8MOE_FLAG_STAGE_SHIFT) & 15u) - 1;
-  const int n_stages = p.mode == kModeGeneral ? 6 : 2;
+  const int n_stages = plan_stages(p);
   if (only >= n_stages) return fail(BFP8MOE_ERR_INVALID_ARG, "stage %d selected, the path has %d", only, n_stages);
   if (ws == nullptr || ws_bytes < p.total)
     return fail(BFP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
@@ -384,7 +395,7 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   char* base = static_cast<char*>(ws);
   bfp8::LaunchHook hook;
   hook.events = o.stage_events;
-  hook.n = o.stage_events ? (p.mode == kModeGeneral ? 7 : 3) : 0;
+  hook.n = o.stage_events ? n_stages + 1 : 0;
   hook.only = only;
   if (p.mode == kModeToken) {
     uint16_t* act = reinterpret_cast<uint16_t*>(base + p.off_act);
@@ -412,16 +423,24 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   uint16_t* y = reinterpret_cast<uint16_t*>(base + p.off_y);
 
   hipError_t e = hipSuccess;
-  hook.before(0, st);
-  if (hook.run(0))
+  // stage numbers: with the input quantisation carried by route preparation
+  // (rq_fused) the stages after it move down by one
+  const int sq = p.rq_fused ? 0 : 1;  // the stage that quantises the input
+  int st_i = 0;
+  hook.before(st_i, st);
+  if (hook.run(st_i)) {
+    const bfp8::QuantArgs qa{hidden, M, H, p.fmt, aq, as};
     e = bfp8::launch_route_prepare(topk_ids, p.R, p.offset, p.L, p.block_m, sorted, eoff, bexp, bstart, p.max_blocks,
-                                   nb, p.route_single, rws, st);
+                                   nb, p.route_single, rws, st, p.rq_fused ? &qa : nullptr);
+  }
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: route prep");
-  hook.before(1, st);
-  if (hook.run(1)) e = bfp8::launch_quant_fp8(hidden, M, H, p.fmt, aq, as, st);
-  if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: input quant");
-  hook.before(2, st);
-  if (hook.run(2))
+  if (sq == 1) {
+    hook.before(++st_i, st);
+    if (hook.run(st_i)) e = bfp8::launch_quant_fp8(hidden, M, H, p.fmt, aq, as, st);
+    if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: input quant");
+  }
+  hook.before(++st_i, st);
+  if (hook.run(st_i))
     e = bfp8::launch_grouped_gemm(aq, as, k, w13, w13_scale, 2 * I, H, sorted, eoff, bexp, bstart, nb, p.max_blocks,
                                   p.block_m, h13, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: gate/up GEMM");
@@ -430,17 +449,17 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   f.offset = p.offset;
   f.L = p.L;
   f.mode = bfp8::kRowsLocalSlice;
-  hook.before(3, st);
-  if (hook.run(3)) e = bfp8::launch_silu_and_mul_quant(h13, p.R, I, f, p.clamp, p.fmt, q, s, st);
+  hook.before(++st_i, st);
+  if (hook.run(st_i)) e = bfp8::launch_silu_and_mul_quant(h13, p.R, I, f, p.clamp, p.fmt, q, s, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: act+quant");
-  hook.before(4, st);
-  if (hook.run(4))
+  hook.before(++st_i, st);
+  if (hook.run(st_i))
     e = bfp8::launch_grouped_gemm(q, s, 1, w2, w2_scale, H, I, sorted, eoff, bexp, bstart, nb, p.max_blocks,
                                   p.block_m, y, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: down GEMM");
-  hook.before(5, st);
-  if (hook.run(5)) e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, p.offset, p.L, M, k, H, out, st);
-  hook.before(6, st);
+  hook.before(++st_i, st);
+  if (hook.run(st_i)) e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, p.offset, p.L, M, k, H, out, st);
+  hook.before(++st_i, st);
   return hip_status(e, "fused_moe_block_fp8: moe_reduce");
 }
 

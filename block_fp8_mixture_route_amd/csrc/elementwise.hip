@@ -53,16 +53,8 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __r
                                                              int gpr, int fmt, uint8_t* __restrict__ q,
                                                              float* __restrict__ s) {
   const int64_t gid = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
-  const int l16 = threadIdx.x & 15;
   if (gid >= n_groups) return;  // whole 16-lane group leaves together
-  const size_t base = (size_t)gid * kGroup + (size_t)l16 * 8;  // rows are contiguous groups
-  uint4 v = *reinterpret_cast<const uint4*>(x + base);
-  float f[8];
-  unpack8(v, f);
-  float amax = max_over_16(lane_amax8(f));
-  float sc = group_scale(amax, fmt);
-  *reinterpret_cast<uint2*>(q + base) = encode8_scaled(f, sc);
-  if (l16 == 0) s[gid] = sc;
+  quant_group8(x, gid, threadIdx.x & 15, fmt, q, s);  // rows are contiguous groups
   (void)gpr;
 }
 

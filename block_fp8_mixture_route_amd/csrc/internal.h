@@ -52,12 +52,25 @@ hipError_t launch_moe_reduce(const uint16_t* y, const float* w, const int32_t* i
 // otherwise count -> scan+scatter over `route_prep_num_segments(R)` workgroups
 // with a workspace of route_prep_ws_bytes(R, L) bytes.
 bool route_prep_single_fits(int64_t R, int32_t L);
+// Input quantisation that the first launch of route preparation can carry
+// (quant_fp8 of x [rows, K] into q, s), so that the layer makes one launch
+// fewer.  Possible unless the single-workgroup path serves more than 512
+// experts.
+struct QuantArgs {
+  const uint16_t* x;
+  int64_t rows;
+  int K;
+  int fmt;
+  uint8_t* q;
+  float* s;
+};
+bool route_prep_can_quant(bool single, int32_t L);
 int route_prep_num_segments(int64_t R);
 size_t route_prep_ws_bytes(int64_t R, int32_t L);
 hipError_t launch_route_prepare(const int32_t* ids, int64_t R, int32_t offset, int32_t L, int32_t block_m,
                                 int32_t* sorted_routes, int32_t* expert_offsets, int32_t* block_expert,
                                 int32_t* block_start, int64_t max_blocks, int32_t* num_blocks, bool single,
-                                void* ws, hipStream_t stream);
+                                void* ws, hipStream_t stream, const QuantArgs* quant = nullptr);
 
 // Grouped block-FP8 GEMM over compact blocks (general path).
 hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div, const uint8_t* B,

@@ -37,6 +37,10 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxL = 2048;
 constexpr int64_t kSingleMaxRoutes = 4096;
+// Largest expert count whose single-workgroup launch also carries the input
+// quantisation: its quantisation workgroups get the same dynamic LDS as the
+// route-prep workgroup, (16 + 3) L + 64 ints, 38 KB at 512.
+constexpr int32_t kQuantMaxL = 512;
 
 __device__ __forceinline__ int local_expert(const int32_t* ids, int64_t r, int32_t offset, int32_t L) {
   int64_t e = (int64_t)ids[r] - offset;
@@ -86,10 +90,34 @@ __device__ int block_exclusive_scan(int* v, int n, int* tmp) {
   return total;
 }
 
+// The optional input quantisation carried by the first launch of route
+// preparation (one launch fewer in the layer): workgroups n_main and up each
+// quantise 64 groups of 128 of x (same arithmetic as quant_fp8).
+struct QuantJob {
+  const uint16_t* x = nullptr;  // nullptr: no quantisation workgroups
+  int64_t n_groups = 0;
+  int fmt = 0;
+  uint8_t* q = nullptr;
+  float* s = nullptr;
+};
+constexpr int kQuantGroupsPerWG = kThreads / 16;
+
+__device__ __forceinline__ bool quant_job(const QuantJob& qj, int n_main) {
+  if (qj.x == nullptr || (int)blockIdx.x < n_main) return false;
+  const int64_t gid = (int64_t)(blockIdx.x - n_main) * kQuantGroupsPerWG + (threadIdx.x >> 4);
+  if (gid < qj.n_groups) quant_group8(qj.x, gid, threadIdx.x & 15, qj.fmt, qj.q, qj.s);
+  return true;
+}
+
+inline unsigned quant_wgs(const QuantJob& qj) {
+  return qj.x ? (unsigned)((qj.n_groups + kQuantGroupsPerWG - 1) / kQuantGroupsPerWG) : 0u;
+}
+
 // Count pass of the multi-workgroup path: hist[seg][e] for each segment.
 __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __restrict__ ids, int64_t R,
                                                                int32_t offset, int32_t L, int64_t seg_len,
-                                                               int32_t* __restrict__ hist) {
+                                                               int32_t* __restrict__ hist, int n_main, QuantJob qj) {
+  if (quant_job(qj, n_main)) return;
   extern __shared__ int lds[];
   int* h = lds;
   for (int e = threadIdx.x; e < L; e += kThreads) h[e] = 0;
@@ -111,7 +139,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t R, int32_t offset, int32_t L, int32_t block_m, int64_t seg_len,
     const int32_t* __restrict__ hist, int n_seg, int32_t* __restrict__ sorted_routes,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ block_expert, int32_t* __restrict__ block_start,
-    int64_t max_blocks, int32_t* __restrict__ num_blocks) {
+    int64_t max_blocks, int32_t* __restrict__ num_blocks, QuantJob qj) {
+  if (quant_job(qj, n_seg)) return;
   extern __shared__ int lds[];
   int* wh = lds;                       // [kWaves][L] wave histograms -> cursors
   int* offs = wh + kWaves * L;         // [L] expert totals -> exclusive offsets
@@ -247,10 +276,22 @@ size_t route_prep_ws_bytes(int64_t R, int32_t L) {
   return sizeof(int32_t) * (size_t)route_prep_num_segments(R) * (size_t)L;
 }
 
+bool route_prep_can_quant(bool single, int32_t L) { return !single || L <= kQuantMaxL; }
+
 hipError_t launch_route_prepare(const int32_t* ids, int64_t R, int32_t offset, int32_t L, int32_t block_m,
                                 int32_t* sorted_routes, int32_t* expert_offsets, int32_t* block_expert,
                                 int32_t* block_start, int64_t max_blocks, int32_t* num_blocks, bool single,
-                                void* ws, hipStream_t stream) {
+                                void* ws, hipStream_t stream, const QuantArgs* quant) {
+  QuantJob qj;
+  if (quant && quant->rows > 0) {
+    if (!route_prep_can_quant(single, L)) return hipErrorInvalidValue;  // the caller checks
+    qj.x = quant->x;
+    qj.n_groups = quant->rows * (quant->K / kGroup);
+    qj.fmt = quant->fmt;
+    qj.q = quant->q;
+    qj.s = quant->s;
+  }
+  const unsigned nq = quant_wgs(qj);
   // Large expert counts need more than 64 KB of LDS in one workgroup
   // (gfx950 allows up to 160 KB); raise the function's limit once.
   static std::once_flag once;
@@ -261,21 +302,21 @@ hipError_t launch_route_prepare(const int32_t* ids, int64_t R, int32_t offset, i
   });
   const size_t lds = scatter_lds_bytes(L);
   if (single) {
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(1), dim3(kThreads), lds, stream, ids, R, offset, L, block_m,
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(1 + nq), dim3(kThreads), lds, stream, ids, R, offset, L, block_m,
                        R > 0 ? R : (int64_t)1, (const int32_t*)nullptr, 1, sorted_routes, expert_offsets,
-                       block_expert, block_start, max_blocks, num_blocks);
+                       block_expert, block_start, max_blocks, num_blocks, qj);
     return hipGetLastError();
   }
   const int n_seg = route_prep_num_segments(R);
   const int64_t seg_len = segment_length(R);
   int32_t* hist = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(route_count_kernel, dim3(n_seg), dim3(kThreads), sizeof(int) * (size_t)L, stream, ids, R,
-                     offset, L, seg_len, hist);
+  hipLaunchKernelGGL(route_count_kernel, dim3(n_seg + nq), dim3(kThreads), sizeof(int) * (size_t)L, stream, ids, R,
+                     offset, L, seg_len, hist, n_seg, qj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_scatter_kernel, dim3(n_seg), dim3(kThreads), lds, stream, ids, R, offset, L, block_m,
                      seg_len, (const int32_t*)hist, n_seg, sorted_routes, expert_offsets, block_expert,
-                     block_start, max_blocks, num_blocks);
+                     block_start, max_blocks, num_blocks, QuantJob());
   return hipGetLastError();
 }
 

@@ -240,9 +240,11 @@ bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_
  * device, and, when names is non-NULL, up to cap stage names (static strings)
  * in order.  The few-token path has two stages ("token_gate_up_swiglu",
  * "token_down_reduce"); the small-batch path two ("decode_gate_up_swiglu", "decode_down_reduce"); the
- * general path six ("route_prepare", "quant_fp8", "gate_up_gemm",
- * "silu_and_mul_quant", "down_gemm", "moe_reduce").  Returns -1 for arguments
- * fused_moe_block_fp8 would reject. */
+ * general path five ("route_prepare_quant", "gate_up_gemm",
+ * "silu_and_mul_quant", "down_gemm", "moe_reduce"): route preparation's first
+ * launch also quantises the input, except where one workgroup sorts for more
+ * than 512 local experts, where it is six ("route_prepare", "quant_fp8", ...).
+ * Returns -1 for arguments fused_moe_block_fp8 would reject. */
 int32_t fused_moe_block_fp8_stages(int64_t M, int32_t H, int32_t k, int32_t E, int32_t I,
                                    const bfp8moe_opts_t* opts, const char** names, int32_t cap);
 
@@ -274,8 +276,9 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
  *   small batch (M <= 8, k <= 8, H <= 8192, I <= 512): two kernels -- gate/up
  *     GEMM with route grouping, input quantisation and SwiGLU fused; then the
  *     SwiGLU output's quantisation, down GEMM and moe_reduce fused;
- *   general: route prep -> quant_fp8 -> grouped GEMM -> silu_and_mul_quant_fp8
- *     -> grouped GEMM -> moe_reduce.
+ *   general: route prep (its first launch also quant_fp8 of the hidden
+ *     states) -> grouped GEMM -> silu_and_mul_quant_fp8 -> grouped GEMM ->
+ *     moe_reduce.
  * Forcing a path on a shape outside its limits returns
  * BFP8MOE_ERR_UNSUPPORTED. */
 bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,

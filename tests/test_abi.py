@@ -51,14 +51,20 @@ def test_stage_lists():
     # the few-token path up to 12 tokens; the others when forced
     assert bfp8.fused_moe_stages(4, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
     assert bfp8.fused_moe_stages(12, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
-    assert bfp8.fused_moe_stages(13, 7168, 8, 256, 256, o)[0] == "route_prepare"
-    assert bfp8.fused_moe_stages(32, 7168, 8, 256, 256, o)[0] == "route_prepare"
+    # the general path: route preparation carries the input quantisation
+    # (one launch fewer) unless one workgroup sorts for more than 512 experts
+    fused = ["route_prepare_quant", "gate_up_gemm", "silu_and_mul_quant", "down_gemm", "moe_reduce"]
+    assert bfp8.fused_moe_stages(13, 7168, 8, 256, 256, o) == fused
+    assert bfp8.fused_moe_stages(32, 7168, 8, 256, 256, o) == fused
+    assert bfp8.fused_moe_stages(2048, 4096, 8, 512, 1024, o) == fused  # many-workgroup route prep
+    assert bfp8.fused_moe_stages(64, 4096, 8, 1024, 256, o) == [
+        "route_prepare", "quant_fp8", "gate_up_gemm", "silu_and_mul_quant", "down_gemm", "moe_reduce"]
     assert bfp8.fused_moe_stages(4, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_DECODE)) == [
         "decode_gate_up_swiglu", "decode_down_reduce"]
     assert bfp8.fused_moe_stages(32, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_TOKEN)) == [
         "token_gate_up_swiglu", "token_down_reduce"]
-    assert bfp8.fused_moe_stages(512, 4096, 8, 256, 768, o)[2] == "gate_up_gemm"
-    assert len(bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_GENERAL))) == 6
+    assert bfp8.fused_moe_stages(512, 4096, 8, 256, 768, o)[1] == "gate_up_gemm"
+    assert len(bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_GENERAL))) == 5
     with pytest.raises(bfp8.BFP8MoEError):
         bfp8.fused_moe_stages(64, 7168, 8, 256, 256, bfp8.opts(flags=bfp8.FLAG_LAYER_DECODE))
     with pytest.raises(bfp8.BFP8MoEError):
