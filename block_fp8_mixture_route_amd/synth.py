@@ -237,3 +237,20 @@ def layer_inputs(case: LayerCase, instance: int = 0, device="cpu", only_active=T
     active = torch.unique(ids).tolist() if only_active else None
     weights = moe_weights(case.E, case.H, case.I, case.name, instance, experts=active, device=device)
     return hidden, ids, w, weights
+
+
+# router inputs: [M, E] fp32 logits, N(0, std); with bf16_valued the logits are
+# rounded to BF16 values first (a router GEMM computed in BF16), which makes
+# equal logits within a token common at E = 256
+def router_logits(M: int, E: int, *key, std=1.0, bf16_valued=False, device="cpu"):
+    g = gen(device, *key, "router_logits", M, E)
+    x = torch.randn(M, E, generator=g, device=device, dtype=torch.float32) * std
+    if bf16_valued:
+        x = x.to(torch.bfloat16).to(torch.float32)
+    return x.contiguous()
+
+
+def router_bias(E: int, *key, std=0.05, device="cpu"):
+    """Per-expert selection bias of sigmoid routing, N(0, std) fp32."""
+    g = gen(device, *key, "router_bias", E)
+    return (torch.randn(E, generator=g, device=device, dtype=torch.float32) * std).contiguous()

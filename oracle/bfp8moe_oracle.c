@@ -390,6 +390,75 @@ void oracle_moe_reduce(const uint16_t* y, const float* w, const int32_t* topk_id
 }
 
 /* ------------------------------------------------------------------------- */
+/* Single-group top-k router: router logits -> top-k expert ids and weights    */
+/* [P2 Changes: fused single-group top-k router; renormalize option]           */
+/* ------------------------------------------------------------------------- */
+
+enum { ORACLE_SCORE_SOFTMAX = 0, ORACLE_SCORE_SIGMOID = 1 };
+
+/* Sigmoid of an fp32 logit, computed in double and rounded once to fp32. */
+float oracle_sigmoid_rn(float x) { return (float)(1.0 / (1.0 + exp(-(double)x))); }
+
+/* The value an expert is ranked by.  Softmax is strictly increasing in the
+ * logit, so ranking the exact probabilities is ranking the logits themselves.
+ * Sigmoid scores are ranked as the fp32 score plus the optional per-expert
+ * selection bias, one fp32 add (the bias steers which experts are chosen, not
+ * their weights). */
+static float router_key(const float* lg, const float* bias, int score_fn, int e)
+{
+    if (score_fn == ORACLE_SCORE_SOFTMAX) return lg[e];
+    float s = oracle_sigmoid_rn(lg[e]);
+    return bias ? s + bias[e] : s;
+}
+
+/* logits: [M, E] fp32; bias: [E] fp32 or NULL (sigmoid scoring only);
+ * topk_ids: [M, k] int32; topk_w: [M, k] fp32.  For each token the k experts
+ * with the largest keys are chosen one at a time, largest first; equal keys go
+ * to the lower expert id.  Weights, in fp64 and rounded once to fp32:
+ *   softmax: exp(l_j - m) / Z with m the largest logit, Z summed over the k
+ *            chosen experts when renormalize is set, else over all E;
+ *   sigmoid: 1 / (1 + exp(-l_j)), divided by the sum over the k chosen when
+ *            renormalize is set;
+ * both then times scale. */
+void oracle_router_topk(const float* logits, int64_t M, int E, int k, int score_fn, const float* bias,
+                        int renormalize, double scale, int32_t* topk_ids, float* topk_w)
+{
+    char* taken = (char*)malloc((size_t)E);
+    double* v = (double*)malloc(sizeof(double) * (size_t)k);
+    for (int64_t t = 0; t < M; t++) {
+        const float* lg = logits + (size_t)t * E;
+        int32_t* ids = topk_ids + (size_t)t * k;
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; j++) {
+            int best = -1;
+            float bk = 0.0f;
+            for (int e = 0; e < E; e++) {
+                if (taken[e]) continue;
+                float key = router_key(lg, bias, score_fn, e);
+                if (best < 0 || key > bk) { best = e; bk = key; }
+            }
+            taken[best] = 1;
+            ids[j] = best;
+        }
+        double z = 0.0;
+        if (score_fn == ORACLE_SCORE_SOFTMAX) {
+            double m = lg[0];
+            for (int e = 1; e < E; e++) if (lg[e] > m) m = lg[e];
+            for (int j = 0; j < k; j++) v[j] = exp((double)lg[ids[j]] - m);
+            if (renormalize) for (int j = 0; j < k; j++) z += v[j];
+            else for (int e = 0; e < E; e++) z += exp((double)lg[e] - m);
+        } else {
+            for (int j = 0; j < k; j++) v[j] = 1.0 / (1.0 + exp(-(double)lg[ids[j]]));
+            if (renormalize) for (int j = 0; j < k; j++) z += v[j];
+            else z = 1.0;
+        }
+        for (int j = 0; j < k; j++) topk_w[(size_t)t * k + j] = (float)(v[j] / z * scale);
+    }
+    free(v);
+    free(taken);
+}
+
+/* ------------------------------------------------------------------------- */
 /* Whole layer for a subset of tokens                                          */
 /* [P1 Modification: gate/up GEMM -> silu_and_mul_post_quant -> FP8 activation  */
 /*  + scale -> down GEMM]; [P4: moe_reduce applies the router weights]          */

@@ -56,6 +56,8 @@ def lib():
             "oracle_route_prepare": (i64, [P, i64, i32, i32, i32, P, P, P, P, i64, P]),
             "oracle_grouped_gemm": (None, [P, P, i32, P, P, i32, i32, P, i64, i32, i32, P]),
             "oracle_moe_reduce": (None, [P, P, P, i32, i32, i64, i32, i32, P]),
+            "oracle_sigmoid_rn": (f32, [f32]),
+            "oracle_router_topk": (None, [P, i64, i32, i32, i32, P, i32, ctypes.c_double, P, P]),
             "oracle_fused_moe": (None, [P, i64, i32, P, P, i32, P, P, P, P, i32, i32, i32, i32, f32,
                                         P, i64, P, P, P, P, P]),
             "oracle_num_threads": (i32, []),
@@ -204,6 +206,27 @@ def moe_reduce(y_bf16, topk_w, topk_ids=None, expert_offset: int = 0, L: int = 1
     out = np.zeros((M, H), np.uint16)
     lib().oracle_moe_reduce(_p(y), _p(w), _p(ids), expert_offset, L, M, k, H, _p(out))
     return out
+
+
+SCORE_SOFTMAX = 0
+SCORE_SIGMOID = 1
+
+
+def router_topk(logits, k: int, score_fn: int = SCORE_SOFTMAX, bias=None, renormalize: bool = True,
+                scale: float = 1.0):
+    """Top-k experts per token from [M, E] fp32 router logits: ([M, k] int32
+    ids, largest first, and [M, k] fp32 weights)."""
+    lg = as_np(logits, np.float32)
+    M, E = lg.shape
+    b = None if bias is None else as_np(bias, np.float32)
+    ids = np.zeros((M, k), np.int32)
+    w = np.zeros((M, k), np.float32)
+    lib().oracle_router_topk(_p(lg), M, E, k, score_fn, _p(b), int(bool(renormalize)), float(scale), _p(ids), _p(w))
+    return ids, w
+
+
+def sigmoid_rn(x: float) -> float:
+    return lib().oracle_sigmoid_rn(x)
 
 
 def fused_moe(hidden, topk_ids, topk_w, w13, w13_s, w2, w2_s, expert_offset: int = 0, L: int = None,
