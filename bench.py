@@ -458,6 +458,37 @@ def suite(hip, stream, dev):
         res["route_prep"][R] = {"L": L, "block_m": bm, "single_us": row[0], "multi_us": row[1]}
         print(f"| {R} | {L} | {bm} | {row[0]:.2f} | {row[1]:.2f} |", flush=True)
 
+    # single-group top-k router: softmax (renormalised) and biased sigmoid
+    # (renormalised), each one launch, beside torch's softmax -> topk ->
+    # renormalise for context
+    print()
+    print("| tokens M | experts E | k | softmax µs | sigmoid + bias µs | torch softmax/topk/renorm µs |")
+    print("|---|---|---|---|---|---|")
+    res["router"] = {}
+    for (M, E) in [(1, 256), (16, 256), (256, 256), (2048, 512), (4096, 256), (16384, 256)]:
+        lg = synth.router_logits(M, E, "bench_router", device=dev)
+        bias = synth.router_bias(E, "bench_router", device=dev)
+        rid = torch.empty(M, 8, dtype=torch.int32, device=dev)
+        rw = torch.empty(M, 8, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+        def rt(score_fn, b):
+            bfp8._lib.check(L_.moe_router_topk(P(lg.data_ptr()), M, E, 8, score_fn,
+                                               None if b is None else P(b.data_ptr()), 1, 1.0, P(rid.data_ptr()),
+                                               P(rw.data_ptr()), stream))
+
+        def torch_router():
+            with torch.cuda.stream(ext):
+                for _ in range(20):
+                    v, _i = torch.topk(torch.softmax(lg, -1), 8, -1)
+                    v / v.sum(-1, keepdim=True)
+
+        ts = time_graph(hip, stream, lambda: [rt(bfp8.SCORE_SOFTMAX, None) for _ in range(20)], 20) * 1e3 / 20
+        tg = time_graph(hip, stream, lambda: [rt(bfp8.SCORE_SIGMOID, bias) for _ in range(20)], 20) * 1e3 / 20
+        tt = time_graph(hip, stream, torch_router, 20) * 1e3 / 20
+        res["router"][f"{M}x{E}"] = {"softmax_us": ts, "sigmoid_bias_us": tg, "torch_us": tt}
+        print(f"| {M} | {E} | 8 | {ts:.2f} | {tg:.2f} | {tt:.2f} |", flush=True)
+
     # a plain device copy of the decode layer's size, rotating over buffers
     # that together exceed the Infinity Cache: the practical HBM ceiling
     nbytes = 44 << 20

@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     FLAG_ROUTE_SINGLE_WG,
     SCALE_FP32,
     SCALE_UE8M0,
+    SCORE_SIGMOID,
+    SCORE_SOFTMAX,
     Opts,
     fused_moe_block_fp8,
     fused_moe_stages,
@@ -25,6 +27,7 @@ from ._lib import (  # noqa: F401
     moe_route_prepare,
     opts,
     quant_fp8,
+    router_topk,
     silu_and_mul,
     silu_and_mul_quant_fp8,
 )

@@ -69,6 +69,7 @@ SIGNATURES = {
     "moe_fp8_grouped_gemm": (ctypes.c_int, [_P, _P, _i32, _P, _P, _i32, _i32, _i32, _P, _P, _P, _P, _P, _i64, _i32,
                                             _i64, _P, _P]),
     "moe_reduce": (ctypes.c_int, [_P, _P, _P, _i32, _i32, _i64, _i32, _i32, _P, _P]),
+    "moe_router_topk": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _P, _i32, ctypes.c_double, _P, _P, _P]),
     "fused_moe_block_fp8_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(Opts)]),
     "fused_moe_block_fp8_stages": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(Opts),
                                           ctypes.POINTER(ctypes.c_char_p), _i32]),
@@ -210,6 +211,25 @@ def moe_reduce(y, topk_w, topk_ids=None, expert_offset=0, L=0, out=None):
     check(lib().moe_reduce(ptr(_u16(y)), ptr(topk_w), ptr(topk_ids), expert_offset, L, M, k, H, ptr(_u16(out)),
                            stream_of(y.device)))
     return out
+
+
+SCORE_SOFTMAX = 0
+SCORE_SIGMOID = 1
+
+
+def router_topk(logits, k, score_fn=SCORE_SOFTMAX, bias=None, renormalize=True, scale=1.0, topk_ids=None,
+                topk_w=None):
+    """[M, E] fp32 router logits -> ([M, k] int32 expert ids, largest first,
+    [M, k] fp32 weights)."""
+    _require_device(logits, bias, topk_ids, topk_w)
+    if logits.dtype != torch.float32:
+        raise ValueError("router logits must be float32")
+    M, E = logits.shape
+    ids = torch.empty(M, k, dtype=torch.int32, device=logits.device) if topk_ids is None else topk_ids
+    w = torch.empty(M, k, dtype=torch.float32, device=logits.device) if topk_w is None else topk_w
+    check(lib().moe_router_topk(ptr(logits), M, E, k, score_fn, ptr(bias), int(bool(renormalize)), float(scale),
+                                ptr(ids), ptr(w), stream_of(logits.device)))
+    return ids, w
 
 
 def fused_moe_workspace_size(M, H, k, E, I, o: Opts) -> int:

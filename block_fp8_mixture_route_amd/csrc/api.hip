@@ -295,6 +295,21 @@ bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_
                     "moe_reduce");
 }
 
+bfp8moe_status_t moe_router_topk(const float* logits, int64_t M, int32_t E, int32_t k, int32_t score_fn,
+                                 const float* bias, int32_t renormalize, double scale, int32_t* topk_ids,
+                                 float* topk_w, void* stream) {
+  REQUIRE(M >= 0, "M=%lld invalid", (long long)M);
+  REQUIRE(E >= 1 && E <= 1024, "E=%d must be in [1, 1024]", E);
+  REQUIRE(k >= 1 && k <= 64 && k <= E, "k=%d must be in [1, min(E, 64)]", k);
+  REQUIRE(score_fn == BFP8MOE_SCORE_SOFTMAX || score_fn == BFP8MOE_SCORE_SIGMOID, "score_fn=%d invalid", score_fn);
+  REQUIRE(bias == nullptr || score_fn == BFP8MOE_SCORE_SIGMOID, "a selection bias needs sigmoid scoring");
+  REQUIRE(isfinite(scale), "scale must be finite");
+  REQUIRE(M == 0 || (logits && topk_ids && topk_w), "logits, topk_ids and topk_w must be non-null");
+  return hip_status(bfp8::launch_router_topk(logits, M, E, k, score_fn, bias, renormalize != 0, scale, topk_ids,
+                                             topk_w, (hipStream_t)stream),
+                    "moe_router_topk");
+}
+
 }  // extern "C"
 
 namespace {

@@ -45,6 +45,12 @@ hipError_t launch_silu_and_mul(const uint16_t* gu, int64_t rows, int I, float li
                                hipStream_t stream);
 hipError_t launch_silu_and_mul_quant(const uint16_t* gu, int64_t rows, int I, const RowFilter& f, float limit,
                                      int fmt, uint8_t* q, float* s, hipStream_t stream);
+// Router scoring functions (values of the C ABI's score_fn).
+enum RouterScore : int { kScoreSoftmax = 0, kScoreSigmoid = 1 };
+
+hipError_t launch_router_topk(const float* logits, int64_t M, int E, int k, int score_fn, const float* bias,
+                              int renorm, double scale, int32_t* ids, float* w, hipStream_t stream);
+
 hipError_t launch_moe_reduce(const uint16_t* y, const float* w, const int32_t* ids, int32_t offset, int32_t L,
                              int64_t M, int k, int H, uint16_t* out, hipStream_t stream);
 

@@ -215,6 +215,33 @@ bfp8moe_status_t moe_fp8_grouped_gemm(const uint8_t* A, const float* A_scale, in
                                       int64_t R, uint16_t* C, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Single-group top-k router                                                 */
+/* [P2 Changes: a fused single-group top-k router, with a renormalize        */
+/*  option, produces the top-k ids and weights the layer consumes]           */
+/* ------------------------------------------------------------------------- */
+
+typedef enum { BFP8MOE_SCORE_SOFTMAX = 0, BFP8MOE_SCORE_SIGMOID = 1 } bfp8moe_score_fn_t;
+
+/* logits [M, E] fp32 -> topk_ids [M, k] int32 and topk_w [M, k] fp32, each
+ * token's k experts in order of decreasing score.  All experts form one group.
+ * Ranking: softmax scoring ranks the logits themselves (softmax is increasing);
+ * sigmoid scoring ranks s_e + bias[e] in fp32, s_e the sigmoid of the logit
+ * computed in fp64 and rounded to fp32, bias [E] fp32 optional (NULL: none;
+ * it steers the choice only, never a weight).  Equal ranks go to the lower
+ * expert id; -0 and +0 rank equal.  Weights, fp64 rounded once to fp32, times
+ * scale:
+ *   softmax:  exp(l_j - max_e l_e) / Z, Z summed over the k chosen experts when
+ *             renormalize != 0, else over all E (plain softmax probabilities);
+ *   sigmoid:  1 / (1 + exp(-l_j)), divided by the sum over the k chosen when
+ *             renormalize != 0.
+ * 1 <= E <= 1024, 1 <= k <= min(E, 64); a bias needs sigmoid scoring; NaN
+ * logits are outside the contract (the ids stay k distinct values in [0, E)).
+ * The output is fed to the layer as its topk_ids / topk_w. */
+bfp8moe_status_t moe_router_topk(const float* logits, int64_t M, int32_t E, int32_t k, int32_t score_fn,
+                                 const float* bias, int32_t renormalize, double scale, int32_t* topk_ids,
+                                 float* topk_w, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* moe_reduce                                                                */
 /* [P4 Pull request overview: a dedicated reduction applies the router        */
 /*  weights, which the expert GEMMs no longer apply]                          */

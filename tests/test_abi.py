@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_route_prepare", "quant_fp8", "moe_fp8_grouped_gemm", "silu_and_mul_quant_fp8", "moe_reduce",
-              "fused_moe_block_fp8", "silu_and_mul", "fused_moe_block_fp8_workspace_size", "bfp8moe_max_blocks"):
+              "fused_moe_block_fp8", "silu_and_mul", "fused_moe_block_fp8_workspace_size", "bfp8moe_max_blocks", "moe_router_topk"):
         assert n in names
 
 
@@ -121,6 +121,16 @@ def test_host_validation_rejects_bad_calls():
     assert st == 1 and "stage 2" in msg
     st, msg = _status(L.moe_reduce, fake, fake, None, 0, 0, 2, 8, 100, fake, None)
     assert st == 1 and "multiple of 8" in msg
+    st, msg = _status(L.moe_router_topk, fake, 4, 2048, 8, 0, None, 1, 1.0, fake, fake, None)
+    assert st == 1 and "E=2048" in msg
+    st, msg = _status(L.moe_router_topk, fake, 4, 16, 17, 0, None, 1, 1.0, fake, fake, None)
+    assert st == 1 and "k=17" in msg
+    st, msg = _status(L.moe_router_topk, fake, 4, 256, 8, 0, fake, 1, 1.0, fake, fake, None)
+    assert st == 1 and "sigmoid" in msg
+    st, msg = _status(L.moe_router_topk, fake, 4, 256, 8, 2, None, 1, 1.0, fake, fake, None)
+    assert st == 1 and "score_fn" in msg
+    st, msg = _status(L.moe_router_topk, fake, 4, 256, 8, 1, None, 1, math.nan, fake, fake, None)
+    assert st == 1 and "scale" in msg
 
 
 def test_binding_refuses_host_tensors():

@@ -1,0 +1,93 @@
+"""GPU parity (through the C ABI) for the single-group top-k router: expert
+ids bit-exact against the CPU oracle, weights within one fp32 ulp (both sides
+form them in fp64 and round once; the exp and the sum order may differ in the
+last fp64 bit)."""
+import numpy as np
+import pytest
+import torch
+
+import block_fp8_mixture_route_amd as bfp8
+from block_fp8_mixture_route_amd import synth
+from oracle import oracle as O
+from tests.gpu_util import dev, print_case
+
+pytestmark = pytest.mark.gpu
+
+# (M, E, k): decode and prefill shapes of the layer's configurations (256 and
+# 512 experts, top-8), a width that is not a multiple of 64, k = E, the
+# largest E and k, one expert, and a ragged token count
+SHAPES = [(1, 256, 8), (7, 256, 8), (2048, 512, 8), (33, 64, 6), (5, 72, 6), (4, 8, 8), (3, 1024, 64),
+          (9, 1, 1), (130, 160, 2)]
+
+
+def ulps(a, b):
+    a = np.asarray(a, np.float32).astype(np.float64)
+    b = np.asarray(b, np.float32).astype(np.float64)
+    return np.abs(a - b) / np.spacing(np.abs(b).astype(np.float32)).astype(np.float64)
+
+
+def check(lg, k, score_fn, bias=None, renorm=True, scale=1.0):
+    ids, w = bfp8.router_topk(lg.to(dev()), k, score_fn, None if bias is None else bias.to(dev()), renorm, scale)
+    torch.cuda.synchronize()
+    rid, rw = O.router_topk(lg, k, score_fn, bias, renorm, scale)
+    assert (ids.cpu().numpy() == rid).all(), np.argwhere(ids.cpu().numpy() != rid)[:5]
+    assert ulps(w.cpu().numpy(), rw).max() <= 1.0
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("score_fn", [bfp8.SCORE_SOFTMAX, bfp8.SCORE_SIGMOID])
+@pytest.mark.parametrize("M,E,k", SHAPES)
+def test_router_parity(M, E, k, score_fn, renorm):
+    print_case("router", M, E, k, score_fn, renorm)
+    # BF16-valued logits (equal values within a token are common) and plain fp32 ones
+    for bf16_valued in (True, False):
+        lg = synth.router_logits(M, E, "router", bf16_valued, std=2.0, bf16_valued=bf16_valued)
+        bias = synth.router_bias(E, "router", std=0.1) if score_fn == bfp8.SCORE_SIGMOID else None
+        check(lg, k, score_fn, bias, renorm, 2.5 if score_fn == bfp8.SCORE_SIGMOID else 1.0)
+        if bias is not None:
+            check(lg, k, score_fn, None, renorm)
+
+
+def test_router_edge_values():
+    print_case("router edge values")
+    # all equal, signed zeros, infinities, logits near +-800 (exp without the
+    # max subtracted over- or underflows), huge sigmoid arguments
+    lg = torch.zeros(8, 96)
+    lg[1, 10] = -0.0
+    lg[1, 20] = 1.0
+    lg[2] = torch.linspace(-800, 800, 96)
+    lg[3, :] = float("-inf")
+    lg[3, 50] = 0.0
+    lg[4, 7] = float("inf")
+    lg[5] = 800.0 + torch.randn(96, generator=torch.Generator().manual_seed(3))
+    lg[6] = -800.0 + torch.randn(96, generator=torch.Generator().manual_seed(4))
+    lg[7, ::2] = -0.0
+    for score_fn in (bfp8.SCORE_SOFTMAX, bfp8.SCORE_SIGMOID):
+        ids, _ = bfp8.router_topk(lg.to(dev()), 8, score_fn)
+        torch.cuda.synchronize()
+        rid, _ = O.router_topk(lg, 8, score_fn)
+        assert (ids.cpu().numpy() == rid).all()
+    ids, w = bfp8.router_topk(lg[[0, 1, 2, 5, 6, 7]].contiguous().to(dev()), 8)
+    torch.cuda.synchronize()
+    rid, rw = O.router_topk(lg[[0, 1, 2, 5, 6, 7]], 8)
+    assert (ids.cpu().numpy() == rid).all() and ulps(w.cpu().numpy(), rw).max() <= 1.0
+    assert ids[0].tolist() == list(range(8))
+
+
+def test_router_zero_tokens_and_layer_feed():
+    print_case("router zero tokens / layer feed")
+    ids, w = bfp8.router_topk(torch.empty(0, 256, device=dev()), 8)
+    assert tuple(ids.shape) == (0, 8)
+    # the router's output drives the layer: same result as the oracle's routing
+    M, E, k, H, I = 3, 16, 4, 256, 128
+    lg = synth.router_logits(M, E, "feed")
+    ids, w = bfp8.router_topk(lg.to(dev()), k)
+    mw = synth.moe_weights(E, H, I, "feed", device="cpu")
+    hidden = synth.hidden_states(M, H, "feed")
+    out = bfp8.fused_moe_block_fp8(hidden.to(dev()), ids, w, mw.w13.to(dev()), mw.w13_s.to(dev()), mw.w2.to(dev()),
+                                   mw.w2_s.to(dev()), E=E)
+    torch.cuda.synchronize()
+    rid, rw = O.router_topk(lg, k)
+    ref = O.fused_moe(hidden, rid, rw, mw.w13, mw.w13_s, mw.w2, mw.w2_s)
+    from tests.gpu_util import bf16_np, normwise_err, LAYER_TOL
+    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
