@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import json
 import math
 import os
@@ -299,6 +300,113 @@ def launch_floor(hip, stream, dev):
     return us
 
 
+def router_table(hip, stream, dev):
+    """Single-group top-k router, graph-timed: softmax (renormalised) and
+    biased sigmoid (renormalised), each one launch, beside torch's softmax ->
+    topk -> renormalise for context."""
+    import torch
+
+    import block_fp8_mixture_route_amd as bfp8
+    from block_fp8_mixture_route_amd import synth
+
+    L_ = bfp8.lib()
+    P = ctypes.c_void_p
+    ext = torch.cuda.ExternalStream(stream.value, device=dev)
+    print()
+    print("| tokens M | experts E | k | softmax µs | sigmoid + bias µs | torch softmax/topk/renorm µs |")
+    print("|---|---|---|---|---|---|")
+    out = {}
+    for (M, E) in [(1, 256), (16, 256), (256, 256), (2048, 512), (4096, 256), (16384, 256)]:
+        lg = synth.router_logits(M, E, "bench_router", device=dev)
+        bias = synth.router_bias(E, "bench_router", device=dev)
+        rid = torch.empty(M, 8, dtype=torch.int32, device=dev)
+        rw = torch.empty(M, 8, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+        def rt(score_fn, b):
+            bfp8._lib.check(L_.moe_router_topk(P(lg.data_ptr()), M, E, 8, score_fn,
+                                               None if b is None else P(b.data_ptr()), 1, 1.0, P(rid.data_ptr()),
+                                               P(rw.data_ptr()), stream))
+
+        def torch_router():
+            with torch.cuda.stream(ext):
+                for _ in range(20):
+                    v, _i = torch.topk(torch.softmax(lg, -1), 8, -1)
+                    v / v.sum(-1, keepdim=True)
+
+        ts = time_graph(hip, stream, lambda: [rt(bfp8.SCORE_SOFTMAX, None) for _ in range(20)], 20) * 1e3 / 20
+        tg = time_graph(hip, stream, lambda: [rt(bfp8.SCORE_SIGMOID, bias) for _ in range(20)], 20) * 1e3 / 20
+        tt = time_graph(hip, stream, torch_router, 20) * 1e3 / 20
+        out[f"{M}x{E}"] = {"softmax_us": ts, "sigmoid_bias_us": tg, "torch_us": tt}
+        print(f"| {M} | {E} | 8 | {ts:.2f} | {tg:.2f} | {tt:.2f} |", flush=True)
+
+    return out
+
+
+def routed_table(hip, stream, dev):
+    """The decode layers with their router, graph-timed over 8 instances
+    (more weight bytes than the Infinity Cache holds): the router's launch
+    followed by the layer, against the layer with the router folded into its
+    first kernel, and the layer alone on given routing."""
+    import torch
+
+    import block_fp8_mixture_route_amd as bfp8
+    from block_fp8_mixture_route_amd import synth
+
+    L_ = bfp8.lib()
+    P = ctypes.c_void_p
+    print()
+    print("| config | router + layer µs (2 calls) | routed layer µs (router folded) | layer alone µs |")
+    print("|---|---|---|---|")
+    out = {}
+    for M in (1, 2, 3, 4):
+        name = f"decode_m{M}"
+        c = dataclasses.replace(synth.LAYER_CASES["decode_m1"], name=name, M=M)
+        o = bfp8.opts()
+        need = bfp8.fused_moe_workspace_size(c.M, c.H, c.k, c.E, c.I, o)
+        insts = []
+        for i in range(8):
+            lg = synth.router_logits(c.M, c.E, "bench_routed", name, i, device=dev)
+            ids, w = bfp8.router_topk(lg, c.k)
+            mw = synth.moe_weights(c.E, c.H, c.I, "bench_routed", name, i,
+                                   experts=ids.unique().cpu().tolist(), device=dev)
+            hid = synth.hidden_states(c.M, c.H, "bench_routed", name, i, device=dev)
+            insts.append(dict(lg=lg, ids=ids, w=w, mw=mw, hid=hid,
+                              out=torch.empty(c.M, c.H, dtype=torch.bfloat16, device=dev),
+                              ws=torch.empty(max(need, 1), dtype=torch.uint8, device=dev)))
+        torch.cuda.synchronize()
+
+        def layer(x):
+            m = x["mw"]
+            bfp8._lib.check(L_.fused_moe_block_fp8(P(x["hid"].data_ptr()), c.M, c.H, P(x["ids"].data_ptr()),
+                                                   P(x["w"].data_ptr()), c.k, P(m.w13.data_ptr()),
+                                                   P(m.w13_s.data_ptr()), P(m.w2.data_ptr()), P(m.w2_s.data_ptr()),
+                                                   c.E, c.I, ctypes.byref(o), P(x["out"].data_ptr()),
+                                                   P(x["ws"].data_ptr()), x["ws"].numel(), stream))
+
+        def router(x):
+            bfp8._lib.check(L_.moe_router_topk(P(x["lg"].data_ptr()), c.M, c.E, c.k, bfp8.SCORE_SOFTMAX, None, 1,
+                                               1.0, P(x["ids"].data_ptr()), P(x["w"].data_ptr()), stream))
+
+        def routed(x):
+            m = x["mw"]
+            bfp8._lib.check(L_.fused_moe_block_fp8_routed(
+                P(x["hid"].data_ptr()), c.M, c.H, P(x["lg"].data_ptr()), None, bfp8.SCORE_SOFTMAX, 1, 1.0, c.k,
+                P(x["ids"].data_ptr()), P(x["w"].data_ptr()), P(m.w13.data_ptr()), P(m.w13_s.data_ptr()),
+                P(m.w2.data_ptr()), P(m.w2_s.data_ptr()), c.E, c.I, ctypes.byref(o), P(x["out"].data_ptr()),
+                P(x["ws"].data_ptr()), x["ws"].numel(), stream))
+
+        reps = 40
+        t2 = time_graph(hip, stream, lambda: [(router(x), layer(x)) for x in insts * 4], reps) * 1e3 / 32
+        tf = time_graph(hip, stream, lambda: [routed(x) for x in insts * 4], reps) * 1e3 / 32
+        tl = time_graph(hip, stream, lambda: [layer(x) for x in insts * 4], reps) * 1e3 / 32
+        out[name] = {"router_plus_layer_us": t2, "routed_us": tf, "layer_us": tl}
+        print(f"| {name} | {t2:.2f} | {tf:.2f} | {tl:.2f} |", flush=True)
+        del insts
+        torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ suite
 
 SUITE_STEPS = {"tiny": 200, "decode_m1": 480, "decode_m4": 200, "decode_m16": 100, "decode_m32": 100,
@@ -458,36 +566,8 @@ def suite(hip, stream, dev):
         res["route_prep"][R] = {"L": L, "block_m": bm, "single_us": row[0], "multi_us": row[1]}
         print(f"| {R} | {L} | {bm} | {row[0]:.2f} | {row[1]:.2f} |", flush=True)
 
-    # single-group top-k router: softmax (renormalised) and biased sigmoid
-    # (renormalised), each one launch, beside torch's softmax -> topk ->
-    # renormalise for context
-    print()
-    print("| tokens M | experts E | k | softmax µs | sigmoid + bias µs | torch softmax/topk/renorm µs |")
-    print("|---|---|---|---|---|---|")
-    res["router"] = {}
-    for (M, E) in [(1, 256), (16, 256), (256, 256), (2048, 512), (4096, 256), (16384, 256)]:
-        lg = synth.router_logits(M, E, "bench_router", device=dev)
-        bias = synth.router_bias(E, "bench_router", device=dev)
-        rid = torch.empty(M, 8, dtype=torch.int32, device=dev)
-        rw = torch.empty(M, 8, dtype=torch.float32, device=dev)
-        torch.cuda.synchronize()
-
-        def rt(score_fn, b):
-            bfp8._lib.check(L_.moe_router_topk(P(lg.data_ptr()), M, E, 8, score_fn,
-                                               None if b is None else P(b.data_ptr()), 1, 1.0, P(rid.data_ptr()),
-                                               P(rw.data_ptr()), stream))
-
-        def torch_router():
-            with torch.cuda.stream(ext):
-                for _ in range(20):
-                    v, _i = torch.topk(torch.softmax(lg, -1), 8, -1)
-                    v / v.sum(-1, keepdim=True)
-
-        ts = time_graph(hip, stream, lambda: [rt(bfp8.SCORE_SOFTMAX, None) for _ in range(20)], 20) * 1e3 / 20
-        tg = time_graph(hip, stream, lambda: [rt(bfp8.SCORE_SIGMOID, bias) for _ in range(20)], 20) * 1e3 / 20
-        tt = time_graph(hip, stream, torch_router, 20) * 1e3 / 20
-        res["router"][f"{M}x{E}"] = {"softmax_us": ts, "sigmoid_bias_us": tg, "torch_us": tt}
-        print(f"| {M} | {E} | 8 | {ts:.2f} | {tg:.2f} | {tt:.2f} |", flush=True)
+    res["router"] = router_table(hip, stream, dev)
+    res["routed"] = routed_table(hip, stream, dev)
 
     # a plain device copy of the decode layer's size, rotating over buffers
     # that together exceed the Infinity Cache: the practical HBM ceiling
@@ -530,6 +610,7 @@ def main():
                     help="force one implementation of the layer (default: the library's choice by shape)")
     ap.add_argument("--block-m", type=int, default=0, help="routes per compact block of the general path (0 = auto)")
     ap.add_argument("--floor", action="store_true", help="only the graph launch floor of one kernel")
+    ap.add_argument("--router", action="store_true", help="only the router timing table")
     ap.add_argument("--suite", metavar="JSON", default=None,
                     help="instead of the metric line: every layer config, activation+quant, route preparation "
                          "and a plain copy, as markdown tables on stdout and figures in JSON")
@@ -551,6 +632,10 @@ def main():
 
     if args.floor:
         launch_floor(hip, stream, dev)
+        return
+    if args.router:
+        router_table(hip, stream, dev)
+        routed_table(hip, stream, dev)
         return
     if args.suite:
         res = suite(hip, stream, dev)
@@ -615,7 +700,8 @@ def main():
 
 KERNEL_SOURCES = {
     "token_gate_up_swiglu": ["block_fp8_mixture_route_amd/csrc/token.hip",
-                             "block_fp8_mixture_route_amd/csrc/device.h"],
+                             "block_fp8_mixture_route_amd/csrc/device.h",
+                             "block_fp8_mixture_route_amd/csrc/router.h"],
 }
 
 

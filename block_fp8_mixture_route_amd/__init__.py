@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     SCORE_SOFTMAX,
     Opts,
     fused_moe_block_fp8,
+    fused_moe_block_fp8_routed,
     fused_moe_stages,
     fused_moe_workspace_size,
     lib,

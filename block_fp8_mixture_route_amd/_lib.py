@@ -75,6 +75,8 @@ SIGNATURES = {
                                           ctypes.POINTER(ctypes.c_char_p), _i32]),
     "fused_moe_block_fp8": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32,
                                            ctypes.POINTER(Opts), _P, _P, _sz, _P]),
+    "fused_moe_block_fp8_routed": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _i32, ctypes.c_double, _i32, _P, _P,
+                                                  _P, _P, _P, _P, _i32, _i32, ctypes.POINTER(Opts), _P, _P, _sz, _P]),
 }
 
 _lib = None
@@ -262,3 +264,26 @@ def fused_moe_block_fp8(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, 
                                     ptr(w13_scale), ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o),
                                     ptr(_u16(out)), ptr(ws), ws.numel(), stream_of(hidden.device)))
     return out
+
+
+def fused_moe_block_fp8_routed(hidden, router_logits, k, w13, w13_scale, w2, w2_scale, score_fn=SCORE_SOFTMAX,
+                               bias=None, renormalize=True, scale=1.0, o: Opts = None, out=None, ws=None,
+                               topk_ids=None, topk_w=None):
+    """Router and layer in one call: returns (out [M, H] BF16, topk_ids [M, k]
+    int32, topk_w [M, k] fp32)."""
+    _require_device(hidden, router_logits, bias, w13, w13_scale, w2, w2_scale, topk_ids, topk_w)
+    M, H = hidden.shape
+    E = router_logits.shape[1]
+    I = w2.shape[2]
+    o = opts() if o is None else o
+    need = fused_moe_workspace_size(M, H, k, E, I, o)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    out = torch.empty(M, H, dtype=torch.bfloat16, device=hidden.device) if out is None else out
+    ids = torch.empty(M, k, dtype=torch.int32, device=hidden.device) if topk_ids is None else topk_ids
+    w = torch.empty(M, k, dtype=torch.float32, device=hidden.device) if topk_w is None else topk_w
+    check(lib().fused_moe_block_fp8_routed(ptr(_u16(hidden)), M, H, ptr(router_logits), ptr(bias), score_fn,
+                                           int(bool(renormalize)), float(scale), k, ptr(ids), ptr(w), ptr(w13),
+                                           ptr(w13_scale), ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o),
+                                           ptr(_u16(out)), ptr(ws), ws.numel(), stream_of(hidden.device)))
+    return out, ids, w

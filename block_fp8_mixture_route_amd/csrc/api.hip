@@ -478,4 +478,53 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   return hip_status(e, "fused_moe_block_fp8: moe_reduce");
 }
 
+bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, int32_t H, const float* router_logits,
+                                            const float* router_bias, int32_t score_fn, int32_t renormalize,
+                                            double routed_scale, int32_t k, int32_t* topk_ids, float* topk_w,
+                                            const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                            const float* w2_scale, int32_t E, int32_t I, const bfp8moe_opts_t* opts,
+                                            uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  bfp8moe_opts_t o;
+  bfp8moe_opts_init(&o);
+  if (opts) o = *opts;
+  REQUIRE(E >= 1 && E <= 1024, "E=%d must be in [1, 1024]", E);
+  REQUIRE(k >= 1 && k <= 64 && k <= E, "k=%d must be in [1, min(E, 64)]", k);
+  REQUIRE(score_fn == BFP8MOE_SCORE_SOFTMAX || score_fn == BFP8MOE_SCORE_SIGMOID, "score_fn=%d invalid", score_fn);
+  REQUIRE(router_bias == nullptr || score_fn == BFP8MOE_SCORE_SIGMOID, "a selection bias needs sigmoid scoring");
+  REQUIRE(isfinite(routed_scale), "routed_scale must be finite");
+  REQUIRE(o.stage_events == nullptr && ((o.flags >> BFP8MOE_FLAG_STAGE_SHIFT) & 15u) == 0,
+          "the routed layer takes no stage events or stage selection");
+  {
+    const bfp8moe_status_t st = check_layer_shape(M, H, k, E, I, o);
+    if (st != BFP8MOE_OK) return st;
+  }
+  REQUIRE(M == 0 || (router_logits && topk_ids && topk_w), "router_logits, topk_ids and topk_w must be non-null");
+  if (M == 0) return BFP8MOE_OK;
+  // every check of both steps before anything is enqueued
+  REQUIRE(hidden && w13 && w13_scale && w2 && w2_scale && out, "all pointers must be non-null");
+  REQUIRE(aligned16(hidden) && aligned16(w13) && aligned16(w2) && aligned16(out),
+          "hidden, w13, w2 and out must be 16-byte aligned");
+  LayerPlan p;
+  plan_layer(p, M, H, k, E, I, o);
+  if (ws == nullptr || ws_bytes < p.total)
+    return fail(BFP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
+  REQUIRE((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) == 0, "workspace must be 256-byte aligned");
+  if (p.mode == kModeToken && E <= bfp8::kFoldedRouterMaxE && M <= bfp8::kFoldedRouterMaxM) {
+    uint16_t* act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.off_act);
+    const bfp8::RouterArgs ra{router_logits, router_bias, topk_ids, topk_w, routed_scale, E, score_fn,
+                              renormalize != 0};
+    return hip_status(bfp8::launch_token_layer(hidden, M, H, topk_ids, topk_w, k, p.offset, p.L, w13, w13_scale, w2,
+                                               w2_scale, I, p.fmt, p.clamp, act, out, (hipStream_t)stream, nullptr,
+                                               &ra),
+                      "fused_moe_block_fp8_routed (few tokens)");
+  }
+  // other paths: the router's own launch, then the layer
+  const bfp8moe_status_t rs =
+      moe_router_topk(router_logits, M, E, k, score_fn, router_bias, renormalize, routed_scale, topk_ids, topk_w,
+                      stream);
+  if (rs != BFP8MOE_OK) return rs;
+  return fused_moe_block_fp8(hidden, M, H, topk_ids, topk_w, k, w13, w13_scale, w2, w2_scale, E, I, &o, out, ws,
+                             ws_bytes, stream);
+}
+
 }  // extern "C"

@@ -1,0 +1,164 @@
+// router.h -- wave-level pieces of the single-group top-k router, shared by
+// the router kernel and the few-token layer kernel that routes for itself.
+//
+// [P2 Changes: a fused single-group top-k router; renormalize option]
+//   [P2] lmdeploy PR "perf(pytorch): optimize compact blocked FP8 MoE and route
+//        preparation"
+//
+// One wave routes one token.  Lane l holds experts l, l + 64, ... (NPL of
+// them).  Each expert's score becomes an order-preserving unsigned integer
+// (-0 taken as +0).  Each round takes the wave's largest key (DPP-fused maxima
+// within 16-lane rows, row broadcasts across them, one readlane); a ballot per
+// slot finds the lowest expert id holding it, whose lane retires it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace bfp8 {
+namespace router {
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t r = (uint64_t)dpp_u32<CTRL>(0u, (uint32_t)u) | ((uint64_t)dpp_u32<CTRL>(0u, (uint32_t)(u >> 32)) << 32);
+  return __builtin_bit_cast(double, r);
+}
+
+// Largest value of the wave, wave-uniform.  Every lane must be active.  The
+// row maximum by DPP (quad swaps, half-row and row mirrors: every lane of a
+// row ends with it), then the row broadcasts carry rows 0-2 into row 3, whose
+// lane 63 is read.  Rows a broadcast does not write keep their own value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(0u, v));   // quad_perm 1,0,3,2
+  v = max(v, dpp_u32<0x4E>(0u, v));   // quad_perm 2,3,0,1
+  v = max(v, dpp_u32<0x141>(0u, v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(0u, v));  // row_mirror
+  v = max(v, dpp_u32<0x142, 0xA>(v, v));  // row_bcast15: row 0 -> 1, row 2 -> 3
+  v = max(v, dpp_u32<0x143, 0xC>(v, v));  // row_bcast31: row 1 -> 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Sum of the wave's fp64 values, wave-uniform (fixed tree: deterministic).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  double r[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 16 * q);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 16 * q);
+    r[q] = __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+  }
+  return (r[0] + r[1]) + (r[2] + r[3]);
+}
+
+// fp32 bits -> unsigned integer with the same order as the floats; -0 is
+// mapped like +0 so that the two compare equal, as floats do.  Live keys are
+// at least 1 (only a NaN could map lower), so 0 marks a retired or absent
+// expert.
+__device__ __forceinline__ uint32_t order_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return max((u & 0x80000000u) ? ~u : (u | 0x80000000u), 1u);
+}
+
+__device__ __forceinline__ float sigmoid_rn(float x) { return (float)(1.0 / (1.0 + exp(-(double)x))); }
+
+// A token's logits and keys, loaded by one wave.  Loads are unconditional
+// (indexes clamped into the row); absent experts get key 0.
+template <int NPL>
+struct WaveRoute {
+  float v[NPL];
+  uint32_t key[NPL];
+
+  __device__ __forceinline__ void load(const float* lg, int E, int score_fn, const float* bias, int lane) {
+    float b[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; i++) v[i] = lg[min(lane + 64 * i, E - 1)];
+    if (score_fn == kScoreSigmoid && bias) {
+#pragma unroll
+      for (int i = 0; i < NPL; i++) b[i] = bias[min(lane + 64 * i, E - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; i++) {
+      float s = v[i];
+      if (score_fn == kScoreSigmoid) {
+        s = sigmoid_rn(v[i]);
+        if (bias) s = s + b[i];
+      }
+      key[i] = lane + 64 * i < E ? order_bits(s) : 0u;
+    }
+  }
+
+  // One round: the largest remaining key (lowest expert id among equals) is
+  // retired; returns its expert id and logit, wave-uniform.  Needs a live key.
+  __device__ __forceinline__ int take(int lane, float& logit) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < NPL; i++) best = max(best, key[i]);
+    const uint32_t top = wave_max_u32(best);
+    // expert ids grow with the slot, then the lane: the first slot holding
+    // the top key, and its lowest lane
+    int slot = NPL - 1;
+    uint64_t hit = 0;
+#pragma unroll
+    for (int i = NPL - 1; i >= 0; i--) {
+      const uint64_t m = __ballot(key[i] == top);
+      if (m) {
+        slot = i;
+        hit = m;
+      }
+    }
+    const int wl = (int)__builtin_ctzll(hit);
+    float lv = v[0];
+#pragma unroll
+    for (int i = 0; i < NPL; i++) {
+      if (i == slot) {
+        lv = v[i];
+        if (lane == wl) key[i] = 0u;  // retired
+      }
+    }
+    logit = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), wl));
+    return wl + 64 * slot;
+  }
+
+  // Weight of the expert lane j < k chose (my_logit), fp64 rounded once to
+  // fp32; lanes j >= k get 0.  All 64 lanes must call it.
+  __device__ __forceinline__ float weight(float my_logit, int lane, int E, int k, int score_fn, int renorm,
+                                          double scale) const {
+    const bool chosen = lane < k;
+    double num = 0.0, z = 1.0;
+    if (score_fn == kScoreSoftmax) {
+      const double m =
+          (double)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_logit), 0));
+      num = chosen ? exp((double)my_logit - m) : 0.0;
+      if (renorm) {
+        z = wave_sum_f64(num);
+      } else {
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < NPL; i++)
+          if (lane + 64 * i < E) part += exp((double)v[i] - m);
+        z = wave_sum_f64(part);
+      }
+    } else {
+      num = chosen ? 1.0 / (1.0 + exp(-(double)my_logit)) : 0.0;
+      z = renorm ? wave_sum_f64(num) : 1.0;
+    }
+    return (float)(num / z * scale);
+  }
+};
+
+}  // namespace router
+}  // namespace bfp8

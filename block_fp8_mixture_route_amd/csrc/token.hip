@@ -45,6 +45,7 @@
 //   [P4] lmdeploy PR "Moe Reduce kernel"
 #include "device.h"
 #include "internal.h"
+#include "router.h"
 
 namespace bfp8 {
 
@@ -177,11 +178,11 @@ __device__ __forceinline__ int local_expert(int32_t id, int32_t offset, int32_t 
 // barrier would also wait for every column wave to have issued its loads,
 // which the compute unit's memory queue holds back for microseconds, and no
 // wave could start its dot products before then.
-template <int RL, int I>
+template <int RL, int I, bool kRoute>
 __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
     const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, int k, int32_t offset, int32_t L,
     const uint8_t* __restrict__ w13, const float* __restrict__ w13_s, int fmt, float limit, int clamp,
-    uint16_t* __restrict__ act) {
+    uint16_t* __restrict__ act, RouterArgs ra) {
   constexpr int kSlices = I / 8;
   __shared__ __align__(16) h2 s_ah[kMaxH / 2];  // quantised hidden row (E4M3 values as FP16)
   __shared__ float s_as[kMaxH / 128];           // its group scales
@@ -194,7 +195,39 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   const int j = blockIdx.x / kSlices;
   const int n0 = (blockIdx.x - j * kSlices) * 8;
   if (tid == 0) s_ready = 0;
-  const int e = local_expert(ids[j], offset, L);
+  int id_j;
+  if constexpr (kRoute) {
+    // the router folded in: every wave ranks the token's logits the same way
+    // and stops at this route's rank; wave 0 of the token's first workgroup
+    // ranks all k and writes the routing for the down kernel
+    const int tok = j / k, rank = j - tok * k;
+    const bool writer = rank == 0 && n0 == 0 && wave == 0;
+    router::WaveRoute<kFoldedRouterMaxE / 64> r;
+    r.load(ra.logits + (size_t)tok * ra.E, ra.E, ra.score_fn, ra.bias, lane);
+    const int rounds = writer ? k : rank + 1;
+    int my_id = 0;
+    float my_logit = 0.0f;
+    id_j = 0;
+    for (int q = 0; q < rounds; q++) {
+      float lv;
+      const int ex = r.take(lane, lv);
+      if (q == rank) id_j = ex;
+      if (lane == q) {
+        my_id = ex;
+        my_logit = lv;
+      }
+    }
+    if (writer) {
+      const float wt = r.weight(my_logit, lane, ra.E, k, ra.score_fn, ra.renorm, ra.scale);
+      if (lane < k) {
+        ra.ids[(size_t)tok * k + lane] = my_id;
+        ra.w[(size_t)tok * k + lane] = wt;
+      }
+    }
+  } else {
+    id_j = ids[j];
+  }
+  const int e = local_expert(id_j, offset, L);
   if (e < 0) return;  // route outside the local slice: it contributes nothing
 
   // the small operands, loaded by every wave (the column waves' copies go
@@ -446,8 +479,15 @@ bool token_path_fits(int64_t M, int H, int k, int I) {
 hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
                               int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
                               const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
-                              uint16_t* out, hipStream_t stream, const LaunchHook* hook) {
+                              uint16_t* out, hipStream_t stream, const LaunchHook* hook,
+                              const RouterArgs* route) {
   if (!token_path_fits(M, H, k, I)) return hipErrorInvalidValue;  // the caller checks token_path_fits
+  if (route && (route->E < 1 || route->E > kFoldedRouterMaxE || k > route->E)) return hipErrorInvalidValue;
+  const RouterArgs ra = route ? *route : RouterArgs{};
+  if (route) {
+    ids = route->ids;  // written by the gate/up kernel, read by the down kernel
+    topk_w = route->w;
+  }
   const int clamp = __builtin_isfinite(limit) ? 1 : 0;
   const int rl = (H + 1023) / 1024;
   const int dr = token_down_rows(H, I, k);
@@ -461,8 +501,12 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
   const bool run0 = !hook || hook->run(0), run1 = !hook || hook->run(1);
 #define BFP8_TOKEN_CASE(N, II)                                                                                  \
   case N:                                                                                                       \
-    hipLaunchKernelGGL((token_gate_up_kernel<N, II>), dim3(up_grid), dim3(kUpThreads), 0, stream, hidden, H,    \
-                       ids, k, offset, L, w13, w13_s, fmt, limit, clamp, act);                                  \
+    if (route)                                                                                                  \
+      hipLaunchKernelGGL((token_gate_up_kernel<N, II, true>), dim3(up_grid), dim3(kUpThreads), 0, stream,       \
+                         hidden, H, ids, k, offset, L, w13, w13_s, fmt, limit, clamp, act, ra);                 \
+    else                                                                                                        \
+      hipLaunchKernelGGL((token_gate_up_kernel<N, II, false>), dim3(up_grid), dim3(kUpThreads), 0, stream,      \
+                         hidden, H, ids, k, offset, L, w13, w13_s, fmt, limit, clamp, act, ra);                 \
     break;
 #define BFP8_TOKEN_RL(II)   \
   switch (rl) {             \

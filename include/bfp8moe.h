@@ -314,6 +314,23 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
                                      const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
                                      void* stream);
 
+/* The layer with its router: moe_router_topk on router_logits [M, E] fp32
+ * (score_fn, router_bias, renormalize, routed_scale as there), writing the
+ * routing to topk_ids [M, k] / topk_w [M, k] (caller-owned outputs), then
+ * fused_moe_block_fp8 on it; same results as the two calls in a row.
+ * [P2 Changes: the fused single-group top-k router feeds the MoE layer]
+ * On the few-token path with E <= 256 the router is folded into the layer's
+ * first kernel (one launch fewer): each gate/up workgroup ranks its token's
+ * logits itself.  Elsewhere the router runs as its own launch first.  Takes
+ * the workspace of fused_moe_block_fp8_workspace_size for the same sizes and
+ * options; opts must not set stage events or a stage selection. */
+bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, int32_t H, const float* router_logits,
+                                            const float* router_bias, int32_t score_fn, int32_t renormalize,
+                                            double routed_scale, int32_t k, int32_t* topk_ids, float* topk_w,
+                                            const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                            const float* w2_scale, int32_t E, int32_t I, const bfp8moe_opts_t* opts,
+                                            uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

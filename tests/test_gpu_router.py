@@ -91,3 +91,34 @@ def test_router_zero_tokens_and_layer_feed():
     ref = O.fused_moe(hidden, rid, rw, mw.w13, mw.w13_s, mw.w2, mw.w2_s)
     from tests.gpu_util import bf16_np, normwise_err, LAYER_TOL
     assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+
+
+# routed layer: (M, E, k, H, I, score_fn) -- the decode shape with the router
+# folded into the few-token kernel (softmax and biased sigmoid), a small
+# few-token case, and two that take the router's own launch (more than 256
+# experts; more tokens than the few-token path takes by default)
+ROUTED = [(1, 256, 8, 7168, 256, bfp8.SCORE_SOFTMAX), (4, 256, 8, 7168, 256, bfp8.SCORE_SIGMOID),
+          (3, 16, 4, 256, 128, bfp8.SCORE_SOFTMAX), (2, 512, 8, 1024, 256, bfp8.SCORE_SIGMOID),
+          (16, 256, 8, 1024, 256, bfp8.SCORE_SOFTMAX)]
+
+
+@pytest.mark.parametrize("M,E,k,H,I,score_fn", ROUTED)
+def test_routed_layer(M, E, k, H, I, score_fn):
+    print_case("routed layer", M, E, k, H, I, score_fn)
+    from tests.gpu_util import LAYER_TOL, bf16_np, normwise_err
+    lg = synth.router_logits(M, E, "routed", bf16_valued=True, std=2.0)
+    bias = synth.router_bias(E, "routed", std=0.1) if score_fn == bfp8.SCORE_SIGMOID else None
+    scale = 2.5 if score_fn == bfp8.SCORE_SIGMOID else 1.0
+    rid, rw = O.router_topk(lg, k, score_fn, bias, True, scale)
+    mw = synth.moe_weights(E, H, I, "routed", M, experts=np.unique(rid).tolist(), device=dev())
+    hidden = synth.hidden_states(M, H, "routed", M).to(dev())
+    out, ids, w = bfp8.fused_moe_block_fp8_routed(hidden, lg.to(dev()), k, mw.w13, mw.w13_s, mw.w2, mw.w2_s,
+                                                  score_fn, None if bias is None else bias.to(dev()), True, scale)
+    # the same layer from the router's routing, in two calls
+    out2 = bfp8.fused_moe_block_fp8(hidden, ids.clone(), w.clone(), mw.w13, mw.w13_s, mw.w2, mw.w2_s, E=E)
+    torch.cuda.synchronize()
+    assert (ids.cpu().numpy() == rid).all()
+    assert ulps(w.cpu().numpy(), rw).max() <= 1.0
+    assert (bf16_np(out) == bf16_np(out2)).all()
+    ref = O.fused_moe(hidden, rid, rw, mw.w13, mw.w13_s, mw.w2, mw.w2_s)
+    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
