@@ -359,7 +359,7 @@ def routed_table(hip, stream, dev):
     print("| config | router + layer µs (2 calls) | routed layer µs (router folded) | layer alone µs |")
     print("|---|---|---|---|")
     out = {}
-    for M in (1, 2, 3, 4):
+    for M in (1, 2, 4, 8):
         name = f"decode_m{M}"
         c = dataclasses.replace(synth.LAYER_CASES["decode_m1"], name=name, M=M)
         o = bfp8.opts()

@@ -63,11 +63,13 @@ struct RouterArgs {
 };
 // Largest expert count the folded router handles (four experts per lane).
 constexpr int kFoldedRouterMaxE = 256;
-// Most tokens for which the layer folds the router in: every gate/up wave
-// ranks its token, so the ranking work grows with the token count (measured
-// at the 7168 x 256 decode shape: the fold saves 1.9 us at 1 token and 0.4 us
-// at 2, and loses 1.6 us at 3 and 2.0 us at 4).
-constexpr int64_t kFoldedRouterMaxM = 2;
+// Most tokens for which the layer folds the router in: one wave of every
+// gate/up workgroup ranks its token before the weight loads, and that delay
+// grows with the ranks to walk (measured at the 7168 x 256 decode shape:
+// folded against the router's launch then the layer, 15.3 against 17.7 us at
+// 1 token, 42.4 against 44.0 at 4, 74.4 against 73.9 at 8, 104.2 against
+// 100.9 at 12).
+constexpr int64_t kFoldedRouterMaxM = 4;
 
 hipError_t launch_router_topk(const float* logits, int64_t M, int E, int k, int score_fn, const float* bias,
                               int renorm, double scale, int32_t* ids, float* w, hipStream_t stream);

@@ -7,9 +7,10 @@
 //
 // One wave routes one token.  Lane l holds experts l, l + 64, ... (NPL of
 // them).  Each expert's score becomes an order-preserving unsigned integer
-// (-0 taken as +0).  Each round takes the wave's largest key (DPP-fused maxima
-// within 16-lane rows, row broadcasts across them, one readlane); a ballot per
-// slot finds the lowest expert id holding it, whose lane retires it.
+// (-0 taken as +0); each lane sorts its keys once.  Each round takes the
+// largest of the lanes' heads (DPP-fused maxima within 16-lane rows, row
+// broadcasts across them, one readlane); a ballot finds the lane holding it
+// (a minimum over expert ids settles equal heads), and that lane pops it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -46,6 +47,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Smallest value of the wave, wave-uniform; as wave_max_u32.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0xB1>(0u, v));
+  v = min(v, dpp_u32<0x4E>(0u, v));
+  v = min(v, dpp_u32<0x141>(0u, v));
+  v = min(v, dpp_u32<0x140>(0u, v));
+  v = min(v, dpp_u32<0x142, 0xA>(v, v));
+  v = min(v, dpp_u32<0x143, 0xC>(v, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Sum of the wave's fp64 values, wave-uniform (fixed tree: deterministic).
 __device__ __forceinline__ double wave_sum_f64(double v) {
   v += dpp_f64<0xB1>(v);
@@ -79,8 +91,10 @@ __device__ __forceinline__ float sigmoid_rn(float x) { return (float)(1.0 / (1.0
 // (indexes clamped into the row); absent experts get key 0.
 template <int NPL>
 struct WaveRoute {
-  float v[NPL];
-  uint32_t key[NPL];
+  float v[NPL];       // logits in expert order (lane + 64 i)
+  uint32_t key[NPL];  // the lane's keys, sorted largest first; key[0] is its head
+  int id[NPL];        // expert id of each sorted key
+  float sv[NPL];      // logit of each sorted key
 
   __device__ __forceinline__ void load(const float* lg, int E, int score_fn, const float* bias, int lane) {
     float b[NPL];
@@ -98,39 +112,57 @@ struct WaveRoute {
         if (bias) s = s + b[i];
       }
       key[i] = lane + 64 * i < E ? order_bits(s) : 0u;
+      id[i] = lane + 64 * i;
+      sv[i] = v[i];
+    }
+    // odd-even transposition sort, largest first; a swap only on a strictly
+    // smaller key keeps equal keys in ascending id order
+#pragma unroll
+    for (int r = 0; r < NPL; r++) {
+#pragma unroll
+      for (int i = r & 1; i + 1 < NPL; i += 2) {
+        if (key[i] < key[i + 1]) {
+          const uint32_t tk = key[i];
+          key[i] = key[i + 1];
+          key[i + 1] = tk;
+          const int ti = id[i];
+          id[i] = id[i + 1];
+          id[i + 1] = ti;
+          const float tv = sv[i];
+          sv[i] = sv[i + 1];
+          sv[i + 1] = tv;
+        }
+      }
     }
   }
 
   // One round: the largest remaining key (lowest expert id among equals) is
   // retired; returns its expert id and logit, wave-uniform.  Needs a live key.
+  // Each lane's head is its largest key and, among its equal keys, the lowest
+  // id, so the winner is the head equal to the wave maximum with the lowest
+  // id: one lane in the usual case, a second reduction when heads tie.
   __device__ __forceinline__ int take(int lane, float& logit) {
-    uint32_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < NPL; i++) best = max(best, key[i]);
-    const uint32_t top = wave_max_u32(best);
-    // expert ids grow with the slot, then the lane: the first slot holding
-    // the top key, and its lowest lane
-    int slot = NPL - 1;
-    uint64_t hit = 0;
-#pragma unroll
-    for (int i = NPL - 1; i >= 0; i--) {
-      const uint64_t m = __ballot(key[i] == top);
-      if (m) {
-        slot = i;
-        hit = m;
-      }
+    const uint32_t top = wave_max_u32(key[0]);
+    const uint64_t hit = __ballot(key[0] == top);
+    int wl;
+    if (__popcll(hit) == 1) {
+      wl = (int)__builtin_ctzll(hit);
+    } else {
+      const uint32_t lowest = wave_min_u32(key[0] == top ? (uint32_t)id[0] : 0xFFFFFFFFu);
+      wl = (int)(lowest & 63u);  // expert l + 64 i lives in lane l
     }
-    const int wl = (int)__builtin_ctzll(hit);
-    float lv = v[0];
+    const int e = __builtin_amdgcn_readlane(id[0], wl);
+    logit = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[0]), wl));
+    if (lane == wl) {  // pop the head
 #pragma unroll
-    for (int i = 0; i < NPL; i++) {
-      if (i == slot) {
-        lv = v[i];
-        if (lane == wl) key[i] = 0u;  // retired
+      for (int i = 0; i + 1 < NPL; i++) {
+        key[i] = key[i + 1];
+        id[i] = id[i + 1];
+        sv[i] = sv[i + 1];
       }
+      key[NPL - 1] = 0u;
     }
-    logit = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), wl));
-    return wl + 64 * slot;
+    return e;
   }
 
   // Weight of the expert lane j < k chose (my_logit), fp64 rounded once to

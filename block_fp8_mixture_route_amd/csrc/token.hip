@@ -196,39 +196,56 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   const int n0 = (blockIdx.x - j * kSlices) * 8;
   if (tid == 0) s_ready = 0;
   int id_j;
+  // the router folded in: wave 0 ranks the token's logits up to this route's
+  // rank and hands the expert to the other waves through LDS (no weight load
+  // is in flight yet, so the barrier costs only the ranking); in the token's
+  // first workgroup wave 8, a hidden-row wave, later ranks all k on its own,
+  // forms the weights and writes the routing for the down kernel
+  const int tok = j / k, rank = j - tok * k;
+  const bool writer = kRoute && rank == 0 && n0 == 0 && wave == 8;
   if constexpr (kRoute) {
-    // the router folded in: every wave ranks the token's logits the same way
-    // and stops at this route's rank; wave 0 of the token's first workgroup
-    // ranks all k and writes the routing for the down kernel
-    const int tok = j / k, rank = j - tok * k;
-    const bool writer = rank == 0 && n0 == 0 && wave == 0;
+    __shared__ int s_route;
+    if (wave == 0) {
+      router::WaveRoute<kFoldedRouterMaxE / 64> r;
+      r.load(ra.logits + (size_t)tok * ra.E, ra.E, ra.score_fn, ra.bias, lane);
+      int ex = 0;
+      for (int q = 0; q <= rank; q++) {
+        float lv;
+        ex = r.take(lane, lv);
+      }
+      if (lane == 0) s_route = ex;
+    }
+    wg_sync();
+    id_j = s_route;
+  } else {
+    id_j = ids[j];
+  }
+  // the writer's work, done once its hidden-row duties are over (or at once
+  // when the route is not local): off the column waves' path
+  auto write_routing = [&]() {
     router::WaveRoute<kFoldedRouterMaxE / 64> r;
     r.load(ra.logits + (size_t)tok * ra.E, ra.E, ra.score_fn, ra.bias, lane);
-    const int rounds = writer ? k : rank + 1;
     int my_id = 0;
     float my_logit = 0.0f;
-    id_j = 0;
-    for (int q = 0; q < rounds; q++) {
+    for (int q = 0; q < k; q++) {
       float lv;
       const int ex = r.take(lane, lv);
-      if (q == rank) id_j = ex;
       if (lane == q) {
         my_id = ex;
         my_logit = lv;
       }
     }
-    if (writer) {
-      const float wt = r.weight(my_logit, lane, ra.E, k, ra.score_fn, ra.renorm, ra.scale);
-      if (lane < k) {
-        ra.ids[(size_t)tok * k + lane] = my_id;
-        ra.w[(size_t)tok * k + lane] = wt;
-      }
+    const float wt = r.weight(my_logit, lane, ra.E, k, ra.score_fn, ra.renorm, ra.scale);
+    if (lane < k) {
+      ra.ids[(size_t)tok * k + lane] = my_id;
+      ra.w[(size_t)tok * k + lane] = wt;
     }
-  } else {
-    id_j = ids[j];
-  }
+  };
   const int e = local_expert(id_j, offset, L);
-  if (e < 0) return;  // route outside the local slice: it contributes nothing
+  if (e < 0) {  // route outside the local slice: it contributes nothing
+    if (writer) write_routing();
+    return;
+  }
 
   // the small operands, loaded by every wave (the column waves' copies go
   // unused) so that the loads are unconditional: hidden groups t/16 and
@@ -275,6 +292,7 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
     s_tab[te] = tab;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS stores are done
     if (lane == 0) __hip_atomic_fetch_add(&s_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (writer) write_routing();
     return;
   }
 

@@ -319,9 +319,10 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
  * routing to topk_ids [M, k] / topk_w [M, k] (caller-owned outputs), then
  * fused_moe_block_fp8 on it; same results as the two calls in a row.
  * [P2 Changes: the fused single-group top-k router feeds the MoE layer]
- * On the few-token path with E <= 256 the router is folded into the layer's
- * first kernel (one launch fewer): each gate/up workgroup ranks its token's
- * logits itself.  Elsewhere the router runs as its own launch first.  Takes
+ * On the few-token path with E <= 256 and at most 4 tokens the router is
+ * folded into the layer's first kernel (one launch fewer): each gate/up
+ * workgroup ranks its token's logits itself.  Elsewhere the router runs as its
+ * own launch first.  Takes
  * the workspace of fused_moe_block_fp8_workspace_size for the same sizes and
  * options; opts must not set stage events or a stage selection. */
 bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, int32_t H, const float* router_logits,

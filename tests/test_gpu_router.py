@@ -98,7 +98,7 @@ def test_router_zero_tokens_and_layer_feed():
 # few-token case, and two that take the router's own launch (more than 256
 # experts; more tokens than the few-token path takes by default)
 ROUTED = [(1, 256, 8, 7168, 256, bfp8.SCORE_SOFTMAX), (4, 256, 8, 7168, 256, bfp8.SCORE_SIGMOID),
-          (3, 16, 4, 256, 128, bfp8.SCORE_SOFTMAX), (2, 512, 8, 1024, 256, bfp8.SCORE_SIGMOID),
+          (3, 16, 4, 256, 128, bfp8.SCORE_SOFTMAX), (12, 256, 8, 2048, 256, bfp8.SCORE_SOFTMAX), (2, 512, 8, 1024, 256, bfp8.SCORE_SIGMOID),
           (16, 256, 8, 1024, 256, bfp8.SCORE_SOFTMAX)]
 
 
