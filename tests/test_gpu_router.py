@@ -122,3 +122,31 @@ def test_routed_layer(M, E, k, H, I, score_fn):
     assert (bf16_np(out) == bf16_np(out2)).all()
     ref = O.fused_moe(hidden, rid, rw, mw.w13, mw.w13_s, mw.w2, mw.w2_s)
     assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("M", [3, 6])
+def test_routed_layer_expert_slice_and_options(M):
+    # 64 experts of which [16, 40) are local, UE8M0 scales, clamp 7: the
+    # folded path (3 tokens) and the router's own launch (6 tokens) give the
+    # two-call result bit for bit, and the oracle's to the layer tolerance
+    print_case("routed layer slice", M)
+    from tests.gpu_util import LAYER_TOL, bf16_np, normwise_err
+    E, k, H, I, off, L = 64, 8, 1024, 256, 16, 24
+    lg = synth.router_logits(M, E, "routed_slice", std=2.0)
+    lg[1, off:off + L] -= 20.0  # token 1 has no local route: its output row is zero
+    W = synth.moe_weights(L, H, I, "routed_slice", device=dev())
+    hidden = (synth.hidden_states(M, H, "routed_slice").float() * 4).to(torch.bfloat16).to(dev())
+    o = bfp8.opts(scale_fmt=bfp8.SCALE_UE8M0, clamp_limit=7.0, expert_offset=off, local_num_experts=L)
+    out, ids, w = bfp8.fused_moe_block_fp8_routed(hidden, lg.to(dev()), k, W.w13, W.w13_s, W.w2, W.w2_s, o=o)
+    ids2, w2 = bfp8.router_topk(lg.to(dev()), k)
+    out2 = bfp8.fused_moe_block_fp8(hidden, ids2, w2, W.w13, W.w13_s, W.w2, W.w2_s, E=E, o=o)
+    torch.cuda.synchronize()
+    rid, rw = O.router_topk(lg, k)
+    assert (ids.cpu().numpy() == rid).all() and ulps(w.cpu().numpy(), rw).max() <= 1.0
+    assert (bf16_np(out) == bf16_np(out2)).all()
+    local = ((rid >= off) & (rid < off + L)).any(axis=1)
+    assert local.any() and not local[1]
+    assert (bf16_np(out)[1] == 0).all()
+    ref = O.fused_moe(hidden, rid, rw, W.w13, W.w13_s, W.w2, W.w2_s, expert_offset=off, L=L,
+                      scale_fmt=O.SCALE_UE8M0, clamp=7.0)
+    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
