@@ -298,7 +298,8 @@ bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_
 bfp8moe_status_t moe_router_topk(const float* logits, int64_t M, int32_t E, int32_t k, int32_t score_fn,
                                  const float* bias, int32_t renormalize, double scale, int32_t* topk_ids,
                                  float* topk_w, void* stream) {
-  REQUIRE(M >= 0, "M=%lld invalid", (long long)M);
+  // four tokens per workgroup and a 32-bit grid
+  REQUIRE(M >= 0 && M <= 4 * (int64_t)0x7FFFFFFF, "M=%lld out of range", (long long)M);
   REQUIRE(E >= 1 && E <= 1024, "E=%d must be in [1, 1024]", E);
   REQUIRE(k >= 1 && k <= 64 && k <= E, "k=%d must be in [1, min(E, 64)]", k);
   REQUIRE(score_fn == BFP8MOE_SCORE_SOFTMAX || score_fn == BFP8MOE_SCORE_SIGMOID, "score_fn=%d invalid", score_fn);

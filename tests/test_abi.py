@@ -122,6 +122,8 @@ def test_host_validation_rejects_bad_calls():
     assert st == 1 and "stage 2" in msg
     st, msg = _status(L.moe_reduce, fake, fake, None, 0, 0, 2, 8, 100, fake, None)
     assert st == 1 and "multiple of 8" in msg
+    st, msg = _status(L.moe_router_topk, fake, 1 << 34, 256, 8, 0, None, 1, 1.0, fake, fake, None)
+    assert st == 1 and "out of range" in msg
     st, msg = _status(L.moe_router_topk, fake, 4, 2048, 8, 0, None, 1, 1.0, fake, fake, None)
     assert st == 1 and "E=2048" in msg
     st, msg = _status(L.moe_router_topk, fake, 4, 16, 17, 0, None, 1, 1.0, fake, fake, None)
