@@ -23,6 +23,10 @@
 //   hidden row in LDS.  Each route reads its expert's rows: with top-k routing
 //   the routes of one token have distinct experts, and at a few tokens the
 //   rows that two tokens share are a small part of the stream.
+// With the router folded in ([P2 Changes: the fused single-group top-k router
+//   feeds the layer]), one wave of each gate/up workgroup ranks the token's
+//   logits up to the route's rank first, and one wave per token writes the
+//   routing the down kernel reads.
 // down kernel: workgroup (b, t) computes output rows DR b .. DR b + DR - 1 of
 //   token t for its k routes from their W2 pieces (1 KB units: route, kRpl
 //   rows of I bytes), quantises the k SwiGLU rows itself, and ends with the

@@ -13,7 +13,10 @@
  *   silu_and_mul_quant_fp8  SwiGLU (optionally clamped) fused with quant_fp8
  *   moe_reduce              top-k weighted sum back to token order
  *
- * and fused_moe_block_fp8 runs the whole layer in one call.
+ * and fused_moe_block_fp8 runs the whole layer in one call.  The step before
+ * it, the single-group top-k router (moe_router_topk), turns router logits
+ * into the top-k ids and weights; fused_moe_block_fp8_routed runs the router
+ * and the layer in one call.
  *
  * Sources, cited by page title and section:
  *   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
