@@ -15,9 +15,12 @@ pytestmark = pytest.mark.gpu
 
 # (M, E, k): decode and prefill shapes of the layer's configurations (256 and
 # 512 experts, top-8), a width that is not a multiple of 64, k = E, the
-# largest E and k, one expert, and a ragged token count
+# largest E and k, one expert, and ragged token counts; from 8,192 tokens with
+# E <= 256 and k <= 16 the 16-lanes-per-token kernel runs (its largest k, a
+# width that is not a multiple of 16, token counts that leave rows idle)
 SHAPES = [(1, 256, 8), (7, 256, 8), (2048, 512, 8), (33, 64, 6), (5, 72, 6), (4, 8, 8), (3, 1024, 64),
-          (9, 1, 1), (130, 160, 2)]
+          (9, 1, 1), (130, 160, 2), (1000, 256, 8), (4099, 256, 8), (8200, 256, 8), (8192, 200, 16),
+          (8259, 256, 1)]
 
 
 def ulps(a, b):
