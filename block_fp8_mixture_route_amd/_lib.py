@@ -219,6 +219,15 @@ SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
 
 
+def _check_router_buffers(E, k, M, bias, topk_ids, topk_w):
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != E):
+        raise ValueError("the selection bias must be float32 with one value per expert")
+    if topk_ids is not None and (topk_ids.dtype != torch.int32 or tuple(topk_ids.shape) != (M, k)):
+        raise ValueError("topk_ids must be int32 of shape [M, k]")
+    if topk_w is not None and (topk_w.dtype != torch.float32 or tuple(topk_w.shape) != (M, k)):
+        raise ValueError("topk_w must be float32 of shape [M, k]")
+
+
 def router_topk(logits, k, score_fn=SCORE_SOFTMAX, bias=None, renormalize=True, scale=1.0, topk_ids=None,
                 topk_w=None):
     """[M, E] fp32 router logits -> ([M, k] int32 expert ids, largest first,
@@ -227,6 +236,7 @@ def router_topk(logits, k, score_fn=SCORE_SOFTMAX, bias=None, renormalize=True, 
     if logits.dtype != torch.float32:
         raise ValueError("router logits must be float32")
     M, E = logits.shape
+    _check_router_buffers(E, k, M, bias, topk_ids, topk_w)
     ids = torch.empty(M, k, dtype=torch.int32, device=logits.device) if topk_ids is None else topk_ids
     w = torch.empty(M, k, dtype=torch.float32, device=logits.device) if topk_w is None else topk_w
     check(lib().moe_router_topk(ptr(logits), M, E, k, score_fn, ptr(bias), int(bool(renormalize)), float(scale),
@@ -273,8 +283,11 @@ def fused_moe_block_fp8_routed(hidden, router_logits, k, w13, w13_scale, w2, w2_
     int32, topk_w [M, k] fp32)."""
     _require_device(hidden, router_logits, bias, w13, w13_scale, w2, w2_scale, topk_ids, topk_w)
     M, H = hidden.shape
+    if router_logits.dtype != torch.float32 or router_logits.shape[0] != M:
+        raise ValueError("router logits must be float32 of shape [M, E]")
     E = router_logits.shape[1]
     I = w2.shape[2]
+    _check_router_buffers(E, k, M, bias, topk_ids, topk_w)
     o = opts() if o is None else o
     need = fused_moe_workspace_size(M, H, k, E, I, o)
     if ws is None:

@@ -218,7 +218,11 @@ def router_topk(logits, k: int, score_fn: int = SCORE_SOFTMAX, bias=None, renorm
     ids, largest first, and [M, k] fp32 weights)."""
     lg = as_np(logits, np.float32)
     M, E = lg.shape
+    if not 1 <= k <= E:
+        raise ValueError(f"k={k} must be in [1, E={E}]")
     b = None if bias is None else as_np(bias, np.float32)
+    if b is not None and b.size != E:
+        raise ValueError("the selection bias needs one value per expert")
     ids = np.zeros((M, k), np.int32)
     w = np.zeros((M, k), np.float32)
     lib().oracle_router_topk(_p(lg), M, E, k, score_fn, _p(b), int(bool(renormalize)), float(scale), _p(ids), _p(w))

@@ -147,6 +147,18 @@ def test_host_validation_rejects_bad_calls():
     assert st == 1 and "sigmoid" in msg
 
 
+def test_router_binding_checks_buffers():
+    import torch
+    from block_fp8_mixture_route_amd import _lib as B
+    with pytest.raises(ValueError):
+        B._check_router_buffers(256, 8, 4, torch.zeros(255), None, None)
+    with pytest.raises(ValueError):
+        B._check_router_buffers(256, 8, 4, None, torch.zeros(4, 8, dtype=torch.int64), None)
+    with pytest.raises(ValueError):
+        B._check_router_buffers(256, 8, 4, None, None, torch.zeros(4, 7))
+    B._check_router_buffers(256, 8, 4, torch.zeros(256), torch.zeros(4, 8, dtype=torch.int32), torch.zeros(4, 8))
+
+
 def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):

@@ -119,3 +119,8 @@ def test_sigmoid_rn_and_scale():
     _, w1 = O.router_topk(lg, 6)
     _, w2 = O.router_topk(lg, 6, scale=4.0)
     assert np.array_equal(w1 * np.float32(4), w2)
+
+
+def test_rejects_k_above_e():
+    with pytest.raises(ValueError):
+        O.router_topk(np.zeros((1, 4), np.float32), 5)
