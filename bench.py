@@ -404,6 +404,66 @@ def routed_table(hip, stream, dev):
         print(f"| {name} | {t2:.2f} | {tf:.2f} | {tl:.2f} |", flush=True)
         del insts
         torch.cuda.empty_cache()
+    out["shared"] = shared_table(hip, stream, dev)
+    return out
+
+
+def shared_table(hip, stream, dev):
+    """The decode layer with a shared expert of width 2048 split into 8
+    pseudo-experts of width 256 (experts 256..263, weight 1 for every token):
+    one call with 16 routes per token, against the routed layer (8 routes)
+    and the shared expert (8 routes) as two calls (their sum left out, which
+    favours the two calls).  8 instances rotated."""
+    import torch
+
+    import block_fp8_mixture_route_amd as bfp8
+    from block_fp8_mixture_route_amd import synth
+
+    L_ = bfp8.lib()
+    P = ctypes.c_void_p
+    print()
+    print("| tokens M | one call, 16 routes µs | routed + shared, 2 calls µs | routed layer alone µs |")
+    print("|---|---|---|---|")
+    out = {}
+    H, I, E = 7168, 256, 264
+    o = bfp8.opts()
+    for M in (1, 2, 4):
+        insts = []
+        for i in range(8):
+            rid, rw = synth.uniform_routing(M, 256, 8, "bench_shared", M, i, device=dev)
+            sid = torch.arange(256, 264, dtype=torch.int32, device=dev).expand(M, 8)
+            ids16 = torch.cat([rid, sid], dim=1).contiguous()
+            w16 = torch.cat([rw, torch.ones(M, 8, device=dev)], dim=1).contiguous()
+            experts = torch.unique(ids16).cpu().tolist()
+            mw = synth.moe_weights(E, H, I, "bench_shared", M, i, experts=experts, device=dev)
+            hid = synth.hidden_states(M, H, "bench_shared", M, i, device=dev)
+            x = dict(ids16=ids16, w16=w16, ids8=rid.contiguous(), w8=rw.contiguous(),
+                     sid=(sid - 256).contiguous(), sw=torch.ones(M, 8, device=dev), mw=mw, hid=hid,
+                     out=torch.empty(M, H, dtype=torch.bfloat16, device=dev))
+            need = max(bfp8.fused_moe_workspace_size(M, H, k, E, I, o) for k in (8, 16))
+            x["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            insts.append(x)
+        torch.cuda.synchronize()
+
+        def call(x, ids, w, k, e0, ne):
+            m = x["mw"]
+            w13 = m.w13[e0:e0 + ne]
+            bfp8._lib.check(L_.fused_moe_block_fp8(
+                P(x["hid"].data_ptr()), M, H, P(ids.data_ptr()), P(w.data_ptr()), k, P(w13.data_ptr()),
+                P(m.w13_s[e0:e0 + ne].data_ptr()), P(m.w2[e0:e0 + ne].data_ptr()), P(m.w2_s[e0:e0 + ne].data_ptr()),
+                ne, I, ctypes.byref(o), P(x["out"].data_ptr()), P(x["ws"].data_ptr()), x["ws"].numel(), stream))
+
+        one = lambda: [call(x, x["ids16"], x["w16"], 16, 0, E) for x in insts * 4]
+        two = lambda: [(call(x, x["ids8"], x["w8"], 8, 0, 256), call(x, x["sid"], x["sw"], 8, 256, 8))
+                       for x in insts * 4]
+        routed = lambda: [call(x, x["ids8"], x["w8"], 8, 0, 256) for x in insts * 4]
+        t1 = time_graph(hip, stream, one, 40) * 1e3 / 32
+        t2 = time_graph(hip, stream, two, 40) * 1e3 / 32
+        t0 = time_graph(hip, stream, routed, 40) * 1e3 / 32
+        out[M] = {"one_call_us": t1, "two_calls_us": t2, "routed_us": t0}
+        print(f"| {M} | {t1:.2f} | {t2:.2f} | {t0:.2f} |", flush=True)
+        del insts
+        torch.cuda.empty_cache()
     return out
 
 

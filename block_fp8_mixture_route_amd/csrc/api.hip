@@ -339,7 +339,7 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
                 (long long)M, k, H, I);
   if ((o.flags & BFP8MOE_FLAG_LAYER_TOKEN) && M > 0 && !bfp8::token_path_fits(M, H, k, I))
     return fail(BFP8MOE_ERR_UNSUPPORTED,
-                "few-token path forced but M=%lld k=%d H=%d I=%d do not fit it (M<=32, k<=8, H<=8192, "
+                "few-token path forced but M=%lld k=%d H=%d I=%d do not fit it (M<=32, k<=16, H<=8192, "
                 "I in {128, 256, 512})",
                 (long long)M, k, H, I);
   {

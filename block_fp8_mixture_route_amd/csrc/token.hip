@@ -60,7 +60,7 @@ constexpr int kUpWaves = kUpThreads / 64;
 constexpr int kColumnWaves = 8;
 constexpr int kDownThreads = 1024;  // down kernel: 16 waves
 constexpr int kDownWaves = kDownThreads / 64;
-constexpr int kMaxK = 8;
+constexpr int kMaxK = 16;  // routes per token; the down kernel is built for 8 and for 16
 constexpr int kMaxTokens = 32;  // tokens per call on this path
 constexpr int kMaxH = 8192;
 constexpr int kUnitsPerWave = 4;                            // 1 KB W2 units per down wave
@@ -354,16 +354,16 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
 // depend on the routing), the W2 units, the W2 block scale of each lane's
 // row and group.  Route ids are read with uniform (scalar) loads by each wave
 // that needs them: no barrier stands between the start and the W2 loads.
-template <int I>
+template <int I, int KMAX>
 __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int k,
     int32_t offset, int32_t L, const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int H, int fmt,
     int DR, int DL, uint32_t dl_magic, uint16_t* __restrict__ out) {
   constexpr int GI = I / 128, kRpl = 1024 / I, kLpr = I / 16;
-  constexpr int kActLoads = (kMaxK * GI + kDownWaves - 1) / kDownWaves;  // SwiGLU groups per wave
-  __shared__ __align__(16) h2 s_qh[kMaxK][I / 2];  // quantised SwiGLU rows (E4M3 values as FP16)
-  __shared__ float s_qs[kMaxK][GI];                // their group scales
-  __shared__ float s_y[kMaxK][kMaxDownRows];       // down outputs per route (BF16 values)
+  constexpr int kActLoads = (KMAX * GI + kDownWaves - 1) / kDownWaves;  // SwiGLU groups per wave
+  __shared__ __align__(16) h2 s_qh[KMAX][I / 2];  // quantised SwiGLU rows (E4M3 values as FP16)
+  __shared__ float s_qs[KMAX][GI];                // their group scales
+  __shared__ float s_y[KMAX][kMaxDownRows];       // down outputs per route (BF16 values)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -461,20 +461,20 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
   //    tid < DR <= 64).  The routing comes from the wave's own lanes, read
   //    while every lane is active; every s_y read is issued before the first
   //    is used.
-  float wr[kMaxK];
-  bool lr[kMaxK];
+  float wr[KMAX];
+  bool lr[KMAX];
 #pragma unroll
-  for (int r = 0; r < kMaxK; r++) {
+  for (int r = 0; r < KMAX; r++) {
     lr[r] = r < k && __builtin_amdgcn_readlane(e_lane, r) >= 0;
     wr[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), r));
   }
   if (tid < d_end - d0) {
-    float y[kMaxK];
+    float y[KMAX];
 #pragma unroll
-    for (int r = 0; r < kMaxK; r++) y[r] = s_y[r][tid];
+    for (int r = 0; r < KMAX; r++) y[r] = s_y[r][tid];
     float a = 0.0f;
 #pragma unroll
-    for (int r = 0; r < kMaxK; r++)
+    for (int r = 0; r < KMAX; r++)
       if (lr[r]) a = __builtin_fmaf(wr[r], y[r], a);
     out[d0 + tid] = (uint16_t)f32_to_bf16(a);
   }
@@ -554,10 +554,15 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hook) hook->before(1, stream);
-#define BFP8_TOKEN_DOWN(II)                                                                                    \
-  hipLaunchKernelGGL((token_down_kernel<II>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0, stream, act,  \
-                     ids, topk_w,                                                                              \
-                     k, offset, L, w2, w2_s, H, fmt, dr, dl, dl_magic, out)
+#define BFP8_TOKEN_DOWN(II)                                                                                      \
+  do {                                                                                                           \
+    if (k <= 8)                                                                                                  \
+      hipLaunchKernelGGL((token_down_kernel<II, 8>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0, stream, \
+                         act, ids, topk_w, k, offset, L, w2, w2_s, H, fmt, dr, dl, dl_magic, out);               \
+    else                                                                                                         \
+      hipLaunchKernelGGL((token_down_kernel<II, 16>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0,      \
+                         stream, act, ids, topk_w, k, offset, L, w2, w2_s, H, fmt, dr, dl, dl_magic, out);       \
+  } while (0)
   if (!run1) {
   } else if (I == 128)
     BFP8_TOKEN_DOWN(128);

@@ -296,7 +296,7 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
  * calls.  Calls that share a workspace must not run concurrently.  opts: host
  * pointer (NULL = defaults).
  * Three implementations, chosen by shape unless a test flag forces one:
- *   few tokens (M <= 32, k <= 8, H <= 8192, I in {128, 256, 512}; the
+ *   few tokens (M <= 32, k <= 16, H <= 8192, I in {128, 256, 512}; the
  *     default up to 12 tokens): two matrix-vector kernels -- input
  *     quantisation, gate/up GEMM and SwiGLU per route (M x k x I/8
  *     workgroups; each route reads its expert's rows), then the SwiGLU

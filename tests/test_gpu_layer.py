@@ -292,3 +292,29 @@ def test_layer_zero_tokens(path):
                                    o=bfp8.opts(flags=path))
     torch.cuda.synchronize()
     assert tuple(out.shape) == (0, c.H)
+
+
+# more routes than top-8 on the few-token path (its down kernel is built for 8
+# and for 16 routes per token), among them the shape of 8 routed experts plus
+# a shared expert of width 2048 split into 8 pseudo-experts of width 256 that
+# every token takes with weight 1 (experts 256..263)
+@pytest.mark.parametrize("M,E,k,H,I", [(1, 264, 16, 7168, 256), (3, 64, 12, 2048, 512), (2, 40, 9, 1024, 128)])
+def test_token_path_more_routes(M, E, k, H, I):
+    print_case("token path k", M, E, k, H, I)
+    if E == 264:
+        rid, rw = synth.uniform_routing(M, 256, 8, "k16", M)
+        ids = torch.cat([rid, torch.arange(256, 264, dtype=torch.int32).expand(M, 8)], dim=1).contiguous()
+        w = torch.cat([rw, torch.ones(M, 8)], dim=1).contiguous()
+    else:
+        ids, w = synth.uniform_routing(M, E, k, "k16", M)
+    W = synth.moe_weights(E, H, I, "k16", M, experts=np.unique(ids.numpy()).tolist(), device=dev())
+    hidden = synth.hidden_states(M, H, "k16", M).to(dev())
+    o = bfp8.opts(flags=bfp8.FLAG_LAYER_TOKEN)
+    assert bfp8.fused_moe_stages(M, H, k, E, I, o)[0] == "token_gate_up_swiglu"
+    out = bfp8.fused_moe_block_fp8(hidden, ids.to(dev()), w.to(dev()), W.w13, W.w13_s, W.w2, W.w2_s, E=E, o=o)
+    gen = bfp8.fused_moe_block_fp8(hidden, ids.to(dev()), w.to(dev()), W.w13, W.w13_s, W.w2, W.w2_s, E=E,
+                                   o=bfp8.opts(flags=bfp8.FLAG_LAYER_GENERAL))
+    torch.cuda.synchronize()
+    ref = O.fused_moe(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s)
+    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+    assert normwise_err(bf16_np(gen), ref) <= LAYER_TOL

@@ -102,7 +102,7 @@ def test_router_zero_tokens_and_layer_feed():
 # experts; more tokens than the few-token path takes by default)
 ROUTED = [(1, 256, 8, 7168, 256, bfp8.SCORE_SOFTMAX), (4, 256, 8, 7168, 256, bfp8.SCORE_SIGMOID),
           (3, 16, 4, 256, 128, bfp8.SCORE_SOFTMAX), (12, 256, 8, 2048, 256, bfp8.SCORE_SOFTMAX), (2, 512, 8, 1024, 256, bfp8.SCORE_SIGMOID),
-          (16, 256, 8, 1024, 256, bfp8.SCORE_SOFTMAX)]
+          (16, 256, 8, 1024, 256, bfp8.SCORE_SOFTMAX), (2, 256, 16, 2048, 256, bfp8.SCORE_SOFTMAX)]
 
 
 @pytest.mark.parametrize("M,E,k,H,I,score_fn", ROUTED)
