@@ -290,7 +290,11 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
  * out [M, H] BF16 = moe_reduce over routes of
  *   down( silu_and_mul_quant( gate_up( quant_fp8(hidden) ) ) ).
  * The hidden states and the SwiGLU output are both quantised with
- * opts->scale_fmt.  H and I must be positive multiples of 128.  ws: device
+ * opts->scale_fmt.  H and I must be positive multiples of 128.  A shared
+ * expert can ride along as routes: split its width into experts of width I
+ * (stored after the routed ones) and give every token those ids with weight 1
+ * [P3: the shared expert runs beside the routed layer]; the few-token path
+ * takes up to 16 routes per token.  ws: device
  * workspace of at least fused_moe_block_fp8_workspace_size() bytes, 256-byte
  * aligned; its contents need no initialisation and are not kept between
  * calls.  Calls that share a workspace must not run concurrently.  opts: host
