@@ -31,4 +31,5 @@ from ._lib import (  # noqa: F401
     router_topk,
     silu_and_mul,
     silu_and_mul_quant_fp8,
+    wait_faults,
 )

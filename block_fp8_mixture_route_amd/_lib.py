@@ -60,6 +60,7 @@ SIGNATURES = {
     "bfp8moe_opts_init": (None, [ctypes.POINTER(Opts)]),
     "bfp8moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bfp8moe_last_error": (ctypes.c_char_p, []),
+    "bfp8moe_wait_faults": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]),
     "bfp8moe_max_blocks": (_i64, [_i64, _i32, _i32]),
     "moe_route_prepare_workspace_size": (_sz, [_i64, _i32, _u32]),
     "moe_route_prepare": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _P, _P, _P, _P, _i64, _P, _P, _sz, _u32, _P]),
@@ -125,6 +126,40 @@ def _u16(t):
     return t.view(torch.uint16) if t.dtype == torch.bfloat16 else t
 
 
+def _u8(t):
+    return t.view(torch.uint8) if t is not None and t.dtype == torch.float8_e4m3fn else t
+
+
+def _expect(t, name, dtypes, shape=None):
+    """Raise ValueError unless t has one of `dtypes` and, where given, the shape
+    (None entries match any size).  The library reads raw memory: a wrong
+    dtype or shape would silently be misread or read out of bounds."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and a != s for a, s in zip(t.shape, shape)):
+            raise ValueError(f"{name} must have shape {tuple('*' if s is None else s for s in shape)}, "
+                             f"got {tuple(t.shape)}")
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def wait_faults(clear=True) -> int:
+    """Fault bits of the kernels' bounded waits on the current device since the
+    last clear (0: none).  Synchronises with the device; for tests and
+    debugging."""
+    f = ctypes.c_uint32(0)
+    check(lib().bfp8moe_wait_faults(ctypes.byref(f), int(bool(clear))))
+    return f.value
+
+
 def opts(block_m=0, scale_fmt=SCALE_FP32, clamp_limit=math.inf, expert_offset=0, local_num_experts=0, flags=0):
     o = Opts()
     lib().bfp8moe_opts_init(ctypes.byref(o))
@@ -140,6 +175,7 @@ def max_blocks(R: int, L: int, block_m: int) -> int:
 
 
 def moe_route_prepare(topk_ids: torch.Tensor, expert_offset: int, L: int, block_m: int, with_blocks=True, flags=0):
+    _expect(topk_ids, "topk_ids", torch.int32)
     _require_device(topk_ids)
     ids = topk_ids.reshape(-1)
     R = ids.numel()
@@ -163,8 +199,11 @@ def moe_route_prepare(topk_ids: torch.Tensor, expert_offset: int, L: int, block_
 
 
 def quant_fp8(x: torch.Tensor, scale_fmt=SCALE_FP32, q=None, scales=None):
-    _require_device(x)
+    _expect(x, "x", torch.bfloat16, (None, None))
     rows, K = x.shape
+    _expect(q, "q", _FP8, (rows, K))
+    _expect(scales, "scales", torch.float32, (rows, K // 128))
+    _require_device(x, q, scales)
     q = torch.empty(rows, K, dtype=torch.uint8, device=x.device) if q is None else q
     scales = torch.empty(rows, K // 128, dtype=torch.float32, device=x.device) if scales is None else scales
     check(lib().quant_fp8(ptr(_u16(x)), rows, K, scale_fmt, ptr(q), ptr(scales), stream_of(x.device)))
@@ -172,8 +211,10 @@ def quant_fp8(x: torch.Tensor, scale_fmt=SCALE_FP32, q=None, scales=None):
 
 
 def silu_and_mul(gate_up: torch.Tensor, clamp_limit=math.inf, out=None):
-    _require_device(gate_up)
+    _expect(gate_up, "gate_up", torch.bfloat16, (None, None))
     rows, I2 = gate_up.shape
+    _expect(out, "out", torch.bfloat16, (rows, I2 // 2))
+    _require_device(gate_up, out)
     out = torch.empty(rows, I2 // 2, dtype=torch.bfloat16, device=gate_up.device) if out is None else out
     check(lib().silu_and_mul(ptr(_u16(gate_up)), rows, I2 // 2, clamp_limit, ptr(_u16(out)),
                              stream_of(gate_up.device)))
@@ -182,9 +223,14 @@ def silu_and_mul(gate_up: torch.Tensor, clamp_limit=math.inf, out=None):
 
 def silu_and_mul_quant_fp8(gate_up: torch.Tensor, row_expert_ids=None, expert_map=None, E=0,
                            clamp_limit=math.inf, scale_fmt=SCALE_FP32, q=None, scales=None):
-    _require_device(gate_up, row_expert_ids, expert_map)
+    _expect(gate_up, "gate_up", torch.bfloat16, (None, None))
     rows, I2 = gate_up.shape
     I = I2 // 2
+    _expect(row_expert_ids, "row_expert_ids", torch.int32, (rows,))
+    _expect(expert_map, "expert_map", torch.int32, (E,))
+    _expect(q, "q", _FP8, (rows, I))
+    _expect(scales, "scales", torch.float32, (rows, I // 128))
+    _require_device(gate_up, row_expert_ids, expert_map, q, scales)
     q = torch.empty(rows, I, dtype=torch.uint8, device=gate_up.device) if q is None else q
     scales = torch.empty(rows, I // 128, dtype=torch.float32, device=gate_up.device) if scales is None else scales
     check(lib().silu_and_mul_quant_fp8(ptr(_u16(gate_up)), rows, I, ptr(row_expert_ids), ptr(expert_map), E,
@@ -194,8 +240,16 @@ def silu_and_mul_quant_fp8(gate_up: torch.Tensor, row_expert_ids=None, expert_ma
 
 def moe_fp8_grouped_gemm(A, A_scale, a_row_div, B, B_scale, route, block_m, R, C=None):
     """route: the dict returned by moe_route_prepare (with blocks)."""
-    _require_device(A, A_scale, B, B_scale)
+    _expect(B, "B", _FP8, (None, None, None))
     L, N, K = B.shape
+    _expect(A, "A", _FP8, (None, K))
+    _expect(A_scale, "A_scale", torch.float32, (A.shape[0], K // 128))
+    _expect(B_scale, "B_scale", torch.float32, (L, N // 128, K // 128))
+    if R > A.shape[0] * a_row_div:
+        raise ValueError(f"R={R} routes need {-(-R // a_row_div)} rows of A, it has {A.shape[0]}")
+    _expect(C, "C", torch.bfloat16, (R, N))
+    _require_device(A, A_scale, B, B_scale, C)
+    A, B = _u8(A), _u8(B)
     C = torch.empty(R, N, dtype=torch.bfloat16, device=A.device) if C is None else C
     check(lib().moe_fp8_grouped_gemm(ptr(A), ptr(A_scale), a_row_div, ptr(B), ptr(B_scale), L, N, K,
                                      ptr(route["sorted_routes"]), ptr(route["expert_offsets"]),
@@ -206,9 +260,13 @@ def moe_fp8_grouped_gemm(A, A_scale, a_row_div, B, B_scale, route, block_m, R, C
 
 
 def moe_reduce(y, topk_w, topk_ids=None, expert_offset=0, L=0, out=None):
-    _require_device(y, topk_w, topk_ids)
+    _expect(topk_w, "topk_w", torch.float32, (None, None))
     M, k = topk_w.shape
+    _expect(y, "y", torch.bfloat16, (M * k, None))
     H = y.shape[1]
+    _expect(topk_ids, "topk_ids", torch.int32, (M, k))
+    _expect(out, "out", torch.bfloat16, (M, H))
+    _require_device(y, topk_w, topk_ids, out)
     out = torch.empty(M, H, dtype=torch.bfloat16, device=y.device) if out is None else out
     check(lib().moe_reduce(ptr(_u16(y)), ptr(topk_w), ptr(topk_ids), expert_offset, L, M, k, H, ptr(_u16(out)),
                            stream_of(y.device)))
@@ -258,14 +316,39 @@ def fused_moe_stages(M, H, k, E, I, o: Opts):
     return [names[i].decode() for i in range(n)]
 
 
+def _check_layer_buffers(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, E, o, out, ws, need=None):
+    """dtypes and shapes of the layer's buffers, so that no pointer handed to
+    the library is misread or read past its end: hidden [M, H] bf16, routing
+    [M, k] int32 / fp32, w13 [L', 2I, H] and w2 [L', H, I] E4M3 bytes with
+    L' >= the local expert count, their fp32 block scales, out [M, H] bf16."""
+    _expect(hidden, "hidden", torch.bfloat16, (None, None))
+    M, H = hidden.shape
+    _expect(topk_ids, "topk_ids", torch.int32, (M, None))
+    k = topk_ids.shape[1]
+    _expect(topk_w, "topk_w", torch.float32, (M, k))
+    _expect(w2, "w2", _FP8, (None, H, None))
+    Lw, _, I = w2.shape
+    _expect(w13, "w13", _FP8, (Lw, 2 * I, H))
+    _expect(w13_scale, "w13_scale", torch.float32, (Lw, 2 * I // 128, H // 128))
+    _expect(w2_scale, "w2_scale", torch.float32, (Lw, H // 128, I // 128))
+    L = o.local_num_experts if o.local_num_experts > 0 else E
+    if Lw < L:
+        raise ValueError(f"the weights hold {Lw} experts, the call addresses {L}")
+    _expect(out, "out", torch.bfloat16, (M, H))
+    if ws is not None:
+        _expect(ws, "ws", torch.uint8, (None,))
+        if need is not None and ws.numel() < need:
+            raise ValueError(f"workspace of {ws.numel()} bytes, {need} needed")
+    return M, H, k, I
+
+
 def fused_moe_block_fp8(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, E=None, o: Opts = None,
                         out=None, ws=None):
-    _require_device(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale)
-    M, H = hidden.shape
-    k = topk_ids.shape[1]
-    I = w2.shape[2]
     E = w13.shape[0] if E is None else E
     o = opts() if o is None else o
+    M, H, k, I = _check_layer_buffers(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, E, o, out, ws)
+    _require_device(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, out, ws)
+    w13, w2 = _u8(w13), _u8(w2)
     need = fused_moe_workspace_size(M, H, k, E, I, o)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
@@ -281,14 +364,19 @@ def fused_moe_block_fp8_routed(hidden, router_logits, k, w13, w13_scale, w2, w2_
                                topk_ids=None, topk_w=None):
     """Router and layer in one call: returns (out [M, H] BF16, topk_ids [M, k]
     int32, topk_w [M, k] fp32)."""
-    _require_device(hidden, router_logits, bias, w13, w13_scale, w2, w2_scale, topk_ids, topk_w)
+    _expect(hidden, "hidden", torch.bfloat16, (None, None))
     M, H = hidden.shape
-    if router_logits.dtype != torch.float32 or router_logits.shape[0] != M:
+    if router_logits.dtype != torch.float32 or router_logits.dim() != 2 or router_logits.shape[0] != M:
         raise ValueError("router logits must be float32 of shape [M, E]")
     E = router_logits.shape[1]
-    I = w2.shape[2]
     _check_router_buffers(E, k, M, bias, topk_ids, topk_w)
     o = opts() if o is None else o
+    _check_layer_buffers(hidden, torch.empty(M, k, dtype=torch.int32, device="meta"),
+                         torch.empty(M, k, dtype=torch.float32, device="meta"), w13, w13_scale, w2, w2_scale, E, o,
+                         out, ws)
+    _require_device(hidden, router_logits, bias, w13, w13_scale, w2, w2_scale, topk_ids, topk_w, out, ws)
+    w13, w2 = _u8(w13), _u8(w2)
+    I = w2.shape[2]
     need = fused_moe_workspace_size(M, H, k, E, I, o)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)

@@ -1,7 +1,8 @@
 // api.hip -- the C ABI declared in include/bfp8moe.h.  Host code: validates
 // arguments before anything is enqueued, lays out workspaces, picks kernels
 // by shape and launches them on the caller's stream.  Never allocates device
-// memory, never synchronises, never reads device data.
+// memory, never synchronises, never reads device data (except the debugging
+// query bfp8moe_wait_faults).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -172,6 +173,15 @@ const char* bfp8moe_status_string(int status) {
 }
 
 const char* bfp8moe_last_error(void) { return g_last_error.c_str(); }
+
+bfp8moe_status_t bfp8moe_wait_faults(uint32_t* flags, int clear) {
+  REQUIRE(flags != nullptr, "flags must be non-null");
+  unsigned f = 0;
+  const hipError_t e = bfp8::read_wait_faults(&f, clear != 0);
+  if (e != hipSuccess) return hip_status(e, "bfp8moe_wait_faults");
+  *flags = f;
+  return BFP8MOE_OK;
+}
 
 int64_t bfp8moe_max_blocks(int64_t R, int32_t L, int32_t block_m) {
   if (R <= 0 || L <= 0 || block_m <= 0) return 0;

@@ -116,6 +116,10 @@ bool decode_path_fits(int64_t M, int H, int k, int I);
 // expert's rows).  act: [M*k, I] BF16 scratch.
 bool token_path_fits(int64_t M, int H, int k, int I);
 int device_cu_count();  // of the current device; 0 when there is none
+// Fault bits of the bounded in-kernel waits on the current device (bit 0: the
+// few-token gate/up kernel's wait for its hidden row ran out); optionally
+// cleared.  Synchronous.
+hipError_t read_wait_faults(unsigned* flags, bool clear);
 hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
                               int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
                               const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,

@@ -16,6 +16,10 @@
 // [P4 Pull request overview] the down projection ends with the top-k weighted
 // reduction, routes in order.
 //
+// The column waves' wait for the hidden row is bounded; running out of it
+// ends the kernel normally and sets a device flag the host can read
+// (bfp8moe_wait_faults).
+//
 // gate/up kernel: workgroup (route j, slice q) computes columns n = 8 q .. 8 q
 //   + 7 of route j's SwiGLU row (route j = t k + r belongs to token t), one
 //   column (gate row n and up row I + n) per column wave, each written as one
@@ -68,6 +72,16 @@ constexpr int kMaxUnits = kDownWaves * kUnitsPerWave;       // per down workgrou
 constexpr int kMaxDownRows = 64;
 constexpr int kDownTarget = 256;  // down workgroups aimed at (one per compute unit of MI355X)
 constexpr unsigned kSpinLimit = 1u << 20;  // bound of the LDS waits (about 0.03 s)
+
+}  // namespace
+
+// Bit 0: a column wave of the gate/up kernel ran out of its bounded wait for
+// the hidden row (its column's value is then unspecified).  Set with a device
+// atomic, never cleared by the kernels; read and cleared by
+// read_wait_faults (bfp8moe_wait_faults in the C ABI).
+__device__ unsigned int g_wait_faults = 0;
+
+namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
@@ -323,6 +337,9 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
        spins < kSpinLimit;
        spins++)
     __builtin_amdgcn_s_sleep(1);
+  if (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kUpWaves - kColumnWaves &&
+      lane == 0)
+    atomicOr(&g_wait_faults, 1u);  // ran out: report it
 
   // gate and up dot products as the data lands
   float ag = 0.0f, au = 0.0f;
@@ -491,6 +508,15 @@ int token_down_rows(int H, int I, int k) {
   dl = dl < kMaxUnits / k ? dl : kMaxUnits / k;
   dl = dl < kMaxDownRows / rpl ? dl : kMaxDownRows / rpl;
   return (dl > 1 ? dl : 1) * rpl;
+}
+
+hipError_t read_wait_faults(unsigned* flags, bool clear) {
+  hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_wait_faults), sizeof(unsigned), 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear) {
+    const unsigned zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_wait_faults), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  }
+  return e;
 }
 
 bool token_path_fits(int64_t M, int H, int k, int I) {

@@ -254,3 +254,68 @@ def router_bias(E: int, *key, std=0.05, device="cpu"):
     """Per-expert selection bias of sigmoid routing, N(0, std) fp32."""
     g = gen(device, *key, "router_bias", E)
     return (torch.randn(E, generator=g, device=device, dtype=torch.float32) * std).contiguous()
+
+
+# --------------------------------------------------------------------------
+# a layer instance whose arithmetic is exact up to its final roundings
+# --------------------------------------------------------------------------
+
+def _e4m3_codes_of(values: torch.Tensor) -> torch.Tensor:
+    """E4M3FN bytes of values that are exactly representable (small integers,
+    448): torch's cast, which is exact on them."""
+    return values.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def exact_layer_inputs(M: int, E: int, k: int, H: int, I: int, *key, device="cpu"):
+    """hidden, topk ids, topk weights and weights of one layer instance built so
+    that every sum the layer forms is exact in fp32, whatever the order:
+
+    * hidden row t: integers in [-4, 4] times 2^m_t (m_t in {-4, -3, -2}), and in
+      every group of 128 one position holding +-448 * 2^m_t, so that each group's
+      amax is 448 * 2^m_t and its scale (fp32 or UE8M0) is exactly 2^m_t; the
+      quantised row is the integers and +-448 themselves;
+    * W13: integer codes in [-2, 2], block scales 2^b with b in {-9, -8, -7}: a
+      gate/up sum is a multiple of 2^(m_t - 9) below 2^(m_t + 10);
+    * W2: in each row n, two non-zero codes (+-1, +-2), one in each half of one
+      16-wide slice of K (the slice varies with n), the rest zero, block
+      scales 2^b as above: with power-of-two (UE8M0) activation scales a down
+      output is at most two products of E4M3 values times powers of two, and
+      two such products never lie in one run of 8 consecutive K (where FP8
+      MFMA hardware aligns products to their largest before adding them);
+    * routing: uniform top-k, with a few routes of token 0 masked (-1) when
+      k > 2, and fp32 renormalised weights.
+
+    With UE8M0 activation scales the two GEMMs are then exact in any
+    accumulation order, so the BF16 gate/up values, the SwiGLU row, its codes
+    and scales, the down outputs and the reduction are each determined by
+    their definition alone."""
+    g = gen(device, *key, "exact_layer", M, E, k, H, I)
+    G, GI = H // GROUP, I // GROUP
+    m = torch.randint(-4, -1, (M, 1), generator=g, device=device).to(torch.float32)
+    n = torch.randint(-4, 5, (M, H), generator=g, device=device).to(torch.float32)
+    pos = torch.randint(0, GROUP, (M, G), generator=g, device=device)
+    sign = torch.randint(0, 2, (M, G), generator=g, device=device).to(torch.float32) * 2 - 1
+    n.view(M, G, GROUP).scatter_(2, pos[:, :, None], (448.0 * sign)[:, :, None])
+    hidden = (n * torch.exp2(m)).to(torch.bfloat16).contiguous()
+
+    ids, w = uniform_routing(M, E, k, *key, "exact_routing", device=device)
+    if k > 2:
+        ids = ids.clone()
+        ids[0, 1] = -1
+        ids[0, k - 1] = -1
+
+    w13i = torch.randint(-2, 3, (E, 2 * I, H), generator=g, device=device)
+    w13 = _e4m3_codes_of(w13i).contiguous()
+    w13_s = torch.exp2(torch.randint(-9, -6, (E, 2 * I // GROUP, G), generator=g, device=device).to(torch.float32))
+    # W2 row n: two non-zero codes, one in each half of one 16-wide K slice
+    # (the slice varies with n), so each down output is one or two products
+    w2i = torch.zeros(E, H, I, dtype=torch.float32, device=device)
+    sl = torch.randint(0, I // 16, (E, H, 1), generator=g, device=device)
+    off = torch.randint(0, 8, (E, H, 2), generator=g, device=device)
+    pos = sl * 16 + torch.tensor([0, 8], device=device) + off
+    val = torch.randint(1, 3, (E, H, 2), generator=g, device=device).to(torch.float32)
+    val = val * (torch.randint(0, 2, (E, H, 2), generator=g, device=device).to(torch.float32) * 2 - 1)
+    w2i.scatter_(2, pos, val)
+    w2 = _e4m3_codes_of(w2i).contiguous()
+    w2_s = torch.exp2(torch.randint(-9, -6, (E, H // GROUP, GI), generator=g, device=device).to(torch.float32))
+    return hidden, ids.contiguous(), w, MoEWeights(w13, w13_s.contiguous(), w2, w2_s.contiguous())

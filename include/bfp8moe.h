@@ -31,7 +31,8 @@
  * Memory.  Every pointer argument is a DEVICE pointer unless it is marked
  *   "host".  The caller owns all memory (inputs, outputs, workspace); the
  *   library never allocates, frees, synchronises the host or reads device data
- *   on the host, so every call is legal inside HIP stream capture.
+ *   on the host, so every call is legal inside HIP stream capture (the one
+ *   exception is the debugging query bfp8moe_wait_faults).
  * Layout.  Row-major and contiguous.  BF16 is passed as uint16_t bit patterns,
  *   E4M3FN as uint8_t codes.  Device pointers must be 16-byte aligned.
  * Streams.  `stream` is a hipStream_t passed as void*; NULL is the default
@@ -112,6 +113,15 @@ const char* bfp8moe_status_string(int status);
 /* Message of the last failure on this thread ("" if none).  Host string owned
  * by the library, valid until the next call on the same thread. */
 const char* bfp8moe_last_error(void);
+
+/* Fault bits of the kernels' bounded waits on the current device, accumulated
+ * since the last clear: bit 0 is set when a column wave of the few-token
+ * gate/up kernel ran out of its bounded wait for the quantised hidden row (the
+ * kernel then ends normally, but that column of that call is unspecified).
+ * flags: host pointer.  clear != 0 resets them afterwards.  A debugging and
+ * testing query: it synchronises with the device (it copies one word), so it
+ * is not for use inside stream capture or a latency-critical loop. */
+bfp8moe_status_t bfp8moe_wait_faults(uint32_t* flags, int clear);
 
 /* ------------------------------------------------------------------------- */
 /* Route preparation                                                         */

@@ -314,28 +314,61 @@ int64_t oracle_route_prepare(const int32_t* topk_ids, int64_t R, int expert_offs
 /* [P1 Motivation: gate/up GEMM and down-projection on FP8 inputs]             */
 /* ------------------------------------------------------------------------- */
 
+/* One output of the block-FP8 GEMM before its rounding:
+ *   sum_g (a_s[g] * w_s[g]) * sum_{i in group g} dec(a[i]) * dec(w[i])
+ * ad: [K] decoded activation values; a_s: [K/128]; w: one weight row [K]
+ * (E4M3 codes); w_s: that row's [K/128] block scales.  All arithmetic is fp64:
+ * each product of two E4M3 values has at most 8 significant bits and a group
+ * sum of 128 of them is exact, so only the scale products and the sum over
+ * groups round, at 2^-53.  When abs_sum is non-NULL it receives
+ * sum_g |a_s[g] * w_s[g]| * sum_i |dec(a[i]) * dec(w[i])|, the magnitude that
+ * bounds the rounding error of any fp32 evaluation of the same sum. */
+static double gemm_dot(const double* ad, const float* a_s, const uint8_t* w, const float* w_s, int G,
+                       double* abs_sum)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int g = 0; g < G; g++) {
+        double p = 0.0, pa = 0.0;
+        for (int i = g * ORACLE_GROUP; i < (g + 1) * ORACLE_GROUP; i++) {
+            double t = ad[i] * oracle_e4m3_decode(w[i]);
+            p += t;
+            pa += fabs(t);
+        }
+        double c = (double)a_s[g] * (double)w_s[g];
+        acc += c * p;
+        mag += fabs(c) * pa;
+    }
+    if (abs_sum) *abs_sum = mag;
+    return acc;
+}
+
 /* out[n] = bf16( sum_g  (a_s[g] * w_s[n/128][g]) * sum_{i in group g} dec(a[i]) * dec(W[n][i]) )
  * a: [K] E4M3, a_s: [K/128]; W: [N, K] E4M3 (row n = output n, K contiguous);
- * w_s: [N/128, K/128].  All arithmetic in fp64; the inner group sum is exact. */
-static void gemm_row(const uint8_t* a, const float* a_s, const uint8_t* W, const float* w_s,
-                     int N, int K, uint16_t* out)
+ * w_s: [N/128, K/128].  The sum is gemm_dot's, rounded once to BF16.  When
+ * acc_out / abs_out are non-NULL they receive the unrounded value and its
+ * magnitude bound for each n.  Output rows are independent: OpenMP spreads
+ * them over the host's threads. */
+static void gemm_row_ex(const uint8_t* a, const float* a_s, const uint8_t* W, const float* w_s,
+                        int N, int K, uint16_t* out, double* acc_out, double* abs_out)
 {
     int G = K / ORACLE_GROUP;
     double* ad = (double*)malloc(sizeof(double) * (size_t)K);
     for (int i = 0; i < K; i++) ad[i] = oracle_e4m3_decode(a[i]);
+#pragma omp parallel for schedule(static)
     for (int n = 0; n < N; n++) {
-        const uint8_t* wr = W + (size_t)n * K;
-        double acc = 0.0;
-        for (int g = 0; g < G; g++) {
-            double p = 0.0;
-            for (int i = g * ORACLE_GROUP; i < (g + 1) * ORACLE_GROUP; i++)
-                p += ad[i] * oracle_e4m3_decode(wr[i]);
-            double c = (double)a_s[g] * (double)w_s[(size_t)(n / ORACLE_GROUP) * G + g];
-            acc += c * p;
-        }
-        out[n] = oracle_f64_to_bf16(acc);
+        double mag;
+        double acc = gemm_dot(ad, a_s, W + (size_t)n * K, w_s + (size_t)(n / ORACLE_GROUP) * G, G, &mag);
+        if (out) out[n] = oracle_f64_to_bf16(acc);
+        if (acc_out) acc_out[n] = acc;
+        if (abs_out) abs_out[n] = mag;
     }
     free(ad);
+}
+
+static void gemm_row(const uint8_t* a, const float* a_s, const uint8_t* W, const float* w_s,
+                     int N, int K, uint16_t* out)
+{
+    gemm_row_ex(a, a_s, W, w_s, N, K, out, NULL, NULL);
 }
 
 /* Grouped GEMM over routes.  For every route r with local expert e in [0, L):
@@ -349,7 +382,6 @@ void oracle_grouped_gemm(const uint8_t* A, const float* A_s, int a_row_div,
                          uint16_t* C)
 {
     int G = K / ORACLE_GROUP;
-#pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < R; r++) {
         int64_t e = (int64_t)topk_ids[r] - expert_offset;
         if (e < 0 || e >= L) continue;
@@ -357,6 +389,27 @@ void oracle_grouped_gemm(const uint8_t* A, const float* A_s, int a_row_div,
         gemm_row(A + (size_t)arow * K, A_s + (size_t)arow * G,
                  B + (size_t)e * N * K, B_s + (size_t)e * (N / ORACLE_GROUP) * G,
                  N, K, C + (size_t)r * N);
+    }
+}
+
+/* The same grouped GEMM before its BF16 rounding: acc[r, n] is gemm_dot's fp64
+ * value and mag[r, n] its magnitude bound (both [R, N] doubles; rows of
+ * dropped routes untouched).  Test infrastructure: a GPU result whose fp32
+ * accumulation may land on either side of a BF16 rounding boundary is told
+ * apart from a wrong one by these two numbers. */
+void oracle_grouped_gemm_f64(const uint8_t* A, const float* A_s, int a_row_div,
+                             const uint8_t* B, const float* B_s, int N, int K,
+                             const int32_t* topk_ids, int64_t R, int expert_offset, int L,
+                             double* acc, double* mag)
+{
+    int G = K / ORACLE_GROUP;
+    for (int64_t r = 0; r < R; r++) {
+        int64_t e = (int64_t)topk_ids[r] - expert_offset;
+        if (e < 0 || e >= L) continue;
+        int64_t arow = r / a_row_div;
+        gemm_row_ex(A + (size_t)arow * K, A_s + (size_t)arow * G,
+                    B + (size_t)e * N * K, B_s + (size_t)e * (N / ORACLE_GROUP) * G,
+                    N, K, NULL, acc + (size_t)r * N, mag + (size_t)r * N);
     }
 }
 
@@ -483,40 +536,36 @@ void oracle_fused_moe(const uint16_t* hidden, int64_t M, int H,
 {
     int GH = H / ORACLE_GROUP, GI = I / ORACLE_GROUP;
     if (!tokens) n_tokens = M;
-#pragma omp parallel
-    {
-        uint8_t* aq = (uint8_t*)malloc((size_t)H);
-        float* as = (float*)malloc(sizeof(float) * (size_t)GH);
-        uint16_t* h13 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)2 * I);
-        uint8_t* q = (uint8_t*)malloc((size_t)I);
-        float* s = (float*)malloc(sizeof(float) * (size_t)GI);
-        uint16_t* y = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)k * H);
-        float* w = (float*)malloc(sizeof(float) * (size_t)k);
-        int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
-#pragma omp for schedule(dynamic, 1)
-        for (int64_t ti = 0; ti < n_tokens; ti++) {
-            int64_t t = tokens ? tokens[ti] : ti;
-            oracle_quant_fp8(hidden + (size_t)t * H, 1, H, scale_fmt, aq, as);
-            for (int j = 0; j < k; j++) {
-                int64_t r = t * k + j;
-                ids[j] = topk_ids[r];
-                w[j] = topk_w[r];
-                int64_t e = (int64_t)topk_ids[r] - expert_offset;
-                if (e < 0 || e >= L) continue;
-                gemm_row(aq, as, w13 + (size_t)e * 2 * I * H, w13_s + (size_t)e * (2 * I / ORACLE_GROUP) * GH,
-                         2 * I, H, h13);
-                oracle_silu_and_mul_quant_fp8(h13, 1, I, NULL, NULL, 0, clamp_limit, scale_fmt, q, s);
-                gemm_row(q, s, w2 + (size_t)e * H * I, w2_s + (size_t)e * GH * GI, H, I, y + (size_t)j * H);
-                if (h13_out) memcpy(h13_out + (size_t)r * 2 * I, h13, sizeof(uint16_t) * 2 * I);
-                if (q_out) memcpy(q_out + (size_t)r * I, q, (size_t)I);
-                if (s_out) memcpy(s_out + (size_t)r * GI, s, sizeof(float) * GI);
-                if (y_out) memcpy(y_out + (size_t)r * H, y + (size_t)j * H, sizeof(uint16_t) * H);
-            }
-            /* reduce this token's k routes; ids are re-based to a single token */
-            oracle_moe_reduce(y, w, ids, expert_offset, L, 1, k, H, out + (size_t)t * H);
+    uint8_t* aq = (uint8_t*)malloc((size_t)H);
+    float* as = (float*)malloc(sizeof(float) * (size_t)GH);
+    uint16_t* h13 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)2 * I);
+    uint8_t* q = (uint8_t*)malloc((size_t)I);
+    float* s = (float*)malloc(sizeof(float) * (size_t)GI);
+    uint16_t* y = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)k * H);
+    float* w = (float*)malloc(sizeof(float) * (size_t)k);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    for (int64_t ti = 0; ti < n_tokens; ti++) {
+        int64_t t = tokens ? tokens[ti] : ti;
+        oracle_quant_fp8(hidden + (size_t)t * H, 1, H, scale_fmt, aq, as);
+        for (int j = 0; j < k; j++) {
+            int64_t r = t * k + j;
+            ids[j] = topk_ids[r];
+            w[j] = topk_w[r];
+            int64_t e = (int64_t)topk_ids[r] - expert_offset;
+            if (e < 0 || e >= L) continue;
+            gemm_row(aq, as, w13 + (size_t)e * 2 * I * H, w13_s + (size_t)e * (2 * I / ORACLE_GROUP) * GH,
+                     2 * I, H, h13);
+            oracle_silu_and_mul_quant_fp8(h13, 1, I, NULL, NULL, 0, clamp_limit, scale_fmt, q, s);
+            gemm_row(q, s, w2 + (size_t)e * H * I, w2_s + (size_t)e * GH * GI, H, I, y + (size_t)j * H);
+            if (h13_out) memcpy(h13_out + (size_t)r * 2 * I, h13, sizeof(uint16_t) * 2 * I);
+            if (q_out) memcpy(q_out + (size_t)r * I, q, (size_t)I);
+            if (s_out) memcpy(s_out + (size_t)r * GI, s, sizeof(float) * GI);
+            if (y_out) memcpy(y_out + (size_t)r * H, y + (size_t)j * H, sizeof(uint16_t) * H);
         }
-        free(aq); free(as); free(h13); free(q); free(s); free(y); free(w); free(ids);
+        /* reduce this token's k routes; ids are re-based to a single token */
+        oracle_moe_reduce(y, w, ids, expert_offset, L, 1, k, H, out + (size_t)t * H);
     }
+    free(aq); free(as); free(h13); free(q); free(s); free(y); free(w); free(ids);
 }
 
 /* Threads OpenMP would use (for reporting the CPU baseline's core count),

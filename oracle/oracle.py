@@ -55,6 +55,7 @@ def lib():
             "oracle_max_blocks": (i64, [i64, i32, i32]),
             "oracle_route_prepare": (i64, [P, i64, i32, i32, i32, P, P, P, P, i64, P]),
             "oracle_grouped_gemm": (None, [P, P, i32, P, P, i32, i32, P, i64, i32, i32, P]),
+            "oracle_grouped_gemm_f64": (None, [P, P, i32, P, P, i32, i32, P, i64, i32, i32, P, P]),
             "oracle_moe_reduce": (None, [P, P, P, i32, i32, i64, i32, i32, P]),
             "oracle_sigmoid_rn": (f32, [f32]),
             "oracle_router_topk": (None, [P, i64, i32, i32, i32, P, i32, ctypes.c_double, P, P]),
@@ -195,6 +196,22 @@ def grouped_gemm(A, A_s, a_row_div: int, B, B_s, topk_ids, expert_offset: int, L
     lib().oracle_grouped_gemm(_p(A), _p(A_s), a_row_div, _p(B), _p(B_s), N, K, _p(ids), R,
                               expert_offset, L, _p(C))
     return C
+
+
+def grouped_gemm_f64(A, A_s, a_row_div: int, B, B_s, topk_ids, expert_offset: int, L: int):
+    """The grouped GEMM before its BF16 rounding: ([R, N] fp64 values, [R, N]
+    fp64 magnitude bounds sum |scale products| * |code products|).  Rows of
+    dropped routes are NaN."""
+    A = as_np(A, np.uint8); A_s = as_np(A_s, np.float32)
+    B = as_np(B, np.uint8); B_s = as_np(B_s, np.float32)
+    ids = as_np(topk_ids, np.int32).reshape(-1)
+    N, K = B.shape[1], B.shape[2]
+    R = ids.size
+    acc = np.full((R, N), np.nan)
+    mag = np.full((R, N), np.nan)
+    lib().oracle_grouped_gemm_f64(_p(A), _p(A_s), a_row_div, _p(B), _p(B_s), N, K, _p(ids), R,
+                                  expert_offset, L, _p(acc), _p(mag))
+    return acc, mag
 
 
 def moe_reduce(y_bf16, topk_w, topk_ids=None, expert_offset: int = 0, L: int = 1 << 30):

@@ -26,3 +26,17 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _bounded_waits_never_ran_out(request):
+    """After every GPU test: no kernel's bounded wait ran out (the device fault
+    bits the library keeps are clear), then clear them for the next test."""
+    yield
+    if "gpu" not in request.keywords:
+        return
+    import torch
+    if not torch.cuda.is_available():
+        return
+    import block_fp8_mixture_route_amd as bfp8
+    assert bfp8.wait_faults(clear=True) == 0, "a kernel's bounded wait ran out during this test"
