@@ -17,7 +17,9 @@ from ._lib import (  # noqa: F401
     SCORE_SIGMOID,
     SCORE_SOFTMAX,
     Opts,
+    NOALLOC_SCRATCH_BYTES,
     fused_moe_block_fp8,
+    fused_moe_block_fp8_noalloc,
     fused_moe_block_fp8_routed,
     fused_moe_stages,
     fused_moe_workspace_size,

@@ -76,6 +76,8 @@ SIGNATURES = {
                                           ctypes.POINTER(ctypes.c_char_p), _i32]),
     "fused_moe_block_fp8": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32,
                                            ctypes.POINTER(Opts), _P, _P, _sz, _P]),
+    "fused_moe_block_fp8_noalloc": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32,
+                                                   ctypes.POINTER(Opts), _P, _P]),
     "fused_moe_block_fp8_routed": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _i32, ctypes.c_double, _i32, _P, _P,
                                                   _P, _P, _P, _P, _i32, _i32, ctypes.POINTER(Opts), _P, _P, _sz, _P]),
 }
@@ -356,6 +358,26 @@ def fused_moe_block_fp8(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, 
     check(lib().fused_moe_block_fp8(ptr(_u16(hidden)), M, H, ptr(topk_ids), ptr(topk_w), k, ptr(w13),
                                     ptr(w13_scale), ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o),
                                     ptr(_u16(out)), ptr(ws), ws.numel(), stream_of(hidden.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def fused_moe_block_fp8_noalloc(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, E=None, o: Opts = None,
+                                out=None):
+    """fused_moe_block_fp8 on the library's own per-device scratch array (the
+    C entry point allocates nothing; pass `out` to allocate nothing here
+    either).  Calls that overlap on one GPU race."""
+    E = w13.shape[0] if E is None else E
+    o = opts() if o is None else o
+    M, H, k, I = _check_layer_buffers(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, E, o, out, None)
+    _require_device(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, out)
+    w13, w2 = _u8(w13), _u8(w2)
+    out = torch.empty(M, H, dtype=torch.bfloat16, device=hidden.device) if out is None else out
+    check(lib().fused_moe_block_fp8_noalloc(ptr(_u16(hidden)), M, H, ptr(topk_ids), ptr(topk_w), k, ptr(w13),
+                                            ptr(w13_scale), ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o),
+                                            ptr(_u16(out)), stream_of(hidden.device)))
     return out
 
 

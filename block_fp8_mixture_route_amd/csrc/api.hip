@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/bfp8moe.h"
@@ -539,3 +540,68 @@ bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, i
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The layer without a workspace argument, for callers that cannot allocate.
+// Its workspace is `scratch`, a file-scope device array: each GPU the library
+// runs on holds its own copy for the life of the process.  In host code the
+// array's name is a host-side stand-in, so its device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and only
+// that address is handed to kernels.
+
+static __device__ __align__(256) uint8_t scratch[BFP8MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on each device).
+bfp8moe_status_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BFP8MOE_ERR_UNSUPPORTED, "fused_moe_block_fp8_noalloc: device %d beyond the %d the library tracks",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8_noalloc: hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(BFP8MOE_ERR_HIP, "fused_moe_block_fp8_noalloc: null scratch address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BFP8MOE_OK;
+}
+
+}  // namespace
+
+extern "C" bfp8moe_status_t fused_moe_block_fp8_noalloc(const uint16_t* hidden, int64_t M, int32_t H,
+                                                        const int32_t* topk_ids, const float* topk_w, int32_t k,
+                                                        const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
+                                                        const float* w2_scale, int32_t E, int32_t I,
+                                                        const bfp8moe_opts_t* opts, uint16_t* out, void* stream) {
+  bfp8moe_opts_t o;
+  bfp8moe_opts_init(&o);
+  if (opts) o = *opts;
+  {
+    const bfp8moe_status_t st = check_layer_shape(M, H, k, E, I, o);
+    if (st != BFP8MOE_OK) return st;
+  }
+  LayerPlan p;
+  plan_layer(p, M, H, k, E, I, o);
+  if (p.total > (size_t)BFP8MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(BFP8MOE_ERR_WORKSPACE,
+                "fused_moe_block_fp8_noalloc: this call needs %zu bytes of scratch, the limit is %zu; "
+                "use fused_moe_block_fp8 with a workspace",
+                p.total, (size_t)BFP8MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const bfp8moe_status_t st = scratch_address(&ws);
+  if (st != BFP8MOE_OK) return st;
+  return fused_moe_block_fp8(hidden, M, H, topk_ids, topk_w, k, w13, w13_scale, w2, w2_scale, E, I, &o, out, ws,
+                             (size_t)BFP8MOE_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -349,6 +349,25 @@ bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, i
                                             const float* w2_scale, int32_t E, int32_t I, const bfp8moe_opts_t* opts,
                                             uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fused_moe_block_fp8 with the same arguments and results, whose workspace is
+ * a device array the library holds, BFP8MOE_NOALLOC_SCRATCH_BYTES per GPU for
+ * the life of the process (its address is looked up on the first call on each
+ * device).  The call allocates nothing; the caller still passes inputs and
+ * the output.  A call whose workspace (fused_moe_block_fp8_workspace_size)
+ * exceeds the limit returns BFP8MOE_ERR_WORKSPACE, having launched nothing.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, different host threads) race and must be
+ * serialised by the caller.  The array needs no initialisation and keeps the
+ * last call's intermediates. */
+#define BFP8MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+bfp8moe_status_t fused_moe_block_fp8_noalloc(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
+                                             const float* topk_w, int32_t k, const uint8_t* w13,
+                                             const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                                             int32_t E, int32_t I, const bfp8moe_opts_t* opts, uint16_t* out,
+                                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif
