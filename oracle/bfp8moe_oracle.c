@@ -512,6 +512,84 @@ void oracle_router_topk(const float* logits, int64_t M, int E, int k, int score_
 }
 
 /* ------------------------------------------------------------------------- */
+/* Group-limited noaux-TC router                                               */
+/* [P2 Reviewed changes: route_noaux_tc.py, a noaux-TC routing kernel, which   */
+/*  the MoE router switches to]                                                */
+/* The pages name the method only.  Reading (the published auxiliary-loss-free */
+/* routing with a per-expert selection bias and group-limited selection):      */
+/* sigmoid scores; each expert's choice key is its score plus its bias; the E  */
+/* experts form n_group groups of E / n_group consecutive ids; a group's score */
+/* is the sum of its two largest keys (its one key when groups have one       */
+/* expert); the topk_group best groups are kept; the k largest keys among     */
+/* their experts are chosen; weights come from the unbiased scores.           */
+/* ------------------------------------------------------------------------- */
+
+/* logits: [M, E] fp32; bias: [E] fp32 or NULL; topk_ids / topk_w: [M, k].
+ * Keys: RN32(sigmoid_rn(l_e) + bias_e) (sigmoid_rn alone without a bias).
+ * Group score: RN32(key_a + key_b), key_a >= key_b the two largest keys of the
+ * group.  Groups are chosen one at a time, largest score first, equal scores
+ * to the lower group index; experts likewise among the chosen groups, equal
+ * keys to the lower expert id.  Weights as oracle_router_topk's sigmoid
+ * scoring: 1 / (1 + exp(-l_j)) in fp64, divided by their sum over the k chosen
+ * when renormalize is set, times scale, rounded once to fp32.
+ * Requires E % n_group == 0, 1 <= topk_group <= n_group and
+ * 1 <= k <= topk_group * (E / n_group). */
+void oracle_router_noaux_tc(const float* logits, int64_t M, int E, int k, int n_group, int topk_group,
+                            const float* bias, int renormalize, double scale, int32_t* topk_ids, float* topk_w)
+{
+    int gs = E / n_group;
+    float* key = (float*)malloc(sizeof(float) * (size_t)E);
+    float* gscore = (float*)malloc(sizeof(float) * (size_t)n_group);
+    char* gsel = (char*)malloc((size_t)n_group);
+    char* taken = (char*)malloc((size_t)E);
+    double* v = (double*)malloc(sizeof(double) * (size_t)k);
+    for (int64_t t = 0; t < M; t++) {
+        const float* lg = logits + (size_t)t * E;
+        int32_t* ids = topk_ids + (size_t)t * k;
+        for (int e = 0; e < E; e++) {
+            float sc = oracle_sigmoid_rn(lg[e]);
+            key[e] = bias ? sc + bias[e] : sc;
+        }
+        /* group scores: the two largest keys of each group, added in fp32 */
+        for (int g = 0; g < n_group; g++) {
+            int a = -1, b = -1;
+            for (int e = g * gs; e < (g + 1) * gs; e++) {
+                if (a < 0 || key[e] > key[a]) { b = a; a = e; }
+                else if (b < 0 || key[e] > key[b]) { b = e; }
+            }
+            gscore[g] = b < 0 ? key[a] : key[a] + key[b];
+        }
+        /* the topk_group best groups */
+        memset(gsel, 0, (size_t)n_group);
+        for (int j = 0; j < topk_group; j++) {
+            int best = -1;
+            for (int g = 0; g < n_group; g++) {
+                if (gsel[g]) continue;
+                if (best < 0 || gscore[g] > gscore[best]) best = g;
+            }
+            gsel[best] = 1;
+        }
+        /* the k largest keys among the chosen groups' experts */
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; j++) {
+            int best = -1;
+            for (int e = 0; e < E; e++) {
+                if (taken[e] || !gsel[e / gs]) continue;
+                if (best < 0 || key[e] > key[best]) best = e;
+            }
+            taken[best] = 1;
+            ids[j] = best;
+        }
+        double z = 0.0;
+        for (int j = 0; j < k; j++) v[j] = 1.0 / (1.0 + exp(-(double)lg[ids[j]]));
+        if (renormalize) for (int j = 0; j < k; j++) z += v[j];
+        else z = 1.0;
+        for (int j = 0; j < k; j++) topk_w[(size_t)t * k + j] = (float)(v[j] / z * scale);
+    }
+    free(v); free(taken); free(gsel); free(gscore); free(key);
+}
+
+/* ------------------------------------------------------------------------- */
 /* Whole layer for a subset of tokens                                          */
 /* [P1 Modification: gate/up GEMM -> silu_and_mul_post_quant -> FP8 activation  */
 /*  + scale -> down GEMM]; [P4: moe_reduce applies the router weights]          */

@@ -59,6 +59,7 @@ def lib():
             "oracle_moe_reduce": (None, [P, P, P, i32, i32, i64, i32, i32, P]),
             "oracle_sigmoid_rn": (f32, [f32]),
             "oracle_router_topk": (None, [P, i64, i32, i32, i32, P, i32, ctypes.c_double, P, P]),
+            "oracle_router_noaux_tc": (None, [P, i64, i32, i32, i32, i32, P, i32, ctypes.c_double, P, P]),
             "oracle_fused_moe": (None, [P, i64, i32, P, P, i32, P, P, P, P, i32, i32, i32, i32, f32,
                                         P, i64, P, P, P, P, P]),
             "oracle_num_threads": (i32, []),
@@ -243,6 +244,24 @@ def router_topk(logits, k: int, score_fn: int = SCORE_SOFTMAX, bias=None, renorm
     ids = np.zeros((M, k), np.int32)
     w = np.zeros((M, k), np.float32)
     lib().oracle_router_topk(_p(lg), M, E, k, score_fn, _p(b), int(bool(renormalize)), float(scale), _p(ids), _p(w))
+    return ids, w
+
+
+def router_noaux_tc(logits, k: int, n_group: int, topk_group: int, bias=None, renormalize: bool = True,
+                    scale: float = 1.0):
+    """Group-limited noaux-TC routing of [M, E] fp32 logits: ([M, k] int32 ids,
+    largest key first, [M, k] fp32 weights)."""
+    lg = as_np(logits, np.float32)
+    M, E = lg.shape
+    if n_group < 1 or E % n_group or not 1 <= topk_group <= n_group or not 1 <= k <= topk_group * (E // n_group):
+        raise ValueError(f"bad grouping: E={E} n_group={n_group} topk_group={topk_group} k={k}")
+    b = None if bias is None else as_np(bias, np.float32)
+    if b is not None and b.size != E:
+        raise ValueError("the selection bias needs one value per expert")
+    ids = np.zeros((M, k), np.int32)
+    w = np.zeros((M, k), np.float32)
+    lib().oracle_router_noaux_tc(_p(lg), M, E, k, n_group, topk_group, _p(b), int(bool(renormalize)), float(scale),
+                                 _p(ids), _p(w))
     return ids, w
 
 
