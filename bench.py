@@ -391,7 +391,7 @@ def routed_table(hip, stream, dev):
         def routed(x):
             m = x["mw"]
             bfp8._lib.check(L_.fused_moe_block_fp8_routed(
-                P(x["hid"].data_ptr()), c.M, c.H, P(x["lg"].data_ptr()), None, bfp8.SCORE_SOFTMAX, 1, 1.0, c.k,
+                P(x["hid"].data_ptr()), c.M, c.H, P(x["lg"].data_ptr()), None, bfp8.SCORE_SOFTMAX, 1, 1.0, 1, 1, c.k,
                 P(x["ids"].data_ptr()), P(x["w"].data_ptr()), P(m.w13.data_ptr()), P(m.w13_s.data_ptr()),
                 P(m.w2.data_ptr()), P(m.w2_s.data_ptr()), c.E, c.I, ctypes.byref(o), P(x["out"].data_ptr()),
                 P(x["ws"].data_ptr()), x["ws"].numel(), stream))

@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     moe_route_prepare,
     opts,
     quant_fp8,
+    router_noaux_tc,
     router_topk,
     silu_and_mul,
     silu_and_mul_quant_fp8,

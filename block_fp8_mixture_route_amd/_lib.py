@@ -71,6 +71,8 @@ SIGNATURES = {
                                             _i64, _P, _P]),
     "moe_reduce": (ctypes.c_int, [_P, _P, _P, _i32, _i32, _i64, _i32, _i32, _P, _P]),
     "moe_router_topk": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _P, _i32, ctypes.c_double, _P, _P, _P]),
+    "moe_router_noaux_tc": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _i32, _P, _i32, ctypes.c_double, _P, _P,
+                                           _P]),
     "fused_moe_block_fp8_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(Opts)]),
     "fused_moe_block_fp8_stages": (_i32, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(Opts),
                                           ctypes.POINTER(ctypes.c_char_p), _i32]),
@@ -78,7 +80,8 @@ SIGNATURES = {
                                            ctypes.POINTER(Opts), _P, _P, _sz, _P]),
     "fused_moe_block_fp8_noalloc": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32,
                                                    ctypes.POINTER(Opts), _P, _P]),
-    "fused_moe_block_fp8_routed": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _i32, ctypes.c_double, _i32, _P, _P,
+    "fused_moe_block_fp8_routed": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _i32, ctypes.c_double, _i32, _i32,
+                                                  _i32, _P, _P,
                                                   _P, _P, _P, _P, _i32, _i32, ctypes.POINTER(Opts), _P, _P, _sz, _P]),
 }
 
@@ -304,6 +307,21 @@ def router_topk(logits, k, score_fn=SCORE_SOFTMAX, bias=None, renormalize=True, 
     return ids, w
 
 
+def router_noaux_tc(logits, k, n_group, topk_group, bias=None, renormalize=True, scale=1.0, topk_ids=None,
+                    topk_w=None):
+    """Group-limited noaux-TC routing of [M, E] fp32 logits -> ([M, k] int32
+    ids, largest key first, [M, k] fp32 weights)."""
+    _expect(logits, "logits", torch.float32, (None, None))
+    M, E = logits.shape
+    _check_router_buffers(E, k, M, bias, topk_ids, topk_w)
+    _require_device(logits, bias, topk_ids, topk_w)
+    ids = torch.empty(M, k, dtype=torch.int32, device=logits.device) if topk_ids is None else topk_ids
+    w = torch.empty(M, k, dtype=torch.float32, device=logits.device) if topk_w is None else topk_w
+    check(lib().moe_router_noaux_tc(ptr(logits), M, E, k, n_group, topk_group, ptr(bias), int(bool(renormalize)),
+                                    float(scale), ptr(ids), ptr(w), stream_of(logits.device)))
+    return ids, w
+
+
 def fused_moe_workspace_size(M, H, k, E, I, o: Opts) -> int:
     return lib().fused_moe_block_fp8_workspace_size(M, H, k, E, I, ctypes.byref(o))
 
@@ -383,7 +401,7 @@ def fused_moe_block_fp8_noalloc(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2
 
 def fused_moe_block_fp8_routed(hidden, router_logits, k, w13, w13_scale, w2, w2_scale, score_fn=SCORE_SOFTMAX,
                                bias=None, renormalize=True, scale=1.0, o: Opts = None, out=None, ws=None,
-                               topk_ids=None, topk_w=None):
+                               topk_ids=None, topk_w=None, n_group=1, topk_group=1):
     """Router and layer in one call: returns (out [M, H] BF16, topk_ids [M, k]
     int32, topk_w [M, k] fp32)."""
     _expect(hidden, "hidden", torch.bfloat16, (None, None))
@@ -406,7 +424,7 @@ def fused_moe_block_fp8_routed(hidden, router_logits, k, w13, w13_scale, w2, w2_
     ids = torch.empty(M, k, dtype=torch.int32, device=hidden.device) if topk_ids is None else topk_ids
     w = torch.empty(M, k, dtype=torch.float32, device=hidden.device) if topk_w is None else topk_w
     check(lib().fused_moe_block_fp8_routed(ptr(_u16(hidden)), M, H, ptr(router_logits), ptr(bias), score_fn,
-                                           int(bool(renormalize)), float(scale), k, ptr(ids), ptr(w), ptr(w13),
+                                           int(bool(renormalize)), float(scale), n_group, topk_group, k, ptr(ids), ptr(w), ptr(w13),
                                            ptr(w13_scale), ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o),
                                            ptr(_u16(out)), ptr(ws), ws.numel(), stream_of(hidden.device)))
     return out, ids, w

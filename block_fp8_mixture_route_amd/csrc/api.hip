@@ -322,6 +322,23 @@ bfp8moe_status_t moe_router_topk(const float* logits, int64_t M, int32_t E, int3
                     "moe_router_topk");
 }
 
+bfp8moe_status_t moe_router_noaux_tc(const float* logits, int64_t M, int32_t E, int32_t k, int32_t n_group,
+                                     int32_t topk_group, const float* bias, int32_t renormalize, double scale,
+                                     int32_t* topk_ids, float* topk_w, void* stream) {
+  REQUIRE(M >= 0 && M <= 4 * (int64_t)0x7FFFFFFF, "M=%lld out of range", (long long)M);
+  REQUIRE(E >= 1 && E <= 1024, "E=%d must be in [1, 1024]", E);
+  REQUIRE(n_group >= 1 && n_group <= 64 && E % n_group == 0, "n_group=%d must divide E=%d and be in [1, 64]",
+          n_group, E);
+  REQUIRE(topk_group >= 1 && topk_group <= n_group, "topk_group=%d must be in [1, n_group=%d]", topk_group, n_group);
+  REQUIRE(k >= 1 && k <= 64 && (int64_t)k <= (int64_t)topk_group * (E / n_group),
+          "k=%d must be in [1, min(64, topk_group * E / n_group)]", k);
+  REQUIRE(isfinite(scale), "scale must be finite");
+  REQUIRE(M == 0 || (logits && topk_ids && topk_w), "logits, topk_ids and topk_w must be non-null");
+  return hip_status(bfp8::launch_router_noaux_tc(logits, M, E, k, n_group, topk_group, bias, renormalize != 0, scale,
+                                                 topk_ids, topk_w, (hipStream_t)stream),
+                    "moe_router_noaux_tc");
+}
+
 }  // extern "C"
 
 namespace {
@@ -492,7 +509,8 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
 
 bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, int32_t H, const float* router_logits,
                                             const float* router_bias, int32_t score_fn, int32_t renormalize,
-                                            double routed_scale, int32_t k, int32_t* topk_ids, float* topk_w,
+                                            double routed_scale, int32_t n_group, int32_t topk_group, int32_t k,
+                                            int32_t* topk_ids, float* topk_w,
                                             const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
                                             const float* w2_scale, int32_t E, int32_t I, const bfp8moe_opts_t* opts,
                                             uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
@@ -504,6 +522,12 @@ bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, i
   REQUIRE(score_fn == BFP8MOE_SCORE_SOFTMAX || score_fn == BFP8MOE_SCORE_SIGMOID, "score_fn=%d invalid", score_fn);
   REQUIRE(router_bias == nullptr || score_fn == BFP8MOE_SCORE_SIGMOID, "a selection bias needs sigmoid scoring");
   REQUIRE(isfinite(routed_scale), "routed_scale must be finite");
+  REQUIRE(n_group >= 1 && n_group <= 64 && E % n_group == 0, "n_group=%d must divide E=%d and be in [1, 64]",
+          n_group, E);
+  REQUIRE(n_group == 1 || score_fn == BFP8MOE_SCORE_SIGMOID, "grouped (noaux-TC) selection uses sigmoid scoring");
+  REQUIRE(topk_group >= 1 && topk_group <= n_group, "topk_group=%d must be in [1, n_group=%d]", topk_group, n_group);
+  REQUIRE((int64_t)k <= (int64_t)topk_group * (E / n_group), "k=%d exceeds the experts of %d groups", k,
+          topk_group);
   REQUIRE(o.stage_events == nullptr && ((o.flags >> BFP8MOE_FLAG_STAGE_SHIFT) & 15u) == 0,
           "the routed layer takes no stage events or stage selection");
   {
@@ -524,7 +548,7 @@ bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, i
   if (p.mode == kModeToken && E <= bfp8::kFoldedRouterMaxE && M <= bfp8::kFoldedRouterMaxM) {
     uint16_t* act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.off_act);
     const bfp8::RouterArgs ra{router_logits, router_bias, topk_ids, topk_w, routed_scale, E, score_fn,
-                              renormalize != 0};
+                              renormalize != 0, n_group, topk_group};
     return hip_status(bfp8::launch_token_layer(hidden, M, H, topk_ids, topk_w, k, p.offset, p.L, w13, w13_scale, w2,
                                                w2_scale, I, p.fmt, p.clamp, act, out, (hipStream_t)stream, nullptr,
                                                &ra),
@@ -532,8 +556,10 @@ bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, i
   }
   // other paths: the router's own launch, then the layer
   const bfp8moe_status_t rs =
-      moe_router_topk(router_logits, M, E, k, score_fn, router_bias, renormalize, routed_scale, topk_ids, topk_w,
-                      stream);
+      n_group > 1 ? moe_router_noaux_tc(router_logits, M, E, k, n_group, topk_group, router_bias, renormalize,
+                                        routed_scale, topk_ids, topk_w, stream)
+                  : moe_router_topk(router_logits, M, E, k, score_fn, router_bias, renormalize, routed_scale,
+                                    topk_ids, topk_w, stream);
   if (rs != BFP8MOE_OK) return rs;
   return fused_moe_block_fp8(hidden, M, H, topk_ids, topk_w, k, w13, w13_scale, w2, w2_scale, E, I, &o, out, ws,
                              ws_bytes, stream);

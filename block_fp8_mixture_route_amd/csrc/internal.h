@@ -60,6 +60,8 @@ struct RouterArgs {
   int E;
   int score_fn;
   int renorm;
+  int n_group;     // > 1: group-limited (noaux-TC) selection, sigmoid scoring
+  int topk_group;
 };
 // Largest expert count the folded router handles (four experts per lane).
 constexpr int kFoldedRouterMaxE = 256;
@@ -73,6 +75,11 @@ constexpr int64_t kFoldedRouterMaxM = 4;
 
 hipError_t launch_router_topk(const float* logits, int64_t M, int E, int k, int score_fn, const float* bias,
                               int renorm, double scale, int32_t* ids, float* w, hipStream_t stream);
+// Group-limited noaux-TC routing (sigmoid scores; n_group <= 1 is the
+// single-group sigmoid router).
+hipError_t launch_router_noaux_tc(const float* logits, int64_t M, int E, int k, int n_group, int topk_group,
+                                  const float* bias, int renorm, double scale, int32_t* ids, float* w,
+                                  hipStream_t stream);
 
 hipError_t launch_moe_reduce(const uint16_t* y, const float* w, const int32_t* ids, int32_t offset, int32_t L,
                              int64_t M, int k, int H, uint16_t* out, hipStream_t stream);

@@ -1,13 +1,18 @@
-// router.h -- wave-level pieces of the single-group top-k router, shared by
-// the router kernel and the few-token layer kernel that routes for itself.
+// router.h -- wave-level pieces of the top-k routers, shared by the router
+// kernel and the few-token layer kernel that routes for itself.
 //
 // [P2 Changes: a fused single-group top-k router; renormalize option]
+// [P2 Reviewed changes: route_noaux_tc.py, group-limited noaux-TC routing]
 //   [P2] lmdeploy PR "perf(pytorch): optimize compact blocked FP8 MoE and route
 //        preparation"
 //
 // One wave routes one token.  Lane l holds experts l, l + 64, ... (NPL of
-// them).  Each expert's score becomes an order-preserving unsigned integer
-// (-0 taken as +0); each lane sorts its keys once.  Each round takes the
+// them).  With groups (noaux-TC), the keys of experts outside the chosen
+// groups are retired before the sort: each lane g < n_group scores group g
+// (the fp32 sum of its two largest keys, read from LDS), and topk_group
+// rounds of wave maxima pick the groups (the lowest index among equal scores).
+// Each expert's score becomes an order-preserving unsigned integer (-0 taken
+// as +0); each lane sorts its keys once.  Each round takes the
 // largest of the lanes' heads (DPP-fused maxima within 16-lane rows, row
 // broadcasts across them, one readlane); a ballot finds the lane holding it
 // (a minimum over expert ids settles equal heads), and that lane pops it.
@@ -96,8 +101,12 @@ struct WaveRoute {
   int id[NPL];        // expert id of each sorted key
   float sv[NPL];      // logit of each sorted key
 
-  __device__ __forceinline__ void load(const float* lg, int E, int score_fn, const float* bias, int lane) {
-    float b[NPL];
+  // n_group > 1: keep only the experts of the topk_group best groups of
+  // E / n_group consecutive experts (n_group <= 64); s_key: E floats of LDS
+  // private to this wave.
+  __device__ __forceinline__ void load(const float* lg, int E, int score_fn, const float* bias, int lane,
+                                       int n_group = 1, int topk_group = 1, float* s_key = nullptr) {
+    float b[NPL], sc[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; i++) v[i] = lg[min(lane + 64 * i, E - 1)];
     if (score_fn == kScoreSigmoid && bias) {
@@ -111,9 +120,41 @@ struct WaveRoute {
         s = sigmoid_rn(v[i]);
         if (bias) s = s + b[i];
       }
+      sc[i] = s;
       key[i] = lane + 64 * i < E ? order_bits(s) : 0u;
       id[i] = lane + 64 * i;
       sv[i] = v[i];
+    }
+    if (n_group > 1) {
+      const int gs = E / n_group;
+#pragma unroll
+      for (int i = 0; i < NPL; i++)
+        if (lane + 64 * i < E) s_key[lane + 64 * i] = sc[i];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
+      uint32_t gkey = 0u;
+      if (lane < n_group) {
+        float a = -__builtin_inff(), c = -__builtin_inff();
+        for (int e = lane * gs; e < (lane + 1) * gs; e++) {
+          const float x = s_key[e];
+          if (x > a) {
+            c = a;
+            a = x;
+          } else if (x > c) {
+            c = x;
+          }
+        }
+        gkey = order_bits(gs > 1 ? a + c : a);
+      }
+      uint64_t chosen = 0;
+      for (int j = 0; j < topk_group; j++) {
+        const uint32_t top = wave_max_u32(gkey);
+        const int wl = (int)__builtin_ctzll(__ballot(gkey == top));  // lowest group among equal scores
+        chosen |= 1ull << wl;
+        if (lane == wl) gkey = 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < NPL; i++)
+        if (lane + 64 * i < E && !((chosen >> ((lane + 64 * i) / gs)) & 1ull)) key[i] = 0u;
     }
     // odd-even transposition sort, largest first; a swap only on a strictly
     // smaller key keeps equal keys in ascending id order

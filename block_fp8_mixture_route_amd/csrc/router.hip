@@ -1,7 +1,9 @@
-// router.hip -- single-group top-k router for gfx950: router logits [M, E]
-// fp32 -> the k chosen experts per token (largest first) and their weights.
+// router.hip -- top-k routers for gfx950: router logits [M, E] fp32 -> the k
+// chosen experts per token (largest first) and their weights; single-group,
+// and group-limited noaux-TC.
 //
 // [P2 Changes: a fused single-group top-k router; renormalize option]
+// [P2 Reviewed changes: route_noaux_tc.py, a noaux-TC routing kernel]
 //   [P2] lmdeploy PR "perf(pytorch): optimize compact blocked FP8 MoE and route
 //        preparation"
 //
@@ -25,17 +27,23 @@ constexpr int kTokensPerWG = kRouterThreads / 64;
 // four times longer.
 constexpr int64_t kRowsMinM = 8192;
 
-template <int NPL>
+template <int NPL, bool kGrouped>
 __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(const float* __restrict__ logits, int64_t M,
                                                                      int E, int k, int score_fn,
                                                                      const float* __restrict__ bias, int renorm,
                                                                      double scale, int32_t* __restrict__ ids,
-                                                                     float* __restrict__ w) {
+                                                                     float* __restrict__ w, int n_group,
+                                                                     int topk_group) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kTokensPerWG + (threadIdx.x >> 6);
   if (t >= M) return;  // whole waves only: the reductions need all 64 lanes
   router::WaveRoute<NPL> r;
-  r.load(logits + t * (int64_t)E, E, score_fn, bias, lane);
+  if constexpr (kGrouped) {
+    __shared__ float s_key[kTokensPerWG][64 * NPL];  // each wave's choice keys
+    r.load(logits + t * (int64_t)E, E, score_fn, bias, lane, n_group, topk_group, s_key[threadIdx.x >> 6]);
+  } else {
+    r.load(logits + t * (int64_t)E, E, score_fn, bias, lane);
+  }
   // k rounds; lane j keeps winner j
   int my_id = 0;
   float my_logit = 0.0f;
@@ -170,10 +178,15 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_rows_kernel(const 
 
 template <int NPL>
 hipError_t launch_npl(const float* logits, int64_t M, int E, int k, int score_fn, const float* bias, int renorm,
-                      double scale, int32_t* ids, float* w, hipStream_t stream) {
+                      double scale, int32_t* ids, float* w, hipStream_t stream, int n_group = 1,
+                      int topk_group = 1) {
   const int64_t grid = (M + kTokensPerWG - 1) / kTokensPerWG;
-  hipLaunchKernelGGL(router_topk_kernel<NPL>, dim3((unsigned)grid), dim3(kRouterThreads), 0, stream, logits, M, E, k,
-                     score_fn, bias, renorm, scale, ids, w);
+  if (n_group > 1)
+    hipLaunchKernelGGL((router_topk_kernel<NPL, true>), dim3((unsigned)grid), dim3(kRouterThreads), 0, stream, logits,
+                       M, E, k, score_fn, bias, renorm, scale, ids, w, n_group, topk_group);
+  else
+    hipLaunchKernelGGL((router_topk_kernel<NPL, false>), dim3((unsigned)grid), dim3(kRouterThreads), 0, stream,
+                       logits, M, E, k, score_fn, bias, renorm, scale, ids, w, 1, 1);
   return hipGetLastError();
 }
 
@@ -193,6 +206,20 @@ hipError_t launch_router_topk(const float* logits, int64_t M, int E, int k, int 
   if (E <= 256) return launch_npl<4>(logits, M, E, k, score_fn, bias, renorm, scale, ids, w, stream);
   if (E <= 512) return launch_npl<8>(logits, M, E, k, score_fn, bias, renorm, scale, ids, w, stream);
   return launch_npl<16>(logits, M, E, k, score_fn, bias, renorm, scale, ids, w, stream);
+}
+
+hipError_t launch_router_noaux_tc(const float* logits, int64_t M, int E, int k, int n_group, int topk_group,
+                                  const float* bias, int renorm, double scale, int32_t* ids, float* w,
+                                  hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  if (n_group <= 1)
+    return launch_router_topk(logits, M, E, k, kScoreSigmoid, bias, renorm, scale, ids, w, stream);
+  const int s = kScoreSigmoid;
+  if (E <= 64) return launch_npl<1>(logits, M, E, k, s, bias, renorm, scale, ids, w, stream, n_group, topk_group);
+  if (E <= 128) return launch_npl<2>(logits, M, E, k, s, bias, renorm, scale, ids, w, stream, n_group, topk_group);
+  if (E <= 256) return launch_npl<4>(logits, M, E, k, s, bias, renorm, scale, ids, w, stream, n_group, topk_group);
+  if (E <= 512) return launch_npl<8>(logits, M, E, k, s, bias, renorm, scale, ids, w, stream, n_group, topk_group);
+  return launch_npl<16>(logits, M, E, k, s, bias, renorm, scale, ids, w, stream, n_group, topk_group);
 }
 
 }  // namespace bfp8

@@ -221,11 +221,14 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   // forms the weights and writes the routing for the down kernel
   const int tok = j / k, rank = j - tok * k;
   const bool writer = kRoute && rank == 0 && n0 == 0 && wave == 8;
+  // LDS for the grouped selection's keys: wave 0 and the writer (wave 8) each
+  __shared__ float s_rkey[kRoute ? 2 : 1][kRoute ? kFoldedRouterMaxE : 1];
   if constexpr (kRoute) {
     __shared__ int s_route;
     if (wave == 0) {
       router::WaveRoute<kFoldedRouterMaxE / 64> r;
-      r.load(ra.logits + (size_t)tok * ra.E, ra.E, ra.score_fn, ra.bias, lane);
+      r.load(ra.logits + (size_t)tok * ra.E, ra.E, ra.score_fn, ra.bias, lane, ra.n_group, ra.topk_group,
+             s_rkey[0]);
       int ex = 0;
       for (int q = 0; q <= rank; q++) {
         float lv;
@@ -242,7 +245,8 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   // when the route is not local): off the column waves' path
   auto write_routing = [&]() {
     router::WaveRoute<kFoldedRouterMaxE / 64> r;
-    r.load(ra.logits + (size_t)tok * ra.E, ra.E, ra.score_fn, ra.bias, lane);
+    r.load(ra.logits + (size_t)tok * ra.E, ra.E, ra.score_fn, ra.bias, lane, ra.n_group, ra.topk_group,
+           s_rkey[kRoute ? 1 : 0]);
     int my_id = 0;
     float my_logit = 0.0f;
     for (int q = 0; q < k; q++) {

@@ -254,6 +254,23 @@ bfp8moe_status_t moe_router_topk(const float* logits, int64_t M, int32_t E, int3
                                  const float* bias, int32_t renormalize, double scale, int32_t* topk_ids,
                                  float* topk_w, void* stream);
 
+/* Group-limited noaux-TC router [P2 Reviewed changes: route_noaux_tc.py, a
+ * noaux-TC routing kernel the MoE router switches to].  Reading of the method
+ * the pages name: sigmoid scores s_e computed as above; choice keys
+ * s_e + bias[e] in fp32 (s_e alone when bias is NULL); the E experts form
+ * n_group groups of E / n_group consecutive ids, each scored by the fp32 sum of
+ * its two largest keys (its one key when a group has one expert); the
+ * topk_group best groups are kept (equal scores: the lower group index); the
+ * k largest keys among their experts are chosen, largest first (equal keys:
+ * the lower expert id).  Weights as moe_router_topk's sigmoid scoring: from
+ * the unbiased scores, divided by their sum over the k chosen when
+ * renormalize != 0, times scale.  1 <= E <= 1024, n_group in [1, 64] dividing
+ * E, 1 <= topk_group <= n_group, 1 <= k <= min(64, topk_group * E / n_group);
+ * n_group = 1 is moe_router_topk with sigmoid scoring. */
+bfp8moe_status_t moe_router_noaux_tc(const float* logits, int64_t M, int32_t E, int32_t k, int32_t n_group,
+                                     int32_t topk_group, const float* bias, int32_t renormalize, double scale,
+                                     int32_t* topk_ids, float* topk_w, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* moe_reduce                                                                */
 /* [P4 Pull request overview: a dedicated reduction applies the router        */
@@ -332,10 +349,13 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
                                      void* stream);
 
 /* The layer with its router: moe_router_topk on router_logits [M, E] fp32
- * (score_fn, router_bias, renormalize, routed_scale as there), writing the
- * routing to topk_ids [M, k] / topk_w [M, k] (caller-owned outputs), then
- * fused_moe_block_fp8 on it; same results as the two calls in a row.
- * [P2 Changes: the fused single-group top-k router feeds the MoE layer]
+ * (score_fn, router_bias, renormalize, routed_scale as there) -- or, with
+ * n_group > 1, moe_router_noaux_tc (n_group groups keeping topk_group; sigmoid
+ * scoring) -- writing the routing to topk_ids [M, k] / topk_w [M, k]
+ * (caller-owned outputs), then fused_moe_block_fp8 on it; same results as
+ * the two calls in a row.
+ * [P2 Changes: the fused single-group top-k router feeds the MoE layer;
+ *  Reviewed changes: route_noaux_tc.py]
  * On the few-token path with E <= 256 and at most 4 tokens the router is
  * folded into the layer's first kernel (one launch fewer): each gate/up
  * workgroup ranks its token's logits itself.  Elsewhere the router runs as its
@@ -344,7 +364,8 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
  * options; opts must not set stage events or a stage selection. */
 bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, int32_t H, const float* router_logits,
                                             const float* router_bias, int32_t score_fn, int32_t renormalize,
-                                            double routed_scale, int32_t k, int32_t* topk_ids, float* topk_w,
+                                            double routed_scale, int32_t n_group, int32_t topk_group, int32_t k,
+                                            int32_t* topk_ids, float* topk_w,
                                             const uint8_t* w13, const float* w13_scale, const uint8_t* w2,
                                             const float* w2_scale, int32_t E, int32_t I, const bfp8moe_opts_t* opts,
                                             uint16_t* out, void* ws, size_t ws_bytes, void* stream);

@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_route_prepare", "quant_fp8", "moe_fp8_grouped_gemm", "silu_and_mul_quant_fp8", "moe_reduce",
               "fused_moe_block_fp8", "silu_and_mul", "fused_moe_block_fp8_workspace_size", "bfp8moe_max_blocks", "moe_router_topk",
-              "fused_moe_block_fp8_routed"):
+              "fused_moe_block_fp8_routed", "moe_router_noaux_tc", "fused_moe_block_fp8_noalloc"):
         assert n in names
 
 
@@ -135,16 +135,25 @@ def test_host_validation_rejects_bad_calls():
     st, msg = _status(L.moe_router_topk, fake, 4, 256, 8, 1, None, 1, math.nan, fake, fake, None)
     assert st == 1 and "scale" in msg
     o = bfp8.opts(flags=bfp8.FLAG_ONLY_STAGE(0))
-    st, msg = _status(L.fused_moe_block_fp8_routed, fake, 1, 7168, fake, None, 0, 1, 1.0, 8, fake, fake, fake, fake,
+    st, msg = _status(L.fused_moe_block_fp8_routed, fake, 1, 7168, fake, None, 0, 1, 1.0, 1, 1, 8, fake, fake, fake, fake,
                       fake, fake, 256, 256, ctypes.byref(o), fake, fake, 1 << 30, None)
     assert st == 1 and "stage" in msg
     o = bfp8.opts()
-    st, msg = _status(L.fused_moe_block_fp8_routed, fake, 1, 7168, fake, None, 0, 1, 1.0, 8, fake, fake, fake, fake,
+    st, msg = _status(L.fused_moe_block_fp8_routed, fake, 1, 7168, fake, None, 0, 1, 1.0, 1, 1, 8, fake, fake, fake, fake,
                       fake, fake, 256, 256, ctypes.byref(o), fake, fake, 16, None)
     assert st == 3 and "workspace" in msg
-    st, msg = _status(L.fused_moe_block_fp8_routed, fake, 1, 7168, fake, fake, 0, 1, 1.0, 8, fake, fake, fake, fake,
+    st, msg = _status(L.fused_moe_block_fp8_routed, fake, 1, 7168, fake, fake, 0, 1, 1.0, 1, 1, 8, fake, fake, fake, fake,
                       fake, fake, 256, 256, ctypes.byref(o), fake, fake, 1 << 30, None)
     assert st == 1 and "sigmoid" in msg
+    # grouped selection: n_group must divide E, topk_group <= n_group, sigmoid scoring
+    for ng, tg, sf, what in ((7, 1, 1, "n_group"), (8, 9, 1, "topk_group"), (8, 4, 0, "sigmoid")):
+        st, msg = _status(L.fused_moe_block_fp8_routed, fake, 1, 7168, fake, None, sf, 1, 1.0, ng, tg, 8, fake, fake,
+                          fake, fake, fake, fake, 256, 256, ctypes.byref(o), fake, fake, 1 << 30, None)
+        assert st == 1 and what in msg, msg
+    st, msg = _status(L.moe_router_noaux_tc, fake, 4, 256, 8, 6, 2, None, 1, 1.0, fake, fake, None)
+    assert st == 1 and "n_group" in msg
+    st, msg = _status(L.moe_router_noaux_tc, fake, 4, 256, 80, 8, 2, None, 1, 1.0, fake, fake, None)
+    assert st == 1 and "k=80" in msg
 
 
 def test_router_binding_checks_buffers():

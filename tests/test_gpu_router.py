@@ -9,7 +9,7 @@ import torch
 import block_fp8_mixture_route_amd as bfp8
 from block_fp8_mixture_route_amd import synth
 from oracle import oracle as O
-from tests.gpu_util import dev, print_case
+from tests.gpu_util import assert_layer_elementwise, dev, print_case
 
 pytestmark = pytest.mark.gpu
 
@@ -91,9 +91,9 @@ def test_router_zero_tokens_and_layer_feed():
                                    mw.w2_s.to(dev()), E=E)
     torch.cuda.synchronize()
     rid, rw = O.router_topk(lg, k)
-    ref = O.fused_moe(hidden, rid, rw, mw.w13, mw.w13_s, mw.w2, mw.w2_s)
-    from tests.gpu_util import bf16_np, normwise_err, LAYER_TOL
-    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+    assert (ids.cpu().numpy() == rid).all()
+    assert_layer_elementwise(out, hidden, torch.from_numpy(rid), torch.from_numpy(rw), mw, bfp8.SCALE_FP32,
+                             float("inf"), E=E, what="router feeds the layer")
 
 
 # routed layer: (M, E, k, H, I, score_fn) -- the decode shape with the router
@@ -108,7 +108,7 @@ ROUTED = [(1, 256, 8, 7168, 256, bfp8.SCORE_SOFTMAX), (4, 256, 8, 7168, 256, bfp
 @pytest.mark.parametrize("M,E,k,H,I,score_fn", ROUTED)
 def test_routed_layer(M, E, k, H, I, score_fn):
     print_case("routed layer", M, E, k, H, I, score_fn)
-    from tests.gpu_util import LAYER_TOL, bf16_np, normwise_err
+    from tests.gpu_util import bf16_np
     lg = synth.router_logits(M, E, "routed", bf16_valued=True, std=2.0)
     bias = synth.router_bias(E, "routed", std=0.1) if score_fn == bfp8.SCORE_SIGMOID else None
     scale = 2.5 if score_fn == bfp8.SCORE_SIGMOID else 1.0
@@ -123,8 +123,38 @@ def test_routed_layer(M, E, k, H, I, score_fn):
     assert (ids.cpu().numpy() == rid).all()
     assert ulps(w.cpu().numpy(), rw).max() <= 1.0
     assert (bf16_np(out) == bf16_np(out2)).all()
-    ref = O.fused_moe(hidden, rid, rw, mw.w13, mw.w13_s, mw.w2, mw.w2_s)
-    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+    assert_layer_elementwise(out, hidden, torch.from_numpy(rid), torch.from_numpy(rw), mw, bfp8.SCALE_FP32,
+                             float("inf"), E=E, what=f"routed M={M} E={E}", o=bfp8.opts())
+
+
+# routed layer with group-limited noaux-TC selection: (M, E, k, H, I, n_group,
+# topk_group) -- folded into the few-token kernel (1 and 4 tokens), the
+# router's own launch before the few-token path (12 tokens) and before the
+# general path (40 tokens)
+ROUTED_GROUPED = [(1, 256, 8, 7168, 256, 8, 4), (4, 256, 8, 2048, 256, 8, 4), (12, 256, 8, 2048, 256, 8, 4),
+                  (40, 256, 8, 1024, 256, 8, 4), (2, 64, 6, 1024, 128, 4, 2)]
+
+
+@pytest.mark.parametrize("M,E,k,H,I,n_group,topk_group", ROUTED_GROUPED)
+def test_routed_layer_grouped(M, E, k, H, I, n_group, topk_group):
+    print_case("routed layer grouped", M, E, k, H, I, n_group, topk_group)
+    from tests.gpu_util import bf16_np
+    lg = synth.router_logits(M, E, "routed_grp", bf16_valued=True, std=2.0)
+    bias = synth.router_bias(E, "routed_grp", std=0.1)
+    rid, rw = O.router_noaux_tc(lg, k, n_group, topk_group, bias, True, 2.5)
+    mw = synth.moe_weights(E, H, I, "routed_grp", M, experts=np.unique(rid).tolist(), device=dev())
+    hidden = synth.hidden_states(M, H, "routed_grp", M).to(dev())
+    out, ids, w = bfp8.fused_moe_block_fp8_routed(hidden, lg.to(dev()), k, mw.w13, mw.w13_s, mw.w2, mw.w2_s,
+                                                  bfp8.SCORE_SIGMOID, bias.to(dev()), True, 2.5, n_group=n_group,
+                                                  topk_group=topk_group)
+    ids2, w2 = bfp8.router_noaux_tc(lg.to(dev()), k, n_group, topk_group, bias.to(dev()), True, 2.5)
+    out2 = bfp8.fused_moe_block_fp8(hidden, ids2, w2, mw.w13, mw.w13_s, mw.w2, mw.w2_s, E=E)
+    torch.cuda.synchronize()
+    assert (ids.cpu().numpy() == rid).all()
+    assert ulps(w.cpu().numpy(), rw).max() <= 1.0
+    assert (bf16_np(out) == bf16_np(out2)).all()
+    assert_layer_elementwise(out, hidden, torch.from_numpy(rid), torch.from_numpy(rw), mw, bfp8.SCALE_FP32,
+                             float("inf"), E=E, what=f"routed grouped M={M}", o=bfp8.opts())
 
 
 @pytest.mark.parametrize("M", [3, 6])
@@ -133,7 +163,7 @@ def test_routed_layer_expert_slice_and_options(M):
     # folded path (3 tokens) and the router's own launch (6 tokens) give the
     # two-call result bit for bit, and the oracle's to the layer tolerance
     print_case("routed layer slice", M)
-    from tests.gpu_util import LAYER_TOL, bf16_np, normwise_err
+    from tests.gpu_util import bf16_np
     E, k, H, I, off, L = 64, 8, 1024, 256, 16, 24
     lg = synth.router_logits(M, E, "routed_slice", std=2.0)
     lg[1, off:off + L] -= 20.0  # token 1 has no local route: its output row is zero
@@ -150,6 +180,5 @@ def test_routed_layer_expert_slice_and_options(M):
     local = ((rid >= off) & (rid < off + L)).any(axis=1)
     assert local.any() and not local[1]
     assert (bf16_np(out)[1] == 0).all()
-    ref = O.fused_moe(hidden, rid, rw, W.w13, W.w13_s, W.w2, W.w2_s, expert_offset=off, L=L,
-                      scale_fmt=O.SCALE_UE8M0, clamp=7.0)
-    assert normwise_err(bf16_np(out), ref) <= LAYER_TOL
+    assert_layer_elementwise(out, hidden, torch.from_numpy(rid), torch.from_numpy(rw), W, bfp8.SCALE_UE8M0, 7.0,
+                             E=E, expert_offset=off, L=L, what=f"routed slice M={M}", o=o)
