@@ -301,9 +301,10 @@ def launch_floor(hip, stream, dev):
 
 
 def router_table(hip, stream, dev):
-    """Single-group top-k router, graph-timed: softmax (renormalised) and
-    biased sigmoid (renormalised), each one launch, beside torch's softmax ->
-    topk -> renormalise for context."""
+    """Top-k routers, graph-timed: single-group softmax (renormalised) and
+    biased sigmoid (renormalised), and group-limited noaux-TC (biased sigmoid,
+    8 groups keeping 4), each one launch, beside torch's softmax -> topk ->
+    renormalise for context."""
     import torch
 
     import block_fp8_mixture_route_amd as bfp8
@@ -313,8 +314,9 @@ def router_table(hip, stream, dev):
     P = ctypes.c_void_p
     ext = torch.cuda.ExternalStream(stream.value, device=dev)
     print()
-    print("| tokens M | experts E | k | softmax µs | sigmoid + bias µs | torch softmax/topk/renorm µs |")
-    print("|---|---|---|---|---|---|")
+    print("| tokens M | experts E | k | softmax µs | sigmoid + bias µs | noaux-TC 8 groups keep 4 µs "
+          "| torch softmax/topk/renorm µs |")
+    print("|---|---|---|---|---|---|---|")
     out = {}
     for (M, E) in [(1, 256), (16, 256), (256, 256), (2048, 512), (4096, 256), (16384, 256)]:
         lg = synth.router_logits(M, E, "bench_router", device=dev)
@@ -336,9 +338,15 @@ def router_table(hip, stream, dev):
 
         ts = time_graph(hip, stream, lambda: [rt(bfp8.SCORE_SOFTMAX, None) for _ in range(20)], 20) * 1e3 / 20
         tg = time_graph(hip, stream, lambda: [rt(bfp8.SCORE_SIGMOID, bias) for _ in range(20)], 20) * 1e3 / 20
+
+        def rt_grouped():
+            bfp8._lib.check(L_.moe_router_noaux_tc(P(lg.data_ptr()), M, E, 8, 8, 4, P(bias.data_ptr()), 1, 1.0,
+                                                   P(rid.data_ptr()), P(rw.data_ptr()), stream))
+
+        tn = time_graph(hip, stream, lambda: [rt_grouped() for _ in range(20)], 20) * 1e3 / 20
         tt = time_graph(hip, stream, torch_router, 20) * 1e3 / 20
-        out[f"{M}x{E}"] = {"softmax_us": ts, "sigmoid_bias_us": tg, "torch_us": tt}
-        print(f"| {M} | {E} | 8 | {ts:.2f} | {tg:.2f} | {tt:.2f} |", flush=True)
+        out[f"{M}x{E}"] = {"softmax_us": ts, "sigmoid_bias_us": tg, "noaux_tc_8x4_us": tn, "torch_us": tt}
+        print(f"| {M} | {E} | 8 | {ts:.2f} | {tg:.2f} | {tn:.2f} | {tt:.2f} |", flush=True)
 
     return out
 

@@ -92,6 +92,14 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
 
 __device__ __forceinline__ float sigmoid_rn(float x) { return (float)(1.0 / (1.0 + exp(-(double)x))); }
 
+// (a1, a2), a1 >= a2, becomes the two largest of {a1, a2, b1, b2} (b1 >= b2);
+// equal values count twice, as two experts with equal keys do.
+__device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float b2) {
+  const float n2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+  a1 = fmaxf(a1, b1);
+  a2 = n2;
+}
+
 // A token's logits and keys, loaded by one wave.  Loads are unconditional
 // (indexes clamped into the row); absent experts get key 0.
 template <int NPL>
@@ -102,8 +110,8 @@ struct WaveRoute {
   float sv[NPL];      // logit of each sorted key
 
   // n_group > 1: keep only the experts of the topk_group best groups of
-  // E / n_group consecutive experts (n_group <= 64); s_key: E floats of LDS
-  // private to this wave.
+  // E / n_group consecutive experts (n_group <= 64); s_key: n_group + E floats
+  // of LDS private to this wave.
   __device__ __forceinline__ void load(const float* lg, int E, int score_fn, const float* bias, int lane,
                                        int n_group = 1, int topk_group = 1, float* s_key = nullptr) {
     float b[NPL], sc[NPL];
@@ -127,24 +135,41 @@ struct WaveRoute {
     }
     if (n_group > 1) {
       const int gs = E / n_group;
-#pragma unroll
-      for (int i = 0; i < NPL; i++)
-        if (lane + 64 * i < E) s_key[lane + 64 * i] = sc[i];
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
       uint32_t gkey = 0u;
-      if (lane < n_group) {
-        float a = -__builtin_inff(), c = -__builtin_inff();
-        for (int e = lane * gs; e < (lane + 1) * gs; e++) {
-          const float x = s_key[e];
-          if (x > a) {
-            c = a;
-            a = x;
-          } else if (x > c) {
-            c = x;
-          }
+      if ((gs & (gs - 1)) == 0 && gs < 64) {
+        // groups within 64 lanes: a top-2 butterfly over each aligned run of
+        // gs lanes, slot by slot; the run's first lane stores the score
+#pragma unroll
+        for (int i = 0; i < NPL; i++) {
+          float a1 = lane + 64 * i < E ? sc[i] : -__builtin_inff(), a2 = -__builtin_inff();
+          for (int d = 1; d < gs; d <<= 1) top2_merge(a1, a2, __shfl_xor(a1, d), __shfl_xor(a2, d));
+          if ((lane & (gs - 1)) == 0 && lane + 64 * i < E) s_key[(lane + 64 * i) / gs] = gs > 1 ? a1 + a2 : a1;
         }
-        gkey = order_bits(gs > 1 ? a + c : a);
+      } else if (gs % 64 == 0) {
+        // groups of whole slots: each lane's top-2 over the group's slots,
+        // then a butterfly over the wave
+        for (int g = 0; g < n_group; g++) {
+          float a1 = -__builtin_inff(), a2 = -__builtin_inff();
+#pragma unroll
+          for (int i = 0; i < NPL; i++)
+            if (64 * i >= g * gs && 64 * i < (g + 1) * gs) top2_merge(a1, a2, sc[i], -__builtin_inff());
+          for (int d = 1; d < 64; d <<= 1) top2_merge(a1, a2, __shfl_xor(a1, d), __shfl_xor(a2, d));
+          if (lane == 0) s_key[g] = a1 + a2;
+        }
+      } else {
+        // other group widths: lane g scans group g's keys
+#pragma unroll
+        for (int i = 0; i < NPL; i++)
+          if (lane + 64 * i < E) s_key[n_group + lane + 64 * i] = sc[i];
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
+        if (lane < n_group) {
+          float a1 = -__builtin_inff(), a2 = -__builtin_inff();
+          for (int e = lane * gs; e < (lane + 1) * gs; e++) top2_merge(a1, a2, s_key[n_group + e], -__builtin_inff());
+          s_key[lane] = gs > 1 ? a1 + a2 : a1;
+        }
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the group scores are in LDS
+      if (lane < n_group) gkey = order_bits(s_key[lane]);
       uint64_t chosen = 0;
       for (int j = 0; j < topk_group; j++) {
         const uint32_t top = wave_max_u32(gkey);

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(const float
   if (t >= M) return;  // whole waves only: the reductions need all 64 lanes
   router::WaveRoute<NPL> r;
   if constexpr (kGrouped) {
-    __shared__ float s_key[kTokensPerWG][64 * NPL];  // each wave's choice keys
+    __shared__ float s_key[kTokensPerWG][64 + 64 * NPL];  // each wave's group scores and choice keys
     r.load(logits + t * (int64_t)E, E, score_fn, bias, lane, n_group, topk_group, s_key[threadIdx.x >> 6]);
   } else {
     r.load(logits + t * (int64_t)E, E, score_fn, bias, lane);

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   const int tok = j / k, rank = j - tok * k;
   const bool writer = kRoute && rank == 0 && n0 == 0 && wave == 8;
   // LDS for the grouped selection's keys: wave 0 and the writer (wave 8) each
-  __shared__ float s_rkey[kRoute ? 2 : 1][kRoute ? kFoldedRouterMaxE : 1];
+  __shared__ float s_rkey[kRoute ? 2 : 1][kRoute ? 64 + kFoldedRouterMaxE : 1];
   if constexpr (kRoute) {
     __shared__ int s_route;
     if (wave == 0) {
