@@ -414,6 +414,140 @@ void oracle_grouped_gemm_f64(const uint8_t* A, const float* A_s, int a_row_div,
 }
 
 /* ------------------------------------------------------------------------- */
+/* W8A8 variant: per-token activation scales, per-output-channel weight scales */
+/* [P2 Reviewed changes: w8a8.py, the static FP8 MoE backend; P4 Pull request  */
+/*  overview: the W8A8 fused MoE ends with moe_reduce too]                     */
+/* The pages name the variant only.  Reading: the same pipeline with one scale */
+/* per activation row (the row's amax / 448 over all K, or a given static      */
+/* per-tensor scale) and one fp32 scale per weight row (output channel).       */
+/* ------------------------------------------------------------------------- */
+
+void oracle_moe_reduce(const uint16_t* y, const float* w, const int32_t* topk_ids, int expert_offset, int L,
+                       int64_t M, int k, int H, uint16_t* out);
+
+/* One row's scale: static_scale when > 0, else the group-scale formula applied
+ * to the amax over the whole row. */
+static float row_scale(const float* x, int K, int fmt, float static_scale)
+{
+    if (static_scale > 0.0f) return static_scale;
+    float amax = 0.0f;
+    for (int i = 0; i < K; i++) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    return oracle_group_scale(amax, fmt);
+}
+
+/* x: [rows, K] BF16 -> q [rows, K] E4M3 (saturating) and s [rows] fp32. */
+void oracle_quant_fp8_rows(const uint16_t* x, int64_t rows, int K, int fmt, float static_scale, uint8_t* q, float* s)
+{
+    float* row = (float*)malloc(sizeof(float) * (size_t)K);
+    for (int64_t r = 0; r < rows; r++) {
+        for (int i = 0; i < K; i++) row[i] = bf16_to_f32(x[(size_t)r * K + i]);
+        float sc = row_scale(row, K, fmt, static_scale);
+        s[r] = sc;
+        for (int i = 0; i < K; i++) q[(size_t)r * K + i] = oracle_e4m3_encode(row[i] / sc);
+    }
+    free(row);
+}
+
+/* Fused SwiGLU + per-row quantisation of each live row (rows filtered as in
+ * oracle_silu_and_mul_quant_fp8 are not written). */
+void oracle_silu_and_mul_quant_fp8_rows(const uint16_t* gate_up, int64_t rows, int I,
+                                        const int32_t* row_expert_ids, const int32_t* expert_map, int E,
+                                        float clamp_limit, int fmt, float static_scale, uint8_t* q, float* s)
+{
+    uint16_t* act = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)I);
+    for (int64_t r = 0; r < rows; r++) {
+        if (!row_is_live(row_expert_ids, expert_map, E, r)) continue;
+        oracle_silu_and_mul(gate_up + (size_t)r * 2 * I, 1, I, clamp_limit, act);
+        oracle_quant_fp8_rows(act, 1, I, fmt, static_scale, q + (size_t)r * I, s + r);
+    }
+    free(act);
+}
+
+/* out[n] = bf16(a_s * w_s[n] * sum_k dec(a_k) dec(W[n, k])), all in fp64 (the
+ * code sum is exact up to K = 2^24 terms); acc_out / abs_out as gemm_row_ex. */
+static void gemm_row_channel(const uint8_t* a, float a_s, const uint8_t* W, const float* w_s, int N, int K,
+                             uint16_t* out, double* acc_out, double* abs_out)
+{
+    double* ad = (double*)malloc(sizeof(double) * (size_t)K);
+    for (int i = 0; i < K; i++) ad[i] = oracle_e4m3_decode(a[i]);
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; n++) {
+        const uint8_t* wr = W + (size_t)n * K;
+        double p = 0.0, pa = 0.0;
+        for (int i = 0; i < K; i++) {
+            double t = ad[i] * oracle_e4m3_decode(wr[i]);
+            p += t;
+            pa += fabs(t);
+        }
+        double c = (double)a_s * (double)w_s[n];
+        if (out) out[n] = oracle_f64_to_bf16(c * p);
+        if (acc_out) acc_out[n] = c * p;
+        if (abs_out) abs_out[n] = fabs(c) * pa;
+    }
+    free(ad);
+}
+
+/* Grouped GEMM with per-row activation scales A_s [rows] and per-channel weight
+ * scales B_s [L, N]; acc / mag (both NULL, or both [R, N]) receive the
+ * unrounded values and magnitudes instead of C. */
+void oracle_grouped_gemm_channel(const uint8_t* A, const float* A_s, int a_row_div, const uint8_t* B,
+                                 const float* B_s, int N, int K, const int32_t* topk_ids, int64_t R,
+                                 int expert_offset, int L, uint16_t* C, double* acc, double* mag)
+{
+    for (int64_t r = 0; r < R; r++) {
+        int64_t e = (int64_t)topk_ids[r] - expert_offset;
+        if (e < 0 || e >= L) continue;
+        int64_t arow = r / a_row_div;
+        gemm_row_channel(A + (size_t)arow * K, A_s[arow], B + (size_t)e * N * K, B_s + (size_t)e * N, N, K,
+                         C ? C + (size_t)r * N : NULL, acc ? acc + (size_t)r * N : NULL,
+                         mag ? mag + (size_t)r * N : NULL);
+    }
+}
+
+/* The whole W8A8 layer: w13_s [L, 2I], w2_s [L, H]; a1_static / a2_static > 0
+ * are static scales of the hidden states / the SwiGLU output, else per-row
+ * dynamic ones (scale_fmt).  Intermediates as oracle_fused_moe (act_s is
+ * [M*k] here). */
+void oracle_fused_moe_w8a8(const uint16_t* hidden, int64_t M, int H, const int32_t* topk_ids, const float* topk_w,
+                           int k, const uint8_t* w13, const float* w13_s, const uint8_t* w2, const float* w2_s,
+                           int expert_offset, int L, int I, int scale_fmt, float a1_static, float a2_static,
+                           float clamp_limit, uint16_t* out, uint16_t* h13_out, uint8_t* q_out, float* s_out,
+                           uint16_t* y_out)
+{
+    uint8_t* aq = (uint8_t*)malloc((size_t)H);
+    uint16_t* h13 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)2 * I);
+    uint8_t* q = (uint8_t*)malloc((size_t)I);
+    uint16_t* y = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)k * H);
+    float* w = (float*)malloc(sizeof(float) * (size_t)k);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    for (int64_t t = 0; t < M; t++) {
+        float as, s;
+        oracle_quant_fp8_rows(hidden + (size_t)t * H, 1, H, scale_fmt, a1_static, aq, &as);
+        for (int j = 0; j < k; j++) {
+            int64_t r = t * k + j;
+            ids[j] = topk_ids[r];
+            w[j] = topk_w[r];
+            int64_t e = (int64_t)topk_ids[r] - expert_offset;
+            if (e < 0 || e >= L) continue;
+            gemm_row_channel(aq, as, w13 + (size_t)e * 2 * I * H, w13_s + (size_t)e * 2 * I, 2 * I, H, h13, NULL,
+                             NULL);
+            oracle_silu_and_mul_quant_fp8_rows(h13, 1, I, NULL, NULL, 0, clamp_limit, scale_fmt, a2_static, q, &s);
+            gemm_row_channel(q, s, w2 + (size_t)e * H * I, w2_s + (size_t)e * H, H, I, y + (size_t)j * H, NULL,
+                             NULL);
+            if (h13_out) memcpy(h13_out + (size_t)r * 2 * I, h13, sizeof(uint16_t) * 2 * I);
+            if (q_out) memcpy(q_out + (size_t)r * I, q, (size_t)I);
+            if (s_out) s_out[r] = s;
+            if (y_out) memcpy(y_out + (size_t)r * H, y + (size_t)j * H, sizeof(uint16_t) * H);
+        }
+        oracle_moe_reduce(y, w, ids, expert_offset, L, 1, k, H, out + (size_t)t * H);
+    }
+    free(aq); free(h13); free(q); free(y); free(w); free(ids);
+}
+
+/* ------------------------------------------------------------------------- */
 /* moe_reduce: top-k weighted sum back to token order                          */
 /* [P4 Pull request overview: weights applied by a dedicated reduction]        */
 /* [P4 review discussion: accumulation precision left to each kernel; fp32]    */

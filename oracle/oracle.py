@@ -60,6 +60,11 @@ def lib():
             "oracle_sigmoid_rn": (f32, [f32]),
             "oracle_router_topk": (None, [P, i64, i32, i32, i32, P, i32, ctypes.c_double, P, P]),
             "oracle_router_noaux_tc": (None, [P, i64, i32, i32, i32, i32, P, i32, ctypes.c_double, P, P]),
+            "oracle_quant_fp8_rows": (None, [P, i64, i32, i32, f32, P, P]),
+            "oracle_silu_and_mul_quant_fp8_rows": (None, [P, i64, i32, P, P, i32, f32, i32, f32, P, P]),
+            "oracle_grouped_gemm_channel": (None, [P, P, i32, P, P, i32, i32, P, i64, i32, i32, P, P, P]),
+            "oracle_fused_moe_w8a8": (None, [P, i64, i32, P, P, i32, P, P, P, P, i32, i32, i32, i32, f32, f32, f32,
+                                             P, P, P, P, P]),
             "oracle_fused_moe": (None, [P, i64, i32, P, P, i32, P, P, P, P, i32, i32, i32, i32, f32,
                                         P, i64, P, P, P, P, P]),
             "oracle_num_threads": (i32, []),
@@ -297,6 +302,80 @@ def fused_moe(hidden, topk_ids, topk_w, w13, w13_s, w2, w2_s, expert_offset: int
                            expert_offset, L, I, scale_fmt, clamp, _p(tok), nt, _p(out),
                            _p(inter["h13"]) if inter else None, _p(inter["q"]) if inter else None,
                            _p(inter["s"]) if inter else None, _p(inter["y"]) if inter else None)
+    return (out, inter) if want_intermediates else out
+
+
+# ---------------------------------------------------------------- W8A8 variant
+
+def quant_fp8_rows(x_bf16, fmt: int = SCALE_FP32, static_scale: float = 0.0):
+    """One scale per row (static when > 0, else the row's amax / 448): ([rows, K]
+    codes, [rows] scales)."""
+    x = as_np(x_bf16, np.uint16)
+    rows, K = x.shape
+    q = np.zeros((rows, K), np.uint8)
+    s = np.zeros(rows, np.float32)
+    lib().oracle_quant_fp8_rows(_p(x), rows, K, fmt, static_scale, _p(q), _p(s))
+    return q, s
+
+
+def silu_and_mul_quant_fp8_rows(gate_up_bf16, row_expert_ids=None, expert_map=None, E: int = 0,
+                                clamp: float = float("inf"), fmt: int = SCALE_FP32, static_scale: float = 0.0,
+                                q_init=None, s_init=None):
+    x = as_np(gate_up_bf16, np.uint16)
+    rows, I2 = x.shape
+    I = I2 // 2
+    q = np.zeros((rows, I), np.uint8) if q_init is None else np.array(q_init, np.uint8, copy=True)
+    s = np.zeros(rows, np.float32) if s_init is None else np.array(s_init, np.float32, copy=True)
+    ids = None if row_expert_ids is None else as_np(row_expert_ids, np.int32)
+    emap = None if expert_map is None else as_np(expert_map, np.int32)
+    lib().oracle_silu_and_mul_quant_fp8_rows(_p(x), rows, I, _p(ids), _p(emap), E, clamp, fmt, static_scale, _p(q),
+                                            _p(s))
+    return q, s
+
+
+def grouped_gemm_channel(A, A_s, a_row_div: int, B, B_s, topk_ids, expert_offset: int, L: int, exact=False):
+    """Per-row activation scales A_s [rows], per-channel weight scales B_s [L, N].
+    exact: ([R, N] fp64 values, magnitudes) instead of [R, N] BF16 bits."""
+    A = as_np(A, np.uint8); A_s = as_np(A_s, np.float32)
+    B = as_np(B, np.uint8); B_s = as_np(B_s, np.float32)
+    ids = as_np(topk_ids, np.int32).reshape(-1)
+    N, K = B.shape[1], B.shape[2]
+    R = ids.size
+    if exact:
+        acc = np.full((R, N), np.nan)
+        mag = np.full((R, N), np.nan)
+        lib().oracle_grouped_gemm_channel(_p(A), _p(A_s), a_row_div, _p(B), _p(B_s), N, K, _p(ids), R,
+                                          expert_offset, L, None, _p(acc), _p(mag))
+        return acc, mag
+    C = np.zeros((R, N), np.uint16)
+    lib().oracle_grouped_gemm_channel(_p(A), _p(A_s), a_row_div, _p(B), _p(B_s), N, K, _p(ids), R, expert_offset, L,
+                                      _p(C), None, None)
+    return C
+
+
+def fused_moe_w8a8(hidden, topk_ids, topk_w, w13, w13_s, w2, w2_s, expert_offset: int = 0, L: int = None,
+                   scale_fmt: int = SCALE_FP32, a1_static: float = 0.0, a2_static: float = 0.0,
+                   clamp: float = float("inf"), want_intermediates: bool = False):
+    """The W8A8 layer (w13_s [L, 2I], w2_s [L, H]): [M, H] BF16 output and
+    optionally the intermediates keyed by route id (s is [M*k])."""
+    h = as_np(hidden, np.uint16)
+    ids = as_np(topk_ids, np.int32)
+    w = as_np(topk_w, np.float32)
+    w13 = as_np(w13, np.uint8); w13_s = as_np(w13_s, np.float32)
+    w2 = as_np(w2, np.uint8); w2_s = as_np(w2_s, np.float32)
+    M, H = h.shape
+    k = ids.shape[1]
+    L = w13.shape[0] if L is None else L
+    I = w2.shape[2]
+    out = np.zeros((M, H), np.uint16)
+    inter = None
+    if want_intermediates:
+        inter = dict(h13=np.zeros((M * k, 2 * I), np.uint16), q=np.zeros((M * k, I), np.uint8),
+                     s=np.zeros(M * k, np.float32), y=np.zeros((M * k, H), np.uint16))
+    lib().oracle_fused_moe_w8a8(_p(h), M, H, _p(ids), _p(w), k, _p(w13), _p(w13_s), _p(w2), _p(w2_s), expert_offset,
+                                L, I, scale_fmt, a1_static, a2_static, clamp, _p(out),
+                                _p(inter["h13"]) if inter else None, _p(inter["q"]) if inter else None,
+                                _p(inter["s"]) if inter else None, _p(inter["y"]) if inter else None)
     return (out, inter) if want_intermediates else out
 
 
