@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     SCALE_UE8M0,
     SCORE_SIGMOID,
     SCORE_SOFTMAX,
+    WEIGHT_SCALE_BLOCK,
+    WEIGHT_SCALE_CHANNEL,
     Opts,
     NOALLOC_SCRATCH_BYTES,
     fused_moe_block_fp8,
@@ -26,13 +28,16 @@ from ._lib import (  # noqa: F401
     lib,
     max_blocks,
     moe_fp8_grouped_gemm,
+    moe_fp8_grouped_gemm_channel,
     moe_reduce,
     moe_route_prepare,
     opts,
     quant_fp8,
+    quant_fp8_rows,
     router_noaux_tc,
     router_topk,
     silu_and_mul,
     silu_and_mul_quant_fp8,
+    silu_and_mul_quant_fp8_rows,
     wait_faults,
 )

@@ -44,7 +44,14 @@ class Opts(ctypes.Structure):
         ("local_num_experts", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
         ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+        ("weight_scale_mode", ctypes.c_int32),
+        ("act_static_scale", ctypes.c_float),
+        ("inter_static_scale", ctypes.c_float),
     ]
+
+
+WEIGHT_SCALE_BLOCK = 0
+WEIGHT_SCALE_CHANNEL = 1
 
 
 class BFP8MoEError(RuntimeError):
@@ -69,6 +76,10 @@ SIGNATURES = {
     "silu_and_mul_quant_fp8": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _f32, _i32, _P, _P, _P]),
     "moe_fp8_grouped_gemm": (ctypes.c_int, [_P, _P, _i32, _P, _P, _i32, _i32, _i32, _P, _P, _P, _P, _P, _i64, _i32,
                                             _i64, _P, _P]),
+    "quant_fp8_rows": (ctypes.c_int, [_P, _i64, _i32, _i32, _f32, _P, _P, _P]),
+    "silu_and_mul_quant_fp8_rows": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _f32, _i32, _f32, _P, _P, _P]),
+    "moe_fp8_grouped_gemm_channel": (ctypes.c_int, [_P, _P, _i32, _P, _P, _i32, _i32, _i32, _P, _P, _P, _P, _P,
+                                                    _i64, _i32, _i64, _P, _P]),
     "moe_reduce": (ctypes.c_int, [_P, _P, _P, _i32, _i32, _i64, _i32, _i32, _P, _P]),
     "moe_router_topk": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _P, _i32, ctypes.c_double, _P, _P, _P]),
     "moe_router_noaux_tc": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _i32, _P, _i32, ctypes.c_double, _P, _P,
@@ -165,11 +176,14 @@ def wait_faults(clear=True) -> int:
     return f.value
 
 
-def opts(block_m=0, scale_fmt=SCALE_FP32, clamp_limit=math.inf, expert_offset=0, local_num_experts=0, flags=0):
+def opts(block_m=0, scale_fmt=SCALE_FP32, clamp_limit=math.inf, expert_offset=0, local_num_experts=0, flags=0,
+         weight_scale_mode=WEIGHT_SCALE_BLOCK, act_static_scale=0.0, inter_static_scale=0.0):
     o = Opts()
     lib().bfp8moe_opts_init(ctypes.byref(o))
     o.block_m, o.scale_fmt, o.clamp_limit = block_m, scale_fmt, clamp_limit
     o.expert_offset, o.local_num_experts, o.flags = expert_offset, local_num_experts, flags
+    o.weight_scale_mode, o.act_static_scale, o.inter_static_scale = weight_scale_mode, act_static_scale, \
+        inter_static_scale
     return o
 
 
@@ -264,6 +278,60 @@ def moe_fp8_grouped_gemm(A, A_scale, a_row_div, B, B_scale, route, block_m, R, C
     return C
 
 
+def quant_fp8_rows(x, scale_fmt=SCALE_FP32, static_scale=0.0, q=None, scales=None):
+    """One scale per row (static when > 0, else the row's amax / 448)."""
+    _expect(x, "x", torch.bfloat16, (None, None))
+    rows, K = x.shape
+    _expect(q, "q", _FP8, (rows, K))
+    _expect(scales, "scales", torch.float32, (rows,))
+    _require_device(x, q, scales)
+    q = torch.empty(rows, K, dtype=torch.uint8, device=x.device) if q is None else q
+    scales = torch.empty(rows, dtype=torch.float32, device=x.device) if scales is None else scales
+    check(lib().quant_fp8_rows(ptr(_u16(x)), rows, K, scale_fmt, static_scale, ptr(q), ptr(scales),
+                               stream_of(x.device)))
+    return q, scales
+
+
+def silu_and_mul_quant_fp8_rows(gate_up, row_expert_ids=None, expert_map=None, E=0, clamp_limit=math.inf,
+                                scale_fmt=SCALE_FP32, static_scale=0.0, q=None, scales=None):
+    _expect(gate_up, "gate_up", torch.bfloat16, (None, None))
+    rows, I2 = gate_up.shape
+    I = I2 // 2
+    _expect(row_expert_ids, "row_expert_ids", torch.int32, (rows,))
+    _expect(expert_map, "expert_map", torch.int32, (E,))
+    _expect(q, "q", _FP8, (rows, I))
+    _expect(scales, "scales", torch.float32, (rows,))
+    _require_device(gate_up, row_expert_ids, expert_map, q, scales)
+    q = torch.empty(rows, I, dtype=torch.uint8, device=gate_up.device) if q is None else q
+    scales = torch.empty(rows, dtype=torch.float32, device=gate_up.device) if scales is None else scales
+    check(lib().silu_and_mul_quant_fp8_rows(ptr(_u16(gate_up)), rows, I, ptr(row_expert_ids), ptr(expert_map), E,
+                                            clamp_limit, scale_fmt, static_scale, ptr(q), ptr(scales),
+                                            stream_of(gate_up.device)))
+    return q, scales
+
+
+def moe_fp8_grouped_gemm_channel(A, A_scale, a_row_div, B, B_scale, route, block_m, R, C=None):
+    """Grouped GEMM with per-row activation scales A_scale [rows] and
+    per-channel weight scales B_scale [L, N]; route as moe_fp8_grouped_gemm."""
+    _expect(B, "B", _FP8, (None, None, None))
+    L, N, K = B.shape
+    _expect(A, "A", _FP8, (None, K))
+    _expect(A_scale, "A_scale", torch.float32, (A.shape[0],))
+    _expect(B_scale, "B_scale", torch.float32, (L, N))
+    if R > A.shape[0] * a_row_div:
+        raise ValueError(f"R={R} routes need {-(-R // a_row_div)} rows of A, it has {A.shape[0]}")
+    _expect(C, "C", torch.bfloat16, (R, N))
+    _require_device(A, A_scale, B, B_scale, C)
+    A, B = _u8(A), _u8(B)
+    C = torch.empty(R, N, dtype=torch.bfloat16, device=A.device) if C is None else C
+    check(lib().moe_fp8_grouped_gemm_channel(ptr(A), ptr(A_scale), a_row_div, ptr(B), ptr(B_scale), L, N, K,
+                                             ptr(route["sorted_routes"]), ptr(route["expert_offsets"]),
+                                             ptr(route["block_expert"]), ptr(route["block_start"]),
+                                             ptr(route["num_blocks"]), route["max_blocks"], block_m, R, ptr(_u16(C)),
+                                             stream_of(A.device)))
+    return C
+
+
 def moe_reduce(y, topk_w, topk_ids=None, expert_offset=0, L=0, out=None):
     _expect(topk_w, "topk_w", torch.float32, (None, None))
     M, k = topk_w.shape
@@ -349,8 +417,12 @@ def _check_layer_buffers(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale,
     _expect(w2, "w2", _FP8, (None, H, None))
     Lw, _, I = w2.shape
     _expect(w13, "w13", _FP8, (Lw, 2 * I, H))
-    _expect(w13_scale, "w13_scale", torch.float32, (Lw, 2 * I // 128, H // 128))
-    _expect(w2_scale, "w2_scale", torch.float32, (Lw, H // 128, I // 128))
+    if o.weight_scale_mode == WEIGHT_SCALE_CHANNEL:
+        _expect(w13_scale, "w13_scale", torch.float32, (Lw, 2 * I))
+        _expect(w2_scale, "w2_scale", torch.float32, (Lw, H))
+    else:
+        _expect(w13_scale, "w13_scale", torch.float32, (Lw, 2 * I // 128, H // 128))
+        _expect(w2_scale, "w2_scale", torch.float32, (Lw, H // 128, I // 128))
     L = o.local_num_experts if o.local_num_experts > 0 else E
     if Lw < L:
         raise ValueError(f"the weights hold {Lw} experts, the call addresses {L}")

@@ -50,6 +50,8 @@ struct LayerPlan {
   int64_t max_blocks;
   bool route_single;
   bool rq_fused;  // general path: route preparation carries the input quantisation
+  bool channel;   // the W8A8 variant: per-row activation and per-channel weight scales
+  float a1_static, a2_static;
   int mode;  // kModeGeneral, kModeDecode, kModeToken
   size_t off_aq, off_as, off_sorted, off_eoff, off_bexp, off_bstart, off_nb, off_rws, off_h13, off_q, off_s,
       off_y, off_act, total;
@@ -61,6 +63,8 @@ const char* const kGeneralStages[] = {"route_prepare", "quant_fp8", "gate_up_gem
 // fewer): stage 0 covers both.
 const char* const kGeneralFusedStages[] = {"route_prepare_quant", "gate_up_gemm", "silu_and_mul_quant", "down_gemm",
                                            "moe_reduce"};
+const char* const kChannelStages[] = {"route_prepare", "quant_fp8_rows", "gate_up_gemm_channel",
+                                      "silu_and_mul_quant_rows", "down_gemm_channel", "moe_reduce"};
 const char* const kDecodeStages[] = {"decode_gate_up_swiglu", "decode_down_reduce"};
 const char* const kTokenStages[] = {"token_gate_up_swiglu", "token_down_reduce"};
 enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
@@ -97,8 +101,11 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.clamp = o.clamp_limit;
   p.block_m = o.block_m > 0 ? o.block_m : auto_block_m(p.R, p.L);
   p.max_blocks = bfp8moe_max_blocks(p.R, p.L, p.block_m);
-  const bool fits = bfp8::decode_path_fits(M, H, k, I);
-  const bool token_fits = bfp8::token_path_fits(M, H, k, I);
+  p.channel = o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_CHANNEL;
+  p.a1_static = o.act_static_scale;
+  p.a2_static = o.inter_static_scale;
+  const bool fits = !p.channel && bfp8::decode_path_fits(M, H, k, I);
+  const bool token_fits = !p.channel && bfp8::token_path_fits(M, H, k, I);
   if (o.flags & BFP8MOE_FLAG_LAYER_GENERAL)
     p.mode = kModeGeneral;
   else if (o.flags & BFP8MOE_FLAG_LAYER_DECODE)
@@ -115,7 +122,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
     p.route_single = false;
   else
     p.route_single = bfp8::route_prep_single_fits(p.R, p.L);
-  p.rq_fused = bfp8::route_prep_can_quant(p.route_single, p.L);
+  p.rq_fused = !p.channel && bfp8::route_prep_can_quant(p.route_single, p.L);
   size_t o_ = 0;
   auto take = [&](size_t bytes) {
     size_t at = o_;
@@ -129,7 +136,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   }
   p.off_act = 0;
   p.off_aq = take((size_t)M * H);
-  p.off_as = take(sizeof(float) * (size_t)M * (H / 128));
+  p.off_as = take(sizeof(float) * (size_t)M * (p.channel ? 1 : H / 128));
   p.off_sorted = take(sizeof(int32_t) * (size_t)p.R);
   p.off_eoff = take(sizeof(int32_t) * ((size_t)p.L + 1));
   p.off_bexp = take(sizeof(int32_t) * (size_t)p.max_blocks);
@@ -138,7 +145,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.off_rws = take(p.route_single ? 0 : bfp8::route_prep_ws_bytes(p.R, p.L));
   p.off_h13 = take(sizeof(uint16_t) * (size_t)p.R * 2 * I);
   p.off_q = take((size_t)p.R * I);
-  p.off_s = take(sizeof(float) * (size_t)p.R * (I / 128));
+  p.off_s = take(sizeof(float) * (size_t)p.R * (p.channel ? 1 : I / 128));
   p.off_y = take(sizeof(uint16_t) * (size_t)p.R * H);
   p.total = o_;
 }
@@ -160,6 +167,9 @@ void bfp8moe_opts_init(bfp8moe_opts_t* opts) {
   opts->local_num_experts = 0;
   opts->flags = 0;
   opts->stage_events = nullptr;
+  opts->weight_scale_mode = BFP8MOE_WEIGHT_SCALE_BLOCK;
+  opts->act_static_scale = 0.0f;
+  opts->inter_static_scale = 0.0f;
 }
 
 const char* bfp8moe_status_string(int status) {
@@ -294,6 +304,66 @@ bfp8moe_status_t moe_fp8_grouped_gemm(const uint8_t* A, const float* A_scale, in
                     "moe_fp8_grouped_gemm");
 }
 
+bfp8moe_status_t quant_fp8_rows(const uint16_t* x, int64_t rows, int32_t K, int32_t scale_fmt, float static_scale,
+                                uint8_t* q, float* scales, void* stream) {
+  REQUIRE(rows >= 0 && rows <= 0x7FFFFFFF, "rows=%lld out of range", (long long)rows);
+  REQUIRE(bfp8::rows_quant_fits(K), "K=%d must be a positive multiple of 128 up to 8192", K);
+  REQUIRE(valid_fmt(scale_fmt), "scale_fmt=%d is not 0 (fp32) or 1 (ue8m0)", scale_fmt);
+  REQUIRE(isfinite(static_scale) && static_scale >= 0, "static_scale must be finite and >= 0 (0 = dynamic)");
+  REQUIRE(rows == 0 || (x && q && scales), "x, q and scales must be non-null");
+  REQUIRE(aligned16(x) && aligned16(q), "x and q must be 16-byte aligned");
+  return hip_status(bfp8::launch_quant_fp8_rows(x, rows, K, scale_fmt, static_scale, q, scales, (hipStream_t)stream),
+                    "quant_fp8_rows");
+}
+
+bfp8moe_status_t silu_and_mul_quant_fp8_rows(const uint16_t* gate_up, int64_t rows, int32_t I,
+                                             const int32_t* row_expert_ids, const int32_t* expert_map, int32_t E,
+                                             float clamp_limit, int32_t scale_fmt, float static_scale, uint8_t* q,
+                                             float* scales, void* stream) {
+  REQUIRE(rows >= 0 && rows <= 0x7FFFFFFF, "rows=%lld out of range", (long long)rows);
+  REQUIRE(bfp8::rows_quant_fits(I), "I=%d must be a positive multiple of 128 up to 8192", I);
+  REQUIRE(valid_fmt(scale_fmt), "scale_fmt=%d is not 0 (fp32) or 1 (ue8m0)", scale_fmt);
+  REQUIRE(!isnan(clamp_limit) && clamp_limit > 0, "clamp_limit must be positive (+inf = unclamped)");
+  REQUIRE(isfinite(static_scale) && static_scale >= 0, "static_scale must be finite and >= 0 (0 = dynamic)");
+  REQUIRE(rows == 0 || (gate_up && q && scales), "gate_up, q and scales must be non-null");
+  REQUIRE(expert_map == nullptr || row_expert_ids != nullptr, "expert_map requires row_expert_ids");
+  REQUIRE(row_expert_ids == nullptr || E >= 1, "E=%d must be >= 1 when row_expert_ids is given", E);
+  REQUIRE(aligned16(gate_up) && aligned16(q), "gate_up and q must be 16-byte aligned");
+  bfp8::RowFilter f;
+  f.ids = row_expert_ids;
+  f.map = expert_map;
+  f.E = E;
+  f.mode = row_expert_ids == nullptr ? bfp8::kRowsAll : (expert_map ? bfp8::kRowsIdsMap : bfp8::kRowsIds);
+  return hip_status(bfp8::launch_silu_and_mul_quant_rows(gate_up, rows, I, f, clamp_limit, scale_fmt, static_scale, q,
+                                                         scales, (hipStream_t)stream),
+                    "silu_and_mul_quant_fp8_rows");
+}
+
+bfp8moe_status_t moe_fp8_grouped_gemm_channel(const uint8_t* A, const float* A_scale, int32_t a_row_div,
+                                              const uint8_t* B, const float* B_scale, int32_t L, int32_t N,
+                                              int32_t K, const int32_t* sorted_routes,
+                                              const int32_t* expert_offsets, const int32_t* block_expert,
+                                              const int32_t* block_start, const int32_t* num_blocks,
+                                              int64_t max_blocks, int32_t block_m, int64_t R, uint16_t* C,
+                                              void* stream) {
+  REQUIRE(N > 0 && N % 128 == 0, "N=%d must be a positive multiple of 128", N);
+  REQUIRE(K > 0 && K % 128 == 0, "K=%d must be a positive multiple of 128", K);
+  REQUIRE(L >= 1, "L=%d must be >= 1", L);
+  REQUIRE(a_row_div >= 1, "a_row_div=%d must be >= 1", a_row_div);
+  REQUIRE(block_m == 16 || block_m == 32 || block_m == 64, "block_m=%d must be 16, 32 or 64", block_m);
+  REQUIRE(R >= 0 && R <= 0x7FFFFFFF, "R=%lld out of range", (long long)R);
+  REQUIRE(max_blocks >= 0, "max_blocks must be >= 0");
+  REQUIRE(max_blocks == 0 || (A && A_scale && B && B_scale && sorted_routes && expert_offsets && block_expert &&
+                              block_start && num_blocks && C),
+          "all pointers must be non-null");
+  REQUIRE(aligned16(A) && aligned16(B) && aligned16(C) && aligned16(B_scale),
+          "A, B, B_scale and C must be 16-byte aligned");
+  return hip_status(bfp8::launch_grouped_gemm(A, A_scale, a_row_div, B, B_scale, N, K, sorted_routes,
+                                              expert_offsets, block_expert, block_start, num_blocks, max_blocks,
+                                              block_m, C, (hipStream_t)stream, true),
+                    "moe_fp8_grouped_gemm_channel");
+}
+
 bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_t* topk_ids, int32_t expert_offset,
                             int32_t L, int64_t M, int32_t k, int32_t H, uint16_t* out, void* stream) {
   REQUIRE(M >= 0 && k >= 1, "M=%lld k=%d invalid", (long long)M, k);
@@ -360,6 +430,17 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
               (BFP8MOE_FLAG_ROUTE_SINGLE_WG | BFP8MOE_FLAG_ROUTE_MULTI_WG),
           "route flags are exclusive");
   if (L > 2048) return fail(BFP8MOE_ERR_UNSUPPORTED, "local_num_experts=%d above 2048", L);
+  REQUIRE(o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_BLOCK || o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_CHANNEL,
+          "weight_scale_mode=%d is not 0 (block) or 1 (channel)", o.weight_scale_mode);
+  REQUIRE(isfinite(o.act_static_scale) && o.act_static_scale >= 0 && isfinite(o.inter_static_scale) &&
+              o.inter_static_scale >= 0,
+          "static scales must be finite and >= 0 (0 = dynamic)");
+  if (o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_CHANNEL) {
+    if (!bfp8::rows_quant_fits(H) || !bfp8::rows_quant_fits(I))
+      return fail(BFP8MOE_ERR_UNSUPPORTED, "the W8A8 (channel) variant takes H and I up to 8192 (H=%d I=%d)", H, I);
+    if (o.flags & (BFP8MOE_FLAG_LAYER_DECODE | BFP8MOE_FLAG_LAYER_TOKEN))
+      return fail(BFP8MOE_ERR_UNSUPPORTED, "the W8A8 (channel) variant runs on the general path only");
+  }
   if ((o.flags & BFP8MOE_FLAG_LAYER_DECODE) && M > 0 && !bfp8::decode_path_fits(M, H, k, I))
     return fail(BFP8MOE_ERR_UNSUPPORTED,
                 "small-batch path forced but M=%lld k=%d H=%d I=%d exceed its limits (M<=8, k<=8, H<=8192, "
@@ -391,6 +472,7 @@ int32_t fused_moe_block_fp8_stages(int64_t M, int32_t H, int32_t k, int32_t E, i
   plan_layer(p, M, H, k, E, I, o);
   const char* const* list = p.mode == kModeToken    ? kTokenStages
                             : p.mode == kModeDecode ? kDecodeStages
+                            : p.channel             ? kChannelStages
                             : p.rq_fused            ? kGeneralFusedStages
                                                     : kGeneralStages;
   const int32_t n = plan_stages(p);
@@ -425,6 +507,8 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
           "all pointers must be non-null");
   REQUIRE(aligned16(hidden) && aligned16(w13) && aligned16(w2) && aligned16(out),
           "hidden, w13, w2 and out must be 16-byte aligned");
+  REQUIRE(o.weight_scale_mode != BFP8MOE_WEIGHT_SCALE_CHANNEL || (aligned16(w13_scale) && aligned16(w2_scale)),
+          "channel weight scales must be 16-byte aligned");
   if (M == 0) return BFP8MOE_OK;
   LayerPlan p;
   plan_layer(p, M, H, k, E, I, o);
@@ -480,13 +564,15 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: route prep");
   if (sq == 1) {
     hook.before(++st_i, st);
-    if (hook.run(st_i)) e = bfp8::launch_quant_fp8(hidden, M, H, p.fmt, aq, as, st);
+    if (hook.run(st_i))
+      e = p.channel ? bfp8::launch_quant_fp8_rows(hidden, M, H, p.fmt, p.a1_static, aq, as, st)
+                    : bfp8::launch_quant_fp8(hidden, M, H, p.fmt, aq, as, st);
     if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: input quant");
   }
   hook.before(++st_i, st);
   if (hook.run(st_i))
     e = bfp8::launch_grouped_gemm(aq, as, k, w13, w13_scale, 2 * I, H, sorted, eoff, bexp, bstart, nb, p.max_blocks,
-                                  p.block_m, h13, st);
+                                  p.block_m, h13, st, p.channel);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: gate/up GEMM");
   bfp8::RowFilter f;
   f.ids = topk_ids;
@@ -494,12 +580,14 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   f.L = p.L;
   f.mode = bfp8::kRowsLocalSlice;
   hook.before(++st_i, st);
-  if (hook.run(st_i)) e = bfp8::launch_silu_and_mul_quant(h13, p.R, I, f, p.clamp, p.fmt, q, s, st);
+  if (hook.run(st_i))
+    e = p.channel ? bfp8::launch_silu_and_mul_quant_rows(h13, p.R, I, f, p.clamp, p.fmt, p.a2_static, q, s, st)
+                  : bfp8::launch_silu_and_mul_quant(h13, p.R, I, f, p.clamp, p.fmt, q, s, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: act+quant");
   hook.before(++st_i, st);
   if (hook.run(st_i))
     e = bfp8::launch_grouped_gemm(q, s, 1, w2, w2_scale, H, I, sorted, eoff, bexp, bstart, nb, p.max_blocks,
-                                  p.block_m, y, st);
+                                  p.block_m, y, st, p.channel);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: down GEMM");
   hook.before(++st_i, st);
   if (hook.run(st_i)) e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, p.offset, p.L, M, k, H, out, st);

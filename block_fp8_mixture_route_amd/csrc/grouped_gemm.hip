@@ -1,6 +1,8 @@
 // grouped_gemm.hip -- block-FP8 grouped GEMM over compact route blocks, gfx950.
 //
-// [P3 Purpose] W8A8 with [128, 128] weight blocks and 1x128 activation groups.
+// [P3 Purpose] W8A8 with [128, 128] weight blocks and 1x128 activation groups;
+// [P2 Reviewed changes: w8a8.py] also per-row activation and per-channel
+// weight scales (the W8A8 variant).
 // [P1 Modification, Active-expert block scheduling] one workgroup tile per
 // (compact block, 128 output rows); tiles past the device-side block count
 // exit at once, so inactive experts cost nothing but an early return.
@@ -62,7 +64,10 @@ struct XRegs<false, XL, CT> {
   typedef v8i type[CT];
 };
 
-template <int BM>
+// kChannel (the W8A8 variant): As holds one scale per activation row and Bs
+// one per weight row (output channel); the K loop adds the chunks' sums
+// unscaled and the epilogue applies a_scale(route) * w_scale(row).
+template <int BM, bool kChannel>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 64 ? 3 : 1))) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, int a_row_div, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, int N, int K, const int32_t* __restrict__ sorted_routes,
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
     route[t] = j < len ? sorted_routes[start + j] : -1;
     const int64_t ar = route[t] >= 0 ? route[t] / a_row_div : 0;
     arow[t] = A + (size_t)ar * K;
-    asrow[t] = As + (size_t)ar * G;
+    asrow[t] = As + (size_t)ar * (kChannel ? 1 : G);
   }
   // shared path: the activation rows this thread loads, row tid / 8 + 32 x
   // of the block, bytes 16 (tid % 8) .. + 15 of each chunk (full 128-byte
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
   // weight rows of this lane
   const int n0 = nt * kBN + wave * kWN;
   const uint8_t* wrow0 = B + ((size_t)e * N + n0) * K;  // the wave's first weight row
-  const float* ws = Bs + ((size_t)e * n_tiles + nt) * G;
+  const float* ws = kChannel ? Bs + (size_t)e * N + n0 : Bs + ((size_t)e * n_tiles + nt) * G;
 
   v4f acc[kRT][CT];
 #pragma unroll
@@ -168,9 +173,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
   // so the wait before the multiply covers the current chunk only.
   auto step = [&](int gn, u32x4 (&wc)[4], auto& xc, float (&sc)[CT], float wsc, u32x4 (&wn)[4], auto& xn,
                   float (&sn)[CT], float& wsn, u32x4* xb) __attribute__((always_inline)) {
-    wsn = ws[gn];
+    if constexpr (!kChannel) {
+      wsn = ws[gn];
 #pragma unroll
-    for (int t = 0; t < CT; t++) sn[t] = asrow[t][gn];
+      for (int t = 0; t < CT; t++) sn[t] = asrow[t][gn];
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) wn[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * K + (size_t)gn * kGroup);
     if constexpr (kSharedX) {
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
       } else {
         xf = xc[t];
       }
-      const float asc = route[t] >= 0 ? sc[t] * wsc : 0.0f;
+      const float asc = route[t] >= 0 ? (kChannel ? 1.0f : sc[t] * wsc) : 0.0f;
 #pragma unroll
       for (int i = 0; i < kRT; i++) {
         const v4f p = mfma_f8_16x16x128(wa[i], xf, v4f{0.f, 0.f, 0.f, 0.f});
@@ -234,9 +241,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
   u32x4 w0[4], w1[4];
   XR x0, x1;
   float s0[CT], s1[CT];
-  float ws0 = ws[0], ws1 = 0.0f;
+  float ws0 = kChannel ? 1.0f : ws[0], ws1 = 0.0f;
 #pragma unroll
-  for (int t = 0; t < CT; t++) s0[t] = asrow[t][0];
+  for (int t = 0; t < CT; t++) s0[t] = kChannel ? 1.0f : asrow[t][0];
 #pragma unroll
   for (int i = 0; i < 4; i++) w0[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * K);
   if constexpr (kSharedX) {
@@ -258,6 +265,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
   if (g < G) step(g, w0, x0, s0, ws0, w1, x1, s1, ws1, s_x[0]);
 
   // epilogue: lane holds rows n0 + 16*i + 4*kq + v (v = 0..3) of route[t]
+  if constexpr (kChannel) {
+    float4 wsv[kRT];
+#pragma unroll
+    for (int i = 0; i < kRT; i++) wsv[i] = *reinterpret_cast<const float4*>(ws + i * 16 + 4 * kq);
+#pragma unroll
+    for (int t = 0; t < CT; t++) {
+      const float a_s = asrow[t][0];
+#pragma unroll
+      for (int i = 0; i < kRT; i++) {
+        acc[i][t][0] *= a_s * wsv[i].x;
+        acc[i][t][1] *= a_s * wsv[i].y;
+        acc[i][t][2] *= a_s * wsv[i].z;
+        acc[i][t][3] *= a_s * wsv[i].w;
+      }
+    }
+  }
 #pragma unroll
   for (int t = 0; t < CT; t++) {
     if (route[t] < 0) continue;
@@ -278,16 +301,21 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
                                const float* Bs, int N, int K, const int32_t* sorted_routes,
                                const int32_t* expert_offsets, const int32_t* block_expert,
                                const int32_t* block_start, const int32_t* num_blocks, int64_t max_blocks,
-                               int block_m, uint16_t* C, hipStream_t stream) {
+                               int block_m, uint16_t* C, hipStream_t stream, bool channel) {
   if (max_blocks == 0 || N / kBN == 0) return hipSuccess;
   const int gb = gemm_group_blocks(max_blocks);
   const int64_t grid = gemm_slots_per_xcd(max_blocks, N / kBN, gb) * kXcd;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
 #define BFP8_GEMM_CASE(BMV)                                                                                   \
   case BMV:                                                                                                   \
-    hipLaunchKernelGGL(grouped_gemm_kernel<BMV>, dim3((unsigned)grid), dim3(kThreads), 0, stream, A, As,      \
-                       a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,     \
-                       num_blocks, max_blocks, gb, C);                                                       \
+    if (channel)                                                                                              \
+      hipLaunchKernelGGL((grouped_gemm_kernel<BMV, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A, \
+                         As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,     \
+                         num_blocks, max_blocks, gb, C);                                                     \
+    else                                                                                                      \
+      hipLaunchKernelGGL((grouped_gemm_kernel<BMV, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A, \
+                         As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,     \
+                         num_blocks, max_blocks, gb, C);                                                     \
     break;
   switch (block_m) {
     BFP8_GEMM_CASE(16)

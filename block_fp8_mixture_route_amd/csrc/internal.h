@@ -113,7 +113,15 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
                                const float* Bs, int N, int K, const int32_t* sorted_routes,
                                const int32_t* expert_offsets, const int32_t* block_expert,
                                const int32_t* block_start, const int32_t* num_blocks, int64_t max_blocks,
-                               int block_m, uint16_t* C, hipStream_t stream);
+                               int block_m, uint16_t* C, hipStream_t stream, bool channel = false);
+
+// W8A8 variant: one scale per activation row (dynamic: amax / 448 of the row
+// in fmt; static_scale > 0: that scale for every row).  Rows of up to 8192.
+bool rows_quant_fits(int K);
+hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t rows, int K, int fmt, float static_scale, uint8_t* q,
+                                 float* s, hipStream_t stream);
+hipError_t launch_silu_and_mul_quant_rows(const uint16_t* gu, int64_t rows, int I, const RowFilter& f, float limit,
+                                          int fmt, float static_scale, uint8_t* q, float* s, hipStream_t stream);
 
 // Small-batch path of the fused layer: gate/up + SwiGLU kernel, then down +
 // moe_reduce kernel.  act: [M*k, I] BF16 scratch.

@@ -103,10 +103,25 @@ typedef struct {
                                    of n stages (fused_moe_block_fp8_stages); event i is recorded on the
                                    stream before stage i, event n after the last.  Events are caller-owned.
                                    For eager calls; not for use under stream capture. */
+    int32_t weight_scale_mode;  /* bfp8moe_weight_scale_t: BLOCK (default) or CHANNEL (the W8A8 variant) */
+    float act_static_scale;     /* CHANNEL only: > 0 a static per-tensor scale of the hidden states;
+                                   0 = one dynamic scale per token (its amax / 448, in scale_fmt) */
+    float inter_static_scale;   /* CHANNEL only: the same for the SwiGLU output (per route row) */
 } bfp8moe_opts_t;
 
+/* How the layer's weights and activations are scaled.
+ * BLOCK:   [128, 128] weight blocks (w13_scale [L, 2I/128, H/128], w2_scale
+ *          [L, H/128, I/128]) and 1x128 activation groups -- the block-FP8
+ *          layer [P3 Purpose: FP8 W8A8 block shape [128, 128]].
+ * CHANNEL: one fp32 scale per weight row (w13_scale [L, 2I], w2_scale [L, H])
+ *          and one per activation row, dynamic or static -- the W8A8 variant
+ *          [P2 Reviewed changes: w8a8.py, the static FP8 MoE backend].  Runs
+ *          the general path (six launches); H and I at most 8192. */
+typedef enum { BFP8MOE_WEIGHT_SCALE_BLOCK = 0, BFP8MOE_WEIGHT_SCALE_CHANNEL = 1 } bfp8moe_weight_scale_t;
+
 /* Fill *opts with the defaults: block_m 0, FP32 scales, no clamp, the full
- * expert range, no flags, no stage events.  opts: host pointer. */
+ * expert range, no flags, no stage events, block scaling.  opts: host
+ * pointer. */
 void bfp8moe_opts_init(bfp8moe_opts_t* opts);
 
 const char* bfp8moe_status_string(int status);
@@ -201,6 +216,22 @@ bfp8moe_status_t silu_and_mul_quant_fp8(const uint16_t* gate_up, int64_t rows, i
                                         float clamp_limit, int32_t scale_fmt, uint8_t* q, float* scales,
                                         void* stream);
 
+/* The W8A8 variant's quantisation [P2 Reviewed changes: w8a8.py, the static
+ * FP8 MoE backend]: one scale per row.  x [rows, K] BF16 -> q [rows, K]
+ * E4M3FN and scales [rows] fp32; the scale is static_scale when > 0 (codes
+ * saturate at +-448), else the row's amax / 448 over all K (in scale_fmt, as
+ * quant_fp8's group scale).  K a positive multiple of 128, at most 8192. */
+bfp8moe_status_t quant_fp8_rows(const uint16_t* x, int64_t rows, int32_t K, int32_t scale_fmt, float static_scale,
+                                uint8_t* q, float* scales, void* stream);
+
+/* Fused SwiGLU + per-row quantisation (the W8A8 variant): for every live row
+ * (filtering as silu_and_mul_quant_fp8), q [rows, I] and scales [rows] equal
+ * quant_fp8_rows(silu_and_mul(gate_up)).  I at most 8192. */
+bfp8moe_status_t silu_and_mul_quant_fp8_rows(const uint16_t* gate_up, int64_t rows, int32_t I,
+                                             const int32_t* row_expert_ids, const int32_t* expert_map, int32_t E,
+                                             float clamp_limit, int32_t scale_fmt, float static_scale, uint8_t* q,
+                                             float* scales, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Block-FP8 grouped GEMM over compact blocks                                */
 /* [P3 Purpose: FP8 W8A8 block shape [128, 128]; P1 Modification:            */
@@ -226,6 +257,18 @@ bfp8moe_status_t moe_fp8_grouped_gemm(const uint8_t* A, const float* A_scale, in
                                       const int32_t* block_expert, const int32_t* block_start,
                                       const int32_t* num_blocks, int64_t max_blocks, int32_t block_m,
                                       int64_t R, uint16_t* C, void* stream);
+
+/* The grouped GEMM of the W8A8 variant: as moe_fp8_grouped_gemm with one
+ * activation scale per row, A_scale [R/a_row_div rows], and one weight scale
+ * per output channel, B_scale [L, N] (16-byte aligned):
+ *   C[r, n] = bf16( A_scale[r/a_row_div] * B_scale[e, n] * sum_i A[r/a_row_div, i] * B[e, n, i] ). */
+bfp8moe_status_t moe_fp8_grouped_gemm_channel(const uint8_t* A, const float* A_scale, int32_t a_row_div,
+                                              const uint8_t* B, const float* B_scale, int32_t L, int32_t N,
+                                              int32_t K, const int32_t* sorted_routes,
+                                              const int32_t* expert_offsets, const int32_t* block_expert,
+                                              const int32_t* block_start, const int32_t* num_blocks,
+                                              int64_t max_blocks, int32_t block_m, int64_t R, uint16_t* C,
+                                              void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Single-group top-k router                                                 */

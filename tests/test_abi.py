@@ -39,9 +39,24 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_opts_layout_and_defaults():
-    assert ctypes.sizeof(_lib.Opts) == 32
+    assert ctypes.sizeof(_lib.Opts) == 48  # 6 words, a pointer, 3 words, padding to 8 bytes
     o = bfp8.opts()
     assert o.block_m == 0 and o.scale_fmt == 0 and math.isinf(o.clamp_limit) and o.flags == 0
+    assert o.weight_scale_mode == bfp8.WEIGHT_SCALE_BLOCK and o.act_static_scale == 0 and o.inter_static_scale == 0
+
+
+def test_w8a8_layer_runs_the_general_path_only():
+    o = bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL)
+    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == [
+        "route_prepare", "quant_fp8_rows", "gate_up_gemm_channel", "silu_and_mul_quant_rows", "down_gemm_channel",
+        "moe_reduce"]
+    for flag in (bfp8.FLAG_LAYER_TOKEN, bfp8.FLAG_LAYER_DECODE):
+        with pytest.raises(bfp8.BFP8MoEError):
+            bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(weight_scale_mode=1, flags=flag))
+    with pytest.raises(bfp8.BFP8MoEError):  # rows beyond 8192
+        bfp8.fused_moe_stages(1, 8320, 8, 256, 256, o)
+    with pytest.raises(bfp8.BFP8MoEError):
+        bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(weight_scale_mode=1, act_static_scale=-1.0))
 
 
 def test_stage_lists():
