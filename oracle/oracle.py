@@ -177,6 +177,26 @@ def max_blocks(R: int, L: int, block_m: int) -> int:
     return lib().oracle_max_blocks(R, L, block_m)
 
 
+def apply_expert_map(topk_ids, expert_map, L: int):
+    """Local expert ids under an expert map (vLLM PR "[Kernel][Perf] Fuse
+    clamped MoE activation and UE8M0 FP8 block quantization", Purpose: rows
+    of experts the map marks non-local are filtered out).  Reading: global id
+    i selects local expert expert_map[i]; an id outside [0, E) or an entry
+    outside [0, L) leaves the route masked (-1).  The result feeds every
+    other oracle function with expert_offset 0 and L local experts, so the
+    map form of each step is that step on the mapped ids."""
+    ids = as_np(topk_ids, np.int32)
+    emap = as_np(expert_map, np.int32).reshape(-1)
+    out = np.full(ids.shape, -1, np.int32)
+    for idx in np.ndindex(ids.shape):
+        g = int(ids[idx])
+        if 0 <= g < emap.size:
+            e = int(emap[g])
+            if 0 <= e < L:
+                out[idx] = e
+    return out
+
+
 def route_prepare(topk_ids, expert_offset: int, L: int, block_m: int, with_blocks: bool = True):
     ids = as_np(topk_ids, np.int32).reshape(-1)
     R = ids.size
