@@ -47,6 +47,7 @@ class Opts(ctypes.Structure):
         ("weight_scale_mode", ctypes.c_int32),
         ("act_static_scale", ctypes.c_float),
         ("inter_static_scale", ctypes.c_float),
+        ("expert_map", ctypes.c_void_p),
     ]
 
 
@@ -71,6 +72,8 @@ SIGNATURES = {
     "bfp8moe_max_blocks": (_i64, [_i64, _i32, _i32]),
     "moe_route_prepare_workspace_size": (_sz, [_i64, _i32, _u32]),
     "moe_route_prepare": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _P, _P, _P, _P, _i64, _P, _P, _sz, _u32, _P]),
+    "moe_route_prepare_map": (ctypes.c_int, [_P, _i64, _P, _i32, _i32, _i32, _P, _P, _P, _P, _i64, _P, _P, _sz, _u32,
+                                             _P]),
     "quant_fp8": (ctypes.c_int, [_P, _i64, _i32, _i32, _P, _P, _P]),
     "silu_and_mul": (ctypes.c_int, [_P, _i64, _i32, _f32, _P, _P]),
     "silu_and_mul_quant_fp8": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _f32, _i32, _P, _P, _P]),
@@ -81,6 +84,7 @@ SIGNATURES = {
     "moe_fp8_grouped_gemm_channel": (ctypes.c_int, [_P, _P, _i32, _P, _P, _i32, _i32, _i32, _P, _P, _P, _P, _P,
                                                     _i64, _i32, _i64, _P, _P]),
     "moe_reduce": (ctypes.c_int, [_P, _P, _P, _i32, _i32, _i64, _i32, _i32, _P, _P]),
+    "moe_reduce_map": (ctypes.c_int, [_P, _P, _P, _P, _i32, _i32, _i64, _i32, _i32, _P, _P]),
     "moe_router_topk": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _P, _i32, ctypes.c_double, _P, _P, _P]),
     "moe_router_noaux_tc": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _i32, _P, _i32, ctypes.c_double, _P, _P,
                                            _P]),
@@ -177,13 +181,21 @@ def wait_faults(clear=True) -> int:
 
 
 def opts(block_m=0, scale_fmt=SCALE_FP32, clamp_limit=math.inf, expert_offset=0, local_num_experts=0, flags=0,
-         weight_scale_mode=WEIGHT_SCALE_BLOCK, act_static_scale=0.0, inter_static_scale=0.0):
+         weight_scale_mode=WEIGHT_SCALE_BLOCK, act_static_scale=0.0, inter_static_scale=0.0, expert_map=None):
+    """Layer options.  expert_map: device int32 [E] (global expert -> local
+    expert, outside [0, local_num_experts) = held elsewhere), kept alive by
+    the returned object."""
     o = Opts()
     lib().bfp8moe_opts_init(ctypes.byref(o))
     o.block_m, o.scale_fmt, o.clamp_limit = block_m, scale_fmt, clamp_limit
     o.expert_offset, o.local_num_experts, o.flags = expert_offset, local_num_experts, flags
     o.weight_scale_mode, o.act_static_scale, o.inter_static_scale = weight_scale_mode, act_static_scale, \
         inter_static_scale
+    if expert_map is not None:
+        _expect(expert_map, "expert_map", torch.int32, (None,))
+        _require_device(expert_map)
+        o.expert_map = ptr(expert_map).value
+        o._expert_map = expert_map  # the pointer's owner
     return o
 
 
@@ -193,9 +205,16 @@ def max_blocks(R: int, L: int, block_m: int) -> int:
     return lib().bfp8moe_max_blocks(R, L, block_m)
 
 
-def moe_route_prepare(topk_ids: torch.Tensor, expert_offset: int, L: int, block_m: int, with_blocks=True, flags=0):
+def moe_route_prepare(topk_ids: torch.Tensor, expert_offset: int, L: int, block_m: int, with_blocks=True, flags=0,
+                      expert_map=None):
+    """Route preparation over the slice [expert_offset, expert_offset + L),
+    or, with expert_map (device int32 [E]; expert_offset must be 0), over the
+    experts the map sends into [0, L)."""
     _expect(topk_ids, "topk_ids", torch.int32)
-    _require_device(topk_ids)
+    _expect(expert_map, "expert_map", torch.int32, (None,))
+    _require_device(topk_ids, expert_map)
+    if expert_map is not None and expert_offset != 0:
+        raise ValueError("expert_map and expert_offset are exclusive")
     ids = topk_ids.reshape(-1)
     R = ids.numel()
     dev = ids.device
@@ -210,9 +229,12 @@ def moe_route_prepare(topk_ids: torch.Tensor, expert_offset: int, L: int, block_
     )
     wsb = lib().moe_route_prepare_workspace_size(R, L, flags)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    check(lib().moe_route_prepare(ptr(ids), R, expert_offset, L, block_m, ptr(out["sorted_routes"]),
-                                  ptr(out["expert_offsets"]), ptr(out["block_expert"]), ptr(out["block_start"]),
-                                  mb, ptr(out["num_blocks"]), ptr(ws), wsb, flags, stream_of(dev)))
+    outs = (ptr(out["sorted_routes"]), ptr(out["expert_offsets"]), ptr(out["block_expert"]), ptr(out["block_start"]),
+            mb, ptr(out["num_blocks"]), ptr(ws), wsb, flags, stream_of(dev))
+    if expert_map is None:
+        check(lib().moe_route_prepare(ptr(ids), R, expert_offset, L, block_m, *outs))
+    else:
+        check(lib().moe_route_prepare_map(ptr(ids), R, ptr(expert_map), expert_map.numel(), L, block_m, *outs))
     out["_ws"] = ws  # keep alive until the stream has consumed it
     return out
 
@@ -332,17 +354,25 @@ def moe_fp8_grouped_gemm_channel(A, A_scale, a_row_div, B, B_scale, route, block
     return C
 
 
-def moe_reduce(y, topk_w, topk_ids=None, expert_offset=0, L=0, out=None):
+def moe_reduce(y, topk_w, topk_ids=None, expert_offset=0, L=0, out=None, expert_map=None):
+    """Weighted top-k reduction; live routes: all (topk_ids None), the slice
+    [expert_offset, expert_offset + L), or with expert_map (device int32 [E])
+    the ids the map sends into [0, L)."""
     _expect(topk_w, "topk_w", torch.float32, (None, None))
     M, k = topk_w.shape
     _expect(y, "y", torch.bfloat16, (M * k, None))
     H = y.shape[1]
     _expect(topk_ids, "topk_ids", torch.int32, (M, k))
     _expect(out, "out", torch.bfloat16, (M, H))
-    _require_device(y, topk_w, topk_ids, out)
+    _expect(expert_map, "expert_map", torch.int32, (None,))
+    _require_device(y, topk_w, topk_ids, out, expert_map)
     out = torch.empty(M, H, dtype=torch.bfloat16, device=y.device) if out is None else out
-    check(lib().moe_reduce(ptr(_u16(y)), ptr(topk_w), ptr(topk_ids), expert_offset, L, M, k, H, ptr(_u16(out)),
-                           stream_of(y.device)))
+    if expert_map is None:
+        check(lib().moe_reduce(ptr(_u16(y)), ptr(topk_w), ptr(topk_ids), expert_offset, L, M, k, H, ptr(_u16(out)),
+                               stream_of(y.device)))
+    else:
+        check(lib().moe_reduce_map(ptr(_u16(y)), ptr(topk_w), ptr(topk_ids), ptr(expert_map), expert_map.numel(), L,
+                                   M, k, H, ptr(_u16(out)), stream_of(y.device)))
     return out
 
 
@@ -424,6 +454,8 @@ def _check_layer_buffers(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale,
         _expect(w13_scale, "w13_scale", torch.float32, (Lw, 2 * I // 128, H // 128))
         _expect(w2_scale, "w2_scale", torch.float32, (Lw, H // 128, I // 128))
     L = o.local_num_experts if o.local_num_experts > 0 else E
+    if o.expert_map and getattr(o, "_expert_map", None) is not None and o._expert_map.numel() != E:
+        raise ValueError(f"the expert map has {o._expert_map.numel()} entries, E is {E}")
     if Lw < L:
         raise ValueError(f"the weights hold {Lw} experts, the call addresses {L}")
     _expect(out, "out", torch.bfloat16, (M, H))

@@ -46,6 +46,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct LayerPlan {
   int64_t M, R;
   int32_t H, I, k, E, L, offset, block_m, fmt;
+  const int32_t* map;  // expert map (device, [E]) or null: the slice [offset, offset + L)
   float clamp;
   int64_t max_blocks;
   bool route_single;
@@ -97,6 +98,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.R = M * k;
   p.L = o.local_num_experts > 0 ? o.local_num_experts : E;
   p.offset = o.expert_offset;
+  p.map = o.expert_map;
   p.fmt = o.scale_fmt;
   p.clamp = o.clamp_limit;
   p.block_m = o.block_m > 0 ? o.block_m : auto_block_m(p.R, p.L);
@@ -150,9 +152,60 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.total = o_;
 }
 
+bfp8::ExpertSel layer_sel(const LayerPlan& p) {
+  bfp8::ExpertSel sel;
+  sel.map = p.map;
+  sel.E = p.E;
+  sel.offset = p.offset;
+  sel.L = p.L;
+  return sel;
+}
+
 int plan_stages(const LayerPlan& p) { return p.mode == kModeGeneral ? (p.rq_fused ? 5 : 6) : 2; }
 
 bool valid_fmt(int32_t f) { return f == BFP8MOE_SCALE_FP32 || f == BFP8MOE_SCALE_UE8M0; }
+
+// Route preparation under either form of the local expert set (checks, then
+// the launch).
+bfp8moe_status_t route_prepare_sel(const int32_t* topk_ids, int64_t R, const bfp8::ExpertSel& sel, int32_t block_m,
+                                   int32_t* sorted_routes, int32_t* expert_offsets, int32_t* block_expert,
+                                   int32_t* block_start, int64_t max_blocks, int32_t* num_blocks, void* ws,
+                                   size_t ws_bytes, uint32_t flags, void* stream) {
+  REQUIRE(R >= 0 && R <= 0x7FFFFFFF, "R=%lld out of range [0, 2^31)", (long long)R);
+  const int32_t L = sel.L;
+  REQUIRE(L >= 1, "local_num_experts=%d must be >= 1", L);
+  REQUIRE(block_m >= 1, "block_m=%d must be >= 1", block_m);
+  REQUIRE(R == 0 || (topk_ids && sorted_routes), "topk_ids and sorted_routes must be non-null");
+  REQUIRE(expert_offsets && num_blocks, "expert_offsets and num_blocks must be non-null");
+  REQUIRE((block_expert == nullptr) == (block_start == nullptr),
+          "block_expert and block_start must both be given or both be null");
+  const int64_t need_blocks = bfp8moe_max_blocks(R, L, block_m);
+  REQUIRE(block_expert == nullptr || max_blocks >= need_blocks, "max_blocks=%lld < required %lld",
+          (long long)max_blocks, (long long)need_blocks);
+  if (L > 2048) return fail(BFP8MOE_ERR_UNSUPPORTED, "local_num_experts=%d above 2048", L);
+  const bool single = (flags & BFP8MOE_FLAG_ROUTE_SINGLE_WG)  ? true
+                      : (flags & BFP8MOE_FLAG_ROUTE_MULTI_WG) ? false
+                                                               : bfp8::route_prep_single_fits(R, L);
+  const size_t need = single ? 0 : bfp8::route_prep_ws_bytes(R, L);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(BFP8MOE_ERR_WORKSPACE, "route workspace %zu bytes < required %zu", ws_bytes, need);
+  return hip_status(bfp8::launch_route_prepare(topk_ids, R, sel, block_m, sorted_routes, expert_offsets,
+                                               block_expert, block_start, block_expert ? max_blocks : 0, num_blocks,
+                                               single, ws, (hipStream_t)stream),
+                    "moe_route_prepare");
+}
+
+// moe_reduce under either form of the local expert set.
+bfp8moe_status_t reduce_sel(const uint16_t* y, const float* topk_w, const int32_t* topk_ids,
+                            const bfp8::ExpertSel& sel, int64_t M, int32_t k, int32_t H, uint16_t* out,
+                            void* stream) {
+  REQUIRE(M >= 0 && k >= 1, "M=%lld k=%d invalid", (long long)M, k);
+  REQUIRE(H > 0 && H % 8 == 0, "H=%d must be a positive multiple of 8", H);
+  REQUIRE(M == 0 || (y && topk_w && out), "y, topk_w and out must be non-null");
+  REQUIRE(aligned16(y) && aligned16(out), "y and out must be 16-byte aligned");
+  return hip_status(bfp8::launch_moe_reduce(y, topk_w, topk_ids, sel, M, k, H, out, (hipStream_t)stream),
+                    "moe_reduce");
+}
 
 }  // namespace
 
@@ -165,6 +218,7 @@ void bfp8moe_opts_init(bfp8moe_opts_t* opts) {
   opts->clamp_limit = INFINITY;
   opts->expert_offset = 0;
   opts->local_num_experts = 0;
+  opts->expert_map = nullptr;
   opts->flags = 0;
   opts->stage_events = nullptr;
   opts->weight_scale_mode = BFP8MOE_WEIGHT_SCALE_BLOCK;
@@ -213,29 +267,27 @@ bfp8moe_status_t moe_route_prepare(const int32_t* topk_ids, int64_t R, int32_t e
                                    int32_t* block_expert, int32_t* block_start, int64_t max_blocks,
                                    int32_t* num_blocks, void* ws, size_t ws_bytes, uint32_t flags,
                                    void* stream) {
-  REQUIRE(R >= 0 && R <= 0x7FFFFFFF, "R=%lld out of range [0, 2^31)", (long long)R);
-  REQUIRE(L >= 1, "local_num_experts=%d must be >= 1", L);
   REQUIRE(expert_offset >= 0, "expert_offset=%d must be >= 0", expert_offset);
-  REQUIRE(block_m >= 1, "block_m=%d must be >= 1", block_m);
-  REQUIRE(R == 0 || (topk_ids && sorted_routes), "topk_ids and sorted_routes must be non-null");
-  REQUIRE(expert_offsets && num_blocks, "expert_offsets and num_blocks must be non-null");
-  REQUIRE((block_expert == nullptr) == (block_start == nullptr),
-          "block_expert and block_start must both be given or both be null");
-  const int64_t need_blocks = bfp8moe_max_blocks(R, L, block_m);
-  REQUIRE(block_expert == nullptr || max_blocks >= need_blocks, "max_blocks=%lld < required %lld",
-          (long long)max_blocks, (long long)need_blocks);
-  if (L > 2048) return fail(BFP8MOE_ERR_UNSUPPORTED, "local_num_experts=%d above 2048", L);
-  const bool single = (flags & BFP8MOE_FLAG_ROUTE_SINGLE_WG)  ? true
-                      : (flags & BFP8MOE_FLAG_ROUTE_MULTI_WG) ? false
-                                                               : bfp8::route_prep_single_fits(R, L);
-  const size_t need = single ? 0 : bfp8::route_prep_ws_bytes(R, L);
-  if (need > 0 && (ws == nullptr || ws_bytes < need))
-    return fail(BFP8MOE_ERR_WORKSPACE, "route workspace %zu bytes < required %zu", ws_bytes, need);
-  return hip_status(bfp8::launch_route_prepare(topk_ids, R, expert_offset, L, block_m, sorted_routes,
-                                               expert_offsets, block_expert, block_start,
-                                               block_expert ? max_blocks : 0, num_blocks, single, ws,
-                                               (hipStream_t)stream),
-                    "moe_route_prepare");
+  bfp8::ExpertSel sel;
+  sel.offset = expert_offset;
+  sel.L = L;
+  return route_prepare_sel(topk_ids, R, sel, block_m, sorted_routes, expert_offsets, block_expert, block_start,
+                           max_blocks, num_blocks, ws, ws_bytes, flags, stream);
+}
+
+bfp8moe_status_t moe_route_prepare_map(const int32_t* topk_ids, int64_t R, const int32_t* expert_map,
+                                       int32_t num_experts, int32_t L, int32_t block_m, int32_t* sorted_routes,
+                                       int32_t* expert_offsets, int32_t* block_expert, int32_t* block_start,
+                                       int64_t max_blocks, int32_t* num_blocks, void* ws, size_t ws_bytes,
+                                       uint32_t flags, void* stream) {
+  REQUIRE(expert_map != nullptr, "expert_map must be non-null");
+  REQUIRE(num_experts >= 1, "num_experts=%d must be >= 1", num_experts);
+  bfp8::ExpertSel sel;
+  sel.map = expert_map;
+  sel.E = num_experts;
+  sel.L = L;
+  return route_prepare_sel(topk_ids, R, sel, block_m, sorted_routes, expert_offsets, block_expert, block_start,
+                           max_blocks, num_blocks, ws, ws_bytes, flags, stream);
 }
 
 bfp8moe_status_t quant_fp8(const uint16_t* x, int64_t rows, int32_t K, int32_t scale_fmt, uint8_t* q,
@@ -366,14 +418,23 @@ bfp8moe_status_t moe_fp8_grouped_gemm_channel(const uint8_t* A, const float* A_s
 
 bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_t* topk_ids, int32_t expert_offset,
                             int32_t L, int64_t M, int32_t k, int32_t H, uint16_t* out, void* stream) {
-  REQUIRE(M >= 0 && k >= 1, "M=%lld k=%d invalid", (long long)M, k);
-  REQUIRE(H > 0 && H % 8 == 0, "H=%d must be a positive multiple of 8", H);
   REQUIRE(topk_ids == nullptr || (L >= 1 && expert_offset >= 0), "invalid expert slice");
-  REQUIRE(M == 0 || (y && topk_w && out), "y, topk_w and out must be non-null");
-  REQUIRE(aligned16(y) && aligned16(out), "y and out must be 16-byte aligned");
-  return hip_status(bfp8::launch_moe_reduce(y, topk_w, topk_ids, expert_offset, L, M, k, H, out,
-                                            (hipStream_t)stream),
-                    "moe_reduce");
+  bfp8::ExpertSel sel;
+  sel.offset = expert_offset;
+  sel.L = L;
+  return reduce_sel(y, topk_w, topk_ids, sel, M, k, H, out, stream);
+}
+
+bfp8moe_status_t moe_reduce_map(const uint16_t* y, const float* topk_w, const int32_t* topk_ids,
+                                const int32_t* expert_map, int32_t num_experts, int32_t L, int64_t M, int32_t k,
+                                int32_t H, uint16_t* out, void* stream) {
+  REQUIRE(topk_ids && expert_map, "topk_ids and expert_map must be non-null");
+  REQUIRE(num_experts >= 1 && L >= 1, "num_experts=%d and L=%d must be >= 1", num_experts, L);
+  bfp8::ExpertSel sel;
+  sel.map = expert_map;
+  sel.E = num_experts;
+  sel.L = L;
+  return reduce_sel(y, topk_w, topk_ids, sel, M, k, H, out, stream);
 }
 
 bfp8moe_status_t moe_router_topk(const float* logits, int64_t M, int32_t E, int32_t k, int32_t score_fn,
@@ -424,6 +485,7 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
   const int32_t L = o.local_num_experts > 0 ? o.local_num_experts : E;
   REQUIRE(o.local_num_experts >= 0 && o.expert_offset >= 0 && (int64_t)o.expert_offset + L <= E,
           "expert slice [%d, %d + %d) is not inside [0, %d)", o.expert_offset, o.expert_offset, L, E);
+  REQUIRE(o.expert_map == nullptr || o.expert_offset == 0, "expert_map and expert_offset are exclusive");
   REQUIRE(o.block_m == 0 || o.block_m == 16 || o.block_m == 32 || o.block_m == 64,
           "block_m=%d must be 0, 16, 32 or 64", o.block_m);
   REQUIRE((o.flags & (BFP8MOE_FLAG_ROUTE_SINGLE_WG | BFP8MOE_FLAG_ROUTE_MULTI_WG)) !=
@@ -527,13 +589,13 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   hook.only = only;
   if (p.mode == kModeToken) {
     uint16_t* act = reinterpret_cast<uint16_t*>(base + p.off_act);
-    return hip_status(bfp8::launch_token_layer(hidden, M, H, topk_ids, topk_w, k, p.offset, p.L, w13, w13_scale,
+    return hip_status(bfp8::launch_token_layer(hidden, M, H, topk_ids, topk_w, k, layer_sel(p), w13, w13_scale,
                                                w2, w2_scale, I, p.fmt, p.clamp, act, out, st, &hook),
                       "fused_moe_block_fp8 (few tokens)");
   }
   if (p.mode == kModeDecode) {
     uint16_t* act = reinterpret_cast<uint16_t*>(base + p.off_act);
-    return hip_status(bfp8::launch_decode_layer(hidden, M, H, topk_ids, topk_w, k, p.offset, p.L, w13, w13_scale, w2,
+    return hip_status(bfp8::launch_decode_layer(hidden, M, H, topk_ids, topk_w, k, layer_sel(p), w13, w13_scale, w2,
                                                 w2_scale, I, p.fmt, p.clamp, act, out, st, &hook),
                       "fused_moe_block_fp8 (small batch)");
   }
@@ -558,7 +620,7 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   hook.before(st_i, st);
   if (hook.run(st_i)) {
     const bfp8::QuantArgs qa{hidden, M, H, p.fmt, aq, as};
-    e = bfp8::launch_route_prepare(topk_ids, p.R, p.offset, p.L, p.block_m, sorted, eoff, bexp, bstart, p.max_blocks,
+    e = bfp8::launch_route_prepare(topk_ids, p.R, layer_sel(p), p.block_m, sorted, eoff, bexp, bstart, p.max_blocks,
                                    nb, p.route_single, rws, st, p.rq_fused ? &qa : nullptr);
   }
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: route prep");
@@ -574,15 +636,16 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
     e = bfp8::launch_grouped_gemm(aq, as, k, w13, w13_scale, 2 * I, H, sorted, eoff, bexp, bstart, nb, p.max_blocks,
                                   p.block_m, h13, st, p.channel);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: gate/up GEMM");
+  // act+quant over the local routes only: route preparation's sorted list
+  // and its kept count (per-row scales: every row, filtered)
   bfp8::RowFilter f;
   f.ids = topk_ids;
-  f.offset = p.offset;
-  f.L = p.L;
-  f.mode = bfp8::kRowsLocalSlice;
+  f.sel = layer_sel(p);
+  f.mode = bfp8::kRowsLocal;
   hook.before(++st_i, st);
   if (hook.run(st_i))
     e = p.channel ? bfp8::launch_silu_and_mul_quant_rows(h13, p.R, I, f, p.clamp, p.fmt, p.a2_static, q, s, st)
-                  : bfp8::launch_silu_and_mul_quant(h13, p.R, I, f, p.clamp, p.fmt, q, s, st);
+                  : bfp8::launch_silu_and_mul_quant_list(h13, sorted, eoff + p.L, p.R, I, p.clamp, p.fmt, q, s, st);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: act+quant");
   hook.before(++st_i, st);
   if (hook.run(st_i))
@@ -590,7 +653,7 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
                                   p.block_m, y, st, p.channel);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: down GEMM");
   hook.before(++st_i, st);
-  if (hook.run(st_i)) e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, p.offset, p.L, M, k, H, out, st);
+  if (hook.run(st_i)) e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, layer_sel(p), M, k, H, out, st);
   hook.before(++st_i, st);
   return hip_status(e, "fused_moe_block_fp8: moe_reduce");
 }
@@ -637,7 +700,7 @@ bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, i
     uint16_t* act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.off_act);
     const bfp8::RouterArgs ra{router_logits, router_bias, topk_ids, topk_w, routed_scale, E, score_fn,
                               renormalize != 0, n_group, topk_group};
-    return hip_status(bfp8::launch_token_layer(hidden, M, H, topk_ids, topk_w, k, p.offset, p.L, w13, w13_scale, w2,
+    return hip_status(bfp8::launch_token_layer(hidden, M, H, topk_ids, topk_w, k, layer_sel(p), w13, w13_scale, w2,
                                                w2_scale, I, p.fmt, p.clamp, act, out, (hipStream_t)stream, nullptr,
                                                &ra),
                       "fused_moe_block_fp8_routed (few tokens)");

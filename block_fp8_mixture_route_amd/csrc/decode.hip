@@ -116,8 +116,8 @@ __device__ __forceinline__ void load_row(const uint16_t* __restrict__ row, int G
 }
 
 __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
-    const uint16_t* __restrict__ hidden, int M, int H, const int32_t* __restrict__ ids, int k, int32_t offset,
-    int32_t L, const uint8_t* __restrict__ w13, const float* __restrict__ w13_s, int I, int fmt, float limit,
+    const uint16_t* __restrict__ hidden, int M, int H, const int32_t* __restrict__ ids, int k, ExpertSel sel,
+    const uint8_t* __restrict__ w13, const float* __restrict__ w13_s, int I, int fmt, float limit,
     int clamp, int tile_cap, uint16_t* __restrict__ act) {
   __shared__ int s_e[kMaxR];
   __shared__ int s_first[kMaxR];
@@ -139,10 +139,7 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
   // 0. routing ids, and the first 4 tokens' hidden rows: nothing depends on
   //    anything yet, so all of these loads leave at once
   int e_mine = -1;
-  if (tid < R) {
-    const int64_t e = (int64_t)ids[tid] - offset;
-    e_mine = (e >= 0 && e < L) ? (int)e : -1;
-  }
+  if (tid < R) e_mine = local_of(sel, ids[tid]);
   uint4 hv[4][4];
 #pragma unroll
   for (int t = 0; t < 4; t++) load_row(hidden + (size_t)min(t, M - 1) * H, G, hv[t]);
@@ -280,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void decode_gate_up_kernel(
 
 __global__ __launch_bounds__(kThreads) void decode_down_reduce_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int k,
-    int32_t offset, int32_t L, const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int H, int I,
+    ExpertSel sel, const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int H, int I,
     int fmt, uint16_t* __restrict__ out) {
   __shared__ int s_e[kMaxK];
   __shared__ float s_w[kMaxK];
@@ -313,10 +310,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_reduce_kernel(
   for (int jj = 0; jj < 2; jj++) {
     const int j = wave + 4 * jj;
     ej[jj] = -1;
-    if (j < k) {
-      const int64_t e = (int64_t)ids[(size_t)t * k + j] - offset;
-      ej[jj] = (e >= 0 && e < L) ? (int)e : -1;
-    }
+    if (j < k) ej[jj] = local_of(sel, ids[(size_t)t * k + j]);
   }
   const int rblk = n0 / kGroup;
   v8i wb[2][2][kMaxG2];
@@ -335,8 +329,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_reduce_kernel(
   }
 
   if (tid < k) {
-    const int64_t e = (int64_t)ids[(size_t)t * k + tid] - offset;
-    s_e[tid] = (e >= 0 && e < L) ? (int)e : -1;
+    s_e[tid] = local_of(sel, ids[(size_t)t * k + tid]);
     s_w[tid] = topk_w[(size_t)t * k + tid];
   }
 
@@ -417,11 +410,11 @@ size_t decode_gate_up_lds(int H, int M, int tile_cap) {
 }
 
 hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
-                               int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
+                               int k, const ExpertSel& sel, const uint8_t* w13, const float* w13_s,
                                const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
                                uint16_t* out, hipStream_t stream, const LaunchHook* hook) {
   const int R = (int)M * k;
-  const int slots = R < L ? R : L;
+  const int slots = R < sel.L ? R : sel.L;
   const int clamp = __builtin_isfinite(limit) ? 1 : 0;
   // an expert serves at most R routes
   const int tile_cap = (R + 15) / 16;
@@ -435,13 +428,13 @@ hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const i
   if (hook) hook->before(0, stream);
   if (!hook || hook->run(0))
     hipLaunchKernelGGL(decode_gate_up_kernel, dim3(I / 8, slots), dim3(kThreads), lds, stream, hidden, (int)M, H,
-                       ids, k, offset, L, w13, w13_s, I, fmt, limit, clamp, tile_cap, act);
+                       ids, k, sel, w13, w13_s, I, fmt, limit, clamp, tile_cap, act);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hook) hook->before(1, stream);
   if (!hook || hook->run(1))
     hipLaunchKernelGGL(decode_down_reduce_kernel, dim3(H / kDownRows, (unsigned)M), dim3(kThreads), 0, stream,
-                       act, ids, topk_w, k, offset, L, w2, w2_s, H, I, fmt, out);
+                       act, ids, topk_w, k, sel, w2, w2_s, H, I, fmt, out);
   e = hipGetLastError();
   if (hook) hook->before(2, stream);
   return e;

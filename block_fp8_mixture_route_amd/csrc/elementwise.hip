@@ -18,6 +18,8 @@
 //   [P3] vLLM PR "[Kernel][Perf] Fuse clamped MoE activation and UE8M0 FP8 block
 //        quantization"
 //   [P4] lmdeploy PR "Moe Reduce kernel"
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 
@@ -56,18 +58,6 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __r
   if (gid >= n_groups) return;  // whole 16-lane group leaves together
   quant_group8(x, gid, threadIdx.x & 15, fmt, q, s);  // rows are contiguous groups
   (void)gpr;
-}
-
-__device__ __forceinline__ bool row_live(const RowFilter& f, int64_t r) {
-  if (f.mode == kRowsAll) return true;
-  int32_t id = f.ids[r];
-  if (f.mode == kRowsLocalSlice) {
-    int64_t e = (int64_t)id - f.offset;
-    return e >= 0 && e < f.L;
-  }
-  if (id < 0 || id >= f.E) return false;
-  if (f.mode == kRowsIdsMap && f.map[id] < 0) return false;
-  return true;
 }
 
 // SwiGLU of this lane's 8 outputs of group g in row r (gate at column
@@ -126,13 +116,67 @@ __global__ __launch_bounds__(kThreads) void silu_and_mul_quant_kernel(const uint
   if (l16 == 0) s[(size_t)r * gpr + g] = sc;
 }
 
+// Act+quant over a filtered row set or a row list, one item per 16-lane
+// group: item f in [0, n gpr) is group f % gpr of position f / gpr.  Its
+// loads leave in dependent steps: the position's row (list entry, or row id
+// and then the id's map entry), then the gate/up values when the row is
+// live.  Positions are rows under the filter when kList is false, else
+// list[p] for p < *count (e.g. route preparation's sorted routes and its kept
+// count: the rows past the count cost one count read).  Index arithmetic is
+// 32-bit (the host keeps n gpr below 2^31).  Measured at top-k 6, width 2048,
+// 1/8 of the rows local, 6 to 6144 rows: several items per lane group, the
+// rows compacted per workgroup by ballot, and 512- or 1024-thread
+// workgroups were all as fast or slower.
+template <bool kTable, bool kList>
+__global__ __launch_bounds__(kThreads) void silu_and_mul_quant_items_kernel(
+    const uint16_t* __restrict__ gu, int n, const int32_t* __restrict__ list, const int32_t* __restrict__ count,
+    RowFilter filt, int I, float limit, int clamp, int fmt, uint8_t* __restrict__ q, float* __restrict__ s) {
+  const int l16 = threadIdx.x & 15;
+  const unsigned gpr = (unsigned)I / kGroup;
+  const unsigned f = blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4);
+  const unsigned n_pos = kList ? (unsigned)max(0, min(*count, n)) : (unsigned)n;
+  if (f >= n_pos * gpr) return;  // whole 16-lane group leaves together
+  const unsigned pos = f / gpr, g = f - pos * gpr;
+  const int32_t v = kList ? list[pos] : filt.ids[pos];
+  unsigned row = pos;
+  if constexpr (kList) {
+    row = (unsigned)v;
+  } else {
+    const bool local = filt.mode == kRowsLocal;
+    const int32_t* map = local ? filt.sel.map : filt.map;
+    const int32_t E = local ? filt.sel.E : filt.E;
+    bool ok;
+    if (local && !map) {
+      const int64_t e = (int64_t)v - filt.sel.offset;
+      ok = e >= 0 && e < filt.sel.L;
+    } else {
+      ok = v >= 0 && v < E;
+      if (ok && map) {
+        const int32_t m = map[v];
+        ok = m >= 0 && (!local || m < filt.sel.L);
+      }
+    }
+    if (!ok) return;  // masked rows are left untouched
+  }
+  const uint16_t* src = gu + (size_t)row * 2 * I + g * kGroup + l16 * 8;
+  const uint4 gv = *reinterpret_cast<const uint4*>(src);
+  const uint4 uv = *reinterpret_cast<const uint4*>(src + I);
+  float gf[8], uf[8], a[8];
+  unpack8(gv, gf);
+  unpack8(uv, uf);
+#pragma unroll
+  for (int i = 0; i < 8; i++) a[i] = swiglu_bf16<kTable>(gf[i], uf[i], limit, clamp != 0);
+  const float sc = group_scale(max_over_16(lane_amax8(a)), fmt);
+  *reinterpret_cast<uint2*>(q + (size_t)row * I + g * kGroup + l16 * 8) = encode8_scaled(a, sc);
+  if (l16 == 0) s[(size_t)row * gpr + g] = sc;
+}
+
 // One thread per (token, 8 consecutive columns): acc over the k routes in
 // order with fmaf, one rounding to BF16.
 __global__ __launch_bounds__(kThreads) void moe_reduce_kernel(const uint16_t* __restrict__ y,
                                                               const float* __restrict__ w,
-                                                              const int32_t* __restrict__ ids, int32_t offset,
-                                                              int32_t L, int64_t M, int k, int H,
-                                                              uint16_t* __restrict__ out) {
+                                                              const int32_t* __restrict__ ids, ExpertSel sel,
+                                                              int64_t M, int k, int H, uint16_t* __restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int h8 = H / 8;
   if (idx >= M * h8) return;
@@ -143,10 +187,7 @@ __global__ __launch_bounds__(kThreads) void moe_reduce_kernel(const uint16_t* __
   for (int i = 0; i < 8; i++) acc[i] = 0.0f;
   for (int j = 0; j < k; j++) {
     const int64_t r = t * k + j;
-    if (ids) {
-      int64_t e = (int64_t)ids[r] - offset;
-      if (e < 0 || e >= L) continue;
-    }
+    if (ids && local_of(sel, ids[r]) < 0) continue;
     const float wt = w[r];
     uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)r * H + c);
     float f[8];
@@ -163,6 +204,44 @@ __global__ __launch_bounds__(kThreads) void moe_reduce_kernel(const uint16_t* __
 }
 
 inline unsigned blocks_for(int64_t n, int64_t per) { return (unsigned)((n + per - 1) / per); }
+
+// The filtered / listed act+quant: the item kernel while n * gpr fits its
+// 32-bit indexing (always, for the layer's route lists), else the flat
+// kernel with the filter (list form: rejected).
+hipError_t launch_items(const uint16_t* gu, int64_t n, const int32_t* list, const int32_t* count,
+                        const RowFilter& f, int I, float limit, int fmt, uint8_t* q, float* s, hipStream_t stream) {
+  const int clamp = __builtin_isfinite(limit) ? 1 : 0;
+  const int64_t items = n * (I / kGroup);
+  const dim3 grid(blocks_for(items, kGroupsPerBlock));
+  const bool table = items >= kTableMinGroups;
+  if (items > 0x7FFFFFFF) {
+    if (list) return hipErrorInvalidValue;
+    if (table)
+      hipLaunchKernelGGL(silu_and_mul_quant_kernel<true>, grid, dim3(kThreads), 0, stream, gu, items, I, f, limit,
+                         clamp, fmt, q, s);
+    else
+      hipLaunchKernelGGL(silu_and_mul_quant_kernel<false>, grid, dim3(kThreads), 0, stream, gu, items, I, f, limit,
+                         clamp, fmt, q, s);
+    return hipGetLastError();
+  }
+  const int nn = (int)n;
+#define BFP8_ITEMS(T, LST)                                                                                    \
+  hipLaunchKernelGGL((silu_and_mul_quant_items_kernel<T, LST>), grid, dim3(kThreads), 0, stream, gu, nn, list, \
+                     count, f, I, limit, clamp, fmt, q, s)
+  if (list) {
+    if (table)
+      BFP8_ITEMS(true, true);
+    else
+      BFP8_ITEMS(false, true);
+  } else {
+    if (table)
+      BFP8_ITEMS(true, false);
+    else
+      BFP8_ITEMS(false, false);
+  }
+#undef BFP8_ITEMS
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -193,6 +272,7 @@ hipError_t launch_silu_and_mul_quant(const uint16_t* gu, int64_t rows, int I, co
                                      int fmt, uint8_t* q, float* s, hipStream_t stream) {
   const int64_t ng = rows * (I / kGroup);
   if (ng == 0) return hipSuccess;
+  if (f.mode != kRowsAll) return launch_items(gu, rows, nullptr, nullptr, f, I, limit, fmt, q, s, stream);
   const int clamp = __builtin_isfinite(limit) ? 1 : 0;
   if (ng >= kTableMinGroups)
     hipLaunchKernelGGL(silu_and_mul_quant_kernel<true>, dim3(blocks_for(ng, kGroupsPerBlock)), dim3(kThreads), 0,
@@ -203,12 +283,19 @@ hipError_t launch_silu_and_mul_quant(const uint16_t* gu, int64_t rows, int I, co
   return hipGetLastError();
 }
 
-hipError_t launch_moe_reduce(const uint16_t* y, const float* w, const int32_t* ids, int32_t offset, int32_t L,
-                             int64_t M, int k, int H, uint16_t* out, hipStream_t stream) {
+hipError_t launch_silu_and_mul_quant_list(const uint16_t* gu, const int32_t* list, const int32_t* count,
+                                          int64_t n_list, int I, float limit, int fmt, uint8_t* q, float* s,
+                                          hipStream_t stream) {
+  if (n_list == 0) return hipSuccess;
+  return launch_items(gu, n_list, list, count, RowFilter{}, I, limit, fmt, q, s, stream);
+}
+
+hipError_t launch_moe_reduce(const uint16_t* y, const float* w, const int32_t* ids, const ExpertSel& sel, int64_t M,
+                             int k, int H, uint16_t* out, hipStream_t stream) {
   const int64_t n = M * (H / 8);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_reduce_kernel, dim3(blocks_for(n, kThreads)), dim3(kThreads), 0, stream, y, w, ids, offset,
-                     L, M, k, H, out);
+  hipLaunchKernelGGL(moe_reduce_kernel, dim3(blocks_for(n, kThreads)), dim3(kThreads), 0, stream, y, w, ids, sel, M,
+                     k, H, out);
   return hipGetLastError();
 }
 

@@ -9,12 +9,34 @@
 
 namespace bfp8 {
 
+// The experts of this device, as the layer and route preparation see them:
+// either the contiguous slice [offset, offset + L) of the global ids, or an
+// expert map from global id to local expert (map[id] for id in [0, E); a
+// value outside [0, L) marks a remote expert).
+struct ExpertSel {
+  const int32_t* map = nullptr;  // device, [E]; null: the slice
+  int32_t E = 0;                 // global expert count (map form)
+  int32_t offset = 0;            // first global id of the slice (slice form)
+  int32_t L = 0;                 // local experts
+};
+
+// The local expert global id `id` selects, or -1 when it is not local.
+__device__ __forceinline__ int local_of(const ExpertSel& s, int32_t id) {
+  if (s.map) {
+    if (id < 0 || id >= s.E) return -1;
+    const int32_t m = s.map[id];
+    return (m >= 0 && m < s.L) ? m : -1;
+  }
+  const int64_t e = (int64_t)id - s.offset;
+  return (e >= 0 && e < s.L) ? (int)e : -1;
+}
+
 // Which rows of an act+quant call are processed.
 enum RowFilterMode : int {
-  kRowsAll = 0,       // every row
-  kRowsIds = 1,       // ids[r] in [0, E)
-  kRowsIdsMap = 2,    // ids[r] in [0, E) and map[ids[r]] >= 0
-  kRowsLocalSlice = 3 // ids[r] - offset in [0, L)
+  kRowsAll = 0,    // every row
+  kRowsIds = 1,    // ids[r] in [0, E)
+  kRowsIdsMap = 2, // ids[r] in [0, E) and map[ids[r]] >= 0
+  kRowsLocal = 3   // local_of(sel, ids[r]) >= 0
 };
 
 // Optional profiling hook: records caller-owned HIP events on the stream
@@ -32,12 +54,19 @@ struct LaunchHook {
 
 struct RowFilter {
   const int32_t* ids = nullptr;
-  const int32_t* map = nullptr;
-  int32_t E = 0;
-  int32_t offset = 0;
-  int32_t L = 0;
+  const int32_t* map = nullptr;  // kRowsIdsMap
+  int32_t E = 0;                 // kRowsIds, kRowsIdsMap
+  ExpertSel sel;                 // kRowsLocal
   int mode = kRowsAll;
 };
+
+__device__ __forceinline__ bool row_live(const RowFilter& f, int64_t r) {
+  if (f.mode == kRowsAll) return true;
+  const int32_t id = f.ids[r];
+  if (f.mode == kRowsLocal) return local_of(f.sel, id) >= 0;
+  if (id < 0 || id >= f.E) return false;
+  return f.mode != kRowsIdsMap || f.map[id] >= 0;
+}
 
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t rows, int K, int fmt, uint8_t* q, float* s,
                             hipStream_t stream);
@@ -45,6 +74,11 @@ hipError_t launch_silu_and_mul(const uint16_t* gu, int64_t rows, int I, float li
                                hipStream_t stream);
 hipError_t launch_silu_and_mul_quant(const uint16_t* gu, int64_t rows, int I, const RowFilter& f, float limit,
                                      int fmt, uint8_t* q, float* s, hipStream_t stream);
+// The same over a row list: rows list[i] for i < *count (count on the device,
+// at most n_list), e.g. route preparation's sorted routes and kept count.
+hipError_t launch_silu_and_mul_quant_list(const uint16_t* gu, const int32_t* list, const int32_t* count,
+                                          int64_t n_list, int I, float limit, int fmt, uint8_t* q, float* s,
+                                          hipStream_t stream);
 // Router scoring functions (values of the C ABI's score_fn).
 enum RouterScore : int { kScoreSoftmax = 0, kScoreSigmoid = 1 };
 
@@ -81,8 +115,9 @@ hipError_t launch_router_noaux_tc(const float* logits, int64_t M, int E, int k, 
                                   const float* bias, int renorm, double scale, int32_t* ids, float* w,
                                   hipStream_t stream);
 
-hipError_t launch_moe_reduce(const uint16_t* y, const float* w, const int32_t* ids, int32_t offset, int32_t L,
-                             int64_t M, int k, int H, uint16_t* out, hipStream_t stream);
+// ids null: every route counts; otherwise only routes local under sel.
+hipError_t launch_moe_reduce(const uint16_t* y, const float* w, const int32_t* ids, const ExpertSel& sel, int64_t M,
+                             int k, int H, uint16_t* out, hipStream_t stream);
 
 // Route preparation.  Picks the single-workgroup kernel when `single` is true,
 // otherwise count -> scan+scatter over `route_prep_num_segments(R)` workgroups
@@ -103,7 +138,7 @@ struct QuantArgs {
 bool route_prep_can_quant(bool single, int32_t L);
 int route_prep_num_segments(int64_t R);
 size_t route_prep_ws_bytes(int64_t R, int32_t L);
-hipError_t launch_route_prepare(const int32_t* ids, int64_t R, int32_t offset, int32_t L, int32_t block_m,
+hipError_t launch_route_prepare(const int32_t* ids, int64_t R, const ExpertSel& sel, int32_t block_m,
                                 int32_t* sorted_routes, int32_t* expert_offsets, int32_t* block_expert,
                                 int32_t* block_start, int64_t max_blocks, int32_t* num_blocks, bool single,
                                 void* ws, hipStream_t stream, const QuantArgs* quant = nullptr);
@@ -136,12 +171,12 @@ int device_cu_count();  // of the current device; 0 when there is none
 // cleared.  Synchronous.
 hipError_t read_wait_faults(unsigned* flags, bool clear);
 hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
-                              int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
+                              int k, const ExpertSel& sel, const uint8_t* w13, const float* w13_s,
                               const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
                               uint16_t* out, hipStream_t stream, const LaunchHook* hook,
                               const RouterArgs* route = nullptr);
 hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
-                               int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
+                               int k, const ExpertSel& sel, const uint8_t* w13, const float* w13_s,
                                const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
                                uint16_t* out, hipStream_t stream, const LaunchHook* hook);
 

@@ -6,6 +6,8 @@
 // run a count pass over many workgroups, then a scan + scatter pass.
 // [P2 Suppressed comments] the slice [expert_offset, expert_offset + L) is
 // validated on the host before anything runs.
+// [P3 Purpose] the local experts can also be given by an expert map from
+// global to local ids (remote experts marked negative).
 // [P1 Modification, Active-expert block scheduling] blocks exist only for
 // experts with routes.
 //
@@ -41,11 +43,6 @@ constexpr int64_t kSingleMaxRoutes = 4096;
 // quantisation: its quantisation workgroups get the same dynamic LDS as the
 // route-prep workgroup, (16 + 3) L + 64 ints, 38 KB at 512.
 constexpr int32_t kQuantMaxL = 512;
-
-__device__ __forceinline__ int local_expert(const int32_t* ids, int64_t r, int32_t offset, int32_t L) {
-  int64_t e = (int64_t)ids[r] - offset;
-  return (e >= 0 && e < L) ? (int)e : -1;
-}
 
 // Exclusive scan of v[0..n) in LDS by the whole 1024-thread workgroup.
 // Returns the total.  tmp: 32 ints of LDS.  Ends with a barrier.
@@ -115,9 +112,10 @@ inline unsigned quant_wgs(const QuantJob& qj) {
 
 // Count pass of the multi-workgroup path: hist[seg][e] for each segment.
 __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __restrict__ ids, int64_t R,
-                                                               int32_t offset, int32_t L, int64_t seg_len,
+                                                               ExpertSel sel, int64_t seg_len,
                                                                int32_t* __restrict__ hist, int n_main, QuantJob qj) {
   if (quant_job(qj, n_main)) return;
+  const int32_t L = sel.L;
   extern __shared__ int lds[];
   int* h = lds;
   for (int e = threadIdx.x; e < L; e += kThreads) h[e] = 0;
@@ -125,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __
   const int64_t s0 = (int64_t)blockIdx.x * seg_len;
   const int64_t s1 = s0 + seg_len < R ? s0 + seg_len : R;
   for (int64_t r = s0 + threadIdx.x; r < s1; r += kThreads) {
-    int e = local_expert(ids, r, offset, L);
+    const int e = local_of(sel, ids[r]);
     if (e >= 0) atomicAdd(&h[e], 1);
   }
   __syncthreads();
@@ -136,11 +134,12 @@ __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __
 // single-workgroup route preparation.  Workgroup 0 also writes the offsets,
 // the blocks and the -1 fills.
 __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t R, int32_t offset, int32_t L, int32_t block_m, int64_t seg_len,
+    const int32_t* __restrict__ ids, int64_t R, ExpertSel sel, int32_t block_m, int64_t seg_len,
     const int32_t* __restrict__ hist, int n_seg, int32_t* __restrict__ sorted_routes,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ block_expert, int32_t* __restrict__ block_start,
     int64_t max_blocks, int32_t* __restrict__ num_blocks, QuantJob qj) {
   if (quant_job(qj, n_seg)) return;
+  const int32_t L = sel.L;
   extern __shared__ int lds[];
   int* wh = lds;                       // [kWaves][L] wave histograms -> cursors
   int* offs = wh + kWaves * L;         // [L] expert totals -> exclusive offsets
@@ -162,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 
   // 1. wave histograms
   for (int64_t r = w0 + lane; r < w1; r += 64) {
-    int e = local_expert(ids, r, offset, L);
+    const int e = local_of(sel, ids[r]);
     if (e >= 0) atomicAdd(&wh[wave * L + e], 1);
   }
   __syncthreads();
@@ -214,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t c0 = w0; c0 < w1; c0 += 64) {
     const int64_t r = c0 + lane;
-    int e = r < w1 ? local_expert(ids, r, offset, L) : -1;
+    int e = r < w1 ? local_of(sel, ids[r]) : -1;
     uint64_t same = __ballot(e >= 0);
     for (int bit = 0; bit < nbits; bit++) {
       uint64_t m = __ballot(e >= 0 && ((e >> bit) & 1));
@@ -278,10 +277,11 @@ size_t route_prep_ws_bytes(int64_t R, int32_t L) {
 
 bool route_prep_can_quant(bool single, int32_t L) { return !single || L <= kQuantMaxL; }
 
-hipError_t launch_route_prepare(const int32_t* ids, int64_t R, int32_t offset, int32_t L, int32_t block_m,
+hipError_t launch_route_prepare(const int32_t* ids, int64_t R, const ExpertSel& sel, int32_t block_m,
                                 int32_t* sorted_routes, int32_t* expert_offsets, int32_t* block_expert,
                                 int32_t* block_start, int64_t max_blocks, int32_t* num_blocks, bool single,
                                 void* ws, hipStream_t stream, const QuantArgs* quant) {
+  const int32_t L = sel.L;
   QuantJob qj;
   if (quant && quant->rows > 0) {
     if (!route_prep_can_quant(single, L)) return hipErrorInvalidValue;  // the caller checks
@@ -302,7 +302,7 @@ hipError_t launch_route_prepare(const int32_t* ids, int64_t R, int32_t offset, i
   });
   const size_t lds = scatter_lds_bytes(L);
   if (single) {
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(1 + nq), dim3(kThreads), lds, stream, ids, R, offset, L, block_m,
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(1 + nq), dim3(kThreads), lds, stream, ids, R, sel, block_m,
                        R > 0 ? R : (int64_t)1, (const int32_t*)nullptr, 1, sorted_routes, expert_offsets,
                        block_expert, block_start, max_blocks, num_blocks, qj);
     return hipGetLastError();
@@ -311,10 +311,10 @@ hipError_t launch_route_prepare(const int32_t* ids, int64_t R, int32_t offset, i
   const int64_t seg_len = segment_length(R);
   int32_t* hist = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(route_count_kernel, dim3(n_seg + nq), dim3(kThreads), sizeof(int) * (size_t)L, stream, ids, R,
-                     offset, L, seg_len, hist, n_seg, qj);
+                     sel, seg_len, hist, n_seg, qj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(n_seg), dim3(kThreads), lds, stream, ids, R, offset, L, block_m,
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(n_seg), dim3(kThreads), lds, stream, ids, R, sel, block_m,
                      seg_len, (const int32_t*)hist, n_seg, sorted_routes, expert_offsets, block_expert,
                      block_start, max_blocks, num_blocks, QuantJob());
   return hipGetLastError();

@@ -178,12 +178,6 @@ __device__ __forceinline__ h2 quant2(float a, float b, float sc) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, 1.0f, false);
 }
 
-// Route r's expert within the local slice [offset, offset + L), or -1.
-__device__ __forceinline__ int local_expert(int32_t id, int32_t offset, int32_t L) {
-  const int64_t e = (int64_t)id - offset;
-  return (e >= 0 && e < L) ? (int)e : -1;
-}
-
 // ------------------------------------------------------------------ gate/up
 //
 // Workgroup (route j, slice q) computes columns 8 q .. 8 q + 7 of route j's
@@ -198,7 +192,7 @@ __device__ __forceinline__ int local_expert(int32_t id, int32_t offset, int32_t 
 // wave could start its dot products before then.
 template <int RL, int I, bool kRoute>
 __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
-    const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, int k, int32_t offset, int32_t L,
+    const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, int k, ExpertSel sel,
     const uint8_t* __restrict__ w13, const float* __restrict__ w13_s, int fmt, float limit, int clamp,
     uint16_t* __restrict__ act, RouterArgs ra) {
   constexpr int kSlices = I / 8;
@@ -263,7 +257,7 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
       ra.w[(size_t)tok * k + lane] = wt;
     }
   };
-  const int e = local_expert(id_j, offset, L);
+  const int e = local_of(sel, id_j);
   if (e < 0) {  // route outside the local slice: it contributes nothing
     if (writer) write_routing();
     return;
@@ -378,7 +372,7 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
 template <int I, int KMAX>
 __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int k,
-    int32_t offset, int32_t L, const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int H, int fmt,
+    ExpertSel sel, const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int H, int fmt,
     int DR, int DL, uint32_t dl_magic, uint16_t* __restrict__ out) {
   constexpr int GI = I / 128, kRpl = 1024 / I, kLpr = I / 16;
   constexpr int kActLoads = (KMAX * GI + kDownWaves - 1) / kDownWaves;  // SwiGLU groups per wave
@@ -411,7 +405,7 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
     av[m] = *reinterpret_cast<const uint32_t*>(act + (size_t)(gi / GI) * I + (gi % GI) * 128 + 2 * lane);
   }
   __builtin_amdgcn_sched_barrier(0);
-  const int e_lane = local_expert(id_lane, offset, L);
+  const int e_lane = local_of(sel, id_lane);
 
   // 2. the wave's W2 units (past the last: repeats of it, cache hits).  A
   //    unit of a masked route reads a line of the SwiGLU buffer instead (in
@@ -529,7 +523,7 @@ bool token_path_fits(int64_t M, int H, int k, int I) {
 }
 
 hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
-                              int k, int32_t offset, int32_t L, const uint8_t* w13, const float* w13_s,
+                              int k, const ExpertSel& sel, const uint8_t* w13, const float* w13_s,
                               const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
                               uint16_t* out, hipStream_t stream, const LaunchHook* hook,
                               const RouterArgs* route) {
@@ -555,10 +549,10 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
   case N:                                                                                                       \
     if (route)                                                                                                  \
       hipLaunchKernelGGL((token_gate_up_kernel<N, II, true>), dim3(up_grid), dim3(kUpThreads), 0, stream,       \
-                         hidden, H, ids, k, offset, L, w13, w13_s, fmt, limit, clamp, act, ra);                 \
+                         hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);                       \
     else                                                                                                        \
       hipLaunchKernelGGL((token_gate_up_kernel<N, II, false>), dim3(up_grid), dim3(kUpThreads), 0, stream,      \
-                         hidden, H, ids, k, offset, L, w13, w13_s, fmt, limit, clamp, act, ra);                 \
+                         hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);                       \
     break;
 #define BFP8_TOKEN_RL(II)   \
   switch (rl) {             \
@@ -588,10 +582,10 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
   do {                                                                                                           \
     if (k <= 8)                                                                                                  \
       hipLaunchKernelGGL((token_down_kernel<II, 8>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0, stream, \
-                         act, ids, topk_w, k, offset, L, w2, w2_s, H, fmt, dr, dl, dl_magic, out);               \
+                         act, ids, topk_w, k, sel, w2, w2_s, H, fmt, dr, dl, dl_magic, out);                     \
     else                                                                                                         \
       hipLaunchKernelGGL((token_down_kernel<II, 16>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0,      \
-                         stream, act, ids, topk_w, k, offset, L, w2, w2_s, H, fmt, dr, dl, dl_magic, out);       \
+                         stream, act, ids, topk_w, k, sel, w2, w2_s, H, fmt, dr, dl, dl_magic, out);             \
   } while (0)
   if (!run1) {
   } else if (I == 128)

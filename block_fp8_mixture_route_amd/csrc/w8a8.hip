@@ -45,17 +45,6 @@ __device__ __forceinline__ float block_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ bool row_live(const RowFilter& f, int64_t r) {
-  if (f.mode == kRowsAll) return true;
-  const int32_t id = f.ids[r];
-  if (f.mode == kRowsLocalSlice) {
-    const int64_t e = (int64_t)id - f.offset;
-    return e >= 0 && e < f.L;
-  }
-  if (id < 0 || id >= f.E) return false;
-  return f.mode != kRowsIdsMap || f.map[id] >= 0;
-}
-
 // Quantise this thread's pieces of a row held in v[p] (BF16-valued floats)
 // with the row's scale; thread 0 stores the scale.
 __device__ __forceinline__ void quant_row_pieces(const float (&v)[kMaxPieces][8], int pieces, int fmt,

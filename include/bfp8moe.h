@@ -45,6 +45,12 @@
  *   [0, local_num_experts) -- for example -1 -- is not an error: it is skipped
  *   by every step, and rows that belong to it are left untouched
  *   [P3 Purpose: optional filtering of invalid or non-local expert rows].
+ * Expert maps.  Instead of a contiguous slice, the local experts can be given
+ *   by an expert map: a device int32 array of E entries, entry i the local
+ *   expert of global expert i, or a value outside [0, local_num_experts) --
+ *   for example -1 -- for an expert held elsewhere [P3 Purpose: the
+ *   expert_map of expert parallelism].  Routes whose ids fall outside [0, E)
+ *   or whose entry is outside [0, local_num_experts) are masked.
  * Determinism.  Repeated calls with the same inputs give bit-identical outputs.
  */
 #ifndef BFP8MOE_H
@@ -107,6 +113,9 @@ typedef struct {
     float act_static_scale;     /* CHANNEL only: > 0 a static per-tensor scale of the hidden states;
                                    0 = one dynamic scale per token (its amax / 448, in scale_fmt) */
     float inter_static_scale;   /* CHANNEL only: the same for the SwiGLU output (per route row) */
+    const int32_t* expert_map;  /* NULL = the slice above; else the expert map (device, [E] int32; see
+                                   "Expert maps"), with expert_offset 0 and local_num_experts the weights'
+                                   leading dimension.  Read by the kernels, not by the host. */
 } bfp8moe_opts_t;
 
 /* How the layer's weights and activations are scaled.
@@ -176,6 +185,19 @@ bfp8moe_status_t moe_route_prepare(const int32_t* topk_ids, int64_t R, int32_t e
                                    int32_t* block_expert, int32_t* block_start, int64_t max_blocks,
                                    int32_t* num_blocks, void* ws, size_t ws_bytes, uint32_t flags,
                                    void* stream);
+
+/* moe_route_prepare with the local experts given by an expert map
+ * [P3 Purpose: expert_map]: route r is kept when topk_ids[r] lies in
+ * [0, num_experts) and e = expert_map[topk_ids[r]] lies in [0, L); it joins
+ * local expert e's segment.  expert_map: device int32 [num_experts], read by
+ * the kernels (its values are not checked on the host: any value outside
+ * [0, L) masks).  Outputs, ordering, workspace and the other requirements as
+ * moe_route_prepare; num_experts >= 1. */
+bfp8moe_status_t moe_route_prepare_map(const int32_t* topk_ids, int64_t R, const int32_t* expert_map,
+                                       int32_t num_experts, int32_t L, int32_t block_m, int32_t* sorted_routes,
+                                       int32_t* expert_offsets, int32_t* block_expert, int32_t* block_start,
+                                       int64_t max_blocks, int32_t* num_blocks, void* ws, size_t ws_bytes,
+                                       uint32_t flags, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Group-128 activation quantisation                                         */
@@ -328,6 +350,13 @@ bfp8moe_status_t moe_router_noaux_tc(const float* logits, int64_t M, int32_t E, 
 bfp8moe_status_t moe_reduce(const uint16_t* y, const float* topk_w, const int32_t* topk_ids,
                             int32_t expert_offset, int32_t L, int64_t M, int32_t k, int32_t H, uint16_t* out,
                             void* stream);
+
+/* moe_reduce with live routes given by an expert map: topk_ids[t, j] in
+ * [0, num_experts) and expert_map[topk_ids[t, j]] in [0, L).  topk_ids and
+ * expert_map (device int32 [num_experts]) non-null; num_experts, L >= 1. */
+bfp8moe_status_t moe_reduce_map(const uint16_t* y, const float* topk_w, const int32_t* topk_ids,
+                                const int32_t* expert_map, int32_t num_experts, int32_t L, int64_t M, int32_t k,
+                                int32_t H, uint16_t* out, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* The whole layer                                                           */

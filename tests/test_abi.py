@@ -5,6 +5,7 @@ import ctypes
 import math
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -39,10 +40,27 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_opts_layout_and_defaults():
-    assert ctypes.sizeof(_lib.Opts) == 48  # 6 words, a pointer, 3 words, padding to 8 bytes
+    assert ctypes.sizeof(_lib.Opts) == 56  # 6 words, a pointer, 3 words and padding, a pointer
     o = bfp8.opts()
     assert o.block_m == 0 and o.scale_fmt == 0 and math.isinf(o.clamp_limit) and o.flags == 0
     assert o.weight_scale_mode == bfp8.WEIGHT_SCALE_BLOCK and o.act_static_scale == 0 and o.inter_static_scale == 0
+    assert not o.expert_map
+
+
+def test_opts_layout_matches_the_c_compiler(tmp_path):
+    # every field's offset and the struct's size as gcc lays out the header's
+    # struct, against the binding's ctypes mirror
+    fields = [f for f, _ in _lib.Opts._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "bfp8moe.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(bfp8moe_opts_t));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(bfp8moe_opts_t, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    assert got[0] == ctypes.sizeof(_lib.Opts)
+    assert got[1:] == [getattr(_lib.Opts, f).offset for f in fields]
 
 
 def test_w8a8_layer_runs_the_general_path_only():
