@@ -39,17 +39,15 @@ constexpr int kWN = 32;       // weight rows per wave
 constexpr int kRT = kWN / 16; // row tiles per wave
 constexpr int kXcd = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
 
-// Route blocks scheduled together on one XCD (see the kernel): pairs from
-// 512 possible blocks up (64 per XCD), single blocks below, where the
-// balance across XCDs counts for more than shared weight reads (measured).
-inline int gemm_group_blocks(int64_t max_blocks) { return max_blocks >= 64 * kXcd ? 2 : 1; }
+// Most consecutive blocks of one expert whose workgroups share each weight
+// tile through one XCD's L2 (a chunk; see the kernel).
+constexpr int kChunkBlocks = 8;
 
-// Workgroups per XCD for max_blocks route blocks of n_tiles tiles each in
-// groups of gb: every XCD gets the same number of groups (the last groups
-// may be partial or past the end: their workgroups return at once).
-inline int64_t gemm_slots_per_xcd(int64_t max_blocks, int n_tiles, int gb) {
-  const int64_t groups = (max_blocks + gb - 1) / gb;
-  return (groups + kXcd - 1) / kXcd * gb * n_tiles;
+// Workgroups per XCD for at most max_blocks route blocks of n_tiles tiles
+// each: an XCD's range holds at most ceil(max_blocks / 8) blocks (workgroups
+// past the range in use return at once).
+inline int64_t gemm_slots_per_xcd(int64_t max_blocks, int n_tiles) {
+  return (max_blocks + kXcd - 1) / kXcd * n_tiles;
 }
 
 // Activation registers of one K step: 16-byte line pieces (shared path) or
@@ -72,29 +70,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
     const uint8_t* __restrict__ A, const float* __restrict__ As, int a_row_div, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, int N, int K, const int32_t* __restrict__ sorted_routes,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ block_expert,
-    const int32_t* __restrict__ block_start, const int32_t* __restrict__ num_blocks, int64_t max_blocks,
-    int group_blocks, uint16_t* __restrict__ C) {
+    const int32_t* __restrict__ block_start, const int32_t* __restrict__ num_blocks, uint16_t* __restrict__ C) {
   constexpr int CT = BM / 16;  // route tiles
   const int n_tiles = N / kBN;
-  // XCD-aware order.  Route blocks form groups of group_blocks consecutive
-  // blocks, dealt round-robin to the XCDs, so that the blocks in use (a
-  // prefix of max_blocks) keep every XCD busy.  An XCD runs its groups one
-  // after another, and within a group the tile index outermost: the same
-  // weight tile of consecutive blocks -- one expert's blocks are consecutive
-  // -- is read by adjacent workgroups on one XCD, and its second read is an
-  // L2 hit; a block's activations are reused by its tiles on that XCD too.
+  // XCD-aware order.  Workgroup i runs on XCD i % 8 as that XCD's slot
+  // i / 8 (workgroups are dealt to the XCDs round robin and each XCD takes
+  // its own in order).  The blocks in use [0, nb) are cut into 8 contiguous
+  // ranges of equal size, one per XCD; one expert's blocks are consecutive,
+  // so a range holds whole experts but at its two ends.  Within a range,
+  // each expert's blocks form chunks of up to kChunkBlocks consecutive
+  // blocks, run in order, and inside a chunk the tile index is outermost:
+  // the chunk's workgroups for one weight tile run side by side on one XCD,
+  // so the tile leaves HBM once per chunk and its other reads hit that XCD's
+  // L2, and a chunk's activation rows stay in L2 across its tiles.  Item s of
+  // the XCD lies in the chunk of block gq = lo + s / n_tiles (the chunk's
+  // items fill slots n_tiles (c0 - lo) .. n_tiles (c1 - lo) - 1).
+  const int x = blockIdx.x % kXcd;
   const int64_t slot = blockIdx.x / kXcd;
-  const int64_t T = (int64_t)group_blocks * n_tiles;
-  const int64_t b0 = ((slot / T) * kXcd + blockIdx.x % kXcd) * group_blocks;
-  if (b0 >= max_blocks) return;
-  const int gb = (int)min((int64_t)group_blocks, max_blocks - b0);  // blocks in this group
-  const int within = (int)(slot % T);
-  if (within >= gb * n_tiles) return;
-  const int64_t blk = b0 + within % gb;
-  const int nt = within / gb;
-  if (blk >= *num_blocks) return;
+  const int64_t nb = *num_blocks;
+  const int64_t lo = nb * x / kXcd, hi = nb * (x + 1) / kXcd;
+  if (slot >= (hi - lo) * n_tiles) return;
+  const int64_t gq = lo + slot / n_tiles;
+  const int eg = block_expert[gq];
+  const int off_e = expert_offsets[eg];
+  const int ig = (block_start[gq] - off_e) / BM;                             // gq among its expert's blocks
+  const int nbe = (expert_offsets[eg + 1] - off_e + BM - 1) / BM;            // the expert's blocks
+  const int cq = ig / kChunkBlocks * kChunkBlocks;                           // chunk's first, in the expert
+  const int64_t c0 = max(gq - ig + cq, lo);
+  const int64_t c1 = min(gq - ig + min(cq + kChunkBlocks, nbe), hi);
+  const int64_t r = slot - (c0 - lo) * n_tiles;
+  const int nt = (int)(r / (c1 - c0));
+  const int64_t blk = c0 + r % (c1 - c0);
 
-  const int e = block_expert[blk];
+  const int e = eg;
   const int start = block_start[blk];
   const int end_e = expert_offsets[e + 1];
   const int len = min(BM, end_e - start);
@@ -303,19 +311,18 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
                                const int32_t* block_start, const int32_t* num_blocks, int64_t max_blocks,
                                int block_m, uint16_t* C, hipStream_t stream, bool channel) {
   if (max_blocks == 0 || N / kBN == 0) return hipSuccess;
-  const int gb = gemm_group_blocks(max_blocks);
-  const int64_t grid = gemm_slots_per_xcd(max_blocks, N / kBN, gb) * kXcd;
+  const int64_t grid = gemm_slots_per_xcd(max_blocks, N / kBN) * kXcd;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
 #define BFP8_GEMM_CASE(BMV)                                                                                   \
   case BMV:                                                                                                   \
     if (channel)                                                                                              \
       hipLaunchKernelGGL((grouped_gemm_kernel<BMV, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A, \
                          As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,     \
-                         num_blocks, max_blocks, gb, C);                                                     \
+                         num_blocks, C);                                                                     \
     else                                                                                                      \
       hipLaunchKernelGGL((grouped_gemm_kernel<BMV, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A, \
                          As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,     \
-                         num_blocks, max_blocks, gb, C);                                                     \
+                         num_blocks, C);                                                                     \
     break;
   switch (block_m) {
     BFP8_GEMM_CASE(16)
