@@ -548,6 +548,139 @@ void oracle_fused_moe_w8a8(const uint16_t* hidden, int64_t M, int H, const int32
 }
 
 /* ------------------------------------------------------------------------- */
+/* MXFP4-weight variant                                                        */
+/* [P2 Reviewed changes: v4_fp4_grouped_gemm.py, v4_swiglu_quant.py and the    */
+/*  v4 FP4 fused MoE backend; P3 Matched GLM serving A/B: MXFP4 is the default */
+/*  weight format of the DeepSeek-V4 checkpoint it names]                      */
+/* The pages name the variant only.  Reading, from the OCP Microscaling (MX)   */
+/* Formats specification v1.0: a weight row is a sequence of E2M1 elements,    */
+/* two to a byte with the even-indexed element in the low four bits, and each  */
+/* run of 32 consecutive elements along K shares one E8M0 scale byte.  The     */
+/* activations stay those of the block-FP8 layer (E4M3 with one scale per 128  */
+/* along K; the SwiGLU quantisation is P3's), and every other step is          */
+/* unchanged.                                                                  */
+/* ------------------------------------------------------------------------- */
+
+#define ORACLE_MX_BLOCK 32
+
+/* E2M1: sign in bit 3, a 2-bit exponent (bias 1) in bits 2..1, one mantissa
+ * bit; exponent 0 holds 0 and the subnormal 0.5.  Every code is finite. */
+double oracle_e2m1_decode(uint8_t c)
+{
+    int sign = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+/* E8M0: 2^(e - 127); the byte 255 is NaN. */
+double oracle_e8m0_decode(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* Element i of a packed E2M1 row. */
+static uint8_t e2m1_at(const uint8_t* row, int i) { return (uint8_t)((row[i / 2] >> (4 * (i & 1))) & 15); }
+
+/* sum_g a_s[g] * sum_{b in group g} 2^(e_b - 127) * sum_{i in block b} dec(a[i]) * dec(w[i])
+ * for one packed weight row w ([K/2] bytes) with its scale bytes ws ([K/32]).
+ * A block's sum of 32 products (each at most 5 significant bits) is exact in
+ * fp64 and the E8M0 factor is a power of two; the activation-scale product and
+ * the sums over blocks round at 2^-53.  abs_sum as in gemm_dot. */
+static double gemm_dot_mx(const double* ad, const float* a_s, const uint8_t* w, const uint8_t* ws, int K,
+                          double* abs_sum)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int b = 0; b < K / ORACLE_MX_BLOCK; b++) {
+        double p = 0.0, pa = 0.0;
+        for (int i = b * ORACLE_MX_BLOCK; i < (b + 1) * ORACLE_MX_BLOCK; i++) {
+            double t = ad[i] * oracle_e2m1_decode(e2m1_at(w, i));
+            p += t;
+            pa += fabs(t);
+        }
+        double c = (double)a_s[(b * ORACLE_MX_BLOCK) / ORACLE_GROUP] * oracle_e8m0_decode(ws[b]);
+        acc += c * p;
+        mag += fabs(c) * pa;
+    }
+    if (abs_sum) *abs_sum = mag;
+    return acc;
+}
+
+/* out[n] = bf16(gemm_dot_mx(a, W[n])) for W [N, K/2] packed rows and W_s
+ * [N, K/32] scale bytes; acc_out / abs_out as gemm_row_ex. */
+static void gemm_row_mx(const uint8_t* a, const float* a_s, const uint8_t* W, const uint8_t* W_s, int N, int K,
+                        uint16_t* out, double* acc_out, double* abs_out)
+{
+    double* ad = (double*)malloc(sizeof(double) * (size_t)K);
+    for (int i = 0; i < K; i++) ad[i] = oracle_e4m3_decode(a[i]);
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; n++) {
+        double mag;
+        double acc = gemm_dot_mx(ad, a_s, W + (size_t)n * (K / 2), W_s + (size_t)n * (K / ORACLE_MX_BLOCK), K, &mag);
+        if (out) out[n] = oracle_f64_to_bf16(acc);
+        if (acc_out) acc_out[n] = acc;
+        if (abs_out) abs_out[n] = mag;
+    }
+    free(ad);
+}
+
+/* Grouped GEMM with MXFP4 weights B [L, N, K/2], B_s [L, N, K/32] and E4M3
+ * activations A [rows, K] with group-128 scales A_s [rows, K/128]; routes and
+ * outputs as oracle_grouped_gemm.  acc / mag (both NULL, or both [R, N])
+ * receive the unrounded values and magnitudes instead of C. */
+void oracle_grouped_gemm_mxfp4(const uint8_t* A, const float* A_s, int a_row_div, const uint8_t* B,
+                               const uint8_t* B_s, int N, int K, const int32_t* topk_ids, int64_t R,
+                               int expert_offset, int L, uint16_t* C, double* acc, double* mag)
+{
+    int G = K / ORACLE_GROUP;
+    for (int64_t r = 0; r < R; r++) {
+        int64_t e = (int64_t)topk_ids[r] - expert_offset;
+        if (e < 0 || e >= L) continue;
+        int64_t arow = r / a_row_div;
+        gemm_row_mx(A + (size_t)arow * K, A_s + (size_t)arow * G, B + (size_t)e * N * (K / 2),
+                    B_s + (size_t)e * N * (K / ORACLE_MX_BLOCK), N, K, C ? C + (size_t)r * N : NULL,
+                    acc ? acc + (size_t)r * N : NULL, mag ? mag + (size_t)r * N : NULL);
+    }
+}
+
+/* The whole layer with MXFP4 weights: w13 [L, 2I, H/2], w13_s [L, 2I, H/32],
+ * w2 [L, H, I/2], w2_s [L, H, I/32]; everything else and the intermediates as
+ * oracle_fused_moe (all tokens). */
+void oracle_fused_moe_mxfp4(const uint16_t* hidden, int64_t M, int H, const int32_t* topk_ids,
+                            const float* topk_w, int k, const uint8_t* w13, const uint8_t* w13_s,
+                            const uint8_t* w2, const uint8_t* w2_s, int expert_offset, int L, int I, int scale_fmt,
+                            float clamp_limit, uint16_t* out, uint16_t* h13_out, uint8_t* q_out, float* s_out,
+                            uint16_t* y_out)
+{
+    int GH = H / ORACLE_GROUP, GI = I / ORACLE_GROUP;
+    uint8_t* aq = (uint8_t*)malloc((size_t)H);
+    float* as = (float*)malloc(sizeof(float) * (size_t)GH);
+    uint16_t* h13 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)2 * I);
+    uint8_t* q = (uint8_t*)malloc((size_t)I);
+    float* s = (float*)malloc(sizeof(float) * (size_t)GI);
+    uint16_t* y = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)k * H);
+    float* w = (float*)malloc(sizeof(float) * (size_t)k);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    for (int64_t t = 0; t < M; t++) {
+        oracle_quant_fp8(hidden + (size_t)t * H, 1, H, scale_fmt, aq, as);
+        for (int j = 0; j < k; j++) {
+            int64_t r = t * k + j;
+            ids[j] = topk_ids[r];
+            w[j] = topk_w[r];
+            int64_t e = (int64_t)topk_ids[r] - expert_offset;
+            if (e < 0 || e >= L) continue;
+            gemm_row_mx(aq, as, w13 + (size_t)e * 2 * I * (H / 2), w13_s + (size_t)e * 2 * I * (H / ORACLE_MX_BLOCK),
+                        2 * I, H, h13, NULL, NULL);
+            oracle_silu_and_mul_quant_fp8(h13, 1, I, NULL, NULL, 0, clamp_limit, scale_fmt, q, s);
+            gemm_row_mx(q, s, w2 + (size_t)e * H * (I / 2), w2_s + (size_t)e * H * (I / ORACLE_MX_BLOCK), H, I,
+                        y + (size_t)j * H, NULL, NULL);
+            if (h13_out) memcpy(h13_out + (size_t)r * 2 * I, h13, sizeof(uint16_t) * 2 * I);
+            if (q_out) memcpy(q_out + (size_t)r * I, q, (size_t)I);
+            if (s_out) memcpy(s_out + (size_t)r * GI, s, sizeof(float) * GI);
+            if (y_out) memcpy(y_out + (size_t)r * H, y + (size_t)j * H, sizeof(uint16_t) * H);
+        }
+        oracle_moe_reduce(y, w, ids, expert_offset, L, 1, k, H, out + (size_t)t * H);
+    }
+    free(aq); free(as); free(h13); free(q); free(s); free(y); free(w); free(ids);
+}
+
+/* ------------------------------------------------------------------------- */
 /* moe_reduce: top-k weighted sum back to token order                          */
 /* [P4 Pull request overview: weights applied by a dedicated reduction]        */
 /* [P4 review discussion: accumulation precision left to each kernel; fp32]    */

@@ -67,6 +67,11 @@ def lib():
                                              P, P, P, P, P]),
             "oracle_fused_moe": (None, [P, i64, i32, P, P, i32, P, P, P, P, i32, i32, i32, i32, f32,
                                         P, i64, P, P, P, P, P]),
+            "oracle_e2m1_decode": (ctypes.c_double, [ctypes.c_uint8]),
+            "oracle_e8m0_decode": (ctypes.c_double, [ctypes.c_uint8]),
+            "oracle_grouped_gemm_mxfp4": (None, [P, P, i32, P, P, i32, i32, P, i64, i32, i32, P, P, P]),
+            "oracle_fused_moe_mxfp4": (None, [P, i64, i32, P, P, i32, P, P, P, P, i32, i32, i32, i32, f32,
+                                              P, P, P, P, P]),
             "oracle_num_threads": (i32, []),
             "oracle_set_threads": (None, [i32]),
         }
@@ -396,6 +401,62 @@ def fused_moe_w8a8(hidden, topk_ids, topk_w, w13, w13_s, w2, w2_s, expert_offset
                                 L, I, scale_fmt, a1_static, a2_static, clamp, _p(out),
                                 _p(inter["h13"]) if inter else None, _p(inter["q"]) if inter else None,
                                 _p(inter["s"]) if inter else None, _p(inter["y"]) if inter else None)
+    return (out, inter) if want_intermediates else out
+
+
+def e2m1_decode(c: int) -> float:
+    return lib().oracle_e2m1_decode(c)
+
+
+def e8m0_decode(e: int) -> float:
+    return lib().oracle_e8m0_decode(e)
+
+
+def grouped_gemm_mxfp4(A, A_s, a_row_div: int, B, B_s, topk_ids, expert_offset: int, L: int, exact=False):
+    """MXFP4 weights B [L, N, K/2] (packed E2M1, even element in the low
+    nibble) with E8M0 scale bytes B_s [L, N, K/32]; E4M3 activations with
+    group-128 scales.  exact: ([R, N] fp64 values, magnitudes) instead of
+    [R, N] BF16 bits."""
+    A = as_np(A, np.uint8); A_s = as_np(A_s, np.float32)
+    B = as_np(B, np.uint8); B_s = as_np(B_s, np.uint8)
+    ids = as_np(topk_ids, np.int32).reshape(-1)
+    N, K = B.shape[1], 2 * B.shape[2]
+    R = ids.size
+    if exact:
+        acc = np.full((R, N), np.nan)
+        mag = np.full((R, N), np.nan)
+        lib().oracle_grouped_gemm_mxfp4(_p(A), _p(A_s), a_row_div, _p(B), _p(B_s), N, K, _p(ids), R, expert_offset,
+                                        L, None, _p(acc), _p(mag))
+        return acc, mag
+    C = np.zeros((R, N), np.uint16)
+    lib().oracle_grouped_gemm_mxfp4(_p(A), _p(A_s), a_row_div, _p(B), _p(B_s), N, K, _p(ids), R, expert_offset, L,
+                                    _p(C), None, None)
+    return C
+
+
+def fused_moe_mxfp4(hidden, topk_ids, topk_w, w13, w13_s, w2, w2_s, expert_offset: int = 0, L: int = None,
+                    scale_fmt: int = SCALE_FP32, clamp: float = float("inf"), want_intermediates: bool = False):
+    """The layer with MXFP4 weights (w13 [L, 2I, H/2], w13_s [L, 2I, H/32],
+    w2 [L, H, I/2], w2_s [L, H, I/32]): [M, H] BF16 output and optionally
+    the intermediates keyed by route id."""
+    h = as_np(hidden, np.uint16)
+    ids = as_np(topk_ids, np.int32)
+    w = as_np(topk_w, np.float32)
+    w13 = as_np(w13, np.uint8); w13_s = as_np(w13_s, np.uint8)
+    w2 = as_np(w2, np.uint8); w2_s = as_np(w2_s, np.uint8)
+    M, H = h.shape
+    k = ids.shape[1]
+    L = w13.shape[0] if L is None else L
+    I = 2 * w2.shape[2]
+    out = np.zeros((M, H), np.uint16)
+    inter = None
+    if want_intermediates:
+        inter = dict(h13=np.zeros((M * k, 2 * I), np.uint16), q=np.zeros((M * k, I), np.uint8),
+                     s=np.zeros((M * k, I // 128), np.float32), y=np.zeros((M * k, H), np.uint16))
+    lib().oracle_fused_moe_mxfp4(_p(h), M, H, _p(ids), _p(w), k, _p(w13), _p(w13_s), _p(w2), _p(w2_s), expert_offset,
+                                 L, I, scale_fmt, clamp, _p(out), _p(inter["h13"]) if inter else None,
+                                 _p(inter["q"]) if inter else None, _p(inter["s"]) if inter else None,
+                                 _p(inter["y"]) if inter else None)
     return (out, inter) if want_intermediates else out
 
 
