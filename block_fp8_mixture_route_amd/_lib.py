@@ -53,6 +53,7 @@ class Opts(ctypes.Structure):
 
 WEIGHT_SCALE_BLOCK = 0
 WEIGHT_SCALE_CHANNEL = 1
+WEIGHT_MXFP4 = 2
 
 
 class BFP8MoEError(RuntimeError):
@@ -83,6 +84,8 @@ SIGNATURES = {
     "silu_and_mul_quant_fp8_rows": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _f32, _i32, _f32, _P, _P, _P]),
     "moe_fp8_grouped_gemm_channel": (ctypes.c_int, [_P, _P, _i32, _P, _P, _i32, _i32, _i32, _P, _P, _P, _P, _P,
                                                     _i64, _i32, _i64, _P, _P]),
+    "moe_mxfp4_grouped_gemm": (ctypes.c_int, [_P, _P, _i32, _P, _P, _i32, _i32, _i32, _P, _P, _P, _P, _P, _i64, _i32,
+                                              _i64, _P, _P]),
     "moe_reduce": (ctypes.c_int, [_P, _P, _P, _i32, _i32, _i64, _i32, _i32, _P, _P]),
     "moe_reduce_map": (ctypes.c_int, [_P, _P, _P, _P, _i32, _i32, _i64, _i32, _i32, _P, _P]),
     "moe_router_topk": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _P, _i32, ctypes.c_double, _P, _P, _P]),
@@ -93,6 +96,8 @@ SIGNATURES = {
                                           ctypes.POINTER(ctypes.c_char_p), _i32]),
     "fused_moe_block_fp8": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32,
                                            ctypes.POINTER(Opts), _P, _P, _sz, _P]),
+    "fused_moe_mxfp4": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32,
+                                       ctypes.POINTER(Opts), _P, _P, _sz, _P]),
     "fused_moe_block_fp8_noalloc": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32,
                                                    ctypes.POINTER(Opts), _P, _P]),
     "fused_moe_block_fp8_routed": (ctypes.c_int, [_P, _i64, _i32, _P, _P, _i32, _i32, ctypes.c_double, _i32, _i32,
@@ -300,6 +305,29 @@ def moe_fp8_grouped_gemm(A, A_scale, a_row_div, B, B_scale, route, block_m, R, C
     return C
 
 
+def moe_mxfp4_grouped_gemm(A, A_scale, a_row_div, B, B_scale, route, block_m, R, C=None):
+    """MXFP4 weights: B [L, N, K/2] packed E2M1 (uint8), B_scale [L, N, K/32]
+    E8M0 bytes (uint8); A, A_scale, route as moe_fp8_grouped_gemm."""
+    _expect(B, "B", torch.uint8, (None, None, None))
+    L, N, K2 = B.shape
+    K = 2 * K2
+    _expect(A, "A", _FP8, (None, K))
+    _expect(A_scale, "A_scale", torch.float32, (A.shape[0], K // 128))
+    _expect(B_scale, "B_scale", torch.uint8, (L, N, K // 32))
+    if R > A.shape[0] * a_row_div:
+        raise ValueError(f"R={R} routes need {-(-R // a_row_div)} rows of A, it has {A.shape[0]}")
+    _expect(C, "C", torch.bfloat16, (R, N))
+    _require_device(A, A_scale, B, B_scale, C)
+    A = _u8(A)
+    C = torch.empty(R, N, dtype=torch.bfloat16, device=A.device) if C is None else C
+    check(lib().moe_mxfp4_grouped_gemm(ptr(A), ptr(A_scale), a_row_div, ptr(B), ptr(B_scale), L, N, K,
+                                       ptr(route["sorted_routes"]), ptr(route["expert_offsets"]),
+                                       ptr(route["block_expert"]), ptr(route["block_start"]),
+                                       ptr(route["num_blocks"]), route["max_blocks"], block_m, R, ptr(_u16(C)),
+                                       stream_of(A.device)))
+    return C
+
+
 def quant_fp8_rows(x, scale_fmt=SCALE_FP32, static_scale=0.0, q=None, scales=None):
     """One scale per row (static when > 0, else the row's amax / 448)."""
     _expect(x, "x", torch.bfloat16, (None, None))
@@ -480,6 +508,45 @@ def fused_moe_block_fp8(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, 
     check(lib().fused_moe_block_fp8(ptr(_u16(hidden)), M, H, ptr(topk_ids), ptr(topk_w), k, ptr(w13),
                                     ptr(w13_scale), ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o),
                                     ptr(_u16(out)), ptr(ws), ws.numel(), stream_of(hidden.device)))
+    return out
+
+
+def fused_moe_mxfp4(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, E=None, o: Opts = None, out=None,
+                    ws=None):
+    """The layer with MXFP4 weights: w13 [L, 2I, H/2] and w2 [L, H, I/2]
+    packed E2M1 (uint8), w13_scale [L, 2I, H/32] and w2_scale [L, H, I/32]
+    E8M0 bytes (uint8).  o: opts(weight_scale_mode=WEIGHT_MXFP4, ...) (the
+    default when None)."""
+    E = w13.shape[0] if E is None else E
+    o = opts(weight_scale_mode=WEIGHT_MXFP4) if o is None else o
+    if o.weight_scale_mode != WEIGHT_MXFP4:
+        raise ValueError("fused_moe_mxfp4 takes options with weight_scale_mode=WEIGHT_MXFP4")
+    _expect(hidden, "hidden", torch.bfloat16, (None, None))
+    M, H = hidden.shape
+    _expect(topk_ids, "topk_ids", torch.int32, (M, None))
+    k = topk_ids.shape[1]
+    _expect(topk_w, "topk_w", torch.float32, (M, k))
+    _expect(w2, "w2", torch.uint8, (None, H, None))
+    Lw, _, I2 = w2.shape
+    I = 2 * I2
+    _expect(w13, "w13", torch.uint8, (Lw, 2 * I, H // 2))
+    _expect(w13_scale, "w13_scale", torch.uint8, (Lw, 2 * I, H // 32))
+    _expect(w2_scale, "w2_scale", torch.uint8, (Lw, H, I // 32))
+    L = o.local_num_experts if o.local_num_experts > 0 else E
+    if Lw < L:
+        raise ValueError(f"the weights hold {Lw} experts, the call addresses {L}")
+    if o.expert_map and getattr(o, "_expert_map", None) is not None and o._expert_map.numel() != E:
+        raise ValueError(f"the expert map has {o._expert_map.numel()} entries, E is {E}")
+    _expect(out, "out", torch.bfloat16, (M, H))
+    _expect(ws, "ws", torch.uint8, (None,))
+    _require_device(hidden, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, out, ws)
+    need = fused_moe_workspace_size(M, H, k, E, I, o)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    out = torch.empty(M, H, dtype=torch.bfloat16, device=hidden.device) if out is None else out
+    check(lib().fused_moe_mxfp4(ptr(_u16(hidden)), M, H, ptr(topk_ids), ptr(topk_w), k, ptr(w13), ptr(w13_scale),
+                                ptr(w2), ptr(w2_scale), E, I, ctypes.byref(o), ptr(_u16(out)), ptr(ws), ws.numel(),
+                                stream_of(hidden.device)))
     return out
 
 

@@ -52,6 +52,7 @@ struct LayerPlan {
   bool route_single;
   bool rq_fused;  // general path: route preparation carries the input quantisation
   bool channel;   // the W8A8 variant: per-row activation and per-channel weight scales
+  bool mxfp4;     // MXFP4 weights (E2M1 with E8M0 scales per 32 along K)
   float a1_static, a2_static;
   int mode;  // kModeGeneral, kModeDecode, kModeToken
   size_t off_aq, off_as, off_sorted, off_eoff, off_bexp, off_bstart, off_nb, off_rws, off_h13, off_q, off_s,
@@ -64,6 +65,10 @@ const char* const kGeneralStages[] = {"route_prepare", "quant_fp8", "gate_up_gem
 // fewer): stage 0 covers both.
 const char* const kGeneralFusedStages[] = {"route_prepare_quant", "gate_up_gemm", "silu_and_mul_quant", "down_gemm",
                                            "moe_reduce"};
+const char* const kMxfp4Stages[] = {"route_prepare", "quant_fp8", "gate_up_gemm_mxfp4", "silu_and_mul_quant",
+                                    "down_gemm_mxfp4", "moe_reduce"};
+const char* const kMxfp4FusedStages[] = {"route_prepare_quant", "gate_up_gemm_mxfp4", "silu_and_mul_quant",
+                                         "down_gemm_mxfp4", "moe_reduce"};
 const char* const kChannelStages[] = {"route_prepare", "quant_fp8_rows", "gate_up_gemm_channel",
                                       "silu_and_mul_quant_rows", "down_gemm_channel", "moe_reduce"};
 const char* const kDecodeStages[] = {"decode_gate_up_swiglu", "decode_down_reduce"};
@@ -104,10 +109,12 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.block_m = o.block_m > 0 ? o.block_m : auto_block_m(p.R, p.L);
   p.max_blocks = bfp8moe_max_blocks(p.R, p.L, p.block_m);
   p.channel = o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_CHANNEL;
+  p.mxfp4 = o.weight_scale_mode == BFP8MOE_WEIGHT_MXFP4;
   p.a1_static = o.act_static_scale;
   p.a2_static = o.inter_static_scale;
-  const bool fits = !p.channel && bfp8::decode_path_fits(M, H, k, I);
-  const bool token_fits = !p.channel && bfp8::token_path_fits(M, H, k, I);
+  const bool block = !p.channel && !p.mxfp4;  // the few-token and small-batch paths take block scales only
+  const bool fits = block && bfp8::decode_path_fits(M, H, k, I);
+  const bool token_fits = block && bfp8::token_path_fits(M, H, k, I);
   if (o.flags & BFP8MOE_FLAG_LAYER_GENERAL)
     p.mode = kModeGeneral;
   else if (o.flags & BFP8MOE_FLAG_LAYER_DECODE)
@@ -492,8 +499,9 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
               (BFP8MOE_FLAG_ROUTE_SINGLE_WG | BFP8MOE_FLAG_ROUTE_MULTI_WG),
           "route flags are exclusive");
   if (L > 2048) return fail(BFP8MOE_ERR_UNSUPPORTED, "local_num_experts=%d above 2048", L);
-  REQUIRE(o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_BLOCK || o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_CHANNEL,
-          "weight_scale_mode=%d is not 0 (block) or 1 (channel)", o.weight_scale_mode);
+  REQUIRE(o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_BLOCK || o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_CHANNEL ||
+              o.weight_scale_mode == BFP8MOE_WEIGHT_MXFP4,
+          "weight_scale_mode=%d is not 0 (block), 1 (channel) or 2 (MXFP4)", o.weight_scale_mode);
   REQUIRE(isfinite(o.act_static_scale) && o.act_static_scale >= 0 && isfinite(o.inter_static_scale) &&
               o.inter_static_scale >= 0,
           "static scales must be finite and >= 0 (0 = dynamic)");
@@ -502,6 +510,13 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
       return fail(BFP8MOE_ERR_UNSUPPORTED, "the W8A8 (channel) variant takes H and I up to 8192 (H=%d I=%d)", H, I);
     if (o.flags & (BFP8MOE_FLAG_LAYER_DECODE | BFP8MOE_FLAG_LAYER_TOKEN))
       return fail(BFP8MOE_ERR_UNSUPPORTED, "the W8A8 (channel) variant runs on the general path only");
+  }
+  if (o.weight_scale_mode == BFP8MOE_WEIGHT_MXFP4) {
+    if (H % 256 != 0 || I % 256 != 0)
+      return fail(BFP8MOE_ERR_UNSUPPORTED, "MXFP4 weights take H and I in multiples of 256 (H=%d I=%d)", H, I);
+    if (o.flags & (BFP8MOE_FLAG_LAYER_DECODE | BFP8MOE_FLAG_LAYER_TOKEN))
+      return fail(BFP8MOE_ERR_UNSUPPORTED, "MXFP4 weights run on the general path only");
+    REQUIRE(o.act_static_scale == 0 && o.inter_static_scale == 0, "static scales belong to the W8A8 variant");
   }
   if ((o.flags & BFP8MOE_FLAG_LAYER_DECODE) && M > 0 && !bfp8::decode_path_fits(M, H, k, I))
     return fail(BFP8MOE_ERR_UNSUPPORTED,
@@ -535,6 +550,7 @@ int32_t fused_moe_block_fp8_stages(int64_t M, int32_t H, int32_t k, int32_t E, i
   const char* const* list = p.mode == kModeToken    ? kTokenStages
                             : p.mode == kModeDecode ? kDecodeStages
                             : p.channel             ? kChannelStages
+                            : p.mxfp4               ? (p.rq_fused ? kMxfp4FusedStages : kMxfp4Stages)
                             : p.rq_fused            ? kGeneralFusedStages
                                                     : kGeneralStages;
   const int32_t n = plan_stages(p);
@@ -553,14 +569,18 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
   return p.total;
 }
 
-bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
-                                     const float* topk_w, int32_t k, const uint8_t* w13, const float* w13_scale,
-                                     const uint8_t* w2, const float* w2_scale, int32_t E, int32_t I,
-                                     const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
-                                     void* stream) {
-  bfp8moe_opts_t o;
-  bfp8moe_opts_init(&o);
-  if (opts) o = *opts;
+}  // extern "C"
+
+namespace {
+
+// The layer for either scale type: w13_scale / w2_scale are fp32 (block and
+// channel scales) or E8M0 bytes (MXFP4), as o.weight_scale_mode says.
+bfp8moe_status_t layer_impl(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
+                            const float* topk_w, int32_t k, const uint8_t* w13, const void* w13_scale_v,
+                            const uint8_t* w2, const void* w2_scale_v, int32_t E, int32_t I, const bfp8moe_opts_t& o,
+                            uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  const float* w13_scale = static_cast<const float*>(w13_scale_v);
+  const float* w2_scale = static_cast<const float*>(w2_scale_v);
   {
     const bfp8moe_status_t st = check_layer_shape(M, H, k, E, I, o);
     if (st != BFP8MOE_OK) return st;
@@ -571,6 +591,9 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
           "hidden, w13, w2 and out must be 16-byte aligned");
   REQUIRE(o.weight_scale_mode != BFP8MOE_WEIGHT_SCALE_CHANNEL || (aligned16(w13_scale) && aligned16(w2_scale)),
           "channel weight scales must be 16-byte aligned");
+  REQUIRE(o.weight_scale_mode != BFP8MOE_WEIGHT_MXFP4 ||
+              ((reinterpret_cast<uintptr_t>(w13_scale_v) & 7u) == 0 && (reinterpret_cast<uintptr_t>(w2_scale_v) & 7u) == 0),
+          "MXFP4 scale bytes must be 8-byte aligned");
   if (M == 0) return BFP8MOE_OK;
   LayerPlan p;
   plan_layer(p, M, H, k, E, I, o);
@@ -633,8 +656,10 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   }
   hook.before(++st_i, st);
   if (hook.run(st_i))
-    e = bfp8::launch_grouped_gemm(aq, as, k, w13, w13_scale, 2 * I, H, sorted, eoff, bexp, bstart, nb, p.max_blocks,
-                                  p.block_m, h13, st, p.channel);
+    e = p.mxfp4 ? bfp8::launch_grouped_gemm_mxfp4(aq, as, k, w13, static_cast<const uint8_t*>(w13_scale_v), 2 * I, H,
+                                                  sorted, eoff, bexp, bstart, nb, p.max_blocks, p.block_m, h13, st)
+                : bfp8::launch_grouped_gemm(aq, as, k, w13, w13_scale, 2 * I, H, sorted, eoff, bexp, bstart, nb,
+                                            p.max_blocks, p.block_m, h13, st, p.channel);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: gate/up GEMM");
   // act+quant over the local routes only: route preparation's sorted list
   // and its kept count (per-row scales: every row, filtered)
@@ -649,13 +674,67 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: act+quant");
   hook.before(++st_i, st);
   if (hook.run(st_i))
-    e = bfp8::launch_grouped_gemm(q, s, 1, w2, w2_scale, H, I, sorted, eoff, bexp, bstart, nb, p.max_blocks,
-                                  p.block_m, y, st, p.channel);
+    e = p.mxfp4 ? bfp8::launch_grouped_gemm_mxfp4(q, s, 1, w2, static_cast<const uint8_t*>(w2_scale_v), H, I, sorted,
+                                                  eoff, bexp, bstart, nb, p.max_blocks, p.block_m, y, st)
+                : bfp8::launch_grouped_gemm(q, s, 1, w2, w2_scale, H, I, sorted, eoff, bexp, bstart, nb,
+                                            p.max_blocks, p.block_m, y, st, p.channel);
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: down GEMM");
   hook.before(++st_i, st);
   if (hook.run(st_i)) e = bfp8::launch_moe_reduce(y, topk_w, topk_ids, layer_sel(p), M, k, H, out, st);
   hook.before(++st_i, st);
   return hip_status(e, "fused_moe_block_fp8: moe_reduce");
+}
+
+}  // namespace
+
+extern "C" {
+
+bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
+                                     const float* topk_w, int32_t k, const uint8_t* w13, const float* w13_scale,
+                                     const uint8_t* w2, const float* w2_scale, int32_t E, int32_t I,
+                                     const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  bfp8moe_opts_t o;
+  bfp8moe_opts_init(&o);
+  if (opts) o = *opts;
+  REQUIRE(o.weight_scale_mode != BFP8MOE_WEIGHT_MXFP4, "MXFP4 weights (E8M0 scale bytes) take fused_moe_mxfp4");
+  return layer_impl(hidden, M, H, topk_ids, topk_w, k, w13, w13_scale, w2, w2_scale, E, I, o, out, ws, ws_bytes,
+                    stream);
+}
+
+bfp8moe_status_t fused_moe_mxfp4(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
+                                 const float* topk_w, int32_t k, const uint8_t* w13, const uint8_t* w13_scale,
+                                 const uint8_t* w2, const uint8_t* w2_scale, int32_t E, int32_t I,
+                                 const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  REQUIRE(opts != nullptr && opts->weight_scale_mode == BFP8MOE_WEIGHT_MXFP4,
+          "fused_moe_mxfp4 takes opts with weight_scale_mode BFP8MOE_WEIGHT_MXFP4");
+  return layer_impl(hidden, M, H, topk_ids, topk_w, k, w13, w13_scale, w2, w2_scale, E, I, *opts, out, ws, ws_bytes,
+                    stream);
+}
+
+bfp8moe_status_t moe_mxfp4_grouped_gemm(const uint8_t* A, const float* A_scale, int32_t a_row_div, const uint8_t* B,
+                                        const uint8_t* B_scale, int32_t L, int32_t N, int32_t K,
+                                        const int32_t* sorted_routes, const int32_t* expert_offsets,
+                                        const int32_t* block_expert, const int32_t* block_start,
+                                        const int32_t* num_blocks, int64_t max_blocks, int32_t block_m, int64_t R,
+                                        uint16_t* C, void* stream) {
+  REQUIRE(N > 0 && N % 128 == 0, "N=%d must be a positive multiple of 128", N);
+  REQUIRE(K > 0 && K % 256 == 0, "K=%d must be a positive multiple of 256", K);
+  REQUIRE(L >= 1, "L=%d must be >= 1", L);
+  REQUIRE(a_row_div >= 1, "a_row_div=%d must be >= 1", a_row_div);
+  REQUIRE(block_m == 16 || block_m == 32 || block_m == 64, "block_m=%d must be 16, 32 or 64", block_m);
+  REQUIRE(R >= 0 && R <= 0x7FFFFFFF, "R=%lld out of range", (long long)R);
+  REQUIRE(max_blocks >= 0, "max_blocks must be >= 0");
+  REQUIRE(max_blocks == 0 || (A && A_scale && B && B_scale && sorted_routes && expert_offsets && block_expert &&
+                              block_start && num_blocks && C),
+          "all pointers must be non-null");
+  REQUIRE(aligned16(A) && aligned16(B) && aligned16(C), "A, B and C must be 16-byte aligned");
+  REQUIRE((reinterpret_cast<uintptr_t>(B_scale) & 7u) == 0, "B_scale must be 8-byte aligned");
+  return hip_status(bfp8::launch_grouped_gemm_mxfp4(A, A_scale, a_row_div, B, B_scale, N, K, sorted_routes,
+                                                    expert_offsets, block_expert, block_start, num_blocks,
+                                                    max_blocks, block_m, C, (hipStream_t)stream),
+                    "moe_mxfp4_grouped_gemm");
 }
 
 bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, int32_t H, const float* router_logits,

@@ -50,6 +50,43 @@ inline int64_t gemm_slots_per_xcd(int64_t max_blocks, int n_tiles) {
   return (max_blocks + kXcd - 1) / kXcd * n_tiles;
 }
 
+// XCD-aware order of the work.  Workgroup i runs on XCD i % 8 as that XCD's
+// slot i / 8 (workgroups are dealt to the XCDs round robin and each XCD takes
+// its own in order).  The blocks in use [0, nb) are cut into 8 contiguous
+// ranges of equal size, one per XCD; one expert's blocks are consecutive, so
+// a range holds whole experts but at its two ends.  Within a range, each
+// expert's blocks form chunks of up to kChunkBlocks consecutive blocks, run
+// in order, and inside a chunk the tile index is outermost: the chunk's
+// workgroups for one weight tile run side by side on one XCD, so the tile
+// leaves HBM once per chunk and its other reads hit that XCD's L2, and a
+// chunk's activation rows stay in L2 across its tiles.  Item s of the XCD
+// lies in the chunk of block gq = lo + s / n_tiles (the chunk's items fill
+// slots n_tiles (c0 - lo) .. n_tiles (c1 - lo) - 1).  Returns false for a
+// workgroup past the work in use; else its block and weight tile.
+template <int BM>
+__device__ __forceinline__ bool gemm_work(int n_tiles, const int32_t* __restrict__ expert_offsets,
+                                          const int32_t* __restrict__ block_expert,
+                                          const int32_t* __restrict__ block_start,
+                                          const int32_t* __restrict__ num_blocks, int64_t& blk, int& nt) {
+  const int x = blockIdx.x % kXcd;
+  const int64_t slot = blockIdx.x / kXcd;
+  const int64_t nb = *num_blocks;
+  const int64_t lo = nb * x / kXcd, hi = nb * (x + 1) / kXcd;
+  if (slot >= (hi - lo) * n_tiles) return false;
+  const int64_t gq = lo + slot / n_tiles;
+  const int eg = block_expert[gq];
+  const int off_e = expert_offsets[eg];
+  const int ig = (block_start[gq] - off_e) / BM;                   // gq among its expert's blocks
+  const int nbe = (expert_offsets[eg + 1] - off_e + BM - 1) / BM;  // the expert's blocks
+  const int cq = ig / kChunkBlocks * kChunkBlocks;                 // chunk's first, in the expert
+  const int64_t c0 = max(gq - ig + cq, lo);
+  const int64_t c1 = min(gq - ig + min(cq + kChunkBlocks, nbe), hi);
+  const int64_t r = slot - (c0 - lo) * n_tiles;
+  nt = (int)(r / (c1 - c0));
+  blk = c0 + r % (c1 - c0);
+  return true;
+}
+
 // Activation registers of one K step: 16-byte line pieces (shared path) or
 // MFMA fragments (direct path).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -73,36 +110,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
     const int32_t* __restrict__ block_start, const int32_t* __restrict__ num_blocks, uint16_t* __restrict__ C) {
   constexpr int CT = BM / 16;  // route tiles
   const int n_tiles = N / kBN;
-  // XCD-aware order.  Workgroup i runs on XCD i % 8 as that XCD's slot
-  // i / 8 (workgroups are dealt to the XCDs round robin and each XCD takes
-  // its own in order).  The blocks in use [0, nb) are cut into 8 contiguous
-  // ranges of equal size, one per XCD; one expert's blocks are consecutive,
-  // so a range holds whole experts but at its two ends.  Within a range,
-  // each expert's blocks form chunks of up to kChunkBlocks consecutive
-  // blocks, run in order, and inside a chunk the tile index is outermost:
-  // the chunk's workgroups for one weight tile run side by side on one XCD,
-  // so the tile leaves HBM once per chunk and its other reads hit that XCD's
-  // L2, and a chunk's activation rows stay in L2 across its tiles.  Item s of
-  // the XCD lies in the chunk of block gq = lo + s / n_tiles (the chunk's
-  // items fill slots n_tiles (c0 - lo) .. n_tiles (c1 - lo) - 1).
-  const int x = blockIdx.x % kXcd;
-  const int64_t slot = blockIdx.x / kXcd;
-  const int64_t nb = *num_blocks;
-  const int64_t lo = nb * x / kXcd, hi = nb * (x + 1) / kXcd;
-  if (slot >= (hi - lo) * n_tiles) return;
-  const int64_t gq = lo + slot / n_tiles;
-  const int eg = block_expert[gq];
-  const int off_e = expert_offsets[eg];
-  const int ig = (block_start[gq] - off_e) / BM;                             // gq among its expert's blocks
-  const int nbe = (expert_offsets[eg + 1] - off_e + BM - 1) / BM;            // the expert's blocks
-  const int cq = ig / kChunkBlocks * kChunkBlocks;                           // chunk's first, in the expert
-  const int64_t c0 = max(gq - ig + cq, lo);
-  const int64_t c1 = min(gq - ig + min(cq + kChunkBlocks, nbe), hi);
-  const int64_t r = slot - (c0 - lo) * n_tiles;
-  const int nt = (int)(r / (c1 - c0));
-  const int64_t blk = c0 + r % (c1 - c0);
-
-  const int e = eg;
+  int64_t blk;
+  int nt;
+  if (!gemm_work<BM>(n_tiles, expert_offsets, block_expert, block_start, num_blocks, blk, nt)) return;
+  const int e = block_expert[blk];
   const int start = block_start[blk];
   const int end_e = expert_offsets[e + 1];
   const int len = min(BM, end_e - start);
@@ -303,6 +314,183 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
   }
 }
 
+// ------------------------------------------------------------------ MXFP4 weights
+//
+// [P2 Reviewed changes: v4_fp4_grouped_gemm.py] the FP4-weight grouped GEMM.
+// Reading (OCP Microscaling Formats v1.0): weight rows of E2M1 elements, two
+// to a byte (the even element in the low nibble), one E8M0 scale byte per 32
+// along K; activations E4M3 with one scale per 128, as in the block-FP8 GEMM.
+// The MFMA takes A in FP4 and B in FP8 with an E8M0 scale per lane (mfma.h):
+// a lane's FP4 slice is 32 consecutive K, one MX block, and its scale byte is
+// that block's; its FP8 slice pairs with it in the hardware's FP8 order.
+// Tile, order and pipeline as grouped_gemm_kernel; the K loop walks 256-wide
+// chunks (two activation groups, eight MX blocks), so that a chunk of a
+// packed weight row is one 128-byte line.  Per chunk and half h (K 128 h ..
+// + 127 of the chunk) one MFMA per (row tile, route tile), its sum times the
+// activation scale of group 2 c + h added to the fp32 accumulator.  The
+// activation chunk (BM rows of 256 bytes) goes through a shared LDS buffer,
+// 16-byte piece p of row r stored at p ^ (r & 15).
+template <int BM>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ As, int a_row_div, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, int N, int K, const int32_t* __restrict__ sorted_routes,
+    const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ block_expert,
+    const int32_t* __restrict__ block_start, const int32_t* __restrict__ num_blocks, uint16_t* __restrict__ C) {
+  constexpr int CT = BM / 16;              // route tiles
+  constexpr int XL = BM * 16 / kThreads;   // 16-byte activation pieces per thread per chunk
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int n_tiles = N / kBN;
+  int64_t blk;
+  int nt;
+  if (!gemm_work<BM>(n_tiles, expert_offsets, block_expert, block_start, num_blocks, blk, nt)) return;
+  const int e = block_expert[blk];
+  const int start = block_start[blk];
+  const int len = min(BM, expert_offsets[e + 1] - start);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kq = lane >> 4;
+  const int G = K / kGroup, KB = K / 2, NS = K / 32;  // groups, packed row bytes, scale bytes per row
+  const int nch = K / 256;                            // K chunks
+
+  // the routes of this lane's MFMA columns and their activation-scale rows
+  const float* asrow[CT];
+  int route[CT];
+#pragma unroll
+  for (int t = 0; t < CT; t++) {
+    const int j = t * 16 + col;
+    route[t] = j < len ? sorted_routes[start + j] : -1;
+    asrow[t] = As + (size_t)(route[t] >= 0 ? route[t] / a_row_div : 0) * G;
+  }
+  // activation pieces this thread loads: piece q = tid + 256 x of the
+  // block's BM x 16, row q / 16, global piece q % 16 (a row without a route
+  // reads activation row 0; its columns are never stored)
+  const uint8_t* xrow[XL];
+#pragma unroll
+  for (int x = 0; x < XL; x++) {
+    const int q = tid + kThreads * x, r = q >> 4;
+    const int rt = r < len ? sorted_routes[start + r] : -1;
+    xrow[x] = A + (size_t)(rt >= 0 ? rt / a_row_div : 0) * K + 16 * (q & 15);
+  }
+  // weight rows: load i of a lane reads row 8 i + lane / 8 of the wave's 32,
+  // bytes 16 (lane % 8) .. + 15 of the chunk's line; the scale bytes of the
+  // lane's fragment rows 16 i + col
+  const int n0 = nt * kBN + wave * kWN;
+  const uint8_t* wl = B + ((size_t)e * N + n0 + (lane >> 3)) * KB + 16 * (lane & 7);
+  const uint8_t* wsr[kRT];
+#pragma unroll
+  for (int i = 0; i < kRT; i++) wsr[i] = Bs + ((size_t)e * N + n0 + 16 * i + col) * NS;
+
+  v4f acc[kRT][CT];
+#pragma unroll
+  for (int i = 0; i < kRT; i++)
+#pragma unroll
+    for (int t = 0; t < CT; t++) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  __shared__ __align__(16) u32x4 s_w[kThreads / 64][kWN * 8];
+  __shared__ __align__(16) u32x4 s_x[2][BM * 16];
+  u32x4* sw = s_w[wave];
+
+  // One K step: request chunk cn into the next register set, then multiply
+  // the chunk held in the current one through shared buffer xb (as in
+  // grouped_gemm_kernel: two sets alternate, every load unconditional and
+  // issued before the current chunk is used).
+  auto step = [&](int cn, u32x4 (&wc)[4], u32x4 (&xc)[XL], float (&sc)[CT][2], uint2 (&bc)[kRT], u32x4 (&wn)[4],
+                  u32x4 (&xn)[XL], float (&sn)[CT][2], uint2 (&bn)[kRT], u32x4* xb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < CT; t++) {
+      sn[t][0] = asrow[t][2 * cn];
+      sn[t][1] = asrow[t][2 * cn + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kRT; i++) bn[i] = *reinterpret_cast<const uint2*>(wsr[i] + 8 * cn);
+#pragma unroll
+    for (int i = 0; i < 4; i++) wn[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * KB + (size_t)cn * 128);
+#pragma unroll
+    for (int x = 0; x < XL; x++) xn[x] = *reinterpret_cast<const u32x4*>(xrow[x] + (size_t)cn * 256);
+    __builtin_amdgcn_sched_barrier(0);  // the loads leave before anything waits
+#pragma unroll
+    for (int x = 0; x < XL; x++) {
+      const int q = tid + kThreads * x, r = q >> 4;
+      xb[r * 16 + ((q & 15) ^ (r & 15))] = xc[x];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = 8 * i + (lane >> 3);
+      sw[r * 8 + ((lane & 7) ^ (r & 7))] = wc[i];
+    }
+    // A fragments: row 16 i + col, bytes 64 h + 16 kq .. + 15 (piece 4 h + kq)
+    v8i wa[kRT][2];
+#pragma unroll
+    for (int i = 0; i < kRT; i++) {
+      const int r = 16 * i + col;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const u32x4 v = sw[r * 8 + ((4 * h + kq) ^ (r & 7))];
+        wa[i][h] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      }
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the shared buffer is written
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < CT; t++) {
+      const int r = 16 * t + col;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        // B fragment: route row r, bytes 128 h + 16 kq .. + 15 and 128 h + 64
+        // + 16 kq .. + 15 (pieces 8 h + kq and 8 h + 4 + kq)
+        const u32x4 lo = xb[r * 16 + ((8 * h + kq) ^ (r & 15))];
+        const u32x4 hi = xb[r * 16 + ((8 * h + 4 + kq) ^ (r & 15))];
+        const v8i xf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const float asc = route[t] >= 0 ? sc[t][h] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kRT; i++) {
+          const int e8 = (int)(((h ? bc[i].y : bc[i].x) >> (8 * kq)) & 0xFFu);
+          const v4f p = mfma_f4f8_16x16x128(wa[i][h], xf, e8, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int v = 0; v < 4; v++) acc[i][t][v] = __builtin_fmaf(p[v], asc, acc[i][t][v]);
+        }
+      }
+    }
+  };
+
+  u32x4 w0[4], w1[4], x0[XL], x1[XL];
+  float s0[CT][2], s1[CT][2];
+  uint2 b0[kRT], b1[kRT];
+#pragma unroll
+  for (int t = 0; t < CT; t++) {
+    s0[t][0] = asrow[t][0];
+    s0[t][1] = asrow[t][1];
+  }
+#pragma unroll
+  for (int i = 0; i < kRT; i++) b0[i] = *reinterpret_cast<const uint2*>(wsr[i]);
+#pragma unroll
+  for (int i = 0; i < 4; i++) w0[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * KB);
+#pragma unroll
+  for (int x = 0; x < XL; x++) x0[x] = *reinterpret_cast<const u32x4*>(xrow[x]);
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    step(c + 1, w0, x0, s0, b0, w1, x1, s1, b1, s_x[0]);
+    step(min(c + 2, nch - 1), w1, x1, s1, b1, w0, x0, s0, b0, s_x[1]);
+  }
+  if (c < nch) step(c, w0, x0, s0, b0, w1, x1, s1, b1, s_x[0]);
+
+  // epilogue: lane holds rows n0 + 16 i + 4 kq + v (v = 0..3) of route[t]
+#pragma unroll
+  for (int t = 0; t < CT; t++) {
+    if (route[t] < 0) continue;
+    uint16_t* crow = C + (size_t)route[t] * N + n0;
+#pragma unroll
+    for (int i = 0; i < kRT; i++) {
+      uint2 o;
+      o.x = f32_to_bf16(acc[i][t][0]) | (f32_to_bf16(acc[i][t][1]) << 16);
+      o.y = f32_to_bf16(acc[i][t][2]) | (f32_to_bf16(acc[i][t][3]) << 16);
+      *reinterpret_cast<uint2*>(crow + i * 16 + 4 * kq) = o;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div, const uint8_t* B,
@@ -332,6 +520,32 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
       return hipErrorInvalidValue;
   }
 #undef BFP8_GEMM_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_mxfp4(const uint8_t* A, const float* As, int a_row_div, const uint8_t* B,
+                                     const uint8_t* Bs, int N, int K, const int32_t* sorted_routes,
+                                     const int32_t* expert_offsets, const int32_t* block_expert,
+                                     const int32_t* block_start, const int32_t* num_blocks, int64_t max_blocks,
+                                     int block_m, uint16_t* C, hipStream_t stream) {
+  if (max_blocks == 0 || N / kBN == 0) return hipSuccess;
+  if (K % 256 != 0) return hipErrorInvalidValue;  // the caller checks
+  const int64_t grid = gemm_slots_per_xcd(max_blocks, N / kBN) * kXcd;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+#define BFP8_MX_CASE(BMV)                                                                                      \
+  case BMV:                                                                                                    \
+    hipLaunchKernelGGL((grouped_gemm_mxfp4_kernel<BMV>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A, As, \
+                       a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,        \
+                       num_blocks, C);                                                                       \
+    break;
+  switch (block_m) {
+    BFP8_MX_CASE(16)
+    BFP8_MX_CASE(32)
+    BFP8_MX_CASE(64)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef BFP8_MX_CASE
   return hipGetLastError();
 }
 

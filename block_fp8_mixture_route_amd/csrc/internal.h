@@ -150,6 +150,14 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
                                const int32_t* block_start, const int32_t* num_blocks, int64_t max_blocks,
                                int block_m, uint16_t* C, hipStream_t stream, bool channel = false);
 
+// MXFP4-weight grouped GEMM: B [L, N, K/2] packed E2M1 with E8M0 scale bytes
+// Bs [L, N, K/32]; A and As as launch_grouped_gemm.  K a multiple of 256.
+hipError_t launch_grouped_gemm_mxfp4(const uint8_t* A, const float* As, int a_row_div, const uint8_t* B,
+                                     const uint8_t* Bs, int N, int K, const int32_t* sorted_routes,
+                                     const int32_t* expert_offsets, const int32_t* block_expert,
+                                     const int32_t* block_start, const int32_t* num_blocks, int64_t max_blocks,
+                                     int block_m, uint16_t* C, hipStream_t stream);
+
 // W8A8 variant: one scale per activation row (dynamic: amax / 448 of the row
 // in fmt; static_scale > 0: that scale for every row).  Rows of up to 8192.
 bool rows_quant_fits(int K);

@@ -4,14 +4,15 @@
 // operands in OCP E4M3: C[16x16] += A[16x128] * B[128x16], fp32 accumulate.
 //
 // Operand fragment of lane l (64 lanes): row (A) or column (B) index l % 16,
-// K slot group kq = l / 16, 32 bytes in 8 VGPRs.  The MFMA pairs A's and B's
-// bytes slot by slot, so the sum over K does not depend on which K index each
-// slot holds as long as A and B use the same assignment.  We choose, for a
-// 128-wide K chunk starting at k0:
+// K slot group kq = l / 16, 32 bytes in 8 VGPRs.  The hardware's K order of
+// an E4M3 fragment (measured through the FP4 x FP8 form, where it shows) is,
+// for a 128-wide K chunk starting at k0:
 //     bytes  0..15 of lane l  <- k0 + 16*kq + [0, 16)
 //     bytes 16..31 of lane l  <- k0 + 64 + 16*kq + [0, 16)
 // so that one 16-byte load per lane reads 64 contiguous bytes of each of the
-// 16 rows, and the two loads together cover the rows' 128-byte chunk.
+// 16 rows, and the two loads together cover the rows' 128-byte chunk.  An
+// E2M1 fragment (16 bytes in 4 VGPRs) holds K k0 + 32*kq + [0, 32) in order,
+// element 2j in the low nibble of byte j.
 //
 // Result fragment: lane l holds C[4*(l/16) + v][l % 16], v = 0..3.
 #pragma once
@@ -27,6 +28,14 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ v4f mfma_f8_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
   // cbsz = blgp = 0: E4M3 operands; scale operands 127 = 2^0.
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// A in E2M1 (cbsz 4: the low 16 bytes of a, 32 elements, element 2j in the
+// low nibble of byte j), B in E4M3 (the order above); scale_a the E8M0 byte
+// of the lane's A slice, B unscaled (127).  The scales act per lane, and a
+// lane's A slice, K 32 (l / 16) .. + 31 of its row, is one MX block of 32.
+__device__ __forceinline__ v4f mfma_f4f8_16x16x128(const v8i& a, const v8i& b, int scale_a, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, scale_a, 0, 127);
 }
 
 // Load the 32-byte fragment of a 128-byte chunk at p (16-byte aligned) for

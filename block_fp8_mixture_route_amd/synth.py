@@ -319,3 +319,82 @@ def exact_layer_inputs(M: int, E: int, k: int, H: int, I: int, *key, device="cpu
     w2 = _e4m3_codes_of(w2i).contiguous()
     w2_s = torch.exp2(torch.randint(-9, -6, (E, H // GROUP, GI), generator=g, device=device).to(torch.float32))
     return hidden, ids.contiguous(), w, MoEWeights(w13, w13_s.contiguous(), w2, w2_s.contiguous())
+
+
+# ------------------------------------------------------------------ MXFP4 weights
+
+MX_BLOCK = 32
+
+
+class MxWeights:
+    """MXFP4 expert weights: w13 [L, 2I, H/2] and w2 [L, H, I/2] packed E2M1
+    codes (the even element of a pair in the low nibble), w13_s [L, 2I, H/32]
+    and w2_s [L, H, I/32] E8M0 scale bytes (all uint8)."""
+
+    def __init__(self, w13, w13_s, w2, w2_s):
+        self.w13, self.w13_s, self.w2, self.w2_s = w13, w13_s, w2, w2_s
+
+
+def pack_e2m1(codes: torch.Tensor) -> torch.Tensor:
+    """[..., K] E2M1 codes (0..15) -> [..., K/2] bytes, element 2j in the low
+    nibble of byte j."""
+    c = codes.to(torch.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).contiguous()
+
+
+def mxfp4_weights(L: int, H: int, I: int, *key, scale_lo=118, scale_hi=124, device="cpu") -> MxWeights:
+    """Random MXFP4 experts: uniform E2M1 codes, scale bytes uniform in
+    [scale_lo, scale_hi) independently per 32-element block."""
+    g = gen(device, *key, "mxfp4_weights", L, H, I)
+    c13 = torch.randint(0, 16, (L, 2 * I, H), generator=g, device=device)
+    c2 = torch.randint(0, 16, (L, H, I), generator=g, device=device)
+    s13 = torch.randint(scale_lo, scale_hi, (L, 2 * I, H // MX_BLOCK), generator=g, device=device).to(torch.uint8)
+    s2 = torch.randint(scale_lo, scale_hi, (L, H, I // MX_BLOCK), generator=g, device=device).to(torch.uint8)
+    return MxWeights(pack_e2m1(c13), s13.contiguous(), pack_e2m1(c2), s2.contiguous())
+
+
+# E2M1 codes of the integer values 0, 1, 2, 3, 4, 6 (negatives: | 8)
+_E2M1_INT = {0: 0, 1: 2, 2: 4, 3: 5, 4: 6, 6: 7}
+
+
+def _e2m1_codes_of(values: torch.Tensor) -> torch.Tensor:
+    mag = values.abs().to(torch.int64)
+    lut = torch.zeros(7, dtype=torch.int64, device=values.device)
+    for v, c in _E2M1_INT.items():
+        lut[v] = c
+    return (lut[mag] | ((values < 0).to(torch.int64) << 3)).to(torch.uint8)
+
+
+def exact_mxfp4_layer_inputs(M: int, E: int, k: int, H: int, I: int, *key, device="cpu"):
+    """hidden, topk ids, topk weights and MXFP4 weights of one layer instance
+    built like exact_layer_inputs so that every sum is exact in fp32 whatever
+    the order: the hidden rows and routing as there; W13 integer E2M1 values in
+    {0, +-1, +-2, +-3} with one scale byte 2^b (b in {-9, -8, -7}) shared by the
+    four blocks of each 128-wide group of a row; W2 rows with two non-zero
+    values (+-1, +-2) in different runs of 8 consecutive K, scales as W13."""
+    g = gen(device, *key, "exact_mxfp4_layer", M, E, k, H, I)
+    G, GI = H // GROUP, I // GROUP
+    m = torch.randint(-4, -1, (M, 1), generator=g, device=device).to(torch.float32)
+    n = torch.randint(-4, 5, (M, H), generator=g, device=device).to(torch.float32)
+    pos = torch.randint(0, GROUP, (M, G), generator=g, device=device)
+    sign = torch.randint(0, 2, (M, G), generator=g, device=device).to(torch.float32) * 2 - 1
+    n.view(M, G, GROUP).scatter_(2, pos[:, :, None], (448.0 * sign)[:, :, None])
+    hidden = (n * torch.exp2(m)).to(torch.bfloat16).contiguous()
+    ids, w = uniform_routing(M, E, k, *key, "exact_mx_routing", device=device)
+    if k > 2:
+        ids = ids.clone()
+        ids[0, 1] = -1
+        ids[0, k - 1] = -1
+    w13v = torch.randint(-3, 4, (E, 2 * I, H), generator=g, device=device)
+    b13 = torch.randint(127 - 9, 127 - 6, (E, 2 * I, G), generator=g, device=device)
+    w2v = torch.zeros(E, H, I, dtype=torch.int64, device=device)
+    sl = torch.randint(0, I // 16, (E, H, 1), generator=g, device=device)
+    off = torch.randint(0, 8, (E, H, 2), generator=g, device=device)
+    p2 = sl * 16 + torch.tensor([0, 8], device=device) + off
+    val = torch.randint(1, 3, (E, H, 2), generator=g, device=device)
+    val = val * (torch.randint(0, 2, (E, H, 2), generator=g, device=device) * 2 - 1)
+    w2v.scatter_(2, p2, val)
+    b2 = torch.randint(127 - 9, 127 - 6, (E, H, GI), generator=g, device=device)
+    W = MxWeights(pack_e2m1(_e2m1_codes_of(w13v)), b13.repeat_interleave(GROUP // MX_BLOCK, 2).to(torch.uint8).contiguous(),
+                  pack_e2m1(_e2m1_codes_of(w2v)), b2.repeat_interleave(GROUP // MX_BLOCK, 2).to(torch.uint8).contiguous())
+    return hidden, ids.contiguous(), w, W

@@ -125,8 +125,20 @@ typedef struct {
  * CHANNEL: one fp32 scale per weight row (w13_scale [L, 2I], w2_scale [L, H])
  *          and one per activation row, dynamic or static -- the W8A8 variant
  *          [P2 Reviewed changes: w8a8.py, the static FP8 MoE backend].  Runs
- *          the general path (six launches); H and I at most 8192. */
-typedef enum { BFP8MOE_WEIGHT_SCALE_BLOCK = 0, BFP8MOE_WEIGHT_SCALE_CHANNEL = 1 } bfp8moe_weight_scale_t;
+ *          the general path (six launches); H and I at most 8192.
+ * MXFP4:   weights in OCP MX FP4 -- E2M1 elements two to a byte (the even
+ *          element of a pair in the low nibble) with one E8M0 scale byte per 32
+ *          along K (w13 [L, 2I, H/2] with w13_scale [L, 2I, H/32] bytes, w2
+ *          [L, H, I/2] with w2_scale [L, H, I/32]); activations as BLOCK
+ *          [P2 Reviewed changes: v4_fp4_grouped_gemm.py, v4_swiglu_quant.py;
+ *          P3 Matched GLM serving A/B: MXFP4 the DeepSeek-V4 checkpoint's
+ *          weight format].  Called through fused_moe_mxfp4 (byte scales); runs
+ *          the general path; H and I multiples of 256. */
+typedef enum {
+    BFP8MOE_WEIGHT_SCALE_BLOCK = 0,
+    BFP8MOE_WEIGHT_SCALE_CHANNEL = 1,
+    BFP8MOE_WEIGHT_MXFP4 = 2
+} bfp8moe_weight_scale_t;
 
 /* Fill *opts with the defaults: block_m 0, FP32 scales, no clamp, the full
  * expert range, no flags, no stage events, block scaling.  opts: host
@@ -280,6 +292,20 @@ bfp8moe_status_t moe_fp8_grouped_gemm(const uint8_t* A, const float* A_scale, in
                                       const int32_t* num_blocks, int64_t max_blocks, int32_t block_m,
                                       int64_t R, uint16_t* C, void* stream);
 
+/* The grouped GEMM with MXFP4 weights: as moe_fp8_grouped_gemm with
+ * B [L, N, K/2] packed E2M1 and B_scale [L, N, K/32] E8M0 bytes (8-byte
+ * aligned):
+ *   C[r, n] = bf16( sum_g A_scale[r/a_row_div, g] * sum_{b in group g} 2^(B_scale[e, n, b] - 127)
+ *                        * sum_{i in block b} A[r/a_row_div, i] * B[e, n, i] ),
+ * blocks b of 32 along K, accumulated in fp32.  K a positive multiple of 256
+ * [P2 Reviewed changes: v4_fp4_grouped_gemm.py]. */
+bfp8moe_status_t moe_mxfp4_grouped_gemm(const uint8_t* A, const float* A_scale, int32_t a_row_div, const uint8_t* B,
+                                        const uint8_t* B_scale, int32_t L, int32_t N, int32_t K,
+                                        const int32_t* sorted_routes, const int32_t* expert_offsets,
+                                        const int32_t* block_expert, const int32_t* block_start,
+                                        const int32_t* num_blocks, int64_t max_blocks, int32_t block_m, int64_t R,
+                                        uint16_t* C, void* stream);
+
 /* The grouped GEMM of the W8A8 variant: as moe_fp8_grouped_gemm with one
  * activation scale per row, A_scale [R/a_row_div rows], and one weight scale
  * per output channel, B_scale [L, N] (16-byte aligned):
@@ -419,6 +445,20 @@ bfp8moe_status_t fused_moe_block_fp8(const uint16_t* hidden, int64_t M, int32_t 
                                      const uint8_t* w2, const float* w2_scale, int32_t E, int32_t I,
                                      const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* The layer with MXFP4 weights (see bfp8moe_weight_scale_t): arguments as
+ * fused_moe_block_fp8 with w13 [L, 2I, H/2], w13_scale [L, 2I, H/32], w2
+ * [L, H, I/2], w2_scale [L, H, I/32] (E8M0 bytes, 8-byte aligned).  opts is
+ * required and must have weight_scale_mode BFP8MOE_WEIGHT_MXFP4; the
+ * workspace is fused_moe_block_fp8_workspace_size with the same opts.  Stages:
+ * "route_prepare_quant", "gate_up_gemm_mxfp4", "silu_and_mul_quant",
+ * "down_gemm_mxfp4", "moe_reduce" (a separate "quant_fp8" where route
+ * preparation cannot carry it). */
+bfp8moe_status_t fused_moe_mxfp4(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
+                                 const float* topk_w, int32_t k, const uint8_t* w13, const uint8_t* w13_scale,
+                                 const uint8_t* w2, const uint8_t* w2_scale, int32_t E, int32_t I,
+                                 const bfp8moe_opts_t* opts, uint16_t* out, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* The layer with its router: moe_router_topk on router_logits [M, E] fp32
  * (score_fn, router_bias, renormalize, routed_scale as there) -- or, with

@@ -205,3 +205,25 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         bfp8.quant_fp8(torch.zeros(1, 128, dtype=torch.bfloat16))
+
+
+def test_mxfp4_layer_host_checks():
+    o = bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4)
+    assert bfp8.fused_moe_stages(64, 2048, 8, 32, 768, o) == [
+        "route_prepare_quant", "gate_up_gemm_mxfp4", "silu_and_mul_quant", "down_gemm_mxfp4", "moe_reduce"]
+    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o)[1] == "gate_up_gemm_mxfp4"  # never the few-token path
+    for bad in (dict(), dict(flags=bfp8.FLAG_LAYER_TOKEN), dict(flags=bfp8.FLAG_LAYER_DECODE),
+                dict(act_static_scale=0.5)):
+        H, I = (256, 128) if not bad else (256, 256)
+        with pytest.raises(bfp8.BFP8MoEError):
+            bfp8.fused_moe_stages(4, H, 2, 8, I, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4, **bad))
+    # byte scales do not go through the fp32-scale entry point, nor block scales through fused_moe_mxfp4
+    # (both fail in the host checks, before anything is launched)
+    st = _lib.lib().fused_moe_block_fp8(None, 0, 256, None, None, 2, None, None, None, None, 8, 256,
+                                        ctypes.byref(o), None, None, 0, None)
+    assert st == 1
+    st = _lib.lib().fused_moe_mxfp4(None, 0, 256, None, None, 2, None, None, None, None, 8, 256,
+                                    ctypes.byref(bfp8.opts()), None, None, 0, None)
+    assert st == 1
+    assert _lib.lib().fused_moe_mxfp4(None, 0, 256, None, None, 2, None, None, None, None, 8, 256, None, None,
+                                      None, 0, None) == 1
