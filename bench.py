@@ -481,6 +481,76 @@ SUITE_STEPS = {"tiny": 200, "decode_m1": 480, "decode_m4": 200, "decode_m16": 10
                "small_m128": 20, "small_m512": 20, "large_m2048": 10}
 
 
+def variants_table(hip, stream, dev):
+    """The layer with each weight format on the general-path configs, one
+    instance each (its weights exceed the Infinity Cache several times over),
+    graph-timed over 8 calls: block FP8, the W8A8 variant (random E4M3 codes,
+    per-channel scales, dynamic per-token activation scales) and MXFP4 weights
+    (random E2M1 codes, E8M0 scales per 32).  Compulsory bytes: the active
+    experts' weights and scales in each format, hidden states in, output out,
+    routing in."""
+    import torch
+
+    import block_fp8_mixture_route_amd as bfp8
+    from block_fp8_mixture_route_amd import synth
+
+    print()
+    print("| config | format | µs / layer | compulsory MB | GB/s | HBM roofline µs | fraction |")
+    print("|---|---|---|---|---|---|---|")
+    res = {}
+    for name in ("small_m128", "small_m512", "large_m2048"):
+        case = synth.LAYER_CASES[name]
+        M, E, k, H, I = case.M, case.E, case.k, case.H, case.I
+        hidden, ids, w, W = synth.layer_inputs(case, 0, device=dev)
+        d = int(torch.unique(ids[ids >= 0]).numel())
+        io = M * H * 2 * 2 + M * k * 8
+        g = torch.Generator(device=dev).manual_seed(synth.seed_of("variants", name))
+
+        def e4m3(shape):
+            # random E4M3 codes but the NaN ones, drawn one expert at a time
+            # (no single random tensor grows with E)
+            t = torch.empty(shape, dtype=torch.uint8, device=dev)
+            for e in range(shape[0]):
+                mag = torch.randint(0, 0x7F, shape[1:], generator=g, device=dev, dtype=torch.uint8)
+                t[e].copy_(mag | (torch.randint(0, 2, shape[1:], generator=g, device=dev, dtype=torch.uint8) << 7))
+            return t
+
+        c13, c2 = e4m3((E, 2 * I, H)), e4m3((E, H, I))
+        s13 = torch.rand(E, 2 * I, generator=g, device=dev) * 1e-3 + 1e-4
+        s2 = torch.rand(E, H, generator=g, device=dev) * 1e-3 + 1e-4
+        MX = synth.mxfp4_weights(E, H, I, "variants", name, device=dev)
+        out = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+        forms = {
+            "block FP8": (lambda: bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=E, out=out,
+                                                          ws=ws["block FP8"]),
+                          bfp8.opts(), d * (3 * I * H + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)))),
+            "W8A8": (lambda: bfp8.fused_moe_block_fp8(hidden, ids, w, c13, s13, c2, s2, E=E, out=out, ws=ws["W8A8"],
+                                                     o=opts["W8A8"]),
+                     bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL), d * (3 * I * H + 4 * (2 * I + H))),
+            "MXFP4": (lambda: bfp8.fused_moe_mxfp4(hidden, ids, w, MX.w13, MX.w13_s, MX.w2, MX.w2_s, E=E, out=out,
+                                                  ws=ws["MXFP4"], o=opts["MXFP4"]),
+                      bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4), d * (3 * I * H // 2 + 3 * I * H // 32)),
+        }
+        opts = {f: v[1] for f, v in forms.items()}
+        ws = {f: torch.empty(max(bfp8.fused_moe_workspace_size(M, H, k, E, I, v[1]), 1), dtype=torch.uint8,
+                             device=dev) for f, v in forms.items()}
+        res[name] = {}
+        ext = torch.cuda.ExternalStream(stream.value, device=dev)
+        for f, (fn, _, wbytes) in forms.items():
+            with torch.cuda.stream(ext):  # the binding launches on torch's current stream: the timed one
+                fn()
+                hip.sync(stream)
+                us = time_graph(hip, stream, lambda: [fn() for _ in range(8)], 5) * 1e3 / 8
+            nbytes = wbytes + io
+            roof = nbytes / 8e12 * 1e6
+            res[name][f] = {"us": us, "bytes": nbytes, "roofline_us": roof}
+            print(f"| {name} | {f} | {us:.2f} | {nbytes / 1e6:.1f} | {nbytes / (us * 1e3):.0f} | {roof:.2f} | "
+                  f"{roof / us:.3f} |", flush=True)
+        del c13, c2, MX, W
+        torch.cuda.empty_cache()
+    return res
+
+
 def suite(hip, stream, dev):
     """Every layer config, the activation+quant workload (fused against two
     kernels), route preparation (one workgroup against many) and a plain copy
@@ -634,6 +704,7 @@ def suite(hip, stream, dev):
         res["route_prep"][R] = {"L": L, "block_m": bm, "single_us": row[0], "multi_us": row[1]}
         print(f"| {R} | {L} | {bm} | {row[0]:.2f} | {row[1]:.2f} |", flush=True)
 
+    res["variants"] = variants_table(hip, stream, dev)
     res["router"] = router_table(hip, stream, dev)
     res["routed"] = routed_table(hip, stream, dev)
 
@@ -829,7 +900,7 @@ def oracle_layer_seconds(case, inst, seconds, threads=None, min_runs=1):
     if threads is not None:
         O.set_threads(threads)
     try:
-        used_threads = min(O.num_threads(), case.M)  # the oracle parallelises over tokens
+        used_threads = O.num_threads()  # the oracle's GEMMs spread their output rows over the threads
         t0 = time.time()
         n = 0
         while True:

@@ -344,13 +344,19 @@ def pack_e2m1(codes: torch.Tensor) -> torch.Tensor:
 
 def mxfp4_weights(L: int, H: int, I: int, *key, scale_lo=118, scale_hi=124, device="cpu") -> MxWeights:
     """Random MXFP4 experts: uniform E2M1 codes, scale bytes uniform in
-    [scale_lo, scale_hi) independently per 32-element block."""
+    [scale_lo, scale_hi) independently per 32-element block.  Drawn one
+    expert at a time, so that no single random tensor grows with L."""
     g = gen(device, *key, "mxfp4_weights", L, H, I)
-    c13 = torch.randint(0, 16, (L, 2 * I, H), generator=g, device=device)
-    c2 = torch.randint(0, 16, (L, H, I), generator=g, device=device)
-    s13 = torch.randint(scale_lo, scale_hi, (L, 2 * I, H // MX_BLOCK), generator=g, device=device).to(torch.uint8)
-    s2 = torch.randint(scale_lo, scale_hi, (L, H, I // MX_BLOCK), generator=g, device=device).to(torch.uint8)
-    return MxWeights(pack_e2m1(c13), s13.contiguous(), pack_e2m1(c2), s2.contiguous())
+    W = MxWeights(torch.empty(L, 2 * I, H // 2, dtype=torch.uint8, device=device),
+                  torch.empty(L, 2 * I, H // MX_BLOCK, dtype=torch.uint8, device=device),
+                  torch.empty(L, H, I // 2, dtype=torch.uint8, device=device),
+                  torch.empty(L, H, I // MX_BLOCK, dtype=torch.uint8, device=device))
+    for e in range(L):
+        W.w13[e].copy_(pack_e2m1(torch.randint(0, 16, (2 * I, H), generator=g, device=device)))
+        W.w2[e].copy_(pack_e2m1(torch.randint(0, 16, (H, I), generator=g, device=device)))
+        W.w13_s[e].copy_(torch.randint(scale_lo, scale_hi, (2 * I, H // MX_BLOCK), generator=g, device=device))
+        W.w2_s[e].copy_(torch.randint(scale_lo, scale_hi, (H, I // MX_BLOCK), generator=g, device=device))
+    return W
 
 
 # E2M1 codes of the integer values 0, 1, 2, 3, 4, 6 (negatives: | 8)
