@@ -16,7 +16,9 @@ import os
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libbfp8moe.so")
+# BFP8MOE_LIB names another build of the same library (the host-sanitized one
+# of tests/run_sanitized.py); by default the in-tree build
+LIB_PATH = os.environ.get("BFP8MOE_LIB") or os.path.join(PKG, "libbfp8moe.so")
 
 SCALE_FP32 = 0
 SCALE_UE8M0 = 1

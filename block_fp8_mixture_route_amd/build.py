@@ -36,20 +36,30 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (the
+# argument checks, planning and launch set-up of the C ABI); the device code
+# is built as always.  The library then needs clang's shared ASan runtime
+# preloaded into the process (tests/run_sanitized.py does this).
+SAN_LIB = os.path.join(PKG, "libbfp8moe_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-shared-libasan"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     from . import gen_exp_table
 
     gen_exp_table.write()  # csrc/exp_neg_table.h, included by device.h
     srcs = sources()
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+    out = SAN_LIB if sanitize else LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(SAN_FLAGS if sanitize else []), "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB)
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -20,14 +20,22 @@ SCALE_FP32 = 0
 SCALE_UE8M0 = 1
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc: -O2, no FP contraction, no fast-math."""
-    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        tmp = LIB + ".tmp"
+SAN_LIB = os.path.join(HERE, "liboracle_san.so")
+
+
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc: -O2, no FP contraction, no fast-math.
+    sanitize: a separate build with AddressSanitizer and
+    UndefinedBehaviorSanitizer (gcc's libasan must then be preloaded)."""
+    out = SAN_LIB if sanitize else LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(SRC):
+        tmp = out + ".tmp"
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
         subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-                               "-std=gnu11", "-Wall", "-shared", "-fPIC", SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, LIB)
-    return LIB
+                               "-std=gnu11", "-Wall", "-shared", "-fPIC", *(san if sanitize else []), SRC,
+                               "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -36,8 +44,10 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(LIB)
+        # BFP8MOE_ORACLE_LIB names another build (the sanitized one of
+        # tests/run_sanitized.py); by default this directory's, built on demand
+        path = os.environ.get("BFP8MOE_ORACLE_LIB") or build()
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         sig = {
