@@ -551,6 +551,73 @@ def variants_table(hip, stream, dev):
     return res
 
 
+def phase_table(hip, stream, dev, steps):
+    """Where the decode layer's time goes.  The M=1, E=256, top-k 8, I=256
+    layer at hidden widths 1024..7168: each of its two kernels alone and the
+    whole layer, graph-timed over instances whose weights exceed the Infinity
+    Cache (measure_layer).  A least-squares line per kernel, time = fixed +
+    bytes / rate over the widths, gives its fixed cost (launch, the first
+    loads' latency, the tail after the last weight byte) and the rate at which
+    it streams; the H=7168 layer is then split into those parts and the time
+    between the kernels (the layer minus the two kernels alone)."""
+    import numpy as np
+
+    from block_fp8_mixture_route_amd import synth
+
+    base = synth.LAYER_CASES["decode_m1"]
+    rows = []
+    print()
+    print("| H | gate/up MB | gate/up µs | down MB | down µs | layer µs |")
+    print("|---|---|---|---|---|---|")
+    for H in (1024, 2048, 3584, 5120, 7168):
+        case = dataclasses.replace(base, name=f"decode_m1_h{H}", H=H)
+        r = measure_layer(case, steps, 8, 0, hip, stream, dev)
+        ids = r["insts"][0][1]
+        d = int(torch_unique_count(ids))
+        b_up = d * (2 * case.I * H + 4 * (2 * case.I // 128) * (H // 128)) + H * 2 + case.k * 8 + case.k * case.I * 2
+        b_dn = d * (H * case.I + 4 * (H // 128) * (case.I // 128)) + case.k * case.I * 2 + case.k * 8 + H * 2
+        st = r["stage_us"]
+        rows.append((H, b_up, st["token_gate_up_swiglu"], b_dn, st["token_down_reduce"], r["us_per_layer"]))
+        print(f"| {H} | {b_up / 1e6:.2f} | {rows[-1][2]:.2f} | {b_dn / 1e6:.2f} | {rows[-1][4]:.2f} | "
+              f"{rows[-1][5]:.2f} |", flush=True)
+        del r
+    a = np.array(rows, dtype=np.float64)
+    fit = {}
+    for name, bcol, tcol in (("gate/up", 1, 2), ("down", 3, 4)):
+        slope, icpt = np.polyfit(a[:, bcol], a[:, tcol], 1)  # µs per byte, µs
+        fit[name] = (icpt, 1.0 / slope / 1e3)                  # fixed µs, GB/s
+    H, b_up, t_up, b_dn, t_dn, t_layer = rows[-1]
+    between = t_layer - t_up - t_dn
+    print()
+    print("| kernel | fixed µs (intercept) | streaming GB/s (slope) |")
+    print("|---|---|---|")
+    for name, (f0, gbs) in fit.items():
+        print(f"| {name} | {f0:.2f} | {gbs:.0f} |")
+    print()
+    print(f"H = {H} layer, {t_layer:.2f} µs:")
+    print()
+    print("| part | µs |")
+    print("|---|---|")
+    parts = [("gate/up: fixed cost", fit["gate/up"][0]),
+             (f"gate/up: {b_up / 1e6:.1f} MB at {fit['gate/up'][1]:.0f} GB/s", b_up / (fit["gate/up"][1] * 1e3)),
+             ("gate/up: fitted minus measured", t_up - fit["gate/up"][0] - b_up / (fit["gate/up"][1] * 1e3)),
+             ("down: fixed cost", fit["down"][0]),
+             (f"down: {b_dn / 1e6:.1f} MB at {fit['down'][1]:.0f} GB/s", b_dn / (fit["down"][1] * 1e3)),
+             ("down: fitted minus measured", t_dn - fit["down"][0] - b_dn / (fit["down"][1] * 1e3)),
+             ("between the kernels (layer minus both alone)", between)]
+    for name, v in parts:
+        print(f"| {name} | {v:.2f} |")
+    print(f"| total | {sum(v for _, v in parts):.2f} |")
+    print()
+    print(f"All {(b_up + b_dn) / 1e6:.1f} MB at 8 TB/s: {(b_up + b_dn) / 8e6:.2f} µs; at the gate/up kernel's own "
+          f"streaming rate: {(b_up + b_dn) / (fit['gate/up'][1] * 1e3):.2f} µs.", flush=True)
+
+
+def torch_unique_count(ids):
+    import torch
+    return torch.unique(ids[ids >= 0]).numel()
+
+
 def suite(hip, stream, dev):
     """Every layer config, the activation+quant workload (fused against two
     kernels), route preparation (one workgroup against many) and a plain copy
@@ -750,6 +817,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=0, help="routes per compact block of the general path (0 = auto)")
     ap.add_argument("--floor", action="store_true", help="only the graph launch floor of one kernel")
     ap.add_argument("--router", action="store_true", help="only the router timing table")
+    ap.add_argument("--phases", action="store_true",
+                    help="only the decode layer's phase table: each kernel alone and the layer at five hidden widths, "
+                         "fixed cost and streaming rate per kernel fitted, the H=7168 layer split into them")
     ap.add_argument("--suite", metavar="JSON", default=None,
                     help="instead of the metric line: every layer config, activation+quant, route preparation "
                          "and a plain copy, as markdown tables on stdout and figures in JSON")
@@ -775,6 +845,9 @@ def main():
     if args.router:
         router_table(hip, stream, dev)
         routed_table(hip, stream, dev)
+        return
+    if args.phases:
+        phase_table(hip, stream, dev, args.steps)
         return
     if args.suite:
         res = suite(hip, stream, dev)
