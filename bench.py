@@ -825,6 +825,11 @@ def main():
                          "and a plain copy, as markdown tables on stdout and figures in JSON")
     args = ap.parse_args()
 
+    if args.suite and os.environ.get("BFP8MOE_SUITE_ENABLE") != "1":
+        print("bench.py --suite is disabled: its last run ended in a GPU memory fault whose cause has not been found "
+              "(the single-table modes --config, --phases, --floor and --router are unaffected; "
+              "BFP8MOE_SUITE_ENABLE=1 runs it anyway)", file=sys.stderr)
+        sys.exit(3)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -913,7 +918,8 @@ def main():
 KERNEL_SOURCES = {
     "token_gate_up_swiglu": ["block_fp8_mixture_route_amd/csrc/token.hip",
                              "block_fp8_mixture_route_amd/csrc/device.h",
-                             "block_fp8_mixture_route_amd/csrc/router.h"],
+                             "block_fp8_mixture_route_amd/csrc/router.h",
+                             "block_fp8_mixture_route_amd/csrc/internal.h"],
 }
 
 
