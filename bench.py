@@ -910,6 +910,9 @@ def main():
         },
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": roofline,
+        # the whole layer against the same peak (roofline above: its dominant kernel alone)
+        "layer_roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(r["gbs"] / HBM_PEAK_GBS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
