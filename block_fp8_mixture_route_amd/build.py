@@ -27,6 +27,10 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # packed fp32 VALU forms are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the leading kernel arguments arrive in SGPRs with the dispatch (no
+    # scalar load of the argument segment before the first address is known;
+    # the compiler keeps a loading prologue for firmware that does not preload)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]
