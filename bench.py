@@ -354,8 +354,11 @@ def router_table(hip, stream, dev):
 def routed_table(hip, stream, dev):
     """The decode layers with their router, graph-timed over 8 instances
     (more weight bytes than the Infinity Cache holds): the router's launch
-    followed by the layer, against the layer with the router folded into its
-    first kernel, and the layer alone on given routing."""
+    followed by the layer, against the routed layer (the router folded into
+    the few-token gate/up kernel up to 4 tokens, its own launch from 8), the
+    routed layer with the router inside route preparation's workgroup on the
+    general path (16 to 64 tokens, BFP8MOE_FLAG_ROUTER_IN_ROUTE_PREP), and
+    the layer alone on given routing."""
     import torch
 
     import block_fp8_mixture_route_amd as bfp8
@@ -364,10 +367,11 @@ def routed_table(hip, stream, dev):
     L_ = bfp8.lib()
     P = ctypes.c_void_p
     print()
-    print("| config | router + layer µs (2 calls) | routed layer µs (router folded) | layer alone µs |")
-    print("|---|---|---|---|")
+    print("| config | router + layer µs (2 calls) | routed layer µs | routed, router in route prep µs | "
+          "layer alone µs |")
+    print("|---|---|---|---|---|")
     out = {}
-    for M in (1, 2, 4, 8):
+    for M in (1, 2, 4, 8, 16, 32, 64):
         name = f"decode_m{M}"
         c = dataclasses.replace(synth.LAYER_CASES["decode_m1"], name=name, M=M)
         o = bfp8.opts()
@@ -396,20 +400,25 @@ def routed_table(hip, stream, dev):
             bfp8._lib.check(L_.moe_router_topk(P(x["lg"].data_ptr()), c.M, c.E, c.k, bfp8.SCORE_SOFTMAX, None, 1,
                                                1.0, P(x["ids"].data_ptr()), P(x["w"].data_ptr()), stream))
 
-        def routed(x):
+        o_rp = bfp8.opts(flags=bfp8.FLAG_ROUTER_IN_ROUTE_PREP)
+
+        def routed(x, ro=o):
             m = x["mw"]
             bfp8._lib.check(L_.fused_moe_block_fp8_routed(
                 P(x["hid"].data_ptr()), c.M, c.H, P(x["lg"].data_ptr()), None, bfp8.SCORE_SOFTMAX, 1, 1.0, 1, 1, c.k,
                 P(x["ids"].data_ptr()), P(x["w"].data_ptr()), P(m.w13.data_ptr()), P(m.w13_s.data_ptr()),
-                P(m.w2.data_ptr()), P(m.w2_s.data_ptr()), c.E, c.I, ctypes.byref(o), P(x["out"].data_ptr()),
+                P(m.w2.data_ptr()), P(m.w2_s.data_ptr()), c.E, c.I, ctypes.byref(ro), P(x["out"].data_ptr()),
                 P(x["ws"].data_ptr()), x["ws"].numel(), stream))
 
         reps = 40
         t2 = time_graph(hip, stream, lambda: [(router(x), layer(x)) for x in insts * 4], reps) * 1e3 / 32
         tf = time_graph(hip, stream, lambda: [routed(x) for x in insts * 4], reps) * 1e3 / 32
+        trp = (time_graph(hip, stream, lambda: [routed(x, o_rp) for x in insts * 4], reps) * 1e3 / 32
+               if M >= 16 else None)
         tl = time_graph(hip, stream, lambda: [layer(x) for x in insts * 4], reps) * 1e3 / 32
-        out[name] = {"router_plus_layer_us": t2, "routed_us": tf, "layer_us": tl}
-        print(f"| {name} | {t2:.2f} | {tf:.2f} | {tl:.2f} |", flush=True)
+        out[name] = {"router_plus_layer_us": t2, "routed_us": tf, "routed_in_route_prep_us": trp, "layer_us": tl}
+        rps = "—" if trp is None else f"{trp:.2f}"
+        print(f"| {name} | {t2:.2f} | {tf:.2f} | {rps} | {tl:.2f} |", flush=True)
         del insts
         torch.cuda.empty_cache()
     out["shared"] = shared_table(hip, stream, dev)

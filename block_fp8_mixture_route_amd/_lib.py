@@ -28,6 +28,7 @@ FLAG_ROUTE_MULTI_WG = 1 << 1
 FLAG_LAYER_GENERAL = 1 << 2
 FLAG_LAYER_DECODE = 1 << 3
 FLAG_LAYER_TOKEN = 1 << 4
+FLAG_ROUTER_IN_ROUTE_PREP = 1 << 5
 
 
 def FLAG_ONLY_STAGE(s):

@@ -574,11 +574,15 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
 namespace {
 
 // The layer for either scale type: w13_scale / w2_scale are fp32 (block and
-// channel scales) or E8M0 bytes (MXFP4), as o.weight_scale_mode says.
+// channel scales) or E8M0 bytes (MXFP4), as o.weight_scale_mode says.  With
+// `route` (general path, single-workgroup route preparation, the caller has
+// checked bfp8::route_prep_can_route), route preparation makes the routing
+// itself and writes it to topk_ids / topk_w, which the later stages read.
 bfp8moe_status_t layer_impl(const uint16_t* hidden, int64_t M, int32_t H, const int32_t* topk_ids,
                             const float* topk_w, int32_t k, const uint8_t* w13, const void* w13_scale_v,
                             const uint8_t* w2, const void* w2_scale_v, int32_t E, int32_t I, const bfp8moe_opts_t& o,
-                            uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+                            uint16_t* out, void* ws, size_t ws_bytes, void* stream,
+                            const bfp8::RouterArgs* route = nullptr) {
   const float* w13_scale = static_cast<const float*>(w13_scale_v);
   const float* w2_scale = static_cast<const float*>(w2_scale_v);
   {
@@ -644,7 +648,7 @@ bfp8moe_status_t layer_impl(const uint16_t* hidden, int64_t M, int32_t H, const 
   if (hook.run(st_i)) {
     const bfp8::QuantArgs qa{hidden, M, H, p.fmt, aq, as};
     e = bfp8::launch_route_prepare(topk_ids, p.R, layer_sel(p), p.block_m, sorted, eoff, bexp, bstart, p.max_blocks,
-                                   nb, p.route_single, rws, st, p.rq_fused ? &qa : nullptr);
+                                   nb, p.route_single, rws, st, p.rq_fused ? &qa : nullptr, route, k);
   }
   if (e != hipSuccess) return hip_status(e, "fused_moe_block_fp8: route prep");
   if (sq == 1) {
@@ -775,6 +779,20 @@ bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, i
   if (ws == nullptr || ws_bytes < p.total)
     return fail(BFP8MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, p.total);
   REQUIRE((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) == 0, "workspace must be 256-byte aligned");
+  REQUIRE(o.weight_scale_mode != BFP8MOE_WEIGHT_MXFP4, "MXFP4 weights (E8M0 scale bytes) take fused_moe_mxfp4");
+  if (o.flags & BFP8MOE_FLAG_ROUTER_IN_ROUTE_PREP) {
+    // the router inside route preparation's workgroup, one launch for both
+    if (p.mode != kModeGeneral || !p.route_single || !bfp8::route_prep_can_route(M, E, p.L, p.R))
+      return fail(BFP8MOE_ERR_UNSUPPORTED,
+                  "the router in route preparation needs the general path, one route-prep workgroup, M <= %lld, "
+                  "E <= %d and L <= %d (M=%lld E=%d L=%d)",
+                  (long long)bfp8::kRoutePrepRouterMaxM, bfp8::kFoldedRouterMaxE, bfp8::kRoutePrepRouterMaxL,
+                  (long long)M, E, p.L);
+    const bfp8::RouterArgs ra{router_logits, router_bias, topk_ids, topk_w, routed_scale, E, score_fn,
+                              renormalize != 0, n_group, topk_group};
+    return layer_impl(hidden, M, H, topk_ids, topk_w, k, w13, w13_scale, w2, w2_scale, E, I, o, out, ws, ws_bytes,
+                      stream, &ra);
+  }
   if (p.mode == kModeToken && E <= bfp8::kFoldedRouterMaxE && M <= bfp8::kFoldedRouterMaxM) {
     uint16_t* act = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.off_act);
     const bfp8::RouterArgs ra{router_logits, router_bias, topk_ids, topk_w, routed_scale, E, score_fn,

@@ -138,10 +138,20 @@ struct QuantArgs {
 bool route_prep_can_quant(bool single, int32_t L);
 int route_prep_num_segments(int64_t R);
 size_t route_prep_ws_bytes(int64_t R, int32_t L);
+// Route preparation can also make the routing itself: with `route`, the
+// single workgroup first ranks the R / k tokens' router logits (one wave per
+// token, as the router kernel), writes route->ids / route->w and sorts those
+// ids (`ids` is then not read).  Up to kRoutePrepRouterMaxM tokens,
+// kFoldedRouterMaxE experts and kRoutePrepRouterMaxL local experts, on the
+// single-workgroup path.
+constexpr int64_t kRoutePrepRouterMaxM = 64;
+constexpr int32_t kRoutePrepRouterMaxL = 512;
+bool route_prep_can_route(int64_t M, int32_t E, int32_t L, int64_t R);
 hipError_t launch_route_prepare(const int32_t* ids, int64_t R, const ExpertSel& sel, int32_t block_m,
                                 int32_t* sorted_routes, int32_t* expert_offsets, int32_t* block_expert,
                                 int32_t* block_start, int64_t max_blocks, int32_t* num_blocks, bool single,
-                                void* ws, hipStream_t stream, const QuantArgs* quant = nullptr);
+                                void* ws, hipStream_t stream, const QuantArgs* quant = nullptr,
+                                const RouterArgs* route = nullptr, int k = 0);
 
 // Grouped block-FP8 GEMM over compact blocks (general path).
 hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div, const uint8_t* B,

@@ -10,6 +10,10 @@
 // global to local ids (remote experts marked negative).
 // [P1 Modification, Active-expert block scheduling] blocks exist only for
 // experts with routes.
+// [P2 Changes: the fused single-group top-k router feeds the layer] for a few
+// tokens the single workgroup can rank the tokens itself first (one wave per
+// token, the router kernel's wave code), so that the router and route
+// preparation are one launch; the counting sort then reads the ids from LDS.
 //
 // Determinism and stability without atomics on positions: every segment of
 // routes is split into 16 contiguous wave sub-segments; each wave counts its
@@ -30,6 +34,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "router.h"
 
 namespace bfp8 {
 
@@ -132,12 +137,16 @@ __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __
 
 // Scan + scatter.  With n_seg == 1 and hist == nullptr this is the whole
 // single-workgroup route preparation.  Workgroup 0 also writes the offsets,
-// the blocks and the -1 fills.
+// the blocks and the -1 fills.  kRoute (single workgroup only): the routes'
+// expert ids are not read from `ids` but made here first from the router
+// logits of the R / k tokens (ra), written to ra.ids / ra.w for the kernels
+// after this one and kept in LDS for the sort.
+template <bool kRoute>
 __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t R, ExpertSel sel, int32_t block_m, int64_t seg_len,
     const int32_t* __restrict__ hist, int n_seg, int32_t* __restrict__ sorted_routes,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ block_expert, int32_t* __restrict__ block_start,
-    int64_t max_blocks, int32_t* __restrict__ num_blocks, QuantJob qj) {
+    int64_t max_blocks, int32_t* __restrict__ num_blocks, QuantJob qj, RouterArgs ra, int k) {
   if (quant_job(qj, n_seg)) return;
   const int32_t L = sel.L;
   extern __shared__ int lds[];
@@ -146,8 +155,43 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
   int* base = offs + L;                // [L] routes of this expert in earlier segments
   int* cnt = base + L;                 // [L] expert totals (kept)
   int* tmp = cnt + L;                  // [64] scan scratch
+  int* s_ids = tmp + 64;               // kRoute: [R] the routes' expert ids
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = blockIdx.x;
+
+  if constexpr (kRoute) {
+    // 0. the router: wave w ranks tokens w, w + 16, ... (all 64 lanes of a
+    //    wave take part in every round), lane j < k keeping winner j
+    float* s_key = reinterpret_cast<float*>(s_ids + R) + (size_t)wave * (64 + ra.E);  // grouped selection only
+    const int64_t M = R / k;
+    for (int64_t t = wave; t < M; t += kWaves) {
+      router::WaveRoute<kFoldedRouterMaxE / 64> rt;
+      rt.load(ra.logits + t * ra.E, ra.E, ra.score_fn, ra.bias, lane, ra.n_group, ra.topk_group, s_key);
+      int my_id = 0;
+      float my_logit = 0.0f;
+      for (int j = 0; j < k; j++) {
+        float lv;
+        const int e = rt.take(lane, lv);
+        if (lane == j) {
+          my_id = e;
+          my_logit = lv;
+        }
+      }
+      const float wt = rt.weight(my_logit, lane, ra.E, k, ra.score_fn, ra.renorm, ra.scale);
+      if (lane < k) {
+        ra.ids[t * k + lane] = my_id;
+        ra.w[t * k + lane] = wt;
+        s_ids[t * k + lane] = my_id;
+      }
+    }
+  }
+  // a route's expert id: made above (kRoute) or given
+  auto id_of = [&](int64_t r) -> int32_t {
+    if constexpr (kRoute)
+      return s_ids[r];
+    else
+      return ids[r];
+  };
 
   for (int i = tid; i < kWaves * L; i += kThreads) wh[i] = 0;
   __syncthreads();
@@ -161,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 
   // 1. wave histograms
   for (int64_t r = w0 + lane; r < w1; r += 64) {
-    const int e = local_of(sel, ids[r]);
+    const int e = local_of(sel, id_of(r));
     if (e >= 0) atomicAdd(&wh[wave * L + e], 1);
   }
   __syncthreads();
@@ -213,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t c0 = w0; c0 < w1; c0 += 64) {
     const int64_t r = c0 + lane;
-    int e = r < w1 ? local_of(sel, ids[r]) : -1;
+    int e = r < w1 ? local_of(sel, id_of(r)) : -1;
     uint64_t same = __ballot(e >= 0);
     for (int bit = 0; bit < nbits; bit++) {
       uint64_t m = __ballot(e >= 0 && ((e >> bit) & 1));
@@ -255,6 +299,12 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 
 size_t scatter_lds_bytes(int32_t L) { return sizeof(int) * ((size_t)(kWaves + 3) * L + 64); }
 
+// With the router folded in: the routes' ids, and each wave's group scores
+// and keys when the selection is grouped.
+size_t routed_lds_bytes(int32_t L, int64_t R, int E, bool grouped) {
+  return scatter_lds_bytes(L) + sizeof(int) * (size_t)R + (grouped ? sizeof(float) * (size_t)kWaves * (64 + E) : 0);
+}
+
 }  // namespace
 
 bool route_prep_single_fits(int64_t R, int32_t L) { return R <= kSingleMaxRoutes && L <= kMaxL; }
@@ -277,11 +327,19 @@ size_t route_prep_ws_bytes(int64_t R, int32_t L) {
 
 bool route_prep_can_quant(bool single, int32_t L) { return !single || L <= kQuantMaxL; }
 
+bool route_prep_can_route(int64_t M, int32_t E, int32_t L, int64_t R) {
+  return M >= 1 && M <= kRoutePrepRouterMaxM && E >= 1 && E <= kFoldedRouterMaxE && L <= kRoutePrepRouterMaxL &&
+         route_prep_single_fits(R, L);
+}
+
 hipError_t launch_route_prepare(const int32_t* ids, int64_t R, const ExpertSel& sel, int32_t block_m,
                                 int32_t* sorted_routes, int32_t* expert_offsets, int32_t* block_expert,
                                 int32_t* block_start, int64_t max_blocks, int32_t* num_blocks, bool single,
-                                void* ws, hipStream_t stream, const QuantArgs* quant) {
+                                void* ws, hipStream_t stream, const QuantArgs* quant, const RouterArgs* route,
+                                int k) {
   const int32_t L = sel.L;
+  if (route && (!single || k < 1 || R % k != 0 || !route_prep_can_route(R / k, route->E, L, R)))
+    return hipErrorInvalidValue;  // the caller checks
   QuantJob qj;
   if (quant && quant->rows > 0) {
     if (!route_prep_can_quant(single, L)) return hipErrorInvalidValue;  // the caller checks
@@ -296,15 +354,24 @@ hipError_t launch_route_prepare(const int32_t* ids, int64_t R, const ExpertSel& 
   // (gfx950 allows up to 160 KB); raise the function's limit once.
   static std::once_flag once;
   std::call_once(once, [] {
-    (void)hipFuncSetAttribute((const void*)route_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)route_scatter_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)scatter_lds_bytes(kMaxL));
+    (void)hipFuncSetAttribute((const void*)route_scatter_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)routed_lds_bytes(kRoutePrepRouterMaxL, kSingleMaxRoutes, kFoldedRouterMaxE, true));
     (void)hipGetLastError();
   });
+  if (route) {
+    const size_t lds = routed_lds_bytes(L, R, route->E, route->n_group > 1);
+    hipLaunchKernelGGL(route_scatter_kernel<true>, dim3(1 + nq), dim3(kThreads), lds, stream, ids, R, sel, block_m,
+                       R > 0 ? R : (int64_t)1, (const int32_t*)nullptr, 1, sorted_routes, expert_offsets,
+                       block_expert, block_start, max_blocks, num_blocks, qj, *route, k);
+    return hipGetLastError();
+  }
   const size_t lds = scatter_lds_bytes(L);
   if (single) {
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(1 + nq), dim3(kThreads), lds, stream, ids, R, sel, block_m,
+    hipLaunchKernelGGL(route_scatter_kernel<false>, dim3(1 + nq), dim3(kThreads), lds, stream, ids, R, sel, block_m,
                        R > 0 ? R : (int64_t)1, (const int32_t*)nullptr, 1, sorted_routes, expert_offsets,
-                       block_expert, block_start, max_blocks, num_blocks, qj);
+                       block_expert, block_start, max_blocks, num_blocks, qj, RouterArgs{}, 0);
     return hipGetLastError();
   }
   const int n_seg = route_prep_num_segments(R);
@@ -314,9 +381,9 @@ hipError_t launch_route_prepare(const int32_t* ids, int64_t R, const ExpertSel& 
                      sel, seg_len, hist, n_seg, qj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(n_seg), dim3(kThreads), lds, stream, ids, R, sel, block_m,
+  hipLaunchKernelGGL(route_scatter_kernel<false>, dim3(n_seg), dim3(kThreads), lds, stream, ids, R, sel, block_m,
                      seg_len, (const int32_t*)hist, n_seg, sorted_routes, expert_offsets, block_expert,
-                     block_start, max_blocks, num_blocks, QuantJob());
+                     block_start, max_blocks, num_blocks, QuantJob(), RouterArgs{}, 0);
   return hipGetLastError();
 }
 

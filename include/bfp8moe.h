@@ -85,6 +85,13 @@ enum {
     BFP8MOE_FLAG_LAYER_GENERAL = 1u << 2,    /* fused layer: staged general path */
     BFP8MOE_FLAG_LAYER_DECODE = 1u << 3,     /* fused layer: small-batch two-kernel path */
     BFP8MOE_FLAG_LAYER_TOKEN = 1u << 4,      /* fused layer: few-token two-kernel path */
+    /* fused_moe_block_fp8_routed on the general path: the router runs inside
+     * route preparation's single workgroup, one wave per token, so router and
+     * route preparation are one launch [P2 Changes: the fused top-k router
+     * feeds the layer].  Up to 64 tokens, 256 experts, 512 local experts;
+     * otherwise the call fails with BFP8MOE_ERR_UNSUPPORTED.  Off by default:
+     * measured slower than the router's own launch at 16 to 64 tokens. */
+    BFP8MOE_FLAG_ROUTER_IN_ROUTE_PREP = 1u << 5,
     BFP8MOE_FLAG_STAGE_SHIFT = 8             /* flags bits 8..11, see BFP8MOE_FLAG_ONLY_STAGE */
 };
 /* Test and profiling switch of the fused layer: launch only stage s (0-based,

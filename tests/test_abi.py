@@ -183,6 +183,12 @@ def test_host_validation_rejects_bad_calls():
         st, msg = _status(L.fused_moe_block_fp8_routed, fake, 1, 7168, fake, None, sf, 1, 1.0, ng, tg, 8, fake, fake,
                           fake, fake, fake, fake, 256, 256, ctypes.byref(o), fake, fake, 1 << 30, None)
         assert st == 1 and what in msg, msg
+    # the router in route preparation: general path, one route-prep workgroup, at most 64 tokens
+    for M, flags in ((1, 0), (65, bfp8.FLAG_LAYER_GENERAL), (16, bfp8.FLAG_LAYER_GENERAL | bfp8.FLAG_ROUTE_MULTI_WG)):
+        o = bfp8.opts(flags=flags | bfp8.FLAG_ROUTER_IN_ROUTE_PREP)
+        st, msg = _status(L.fused_moe_block_fp8_routed, fake, M, 7168, fake, None, 0, 1, 1.0, 1, 1, 8, fake, fake,
+                          fake, fake, fake, fake, 256, 256, ctypes.byref(o), fake, fake, 1 << 30, None)
+        assert st == 2 and "router in route preparation" in msg, msg
     st, msg = _status(L.moe_router_noaux_tc, fake, 4, 256, 8, 6, 2, None, 1, 1.0, fake, fake, None)
     assert st == 1 and "n_group" in msg
     st, msg = _status(L.moe_router_noaux_tc, fake, 4, 256, 80, 8, 2, None, 1, 1.0, fake, fake, None)

@@ -182,3 +182,84 @@ def test_routed_layer_expert_slice_and_options(M):
     assert (bf16_np(out)[1] == 0).all()
     assert_layer_elementwise(out, hidden, torch.from_numpy(rid), torch.from_numpy(rw), W, bfp8.SCALE_UE8M0, 7.0,
                              E=E, expert_offset=off, L=L, what=f"routed slice M={M}", o=o)
+
+
+# routed layer on the general path with FLAG_ROUTER_IN_ROUTE_PREP: route
+# preparation ranks the tokens itself (router and route preparation one
+# launch).  ids as the oracle's router and weights within 1 ulp, ids and
+# weights bit for bit the router kernel's, and the output bit for bit the
+# router kernel followed by the layer.  (M, E, k, H, I, score_fn, n_group,
+# topk_group, local experts); 65 tokens are past the fold: the flag is refused
+# and, without it, the router takes its own launch.
+GENERAL_ROUTED = [
+    (16, 256, 8, 2048, 256, bfp8.SCORE_SOFTMAX, 1, 1, None),
+    (32, 256, 8, 1024, 256, bfp8.SCORE_SIGMOID, 1, 1, None),
+    (64, 256, 8, 1024, 256, bfp8.SCORE_SIGMOID, 8, 4, None),
+    (64, 128, 6, 512, 256, bfp8.SCORE_SOFTMAX, 1, 1, "slice"),
+    (48, 256, 8, 1024, 256, bfp8.SCORE_SIGMOID, 8, 4, "map"),
+    (40, 256, 8, 1024, 256, bfp8.SCORE_SOFTMAX, 1, 1, "w8a8"),
+    (1, 64, 4, 256, 128, bfp8.SCORE_SOFTMAX, 1, 1, None),
+    (65, 256, 8, 1024, 256, bfp8.SCORE_SOFTMAX, 1, 1, None),
+]
+
+
+@pytest.mark.parametrize("M,E,k,H,I,score_fn,n_group,topk_group,local", GENERAL_ROUTED)
+def test_routed_layer_general_path(M, E, k, H, I, score_fn, n_group, topk_group, local):
+    print_case("routed general", M, E, k, H, I, score_fn, n_group, topk_group, local)
+    from tests.gpu_util import bf16_np
+    key = ("routed_gen", M, E)
+    lg = synth.router_logits(M, E, *key, bf16_valued=True, std=2.0)
+    bias = synth.router_bias(E, *key, std=0.1) if score_fn == bfp8.SCORE_SIGMOID else None
+    scale = 2.5 if score_fn == bfp8.SCORE_SIGMOID else 1.0
+    if n_group > 1:
+        rid, rw = O.router_noaux_tc(lg, k, n_group, topk_group, bias, True, scale)
+    else:
+        rid, rw = O.router_topk(lg, k, score_fn, bias, True, scale)
+    fold = M <= 64
+    flags = bfp8.FLAG_LAYER_GENERAL | (bfp8.FLAG_ROUTER_IN_ROUTE_PREP if fold else 0)
+    if local == "slice":
+        off, L = 32, 64
+        W = synth.moe_weights(L, H, I, *key, device=dev())
+        o = bfp8.opts(flags=flags, expert_offset=off, local_num_experts=L)
+    elif local == "map":
+        L = E // 4
+        m = np.full(E, -1, np.int32)
+        m[1::4] = np.arange(L, dtype=np.int32)[::-1]  # every fourth expert is local, in reverse order
+        W = synth.moe_weights(L, H, I, *key, device=dev())
+        o = bfp8.opts(flags=flags, local_num_experts=L, expert_map=torch.from_numpy(m).to(dev()))
+    elif local == "w8a8":
+        g = torch.Generator(device=dev()).manual_seed(synth.seed_of(*key))
+        c13 = torch.randint(0, 0x7F, (E, 2 * I, H), generator=g, device=dev(), dtype=torch.uint8)
+        c2 = torch.randint(0, 0x7F, (E, H, I), generator=g, device=dev(), dtype=torch.uint8)
+        s13 = torch.rand(E, 2 * I, generator=g, device=dev()) * 1e-3 + 1e-4
+        s2 = torch.rand(E, H, generator=g, device=dev()) * 1e-3 + 1e-4
+        W = synth.MoEWeights(c13, s13, c2, s2)
+        o = bfp8.opts(flags=flags, weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL)
+    else:
+        W = synth.moe_weights(E, H, I, *key, experts=np.unique(rid).tolist(), device=dev())
+        o = bfp8.opts(flags=flags)
+    assert bfp8.fused_moe_stages(M, H, k, E, I, o)[0].startswith("route_prepare")
+    hidden = synth.hidden_states(M, H, *key).to(dev())
+    if not fold:
+        o_fold = bfp8.opts(flags=flags | bfp8.FLAG_ROUTER_IN_ROUTE_PREP)
+        with pytest.raises(bfp8.BFP8MoEError) as ei:
+            bfp8.fused_moe_block_fp8_routed(hidden, lg.to(dev()), k, W.w13, W.w13_s, W.w2, W.w2_s, score_fn, None,
+                                            True, scale, o=o_fold)
+        assert ei.value.status == 2
+    out, ids, w = bfp8.fused_moe_block_fp8_routed(hidden, lg.to(dev()), k, W.w13, W.w13_s, W.w2, W.w2_s, score_fn,
+                                                  None if bias is None else bias.to(dev()), True, scale, o=o,
+                                                  n_group=n_group, topk_group=topk_group)
+    # the router kernel, then the layer
+    if n_group > 1:
+        ids2, w2 = bfp8.router_noaux_tc(lg.to(dev()), k, n_group, topk_group, bias.to(dev()), True, scale)
+    else:
+        ids2, w2 = bfp8.router_topk(lg.to(dev()), k, score_fn, None if bias is None else bias.to(dev()), True,
+                                    scale)
+    out2 = bfp8.fused_moe_block_fp8(hidden, ids2, w2, W.w13, W.w13_s, W.w2, W.w2_s, E=E, o=o)
+    torch.cuda.synchronize()
+    assert (ids.cpu().numpy() == rid).all()
+    assert ulps(w.cpu().numpy(), rw).max() <= 1.0
+    assert torch.equal(ids, ids2) and torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    nd = int((bf16_np(out) != bf16_np(out2)).sum())
+    print(f"  {nd} of {out.numel()} outputs differ from the two-call layer", flush=True)
+    assert nd == 0
