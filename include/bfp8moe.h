@@ -477,8 +477,10 @@ bfp8moe_status_t fused_moe_mxfp4(const uint16_t* hidden, int64_t M, int32_t H, c
  *  Reviewed changes: route_noaux_tc.py]
  * On the few-token path with E <= 256 and at most 4 tokens the router is
  * folded into the layer's first kernel (one launch fewer): each gate/up
- * workgroup ranks its token's logits itself.  Elsewhere the router runs as its
- * own launch first.  Takes
+ * workgroup ranks its token's logits itself.  With
+ * BFP8MOE_FLAG_ROUTER_IN_ROUTE_PREP in opts->flags the general path does the
+ * same inside route preparation's launch (up to 64 tokens).  Elsewhere the
+ * router runs as its own launch first.  Takes
  * the workspace of fused_moe_block_fp8_workspace_size for the same sizes and
  * options; opts must not set stage events or a stage selection. */
 bfp8moe_status_t fused_moe_block_fp8_routed(const uint16_t* hidden, int64_t M, int32_t H, const float* router_logits,
