@@ -560,6 +560,78 @@ def variants_table(hip, stream, dev):
     return res
 
 
+def variants_decode_table(hip, stream, dev):
+    """The decode layer (E=256, top-k 8, H=7168, I=256) at 1 and 4 tokens with
+    each weight format: block FP8, W8A8 (random E4M3 codes, per-channel
+    scales, dynamic per-token activation scales) and MXFP4 (random E2M1
+    codes, E8M0 scales per 32).  One set of 256 experts per format; instance
+    i routes to experts disjoint from its neighbours' (8 M consecutive ones),
+    and the rotation of instances reads every expert once, more bytes than the
+    Infinity Cache holds.  Graph-timed; compulsory bytes as variants_table."""
+    import torch
+
+    import block_fp8_mixture_route_amd as bfp8
+    from block_fp8_mixture_route_amd import synth
+
+    E, k, H, I = 256, 8, 7168, 256
+    g = torch.Generator(device=dev).manual_seed(synth.seed_of("variants_decode"))
+
+    def e4m3(shape):
+        t = torch.empty(shape, dtype=torch.uint8, device=dev)
+        for e in range(shape[0]):
+            mag = torch.randint(0, 0x7F, shape[1:], generator=g, device=dev, dtype=torch.uint8)
+            t[e].copy_(mag | (torch.randint(0, 2, shape[1:], generator=g, device=dev, dtype=torch.uint8) << 7))
+        return t
+
+    W = synth.moe_weights(E, H, I, "variants_decode", device=dev)
+    C = synth.MoEWeights(e4m3((E, 2 * I, H)), torch.rand(E, 2 * I, generator=g, device=dev) * 1e-3 + 1e-4,
+                         e4m3((E, H, I)), torch.rand(E, H, generator=g, device=dev) * 1e-3 + 1e-4)
+    MX = synth.mxfp4_weights(E, H, I, "variants_decode", device=dev)
+    print()
+    print("| tokens | format | path | µs / layer | compulsory MB | GB/s | HBM roofline µs | fraction |")
+    print("|---|---|---|---|---|---|---|---|")
+    res = {}
+    ext = torch.cuda.ExternalStream(stream.value, device=dev)
+    for M in (1, 4):
+        n_inst = E // (M * k)
+        insts = []
+        for i in range(n_inst):
+            ids = (torch.arange(M * k, dtype=torch.int32, device=dev) + i * M * k).reshape(M, k) % E
+            w = torch.rand(M, k, generator=g, device=dev) + 0.1
+            insts.append((synth.hidden_states(M, H, "variants_decode", M, i, device=dev), ids.contiguous(),
+                          (w / w.sum(dim=1, keepdim=True)).contiguous(),
+                          torch.empty(M, H, dtype=torch.bfloat16, device=dev)))
+        d = M * k
+        io = M * H * 2 * 2 + M * k * 8
+        forms = {
+            "block FP8": (bfp8.opts(), d * (3 * I * H + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128))),
+                          lambda x, o, ws: bfp8.fused_moe_block_fp8(x[0], x[1], x[2], W.w13, W.w13_s, W.w2, W.w2_s,
+                                                                    E=E, out=x[3], ws=ws, o=o)),
+            "W8A8": (bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL), d * (3 * I * H + 4 * (2 * I + H)),
+                     lambda x, o, ws: bfp8.fused_moe_block_fp8(x[0], x[1], x[2], C.w13, C.w13_s, C.w2, C.w2_s, E=E,
+                                                               out=x[3], ws=ws, o=o)),
+            "MXFP4": (bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4), d * (3 * I * H // 2 + 3 * I * H // 32),
+                      lambda x, o, ws: bfp8.fused_moe_mxfp4(x[0], x[1], x[2], MX.w13, MX.w13_s, MX.w2, MX.w2_s, E=E,
+                                                            out=x[3], ws=ws, o=o)),
+        }
+        res[M] = {}
+        for f, (o, wbytes, fn) in forms.items():
+            ws = torch.empty(max(bfp8.fused_moe_workspace_size(M, H, k, E, I, o), 1), dtype=torch.uint8, device=dev)
+            path = bfp8.fused_moe_stages(M, H, k, E, I, o)[0]
+            with torch.cuda.stream(ext):  # the bindings launch on torch's current stream: the timed one
+                for x in insts:
+                    fn(x, o, ws)
+                hip.sync(stream)
+                us = time_graph(hip, stream, lambda: [fn(x, o, ws) for x in insts], 20) * 1e3 / n_inst
+            nbytes = wbytes + io
+            roof = nbytes / 8e12 * 1e6
+            res[M][f] = {"us": us, "bytes": nbytes, "roofline_us": roof, "first_stage": path}
+            print(f"| {M} | {f} | {path} | {us:.2f} | {nbytes / 1e6:.1f} | {nbytes / (us * 1e3):.0f} | {roof:.2f} | "
+                  f"{roof / us:.3f} |", flush=True)
+            del ws
+    return res
+
+
 def phase_table(hip, stream, dev, steps):
     """Where the decode layer's time goes.  The M=1, E=256, top-k 8, I=256
     layer at hidden widths 1024..7168: each of its two kernels alone and the
@@ -826,6 +898,8 @@ def main():
     ap.add_argument("--block-m", type=int, default=0, help="routes per compact block of the general path (0 = auto)")
     ap.add_argument("--floor", action="store_true", help="only the graph launch floor of one kernel")
     ap.add_argument("--router", action="store_true", help="only the router timing table")
+    ap.add_argument("--variants-decode", action="store_true",
+                    help="only the decode layer (1 and 4 tokens) with block-FP8, W8A8 and MXFP4 weights")
     ap.add_argument("--phases", action="store_true",
                     help="only the decode layer's phase table: each kernel alone and the layer at five hidden widths, "
                          "fixed cost and streaming rate per kernel fitted, the H=7168 layer split into them")
@@ -859,6 +933,9 @@ def main():
     if args.router:
         router_table(hip, stream, dev)
         routed_table(hip, stream, dev)
+        return
+    if args.variants_decode:
+        variants_decode_table(hip, stream, dev)
         return
     if args.phases:
         phase_table(hip, stream, dev, args.steps)
