@@ -588,8 +588,9 @@ def variants_decode_table(hip, stream, dev):
                          e4m3((E, H, I)), torch.rand(E, H, generator=g, device=dev) * 1e-3 + 1e-4)
     MX = synth.mxfp4_weights(E, H, I, "variants_decode", device=dev)
     print()
-    print("| tokens | format | path | µs / layer | compulsory MB | GB/s | HBM roofline µs | fraction |")
-    print("|---|---|---|---|---|---|---|---|")
+    print("| tokens | format | path | µs / layer | compulsory MB | GB/s | HBM roofline µs | fraction | "
+          "stages µs (each alone) |")
+    print("|---|---|---|---|---|---|---|---|---|")
     res = {}
     ext = torch.cuda.ExternalStream(stream.value, device=dev)
     for M in (1, 4):
@@ -623,11 +624,18 @@ def variants_decode_table(hip, stream, dev):
                     fn(x, o, ws)
                 hip.sync(stream)
                 us = time_graph(hip, stream, lambda: [fn(x, o, ws) for x in insts], 20) * 1e3 / n_inst
+                # each stage alone (BFP8MOE_FLAG_ONLY_STAGE), after the whole calls above
+                stages = bfp8.fused_moe_stages(M, H, k, E, I, o)
+                st_us = {}
+                for si, sn in enumerate(stages):
+                    os_ = bfp8.opts(weight_scale_mode=o.weight_scale_mode, flags=bfp8.FLAG_ONLY_STAGE(si))
+                    st_us[sn] = time_graph(hip, stream, lambda: [fn(x, os_, ws) for x in insts], 20) * 1e3 / n_inst
             nbytes = wbytes + io
             roof = nbytes / 8e12 * 1e6
-            res[M][f] = {"us": us, "bytes": nbytes, "roofline_us": roof, "first_stage": path}
+            res[M][f] = {"us": us, "bytes": nbytes, "roofline_us": roof, "first_stage": path, "stage_us": st_us}
+            stx = ", ".join(f"{a} {b:.2f}" for a, b in st_us.items())
             print(f"| {M} | {f} | {path} | {us:.2f} | {nbytes / 1e6:.1f} | {nbytes / (us * 1e3):.0f} | {roof:.2f} | "
-                  f"{roof / us:.3f} |", flush=True)
+                  f"{roof / us:.3f} | {stx} |", flush=True)
             del ws
     return res
 

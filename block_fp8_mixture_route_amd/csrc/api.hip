@@ -73,6 +73,7 @@ const char* const kChannelStages[] = {"route_prepare", "quant_fp8_rows", "gate_u
                                       "silu_and_mul_quant_rows", "down_gemm_channel", "moe_reduce"};
 const char* const kDecodeStages[] = {"decode_gate_up_swiglu", "decode_down_reduce"};
 const char* const kTokenStages[] = {"token_gate_up_swiglu", "token_down_reduce"};
+const char* const kTokenMxfp4Stages[] = {"token_gate_up_swiglu_mxfp4", "token_down_reduce_mxfp4"};
 enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
 
 // The few-token path is the default up to this many tokens: it reads one
@@ -112,9 +113,9 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.mxfp4 = o.weight_scale_mode == BFP8MOE_WEIGHT_MXFP4;
   p.a1_static = o.act_static_scale;
   p.a2_static = o.inter_static_scale;
-  const bool block = !p.channel && !p.mxfp4;  // the few-token and small-batch paths take block scales only
+  const bool block = !p.channel && !p.mxfp4;  // the small-batch path takes block scales only
   const bool fits = block && bfp8::decode_path_fits(M, H, k, I);
-  const bool token_fits = block && bfp8::token_path_fits(M, H, k, I);
+  const bool token_fits = !p.channel && bfp8::token_path_fits(M, H, k, I, p.mxfp4);
   if (o.flags & BFP8MOE_FLAG_LAYER_GENERAL)
     p.mode = kModeGeneral;
   else if (o.flags & BFP8MOE_FLAG_LAYER_DECODE)
@@ -514,8 +515,8 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
   if (o.weight_scale_mode == BFP8MOE_WEIGHT_MXFP4) {
     if (H % 256 != 0 || I % 256 != 0)
       return fail(BFP8MOE_ERR_UNSUPPORTED, "MXFP4 weights take H and I in multiples of 256 (H=%d I=%d)", H, I);
-    if (o.flags & (BFP8MOE_FLAG_LAYER_DECODE | BFP8MOE_FLAG_LAYER_TOKEN))
-      return fail(BFP8MOE_ERR_UNSUPPORTED, "MXFP4 weights run on the general path only");
+    if (o.flags & BFP8MOE_FLAG_LAYER_DECODE)
+      return fail(BFP8MOE_ERR_UNSUPPORTED, "MXFP4 weights run on the general and few-token paths");
     REQUIRE(o.act_static_scale == 0 && o.inter_static_scale == 0, "static scales belong to the W8A8 variant");
   }
   if ((o.flags & BFP8MOE_FLAG_LAYER_DECODE) && M > 0 && !bfp8::decode_path_fits(M, H, k, I))
@@ -523,10 +524,11 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
                 "small-batch path forced but M=%lld k=%d H=%d I=%d exceed its limits (M<=8, k<=8, H<=8192, "
                 "I<=512)",
                 (long long)M, k, H, I);
-  if ((o.flags & BFP8MOE_FLAG_LAYER_TOKEN) && M > 0 && !bfp8::token_path_fits(M, H, k, I))
+  if ((o.flags & BFP8MOE_FLAG_LAYER_TOKEN) && M > 0 &&
+      !bfp8::token_path_fits(M, H, k, I, o.weight_scale_mode == BFP8MOE_WEIGHT_MXFP4))
     return fail(BFP8MOE_ERR_UNSUPPORTED,
                 "few-token path forced but M=%lld k=%d H=%d I=%d do not fit it (M<=32, k<=16, H<=8192, "
-                "I in {128, 256, 512})",
+                "I in {128, 256, 512}; MXFP4: I in {256, 512})",
                 (long long)M, k, H, I);
   {
     const uint32_t paths = o.flags & (BFP8MOE_FLAG_LAYER_GENERAL | BFP8MOE_FLAG_LAYER_DECODE | BFP8MOE_FLAG_LAYER_TOKEN);
@@ -547,7 +549,7 @@ int32_t fused_moe_block_fp8_stages(int64_t M, int32_t H, int32_t k, int32_t E, i
   if (check_layer_shape(M, H, k, E, I, o) != BFP8MOE_OK) return -1;
   LayerPlan p;
   plan_layer(p, M, H, k, E, I, o);
-  const char* const* list = p.mode == kModeToken    ? kTokenStages
+  const char* const* list = p.mode == kModeToken    ? (p.mxfp4 ? kTokenMxfp4Stages : kTokenStages)
                             : p.mode == kModeDecode ? kDecodeStages
                             : p.channel             ? kChannelStages
                             : p.mxfp4               ? (p.rq_fused ? kMxfp4FusedStages : kMxfp4Stages)
@@ -616,8 +618,9 @@ bfp8moe_status_t layer_impl(const uint16_t* hidden, int64_t M, int32_t H, const 
   hook.only = only;
   if (p.mode == kModeToken) {
     uint16_t* act = reinterpret_cast<uint16_t*>(base + p.off_act);
-    return hip_status(bfp8::launch_token_layer(hidden, M, H, topk_ids, topk_w, k, layer_sel(p), w13, w13_scale,
-                                               w2, w2_scale, I, p.fmt, p.clamp, act, out, st, &hook),
+    return hip_status(bfp8::launch_token_layer(hidden, M, H, topk_ids, topk_w, k, layer_sel(p), w13, w13_scale_v,
+                                               w2, w2_scale_v, I, p.fmt, p.clamp, act, out, st, &hook, nullptr,
+                                               p.mxfp4),
                       "fused_moe_block_fp8 (few tokens)");
   }
   if (p.mode == kModeDecode) {

@@ -68,7 +68,9 @@ constexpr int kMaxK = 16;  // routes per token; the down kernel is built for 8 a
 constexpr int kMaxTokens = 32;  // tokens per call on this path
 constexpr int kMaxH = 8192;
 constexpr int kUnitsPerWave = 4;                            // 1 KB W2 units per down wave
+constexpr int kMxUnitsPerWave = 2;  // the same with MXFP4 rows (a unit holds twice the elements)
 constexpr int kMaxUnits = kDownWaves * kUnitsPerWave;       // per down workgroup
+constexpr int kMxMaxUnits = kDownWaves * kMxUnitsPerWave;
 constexpr int kMaxDownRows = 64;
 constexpr int kDownTarget = 256;  // down workgroups aimed at (one per compute unit of MI355X)
 constexpr unsigned kSpinLimit = 1u << 20;  // bound of the LDS waits (about 0.03 s)
@@ -123,13 +125,30 @@ __device__ __forceinline__ void quant_store8(const float (&f)[8], float sc, h2* 
   dst[0] = a; dst[1] = b; dst[2] = c; dst[3] = d;
 }
 
+// The gate/up kernel's hidden row in LDS: FP16 pair i (elements 2 i, 2 i + 1)
+// is stored at act_swz(i).  The 16-byte units (4 pairs) of each run of 16 are
+// permuted by XOR with the run's index, so that the column waves' reads (lane
+// l reading the 8 or 16 pairs of its 16 or 32 consecutive elements) spread a
+// 16-lane pass over all banks instead of a quarter or a sixteenth of them.
+__device__ __forceinline__ int act_swz(int i) { return i ^ (((i >> 6) & 15) << 2); }
+
+// Four FP16 pairs (one 16-byte unit) of the swizzled hidden row from pair i
+// (a multiple of 4).
+__device__ __forceinline__ void act_unit(const h2* row, int i, h2 (&a)[4]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(row + act_swz(i));
+  a[0] = __builtin_bit_cast(h2, v.x);
+  a[1] = __builtin_bit_cast(h2, v.y);
+  a[2] = __builtin_bit_cast(h2, v.z);
+  a[3] = __builtin_bit_cast(h2, v.w);
+}
+
 // sum_i dec(w_i) * a_i over 16 E4M3 weights (one 16-byte load) and 16 E4M3
-// activations held as FP16 pairs at p (LDS, 16-byte aligned).  Weight bytes
-// are widened to FP16 pairs (exact), and each v_dot2 product of two E4M3
-// values is exact in FP32; only the FP32 additions round.  Two chains.
-__device__ __forceinline__ float dot16(const uint4& w, const h2* p) {
-  const h2* q = p;
-  const h2 a0 = q[0], a1 = q[1], a2 = q[2], a3 = q[3], a4 = q[4], a5 = q[5], a6 = q[6], a7 = q[7];
+// activations held as FP16 pairs in LDS: at p (16-byte aligned, contiguous),
+// or at pairs i .. i + 7 of the swizzled hidden row (dot16_row).  Weight
+// bytes are widened to FP16 pairs (exact), and each v_dot2 product of two
+// E4M3 values is exact in FP32; only the FP32 additions round.  Two chains.
+__device__ __forceinline__ float dot16_pairs(const uint4& w, h2 a0, h2 a1, h2 a2, h2 a3, h2 a4, h2 a5, h2 a6,
+                                             h2 a7) {
   float s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.x, 1.0f, false), a0, 0.0f, false);
   float s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.x, 1.0f, true), a1, 0.0f, false);
   s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.y, 1.0f, false), a2, s0, false);
@@ -139,6 +158,55 @@ __device__ __forceinline__ float dot16(const uint4& w, const h2* p) {
   s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.w, 1.0f, false), a6, s0, false);
   s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.w, 1.0f, true), a7, s1, false);
   return s0 + s1;
+}
+__device__ __forceinline__ float dot16(const uint4& w, const h2* q) {
+  return dot16_pairs(w, q[0], q[1], q[2], q[3], q[4], q[5], q[6], q[7]);
+}
+__device__ __forceinline__ float dot16_row(const uint4& w, const h2* row, int i) {
+  h2 a[4], b[4];
+  act_unit(row, i, a);
+  act_unit(row, i + 4, b);
+  return dot16_pairs(w, a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
+}
+
+// sum_i dec(w_i) * a_i over 32 E2M1 weights (one 16-byte load, two to a
+// byte, the even element in the low nibble) and 32 E4M3 activations held as
+// FP16 pairs in LDS: at p (16-byte aligned, contiguous), or at pairs i .. i +
+// 15 of the swizzled hidden row (dot32_fp4_row).  Each weight byte widens to
+// an FP16 pair (exact, unit scale), each v_dot2 product is exact in FP32; only
+// the FP32 additions round.  Two chains.
+__device__ __forceinline__ void dot32_fp4_unit(uint32_t wd, const h2 (&a)[4], float& s0, float& s1) {
+  s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 0), a[0], s0, false);
+  s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 1), a[1], s1, false);
+  s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 2), a[2], s0, false);
+  s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 3), a[3], s1, false);
+}
+__device__ __forceinline__ float dot32_fp4(const uint4& w, const h2* p) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    const h2 a[4] = {p[4 * d], p[4 * d + 1], p[4 * d + 2], p[4 * d + 3]};
+    dot32_fp4_unit(wd[d], a, s0, s1);
+  }
+  return s0 + s1;
+}
+__device__ __forceinline__ float dot32_fp4_row(const uint4& w, const h2* row, int i) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  h2 a[4][4];
+#pragma unroll
+  for (int d = 0; d < 4; d++) act_unit(row, i + 4 * d, a[d]);
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; d++) dot32_fp4_unit(wd[d], a[d], s0, s1);
+  return s0 + s1;
+}
+
+// An E8M0 scale byte as an fp32 value, 2^(s - 127): exact for every byte
+// (2^-127 is an fp32 subnormal); 255 is NaN.
+__device__ __forceinline__ float e8m0_f32(uint32_t s) {
+  return s == 0u ? __builtin_bit_cast(float, 0x00400000u)
+                 : (s == 255u ? __builtin_nanf("") : __builtin_bit_cast(float, s << 23));
 }
 
 // Sum (or max) over aligned groups of N lanes (N = 8, 16, 32 or 64), the
@@ -190,12 +258,17 @@ __device__ __forceinline__ h2 quant2(float a, float b, float sc) {
 // barrier would also wait for every column wave to have issued its loads,
 // which the compute unit's memory queue holds back for microseconds, and no
 // wave could start its dot products before then.
-template <int RL, int I, bool kRoute>
+template <int RL, int I, bool kRoute, bool kMx>
 __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
     const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, int k, ExpertSel sel,
-    const uint8_t* __restrict__ w13, const float* __restrict__ w13_s, int fmt, float limit, int clamp,
+    const uint8_t* __restrict__ w13, const void* __restrict__ w13_sv, int fmt, float limit, int clamp,
     uint16_t* __restrict__ act, RouterArgs ra) {
   constexpr int kSlices = I / 8;
+  // kMx: MXFP4 rows (H / 2 bytes, E2M1) with an E8M0 scale byte per 32
+  // elements; else E4M3 rows (H bytes) with fp32 scales per 128 x 128 block
+  const float* __restrict__ w13_s = static_cast<const float*>(w13_sv);
+  const uint8_t* __restrict__ w13_mx = static_cast<const uint8_t*>(w13_sv);
+  const int RB = kMx ? H / 2 : H;  // bytes per weight row
   __shared__ __align__(16) h2 s_ah[kMaxH / 2];  // quantised hidden row (E4M3 values as FP16)
   __shared__ float s_as[kMaxH / 128];           // its group scales
   __shared__ float s_tab[2 * (kMaxH / 128)];    // W13 block scales: gate row block, then up row block
@@ -288,7 +361,8 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   }
   const int te = min(t, 2 * G - 1);
   const float tab =
-      ws13[((size_t)e * (2 * I / 128) + (te < G ? n0 / 128 : (I + n0) / 128)) * G + (te < G ? te : te - G)];
+      kMx ? 0.0f
+          : ws13[((size_t)e * (2 * I / 128) + (te < G ? n0 / 128 : (I + n0) / 128)) * G + (te < G ? te : te - G)];
   // every wave's small loads have left before any W13 load: the compute
   // unit returns data roughly in issue order, so they land first
   wg_sync();
@@ -302,10 +376,10 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
       float f[8];
       unpack8(hv[p], f);
       const float sc = group_scale(max_over_16(amax8(f)), fmt);
-      quant_store8(f, sc, s_ah + (hg * 128 + l16 * 8) / 2);
+      quant_store8(f, sc, s_ah + act_swz((hg * 128 + l16 * 8) / 2));
       if (l16 == 0) s_as[hg] = sc;
     }
-    s_tab[te] = tab;
+    if constexpr (!kMx) s_tab[te] = tab;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS stores are done
     if (lane == 0) __hip_atomic_fetch_add(&s_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (writer) write_routing();
@@ -316,15 +390,26 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   // loads, all issued before any data is used (every chunk but the last lies
   // inside the row; the last is clamped)
   uint4 wg[RL], wu[RL];
+  uint32_t sg[kMx ? RL : 1], su[kMx ? RL : 1];  // kMx: each load's E8M0 scale byte (one 32-element block)
   {
-    const uint8_t* gsrc = w13 + ((size_t)e * 2 * I + n0 + wave) * H;
-    const uint8_t* usrc = gsrc + (size_t)I * H;
-    const int last = min(1024 * (RL - 1) + 16 * lane, H - 16);
+    const uint8_t* gsrc = w13 + ((size_t)e * 2 * I + n0 + wave) * RB;
+    const uint8_t* usrc = gsrc + (size_t)I * RB;
+    const int last = min(1024 * (RL - 1) + 16 * lane, RB - 16);
 #pragma unroll
     for (int c = 0; c < RL; c++) {
       const int off = c < RL - 1 ? 1024 * c + 16 * lane : last;
       wg[c] = *reinterpret_cast<const uint4*>(gsrc + off);
       wu[c] = *reinterpret_cast<const uint4*>(usrc + off);
+    }
+    if constexpr (kMx) {
+      const uint8_t* gs = w13_mx + ((size_t)e * 2 * I + n0 + wave) * (H / 32);
+      const uint8_t* us = gs + (size_t)I * (H / 32);
+#pragma unroll
+      for (int c = 0; c < RL; c++) {
+        const int off = c < RL - 1 ? 1024 * c + 16 * lane : last;
+        sg[c] = gs[off / 16];
+        su[c] = us[off / 16];
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -343,10 +428,18 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   float ag = 0.0f, au = 0.0f;
 #pragma unroll
   for (int c = 0; c < RL; c++) {
-    const int kof = 1024 * c + 16 * lane;  // past H only in the last chunk: its terms are dropped
-    const float as = s_as[kof / 128];
-    float pg = dot16(wg[c], s_ah + kof / 2) * (as * s_tab[kof / 128]);
-    float pu = dot16(wu[c], s_ah + kof / 2) * (as * s_tab[G + kof / 128]);
+    const int kob = 1024 * c + 16 * lane;    // byte offset in the row: past it only in the last chunk,
+    const int kof = kMx ? 2 * kob : kob;     // whose terms are dropped; kof: first element
+    const int ka = min(kof, H - (kMx ? 32 : 16));  // in range for the dropped lanes' LDS reads
+    const float as = s_as[ka / 128];
+    float pg, pu;
+    if constexpr (kMx) {
+      pg = dot32_fp4_row(wg[c], s_ah, ka / 2) * (as * e8m0_f32(sg[c]));
+      pu = dot32_fp4_row(wu[c], s_ah, ka / 2) * (as * e8m0_f32(su[c]));
+    } else {
+      pg = dot16_row(wg[c], s_ah, ka / 2) * (as * s_tab[ka / 128]);
+      pu = dot16_row(wu[c], s_ah, ka / 2) * (as * s_tab[G + ka / 128]);
+    }
     if (c == RL - 1 && kof >= H) pg = pu = 0.0f;
     ag += pg;
     au += pu;
@@ -362,19 +455,26 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
 // ------------------------------------------------------------------ down + reduce
 //
 // Workgroup b: output rows d0 = DR b .. d0 + DR - 1 (DR a multiple of kRpl =
-// 1024 / I, at most 64).  Its W2 data is k x DL units of 1 KB (route j, piece
-// c: rows d0 + kRpl c .. + kRpl - 1); unit u = wave + 16 i is held by that
-// wave, lane l reading row kRpl c + l / kLpr, bytes 16 (l % kLpr) .. + 15.
+// 1024 / row bytes, at most 64).  Its W2 data is k x DL units of 1 KB (route
+// j, piece c: rows d0 + kRpl c .. + kRpl - 1); unit u = wave + 16 i (i below
+// 4, or 2 for MXFP4 rows, whose units hold twice the elements) is held by
+// that wave, lane l reading row kRpl c + l / kLpr, bytes 16 (l % kLpr) .. + 15.
 // Loads leave in the order their data is needed: the SwiGLU rows (they do not
 // depend on the routing), the W2 units, the W2 block scale of each lane's
 // row and group.  Route ids are read with uniform (scalar) loads by each wave
 // that needs them: no barrier stands between the start and the W2 loads.
-template <int I, int KMAX>
+template <int I, int KMAX, bool kMx>
 __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int k,
-    ExpertSel sel, const uint8_t* __restrict__ w2, const float* __restrict__ w2_s, int H, int fmt,
+    ExpertSel sel, const uint8_t* __restrict__ w2, const void* __restrict__ w2_sv, int H, int fmt,
     int DR, int DL, uint32_t dl_magic, uint16_t* __restrict__ out) {
-  constexpr int GI = I / 128, kRpl = 1024 / I, kLpr = I / 16;
+  // kMx: MXFP4 rows (I / 2 bytes, E2M1) with an E8M0 scale byte per 32
+  // elements; else E4M3 rows (I bytes) with fp32 scales per 128 x 128 block
+  constexpr int RBI = kMx ? I / 2 : I;  // bytes per W2 row
+  constexpr int GI = I / 128, kRpl = 1024 / RBI, kLpr = RBI / 16;
+  constexpr int kUpw = kMx ? kMxUnitsPerWave : kUnitsPerWave;  // W2 units per wave
+  const float* __restrict__ w2_s = static_cast<const float*>(w2_sv);
+  const uint8_t* __restrict__ w2_mx = static_cast<const uint8_t*>(w2_sv);
   constexpr int kActLoads = (KMAX * GI + kDownWaves - 1) / kDownWaves;  // SwiGLU groups per wave
   __shared__ __align__(16) h2 s_qh[KMAX][I / 2];  // quantised SwiGLU rows (E4M3 values as FP16)
   __shared__ float s_qs[KMAX][GI];                // their group scales
@@ -385,7 +485,8 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
   const int G = H / 128;
   const int d0 = blockIdx.x * DR, d_end = min(H, d0 + DR);
   const int n_units = k * DL;
-  const int kof = 16 * (lane % kLpr);
+  const int kob = 16 * (lane % kLpr);      // the lane's byte offset in its row
+  const int kof = kMx ? 2 * kob : kob;     // its first element
   // token blockIdx.y: its k routes, their SwiGLU rows, its output row
   ids += (size_t)blockIdx.y * k;
   topk_w += (size_t)blockIdx.y * k;
@@ -410,30 +511,33 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
   // 2. the wave's W2 units (past the last: repeats of it, cache hits).  A
   //    unit of a masked route reads a line of the SwiGLU buffer instead (in
   //    cache) and its result is dropped.
-  int eu[kUnitsPerWave];
+  int eu[kUpw];
 #pragma unroll
-  for (int i = 0; i < kUnitsPerWave; i++) {
+  for (int i = 0; i < kUpw; i++) {
     const int u = min(wave + kDownWaves * i, n_units - 1);
     eu[i] = __builtin_amdgcn_readlane(e_lane, (int)(((uint32_t)u * dl_magic) >> 16));
   }
-  uint4 wb[kUnitsPerWave];
+  uint4 wb[kUpw];
   const uint8_t* spare = reinterpret_cast<const uint8_t*>(act) + min(16 * lane, k * I * 2 - 16);
 #pragma unroll
-  for (int i = 0; i < kUnitsPerWave; i++) {
+  for (int i = 0; i < kUpw; i++) {
     const int u = min(wave + kDownWaves * i, n_units - 1);
     const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
     const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
-    const uint8_t* src = eu[i] >= 0 ? w2 + ((size_t)eu[i] * H + row) * I + kof : spare;
+    const uint8_t* src = eu[i] >= 0 ? w2 + ((size_t)eu[i] * H + row) * RBI + kob : spare;
     wb[i] = *reinterpret_cast<const uint4*>(src);
   }
   __builtin_amdgcn_sched_barrier(0);
-  float wsc[kUnitsPerWave];
+  float wsc[kUpw];
 #pragma unroll
-  for (int i = 0; i < kUnitsPerWave; i++) {
+  for (int i = 0; i < kUpw; i++) {
     const int u = min(wave + kDownWaves * i, n_units - 1);
     const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
     const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
-    wsc[i] = w2_s[((size_t)max(eu[i], 0) * G + row / 128) * GI + kof / 128];
+    if constexpr (kMx)
+      wsc[i] = e8m0_f32(w2_mx[((size_t)max(eu[i], 0) * H + row) * (I / 32) + kof / 32]);
+    else
+      wsc[i] = w2_s[((size_t)max(eu[i], 0) * G + row / 128) * GI + kof / 128];
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -454,17 +558,20 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
   // 4. down projection: each row's dot product with its route's quantised
   //    SwiGLU row, both block scales applied per group, reduced over the row's
   //    lanes; live rows go to s_y as BF16 values
-  float v[kUnitsPerWave];
+  float v[kUpw];
 #pragma unroll
-  for (int i = 0; i < kUnitsPerWave; i++) {
+  for (int i = 0; i < kUpw; i++) {
     const int u = min(wave + kDownWaves * i, n_units - 1);
     const int j = (int)(((uint32_t)u * dl_magic) >> 16);
-    v[i] = dot16(wb[i], &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * wsc[i]);
+    if constexpr (kMx)
+      v[i] = dot32_fp4(wb[i], &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * wsc[i]);
+    else
+      v[i] = dot16(wb[i], &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * wsc[i]);
   }
 #pragma unroll
-  for (int i = 0; i < kUnitsPerWave; i++) v[i] = group_sum<kLpr>(v[i]);
+  for (int i = 0; i < kUpw; i++) v[i] = group_sum<kLpr>(v[i]);
 #pragma unroll
-  for (int i = 0; i < kUnitsPerWave; i++) {
+  for (int i = 0; i < kUpw; i++) {
     const int u = wave + kDownWaves * i;
     const int j = (int)(((uint32_t)u * dl_magic) >> 16), c = u - j * DL;
     const int rl = c * kRpl + lane / kLpr;
@@ -497,13 +604,14 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
 
 }  // namespace
 
-// Rows per down workgroup: a multiple of the rows of one 1 KB load (1024 / I)
-// giving about 256 workgroups, with at most 64 units and 64 rows per
-// workgroup.
-int token_down_rows(int H, int I, int k) {
-  const int rpl = 1024 / I;
+// Rows per down workgroup: a multiple of the rows of one 1 KB load (1024 /
+// row bytes: I, or I / 2 for MXFP4 rows) giving about 256 workgroups, with at
+// most 64 units and 64 rows per workgroup.
+int token_down_rows(int H, int I, int k, bool mx) {
+  const int rpl = 1024 / (mx ? I / 2 : I);
   int dl = ((H + kDownTarget - 1) / kDownTarget + rpl - 1) / rpl;
-  dl = dl < kMaxUnits / k ? dl : kMaxUnits / k;
+  const int max_units = mx ? kMxMaxUnits : kMaxUnits;
+  dl = dl < max_units / k ? dl : max_units / k;
   dl = dl < kMaxDownRows / rpl ? dl : kMaxDownRows / rpl;
   return (dl > 1 ? dl : 1) * rpl;
 }
@@ -517,17 +625,19 @@ hipError_t read_wait_faults(unsigned* flags, bool clear) {
   return e;
 }
 
-bool token_path_fits(int64_t M, int H, int k, int I) {
+bool token_path_fits(int64_t M, int H, int k, int I, bool mx) {
   if (M < 1 || M > kMaxTokens || k < 1 || k > kMaxK || H < 128 || H > kMaxH || H % 128 != 0) return false;
+  if (mx) return H % 256 == 0 && (I == 256 || I == 512);  // whole 32-element blocks per 16-byte lane load
   return I == 128 || I == 256 || I == 512;
 }
 
 hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
-                              int k, const ExpertSel& sel, const uint8_t* w13, const float* w13_s,
-                              const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
+                              int k, const ExpertSel& sel, const uint8_t* w13, const void* w13_s,
+                              const uint8_t* w2, const void* w2_s, int I, int fmt, float limit, uint16_t* act,
                               uint16_t* out, hipStream_t stream, const LaunchHook* hook,
-                              const RouterArgs* route) {
-  if (!token_path_fits(M, H, k, I)) return hipErrorInvalidValue;  // the caller checks token_path_fits
+                              const RouterArgs* route, bool mx) {
+  if (!token_path_fits(M, H, k, I, mx)) return hipErrorInvalidValue;  // the caller checks token_path_fits
+  if (mx && route) return hipErrorInvalidValue;  // the routed layer takes block-FP8 weights
   if (route && (route->E < 1 || route->E > kFoldedRouterMaxE || k > route->E)) return hipErrorInvalidValue;
   const RouterArgs ra = route ? *route : RouterArgs{};
   if (route) {
@@ -535,9 +645,10 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
     topk_w = route->w;
   }
   const int clamp = __builtin_isfinite(limit) ? 1 : 0;
-  const int rl = (H + 1023) / 1024;
-  const int dr = token_down_rows(H, I, k);
-  const int dl = dr * I / 1024;
+  const int rb = mx ? H / 2 : H, rbi = mx ? I / 2 : I;  // bytes per W13 and W2 row
+  const int rl = (rb + 1023) / 1024;
+  const int dr = token_down_rows(H, I, k, mx);
+  const int dl = dr * rbi / 1024;
   // u / dl for u < 64 by multiply and shift (exact: the multiplier's rounding
   // error stays below one step for such u)
   const uint32_t dl_magic = (65536u + dl - 1) / dl;
@@ -548,11 +659,16 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
 #define BFP8_TOKEN_CASE(N, II)                                                                                  \
   case N:                                                                                                       \
     if (route)                                                                                                  \
-      hipLaunchKernelGGL((token_gate_up_kernel<N, II, true>), dim3(up_grid), dim3(kUpThreads), 0, stream,       \
-                         hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);                       \
+      hipLaunchKernelGGL((token_gate_up_kernel<N, II, true, false>), dim3(up_grid), dim3(kUpThreads), 0,       \
+                         stream, hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);               \
     else                                                                                                        \
-      hipLaunchKernelGGL((token_gate_up_kernel<N, II, false>), dim3(up_grid), dim3(kUpThreads), 0, stream,      \
-                         hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);                       \
+      hipLaunchKernelGGL((token_gate_up_kernel<N, II, false, false>), dim3(up_grid), dim3(kUpThreads), 0,      \
+                         stream, hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);               \
+    break;
+#define BFP8_TOKEN_MX_CASE(N, II)                                                                               \
+  case N:                                                                                                       \
+    hipLaunchKernelGGL((token_gate_up_kernel<N, II, false, true>), dim3(up_grid), dim3(kUpThreads), 0, stream,  \
+                       hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);                         \
     break;
 #define BFP8_TOKEN_RL(II)   \
   switch (rl) {             \
@@ -565,7 +681,20 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
     BFP8_TOKEN_CASE(7, II)  \
     BFP8_TOKEN_CASE(8, II)  \
   }
+#define BFP8_TOKEN_MX_RL(II) \
+  switch (rl) {               \
+    BFP8_TOKEN_MX_CASE(1, II) \
+    BFP8_TOKEN_MX_CASE(2, II) \
+    BFP8_TOKEN_MX_CASE(3, II) \
+    BFP8_TOKEN_MX_CASE(4, II) \
+  }
   if (!run0) {
+  } else if (mx) {
+    if (I == 256) {
+      BFP8_TOKEN_MX_RL(256)
+    } else {
+      BFP8_TOKEN_MX_RL(512)
+    }
   } else if (I == 128) {
     BFP8_TOKEN_RL(128)
   } else if (I == 256) {
@@ -573,27 +702,34 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
   } else {
     BFP8_TOKEN_RL(512)
   }
+#undef BFP8_TOKEN_MX_RL
 #undef BFP8_TOKEN_RL
+#undef BFP8_TOKEN_MX_CASE
 #undef BFP8_TOKEN_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hook) hook->before(1, stream);
-#define BFP8_TOKEN_DOWN(II)                                                                                      \
+#define BFP8_TOKEN_DOWN(II, MX)                                                                                  \
   do {                                                                                                           \
     if (k <= 8)                                                                                                  \
-      hipLaunchKernelGGL((token_down_kernel<II, 8>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0, stream, \
-                         act, ids, topk_w, k, sel, w2, w2_s, H, fmt, dr, dl, dl_magic, out);                     \
+      hipLaunchKernelGGL((token_down_kernel<II, 8, MX>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0,   \
+                         stream, act, ids, topk_w, k, sel, w2, w2_s, H, fmt, dr, dl, dl_magic, out);             \
     else                                                                                                         \
-      hipLaunchKernelGGL((token_down_kernel<II, 16>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0,      \
+      hipLaunchKernelGGL((token_down_kernel<II, 16, MX>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0,  \
                          stream, act, ids, topk_w, k, sel, w2, w2_s, H, fmt, dr, dl, dl_magic, out);             \
   } while (0)
   if (!run1) {
+  } else if (mx) {
+    if (I == 256)
+      BFP8_TOKEN_DOWN(256, true);
+    else
+      BFP8_TOKEN_DOWN(512, true);
   } else if (I == 128)
-    BFP8_TOKEN_DOWN(128);
+    BFP8_TOKEN_DOWN(128, false);
   else if (I == 256)
-    BFP8_TOKEN_DOWN(256);
+    BFP8_TOKEN_DOWN(256, false);
   else
-    BFP8_TOKEN_DOWN(512);
+    BFP8_TOKEN_DOWN(512, false);
 #undef BFP8_TOKEN_DOWN
   e = hipGetLastError();
   if (hook) hook->before(2, stream);

@@ -217,12 +217,21 @@ def test_mxfp4_layer_host_checks():
     o = bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4)
     assert bfp8.fused_moe_stages(64, 2048, 8, 32, 768, o) == [
         "route_prepare_quant", "gate_up_gemm_mxfp4", "silu_and_mul_quant", "down_gemm_mxfp4", "moe_reduce"]
-    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o)[1] == "gate_up_gemm_mxfp4"  # never the few-token path
-    for bad in (dict(), dict(flags=bfp8.FLAG_LAYER_TOKEN), dict(flags=bfp8.FLAG_LAYER_DECODE),
-                dict(act_static_scale=0.5)):
-        H, I = (256, 128) if not bad else (256, 256)
+    # a few tokens take the few-token kernels in their MXFP4 form, forced or by default
+    token = ["token_gate_up_swiglu_mxfp4", "token_down_reduce_mxfp4"]
+    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == token
+    assert bfp8.fused_moe_stages(20, 2048, 8, 64, 512, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4,
+                                                                  flags=bfp8.FLAG_LAYER_TOKEN)) == token
+    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4,
+                                                                  flags=bfp8.FLAG_LAYER_GENERAL))[1] == \
+        "gate_up_gemm_mxfp4"
+    # refused: I = 128 (not whole 256-wide chunks), the few-token path forced at I = 768 or 33 tokens,
+    # the small-batch path, static scales
+    for M, I, bad in ((4, 128, dict()), (4, 768, dict(flags=bfp8.FLAG_LAYER_TOKEN)),
+                      (33, 256, dict(flags=bfp8.FLAG_LAYER_TOKEN)), (4, 256, dict(flags=bfp8.FLAG_LAYER_DECODE)),
+                      (4, 256, dict(act_static_scale=0.5))):
         with pytest.raises(bfp8.BFP8MoEError):
-            bfp8.fused_moe_stages(4, H, 2, 8, I, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4, **bad))
+            bfp8.fused_moe_stages(M, 256, 2, 8, I, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4, **bad))
     # byte scales do not go through the fp32-scale entry point, nor block scales through fused_moe_mxfp4
     # (both fail in the host checks, before anything is launched)
     st = _lib.lib().fused_moe_block_fp8(None, 0, 256, None, None, 2, None, None, None, None, 8, 256,

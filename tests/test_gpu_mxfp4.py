@@ -8,8 +8,10 @@
   random codes with a scale per 32-element block within the fp32 bound plus
   the MFMA's in-chunk cutting (tests.parity.mfma_f4f8_error: the FP8 form's
   model, which bounds every output seen);
-* the layer bit-exact on the exact-arithmetic workload and within the stated
-  normwise bound on random weights."""
+* the layer, on the few-token path (VALU dot products of FP4 values widened
+  to FP16) and on the general path, bit-exact on the exact-arithmetic
+  workload (partial last row chunks, 16 routes per token, I = 512 included)
+  and within the stated normwise bound on random weights."""
 import math
 
 import numpy as np
@@ -96,38 +98,66 @@ def test_gemm_random_codes_within_fp32_bound(M, E, k, N, K, block_m):
     assert ok.all()
 
 
-@pytest.mark.parametrize("M,E,k,H,I", [(1, 16, 8, 2048, 256), (5, 16, 8, 2048, 512), (40, 24, 8, 1024, 256)])
+MX_PATHS = {"token": bfp8.FLAG_LAYER_TOKEN, "general": bfp8.FLAG_LAYER_GENERAL}
+
+
+def _mx_paths(M, H, k, E, I):
+    """The paths that take this shape: (name, flags, first stage)."""
+    out = []
+    for name, flag in MX_PATHS.items():
+        try:
+            st = bfp8.fused_moe_stages(M, H, k, E, I, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4, flags=flag))
+        except bfp8.BFP8MoEError:
+            continue
+        out.append((name, flag, st[0]))
+    return out
+
+
+# (M, E, k, H, I): few-token shapes (the decode widths, a row of 1,280 bytes
+# whose last 1 KB chunk is a quarter filled, 16 routes per token, I = 512) and
+# general-path ones
+@pytest.mark.parametrize("M,E,k,H,I", [(1, 16, 8, 2048, 256), (1, 16, 8, 7168, 256), (1, 16, 8, 2560, 256),
+                                       (5, 16, 8, 2048, 512), (3, 24, 16, 3072, 256), (40, 24, 8, 1024, 256)])
 def test_layer_exact_workload(M, E, k, H, I):
     print_case("mxfp4 layer exact", M, E, k, H, I)
     hidden, ids, w, W = synth.exact_mxfp4_layer_inputs(M, E, k, H, I, "mx_layer")
+    paths = _mx_paths(M, H, k, E, I)
+    assert paths
     for clamp in (math.inf, 7.0):
-        o = bfp8.opts(scale_fmt=bfp8.SCALE_UE8M0, clamp_limit=clamp, weight_scale_mode=bfp8.WEIGHT_MXFP4)
-        out = bfp8.fused_moe_mxfp4(hidden.to(dev()), ids.to(dev()), w.to(dev()), W.w13.to(dev()), W.w13_s.to(dev()),
-                                   W.w2.to(dev()), W.w2_s.to(dev()), E=E, o=o)
-        torch.cuda.synchronize()
         ref = O.fused_moe_mxfp4(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, scale_fmt=O.SCALE_UE8M0, clamp=clamp)
-        got = bf16_np(out)
-        nd = int((got != ref).sum())
-        print(f"  clamp {clamp}: {nd} of {got.size} outputs differ", flush=True)
-        assert nd == 0
+        for name, flag, first in paths:
+            o = bfp8.opts(scale_fmt=bfp8.SCALE_UE8M0, clamp_limit=clamp, weight_scale_mode=bfp8.WEIGHT_MXFP4,
+                          flags=flag)
+            out = bfp8.fused_moe_mxfp4(hidden.to(dev()), ids.to(dev()), w.to(dev()), W.w13.to(dev()),
+                                       W.w13_s.to(dev()), W.w2.to(dev()), W.w2_s.to(dev()), E=E, o=o)
+            torch.cuda.synchronize()
+            got = bf16_np(out)
+            nd = int((got != ref).sum())
+            print(f"  {name} ({first}), clamp {clamp}: {nd} of {got.size} outputs differ", flush=True)
+            assert nd == 0
 
 
-@pytest.mark.parametrize("M,E,k,H,I", [(1, 32, 8, 4096, 256), (64, 32, 8, 2048, 768)])
+@pytest.mark.parametrize("M,E,k,H,I", [(1, 32, 8, 4096, 256), (4, 64, 8, 7168, 256), (64, 32, 8, 2048, 768)])
 def test_layer_random_weights(M, E, k, H, I):
     print_case("mxfp4 layer random", M, E, k, H, I)
     ids, w = synth.uniform_routing(M, E, k, "mx_layer_r", M)
     hidden = synth.hidden_states(M, H, "mx_layer_r", M)
     W = synth.mxfp4_weights(E, H, I, "mx_layer_r", M)
-    o = bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4)
-    assert bfp8.fused_moe_stages(M, H, k, E, I, o) == ["route_prepare_quant", "gate_up_gemm_mxfp4",
-                                                       "silu_and_mul_quant", "down_gemm_mxfp4", "moe_reduce"]
-    out = bfp8.fused_moe_mxfp4(hidden.to(dev()), ids.to(dev()), w.to(dev()), W.w13.to(dev()), W.w13_s.to(dev()),
-                               W.w2.to(dev()), W.w2_s.to(dev()), E=E, o=o)
-    torch.cuda.synchronize()
+    auto = bfp8.fused_moe_stages(M, H, k, E, I, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4))
+    if M <= 4:
+        assert auto == ["token_gate_up_swiglu_mxfp4", "token_down_reduce_mxfp4"]
+    else:
+        assert auto == ["route_prepare_quant", "gate_up_gemm_mxfp4", "silu_and_mul_quant", "down_gemm_mxfp4",
+                        "moe_reduce"]
     ref = O.fused_moe_mxfp4(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s)
-    err = normwise_err(bf16_np(out), ref)
-    print(f"  normwise {err:.2e}", flush=True)
-    assert err <= LAYER_TOL
+    for name, flag, _ in _mx_paths(M, H, k, E, I):
+        o = bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4, flags=flag)
+        out = bfp8.fused_moe_mxfp4(hidden.to(dev()), ids.to(dev()), w.to(dev()), W.w13.to(dev()),
+                                   W.w13_s.to(dev()), W.w2.to(dev()), W.w2_s.to(dev()), E=E, o=o)
+        torch.cuda.synchronize()
+        err = normwise_err(bf16_np(out), ref)
+        print(f"  {name}: normwise {err:.2e}", flush=True)
+        assert err <= LAYER_TOL
 
 
 def test_mxfp4_layer_small_shape():
