@@ -74,6 +74,7 @@ const char* const kChannelStages[] = {"route_prepare", "quant_fp8_rows", "gate_u
 const char* const kDecodeStages[] = {"decode_gate_up_swiglu", "decode_down_reduce"};
 const char* const kTokenStages[] = {"token_gate_up_swiglu", "token_down_reduce"};
 const char* const kTokenMxfp4Stages[] = {"token_gate_up_swiglu_mxfp4", "token_down_reduce_mxfp4"};
+const char* const kTokenChannelStages[] = {"token_gate_up_swiglu_channel", "token_down_reduce_channel"};
 enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
 
 // The few-token path is the default up to this many tokens: it reads one
@@ -115,7 +116,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.a2_static = o.inter_static_scale;
   const bool block = !p.channel && !p.mxfp4;  // the small-batch path takes block scales only
   const bool fits = block && bfp8::decode_path_fits(M, H, k, I);
-  const bool token_fits = !p.channel && bfp8::token_path_fits(M, H, k, I, p.mxfp4);
+  const bool token_fits = bfp8::token_path_fits(M, H, k, I, o.weight_scale_mode);
   if (o.flags & BFP8MOE_FLAG_LAYER_GENERAL)
     p.mode = kModeGeneral;
   else if (o.flags & BFP8MOE_FLAG_LAYER_DECODE)
@@ -509,8 +510,8 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
   if (o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_CHANNEL) {
     if (!bfp8::rows_quant_fits(H) || !bfp8::rows_quant_fits(I))
       return fail(BFP8MOE_ERR_UNSUPPORTED, "the W8A8 (channel) variant takes H and I up to 8192 (H=%d I=%d)", H, I);
-    if (o.flags & (BFP8MOE_FLAG_LAYER_DECODE | BFP8MOE_FLAG_LAYER_TOKEN))
-      return fail(BFP8MOE_ERR_UNSUPPORTED, "the W8A8 (channel) variant runs on the general path only");
+    if (o.flags & BFP8MOE_FLAG_LAYER_DECODE)
+      return fail(BFP8MOE_ERR_UNSUPPORTED, "the W8A8 (channel) variant runs on the general and few-token paths");
   }
   if (o.weight_scale_mode == BFP8MOE_WEIGHT_MXFP4) {
     if (H % 256 != 0 || I % 256 != 0)
@@ -525,7 +526,7 @@ bfp8moe_status_t check_layer_shape(int64_t M, int32_t H, int32_t k, int32_t E, i
                 "I<=512)",
                 (long long)M, k, H, I);
   if ((o.flags & BFP8MOE_FLAG_LAYER_TOKEN) && M > 0 &&
-      !bfp8::token_path_fits(M, H, k, I, o.weight_scale_mode == BFP8MOE_WEIGHT_MXFP4))
+      !bfp8::token_path_fits(M, H, k, I, o.weight_scale_mode))
     return fail(BFP8MOE_ERR_UNSUPPORTED,
                 "few-token path forced but M=%lld k=%d H=%d I=%d do not fit it (M<=32, k<=16, H<=8192, "
                 "I in {128, 256, 512}; MXFP4: I in {256, 512})",
@@ -549,7 +550,9 @@ int32_t fused_moe_block_fp8_stages(int64_t M, int32_t H, int32_t k, int32_t E, i
   if (check_layer_shape(M, H, k, E, I, o) != BFP8MOE_OK) return -1;
   LayerPlan p;
   plan_layer(p, M, H, k, E, I, o);
-  const char* const* list = p.mode == kModeToken    ? (p.mxfp4 ? kTokenMxfp4Stages : kTokenStages)
+  const char* const* list = p.mode == kModeToken    ? (p.mxfp4     ? kTokenMxfp4Stages
+                                                       : p.channel ? kTokenChannelStages
+                                                                   : kTokenStages)
                             : p.mode == kModeDecode ? kDecodeStages
                             : p.channel             ? kChannelStages
                             : p.mxfp4               ? (p.rq_fused ? kMxfp4FusedStages : kMxfp4Stages)
@@ -620,7 +623,7 @@ bfp8moe_status_t layer_impl(const uint16_t* hidden, int64_t M, int32_t H, const 
     uint16_t* act = reinterpret_cast<uint16_t*>(base + p.off_act);
     return hip_status(bfp8::launch_token_layer(hidden, M, H, topk_ids, topk_w, k, layer_sel(p), w13, w13_scale_v,
                                                w2, w2_scale_v, I, p.fmt, p.clamp, act, out, st, &hook, nullptr,
-                                               p.mxfp4),
+                                               o.weight_scale_mode, p.a1_static, p.a2_static),
                       "fused_moe_block_fp8 (few tokens)");
   }
   if (p.mode == kModeDecode) {

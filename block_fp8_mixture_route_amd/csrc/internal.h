@@ -182,21 +182,25 @@ bool decode_path_fits(int64_t M, int H, int k, int I);
 // Few-token path: gate/up + SwiGLU kernel per route, then down + moe_reduce
 // kernel per token, both matrix-vector streaming kernels (each route reads its
 // expert's rows).  act: [M*k, I] BF16 scratch.
-// mx: MXFP4 weights (E2M1 rows, E8M0 scale per 32), H % 256 == 0 and I 256
-// or 512; else block-FP8 weights.
-bool token_path_fits(int64_t M, int H, int k, int I, bool mx = false);
+// wfmt: the weight format, as the C ABI's weight_scale_mode (block-FP8 and
+// W8A8: I 128, 256 or 512; MXFP4: H % 256 == 0 and I 256 or 512).
+bool token_path_fits(int64_t M, int H, int k, int I, int wfmt = 0);
 int device_cu_count();  // of the current device; 0 when there is none
 // Fault bits of the bounded in-kernel waits on the current device (bit 0: the
 // few-token gate/up kernel's wait for its hidden row ran out); optionally
 // cleared.  Synchronous.
 hipError_t read_wait_faults(unsigned* flags, bool clear);
-// w13_s / w2_s: fp32 block scales, or with mx E8M0 bytes [L, 2I, H/32] and
-// [L, H, I/32] (w13 / w2 then packed E2M1, [L, 2I, H/2] and [L, H, I/2]).
+// w13_s / w2_s as wfmt says: fp32 block scales; fp32 scales per row [L, 2I]
+// and [L, H] (W8A8, with a1_static / a2_static > 0 the static activation
+// scales of the hidden and SwiGLU rows, else per-row dynamic ones); or E8M0
+// bytes [L, 2I, H/32] and [L, H, I/32] (MXFP4: w13 / w2 packed E2M1, [L, 2I,
+// H/2] and [L, H, I/2]).
 hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
                               int k, const ExpertSel& sel, const uint8_t* w13, const void* w13_s,
                               const uint8_t* w2, const void* w2_s, int I, int fmt, float limit, uint16_t* act,
                               uint16_t* out, hipStream_t stream, const LaunchHook* hook,
-                              const RouterArgs* route = nullptr, bool mx = false);
+                              const RouterArgs* route = nullptr, int wfmt = 0, float a1_static = 0.0f,
+                              float a2_static = 0.0f);
 hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
                                int k, const ExpertSel& sel, const uint8_t* w13, const float* w13_s,
                                const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,

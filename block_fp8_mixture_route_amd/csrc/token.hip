@@ -74,12 +74,19 @@ constexpr int kMxMaxUnits = kDownWaves * kMxUnitsPerWave;
 constexpr int kMaxDownRows = 64;
 constexpr int kDownTarget = 256;  // down workgroups aimed at (one per compute unit of MI355X)
 constexpr unsigned kSpinLimit = 1u << 20;  // bound of the LDS waits (about 0.03 s)
+// Weight formats of the two kernels (the C ABI's weight_scale_mode values):
+// E4M3 rows with fp32 scales per 128 x 128 block; E4M3 rows with one fp32
+// scale per row (W8A8: the activations then take one scale per row too);
+// E2M1 rows with an E8M0 scale per 32 elements (MXFP4).
+constexpr int kWBlock = 0, kWChannel = 1, kWMx = 2;
 
 }  // namespace
 
 // Bit 0: a column wave of the gate/up kernel ran out of its bounded wait for
-// the hidden row (its column's value is then unspecified).  Set with a device
-// atomic, never cleared by the kernels; read and cleared by
+// the hidden row (its column's value is then unspecified).  Bit 1: a
+// hidden-row wave of the W8A8 form ran out of its wait for the other
+// hidden-row waves' maxima (the row's scale is then unspecified).  Set with a
+// device atomic, never cleared by the kernels; read and cleared by
 // read_wait_faults (bfp8moe_wait_faults in the C ABI).
 __device__ unsigned int g_wait_faults = 0;
 
@@ -115,9 +122,10 @@ __device__ __forceinline__ float amax8(const float (&f)[8]) {
 
 // Quantise 8 BF16-valued floats of one group (scale sc) and store the E4M3
 // values dec(E4M3(x / sc)) as four FP16 pairs (every E4M3 value is exact in
-// FP16, subnormals included) at dst (LDS, 16-byte aligned).
-__device__ __forceinline__ void quant_store8(const float (&f)[8], float sc, h2* dst) {
-  const uint2 q = encode8_scaled(f, sc);
+// FP16, subnormals included) at dst (LDS, 16-byte aligned).  sat: the scale
+// may be below amax / 448 (a static one), quotients beyond saturate.
+__device__ __forceinline__ void quant_store8(const float (&f)[8], float sc, h2* dst, bool sat = false) {
+  const uint2 q = sat ? encode8_scaled_sat(f, sc) : encode8_scaled(f, sc);
   const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)q.x, 1.0f, false);
   const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)q.x, 1.0f, true);
   const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)q.y, 1.0f, false);
@@ -239,10 +247,16 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 // Two BF16-valued floats of one group quantised with scale sc, returned as
-// the FP16 pair of their E4M3 values (same rounding as quant_store8).
-__device__ __forceinline__ h2 quant2(float a, float b, float sc) {
+// the FP16 pair of their E4M3 values (same rounding as quant_store8; sat as
+// there: quotients beyond +-448 saturate).
+__device__ __forceinline__ h2 quant2(float a, float b, float sc, bool sat = false) {
   const double rs = 1.0 / (double)sc;
-  const int q = __builtin_amdgcn_cvt_pk_fp8_f32((float)((double)a * rs), (float)((double)b * rs), 0, false);
+  float qa = (float)((double)a * rs), qb = (float)((double)b * rs);
+  if (sat) {
+    qa = fminf(fmaxf(qa, -kE4M3Max), kE4M3Max);
+    qb = fminf(fmaxf(qb, -kE4M3Max), kE4M3Max);
+  }
+  const int q = __builtin_amdgcn_cvt_pk_fp8_f32(qa, qb, 0, false);
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q, 1.0f, false);
 }
 
@@ -258,14 +272,17 @@ __device__ __forceinline__ h2 quant2(float a, float b, float sc) {
 // barrier would also wait for every column wave to have issued its loads,
 // which the compute unit's memory queue holds back for microseconds, and no
 // wave could start its dot products before then.
-template <int RL, int I, bool kRoute, bool kMx>
+template <int RL, int I, bool kRoute, int kW>
 __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
     const uint16_t* __restrict__ hidden, int H, const int32_t* __restrict__ ids, int k, ExpertSel sel,
-    const uint8_t* __restrict__ w13, const void* __restrict__ w13_sv, int fmt, float limit, int clamp,
-    uint16_t* __restrict__ act, RouterArgs ra) {
+    const uint8_t* __restrict__ w13, const void* __restrict__ w13_sv, int fmt, float a_static, float limit,
+    int clamp, uint16_t* __restrict__ act, RouterArgs ra) {
   constexpr int kSlices = I / 8;
   // kMx: MXFP4 rows (H / 2 bytes, E2M1) with an E8M0 scale byte per 32
-  // elements; else E4M3 rows (H bytes) with fp32 scales per 128 x 128 block
+  // elements; kCh: E4M3 rows with one fp32 scale per row, and the hidden row
+  // quantised with one scale (its amax over H, or a_static when > 0); else
+  // E4M3 rows (H bytes) with fp32 scales per 128 x 128 block
+  constexpr bool kMx = kW == kWMx, kCh = kW == kWChannel;
   const float* __restrict__ w13_s = static_cast<const float*>(w13_sv);
   const uint8_t* __restrict__ w13_mx = static_cast<const uint8_t*>(w13_sv);
   const int RB = kMx ? H / 2 : H;  // bytes per weight row
@@ -273,13 +290,18 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   __shared__ float s_as[kMaxH / 128];           // its group scales
   __shared__ float s_tab[2 * (kMaxH / 128)];    // W13 block scales: gate row block, then up row block
   __shared__ int s_ready;                       // hidden-row waves done
+  __shared__ float s_wmax[kUpWaves - kColumnWaves];  // kCh: each hidden-row wave's amax
+  __shared__ int s_nmax;                        // kCh: hidden-row waves whose amax is in s_wmax
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H / 128;
   const int j = blockIdx.x / kSlices;
   const int n0 = (blockIdx.x - j * kSlices) * 8;
-  if (tid == 0) s_ready = 0;
+  if (tid == 0) {
+    s_ready = 0;
+    s_nmax = 0;
+  }
   int id_j;
   // the router folded in: wave 0 ranks the token's logits up to this route's
   // rank and hands the expert to the other waves through LDS (no weight load
@@ -361,25 +383,51 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   }
   const int te = min(t, 2 * G - 1);
   const float tab =
-      kMx ? 0.0f
+      kW != kWBlock
+          ? 0.0f
           : ws13[((size_t)e * (2 * I / 128) + (te < G ? n0 / 128 : (I + n0) / 128)) * G + (te < G ? te : te - G)];
   // every wave's small loads have left before any W13 load: the compute
   // unit returns data roughly in issue order, so they land first
   wg_sync();
 
   if (wave >= kColumnWaves) {
-    // hidden-row waves: quantise into LDS (same arithmetic as quant_fp8),
-    // store the table, and count themselves done
+    // hidden-row waves: quantise into LDS (same arithmetic as quant_fp8, or
+    // quant_fp8_rows for kCh), store the table, and count themselves done
+    float f[2][8];
+#pragma unroll
+    for (int p = 0; p < 2; p++) unpack8(hv[p], f[p]);
+    float row_sc = 0.0f;
+    if constexpr (kCh) {
+      // one scale for the row: the 8 waves' maxima meet in LDS (bounded wait)
+      row_sc = a_static;
+      if (!(a_static > 0.0f)) {
+        const float m = group_max<64>(fmaxf(amax8(f[0]), amax8(f[1])));
+        if (lane == 0) {
+          s_wmax[wave - kColumnWaves] = m;
+          __hip_atomic_fetch_add(&s_nmax, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        for (unsigned spins = 0;
+             __hip_atomic_load(&s_nmax, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kUpWaves - kColumnWaves &&
+             spins < kSpinLimit;
+             spins++)
+          __builtin_amdgcn_s_sleep(1);
+        if (__hip_atomic_load(&s_nmax, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kUpWaves - kColumnWaves &&
+            lane == 0)
+          atomicOr(&g_wait_faults, 2u);  // ran out: report it
+        float rm = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kUpWaves - kColumnWaves; w++) rm = fmaxf(rm, s_wmax[w]);
+        row_sc = group_scale(rm, fmt);
+      }
+    }
 #pragma unroll
     for (int p = 0; p < 2; p++) {
       const int hg = min((t >> 4) + 32 * p, G - 1);
-      float f[8];
-      unpack8(hv[p], f);
-      const float sc = group_scale(max_over_16(amax8(f)), fmt);
-      quant_store8(f, sc, s_ah + act_swz((hg * 128 + l16 * 8) / 2));
+      const float sc = kCh ? row_sc : group_scale(max_over_16(amax8(f[p])), fmt);
+      quant_store8(f[p], sc, s_ah + act_swz((hg * 128 + l16 * 8) / 2), kCh && a_static > 0.0f);
       if (l16 == 0) s_as[hg] = sc;
     }
-    if constexpr (!kMx) s_tab[te] = tab;
+    if constexpr (kW == kWBlock) s_tab[te] = tab;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS stores are done
     if (lane == 0) __hip_atomic_fetch_add(&s_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (writer) write_routing();
@@ -390,7 +438,8 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
   // loads, all issued before any data is used (every chunk but the last lies
   // inside the row; the last is clamped)
   uint4 wg[RL], wu[RL];
-  uint32_t sg[kMx ? RL : 1], su[kMx ? RL : 1];  // kMx: each load's E8M0 scale byte (one 32-element block)
+  // kMx: each load's E8M0 scale byte (one 32-element block); kCh: the row's fp32 scale (bits)
+  uint32_t sg[kMx ? RL : 1], su[kMx ? RL : 1];
   {
     const uint8_t* gsrc = w13 + ((size_t)e * 2 * I + n0 + wave) * RB;
     const uint8_t* usrc = gsrc + (size_t)I * RB;
@@ -400,6 +449,10 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
       const int off = c < RL - 1 ? 1024 * c + 16 * lane : last;
       wg[c] = *reinterpret_cast<const uint4*>(gsrc + off);
       wu[c] = *reinterpret_cast<const uint4*>(usrc + off);
+    }
+    if constexpr (kCh) {
+      sg[0] = __builtin_bit_cast(uint32_t, w13_s[(size_t)e * 2 * I + n0 + wave]);
+      su[0] = __builtin_bit_cast(uint32_t, w13_s[(size_t)e * 2 * I + I + n0 + wave]);
     }
     if constexpr (kMx) {
       const uint8_t* gs = w13_mx + ((size_t)e * 2 * I + n0 + wave) * (H / 32);
@@ -436,6 +489,10 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
     if constexpr (kMx) {
       pg = dot32_fp4_row(wg[c], s_ah, ka / 2) * (as * e8m0_f32(sg[c]));
       pu = dot32_fp4_row(wu[c], s_ah, ka / 2) * (as * e8m0_f32(su[c]));
+    } else if constexpr (kCh) {
+      pg = dot16_row(wg[c], s_ah, ka / 2);  // one scale for the row: applied to the sum
+      pu = dot16_row(wu[c], s_ah, ka / 2);
+      (void)as;
     } else {
       pg = dot16_row(wg[c], s_ah, ka / 2) * (as * s_tab[ka / 128]);
       pu = dot16_row(wu[c], s_ah, ka / 2) * (as * s_tab[G + ka / 128]);
@@ -443,6 +500,10 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
     if (c == RL - 1 && kof >= H) pg = pu = 0.0f;
     ag += pg;
     au += pu;
+  }
+  if constexpr (kCh) {
+    ag *= s_as[0] * __builtin_bit_cast(float, sg[0]);
+    au *= s_as[0] * __builtin_bit_cast(float, su[0]);
   }
   ag = group_sum<64>(ag);
   au = group_sum<64>(au);
@@ -463,13 +524,16 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
 // depend on the routing), the W2 units, the W2 block scale of each lane's
 // row and group.  Route ids are read with uniform (scalar) loads by each wave
 // that needs them: no barrier stands between the start and the W2 loads.
-template <int I, int KMAX, bool kMx>
+template <int I, int KMAX, int kW>
 __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int k,
-    ExpertSel sel, const uint8_t* __restrict__ w2, const void* __restrict__ w2_sv, int H, int fmt,
+    ExpertSel sel, const uint8_t* __restrict__ w2, const void* __restrict__ w2_sv, int H, int fmt, float q_static,
     int DR, int DL, uint32_t dl_magic, uint16_t* __restrict__ out) {
   // kMx: MXFP4 rows (I / 2 bytes, E2M1) with an E8M0 scale byte per 32
-  // elements; else E4M3 rows (I bytes) with fp32 scales per 128 x 128 block
+  // elements; kCh: E4M3 rows with one fp32 scale per row, and each SwiGLU
+  // row quantised with one scale (its amax over I, or q_static when > 0);
+  // else E4M3 rows (I bytes) with fp32 scales per 128 x 128 block
+  constexpr bool kMx = kW == kWMx, kCh = kW == kWChannel;
   constexpr int RBI = kMx ? I / 2 : I;  // bytes per W2 row
   constexpr int GI = I / 128, kRpl = 1024 / RBI, kLpr = RBI / 16;
   constexpr int kUpw = kMx ? kMxUnitsPerWave : kUnitsPerWave;  // W2 units per wave
@@ -536,20 +600,44 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
     const int row = min(d0 + c * kRpl + lane / kLpr, H - 1);
     if constexpr (kMx)
       wsc[i] = e8m0_f32(w2_mx[((size_t)max(eu[i], 0) * H + row) * (I / 32) + kof / 32]);
+    else if constexpr (kCh)
+      wsc[i] = w2_s[(size_t)max(eu[i], 0) * H + row];
     else
       wsc[i] = w2_s[((size_t)max(eu[i], 0) * G + row / 128) * GI + kof / 128];
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. the live routes' SwiGLU groups quantised into LDS (same arithmetic as
-  //    silu_and_mul_quant_fp8) while W2 is in flight
+  //    silu_and_mul_quant_fp8, or silu_and_mul_quant_fp8_rows for kCh, whose
+  //    row scale takes the maxima of the row's groups, met in LDS) while W2
+  //    is in flight
+  __shared__ float s_gmax[kCh ? KMAX * GI : 1];
+  if constexpr (kCh) {
+#pragma unroll
+    for (int m = 0; m < kActLoads; m++) {
+      const int gi = wave + kDownWaves * m, jq = min(gi / GI, k - 1);
+      if (gi < k * GI && __builtin_amdgcn_readlane(e_lane, jq) >= 0) {
+        const float gm = group_max<64>(fmaxf(fabsf(bf16_to_f32(av[m] & 0xFFFFu)), fabsf(bf16_to_f32(av[m] >> 16))));
+        if (lane == 0) s_gmax[gi] = gm;
+      }
+    }
+    wg_sync();
+  }
 #pragma unroll
   for (int m = 0; m < kActLoads; m++) {
     const int gi = wave + kDownWaves * m, jq = min(gi / GI, k - 1), g = gi % GI;
     if (gi < k * GI && __builtin_amdgcn_readlane(e_lane, jq) >= 0) {
       const float a0 = bf16_to_f32(av[m] & 0xFFFFu), a1 = bf16_to_f32(av[m] >> 16);
-      const float sc = group_scale(group_max<64>(fmaxf(fabsf(a0), fabsf(a1))), fmt);
-      s_qh[jq][g * 64 + lane] = quant2(a0, a1, sc);
+      float sc;
+      if constexpr (kCh) {
+        float rm = 0.0f;
+#pragma unroll
+        for (int g2 = 0; g2 < GI; g2++) rm = fmaxf(rm, s_gmax[jq * GI + g2]);
+        sc = q_static > 0.0f ? q_static : group_scale(rm, fmt);
+      } else {
+        sc = group_scale(group_max<64>(fmaxf(fabsf(a0), fabsf(a1))), fmt);
+      }
+      s_qh[jq][g * 64 + lane] = quant2(a0, a1, sc, kCh && q_static > 0.0f);
       if (lane == 0) s_qs[jq][g] = sc;
     }
   }
@@ -625,19 +713,20 @@ hipError_t read_wait_faults(unsigned* flags, bool clear) {
   return e;
 }
 
-bool token_path_fits(int64_t M, int H, int k, int I, bool mx) {
+bool token_path_fits(int64_t M, int H, int k, int I, int wfmt) {
   if (M < 1 || M > kMaxTokens || k < 1 || k > kMaxK || H < 128 || H > kMaxH || H % 128 != 0) return false;
-  if (mx) return H % 256 == 0 && (I == 256 || I == 512);  // whole 32-element blocks per 16-byte lane load
-  return I == 128 || I == 256 || I == 512;
+  if (wfmt == kWMx) return H % 256 == 0 && (I == 256 || I == 512);  // whole 32-element blocks per 16-byte load
+  return (wfmt == kWBlock || wfmt == kWChannel) && (I == 128 || I == 256 || I == 512);
 }
 
 hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const int32_t* ids, const float* topk_w,
                               int k, const ExpertSel& sel, const uint8_t* w13, const void* w13_s,
                               const uint8_t* w2, const void* w2_s, int I, int fmt, float limit, uint16_t* act,
                               uint16_t* out, hipStream_t stream, const LaunchHook* hook,
-                              const RouterArgs* route, bool mx) {
-  if (!token_path_fits(M, H, k, I, mx)) return hipErrorInvalidValue;  // the caller checks token_path_fits
-  if (mx && route) return hipErrorInvalidValue;  // the routed layer takes block-FP8 weights
+                              const RouterArgs* route, int wfmt, float a1_static, float a2_static) {
+  if (!token_path_fits(M, H, k, I, wfmt)) return hipErrorInvalidValue;  // the caller checks token_path_fits
+  if (wfmt != kWBlock && route) return hipErrorInvalidValue;  // the routed layer takes block-FP8 weights
+  const bool mx = wfmt == kWMx;
   if (route && (route->E < 1 || route->E > kFoldedRouterMaxE || k > route->E)) return hipErrorInvalidValue;
   const RouterArgs ra = route ? *route : RouterArgs{};
   if (route) {
@@ -659,16 +748,19 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
 #define BFP8_TOKEN_CASE(N, II)                                                                                  \
   case N:                                                                                                       \
     if (route)                                                                                                  \
-      hipLaunchKernelGGL((token_gate_up_kernel<N, II, true, false>), dim3(up_grid), dim3(kUpThreads), 0,       \
-                         stream, hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);               \
+      hipLaunchKernelGGL((token_gate_up_kernel<N, II, true, kWBlock>), dim3(up_grid), dim3(kUpThreads), 0,     \
+                         stream, hidden, H, ids, k, sel, w13, w13_s, fmt, a1_static, limit, clamp, act, ra);    \
+    else if (wfmt == kWChannel)                                                                                 \
+      hipLaunchKernelGGL((token_gate_up_kernel<N, II, false, kWChannel>), dim3(up_grid), dim3(kUpThreads), 0,  \
+                         stream, hidden, H, ids, k, sel, w13, w13_s, fmt, a1_static, limit, clamp, act, ra);    \
     else                                                                                                        \
-      hipLaunchKernelGGL((token_gate_up_kernel<N, II, false, false>), dim3(up_grid), dim3(kUpThreads), 0,      \
-                         stream, hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);               \
+      hipLaunchKernelGGL((token_gate_up_kernel<N, II, false, kWBlock>), dim3(up_grid), dim3(kUpThreads), 0,    \
+                         stream, hidden, H, ids, k, sel, w13, w13_s, fmt, a1_static, limit, clamp, act, ra);    \
     break;
 #define BFP8_TOKEN_MX_CASE(N, II)                                                                               \
   case N:                                                                                                       \
-    hipLaunchKernelGGL((token_gate_up_kernel<N, II, false, true>), dim3(up_grid), dim3(kUpThreads), 0, stream,  \
-                       hidden, H, ids, k, sel, w13, w13_s, fmt, limit, clamp, act, ra);                         \
+    hipLaunchKernelGGL((token_gate_up_kernel<N, II, false, kWMx>), dim3(up_grid), dim3(kUpThreads), 0, stream,  \
+                       hidden, H, ids, k, sel, w13, w13_s, fmt, a1_static, limit, clamp, act, ra);              \
     break;
 #define BFP8_TOKEN_RL(II)   \
   switch (rl) {             \
@@ -709,27 +801,36 @@ hipError_t launch_token_layer(const uint16_t* hidden, int64_t M, int H, const in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (hook) hook->before(1, stream);
-#define BFP8_TOKEN_DOWN(II, MX)                                                                                  \
+#define BFP8_TOKEN_DOWN(II, W)                                                                                   \
   do {                                                                                                           \
     if (k <= 8)                                                                                                  \
-      hipLaunchKernelGGL((token_down_kernel<II, 8, MX>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0,   \
-                         stream, act, ids, topk_w, k, sel, w2, w2_s, H, fmt, dr, dl, dl_magic, out);             \
+      hipLaunchKernelGGL((token_down_kernel<II, 8, W>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0,    \
+                         stream, act, ids, topk_w, k, sel, w2, w2_s, H, fmt, a2_static, dr, dl, dl_magic, out);  \
     else                                                                                                         \
-      hipLaunchKernelGGL((token_down_kernel<II, 16, MX>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0,  \
-                         stream, act, ids, topk_w, k, sel, w2, w2_s, H, fmt, dr, dl, dl_magic, out);             \
+      hipLaunchKernelGGL((token_down_kernel<II, 16, W>), dim3(down_grid, (unsigned)M), dim3(kDownThreads), 0,   \
+                         stream, act, ids, topk_w, k, sel, w2, w2_s, H, fmt, a2_static, dr, dl, dl_magic, out);  \
+  } while (0)
+#define BFP8_TOKEN_DOWN_I(W)      \
+  do {                            \
+    if (I == 128)                 \
+      BFP8_TOKEN_DOWN(128, W);    \
+    else if (I == 256)            \
+      BFP8_TOKEN_DOWN(256, W);    \
+    else                          \
+      BFP8_TOKEN_DOWN(512, W);    \
   } while (0)
   if (!run1) {
   } else if (mx) {
     if (I == 256)
-      BFP8_TOKEN_DOWN(256, true);
+      BFP8_TOKEN_DOWN(256, kWMx);
     else
-      BFP8_TOKEN_DOWN(512, true);
-  } else if (I == 128)
-    BFP8_TOKEN_DOWN(128, false);
-  else if (I == 256)
-    BFP8_TOKEN_DOWN(256, false);
-  else
-    BFP8_TOKEN_DOWN(512, false);
+      BFP8_TOKEN_DOWN(512, kWMx);
+  } else if (wfmt == kWChannel) {
+    BFP8_TOKEN_DOWN_I(kWChannel);
+  } else {
+    BFP8_TOKEN_DOWN_I(kWBlock);
+  }
+#undef BFP8_TOKEN_DOWN_I
 #undef BFP8_TOKEN_DOWN
   e = hipGetLastError();
   if (hook) hook->before(2, stream);

@@ -63,14 +63,23 @@ def test_opts_layout_matches_the_c_compiler(tmp_path):
     assert got[1:] == [getattr(_lib.Opts, f).offset for f in fields]
 
 
-def test_w8a8_layer_runs_the_general_path_only():
+def test_w8a8_layer_paths():
     o = bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL)
-    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == [
-        "route_prepare", "quant_fp8_rows", "gate_up_gemm_channel", "silu_and_mul_quant_rows", "down_gemm_channel",
-        "moe_reduce"]
-    for flag in (bfp8.FLAG_LAYER_TOKEN, bfp8.FLAG_LAYER_DECODE):
-        with pytest.raises(bfp8.BFP8MoEError):
-            bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(weight_scale_mode=1, flags=flag))
+    # a few tokens: the few-token kernels in their W8A8 form, by default or forced
+    token = ["token_gate_up_swiglu_channel", "token_down_reduce_channel"]
+    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == token
+    assert bfp8.fused_moe_stages(30, 2048, 8, 64, 128, bfp8.opts(weight_scale_mode=1,
+                                                                  flags=bfp8.FLAG_LAYER_TOKEN)) == token
+    general = ["route_prepare", "quant_fp8_rows", "gate_up_gemm_channel", "silu_and_mul_quant_rows",
+               "down_gemm_channel", "moe_reduce"]
+    assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(weight_scale_mode=1,
+                                                                  flags=bfp8.FLAG_LAYER_GENERAL)) == general
+    assert bfp8.fused_moe_stages(64, 7168, 8, 256, 256, o) == general
+    # not the small-batch path, nor the few-token path at I = 768
+    with pytest.raises(bfp8.BFP8MoEError):
+        bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(weight_scale_mode=1, flags=bfp8.FLAG_LAYER_DECODE))
+    with pytest.raises(bfp8.BFP8MoEError):
+        bfp8.fused_moe_stages(1, 7168, 8, 256, 768, bfp8.opts(weight_scale_mode=1, flags=bfp8.FLAG_LAYER_TOKEN))
     with pytest.raises(bfp8.BFP8MoEError):  # rows beyond 8192
         bfp8.fused_moe_stages(1, 8320, 8, 256, 256, o)
     with pytest.raises(bfp8.BFP8MoEError):

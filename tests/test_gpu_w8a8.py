@@ -83,24 +83,47 @@ def _channel_weights(W, E, H, I, key):
     return c13, c2
 
 
-@pytest.mark.parametrize("M,E,k,H,I", [(1, 16, 8, 7168, 256), (5, 16, 8, 2048, 512), (40, 24, 8, 1024, 256)])
-@pytest.mark.parametrize("statics", [(0.0, 0.0), (0.25, 0.0), (0.25, 2.0 ** -6)])
+W8A8_PATHS = {"token": bfp8.FLAG_LAYER_TOKEN, "general": bfp8.FLAG_LAYER_GENERAL}
+
+
+def _w8a8_paths(M, H, k, E, I):
+    out = []
+    for name, flag in W8A8_PATHS.items():
+        try:
+            bfp8.fused_moe_stages(M, H, k, E, I, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL, flags=flag))
+        except bfp8.BFP8MoEError:
+            continue
+        out.append((name, flag))
+    return out
+
+
+# (M, E, k, H, I): the few-token kernels (their W8A8 form: one scale per hidden
+# row from all 8 hidden-row waves, one per SwiGLU row from its groups' maxima;
+# H not a multiple of 1024 and 16 routes per token included) and the general path
+@pytest.mark.parametrize("M,E,k,H,I", [(1, 16, 8, 7168, 256), (5, 16, 8, 2048, 512), (2, 24, 16, 2560, 128),
+                                       (40, 24, 8, 1024, 256)])
+# static scales: none; the hidden rows' (no value saturates); both, the SwiGLU
+# rows saturating; both saturating (quotients past 448 clamp as quant_fp8's do)
+@pytest.mark.parametrize("statics", [(0.0, 0.0), (0.25, 0.0), (0.25, 2.0 ** -6), (2.0 ** -6, 2.0 ** -6)])
 def test_w8a8_layer_exact_workload(M, E, k, H, I, statics):
     print_case("w8a8 layer exact", M, E, k, H, I, statics)
     hidden, ids, w, W = synth.exact_layer_inputs(M, E, k, H, I, "w8a8_exact")
     c13, c2 = _channel_weights(W, E, H, I, "w8a8_exact")
+    paths = _w8a8_paths(M, H, k, E, I)
+    assert paths
     for clamp in (math.inf, 7.0):
-        o = bfp8.opts(scale_fmt=bfp8.SCALE_UE8M0, clamp_limit=clamp, weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL,
-                      act_static_scale=statics[0], inter_static_scale=statics[1])
-        out = bfp8.fused_moe_block_fp8(hidden.to(dev()), ids.to(dev()), w.to(dev()), W.w13.to(dev()), c13.to(dev()),
-                                       W.w2.to(dev()), c2.to(dev()), E=E, o=o)
-        torch.cuda.synchronize()
         ref = O.fused_moe_w8a8(hidden, ids, w, W.w13, c13, W.w2, c2, scale_fmt=O.SCALE_UE8M0, a1_static=statics[0],
                                a2_static=statics[1], clamp=clamp)
-        got = bf16_np(out)
-        nd = int((got != ref).sum())
-        print(f"  clamp {clamp}: {nd} of {got.size} outputs differ", flush=True)
-        assert nd == 0
+        for name, flag in paths:
+            o = bfp8.opts(scale_fmt=bfp8.SCALE_UE8M0, clamp_limit=clamp, weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL,
+                          act_static_scale=statics[0], inter_static_scale=statics[1], flags=flag)
+            out = bfp8.fused_moe_block_fp8(hidden.to(dev()), ids.to(dev()), w.to(dev()), W.w13.to(dev()),
+                                           c13.to(dev()), W.w2.to(dev()), c2.to(dev()), E=E, o=o)
+            torch.cuda.synchronize()
+            got = bf16_np(out)
+            nd = int((got != ref).sum())
+            print(f"  {name}, clamp {clamp}: {nd} of {got.size} outputs differ", flush=True)
+            assert nd == 0
 
 
 @pytest.mark.parametrize("M,E,k,H,I", [(1, 64, 8, 7168, 256), (64, 32, 8, 4096, 768)])
@@ -116,15 +139,16 @@ def test_w8a8_layer_gaussian(M, E, k, H, I):
     s2 = (w2f.abs().amax(-1) / 448.0).clamp_min(1e-12)
     q13 = (w13f / s13[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
     q2 = (w2f / s2[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
-    o = bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL)
-    out = bfp8.fused_moe_block_fp8(hidden, ids, w, q13, s13.contiguous(), q2, s2.contiguous(), E=E, o=o)
-    torch.cuda.synchronize()
     used = torch.unique(ids).long()
     remap = torch.full((E,), -1, dtype=torch.int32, device=dev())
     remap[used] = torch.arange(used.numel(), dtype=torch.int32, device=dev())
     ids_l = remap[ids.long()]
     ref = O.fused_moe_w8a8(hidden.cpu(), ids_l.cpu(), w.cpu(), q13[used].cpu(), s13[used].cpu(), q2[used].cpu(),
                            s2[used].cpu())
-    err = normwise_err(bf16_np(out), ref)
-    print(f"  normwise {err:.2e}", flush=True)
-    assert err <= LAYER_TOL
+    for name, flag in _w8a8_paths(M, H, k, E, I):
+        o = bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL, flags=flag)
+        out = bfp8.fused_moe_block_fp8(hidden, ids, w, q13, s13.contiguous(), q2, s2.contiguous(), E=E, o=o)
+        torch.cuda.synchronize()
+        err = normwise_err(bf16_np(out), ref)
+        print(f"  {name}: normwise {err:.2e}", flush=True)
+        assert err <= LAYER_TOL
