@@ -560,14 +560,16 @@ def variants_table(hip, stream, dev):
     return res
 
 
-def variants_decode_table(hip, stream, dev):
-    """The decode layer (E=256, top-k 8, H=7168, I=256) at 1 and 4 tokens with
-    each weight format: block FP8, W8A8 (random E4M3 codes, per-channel
+def variants_decode_table(hip, stream, dev, token_counts=(1, 4), both_paths=False):
+    """The decode layer (E=256, top-k 8, H=7168, I=256) at a few token counts
+    with each weight format: block FP8, W8A8 (random E4M3 codes, per-channel
     scales, dynamic per-token activation scales) and MXFP4 (random E2M1
     codes, E8M0 scales per 32).  One set of 256 experts per format; instance
     i routes to experts disjoint from its neighbours' (8 M consecutive ones),
     and the rotation of instances reads every expert once, more bytes than the
-    Infinity Cache holds.  Graph-timed; compulsory bytes as variants_table."""
+    Infinity Cache holds.  Graph-timed; compulsory bytes as variants_table.
+    both_paths: the few-token and general paths forced in turn, else the
+    library's choice."""
     import torch
 
     import block_fp8_mixture_route_amd as bfp8
@@ -593,7 +595,7 @@ def variants_decode_table(hip, stream, dev):
     print("|---|---|---|---|---|---|---|---|---|")
     res = {}
     ext = torch.cuda.ExternalStream(stream.value, device=dev)
-    for M in (1, 4):
+    for M in token_counts:
         n_inst = E // (M * k)
         insts = []
         for i in range(n_inst):
@@ -616,7 +618,12 @@ def variants_decode_table(hip, stream, dev):
                                                             out=x[3], ws=ws, o=o)),
         }
         res[M] = {}
+        runs = []
         for f, (o, wbytes, fn) in forms.items():
+            flag_list = [PATH_FLAGS["token"], PATH_FLAGS["general"]] if both_paths else [0]
+            for fl in flag_list:
+                runs.append((f, bfp8.opts(weight_scale_mode=o.weight_scale_mode, flags=fl), wbytes, fn))
+        for f, o, wbytes, fn in runs:
             ws = torch.empty(max(bfp8.fused_moe_workspace_size(M, H, k, E, I, o), 1), dtype=torch.uint8, device=dev)
             path = bfp8.fused_moe_stages(M, H, k, E, I, o)[0]
             with torch.cuda.stream(ext):  # the bindings launch on torch's current stream: the timed one
@@ -628,11 +635,12 @@ def variants_decode_table(hip, stream, dev):
                 stages = bfp8.fused_moe_stages(M, H, k, E, I, o)
                 st_us = {}
                 for si, sn in enumerate(stages):
-                    os_ = bfp8.opts(weight_scale_mode=o.weight_scale_mode, flags=bfp8.FLAG_ONLY_STAGE(si))
+                    os_ = bfp8.opts(weight_scale_mode=o.weight_scale_mode, flags=o.flags | bfp8.FLAG_ONLY_STAGE(si))
                     st_us[sn] = time_graph(hip, stream, lambda: [fn(x, os_, ws) for x in insts], 20) * 1e3 / n_inst
             nbytes = wbytes + io
             roof = nbytes / 8e12 * 1e6
-            res[M][f] = {"us": us, "bytes": nbytes, "roofline_us": roof, "first_stage": path, "stage_us": st_us}
+            res[M][f + ("" if not both_paths else f" ({path})")] = {
+                "us": us, "bytes": nbytes, "roofline_us": roof, "first_stage": path, "stage_us": st_us}
             stx = ", ".join(f"{a} {b:.2f}" for a, b in st_us.items())
             print(f"| {M} | {f} | {path} | {us:.2f} | {nbytes / 1e6:.1f} | {nbytes / (us * 1e3):.0f} | {roof:.2f} | "
                   f"{roof / us:.3f} | {stx} |", flush=True)
@@ -908,6 +916,9 @@ def main():
     ap.add_argument("--router", action="store_true", help="only the router timing table")
     ap.add_argument("--variants-decode", action="store_true",
                     help="only the decode layer (1 and 4 tokens) with block-FP8, W8A8 and MXFP4 weights")
+    ap.add_argument("--variants-crossover", action="store_true",
+                    help="only the decode layer at 4 to 16 tokens per weight format on the few-token and the "
+                         "general path (where the automatic choice switches)")
     ap.add_argument("--phases", action="store_true",
                     help="only the decode layer's phase table: each kernel alone and the layer at five hidden widths, "
                          "fixed cost and streaming rate per kernel fitted, the H=7168 layer split into them")
@@ -944,6 +955,9 @@ def main():
         return
     if args.variants_decode:
         variants_decode_table(hip, stream, dev)
+        return
+    if args.variants_crossover:
+        variants_decode_table(hip, stream, dev, token_counts=(4, 8, 12, 16), both_paths=True)
         return
     if args.phases:
         phase_table(hip, stream, dev, args.steps)

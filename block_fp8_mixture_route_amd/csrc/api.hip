@@ -85,6 +85,11 @@ enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
 // does not fit.
 constexpr int64_t kTokenAutoMaxM = 12;
 constexpr int64_t kDecodeAutoMaxM = 4;
+// With MXFP4 weights the few-token kernels do as much vector work per
+// element as with E4M3 rows while the general path's FP4 MFMA halves its
+// weight bytes: measured at the decode shape, the two paths are even at 8
+// tokens (66.1 against 65.2 µs) and the general path leads from 12.
+constexpr int64_t kTokenAutoMaxMMxfp4 = 8;
 
 // Routes per compact block of the general path, from the routes per local
 // expert on average: 16 below 8, 32 up to 48, 64 above.  Measured: 16 beat
@@ -123,7 +128,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
     p.mode = fits ? kModeDecode : kModeGeneral;
   else if (o.flags & BFP8MOE_FLAG_LAYER_TOKEN)
     p.mode = token_fits ? kModeToken : kModeGeneral;
-  else if (token_fits && M <= kTokenAutoMaxM)
+  else if (token_fits && M <= (p.mxfp4 ? kTokenAutoMaxMMxfp4 : kTokenAutoMaxM))
     p.mode = kModeToken;
   else
     p.mode = (fits && M <= kDecodeAutoMaxM) ? kModeDecode : kModeGeneral;

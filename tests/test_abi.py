@@ -229,6 +229,8 @@ def test_mxfp4_layer_host_checks():
     # a few tokens take the few-token kernels in their MXFP4 form, forced or by default
     token = ["token_gate_up_swiglu_mxfp4", "token_down_reduce_mxfp4"]
     assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == token
+    assert bfp8.fused_moe_stages(8, 7168, 8, 256, 256, o) == token
+    assert bfp8.fused_moe_stages(9, 7168, 8, 256, 256, o)[0] == "route_prepare_quant"  # the general path from 9
     assert bfp8.fused_moe_stages(20, 2048, 8, 64, 512, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4,
                                                                   flags=bfp8.FLAG_LAYER_TOKEN)) == token
     assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4,
