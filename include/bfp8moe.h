@@ -132,7 +132,9 @@ typedef struct {
  * CHANNEL: one fp32 scale per weight row (w13_scale [L, 2I], w2_scale [L, H])
  *          and one per activation row, dynamic or static -- the W8A8 variant
  *          [P2 Reviewed changes: w8a8.py, the static FP8 MoE backend].  Runs
- *          the general path (six launches); H and I at most 8192.
+ *          the few-token path (two launches; stages
+ *          "token_gate_up_swiglu_channel", "token_down_reduce_channel") or the
+ *          general path (six launches); H and I at most 8192.
  * MXFP4:   weights in OCP MX FP4 -- E2M1 elements two to a byte (the even
  *          element of a pair in the low nibble) with one E8M0 scale byte per 32
  *          along K (w13 [L, 2I, H/2] with w13_scale [L, 2I, H/32] bytes, w2
@@ -140,7 +142,10 @@ typedef struct {
  *          [P2 Reviewed changes: v4_fp4_grouped_gemm.py, v4_swiglu_quant.py;
  *          P3 Matched GLM serving A/B: MXFP4 the DeepSeek-V4 checkpoint's
  *          weight format].  Called through fused_moe_mxfp4 (byte scales); runs
- *          the general path; H and I multiples of 256. */
+ *          the few-token path (up to 8 tokens by default, I 256 or 512; stages
+ *          "token_gate_up_swiglu_mxfp4", "token_down_reduce_mxfp4") or the
+ *          general path; H and I multiples of 256.  Neither variant takes the
+ *          small-batch path. */
 typedef enum {
     BFP8MOE_WEIGHT_SCALE_BLOCK = 0,
     BFP8MOE_WEIGHT_SCALE_CHANNEL = 1,
@@ -160,7 +165,10 @@ const char* bfp8moe_last_error(void);
 /* Fault bits of the kernels' bounded waits on the current device, accumulated
  * since the last clear: bit 0 is set when a column wave of the few-token
  * gate/up kernel ran out of its bounded wait for the quantised hidden row (the
- * kernel then ends normally, but that column of that call is unspecified).
+ * kernel then ends normally, but that column of that call is unspecified);
+ * bit 1 when, in that kernel's W8A8 form, a hidden-row wave ran out of its
+ * wait for the other hidden-row waves' maxima (the row's scale of that call is
+ * then unspecified).
  * flags: host pointer.  clear != 0 resets them afterwards.  A debugging and
  * testing query: it synchronises with the device (it copies one word), so it
  * is not for use inside stream capture or a latency-critical loop. */
