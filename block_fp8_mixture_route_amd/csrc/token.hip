@@ -484,16 +484,16 @@ __global__ __launch_bounds__(kUpThreads) void token_gate_up_kernel(
     const int kob = 1024 * c + 16 * lane;    // byte offset in the row: past it only in the last chunk,
     const int kof = kMx ? 2 * kob : kob;     // whose terms are dropped; kof: first element
     const int ka = min(kof, H - (kMx ? 32 : 16));  // in range for the dropped lanes' LDS reads
-    const float as = s_as[ka / 128];
     float pg, pu;
     if constexpr (kMx) {
+      const float as = s_as[ka / 128];
       pg = dot32_fp4_row(wg[c], s_ah, ka / 2) * (as * e8m0_f32(sg[c]));
       pu = dot32_fp4_row(wu[c], s_ah, ka / 2) * (as * e8m0_f32(su[c]));
     } else if constexpr (kCh) {
-      pg = dot16_row(wg[c], s_ah, ka / 2);  // one scale for the row: applied to the sum
+      pg = dot16_row(wg[c], s_ah, ka / 2);  // one scale for the row: applied to the sum below
       pu = dot16_row(wu[c], s_ah, ka / 2);
-      (void)as;
     } else {
+      const float as = s_as[ka / 128];
       pg = dot16_row(wg[c], s_ah, ka / 2) * (as * s_tab[ka / 128]);
       pu = dot16_row(wu[c], s_ah, ka / 2) * (as * s_tab[G + ka / 128]);
     }
