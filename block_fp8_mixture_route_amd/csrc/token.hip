@@ -133,11 +133,12 @@ __device__ __forceinline__ void quant_store8(const float (&f)[8], float sc, h2* 
   dst[0] = a; dst[1] = b; dst[2] = c; dst[3] = d;
 }
 
-// The gate/up kernel's hidden row in LDS: FP16 pair i (elements 2 i, 2 i + 1)
-// is stored at act_swz(i).  The 16-byte units (4 pairs) of each run of 16 are
-// permuted by XOR with the run's index, so that the column waves' reads (lane
-// l reading the 8 or 16 pairs of its 16 or 32 consecutive elements) spread a
-// 16-lane pass over all banks instead of a quarter or a sixteenth of them.
+// Activation rows in LDS (the gate/up kernel's hidden row, the down kernel's
+// SwiGLU rows): FP16 pair i (elements 2 i, 2 i + 1) is stored at act_swz(i).
+// The 16-byte units (4 pairs) of each run of 16 are permuted by XOR with the
+// run's index, so that reads where lane l takes the 8 or 16 pairs of its 16 or
+// 32 consecutive elements spread a 16-lane pass over all banks instead of a
+// half, a quarter or a sixteenth of them.
 __device__ __forceinline__ int act_swz(int i) { return i ^ (((i >> 6) & 15) << 2); }
 
 // Four FP16 pairs (one 16-byte unit) of the swizzled hidden row from pair i
@@ -151,10 +152,10 @@ __device__ __forceinline__ void act_unit(const h2* row, int i, h2 (&a)[4]) {
 }
 
 // sum_i dec(w_i) * a_i over 16 E4M3 weights (one 16-byte load) and 16 E4M3
-// activations held as FP16 pairs in LDS: at p (16-byte aligned, contiguous),
-// or at pairs i .. i + 7 of the swizzled hidden row (dot16_row).  Weight
-// bytes are widened to FP16 pairs (exact), and each v_dot2 product of two
-// E4M3 values is exact in FP32; only the FP32 additions round.  Two chains.
+// activations held as FP16 pairs in LDS: pairs i .. i + 7 of a row stored
+// with act_swz (dot16_row).  Weight bytes are widened to FP16 pairs (exact),
+// and each v_dot2 product of two E4M3 values is exact in FP32; only the FP32
+// additions round.  Two chains.
 __device__ __forceinline__ float dot16_pairs(const uint4& w, h2 a0, h2 a1, h2 a2, h2 a3, h2 a4, h2 a5, h2 a6,
                                              h2 a7) {
   float s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.x, 1.0f, false), a0, 0.0f, false);
@@ -167,9 +168,6 @@ __device__ __forceinline__ float dot16_pairs(const uint4& w, h2 a0, h2 a1, h2 a2
   s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w.w, 1.0f, true), a7, s1, false);
   return s0 + s1;
 }
-__device__ __forceinline__ float dot16(const uint4& w, const h2* q) {
-  return dot16_pairs(w, q[0], q[1], q[2], q[3], q[4], q[5], q[6], q[7]);
-}
 __device__ __forceinline__ float dot16_row(const uint4& w, const h2* row, int i) {
   h2 a[4], b[4];
   act_unit(row, i, a);
@@ -179,25 +177,15 @@ __device__ __forceinline__ float dot16_row(const uint4& w, const h2* row, int i)
 
 // sum_i dec(w_i) * a_i over 32 E2M1 weights (one 16-byte load, two to a
 // byte, the even element in the low nibble) and 32 E4M3 activations held as
-// FP16 pairs in LDS: at p (16-byte aligned, contiguous), or at pairs i .. i +
-// 15 of the swizzled hidden row (dot32_fp4_row).  Each weight byte widens to
-// an FP16 pair (exact, unit scale), each v_dot2 product is exact in FP32; only
-// the FP32 additions round.  Two chains.
+// FP16 pairs in LDS: pairs i .. i + 15 of a row stored with act_swz
+// (dot32_fp4_row).  Each weight byte widens to an FP16 pair (exact, unit
+// scale), each v_dot2 product is exact in FP32; only the FP32 additions round.
+// Two chains.
 __device__ __forceinline__ void dot32_fp4_unit(uint32_t wd, const h2 (&a)[4], float& s0, float& s1) {
   s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 0), a[0], s0, false);
   s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 1), a[1], s1, false);
   s0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 2), a[2], s0, false);
   s1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 3), a[3], s1, false);
-}
-__device__ __forceinline__ float dot32_fp4(const uint4& w, const h2* p) {
-  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-  float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-  for (int d = 0; d < 4; d++) {
-    const h2 a[4] = {p[4 * d], p[4 * d + 1], p[4 * d + 2], p[4 * d + 3]};
-    dot32_fp4_unit(wd[d], a, s0, s1);
-  }
-  return s0 + s1;
 }
 __device__ __forceinline__ float dot32_fp4_row(const uint4& w, const h2* row, int i) {
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
@@ -540,7 +528,8 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
   const float* __restrict__ w2_s = static_cast<const float*>(w2_sv);
   const uint8_t* __restrict__ w2_mx = static_cast<const uint8_t*>(w2_sv);
   constexpr int kActLoads = (KMAX * GI + kDownWaves - 1) / kDownWaves;  // SwiGLU groups per wave
-  __shared__ __align__(16) h2 s_qh[KMAX][I / 2];  // quantised SwiGLU rows (E4M3 values as FP16)
+  __shared__ __align__(16) h2 s_qh[KMAX][I / 2];  // quantised SwiGLU rows (E4M3 values as FP16), each
+                                                 // swizzled as the gate/up kernel's hidden row (act_swz)
   __shared__ float s_qs[KMAX][GI];                // their group scales
   __shared__ float s_y[KMAX][kMaxDownRows];       // down outputs per route (BF16 values)
 
@@ -637,7 +626,7 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
       } else {
         sc = group_scale(group_max<64>(fmaxf(fabsf(a0), fabsf(a1))), fmt);
       }
-      s_qh[jq][g * 64 + lane] = quant2(a0, a1, sc, kCh && q_static > 0.0f);
+      s_qh[jq][act_swz(g * 64 + lane)] = quant2(a0, a1, sc, kCh && q_static > 0.0f);
       if (lane == 0) s_qs[jq][g] = sc;
     }
   }
@@ -652,9 +641,9 @@ __global__ __launch_bounds__(kDownThreads) void token_down_kernel(
     const int u = min(wave + kDownWaves * i, n_units - 1);
     const int j = (int)(((uint32_t)u * dl_magic) >> 16);
     if constexpr (kMx)
-      v[i] = dot32_fp4(wb[i], &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * wsc[i]);
+      v[i] = dot32_fp4_row(wb[i], s_qh[j], kof / 2) * (s_qs[j][kof / 128] * wsc[i]);
     else
-      v[i] = dot16(wb[i], &s_qh[j][kof / 2]) * (s_qs[j][kof / 128] * wsc[i]);
+      v[i] = dot16_row(wb[i], s_qh[j], kof / 2) * (s_qs[j][kof / 128] * wsc[i]);
   }
 #pragma unroll
   for (int i = 0; i < kUpw; i++) v[i] = group_sum<kLpr>(v[i]);
