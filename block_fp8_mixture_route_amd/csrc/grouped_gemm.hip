@@ -43,6 +43,22 @@ constexpr int kXcd = 8;       // MI355X: workgroups are dealt round-robin to 8 X
 // tile through one XCD's L2 (a chunk; see the kernel).
 constexpr int kChunkBlocks = 8;
 
+// Dynamic LDS of the staged scales (grouped_gemm_kernel with kStage): BM
+// rows of G + 1 activation scales and G weight scales, G = K / 128.  Staged
+// from kStageMinGroups K steps (with fewer, the staging's own round trip
+// costs more than the per-step loads it saves: measured) up to
+// kStageMaxBytes (K up to 15,360 at 32 routes per block, 7,936 at 64), so
+// that the workgroup's LDS stays well inside the 64 KB a launch gets.
+constexpr int kStageMinGroups = 4;
+constexpr size_t kStageMaxBytes = 16384;
+inline size_t gemm_stage_bytes(int bm, int K) {
+  const size_t G = (size_t)K / kGroup;
+  return ((size_t)bm * (G + 1) + G) * sizeof(float);
+}
+inline bool gemm_stages(int bm, int K) {
+  return K / kGroup >= kStageMinGroups && gemm_stage_bytes(bm, K) <= kStageMaxBytes;
+}
+
 // Workgroups per XCD for at most max_blocks route blocks of n_tiles tiles
 // each: an XCD's range holds at most ceil(max_blocks / 8) blocks (workgroups
 // past the range in use return at once).
@@ -62,28 +78,42 @@ inline int64_t gemm_slots_per_xcd(int64_t max_blocks, int n_tiles) {
 // chunk's activation rows stay in L2 across its tiles.  Item s of the XCD
 // lies in the chunk of block gq = lo + s / n_tiles (the chunk's items fill
 // slots n_tiles (c0 - lo) .. n_tiles (c1 - lo) - 1).  Returns false for a
-// workgroup past the work in use; else its block and weight tile.
+// workgroup past the work in use; else its weight tile nt and its block: the
+// block's expert e, first position start in sorted_routes and route count
+// len.  Block i of an expert starts at its segment start + i BM (the layout
+// route preparation writes), so the block's own entries are not read again:
+// the chain of dependent loads before the first weight load is the block
+// count, then gq's expert and start, then that expert's segment bounds.
 template <int BM>
 __device__ __forceinline__ bool gemm_work(int n_tiles, const int32_t* __restrict__ expert_offsets,
                                           const int32_t* __restrict__ block_expert,
                                           const int32_t* __restrict__ block_start,
-                                          const int32_t* __restrict__ num_blocks, int64_t& blk, int& nt) {
-  const int x = blockIdx.x % kXcd;
-  const int64_t slot = blockIdx.x / kXcd;
+                                          const int32_t* __restrict__ num_blocks, int& nt, int& e, int& start,
+                                          int& len) {
+  // 32-bit index arithmetic: block counts are int32 and the grid is below
+  // 2^31 workgroups (64-bit division is a long loop on this target)
+  const unsigned x = blockIdx.x % kXcd;
+  const unsigned slot = blockIdx.x / kXcd;
   const int64_t nb = *num_blocks;
-  const int64_t lo = nb * x / kXcd, hi = nb * (x + 1) / kXcd;
-  if (slot >= (hi - lo) * n_tiles) return false;
-  const int64_t gq = lo + slot / n_tiles;
+  const int lo = (int)(nb * x / kXcd), hi = (int)(nb * (x + 1) / kXcd);
+  if ((int64_t)slot >= (int64_t)(hi - lo) * n_tiles) return false;
+  const int gq = lo + (int)(slot / (unsigned)n_tiles);
   const int eg = block_expert[gq];
+  const int sq = block_start[gq];
   const int off_e = expert_offsets[eg];
-  const int ig = (block_start[gq] - off_e) / BM;                   // gq among its expert's blocks
-  const int nbe = (expert_offsets[eg + 1] - off_e + BM - 1) / BM;  // the expert's blocks
-  const int cq = ig / kChunkBlocks * kChunkBlocks;                 // chunk's first, in the expert
-  const int64_t c0 = max(gq - ig + cq, lo);
-  const int64_t c1 = min(gq - ig + min(cq + kChunkBlocks, nbe), hi);
-  const int64_t r = slot - (c0 - lo) * n_tiles;
-  nt = (int)(r / (c1 - c0));
-  blk = c0 + r % (c1 - c0);
+  const int end_e = expert_offsets[eg + 1];
+  const int ig = (sq - off_e) / BM;                        // gq among its expert's blocks
+  const int nbe = (end_e - off_e + BM - 1) / BM;           // the expert's blocks
+  const int cq = ig / kChunkBlocks * kChunkBlocks;         // chunk's first, in the expert
+  const int c0 = max(gq - ig + cq, lo);
+  const int c1 = min(gq - ig + min(cq + kChunkBlocks, nbe), hi);
+  const unsigned r = slot - (unsigned)(c0 - lo) * (unsigned)n_tiles;
+  const unsigned span = (unsigned)(c1 - c0);
+  nt = (int)(r / span);
+  const int blk = c0 + (int)(r % span);
+  e = eg;
+  start = off_e + (ig + blk - gq) * BM;
+  len = min(BM, end_e - start);
   return true;
 }
 
@@ -102,25 +132,37 @@ struct XRegs<false, XL, CT> {
 // kChannel (the W8A8 variant): As holds one scale per activation row and Bs
 // one per weight row (output channel); the K loop adds the chunks' sums
 // unscaled and the epilogue applies a_scale(route) * w_scale(row).
-template <int BM, bool kChannel>
+// kStage: the block's activation scales and the tile's weight scales are
+// staged in LDS once (dynamic LDS of gemm_stage_bytes) instead of loaded per
+// K step: a step's activation-scale loads touch one line per route, as many
+// line requests as the weight chunk itself.
+template <int BM, bool kChannel, bool kStage>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 64 ? 3 : 1))) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, int a_row_div, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, int N, int K, const int32_t* __restrict__ sorted_routes,
     const int32_t* __restrict__ expert_offsets, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ block_start, const int32_t* __restrict__ num_blocks, uint16_t* __restrict__ C) {
-  constexpr int CT = BM / 16;  // route tiles
+  constexpr int CT = BM / 16;                // route tiles
+  constexpr int kAhead = BM <= 32 ? 2 : 1;   // K chunks in flight
   const int n_tiles = N / kBN;
-  int64_t blk;
-  int nt;
-  if (!gemm_work<BM>(n_tiles, expert_offsets, block_expert, block_start, num_blocks, blk, nt)) return;
-  const int e = block_expert[blk];
-  const int start = block_start[blk];
-  const int end_e = expert_offsets[e + 1];
-  const int len = min(BM, end_e - start);
+  int nt, e, start, len;
+  if (!gemm_work<BM>(n_tiles, expert_offsets, block_expert, block_start, num_blocks, nt, e, start, len)) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kq = lane >> 4;
   const int G = K / kGroup;
+
+  // weight rows of this lane, and the first chunk's weight loads: they need
+  // only the expert and the tile, so they leave before the route loads
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int n0 = nt * kBN + wave * kWN;
+  const uint8_t* wrow0 = B + ((size_t)e * N + n0) * K;  // the wave's first weight row
+  const float* ws = kChannel ? Bs + (size_t)e * N + n0 : Bs + ((size_t)e * n_tiles + nt) * G;
+  const uint8_t* wl = wrow0 + (size_t)(lane >> 3) * K + 16 * (lane & 7);  // load i adds 8 i rows
+  u32x4 w0[4], w1[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) w0[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * K);
+  float ws0 = kChannel || kStage ? 1.0f : ws[0], ws1 = 0.0f;
 
   // The activation chunks of blocks of 32 or 64 routes go through a buffer
   // shared by the workgroup; with 16 routes each wave loads its fragments
@@ -131,32 +173,79 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
   const uint8_t* arow[CT];
   const float* asrow[CT];
   int route[CT];
-#pragma unroll
-  for (int t = 0; t < CT; t++) {
-    const int j = t * 16 + col;
-    route[t] = j < len ? sorted_routes[start + j] : -1;
-    const int64_t ar = route[t] >= 0 ? route[t] / a_row_div : 0;
-    arow[t] = A + (size_t)ar * K;
-    asrow[t] = As + (size_t)ar * (kChannel ? 1 : G);
-  }
   // shared path: the activation rows this thread loads, row tid / 8 + 32 x
   // of the block, bytes 16 (tid % 8) .. + 15 of each chunk (full 128-byte
   // lines; a row without a route reads activation row 0, and its columns are
   // never stored)
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   constexpr int XL = kSharedX ? BM * 8 / kThreads : 1;  // 16-byte activation loads per thread
   const int tid = threadIdx.x;
+  // Every route load is unconditional (position start + 0 stands in for a
+  // column past the block's routes) and all leave before the first is used.
+  int sr[CT], sx[XL];
+#pragma unroll
+  for (int t = 0; t < CT; t++) {
+    const int j = t * 16 + col;
+    sr[t] = sorted_routes[start + (j < len ? j : 0)];
+  }
+#pragma unroll
+  for (int x = 0; x < XL; x++) {
+    const int r = kSharedX ? (tid >> 3) + 32 * x : 0;
+    sx[x] = sorted_routes[start + (r < len ? r : 0)];
+  }
+#pragma unroll
+  for (int t = 0; t < CT; t++) {
+    route[t] = t * 16 + col < len ? sr[t] : -1;
+    const int64_t ar = route[t] >= 0 ? route[t] / a_row_div : 0;
+    arow[t] = A + (size_t)ar * K;
+    asrow[t] = As + (size_t)ar * (kChannel ? 1 : G);
+  }
   const uint8_t* xrow[XL];
 #pragma unroll
   for (int x = 0; x < XL; x++) {
     const int r = kSharedX ? (tid >> 3) + 32 * x : 0;
-    const int rt = r < len ? sorted_routes[start + r] : -1;
+    const int rt = r < len ? sx[x] : -1;
     xrow[x] = A + (size_t)(rt >= 0 ? rt / a_row_div : 0) * K + 16 * (tid & 7);
   }
-  // weight rows of this lane
-  const int n0 = nt * kBN + wave * kWN;
-  const uint8_t* wrow0 = B + ((size_t)e * N + n0) * K;  // the wave's first weight row
-  const float* ws = kChannel ? Bs + (size_t)e * N + n0 : Bs + ((size_t)e * n_tiles + nt) * G;
+
+  // Staged scales: s_as[j * (G + 1) + g] for block row j (0 without a route;
+  // the stride G + 1 keeps the 16 rows of one read in distinct banks), then
+  // s_ws[g].  Wave w writes rows w BM/4 .. (w + 1) BM/4 - 1 and wave 0 the
+  // weight scales; each lane takes items lane + 64 i (row, group) of its
+  // wave's rows, so one load instruction reads whole scale rows, and gets
+  // the row's route from the lane that holds it.  The first step's barrier
+  // (or, with no shared activation buffer, the one below) makes them whole.
+  extern __shared__ float s_dyn[];
+  float* s_as = s_dyn;
+  float* s_ws = s_dyn + BM * (G + 1);
+  if constexpr (kStage) {
+    constexpr int kRW = BM / 4;  // rows per wave
+    const int n_items = kRW * G;
+    for (int b = 0; b < n_items; b += 64 * 8) {
+      float v[8];
+      int dst[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int it = b + lane + 64 * i;
+        const int jw = min(it / G, kRW - 1), g = it - (it / G) * G;
+        const int j = wave * kRW + jw;
+        int rj = -1;
+#pragma unroll
+        for (int t = 0; t < CT; t++) {
+          const int v_t = __shfl(route[t], j & 15);
+          if ((j >> 4) == t) rj = v_t;
+        }
+        const bool ok = it < n_items && rj >= 0;
+        v[i] = ok ? As[(size_t)(rj / a_row_div) * G + g] : 0.0f;
+        dst[i] = it < n_items ? j * (G + 1) + g : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        if (dst[i] >= 0) s_as[dst[i]] = v[i];
+    }
+    if (wave == 0)
+      for (int g = lane; g < G; g += 64) s_ws[g] = ws[g];
+    if constexpr (!kSharedX) __syncthreads();
+  }
 
   v4f acc[kRT][CT];
 #pragma unroll
@@ -183,16 +272,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
   __shared__ __align__(16) u32x4 s_w[kThreads / 64][kWN * 8];
   __shared__ __align__(16) u32x4 s_x[2][kSharedX ? BM * 8 : 1];
   u32x4* sw = s_w[wave];
-  const uint8_t* wl = wrow0 + (size_t)(lane >> 3) * K + 16 * (lane & 7);  // load i adds 8 i rows
 
-  // One K step: request chunk gn into (wn, xn, sn, wsn), then multiply the
-  // chunk held in (wc, xc, sc, wsc) through shared buffer xb.  Two register
-  // sets alternate, so nothing is copied.  Every load is unconditional and
-  // the next chunk's loads are all issued before the current chunk is used,
-  // so the wait before the multiply covers the current chunk only.
-  auto step = [&](int gn, u32x4 (&wc)[4], auto& xc, float (&sc)[CT], float wsc, u32x4 (&wn)[4], auto& xn,
-                  float (&sn)[CT], float& wsn, u32x4* xb) __attribute__((always_inline)) {
-    if constexpr (!kChannel) {
+  // The K loop keeps kAhead chunks in flight: chunk c is multiplied from
+  // register set c % (kAhead + 1) while the loads of the next kAhead chunks
+  // are out (a workgroup's step is bound by the round trip of its loads, not
+  // by the memory system's rate, so a deeper queue per wave streams faster;
+  // blocks of 64 routes keep one chunk ahead, for registers).  fetch
+  // requests chunk gn into (wn, xn, sn, wsn); use multiplies the chunk held
+  // in (wc, xc, sc, wsc) through shared buffer xb.  The sets rotate, so
+  // nothing is copied, and every load is issued before the chunk kAhead
+  // steps older is used, so the wait before a multiply covers that chunk.
+  auto fetch = [&](int gn, u32x4 (&wn)[4], auto& xn, float (&sn)[CT], float& wsn) __attribute__((always_inline)) {
+    if constexpr (!kChannel && !kStage) {
       wsn = ws[gn];
 #pragma unroll
       for (int t = 0; t < CT; t++) sn[t] = asrow[t][gn];
@@ -206,7 +297,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
 #pragma unroll
       for (int t = 0; t < CT; t++) xn[t] = load_frag(arow[t] + (size_t)gn * kGroup, kq);
     }
-    __builtin_amdgcn_sched_barrier(0);  // the loads leave before anything waits
+  };
+  auto use = [&](int gc, u32x4 (&wc)[4], auto& xc, float (&sc)[CT], float wsc, u32x4* xb) __attribute__((always_inline)) {
     if constexpr (kSharedX) {
 #pragma unroll
       for (int x = 0; x < XL; x++) {
@@ -246,7 +338,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
       } else {
         xf = xc[t];
       }
-      const float asc = route[t] >= 0 ? (kChannel ? 1.0f : sc[t] * wsc) : 0.0f;
+      float asc;
+      if constexpr (kChannel)
+        asc = route[t] >= 0 ? 1.0f : 0.0f;
+      else if constexpr (kStage)
+        asc = s_as[(16 * t + col) * (G + 1) + gc] * s_ws[gc];
+      else
+        asc = route[t] >= 0 ? sc[t] * wsc : 0.0f;
 #pragma unroll
       for (int i = 0; i < kRT; i++) {
         const v4f p = mfma_f8_16x16x128(wa[i], xf, v4f{0.f, 0.f, 0.f, 0.f});
@@ -257,14 +355,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
   };
 
   typedef typename XRegs<kSharedX, XL, CT>::type XR;
-  u32x4 w0[4], w1[4];
   XR x0, x1;
   float s0[CT], s1[CT];
-  float ws0 = kChannel ? 1.0f : ws[0], ws1 = 0.0f;
 #pragma unroll
-  for (int t = 0; t < CT; t++) s0[t] = kChannel ? 1.0f : asrow[t][0];
-#pragma unroll
-  for (int i = 0; i < 4; i++) w0[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * K);
+  for (int t = 0; t < CT; t++) s0[t] = kChannel || kStage ? 1.0f : asrow[t][0];
   if constexpr (kSharedX) {
 #pragma unroll
     for (int x = 0; x < XL; x++) x0[x] = *reinterpret_cast<const u32x4*>(xrow[x]);
@@ -272,16 +366,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
 #pragma unroll
     for (int t = 0; t < CT; t++) x0[t] = load_frag(arow[t], kq);
   }
-  // both steps of an iteration run unconditionally (a step in a branch would
-  // have its loads moved into that branch, after the other step's wait); an
-  // odd chunk count ends with one more step.  The last step's request
-  // repeats the last chunk (cache hits, unused).
+  // The steps of an iteration run unconditionally (a fetch in a branch would
+  // be moved into that branch, after the other steps' waits); requests past
+  // the last chunk repeat it (cache hits, unused), and the chunks left after
+  // the loop are already in their sets.  Chunk c goes through shared buffer
+  // c % 2.
   int g = 0;
-  for (; g + 1 < G; g += 2) {
-    step(g + 1, w0, x0, s0, ws0, w1, x1, s1, ws1, s_x[0]);
-    step(min(g + 2, G - 1), w1, x1, s1, ws1, w0, x0, s0, ws0, s_x[1]);
+  if constexpr (kAhead == 2) {
+    u32x4 w2[4];
+    XR x2;
+    float s2[CT], ws2 = 0.0f;
+    fetch(min(1, G - 1), w1, x1, s1, ws1);
+    for (; g + 2 < G; g += 3) {
+      fetch(g + 2, w2, x2, s2, ws2);
+      __builtin_amdgcn_sched_barrier(0);  // the loads leave before anything waits
+      use(g, w0, x0, s0, ws0, s_x[g & 1]);
+      fetch(min(g + 3, G - 1), w0, x0, s0, ws0);
+      __builtin_amdgcn_sched_barrier(0);
+      use(g + 1, w1, x1, s1, ws1, s_x[(g + 1) & 1]);
+      fetch(min(g + 4, G - 1), w1, x1, s1, ws1);
+      __builtin_amdgcn_sched_barrier(0);
+      use(g + 2, w2, x2, s2, ws2, s_x[g & 1]);
+    }
+    if (g < G) use(g, w0, x0, s0, ws0, s_x[g & 1]);
+    if (g + 1 < G) use(g + 1, w1, x1, s1, ws1, s_x[(g + 1) & 1]);
+  } else {
+    for (; g + 1 < G; g += 2) {
+      fetch(g + 1, w1, x1, s1, ws1);
+      __builtin_amdgcn_sched_barrier(0);
+      use(g, w0, x0, s0, ws0, s_x[0]);
+      fetch(min(g + 2, G - 1), w0, x0, s0, ws0);
+      __builtin_amdgcn_sched_barrier(0);
+      use(g + 1, w1, x1, s1, ws1, s_x[1]);
+    }
+    if (g < G) use(g, w0, x0, s0, ws0, s_x[0]);
   }
-  if (g < G) step(g, w0, x0, s0, ws0, w1, x1, s1, ws1, s_x[0]);
 
   // epilogue: lane holds rows n0 + 16*i + 4*kq + v (v = 0..3) of route[t]
   if constexpr (kChannel) {
@@ -340,45 +459,60 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
   constexpr int XL = BM * 16 / kThreads;   // 16-byte activation pieces per thread per chunk
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const int n_tiles = N / kBN;
-  int64_t blk;
-  int nt;
-  if (!gemm_work<BM>(n_tiles, expert_offsets, block_expert, block_start, num_blocks, blk, nt)) return;
-  const int e = block_expert[blk];
-  const int start = block_start[blk];
-  const int len = min(BM, expert_offsets[e + 1] - start);
+  int nt, e, start, len;
+  if (!gemm_work<BM>(n_tiles, expert_offsets, block_expert, block_start, num_blocks, nt, e, start, len)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, kq = lane >> 4;
   const int G = K / kGroup, KB = K / 2, NS = K / 32;  // groups, packed row bytes, scale bytes per row
   const int nch = K / 256;                            // K chunks
 
-  // the routes of this lane's MFMA columns and their activation-scale rows
-  const float* asrow[CT];
-  int route[CT];
-#pragma unroll
-  for (int t = 0; t < CT; t++) {
-    const int j = t * 16 + col;
-    route[t] = j < len ? sorted_routes[start + j] : -1;
-    asrow[t] = As + (size_t)(route[t] >= 0 ? route[t] / a_row_div : 0) * G;
-  }
-  // activation pieces this thread loads: piece q = tid + 256 x of the
-  // block's BM x 16, row q / 16, global piece q % 16 (a row without a route
-  // reads activation row 0; its columns are never stored)
-  const uint8_t* xrow[XL];
-#pragma unroll
-  for (int x = 0; x < XL; x++) {
-    const int q = tid + kThreads * x, r = q >> 4;
-    const int rt = r < len ? sorted_routes[start + r] : -1;
-    xrow[x] = A + (size_t)(rt >= 0 ? rt / a_row_div : 0) * K + 16 * (q & 15);
-  }
   // weight rows: load i of a lane reads row 8 i + lane / 8 of the wave's 32,
   // bytes 16 (lane % 8) .. + 15 of the chunk's line; the scale bytes of the
-  // lane's fragment rows 16 i + col
+  // lane's fragment rows 16 i + col.  The first chunk's weight loads leave
+  // before the route loads (they need only the expert and the tile).
   const int n0 = nt * kBN + wave * kWN;
   const uint8_t* wl = B + ((size_t)e * N + n0 + (lane >> 3)) * KB + 16 * (lane & 7);
   const uint8_t* wsr[kRT];
 #pragma unroll
   for (int i = 0; i < kRT; i++) wsr[i] = Bs + ((size_t)e * N + n0 + 16 * i + col) * NS;
+  u32x4 w0[4], w1[4];
+  uint2 b0[kRT], b1[kRT];
+#pragma unroll
+  for (int i = 0; i < 4; i++) w0[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * KB);
+#pragma unroll
+  for (int i = 0; i < kRT; i++) b0[i] = *reinterpret_cast<const uint2*>(wsr[i]);
+
+  // the routes of this lane's MFMA columns and their activation-scale rows,
+  // and the activation pieces this thread loads: piece q = tid + 256 x of
+  // the block's BM x 16, row q / 16, global piece q % 16 (a row without a
+  // route reads activation row 0; its columns are never stored).  Route
+  // loads are unconditional and all leave first, as in grouped_gemm_kernel.
+  int sr[CT], sx[XL];
+#pragma unroll
+  for (int t = 0; t < CT; t++) {
+    const int j = t * 16 + col;
+    sr[t] = sorted_routes[start + (j < len ? j : 0)];
+  }
+#pragma unroll
+  for (int x = 0; x < XL; x++) {
+    const int r = (tid + kThreads * x) >> 4;
+    sx[x] = sorted_routes[start + (r < len ? r : 0)];
+  }
+  const float* asrow[CT];
+  int route[CT];
+#pragma unroll
+  for (int t = 0; t < CT; t++) {
+    route[t] = t * 16 + col < len ? sr[t] : -1;
+    asrow[t] = As + (size_t)(route[t] >= 0 ? route[t] / a_row_div : 0) * G;
+  }
+  const uint8_t* xrow[XL];
+#pragma unroll
+  for (int x = 0; x < XL; x++) {
+    const int q = tid + kThreads * x, r = q >> 4;
+    const int rt = r < len ? sx[x] : -1;
+    xrow[x] = A + (size_t)(rt >= 0 ? rt / a_row_div : 0) * K + 16 * (q & 15);
+  }
 
   v4f acc[kRT][CT];
 #pragma unroll
@@ -455,18 +589,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
     }
   };
 
-  u32x4 w0[4], w1[4], x0[XL], x1[XL];
+  u32x4 x0[XL], x1[XL];
   float s0[CT][2], s1[CT][2];
-  uint2 b0[kRT], b1[kRT];
 #pragma unroll
   for (int t = 0; t < CT; t++) {
     s0[t][0] = asrow[t][0];
     s0[t][1] = asrow[t][1];
   }
-#pragma unroll
-  for (int i = 0; i < kRT; i++) b0[i] = *reinterpret_cast<const uint2*>(wsr[i]);
-#pragma unroll
-  for (int i = 0; i < 4; i++) w0[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * KB);
 #pragma unroll
   for (int x = 0; x < XL; x++) x0[x] = *reinterpret_cast<const u32x4*>(xrow[x]);
   int c = 0;
@@ -501,16 +630,20 @@ hipError_t launch_grouped_gemm(const uint8_t* A, const float* As, int a_row_div,
   if (max_blocks == 0 || N / kBN == 0) return hipSuccess;
   const int64_t grid = gemm_slots_per_xcd(max_blocks, N / kBN) * kXcd;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-#define BFP8_GEMM_CASE(BMV)                                                                                   \
-  case BMV:                                                                                                   \
-    if (channel)                                                                                              \
-      hipLaunchKernelGGL((grouped_gemm_kernel<BMV, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A, \
-                         As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,     \
-                         num_blocks, C);                                                                     \
-    else                                                                                                      \
-      hipLaunchKernelGGL((grouped_gemm_kernel<BMV, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A, \
-                         As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,     \
-                         num_blocks, C);                                                                     \
+#define BFP8_GEMM_CASE(BMV)                                                                                     \
+  case BMV:                                                                                                     \
+    if (channel)                                                                                                \
+      hipLaunchKernelGGL((grouped_gemm_kernel<BMV, true, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, \
+                         A, As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,    \
+                         num_blocks, C);                                                                       \
+    else if (gemm_stages(BMV, K))                                                                               \
+      hipLaunchKernelGGL((grouped_gemm_kernel<BMV, false, true>), dim3((unsigned)grid), dim3(kThreads),          \
+                         gemm_stage_bytes(BMV, K), stream, A, As, a_row_div, B, Bs, N, K, sorted_routes,          \
+                         expert_offsets, block_expert, block_start, num_blocks, C);                              \
+    else                                                                                                        \
+      hipLaunchKernelGGL((grouped_gemm_kernel<BMV, false, false>), dim3((unsigned)grid), dim3(kThreads), 0,       \
+                         stream, A, As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert,      \
+                         block_start, num_blocks, C);                                                          \
     break;
   switch (block_m) {
     BFP8_GEMM_CASE(16)

@@ -299,7 +299,10 @@ bfp8moe_status_t silu_and_mul_quant_fp8_rows(const uint16_t* gate_up, int64_t ro
  * top-k for the gate/up projection (token rows feed k routes) and 1 for the
  * down projection.  N and K must be positive multiples of 128; block_m one of
  * 16, 32, 64; max_blocks the size of the block arrays; R the number of routes
- * (rows of C). */
+ * (rows of C).  The block arrays must be laid out as moe_route_prepare writes
+ * them for the same block_m: an expert's blocks consecutive, its i-th block
+ * starting at expert_offsets[e] + i * block_m (the kernel derives a block's
+ * start from its expert's segment instead of reading it). */
 bfp8moe_status_t moe_fp8_grouped_gemm(const uint8_t* A, const float* A_scale, int32_t a_row_div,
                                       const uint8_t* B, const float* B_scale, int32_t L, int32_t N, int32_t K,
                                       const int32_t* sorted_routes, const int32_t* expert_offsets,
