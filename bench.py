@@ -490,7 +490,7 @@ SUITE_STEPS = {"tiny": 200, "decode_m1": 480, "decode_m4": 200, "decode_m16": 10
                "small_m128": 20, "small_m512": 20, "large_m2048": 10}
 
 
-def variants_table(hip, stream, dev):
+def variants_table(hip, stream, dev, block_m=0):
     """The layer with each weight format on the general-path configs, one
     instance each (its weights exceed the Infinity Cache several times over),
     graph-timed over 8 calls: block FP8, the W8A8 variant (random E4M3 codes,
@@ -531,14 +531,17 @@ def variants_table(hip, stream, dev):
         out = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
         forms = {
             "block FP8": (lambda: bfp8.fused_moe_block_fp8(hidden, ids, w, W.w13, W.w13_s, W.w2, W.w2_s, E=E, out=out,
-                                                          ws=ws["block FP8"]),
-                          bfp8.opts(), d * (3 * I * H + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)))),
+                                                          ws=ws["block FP8"], o=opts["block FP8"]),
+                          bfp8.opts(block_m=block_m),
+                          d * (3 * I * H + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128)))),
             "W8A8": (lambda: bfp8.fused_moe_block_fp8(hidden, ids, w, c13, s13, c2, s2, E=E, out=out, ws=ws["W8A8"],
                                                      o=opts["W8A8"]),
-                     bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL), d * (3 * I * H + 4 * (2 * I + H))),
+                     bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL, block_m=block_m),
+                     d * (3 * I * H + 4 * (2 * I + H))),
             "MXFP4": (lambda: bfp8.fused_moe_mxfp4(hidden, ids, w, MX.w13, MX.w13_s, MX.w2, MX.w2_s, E=E, out=out,
                                                   ws=ws["MXFP4"], o=opts["MXFP4"]),
-                      bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4), d * (3 * I * H // 2 + 3 * I * H // 32)),
+                      bfp8.opts(weight_scale_mode=bfp8.WEIGHT_MXFP4, block_m=block_m),
+                      d * (3 * I * H // 2 + 3 * I * H // 32)),
         }
         opts = {f: v[1] for f, v in forms.items()}
         ws = {f: torch.empty(max(bfp8.fused_moe_workspace_size(M, H, k, E, I, v[1]), 1), dtype=torch.uint8,
@@ -919,6 +922,8 @@ def main():
     ap.add_argument("--variants-crossover", action="store_true",
                     help="only the decode layer at 4 to 16 tokens per weight format on the few-token and the "
                          "general path (where the automatic choice switches)")
+    ap.add_argument("--variants-general", action="store_true",
+                    help="each weight format on the general-path configs (with --block-m: that block size)")
     ap.add_argument("--phases", action="store_true",
                     help="only the decode layer's phase table: each kernel alone and the layer at five hidden widths, "
                          "fixed cost and streaming rate per kernel fitted, the H=7168 layer split into them")
@@ -961,6 +966,9 @@ def main():
         return
     if args.phases:
         phase_table(hip, stream, dev, args.steps)
+        return
+    if args.variants_general:
+        variants_table(hip, stream, dev, block_m=args.block_m)
         return
     if args.suite:
         res = suite(hip, stream, dev)

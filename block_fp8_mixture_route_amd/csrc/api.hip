@@ -92,13 +92,17 @@ constexpr int64_t kDecodeAutoMaxM = 4;
 constexpr int64_t kTokenAutoMaxMMxfp4 = 8;
 
 // Routes per compact block of the general path, from the routes per local
-// expert on average: 16 below 8, 32 up to 48, 64 above.  Measured: 16 beat
-// 32 at 0.5, 1 and 4 routes per expert (16 and 32 decode-shape tokens, 128
-// small-shape tokens), 32 beat 16 at 16 and 32 (512 small-shape tokens, 2048
-// large-shape tokens), and 64 lost to 32 in all of them.
-int auto_block_m(int64_t R, int32_t L) {
+// expert on average: 16 below 8; then 32, and 64 from 32 routes per expert
+// (MXFP4 weights: above 48).  Measured: 16 beat 32 at 0.5, 1 and 4 routes
+// per expert (16 and 32 decode-shape tokens, 128 small-shape tokens), 32 beat
+// 16 at 16 and 32 (512 small-shape tokens, 2048 large-shape tokens); with the
+// GEMM's scales staged in LDS, 64 beat 32 at 32 routes per expert for block
+// FP8 and W8A8 weights (2048 large-shape tokens: 1,443 against 1,478 us) and
+// lost at 16 (512 small-shape tokens), and the MXFP4 GEMM lost at 64 in all.
+int auto_block_m(int64_t R, int32_t L, int32_t weight_scale_mode) {
   const int64_t per_expert = R / (L > 0 ? L : 1);
-  return per_expert < 8 ? 16 : per_expert <= 48 ? 32 : 64;
+  const int64_t to64 = weight_scale_mode == BFP8MOE_WEIGHT_MXFP4 ? 49 : 32;
+  return per_expert < 8 ? 16 : per_expert < to64 ? 32 : 64;
 }
 
 void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_t I, const bfp8moe_opts_t& o) {
@@ -113,7 +117,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
   p.map = o.expert_map;
   p.fmt = o.scale_fmt;
   p.clamp = o.clamp_limit;
-  p.block_m = o.block_m > 0 ? o.block_m : auto_block_m(p.R, p.L);
+  p.block_m = o.block_m > 0 ? o.block_m : auto_block_m(p.R, p.L, o.weight_scale_mode);
   p.max_blocks = bfp8moe_max_blocks(p.R, p.L, p.block_m);
   p.channel = o.weight_scale_mode == BFP8MOE_WEIGHT_SCALE_CHANNEL;
   p.mxfp4 = o.weight_scale_mode == BFP8MOE_WEIGHT_MXFP4;

@@ -105,8 +105,8 @@ enum {
 /* Options of the fused layer.  Initialise with bfp8moe_opts_init(). */
 typedef struct {
     int32_t block_m;            /* routes per compact block for the general path (16, 32 or 64);
-                                   0 = auto: 16 below 8 routes per local expert, 32 up
-                                   to 48, 64 above */
+                                   0 = auto: 16 below 8 routes per local expert, then 32,
+                                   and 64 from 32 (MXFP4 weights: above 48) */
     int32_t scale_fmt;          /* bfp8moe_scale_fmt_t for both activation quantisations */
     float clamp_limit;          /* SwiGLU clamp; +INFINITY = unclamped [P3 Purpose: finite SwiGLU clamping] */
     int32_t expert_offset;      /* first global expert held locally [P2 Suppressed comments] */
