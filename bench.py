@@ -937,6 +937,11 @@ def main():
               "(the single-table modes --config, --phases, --floor and --router are unaffected; "
               "BFP8MOE_SUITE_ENABLE=1 runs it anyway)", file=sys.stderr)
         sys.exit(3)
+    if args.variants_general and args.block_m not in (32, 64):
+        print("bench.py --variants-general takes --block-m 32 or 64: its run with the automatic block size "
+              "(16 routes per block at small M=128) ended in a GPU memory fault whose cause has not been found",
+              file=sys.stderr)
+        sys.exit(3)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
