@@ -490,7 +490,7 @@ SUITE_STEPS = {"tiny": 200, "decode_m1": 480, "decode_m4": 200, "decode_m16": 10
                "small_m128": 20, "small_m512": 20, "large_m2048": 10}
 
 
-def variants_table(hip, stream, dev, block_m=0):
+def variants_table(hip, stream, dev, block_m=0, configs=("small_m128", "small_m512", "large_m2048"), formats=None):
     """The layer with each weight format on the general-path configs, one
     instance each (its weights exceed the Infinity Cache several times over),
     graph-timed over 8 calls: block FP8, the W8A8 variant (random E4M3 codes,
@@ -507,7 +507,7 @@ def variants_table(hip, stream, dev, block_m=0):
     print("| config | format | µs / layer | compulsory MB | GB/s | HBM roofline µs | fraction |")
     print("|---|---|---|---|---|---|---|")
     res = {}
-    for name in ("small_m128", "small_m512", "large_m2048"):
+    for name in configs:
         case = synth.LAYER_CASES[name]
         M, E, k, H, I = case.M, case.E, case.k, case.H, case.I
         hidden, ids, w, W = synth.layer_inputs(case, 0, device=dev)
@@ -549,6 +549,8 @@ def variants_table(hip, stream, dev, block_m=0):
         res[name] = {}
         ext = torch.cuda.ExternalStream(stream.value, device=dev)
         for f, (fn, _, wbytes) in forms.items():
+            if formats is not None and f not in formats:
+                continue
             with torch.cuda.stream(ext):  # the binding launches on torch's current stream: the timed one
                 fn()
                 hip.sync(stream)
@@ -924,6 +926,10 @@ def main():
                          "general path (where the automatic choice switches)")
     ap.add_argument("--variants-general", action="store_true",
                     help="each weight format on the general-path configs (with --block-m: that block size)")
+    ap.add_argument("--variants-configs", default="small_m128,small_m512,large_m2048",
+                    help="configs of --variants-general, comma-separated")
+    ap.add_argument("--variants-formats", default="block FP8,W8A8,MXFP4",
+                    help="weight formats of --variants-general, comma-separated")
     ap.add_argument("--phases", action="store_true",
                     help="only the decode layer's phase table: each kernel alone and the layer at five hidden widths, "
                          "fixed cost and streaming rate per kernel fitted, the H=7168 layer split into them")
@@ -973,7 +979,8 @@ def main():
         phase_table(hip, stream, dev, args.steps)
         return
     if args.variants_general:
-        variants_table(hip, stream, dev, block_m=args.block_m)
+        variants_table(hip, stream, dev, block_m=args.block_m, configs=args.variants_configs.split(","),
+                       formats=args.variants_formats.split(","))
         return
     if args.suite:
         res = suite(hip, stream, dev)

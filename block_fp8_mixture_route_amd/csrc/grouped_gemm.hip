@@ -117,6 +117,43 @@ __device__ __forceinline__ bool gemm_work(int n_tiles, const int32_t* __restrict
   return true;
 }
 
+// Stages a block's activation scales in LDS: s_as[j * (G + 1) + g] for block
+// row j (0 for a row without a route; the stride G + 1 keeps the 16 rows of
+// one read in distinct banks).  Wave w writes rows w BM/4 .. (w + 1) BM/4 - 1;
+// each lane takes items lane + 64 i (row, group) of its wave's rows, so one
+// load instruction reads whole scale rows, and gets the row's route from the
+// lane of its wave that holds it (route[t] of lane c is row 16 t + c).  The
+// caller's next barrier makes them whole.
+template <int BM>
+__device__ __forceinline__ void stage_act_scales(float* __restrict__ s_as, const float* __restrict__ As,
+                                                 int a_row_div, int G, const int (&route)[BM / 16], int lane,
+                                                 int wave) {
+  constexpr int CT = BM / 16, kRW = BM / 4;  // route tiles, rows per wave
+  const int n_items = kRW * G;
+  for (int b = 0; b < n_items; b += 64 * 8) {
+    float v[8];
+    int dst[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int it = b + lane + 64 * i;
+      const int jw = min(it / G, kRW - 1), g = it - (it / G) * G;
+      const int j = wave * kRW + jw;
+      int rj = -1;
+#pragma unroll
+      for (int t = 0; t < CT; t++) {
+        const int v_t = __shfl(route[t], j & 15);
+        if ((j >> 4) == t) rj = v_t;
+      }
+      const bool ok = it < n_items && rj >= 0;
+      v[i] = ok ? As[(size_t)(rj / a_row_div) * G + g] : 0.0f;
+      dst[i] = it < n_items ? j * (G + 1) + g : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (dst[i] >= 0) s_as[dst[i]] = v[i];
+  }
+}
+
 // Activation registers of one K step: 16-byte line pieces (shared path) or
 // MFMA fragments (direct path).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -207,41 +244,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
     xrow[x] = A + (size_t)(rt >= 0 ? rt / a_row_div : 0) * K + 16 * (tid & 7);
   }
 
-  // Staged scales: s_as[j * (G + 1) + g] for block row j (0 without a route;
-  // the stride G + 1 keeps the 16 rows of one read in distinct banks), then
-  // s_ws[g].  Wave w writes rows w BM/4 .. (w + 1) BM/4 - 1 and wave 0 the
-  // weight scales; each lane takes items lane + 64 i (row, group) of its
-  // wave's rows, so one load instruction reads whole scale rows, and gets
-  // the row's route from the lane that holds it.  The first step's barrier
-  // (or, with no shared activation buffer, the one below) makes them whole.
+  // Staged scales: the block's activation scales (stage_act_scales), then
+  // the tile's weight scales s_ws[g], written by wave 0.  The first step's
+  // barrier (or, with no shared activation buffer, the one below) makes them
+  // whole.
   extern __shared__ float s_dyn[];
   float* s_as = s_dyn;
   float* s_ws = s_dyn + BM * (G + 1);
   if constexpr (kStage) {
-    constexpr int kRW = BM / 4;  // rows per wave
-    const int n_items = kRW * G;
-    for (int b = 0; b < n_items; b += 64 * 8) {
-      float v[8];
-      int dst[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const int it = b + lane + 64 * i;
-        const int jw = min(it / G, kRW - 1), g = it - (it / G) * G;
-        const int j = wave * kRW + jw;
-        int rj = -1;
-#pragma unroll
-        for (int t = 0; t < CT; t++) {
-          const int v_t = __shfl(route[t], j & 15);
-          if ((j >> 4) == t) rj = v_t;
-        }
-        const bool ok = it < n_items && rj >= 0;
-        v[i] = ok ? As[(size_t)(rj / a_row_div) * G + g] : 0.0f;
-        dst[i] = it < n_items ? j * (G + 1) + g : -1;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; i++)
-        if (dst[i] >= 0) s_as[dst[i]] = v[i];
-    }
+    stage_act_scales<BM>(s_as, As, a_row_div, G, route, lane, wave);
     if (wave == 0)
       for (int g = lane; g < G; g += 64) s_ws[g] = ws[g];
     if constexpr (!kSharedX) __syncthreads();
@@ -449,7 +460,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
 // activation scale of group 2 c + h added to the fp32 accumulator.  The
 // activation chunk (BM rows of 256 bytes) goes through a shared LDS buffer,
 // 16-byte piece p of row r stored at p ^ (r & 15).
-template <int BM>
+// kStage: the block's activation scales staged in LDS once (dynamic LDS of
+// gemm_stage_bytes), as in grouped_gemm_kernel.
+template <int BM, bool kStage>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, int a_row_div, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, int N, int K, const int32_t* __restrict__ sorted_routes,
@@ -528,12 +541,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
   // the chunk held in the current one through shared buffer xb (as in
   // grouped_gemm_kernel: two sets alternate, every load unconditional and
   // issued before the current chunk is used).
-  auto step = [&](int cn, u32x4 (&wc)[4], u32x4 (&xc)[XL], float (&sc)[CT][2], uint2 (&bc)[kRT], u32x4 (&wn)[4],
-                  u32x4 (&xn)[XL], float (&sn)[CT][2], uint2 (&bn)[kRT], u32x4* xb) __attribute__((always_inline)) {
+  extern __shared__ float s_dyn[];
+  float* s_as = s_dyn;
+  if constexpr (kStage) stage_act_scales<BM>(s_as, As, a_row_div, G, route, lane, wave);
+
+  auto step = [&](int cn, int cc, u32x4 (&wc)[4], u32x4 (&xc)[XL], float (&sc)[CT][2], uint2 (&bc)[kRT],
+                  u32x4 (&wn)[4], u32x4 (&xn)[XL], float (&sn)[CT][2], uint2 (&bn)[kRT], u32x4* xb)
+      __attribute__((always_inline)) {
+    if constexpr (!kStage) {
 #pragma unroll
-    for (int t = 0; t < CT; t++) {
-      sn[t][0] = asrow[t][2 * cn];
-      sn[t][1] = asrow[t][2 * cn + 1];
+      for (int t = 0; t < CT; t++) {
+        sn[t][0] = asrow[t][2 * cn];
+        sn[t][1] = asrow[t][2 * cn + 1];
+      }
     }
 #pragma unroll
     for (int i = 0; i < kRT; i++) bn[i] = *reinterpret_cast<const uint2*>(wsr[i] + 8 * cn);
@@ -577,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
         const u32x4 lo = xb[r * 16 + ((8 * h + kq) ^ (r & 15))];
         const u32x4 hi = xb[r * 16 + ((8 * h + 4 + kq) ^ (r & 15))];
         const v8i xf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const float asc = route[t] >= 0 ? sc[t][h] : 0.0f;
+        const float asc = kStage ? s_as[(16 * t + col) * (G + 1) + 2 * cc + h] : route[t] >= 0 ? sc[t][h] : 0.0f;
 #pragma unroll
         for (int i = 0; i < kRT; i++) {
           const int e8 = (int)(((h ? bc[i].y : bc[i].x) >> (8 * kq)) & 0xFFu);
@@ -593,17 +613,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
   float s0[CT][2], s1[CT][2];
 #pragma unroll
   for (int t = 0; t < CT; t++) {
-    s0[t][0] = asrow[t][0];
-    s0[t][1] = asrow[t][1];
+    s0[t][0] = kStage ? 1.0f : asrow[t][0];
+    s0[t][1] = kStage ? 1.0f : asrow[t][1];
   }
 #pragma unroll
   for (int x = 0; x < XL; x++) x0[x] = *reinterpret_cast<const u32x4*>(xrow[x]);
   int c = 0;
   for (; c + 1 < nch; c += 2) {
-    step(c + 1, w0, x0, s0, b0, w1, x1, s1, b1, s_x[0]);
-    step(min(c + 2, nch - 1), w1, x1, s1, b1, w0, x0, s0, b0, s_x[1]);
+    step(c + 1, c, w0, x0, s0, b0, w1, x1, s1, b1, s_x[0]);
+    step(min(c + 2, nch - 1), c + 1, w1, x1, s1, b1, w0, x0, s0, b0, s_x[1]);
   }
-  if (c < nch) step(c, w0, x0, s0, b0, w1, x1, s1, b1, s_x[0]);
+  if (c < nch) step(c, c, w0, x0, s0, b0, w1, x1, s1, b1, s_x[0]);
 
   // epilogue: lane holds rows n0 + 16 i + 4 kq + v (v = 0..3) of route[t]
 #pragma unroll
@@ -667,9 +687,14 @@ hipError_t launch_grouped_gemm_mxfp4(const uint8_t* A, const float* As, int a_ro
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
 #define BFP8_MX_CASE(BMV)                                                                                      \
   case BMV:                                                                                                    \
-    hipLaunchKernelGGL((grouped_gemm_mxfp4_kernel<BMV>), dim3((unsigned)grid), dim3(kThreads), 0, stream, A, As, \
-                       a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,        \
-                       num_blocks, C);                                                                       \
+    if (gemm_stages(BMV, K))                                                                                   \
+      hipLaunchKernelGGL((grouped_gemm_mxfp4_kernel<BMV, true>), dim3((unsigned)grid), dim3(kThreads),           \
+                         (size_t)BMV * (K / kGroup + 1) * sizeof(float), stream, A, As, a_row_div, B, Bs, N, K,   \
+                         sorted_routes, expert_offsets, block_expert, block_start, num_blocks, C);               \
+    else                                                                                                       \
+      hipLaunchKernelGGL((grouped_gemm_mxfp4_kernel<BMV, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, \
+                         A, As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,    \
+                         num_blocks, C);                                                                        \
     break;
   switch (block_m) {
     BFP8_MX_CASE(16)
