@@ -75,7 +75,11 @@ def test_gemm_exact_integers(M, E, k, N, K, block_m):
 
 
 @pytest.mark.parametrize("M,E,k,N,K,block_m", [(4, 8, 8, 512, 2048, 16), (64, 16, 8, 1024, 4096, 32),
-                                               (128, 16, 8, 512, 1024, 64)])
+                                               (128, 16, 8, 512, 1024, 64),
+                                               # 1, 3 and 5 chunks of 256 (activation scales staged
+                                               # from 4 groups of 128: not, then staged)
+                                               (8, 8, 4, 256, 256, 32), (8, 8, 4, 256, 768, 16),
+                                               (8, 8, 4, 256, 1280, 64)])
 def test_gemm_random_codes_within_fp32_bound(M, E, k, N, K, block_m):
     print_case("mxfp4 gemm random", M, E, k, N, K, block_m)
     ids, _ = synth.uniform_routing(M, E, k, "mx_rand", M)

@@ -112,6 +112,19 @@ def test_grouped_gemm_down(shape, B):
     assert_gemm_close(got[valid], ref[valid], f"down {shape} B={B}")
 
 
+@pytest.mark.parametrize("B", [16, 32, 64])
+@pytest.mark.parametrize("K", [128, 384, 512, 640, 896, 1152])
+def test_grouped_gemm_k_loop_tails(K, B):
+    # 1, 3, 4, 5, 7 and 9 K chunks: every remainder of the loop that keeps two
+    # chunks in flight (three steps per iteration), and both sides of the
+    # chunk count from which the block scales are staged in LDS
+    print_case("gemm k tails", K, B)
+    got, ref, ids = _gemm_case(8, 4, 8, 256, K, B, seed=K + B)
+    valid = (ids.view(-1) >= 0).numpy()
+    assert (got[~valid] == ref[~valid]).all()
+    assert_gemm_close(got[valid], ref[valid], f"k tails K={K} B={B}")
+
+
 def test_grouped_gemm_hot_expert():
     # one expert takes 200 routes (13 blocks of 16): blocks of one expert in a row
     print_case("gemm hot expert")

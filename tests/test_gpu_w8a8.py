@@ -52,7 +52,10 @@ def test_act_quant_rows_bit_exact(I, fmt, clamp, static):
 
 
 @pytest.mark.parametrize("M,E,k,N,K,block_m", [(1, 256, 8, 512, 7168, 16), (16, 16, 8, 2048, 2048, 32),
-                                               (64, 16, 8, 1024, 768, 64)])
+                                               (64, 16, 8, 1024, 768, 64),
+                                               # 1, 3 and 5 K chunks (the K loop's remainders)
+                                               (8, 8, 4, 256, 128, 16), (8, 8, 4, 256, 384, 64),
+                                               (8, 8, 4, 256, 640, 32)])
 def test_channel_gemm_elementwise(M, E, k, N, K, block_m):
     print_case("channel gemm", M, E, k, N, K, block_m)
     ids, _ = synth.uniform_routing(M, E, k, "w8a8_gemm", M)
