@@ -720,64 +720,20 @@ def torch_unique_count(ids):
     return torch.unique(ids[ids >= 0]).numel()
 
 
-def suite(hip, stream, dev):
-    """Every layer config, the activation+quant workload (fused against two
-    kernels), route preparation (one workgroup against many) and a plain copy
-    as the practical bandwidth ceiling.  Prints markdown tables; returns the
-    figures."""
+def act_quant_tables(hip, stream, dev, res=None):
+    """The fused activation + quantisation on the pages' act+quant workload
+    (rows = tokens x 8, I = 512, clamp 7, UE8M0, ~10 % masked) and under
+    8-way expert parallelism (top-k 6, width 2048, 32 of 256 experts local),
+    graph-timed over 20 calls, against SwiGLU then quant_fp8 as two launches."""
     import torch
 
     import block_fp8_mixture_route_amd as bfp8
     from block_fp8_mixture_route_amd import synth
 
+    res = {} if res is None else res
+    res.setdefault("act_quant", {})
     L_ = bfp8.lib()
     P = ctypes.c_void_p
-    ext = torch.cuda.ExternalStream(stream.value, device=dev)
-    res = {"layers": {}, "act_quant": {}, "route_prep": {}, "copy": {}}
-
-    print("| config | M | E | k | H | I | path | µs / layer | GB/s | roofline µs | fraction | stages µs (each alone) |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
-    runs = [(name, case, 0) for name, case in synth.LAYER_CASES.items()]
-    # the other paths where they apply, forced (the default picks one by M)
-    runs += [(f"{n} (forced)", synth.LAYER_CASES[n], f) for n, f in
-             [("decode_m4", PATH_FLAGS["decode"]), ("decode_m4", PATH_FLAGS["general"]),
-              ("decode_m16", PATH_FLAGS["token"]), ("decode_m32", PATH_FLAGS["token"])]]
-    oracle_insts = {}
-    for name, case, flags in runs:
-        r = measure_layer(case, SUITE_STEPS.get(name.split()[0], 50), 4, 0, hip, stream, dev, flags=flags)
-        insts = r.pop("insts")
-        if not flags:
-            oracle_insts[name] = (case, insts[0], r["us_per_layer"])
-        del insts
-        res["layers"][name + (f" flags {flags}" if flags else "")] = r
-        st = ", ".join(f"{k} {v:.2f}" for k, v in r["stage_us"].items())
-        path = "few tokens" if r["stages"][0].startswith("token") else (
-            "small batch" if r["stages"][0].startswith("decode") else "general")
-        print(f"| {name} | {case.M} | {case.E} | {case.k} | {case.H} | {case.I} | {path} | {r['us_per_layer']:.2f} | "
-              f"{r['gbs']:.0f} | {r['roofline_us']:.2f} | {r['roofline_frac']:.3f} | {st} |", flush=True)
-        torch.cuda.empty_cache()
-
-    # the CPU oracle on instance 0 of every config: one thread and every host
-    # core for the small ones (mean of at least 5 runs and 2 s), every core only for the
-    # configs that take minutes on one (one run)
-    from oracle import oracle as O
-
-    cores = O.num_threads()
-    print()
-    print(f"CPU oracle (host threads available: {cores}), whole layer, instance 0:")
-    print()
-    print("| config | 1 thread s / layer | all threads s / layer (threads) | GPU µs / layer | GPU speedup over all threads |")
-    print("|---|---|---|---|---|")
-    res["oracle"] = {"cores": cores}
-    for name, (case, inst, gpu_us) in oracle_insts.items():
-        big = case.M >= 512
-        t1 = None if big else oracle_layer_seconds(case, inst, 2.0, threads=1, min_runs=1)[0]
-        tn, n, thr = oracle_layer_seconds(case, inst, 0.0 if big else 2.0, threads=cores, min_runs=1 if big else 5)
-        res["oracle"][name] = {"one_thread_s": t1, "all_threads_s": tn, "threads": thr}
-        t1s = "—" if t1 is None else f"{t1:.3f}"
-        print(f"| {name} | {t1s} | {tn:.3f} ({thr}) | {gpu_us:.2f} | {tn * 1e6 / gpu_us:.0f} |", flush=True)
-    oracle_insts.clear()
-    torch.cuda.empty_cache()
 
     # activation + quant (warm, like the pages): fused kernel against SwiGLU
     # then quant_fp8 as two launches
@@ -843,6 +799,69 @@ def suite(hip, stream, dev):
         nbytes = live * (4 * I + I + 4 * (I // 128))
         res["act_quant_ep8"][tok] = {"rows": rows, "local_rows": live, "fused_us": tf, "two_kernel_us": t2}
         print(f"| {tok} | {rows} | {live} | {tf:.2f} | {t2:.2f} | {nbytes / (tf * 1e3):.0f} |", flush=True)
+    return res
+
+
+def suite(hip, stream, dev):
+    """Every layer config, the activation+quant workload (fused against two
+    kernels), route preparation (one workgroup against many) and a plain copy
+    as the practical bandwidth ceiling.  Prints markdown tables; returns the
+    figures."""
+    import torch
+
+    import block_fp8_mixture_route_amd as bfp8
+    from block_fp8_mixture_route_amd import synth
+
+    L_ = bfp8.lib()
+    P = ctypes.c_void_p
+    ext = torch.cuda.ExternalStream(stream.value, device=dev)
+    res = {"layers": {}, "act_quant": {}, "route_prep": {}, "copy": {}}
+
+    print("| config | M | E | k | H | I | path | µs / layer | GB/s | roofline µs | fraction | stages µs (each alone) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    runs = [(name, case, 0) for name, case in synth.LAYER_CASES.items()]
+    # the other paths where they apply, forced (the default picks one by M)
+    runs += [(f"{n} (forced)", synth.LAYER_CASES[n], f) for n, f in
+             [("decode_m4", PATH_FLAGS["decode"]), ("decode_m4", PATH_FLAGS["general"]),
+              ("decode_m16", PATH_FLAGS["token"]), ("decode_m32", PATH_FLAGS["token"])]]
+    oracle_insts = {}
+    for name, case, flags in runs:
+        r = measure_layer(case, SUITE_STEPS.get(name.split()[0], 50), 4, 0, hip, stream, dev, flags=flags)
+        insts = r.pop("insts")
+        if not flags:
+            oracle_insts[name] = (case, insts[0], r["us_per_layer"])
+        del insts
+        res["layers"][name + (f" flags {flags}" if flags else "")] = r
+        st = ", ".join(f"{k} {v:.2f}" for k, v in r["stage_us"].items())
+        path = "few tokens" if r["stages"][0].startswith("token") else (
+            "small batch" if r["stages"][0].startswith("decode") else "general")
+        print(f"| {name} | {case.M} | {case.E} | {case.k} | {case.H} | {case.I} | {path} | {r['us_per_layer']:.2f} | "
+              f"{r['gbs']:.0f} | {r['roofline_us']:.2f} | {r['roofline_frac']:.3f} | {st} |", flush=True)
+        torch.cuda.empty_cache()
+
+    # the CPU oracle on instance 0 of every config: one thread and every host
+    # core for the small ones (mean of at least 5 runs and 2 s), every core only for the
+    # configs that take minutes on one (one run)
+    from oracle import oracle as O
+
+    cores = O.num_threads()
+    print()
+    print(f"CPU oracle (host threads available: {cores}), whole layer, instance 0:")
+    print()
+    print("| config | 1 thread s / layer | all threads s / layer (threads) | GPU µs / layer | GPU speedup over all threads |")
+    print("|---|---|---|---|---|")
+    res["oracle"] = {"cores": cores}
+    for name, (case, inst, gpu_us) in oracle_insts.items():
+        big = case.M >= 512
+        t1 = None if big else oracle_layer_seconds(case, inst, 2.0, threads=1, min_runs=1)[0]
+        tn, n, thr = oracle_layer_seconds(case, inst, 0.0 if big else 2.0, threads=cores, min_runs=1 if big else 5)
+        res["oracle"][name] = {"one_thread_s": t1, "all_threads_s": tn, "threads": thr}
+        t1s = "—" if t1 is None else f"{t1:.3f}"
+        print(f"| {name} | {t1s} | {tn:.3f} ({thr}) | {gpu_us:.2f} | {tn * 1e6 / gpu_us:.0f} |", flush=True)
+    oracle_insts.clear()
+    torch.cuda.empty_cache()
+
+    act_quant_tables(hip, stream, dev, res)
 
     # route preparation: single workgroup against count + scan/scatter
     print()
@@ -930,6 +949,8 @@ def main():
                     help="configs of --variants-general, comma-separated")
     ap.add_argument("--variants-formats", default="block FP8,W8A8,MXFP4",
                     help="weight formats of --variants-general, comma-separated")
+    ap.add_argument("--act-quant", action="store_true",
+                    help="only the activation + quantisation tables (the pages' workload and expert parallelism)")
     ap.add_argument("--phases", action="store_true",
                     help="only the decode layer's phase table: each kernel alone and the layer at five hidden widths, "
                          "fixed cost and streaming rate per kernel fitted, the H=7168 layer split into them")
@@ -977,6 +998,9 @@ def main():
         return
     if args.phases:
         phase_table(hip, stream, dev, args.steps)
+        return
+    if args.act_quant:
+        act_quant_tables(hip, stream, dev)
         return
     if args.variants_general:
         variants_table(hip, stream, dev, block_m=args.block_m, configs=args.variants_configs.split(","),

@@ -77,6 +77,31 @@ def test_silu_and_mul_exhaustive_gate(clamp, I):
         assert ((got == ref) | both_nan).all(), np.argwhere(~((got == ref) | both_nan))[:5]
 
 
+@pytest.mark.parametrize("clamp", [math.inf, 7.0, 7.1])
+def test_act_quant_filtered_every_bf16_gate(clamp):
+    # every BF16 gate value, 32 times, through the filtered act + quant (row
+    # ids, all rows local: 16384 groups of 128, so the kernel whose exp table
+    # sits in LDS); codes and scales bit-exact
+    print_case("act_quant filtered exhaustive", clamp)
+    I = 4096
+    gates = ALL_BF16.reshape(512, 128).repeat(1, I // 128)
+    # ups within +-0.5, so that every product stays finite; the two rows of
+    # NaN and inf gate codes are dropped (their groups' scales are not finite)
+    ups = (torch.randn(512, I, generator=torch.Generator().manual_seed(3)) * 0.2).clamp(-0.5, 0.5)
+    x = torch.cat([gates, ups.to(torch.bfloat16)], dim=1).contiguous()
+    x = x[torch.isfinite(x.float()).all(dim=1)].contiguous()
+    rows = x.shape[0]
+    ids = torch.zeros(rows, dtype=torch.int32)
+    qs = torch.full((rows, I), 0x5A, dtype=torch.uint8)
+    ss = torch.full((rows, I // 128), -3.0)
+    q, s = bfp8.silu_and_mul_quant_fp8(x.to(dev()), q=qs.to(dev()), scales=ss.to(dev()), row_expert_ids=ids.to(dev()),
+                                       expert_map=None, E=4, clamp_limit=clamp, scale_fmt=bfp8.SCALE_FP32)
+    torch.cuda.synchronize()
+    rq, rs = O.silu_and_mul_quant_fp8(x, ids, None, 4, clamp, bfp8.SCALE_FP32, q_init=qs.numpy(), s_init=ss.numpy())
+    assert (q.cpu().numpy() == rq).all()
+    assert (s.cpu().numpy().view(np.uint32) == rs.view(np.uint32)).all()
+
+
 @pytest.mark.parametrize("fmt", [bfp8.SCALE_FP32, bfp8.SCALE_UE8M0])
 @pytest.mark.parametrize("I", [512, 2048])
 @pytest.mark.parametrize("rows", [8, 128, 1024])
