@@ -16,7 +16,9 @@
 // into MFMA fragments through a per-wave LDS slice; for blocks of 32 or 64
 // routes the workgroup loads each chunk of the block's activation rows once,
 // as whole lines, into a shared LDS buffer that all 4 waves read their
-// fragments from (see mfma.h for the K slot order).
+// fragments from (see mfma.h for the K slot order).  The block's activation
+// scales and the tile's weight scales are staged in LDS once per workgroup,
+// and blocks of 16 and 32 routes keep two K chunks in flight.
 //
 // Pages cited in brackets, by key and section:
 //   [P1] lmdeploy PR "Perf/pytorch block fp8 moe decode"
