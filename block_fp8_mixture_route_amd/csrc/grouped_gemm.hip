@@ -288,9 +288,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
 
   // The K loop keeps kAhead chunks in flight: chunk c is multiplied from
   // register set c % (kAhead + 1) while the loads of the next kAhead chunks
-  // are out (a workgroup's step is bound by the round trip of its loads, not
-  // by the memory system's rate, so a deeper queue per wave streams faster;
-  // blocks of 64 routes keep one chunk ahead, for registers).  fetch
+  // are out (two measured a little faster than one at blocks of 16 and 32
+  // routes; blocks of 64 routes keep one, for registers).  fetch
   // requests chunk gn into (wn, xn, sn, wsn); use multiplies the chunk held
   // in (wc, xc, sc, wsc) through shared buffer xb.  The sets rotate, so
   // nothing is copied, and every load is issued before the chunk kAhead
