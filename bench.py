@@ -802,6 +802,43 @@ def act_quant_tables(hip, stream, dev, res=None):
     return res
 
 
+def stream_probe_table(hip, stream, dev):
+    """What this memory system gives a read shape: 4 GiB read once per launch
+    by bfp8moe_stream_probe, contiguous slabs and the grouped GEMM's tile
+    shape (128 rows per workgroup, 8 rows x 128 bytes per load instruction, or
+    1,024 bytes of a row per load), its walk along K in order or rotated per
+    workgroup, at the GEMMs' row lengths, with 2, 3 or 8 workgroups per
+    compute unit (unused LDS); graph-timed over 5 reads."""
+    import torch
+
+    import block_fp8_mixture_route_amd as bfp8
+
+    L_ = bfp8.lib()
+    P = ctypes.c_void_p
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    print("| shape | row bytes | bytes of a row per load | workgroups per CU | TB/s |")
+    print("|---|---|---|---|---|")
+    res = []
+    for occ in (2, 3, 8):
+        lds = 0 if occ >= 8 else 160 * 1024 // occ - 1024
+        for pattern, K, piece in ([(0, 0, 128)] + [(pt, K, pc) for K in (4096, 1024, 7168) for pc in (128, 1024)
+                                                    for pt in (1, 2)]):
+            def body():
+                bfp8._lib.check(L_.bfp8moe_stream_probe(P(buf.data_ptr()), nbytes, pattern, K, piece, lds,
+                                                        P(sink.data_ptr()), sink.numel(), stream))
+
+            used = nbytes if pattern == 0 else nbytes // (128 * K) * 128 * K
+            ms = time_graph(hip, stream, body, 5)
+            tbs = used / (ms * 1e-3) / 1e12
+            shape = ["contiguous", "tile", "tile, K walk rotated per workgroup"][pattern]
+            res.append({"shape": shape, "row_bytes": K, "piece": piece, "wg_per_cu": occ, "tbs": tbs})
+            print(f"| {shape} | {K or '—'} | {piece if pattern else '—'} | {occ} | {tbs:.2f} |", flush=True)
+    return res
+
+
 def suite(hip, stream, dev):
     """Every layer config, the activation+quant workload (fused against two
     kernels), route preparation (one workgroup against many) and a plain copy
@@ -949,6 +986,8 @@ def main():
                     help="configs of --variants-general, comma-separated")
     ap.add_argument("--variants-formats", default="block FP8,W8A8,MXFP4",
                     help="weight formats of --variants-general, comma-separated")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only the read-bandwidth probe: contiguous and GEMM-tile read shapes over 4 GiB")
     ap.add_argument("--act-quant", action="store_true",
                     help="only the activation + quantisation tables (the pages' workload and expert parallelism)")
     ap.add_argument("--phases", action="store_true",
@@ -1001,6 +1040,9 @@ def main():
         return
     if args.act_quant:
         act_quant_tables(hip, stream, dev)
+        return
+    if args.stream_probe:
+        stream_probe_table(hip, stream, dev)
         return
     if args.variants_general:
         variants_table(hip, stream, dev, block_m=args.block_m, configs=args.variants_configs.split(","),

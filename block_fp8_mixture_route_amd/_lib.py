@@ -73,6 +73,9 @@ SIGNATURES = {
     "bfp8moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bfp8moe_last_error": (ctypes.c_char_p, []),
     "bfp8moe_wait_faults": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]),
+    "bfp8moe_stream_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_void_p]),
     "bfp8moe_max_blocks": (_i64, [_i64, _i32, _i32]),
     "moe_route_prepare_workspace_size": (_sz, [_i64, _i32, _u32]),
     "moe_route_prepare": (ctypes.c_int, [_P, _i64, _i32, _i32, _i32, _P, _P, _P, _P, _i64, _P, _P, _sz, _u32, _P]),
@@ -177,6 +180,17 @@ def _expect(t, name, dtypes, shape=None):
 
 
 _FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def stream_probe(buf: torch.Tensor, pattern: int, sink: torch.Tensor, row_bytes=0, piece=128, lds_bytes=0):
+    """One read of the uint8 device buffer `buf` in the probe's shape (pattern
+    0 contiguous, 1 GEMM-shaped tiles of rows of row_bytes); measurement only.
+    sink: int32 device tensor of at least one word per workgroup."""
+    _expect(buf, "buf", torch.uint8, (None,))
+    _expect(sink, "sink", torch.int32, (None,))
+    _require_device(buf, sink)
+    check(lib().bfp8moe_stream_probe(ptr(buf), buf.numel(), pattern, row_bytes, piece, lds_bytes, ptr(sink),
+                                     sink.numel(), stream_of(buf.device)))
 
 
 def wait_faults(clear=True) -> int:

@@ -266,6 +266,27 @@ bfp8moe_status_t bfp8moe_wait_faults(uint32_t* flags, int clear) {
   return BFP8MOE_OK;
 }
 
+bfp8moe_status_t bfp8moe_stream_probe(const uint8_t* buf, size_t bytes, int32_t pattern, int32_t row_bytes,
+                                      int32_t piece, int32_t lds_bytes, uint32_t* sink, int64_t sink_len,
+                                      void* stream) {
+  REQUIRE(buf != nullptr && sink != nullptr, "buf and sink must be non-null");
+  REQUIRE(aligned16(buf), "buf must be 16-byte aligned");
+  REQUIRE(pattern >= 0 && pattern <= 2, "pattern=%d must be 0 (contiguous), 1 (tile) or 2 (tile, rotated)",
+          pattern);
+  if (pattern != 0) {
+    REQUIRE(piece == 128 || piece == 256 || piece == 1024, "piece=%d must be 128, 256 or 1024", piece);
+    REQUIRE(row_bytes >= 1024 && row_bytes % 1024 == 0 && row_bytes % piece == 0,
+            "row_bytes=%d must be a positive multiple of 1024 and of piece", row_bytes);
+  }
+  REQUIRE(lds_bytes >= 0 && lds_bytes <= 163840, "lds_bytes=%d out of [0, 163840]", lds_bytes);
+  const int64_t grid = bfp8::stream_probe_grid(bytes, pattern, row_bytes);
+  REQUIRE(grid >= 1 && grid <= 0x7FFFFFFF, "%zu bytes give %lld workgroups", bytes, (long long)grid);
+  REQUIRE(sink_len >= grid, "sink holds %lld words for %lld workgroups", (long long)sink_len, (long long)grid);
+  return hip_status(bfp8::launch_stream_probe(buf, bytes, pattern, row_bytes, piece, lds_bytes, sink,
+                                              (hipStream_t)stream),
+                    "bfp8moe_stream_probe");
+}
+
 int64_t bfp8moe_max_blocks(int64_t R, int32_t L, int32_t block_m) {
   if (R <= 0 || L <= 0 || block_m <= 0) return 0;
   const int64_t d = R < L ? R : L;

@@ -206,4 +206,13 @@ hipError_t launch_decode_layer(const uint16_t* hidden, int64_t M, int H, const i
                                const uint8_t* w2, const float* w2_s, int I, int fmt, float limit, uint16_t* act,
                                uint16_t* out, hipStream_t stream, const LaunchHook* hook);
 
+// The read-bandwidth probe (stream_probe.hip): pattern 0 contiguous 512 KiB
+// slabs, 1 GEMM-shaped 128-row tiles of row_bytes with `piece` bytes per row
+// per load, 2 the same with each workgroup's walk along K rotated; lds_bytes
+// of unused dynamic LDS per workgroup.  Workgroups of a
+// launch: stream_probe_grid.
+int64_t stream_probe_grid(size_t bytes, int pattern, int row_bytes);
+hipError_t launch_stream_probe(const uint8_t* buf, size_t bytes, int pattern, int row_bytes, int piece,
+                               int lds_bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace bfp8

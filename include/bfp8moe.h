@@ -174,6 +174,22 @@ const char* bfp8moe_last_error(void);
  * is not for use inside stream capture or a latency-critical loop. */
 bfp8moe_status_t bfp8moe_wait_faults(uint32_t* flags, int clear);
 
+/* Measurement only (no part of the layer): one launch that reads the device
+ * buffer buf [bytes] and keeps nothing, to time what this memory system gives
+ * a read shape.  pattern 0: contiguous 512 KiB slabs, one per workgroup
+ * (bytes / 512 KiB workgroups).  pattern 1: the buffer as rows of row_bytes
+ * (a multiple of 1024 and of piece), one workgroup per 128 rows read the way
+ * the grouped GEMM reads a weight tile, piece bytes of each row per load
+ * (128, 256 or 1024; 128 is the GEMM's; bytes / (128 row_bytes)
+ * workgroups).  pattern 2: as 1, workgroup b starting along the row at piece
+ * b mod (row_bytes / piece) and wrapping around.  lds_bytes (0 .. 163840) of unused dynamic LDS per workgroup
+ * bound how many share a compute unit.  sink [sink_len] device uint32, at
+ * least one word per workgroup (never written in practice).  buf 16-byte
+ * aligned.  Returns BFP8MOE_ERR_INVALID_ARG for any other shape. */
+bfp8moe_status_t bfp8moe_stream_probe(const uint8_t* buf, size_t bytes, int32_t pattern, int32_t row_bytes,
+                                      int32_t piece, int32_t lds_bytes, uint32_t* sink, int64_t sink_len,
+                                      void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Route preparation                                                         */
 /* [P2 Changes: shared route preparation, one workgroup for small problems,   */

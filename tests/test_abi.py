@@ -128,6 +128,22 @@ def _status(fn, *args):
     return st, bfp8.lib().bfp8moe_last_error().decode()
 
 
+def test_stream_probe_rejects_bad_shapes():
+    L = bfp8.lib()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: validation fails first
+    one_gib = 1 << 30
+    for args, text in [((fake, one_gib, 3, 0, 128, 0, fake, 1 << 20), "pattern"),
+                       ((fake, one_gib, 1, 4096, 512, 0, fake, 1 << 20), "piece"),
+                       ((fake, one_gib, 1, 1000, 128, 0, fake, 1 << 20), "row_bytes"),
+                       ((fake, one_gib, 1, 4096, 128, 170000, fake, 1 << 20), "lds_bytes"),
+                       ((fake, one_gib, 0, 0, 128, 0, fake, 10), "sink holds"),
+                       ((fake, 1000, 0, 0, 128, 0, fake, 10), "workgroups"),
+                       ((P(0x1001), one_gib, 0, 0, 128, 0, fake, 1 << 20), "aligned")]:
+        st, msg = _status(L.bfp8moe_stream_probe, *args, None)
+        assert st == 1 and text in msg, (args, msg)
+
+
 def test_host_validation_rejects_bad_calls():
     L = bfp8.lib()
     P = ctypes.c_void_p
