@@ -310,7 +310,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
       for (int t = 0; t < CT; t++) xn[t] = load_frag(arow[t] + (size_t)gn * kGroup, kq);
     }
   };
-  auto use = [&](int gc, u32x4 (&wc)[4], auto& xc, float (&sc)[CT], float wsc, u32x4* xb) __attribute__((always_inline)) {
+  auto use = [&](int gc, u32x4 (&wc)[4], auto& xc, float (&sc)[CT], float wsc, u32x4* xb)
+      __attribute__((always_inline)) {
     if constexpr (kSharedX) {
 #pragma unroll
       for (int x = 0; x < XL; x++) {
@@ -462,8 +463,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BM == 
 // activation chunk (BM rows of 256 bytes) goes through a shared LDS buffer,
 // 16-byte piece p of row r stored at p ^ (r & 15).
 // kStage: the block's activation scales staged in LDS once (dynamic LDS of
-// gemm_stage_bytes), as in grouped_gemm_kernel.
-template <int BM, bool kStage>
+// gemm_stage_bytes), as in grouped_gemm_kernel.  kStageW: the tile's weight
+// scale bytes (128 rows x K / 32) staged in LDS once, for K / 128 a power of
+// two from 4 to 32: per K step they were one
+// 8-byte load per fragment row, 16 rows' lines per instruction.
+template <int BM, bool kStage, bool kStageW>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, int a_row_div, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, int N, int K, const int32_t* __restrict__ sorted_routes,
@@ -494,8 +498,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
   uint2 b0[kRT], b1[kRT];
 #pragma unroll
   for (int i = 0; i < 4; i++) w0[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * KB);
+  if constexpr (!kStageW) {
 #pragma unroll
-  for (int i = 0; i < kRT; i++) b0[i] = *reinterpret_cast<const uint2*>(wsr[i]);
+    for (int i = 0; i < kRT; i++) b0[i] = *reinterpret_cast<const uint2*>(wsr[i]);
+  }
 
   // the routes of this lane's MFMA columns and their activation-scale rows,
   // and the activation pieces this thread loads: piece q = tid + 256 x of
@@ -545,6 +551,24 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
   extern __shared__ float s_dyn[];
   float* s_as = s_dyn;
   if constexpr (kStage) stage_act_scales<BM>(s_as, As, a_row_div, G, route, lane, wave);
+  // staged weight scale bytes: word w of tile row r (bytes 4 w .. 4 w + 3 of
+  // its NS) at word w ^ (r % NW) of the row, NW = NS / 4 words per row (a
+  // power of two), so that the 16 rows of one read fall in distinct banks;
+  // the rows of a tile are contiguous in Bs, read 16 bytes per thread
+  __shared__ uint32_t s_wsc[kStageW ? kBN * 32 : 1];
+  const int NW = NS / 4;
+  if constexpr (kStageW) {
+    const uint8_t* wt = Bs + ((size_t)e * N + (size_t)nt * kBN) * NS;
+    for (int q = tid; q < kBN * NS / 16; q += kThreads) {
+      const uint4 v = *reinterpret_cast<const uint4*>(wt + 16 * (size_t)q);
+      const int r = 16 * q / NS, w = (16 * q - r * NS) / 4;
+      uint32_t* row = s_wsc + r * NW;
+      row[(w + 0) ^ (r & (NW - 1))] = v.x;
+      row[(w + 1) ^ (r & (NW - 1))] = v.y;
+      row[(w + 2) ^ (r & (NW - 1))] = v.z;
+      row[(w + 3) ^ (r & (NW - 1))] = v.w;
+    }
+  }
 
   auto step = [&](int cn, int cc, u32x4 (&wc)[4], u32x4 (&xc)[XL], float (&sc)[CT][2], uint2 (&bc)[kRT],
                   u32x4 (&wn)[4], u32x4 (&xn)[XL], float (&sn)[CT][2], uint2 (&bn)[kRT], u32x4* xb)
@@ -556,8 +580,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
         sn[t][1] = asrow[t][2 * cn + 1];
       }
     }
+    if constexpr (!kStageW) {
 #pragma unroll
-    for (int i = 0; i < kRT; i++) bn[i] = *reinterpret_cast<const uint2*>(wsr[i] + 8 * cn);
+      for (int i = 0; i < kRT; i++) bn[i] = *reinterpret_cast<const uint2*>(wsr[i] + 8 * cn);
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) wn[i] = *reinterpret_cast<const u32x4*>(wl + (size_t)(8 * i) * KB + (size_t)cn * 128);
 #pragma unroll
@@ -601,7 +627,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mxfp4_kernel(
         const float asc = kStage ? s_as[(16 * t + col) * (G + 1) + 2 * cc + h] : route[t] >= 0 ? sc[t][h] : 0.0f;
 #pragma unroll
         for (int i = 0; i < kRT; i++) {
-          const int e8 = (int)(((h ? bc[i].y : bc[i].x) >> (8 * kq)) & 0xFFu);
+          int e8;
+          if constexpr (kStageW) {
+            // MX block 8 cc + 4 h + kq of tile row wave 32 + 16 i + col: byte kq of word 2 cc + h
+            const int r = wave * kWN + 16 * i + col;
+            e8 = (int)((s_wsc[r * NW + ((2 * cc + h) ^ (r & (NW - 1)))] >> (8 * kq)) & 0xFFu);
+          } else {
+            e8 = (int)(((h ? bc[i].y : bc[i].x) >> (8 * kq)) & 0xFFu);
+          }
           const v4f p = mfma_f4f8_16x16x128(wa[i][h], xf, e8, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int v = 0; v < 4; v++) acc[i][t][v] = __builtin_fmaf(p[v], asc, acc[i][t][v]);
@@ -686,16 +719,23 @@ hipError_t launch_grouped_gemm_mxfp4(const uint8_t* A, const float* As, int a_ro
   if (K % 256 != 0) return hipErrorInvalidValue;  // the caller checks
   const int64_t grid = gemm_slots_per_xcd(max_blocks, N / kBN) * kXcd;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // the tile's weight scales staged from K = 512 to 4096 with K / 128 a power of two
+  const int kg = K / kGroup;
+  const bool stage_w = kg >= 4 && kg <= 32 && (kg & (kg - 1)) == 0;
+#define BFP8_MX_LAUNCH(BMV, ST, SW)                                                                            \
+  hipLaunchKernelGGL((grouped_gemm_mxfp4_kernel<BMV, ST, SW>), dim3((unsigned)grid), dim3(kThreads),           \
+                     ST ? (size_t)BMV * (K / kGroup + 1) * sizeof(float) : 0, stream, A, As, a_row_div, B, Bs, N,  \
+                     K, sorted_routes, expert_offsets, block_expert, block_start, num_blocks, C)
 #define BFP8_MX_CASE(BMV)                                                                                      \
   case BMV:                                                                                                    \
-    if (gemm_stages(BMV, K))                                                                                   \
-      hipLaunchKernelGGL((grouped_gemm_mxfp4_kernel<BMV, true>), dim3((unsigned)grid), dim3(kThreads),           \
-                         (size_t)BMV * (K / kGroup + 1) * sizeof(float), stream, A, As, a_row_div, B, Bs, N, K,   \
-                         sorted_routes, expert_offsets, block_expert, block_start, num_blocks, C);               \
+    if (gemm_stages(BMV, K) && stage_w)                                                                        \
+      BFP8_MX_LAUNCH(BMV, true, true);                                                                         \
+    else if (gemm_stages(BMV, K))                                                                              \
+      BFP8_MX_LAUNCH(BMV, true, false);                                                                        \
+    else if (stage_w)                                                                                          \
+      BFP8_MX_LAUNCH(BMV, false, true);                                                                        \
     else                                                                                                       \
-      hipLaunchKernelGGL((grouped_gemm_mxfp4_kernel<BMV, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, \
-                         A, As, a_row_div, B, Bs, N, K, sorted_routes, expert_offsets, block_expert, block_start,    \
-                         num_blocks, C);                                                                        \
+      BFP8_MX_LAUNCH(BMV, false, false);                                                                       \
     break;
   switch (block_m) {
     BFP8_MX_CASE(16)
@@ -705,6 +745,7 @@ hipError_t launch_grouped_gemm_mxfp4(const uint8_t* A, const float* As, int a_ro
       return hipErrorInvalidValue;
   }
 #undef BFP8_MX_CASE
+#undef BFP8_MX_LAUNCH
   return hipGetLastError();
 }
 
