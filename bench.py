@@ -1191,18 +1191,45 @@ def oracle_layer_seconds(case, inst, seconds, threads=None, min_runs=1):
 
 def cpu_baseline(case, inst, seconds):
     """The CPU oracle on the same layer (instance 0), repeated for about
-    `seconds`; throughput in the metric's unit (GB/s of compulsory bytes)."""
+    `seconds`; throughput in the metric's unit (GB/s of compulsory bytes).
+
+    Where one oracle run of the whole layer would take longer than `seconds`,
+    the sample is the routes of the first n experts the layer uses (the rest
+    dropped), n sized from a one-expert probe so a run takes about a tenth of
+    `seconds`; the oracle's work is per route, so the layer's time is the
+    sample's scaled by all routes over the sample's routes."""
+    import torch
     from oracle import oracle as O
 
     hidden, ids, w, W = inst
     O.fused_moe  # the library is built and loaded before timing
     nbytes, _ = layer_bytes(case, ids)
-    oracle_layer_seconds(case, inst, 0.0)  # warm
-    dt, n, threads = oracle_layer_seconds(case, inst, seconds)
-    log(f"cpu oracle: {dt * 1e3:.1f} ms/layer over {n} runs, {threads} thread(s)")
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{case.name} instance 0, whole layer, {n} runs ({dt * 1e3:.1f} ms each)",
-            "us_per_layer": round(dt * 1e6, 1)}
+    used = torch.unique(ids[ids >= 0])
+    n_routes = int((ids >= 0).sum())
+
+    def first_experts(n):
+        keep = torch.isin(ids, used[:n])
+        return (hidden, torch.where(keep, ids, torch.full_like(ids, -1)), w, W), int(keep.sum())
+
+    probe, probe_routes = first_experts(1)
+    log(f"cpu oracle: probe on the {probe_routes} routes of one expert of {used.numel()}")
+    dt1, _, _ = oracle_layer_seconds(case, probe, 0.0)  # also warms
+    n = used.numel()
+    if dt1 * n > seconds:
+        n = max(1, min(n, int(seconds / 10 / dt1)))
+    sample, sample_routes = first_experts(n)
+    log(f"cpu oracle: timing {sample_routes} of {n_routes} routes ({n} of {used.numel()} experts) "
+        f"for about {seconds:.0f} s")
+    dt, runs, threads = oracle_layer_seconds(case, sample, seconds)
+    dt_layer = dt * n_routes / sample_routes
+    log(f"cpu oracle: {dt * 1e3:.1f} ms per sample run over {runs} runs, {threads} thread(s); "
+        f"{dt_layer * 1e3:.1f} ms/layer")
+    what = ("whole layer" if n == used.numel() else
+            f"routes of {n} of {used.numel()} experts ({sample_routes} of {n_routes} routes), time scaled "
+            f"by routes to the whole layer")
+    return {"value": round(nbytes / dt_layer / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{case.name} instance 0, {what}, {runs} runs ({dt * 1e3:.1f} ms each)",
+            "us_per_layer": round(dt_layer * 1e6, 1)}
 
 
 if __name__ == "__main__":
