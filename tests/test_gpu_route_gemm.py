@@ -113,11 +113,12 @@ def test_grouped_gemm_down(shape, B):
 
 
 @pytest.mark.parametrize("B", [16, 32, 64])
-@pytest.mark.parametrize("K", [128, 384, 512, 640, 896, 1152])
+@pytest.mark.parametrize("K", [128, 256, 384, 512, 640, 768, 896, 1152])
 def test_grouped_gemm_k_loop_tails(K, B):
-    # 1, 3, 4, 5, 7 and 9 K chunks: every remainder of the loop that keeps two
-    # chunks in flight (three steps per iteration), and both sides of the
-    # chunk count from which the block scales are staged in LDS
+    # 1 to 7 and 9 K chunks: every remainder of the loops that keep two
+    # chunks in flight (three steps per iteration) and one (two steps), twice
+    # over, and both sides of the chunk count from which the block scales are
+    # staged in LDS
     print_case("gemm k tails", K, B)
     got, ref, ids = _gemm_case(8, 4, 8, 256, K, B, seed=K + B)
     valid = (ids.view(-1) >= 0).numpy()
