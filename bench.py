@@ -565,7 +565,7 @@ def variants_table(hip, stream, dev, block_m=0, configs=("small_m128", "small_m5
     return res
 
 
-def variants_decode_table(hip, stream, dev, token_counts=(1, 4), both_paths=False):
+def variants_decode_table(hip, stream, dev, token_counts=(1, 4), both_paths=False, formats=None):
     """The decode layer (E=256, top-k 8, H=7168, I=256) at a few token counts
     with each weight format: block FP8, W8A8 (random E4M3 codes, per-channel
     scales, dynamic per-token activation scales) and MXFP4 (random E2M1
@@ -574,7 +574,7 @@ def variants_decode_table(hip, stream, dev, token_counts=(1, 4), both_paths=Fals
     and the rotation of instances reads every expert once, more bytes than the
     Infinity Cache holds.  Graph-timed; compulsory bytes as variants_table.
     both_paths: the few-token and general paths forced in turn, else the
-    library's choice."""
+    library's choice.  formats: the weight formats to run (default all)."""
     import torch
 
     import block_fp8_mixture_route_amd as bfp8
@@ -625,6 +625,8 @@ def variants_decode_table(hip, stream, dev, token_counts=(1, 4), both_paths=Fals
         res[M] = {}
         runs = []
         for f, (o, wbytes, fn) in forms.items():
+            if formats is not None and f not in formats:
+                continue
             flag_list = [PATH_FLAGS["token"], PATH_FLAGS["general"]] if both_paths else [0]
             for fl in flag_list:
                 runs.append((f, bfp8.opts(weight_scale_mode=o.weight_scale_mode, flags=fl), wbytes, fn))
@@ -972,6 +974,8 @@ def main():
                          "hardware traffic counters)")
     ap.add_argument("--path", choices=sorted(PATH_FLAGS), default="auto",
                     help="force one implementation of the layer (default: the library's choice by shape)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="the config's layer at this many tokens instead (same shape and routing kind)")
     ap.add_argument("--block-m", type=int, default=0, help="routes per compact block of the general path (0 = auto)")
     ap.add_argument("--floor", action="store_true", help="only the graph launch floor of one kernel")
     ap.add_argument("--router", action="store_true", help="only the router timing table")
@@ -985,7 +989,9 @@ def main():
     ap.add_argument("--variants-configs", default="small_m128,small_m512,large_m2048",
                     help="configs of --variants-general, comma-separated")
     ap.add_argument("--variants-formats", default="block FP8,W8A8,MXFP4",
-                    help="weight formats of --variants-general, comma-separated")
+                    help="weight formats of --variants-general and --variants-crossover, comma-separated")
+    ap.add_argument("--crossover-tokens", default="4,8,12,16",
+                    help="token counts of --variants-crossover, comma-separated (each at most 32)")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only the read-bandwidth probe: contiguous and GEMM-tile read shapes over 4 GiB")
     ap.add_argument("--act-quant", action="store_true",
@@ -1008,6 +1014,14 @@ def main():
               "(16 routes per block at small M=128) ended in a GPU memory fault whose cause has not been found",
               file=sys.stderr)
         sys.exit(3)
+    if args.variants_crossover:
+        toks = args.crossover_tokens.split(",")
+        if not all(t.isdigit() and 1 <= int(t) <= 32 for t in toks):
+            print(f"--crossover-tokens takes token counts from 1 to 32 (got {args.crossover_tokens})", file=sys.stderr)
+            sys.exit(2)
+    if args.tokens < 0:
+        print(f"--tokens takes a positive token count (got {args.tokens})", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -1033,7 +1047,8 @@ def main():
         variants_decode_table(hip, stream, dev)
         return
     if args.variants_crossover:
-        variants_decode_table(hip, stream, dev, token_counts=(4, 8, 12, 16), both_paths=True)
+        variants_decode_table(hip, stream, dev, token_counts=tuple(int(t) for t in args.crossover_tokens.split(",")),
+                              both_paths=True, formats=args.variants_formats.split(","))
         return
     if args.phases:
         phase_table(hip, stream, dev, args.steps)
@@ -1055,6 +1070,8 @@ def main():
         return
 
     case = synth.LAYER_CASES[args.config]
+    if args.tokens:
+        case = dataclasses.replace(case, name=f"{case.name}_tokens{args.tokens}", M=args.tokens)
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -1072,7 +1089,7 @@ def main():
     dom_bytes = sum(stage_bytes(case, x[1], dom) for x in insts) / n_inst
     dom_us = stage_us[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = measured_traffic(dom, args.config)
+    traffic = None if args.tokens else measured_traffic(dom, args.config)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes": int(dom_bytes), "avg_us": round(dom_us, 3)}

@@ -78,12 +78,15 @@ const char* const kTokenChannelStages[] = {"token_gate_up_swiglu_channel", "toke
 enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
 
 // The few-token path is the default up to this many tokens: it reads one
-// expert's weights once per route, the general path once per expert, and at
-// the decode shape (256 experts, top-8, H 7168, I 256) the general path
-// overtakes it at about 14 tokens (measured at 4 to 24).  The small-batch
-// path is the default up to kDecodeAutoMaxM tokens where the few-token path
-// does not fit.
-constexpr int64_t kTokenAutoMaxM = 12;
+// expert's weights once per route, the general path once per expert.  At the
+// decode shape (256 experts, top-8, H 7168, I 256, uniform routing) with
+// block scales, the few-token path leads at 14 tokens (113.0 against 120.1 µs)
+// and the general path at 16 (125.3 against 127.1).  With per-channel (W8A8)
+// weights the bound stays where it was measured before the general path's
+// GEMM staged its scales: 12.  The small-batch path is the default up to
+// kDecodeAutoMaxM tokens where the few-token path does not fit.
+constexpr int64_t kTokenAutoMaxM = 15;
+constexpr int64_t kTokenAutoMaxMChannel = 12;
 constexpr int64_t kDecodeAutoMaxM = 4;
 // With MXFP4 weights the few-token kernels do as much vector work per
 // element as with E4M3 rows while the general path's FP4 MFMA halves its
@@ -132,7 +135,7 @@ void plan_layer(LayerPlan& p, int64_t M, int32_t H, int32_t k, int32_t E, int32_
     p.mode = fits ? kModeDecode : kModeGeneral;
   else if (o.flags & BFP8MOE_FLAG_LAYER_TOKEN)
     p.mode = token_fits ? kModeToken : kModeGeneral;
-  else if (token_fits && M <= (p.mxfp4 ? kTokenAutoMaxMMxfp4 : kTokenAutoMaxM))
+  else if (token_fits && M <= (p.mxfp4 ? kTokenAutoMaxMMxfp4 : p.channel ? kTokenAutoMaxMChannel : kTokenAutoMaxM))
     p.mode = kModeToken;
   else
     p.mode = (fits && M <= kDecodeAutoMaxM) ? kModeDecode : kModeGeneral;

@@ -460,7 +460,8 @@ size_t fused_moe_block_fp8_workspace_size(int64_t M, int32_t H, int32_t k, int32
  * pointer (NULL = defaults).
  * Three implementations, chosen by shape unless a test flag forces one:
  *   few tokens (M <= 32, k <= 16, H <= 8192, I in {128, 256, 512}; the
- *     default up to 12 tokens): two matrix-vector kernels -- input
+ *     default up to 15 tokens, 12 with per-channel weight scales, 8 with
+ *     MXFP4 weights): two matrix-vector kernels -- input
  *     quantisation, gate/up GEMM and SwiGLU per route (M x k x I/8
  *     workgroups; each route reads its expert's rows), then the SwiGLU
  *     output's quantisation, down GEMM and moe_reduce per token and block of

@@ -91,13 +91,17 @@ def test_stage_lists():
     assert bfp8.fused_moe_stages(1, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
     # the one-token path needs I in {128, 256, 512}; other shapes fall back
     assert bfp8.fused_moe_stages(1, 4096, 8, 256, 384, o) == ["decode_gate_up_swiglu", "decode_down_reduce"]
-    # the few-token path up to 12 tokens; the others when forced
+    # the few-token path up to 15 tokens (12 with per-channel weight scales);
+    # the others when forced
     assert bfp8.fused_moe_stages(4, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
-    assert bfp8.fused_moe_stages(12, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
+    assert bfp8.fused_moe_stages(15, 7168, 8, 256, 256, o) == ["token_gate_up_swiglu", "token_down_reduce"]
+    ch = bfp8.opts(weight_scale_mode=bfp8.WEIGHT_SCALE_CHANNEL)
+    assert bfp8.fused_moe_stages(12, 7168, 8, 256, 256, ch)[0] == "token_gate_up_swiglu_channel"
+    assert not bfp8.fused_moe_stages(13, 7168, 8, 256, 256, ch)[0].startswith("token_")
     # the general path: route preparation carries the input quantisation
     # (one launch fewer) unless one workgroup sorts for more than 512 experts
     fused = ["route_prepare_quant", "gate_up_gemm", "silu_and_mul_quant", "down_gemm", "moe_reduce"]
-    assert bfp8.fused_moe_stages(13, 7168, 8, 256, 256, o) == fused
+    assert bfp8.fused_moe_stages(16, 7168, 8, 256, 256, o) == fused
     assert bfp8.fused_moe_stages(32, 7168, 8, 256, 256, o) == fused
     assert bfp8.fused_moe_stages(2048, 4096, 8, 512, 1024, o) == fused  # many-workgroup route prep
     assert bfp8.fused_moe_stages(64, 4096, 8, 1024, 256, o) == [
