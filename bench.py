@@ -1023,7 +1023,7 @@ def main():
         print(f"--tokens takes a positive token count (got {args.tokens})", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 
