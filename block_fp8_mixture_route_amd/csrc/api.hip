@@ -80,7 +80,7 @@ enum { kModeGeneral = 0, kModeDecode = 1, kModeToken = 2 };
 // The few-token path is the default up to this many tokens: it reads one
 // expert's weights once per route, the general path once per expert.  At the
 // decode shape (256 experts, top-8, H 7168, I 256, uniform routing) with
-// block scales, the few-token path leads at 14 tokens (113.0 against 120.1 µs)
+// block scales, the few-token path leads at 15 tokens (120.8 against 122.9 µs)
 // and the general path at 16 (125.3 against 127.1).  With per-channel (W8A8)
 // weights the bound stays where it was measured before the general path's
 // GEMM staged its scales: 12.  The small-batch path is the default up to
